@@ -1,0 +1,283 @@
+/*
+ * rope_oracle.c -- CPU oracle for rotary position embedding (RoPE).
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, scalar statement of
+ * what the GPU library computes. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load it; no product code links, includes or
+ * calls it, and it shares no source, header or constant with the GPU library.
+ *
+ * What it computes (binary64 scalar loops, nothing blocked or fused):
+ *
+ *   freq_i = theta^(-2i/R), i = 0 .. R/2-1
+ *       rotary-embedding-torch docs, Key Parameters: `theta` is the base of
+ *       the frequencies (default 10000) and `dim` is the width of the part
+ *       being rotated, so the exponent runs over the rotary dim R.
+ *   angle  = p * freq_i for the token's position p
+ *       "Rotary Embedding Kernel", Overview: applied per position along the
+ *       sequence.
+ *   (x1, x2) -> (x1*cos - x2*sin, x1*sin + x2*cos)
+ *       "Rotary Embedding Kernel", Overview (the rotation of one pair).
+ *   pairs (x[i], x[i + R/2]) or (x[2i], x[2i+1])
+ *       "Rotary Embedding Kernel", Paired Element Layout (split-half and
+ *       interleaved), applied to the first R dims of each head row.
+ *   backward = the same rotation with sin negated
+ *       Unsloth page, Frequently Asked Questions (backward reuses the forward
+ *       kernels under a flag); the transpose of a rotation is the rotation by
+ *       the opposite angle.
+ *   p = pos[b * pos_batch_stride + s] when an index tensor is given, else s
+ *       Unsloth page, Support for Custom Position IDs; a negative (or
+ *       >= table_rows) index leaves the token's row unchanged, which is how
+ *       CLS/register tokens are skipped (rotary-embedding-torch docs,
+ *       flash_attn_with_rotary).
+ *
+ * Table contract ("table mode"): cos and sin of the binary64 angle are each
+ * rounded once to float32, because that is the precision of the tables the
+ * GPU path reads. Each output is then x1*c32 - s*x2*s32 evaluated in binary64
+ * (both products are exact there) and rounded once, to nearest-even, into the
+ * storage dtype. Rows and dims that are not rotated are copied bit for bit.
+ *
+ * "Exact mode" (oracle_rope_exact) uses the unrounded binary64 cos/sin and
+ * binary64 inputs/outputs; it exists for the invariant checks.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* Codes of this file's own interface (mirrored in oracle/__init__.py). */
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_BHSD = 0, ORC_BSHD = 1 };
+enum { ORC_SPLIT_HALF = 0, ORC_INTERLEAVED = 1 };
+
+/* ---------------------------------------------------------------- numbers */
+
+/* Exact value of a stored element as binary64. */
+static double load_elem(const void *base, int64_t idx, int dtype) {
+  if (dtype == ORC_F32) {
+    float v;
+    memcpy(&v, (const char *)base + 4 * idx, 4);
+    return (double)v;
+  }
+  uint16_t h;
+  memcpy(&h, (const char *)base + 2 * idx, 2);
+  if (dtype == ORC_BF16) {
+    /* bfloat16 is the top half of a float32 */
+    uint32_t w = (uint32_t)h << 16;
+    float v;
+    memcpy(&v, &w, 4);
+    return (double)v;
+  }
+  /* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits */
+  int sign = (h >> 15) & 1;
+  int ex = (h >> 10) & 0x1f;
+  int fr = h & 0x3ff;
+  double mag;
+  if (ex == 0)
+    mag = ldexp((double)fr, -24); /* subnormal: fr * 2^-24 */
+  else if (ex == 31)
+    mag = fr ? NAN : INFINITY;
+  else
+    mag = ldexp((double)(fr + 1024), ex - 25); /* (1 + fr/1024) * 2^(ex-15) */
+  return sign ? -mag : mag;
+}
+
+/*
+ * Round y to the nearest value with `prec` significant bits whose exponent is
+ * at least `emin` (values below 2^emin are kept on the fixed grid 2^(emin -
+ * prec + 1), i.e. gradual underflow), ties to even. The scaling by a power of
+ * two is exact, and nearbyint rounds to nearest-even in the default mode.
+ */
+static double round_prec(double y, int prec, int emin) {
+  if (y == 0.0 || !isfinite(y)) return y;
+  int e;
+  frexp(y, &e); /* |y| in [2^(e-1), 2^e) */
+  int lead = e - 1;
+  if (lead < emin) lead = emin;
+  int q = lead - (prec - 1); /* exponent of one unit in the last place */
+  return ldexp(nearbyint(ldexp(y, -q)), q);
+}
+
+/* binary64 -> IEEE binary16 bits, round to nearest-even, overflow to inf. */
+static uint16_t to_f16_bits(double y) {
+  if (isnan(y)) return 0x7e00;
+  uint16_t sign = signbit(y) ? 0x8000 : 0;
+  double r = fabs(round_prec(y, 11, -14));
+  if (r > 65504.0) return sign | 0x7c00;
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, -14)) /* subnormal: r = m * 2^-24 */
+    return sign | (uint16_t)ldexp(r, 24);
+  int e;
+  double m = frexp(r, &e); /* r = m * 2^e, m in [0.5, 1) */
+  uint16_t ex = (uint16_t)(e - 1 + 15);
+  uint16_t fr = (uint16_t)(ldexp(m, 11) - 1024.0);
+  return sign | (uint16_t)(ex << 10) | fr;
+}
+
+/* binary64 -> bfloat16 bits (8 significant bits, float32's exponent range). */
+static uint16_t to_bf16_bits(double y) {
+  if (isnan(y)) return signbit(y) ? 0xffc0 : 0x7fc0;
+  uint16_t sign = signbit(y) ? 0x8000 : 0;
+  double r = fabs(round_prec(y, 8, -126));
+  double maxfin = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+  if (r > maxfin) return sign | 0x7f80;
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, -126)) /* subnormal: r = m * 2^-133 */
+    return sign | (uint16_t)ldexp(r, 133);
+  int e;
+  double m = frexp(r, &e);
+  uint16_t ex = (uint16_t)(e - 1 + 127);
+  uint16_t fr = (uint16_t)(ldexp(m, 8) - 128.0);
+  return sign | (uint16_t)(ex << 7) | fr;
+}
+
+static void store_elem(void *base, int64_t idx, int dtype, double y) {
+  if (dtype == ORC_F32) {
+    float v = (float)y; /* C conversion: round to nearest-even */
+    memcpy((char *)base + 4 * idx, &v, 4);
+    return;
+  }
+  uint16_t h = (dtype == ORC_BF16) ? to_bf16_bits(y) : to_f16_bits(y);
+  memcpy((char *)base + 2 * idx, &h, 2);
+}
+
+static int64_t elem_size(int dtype) { return dtype == ORC_F32 ? 4 : 2; }
+
+/* ------------------------------------------------------------- the method */
+
+/* freq_i = theta^(-2i/R), the exponent formed in binary64 as -(2i)/R. */
+double oracle_freq(double theta, int64_t rotary_dim, int64_t i) {
+  double expo = -(2.0 * (double)i) / (double)rotary_dim;
+  return pow(theta, expo);
+}
+
+/* Table entries of row `p`, column `i`: cos and sin of p*freq_i, each
+ * rounded once to float32. */
+void oracle_table_entry(double theta, int64_t rotary_dim, int64_t p, int64_t i,
+                        float *c32, float *s32) {
+  double angle = (double)p * oracle_freq(theta, rotary_dim, i);
+  *c32 = (float)cos(angle);
+  *s32 = (float)sin(angle);
+}
+
+/* The whole [rows, R/2] table, row-major (for the table pins). */
+void oracle_table(double theta, int64_t rotary_dim, int64_t rows, float *cos_out,
+                  float *sin_out) {
+  int64_t half = rotary_dim / 2;
+  for (int64_t p = 0; p < rows; ++p)
+    for (int64_t i = 0; i < half; ++i)
+      oracle_table_entry(theta, rotary_dim, p, i, &cos_out[p * half + i],
+                         &sin_out[p * half + i]);
+}
+
+/* Element offset of row (b, h, s) for the two layouts. */
+static int64_t row_offset(int layout, int64_t H, int64_t S, int64_t D, int64_t b,
+                          int64_t h, int64_t s) {
+  if (layout == ORC_BHSD) return ((b * H + h) * S + s) * D; /* [B,H,S,D] */
+  return ((b * S + s) * H + h) * D;                          /* [B,S,H,D] */
+}
+
+/* Dims of pair i inside the rotated prefix of R dims. */
+static void pair_dims(int pairing, int64_t R, int64_t i, int64_t *j1, int64_t *j2) {
+  if (pairing == ORC_SPLIT_HALF) {
+    *j1 = i;
+    *j2 = i + R / 2;
+  } else {
+    *j1 = 2 * i;
+    *j2 = 2 * i + 1;
+  }
+}
+
+/* Position of token (b, s), or -1 if the token is left unrotated. */
+static int64_t token_position(const int32_t *pos, int64_t pos_batch_stride,
+                              int64_t table_rows, int64_t b, int64_t s) {
+  int64_t p = pos ? (int64_t)pos[b * pos_batch_stride + s] : s;
+  if (p < 0 || p >= table_rows) return -1;
+  return p;
+}
+
+static int check_args(int dtype, int layout, int pairing, int direction, int64_t B,
+                      int64_t H, int64_t S, int64_t D, int64_t R, int64_t table_rows,
+                      const int32_t *pos) {
+  if (dtype < ORC_F32 || dtype > ORC_BF16) return -3;
+  if (layout != ORC_BHSD && layout != ORC_BSHD) return -4;
+  if (pairing != ORC_SPLIT_HALF && pairing != ORC_INTERLEAVED) return -4;
+  if (direction != 1 && direction != -1) return -2;
+  if (B < 0 || H < 0 || S < 0 || D < 0 || R < 0 || R > D || (R & 1)) return -2;
+  if (!pos && S > table_rows) return -2;
+  return 0;
+}
+
+/*
+ * Table mode. `x` and `y` hold B*H*S*D elements of `dtype` in `layout`;
+ * y receives the rotated copy of x (they may be the same buffer).
+ * direction +1 = forward, -1 = backward. Returns 0, or a negative code for
+ * arguments it cannot interpret.
+ */
+int oracle_rope(const void *x, void *y, int dtype, int layout, int pairing,
+                int direction, int64_t B, int64_t H, int64_t S, int64_t D, int64_t R,
+                double theta, const int32_t *pos, int64_t pos_batch_stride,
+                int64_t table_rows) {
+  int rc = check_args(dtype, layout, pairing, direction, B, H, S, D, R, table_rows, pos);
+  if (rc) return rc;
+  int64_t es = elem_size(dtype);
+  if (x != y) memcpy(y, x, (size_t)(B * H * S * D * es)); /* untouched lanes */
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t s = 0; s < S; ++s) {
+        int64_t p = token_position(pos, pos_batch_stride, table_rows, b, s);
+        if (p < 0) continue; /* masked token: row stays as it was */
+        int64_t row = row_offset(layout, H, S, D, b, h, s);
+        for (int64_t i = 0; i < R / 2; ++i) {
+          float c32, s32;
+          oracle_table_entry(theta, R, p, i, &c32, &s32);
+          double c = c32, sn = (double)direction * (double)s32;
+          int64_t j1, j2;
+          pair_dims(pairing, R, i, &j1, &j2);
+          double x1 = load_elem(x, row + j1, dtype);
+          double x2 = load_elem(x, row + j2, dtype);
+          double y1 = x1 * c - x2 * sn;
+          double y2 = x1 * sn + x2 * c;
+          store_elem(y, row + j1, dtype, y1);
+          store_elem(y, row + j2, dtype, y2);
+        }
+      }
+  return 0;
+}
+
+/* Exact mode: binary64 in and out, unrounded cos/sin of the binary64 angle. */
+int oracle_rope_exact(const double *x, double *y, int layout, int pairing, int direction,
+                      int64_t B, int64_t H, int64_t S, int64_t D, int64_t R, double theta,
+                      const int32_t *pos, int64_t pos_batch_stride, int64_t table_rows) {
+  int rc = check_args(ORC_F32, layout, pairing, direction, B, H, S, D, R, table_rows, pos);
+  if (rc) return rc;
+  if (x != y) memcpy(y, x, (size_t)(B * H * S * D) * sizeof(double));
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t s = 0; s < S; ++s) {
+        int64_t p = token_position(pos, pos_batch_stride, table_rows, b, s);
+        if (p < 0) continue;
+        int64_t row = row_offset(layout, H, S, D, b, h, s);
+        for (int64_t i = 0; i < R / 2; ++i) {
+          double angle = (double)p * oracle_freq(theta, R, i);
+          double c = cos(angle), sn = (double)direction * sin(angle);
+          int64_t j1, j2;
+          pair_dims(pairing, R, i, &j1, &j2);
+          double x1 = y[row + j1], x2 = y[row + j2];
+          y[row + j1] = x1 * c - x2 * sn;
+          y[row + j2] = x1 * sn + x2 * c;
+        }
+      }
+  return 0;
+}
+
+/* Rounding helpers exposed for the pins on the dtype conversions. */
+uint16_t oracle_to_bf16_bits(double y) { return to_bf16_bits(y); }
+uint16_t oracle_to_f16_bits(double y) { return to_f16_bits(y); }
+double oracle_from_bits(uint32_t bits, int dtype) {
+  if (dtype == ORC_F32) {
+    float v;
+    memcpy(&v, &bits, 4);
+    return v;
+  }
+  uint16_t h = (uint16_t)bits;
+  return load_elem(&h, 0, dtype);
+}
