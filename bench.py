@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of librope's fused Q+K RoPE on one MI355X.
+
+One step = the whole hot path once over one batch of the Llama-style GQA
+prefill workload (bf16, Q [4, 32, 4096, 128], K [4, 8, 4096, 128], split-half
+pairs, fp32 cos/sin tables [4096, 64], theta 10000): the forward rotation of
+Q and K in place, then the backward rotation of the incoming gradients dQ,
+dK in place. Inputs are resident in HBM before timing starts. Each step uses
+the next of several buffer sets, whose total exceeds the 256 MB Infinity
+Cache, so a step does not find its operands in cache from an earlier step.
+
+Printed: one JSON line. `value` is achieved GB/s over the algorithmic bytes
+(read + write of the rotated part of every Q/K row once, each cos/sin row
+once, the indices once). It carries a `roofline` object for the dominant
+kernel (its launch duration measured with HIP events on the launch stream),
+a `cpu_baseline` (the CPU oracle timed on the host) and the decode-shape
+µs/call.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused QK RoPE fwd+bwd achieved HBM GB/s (% of peak); µs/call at decode shape"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "rotary_position_embedding_fwd_amd", "csrc", f)
+                  for f in ("rope_kernels.hpp", "rope_plan.hpp", "librope.hip")]
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_rope_rows_bf16_llama_gqa_prefill.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, pos) -> int:
+    """Bytes the method must move for one call on workload w.
+
+    read + write of the first R dims of every rotated Q and K row, each
+    distinct cos/sin row once (2 tables x R/2 x 4 B), each index once.
+    """
+    import numpy as np
+    e = 4 if w.dtype == "f32" else 2
+    R = w.rotary_dim
+    rows_h = w.n_heads_q + w.n_heads_k
+    if pos is None:
+        n_tok = w.batch * w.seq_len
+        distinct = w.seq_len
+        idx_bytes = 0
+    else:
+        p = pos.numpy().astype(np.int64)
+        bs = w.pos_batch_stride
+        idx = (np.arange(w.batch)[:, None] * bs + np.arange(w.seq_len)[None, :]).ravel()
+        pv = p[idx]
+        valid = (pv >= 0) & (pv < w.table_rows)
+        n_tok = int(valid.sum())
+        distinct = int(np.unique(pv[valid]).size)
+        idx_bytes = 4 * int(np.unique(idx).size)
+    rotated = e * R * n_tok * rows_h
+    return 2 * rotated + 4 * R * distinct + idx_bytes
+
+
+def device_inputs(w, sets: int, which=("q", "k", "dq", "dk")):
+    import torch
+    import workloads as W
+    t = W.tensors(w, which)
+    out = []
+    for i in range(sets):
+        out.append({k: v.to("cuda") for k, v in t.items()})
+    return t, out
+
+
+def time_prefill(w, steps: int, warmup: int, sets: int):
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    pos = W.positions(w)
+    cos, sin = rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
+    cos, sin = cos.cuda(), sin.cuda()
+    host, bufs = device_inputs(w, sets)
+    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim,
+              pos=None if pos is None else pos.cuda())
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        b = bufs[i % sets]
+        if ev is not None:
+            ev[0].record(stream)
+        rp.rope_fwd_qk(b["q"], b["k"], cos, sin, stream=stream, **kw)
+        if ev is not None:
+            ev[1].record(stream)
+        rp.rope_bwd_qk(b["dq"], b["dk"], cos, sin, stream=stream, **kw)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    return dict(total_ms=total_ms, wall_s=wall, fwd_ms=fwd_ms, bwd_ms=bwd_ms, pos=pos,
+                host=host)
+
+
+def time_decode(calls: int = 2000, warmup: int = 50):
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    w = W.DECODE
+    pos = W.positions(w).cuda()
+    cos, sin = rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
+    cos, sin = cos.cuda(), sin.cuda()
+    t = W.tensors(w)
+    q, k = t["q"].cuda(), t["k"].cuda()
+    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, pos=pos)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        rp.rope_fwd_qk(q, k, cos, sin, stream=stream, **kw)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(calls):
+        rp.rope_fwd_qk(q, k, cos, sin, stream=stream, **kw)
+    b.record(stream)
+    torch.cuda.synchronize()
+    per_call_us = a.elapsed_time(b) * 1000.0 / calls
+    # kernel-only duration: events around single launches
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(200)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        rp.rope_fwd_qk(q, k, cos, sin, stream=stream, **kw)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    kern = sorted(e0.elapsed_time(e1) * 1000.0 for e0, e1 in evs)
+    nbytes = algorithmic_bytes(w, pos.cpu())
+    return {"workload": w.name, "us_per_call_back_to_back": round(per_call_us, 3),
+            "us_kernel_event_median": round(kern[len(kern) // 2], 3),
+            "algorithmic_bytes": nbytes, "calls": calls}
+
+
+def cpu_baseline(w, host, pos):
+    """The CPU oracle, as it stands, on one full step (fwd + bwd) of w, 1 thread."""
+    import oracle
+    orc = oracle
+    orc.load()
+    nbytes = 2 * algorithmic_bytes(w, pos)
+    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, theta=w.theta,
+              pos=None if pos is None else pos.numpy(), pos_batch_stride=w.pos_batch_stride,
+              table_rows=w.table_rows)
+    arrs = {k: orc.torch_to_storage(v) for k, v in host.items()}
+    t0 = time.perf_counter()
+    orc.rope(arrs["q"], w.dtype, direction=1, **kw)
+    orc.rope(arrs["k"], w.dtype, direction=1, **kw)
+    orc.rope(arrs["dq"], w.dtype, direction=-1, **kw)
+    orc.rope(arrs["dk"], w.dtype, direction=-1, **kw)
+    dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"one full step (fwd of Q,K + bwd of dQ,dK) of {w.name}, "
+                      f"single-threaded scalar binary64 oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model}
+
+
+def stored_traffic():
+    """HBM traffic per launch from the committed rocprofv3 counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
+    """A plain device copy of known size, for scaling the FETCH/WRITE counters."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out: str = TRAFFIC_FILE):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
+    `bench.py --copy-calibration` into per-launch traffic of the forward
+    prefill kernel, scaled by the counters of the 1 GiB copy."""
+    import csv
+    import workloads as W
+
+    def read(d, counter):
+        rows = []
+        for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(p) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    def pick(rows, pred):
+        vals = [v for n, v in rows if pred(n)]
+        return sum(vals) / len(vals) if vals else None
+
+    is_fwd = lambda n: "rope_rows_kernel" in n and "bf16" in n.replace("DF16b", "bf16")  # noqa
+    is_copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()  # noqa
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    f_k, w_k = pick(fetch, is_fwd), pick(write, is_fwd)
+    f_c, w_c = pick(fetch, is_copy), pick(write, is_copy)
+    copy_bytes = 1 << 30
+    res = {"kernel": "rope_rows_kernel<__bf16, 8, split-half> (forward and backward launches)",
+           "workload": W.LLAMA_GQA_PREFILL.name,
+           "fetch_kib_per_launch": f_k, "write_kib_per_launch": w_k,
+           "copy_fetch_kib": f_c, "copy_write_kib": w_c}
+    if None not in (f_k, w_k, f_c, w_c):
+        rf, rw = copy_bytes / (f_c * 1024), copy_bytes / (w_c * 1024)
+        res.update({"fetch_scale": rf, "write_scale": rw,
+                    "bytes_per_launch": round(f_k * 1024 * rf + w_k * 1024 * rw),
+                    "algorithmic_bytes_per_launch":
+                        algorithmic_bytes(W.LLAMA_GQA_PREFILL, None)})
+    res["kernel_source_hash"] = kernel_source_hash()
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=3,
+                    help="buffer sets cycled through (3 x 320 MiB > the 256 MB Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the RoPE path has no cross-GPU step, "
+              "and this build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import rotary_position_embedding_fwd_amd as rp
+    rp.lib()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w = W.LLAMA_GQA_PREFILL
+    r = time_prefill(w, args.steps, args.warmup, args.sets)
+    per_call = algorithmic_bytes(w, r["pos"])
+    step_bytes = 2 * per_call
+    total_s = r["total_ms"] / 1000.0
+    gbs = args.steps * step_bytes / total_s / 1e9
+    fwd = sorted(r["fwd_ms"])
+    bwd = sorted(r["bwd_ms"])
+    fwd_avg_ms = sum(fwd) / len(fwd)
+    achieved = per_call / (fwd_avg_ms / 1000.0) / 1e9
+    traffic = stored_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["total_ms"] / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "q_shape": list(w.q_shape), "k_shape": list(w.k_shape),
+                   "storage_dtype": w.dtype, "layout": w.layout, "pairing": w.pairing,
+                   "rotary_dim": w.rotary_dim, "table": [w.table_rows, w.rotary_dim // 2],
+                   "theta": w.theta, "step": "rope_fwd_qk(Q,K) + rope_bwd_qk(dQ,dK), in place",
+                   "buffer_sets": args.sets,
+                   "algorithmic_bytes_per_call": per_call},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "rope_rows_kernel<__bf16, 8, split-half> forward",
+                     "avg_launch_us": round(fwd_avg_ms * 1000.0, 3),
+                     "median_launch_us": round(fwd[len(fwd) // 2] * 1000.0, 3),
+                     "bwd_avg_launch_us": round(sum(bwd) / len(bwd) * 1000.0, 3)},
+        "wall_s_timed": round(r["wall_s"], 4),
+    }
+    if not args.no_decode:
+        out["decode"] = time_decode()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, r["host"], r["pos"])
+    if args.copy_calibration:
+        copy_calibration()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * librope.h -- fused rotary position embedding (RoPE) for AMD MI355X (gfx950).
+ *
+ * C ABI. Every entry point validates its arguments on the host, then enqueues
+ * GPU work on the caller's HIP stream and returns; nothing here waits for the
+ * GPU, allocates device memory or falls back to another implementation.
+ *
+ * What is computed. For each token (b, s) at position p and each pair
+ * (x1, x2) of the first R dims of every head row,
+ *
+ *     forward : (x1, x2) <- (x1*cos[p,i] - x2*sin[p,i], x1*sin[p,i] + x2*cos[p,i])
+ *     backward: (x1, x2) <- (x1*cos[p,i] + x2*sin[p,i], -x1*sin[p,i] + x2*cos[p,i])
+ *
+ * ("Rotary Embedding Kernel", Overview: the pair rotation, applied per
+ * position along the sequence. How Unsloth Optimizes RoPE Embedding
+ * Computations in Triton Kernels, Frequently Asked Questions: the backward
+ * pass is the forward kernel under a flag; for a rotation that is the
+ * transpose, i.e. sin negated.) Arithmetic is float32 for every storage
+ * dtype; each result is rounded once to the storage dtype, nearest-even.
+ *
+ * Pairs ("Rotary Embedding Kernel", Paired Element Layout):
+ *     ROPE_SPLIT_HALF  : (x[i], x[i + R/2]),  i < R/2
+ *     ROPE_INTERLEAVED : (x[2i], x[2i + 1]),  i < R/2
+ * Dims R .. D-1 are never read or written (rotary-embedding-torch docs, Key
+ * Parameters: `dim` is the width of the rotated part).
+ *
+ * Positions (How Unsloth Optimizes RoPE ..., Support for Custom Position IDs
+ * and Custom Position IDs for Prefix-Tuning; rotary-embedding-torch docs,
+ * flash_attn_with_rotary, skipping CLS/register tokens):
+ *     pos == NULL : p = s
+ *     pos != NULL : p = pos[b * pos_batch_stride + s]
+ * A token whose p is < 0 or >= table_rows is left untouched (every dim keeps
+ * its bits); that is how leading CLS/register tokens are skipped.
+ *
+ * Layouts:
+ *     ROPE_BHSD : Q [batch, n_heads_q, seq_len, head_dim], K [batch, n_heads_k, ...]
+ *                 (Unsloth page, Usage Examples)
+ *     ROPE_BSHD : Q [batch, seq_len, n_heads_q, head_dim] (rotary-embedding-torch
+ *                 docs, seq_before_head_dim)
+ * Both dense and contiguous. GQA: 1 <= n_heads_k <= n_heads_q (Unsloth page,
+ * Manual Triton Kernel Invocation, separate n_heads_K).
+ *
+ * Tables (How Unsloth Optimizes RoPE ..., Usage Examples: precomputed cos and
+ * sin; "Rotary Embedding Kernel", Common Pitfalls: [seq_len, D/2], broadcast
+ * over batch and heads): cos and sin are float32, row-major
+ * [table_rows, R/2]; row p holds the values of position p. rope_build_table
+ * fills them for the standard frequencies.
+ *
+ * Ownership and lifetime. Every pointer in a call is caller-owned. q, k, cos,
+ * sin and pos are device memory on the current HIP device and must stay valid
+ * until the enqueued work completes. q and k are modified in place and must
+ * not overlap each other. The library keeps no mutable global state beyond a
+ * per-device cache of the compute-unit count, filled once; calls are
+ * reentrant and may be issued from several threads on different streams.
+ *
+ * Errors. A negative rope_status_t means nothing was enqueued (validation
+ * errors), or that the launch itself failed (ROPE_ERR_HIP, reported by
+ * hipGetLastError right after the launch). Index values are device data and
+ * are not inspected on the host: an out-of-range index is not an error, the
+ * token simply passes through.
+ */
+#ifndef LIBROPE_H
+#define LIBROPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rope_status {
+  ROPE_OK = 0,
+  ROPE_ERR_NULL = -1,   /* a required pointer is NULL */
+  ROPE_ERR_SHAPE = -2,  /* a size is negative or inconsistent */
+  ROPE_ERR_DTYPE = -3,  /* unknown dtype code */
+  ROPE_ERR_LAYOUT = -4, /* unknown layout, pairing or launch-shape code */
+  ROPE_ERR_ALIGN = -5,  /* a pointer is not aligned to its element size */
+  ROPE_ERR_ALIAS = -6,  /* the q and k byte ranges overlap */
+  ROPE_ERR_HIP = -7     /* the HIP runtime reported an error */
+} rope_status_t;
+
+typedef enum rope_dtype { ROPE_F32 = 0, ROPE_F16 = 1, ROPE_BF16 = 2 } rope_dtype_t;
+typedef enum rope_layout { ROPE_BHSD = 0, ROPE_BSHD = 1 } rope_layout_t;
+typedef enum rope_pairing { ROPE_SPLIT_HALF = 0, ROPE_INTERLEAVED = 1 } rope_pairing_t;
+
+/* Which grid shape to launch. AUTO picks by size: one token per workgroup
+ * (lanes over heads) when there are few tokens, as at decode (seq_len 1);
+ * otherwise token rows across lanes with a loop over heads. The two shapes
+ * run the same per-pair arithmetic and give bit-identical results. */
+typedef enum rope_launch {
+  ROPE_LAUNCH_AUTO = 0,
+  ROPE_LAUNCH_ROWS = 1,  /* lanes over (token, chunk), loop over heads */
+  ROPE_LAUNCH_TOKEN = 2  /* one token per workgroup, lanes over (head, chunk) */
+} rope_launch_t;
+
+typedef struct rope_desc {
+  int64_t batch;       /* B >= 0 */
+  int64_t n_heads_q;   /* Hq >= 0 */
+  int64_t n_heads_k;   /* Hk, 1 <= Hk <= Hq for the _qk calls; ignored by the _q calls */
+  int64_t seq_len;     /* S >= 0 */
+  int64_t head_dim;    /* D >= 0 */
+  int64_t rotary_dim;  /* R, even, 0 <= R <= D */
+  int32_t dtype;       /* rope_dtype_t: storage type of q and k */
+  int32_t layout;      /* rope_layout_t */
+  int32_t pairing;     /* rope_pairing_t */
+  int32_t launch;      /* rope_launch_t; 0 = automatic */
+  const float *cos;    /* device, float32 [table_rows, R/2], 4-byte aligned */
+  const float *sin;    /* device, float32 [table_rows, R/2], 4-byte aligned */
+  int64_t table_rows;  /* rows of cos and sin (the largest position + 1) */
+  const int32_t *pos;  /* device int32 indices, or NULL for p = s */
+  int64_t pos_batch_stride; /* index of token (b, s) is pos[b * stride + s]; 0 shares one row */
+} rope_desc_t;
+
+/* Forward RoPE on Q and K in one launch, in place.
+ * q: device, d->dtype elements in d->layout, shape with n_heads_q heads.
+ * k: device, same with n_heads_k heads; must not overlap q.
+ * stream: a hipStream_t, or NULL for the null stream.
+ * Returns ROPE_OK, a validation error (nothing enqueued) or ROPE_ERR_HIP.
+ * Empty work (batch, seq_len, all heads or rotary_dim zero) returns ROPE_OK
+ * and enqueues nothing. */
+rope_status_t rope_fwd_qk(void *q, void *k, const rope_desc_t *d, void *stream);
+
+/* Backward of rope_fwd_qk: rotates incoming gradients dq, dk in place by the
+ * opposite angle (How Unsloth Optimizes RoPE ..., Frequently Asked Questions:
+ * the backward pass runs the same kernel with its backward flag set). Same
+ * arguments and errors as rope_fwd_qk. */
+rope_status_t rope_bwd_qk(void *dq, void *dk, const rope_desc_t *d, void *stream);
+
+/* Forward RoPE on Q only (How Unsloth Optimizes RoPE ..., Triton Kernel
+ * Architecture for RoPE: the query-only kernel). d->n_heads_k is ignored. */
+rope_status_t rope_fwd_q(void *q, const rope_desc_t *d, void *stream);
+
+/* Backward of rope_fwd_q. */
+rope_status_t rope_bwd_q(void *dq, const rope_desc_t *d, void *stream);
+
+/* Fill host float32 tables cos_out/sin_out, each [table_rows, R/2] row-major,
+ * with cos and sin of p * theta^(-2i/R) for row p and column i: the exponent
+ * -2i/R and the angle are formed in binary64 and each entry is rounded once
+ * to float32 (rotary-embedding-torch docs, Key Parameters: `theta` is the base
+ * of the frequencies, default 10000; "Rotary Embedding Kernel": cos/sin are
+ * precomputed). Host memory, caller-owned; runs on the calling thread.
+ * Returns ROPE_ERR_NULL for NULL outputs with non-empty work and
+ * ROPE_ERR_SHAPE for a negative size, an odd rotary_dim or theta <= 0. */
+rope_status_t rope_build_table(float *cos_out, float *sin_out, int64_t table_rows,
+                               int64_t rotary_dim, double theta);
+
+/* A static, human-readable name for a status code ("unknown status" for
+ * codes this library never returns). */
+const char *rope_status_string(rope_status_t s);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int rope_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBROPE_H */

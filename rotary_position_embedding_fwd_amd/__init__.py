@@ -1,0 +1,214 @@
+"""Python binding of librope (fused RoPE for MI355X): argument marshalling only.
+
+Each function below has the name of a C entry point in include/librope.h,
+builds its rope_desc_t from torch tensors (shapes, dtype, data pointers and
+the current HIP stream) and calls it. No arithmetic of the method happens
+here, and there is no fallback: if librope.so is not built, or a call is
+rejected, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "librope.so")
+
+ROPE_OK = 0
+STATUS_NAMES = {0: "ROPE_OK", -1: "ROPE_ERR_NULL", -2: "ROPE_ERR_SHAPE",
+                -3: "ROPE_ERR_DTYPE", -4: "ROPE_ERR_LAYOUT", -5: "ROPE_ERR_ALIGN",
+                -6: "ROPE_ERR_ALIAS", -7: "ROPE_ERR_HIP"}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+LAYOUTS = {"bhsd": 0, "bshd": 1}
+PAIRINGS = {"split_half": 0, "interleaved": 1}
+LAUNCHES = {"auto": 0, "rows": 1, "token": 2}
+
+
+class RopeDesc(ctypes.Structure):
+    """rope_desc_t of include/librope.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("n_heads_q", ctypes.c_int64),
+        ("n_heads_k", ctypes.c_int64),
+        ("seq_len", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("rotary_dim", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("pairing", ctypes.c_int32),
+        ("launch", ctypes.c_int32),
+        ("cos", ctypes.c_void_p),
+        ("sin", ctypes.c_void_p),
+        ("table_rows", ctypes.c_int64),
+        ("pos", ctypes.c_void_p),
+        ("pos_batch_stride", ctypes.c_int64),
+    ]
+
+
+class RopeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} "
+                         f"({status_string(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded librope.so with argument types set. Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"librope.so is not built ({LIB_PATH}); run "
+                              "`python -m rotary_position_embedding_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, D = ctypes.c_void_p, ctypes.POINTER(RopeDesc)
+        for name in ("rope_fwd_qk", "rope_bwd_qk"):
+            getattr(L, name).argtypes = [P, P, D, P]
+            getattr(L, name).restype = ctypes.c_int
+        for name in ("rope_fwd_q", "rope_bwd_q"):
+            getattr(L, name).argtypes = [P, D, P]
+            getattr(L, name).restype = ctypes.c_int
+        L.rope_build_table.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double]
+        L.rope_build_table.restype = ctypes.c_int
+        L.rope_status_string.argtypes = [ctypes.c_int]
+        L.rope_status_string.restype = ctypes.c_char_p
+        L.rope_version.argtypes = []
+        L.rope_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().rope_status_string(status).decode()
+
+
+def rope_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def rope_version() -> int:
+    return int(lib().rope_version())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _dims(t, layout: str):
+    if t.dim() != 4:
+        raise ValueError("q/k must be 4-d")
+    if layout == "bhsd":
+        B, H, S, D = t.shape
+    else:
+        B, S, H, D = t.shape
+    return B, H, S, D
+
+
+def make_desc(q, k, cos, sin, *, layout: str = "bhsd", pairing: str = "split_half",
+              rotary_dim: Optional[int] = None, pos=None,
+              pos_batch_stride: Optional[int] = None, launch: str = "auto") -> RopeDesc:
+    """rope_desc_t for torch tensors q (and k, or None) and device tables cos/sin."""
+    B, Hq, S, D = _dims(q, layout)
+    Hk = 0
+    if k is not None:
+        Bk, Hk, Sk, Dk = _dims(k, layout)
+        if (Bk, Sk, Dk) != (B, S, D) or k.dtype != q.dtype:
+            raise ValueError("k must match q in batch, seq_len, head_dim and dtype")
+    for name, t in (("q", q), ("k", k)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (it is rotated in place)")
+    R = D if rotary_dim is None else int(rotary_dim)
+    if cos.dtype != sin.dtype or cos.shape != sin.shape or cos.dim() != 2:
+        raise ValueError("cos and sin must be matching 2-d float32 tables")
+    import torch
+    if cos.dtype != torch.float32 or not cos.is_contiguous() or not sin.is_contiguous():
+        raise ValueError("cos and sin must be contiguous float32 [table_rows, R/2]")
+    if cos.shape[1] != R // 2:
+        raise ValueError(f"tables have {cos.shape[1]} columns, expected R/2 = {R // 2}")
+    d = RopeDesc()
+    d.batch, d.n_heads_q, d.n_heads_k, d.seq_len, d.head_dim = B, Hq, Hk, S, D
+    d.rotary_dim = R
+    d.dtype = _dtype_code(q)
+    d.layout = LAYOUTS[layout]
+    d.pairing = PAIRINGS[pairing]
+    d.launch = LAUNCHES[launch]
+    d.cos, d.sin = cos.data_ptr(), sin.data_ptr()
+    d.table_rows = cos.shape[0]
+    if pos is not None:
+        if pos.dtype != torch.int32 or not pos.is_contiguous():
+            raise ValueError("pos must be a contiguous int32 tensor")
+        if pos_batch_stride is None:
+            if pos.dim() == 2:
+                pos_batch_stride = pos.stride(0)
+            elif pos.numel() == S:
+                pos_batch_stride = 0
+            elif pos.numel() == B * S:
+                pos_batch_stride = S
+            else:
+                raise ValueError("pos must hold seq_len or batch*seq_len indices")
+        need = (B - 1) * pos_batch_stride + S if B > 0 and S > 0 else 0
+        if pos.numel() < need:
+            raise ValueError(f"pos holds {pos.numel()} indices, needs {need}")
+        d.pos = pos.data_ptr()
+        d.pos_batch_stride = pos_batch_stride
+    return d
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != ROPE_OK:
+        raise RopeError(status, where)
+
+
+def rope_fwd_qk(q, k, cos, sin, *, stream=None, **kw):
+    """Forward RoPE on q and k in place (one launch). See make_desc for options."""
+    d = make_desc(q, k, cos, sin, **kw)
+    _check(lib().rope_fwd_qk(q.data_ptr(), k.data_ptr(), ctypes.byref(d), _stream(stream)),
+           "rope_fwd_qk")
+    return q, k
+
+
+def rope_bwd_qk(dq, dk, cos, sin, *, stream=None, **kw):
+    """Backward RoPE on gradients dq and dk in place."""
+    d = make_desc(dq, dk, cos, sin, **kw)
+    _check(lib().rope_bwd_qk(dq.data_ptr(), dk.data_ptr(), ctypes.byref(d), _stream(stream)),
+           "rope_bwd_qk")
+    return dq, dk
+
+
+def rope_fwd_q(q, cos, sin, *, stream=None, **kw):
+    """Forward RoPE on q only, in place."""
+    d = make_desc(q, None, cos, sin, **kw)
+    _check(lib().rope_fwd_q(q.data_ptr(), ctypes.byref(d), _stream(stream)), "rope_fwd_q")
+    return q
+
+
+def rope_bwd_q(dq, cos, sin, *, stream=None, **kw):
+    """Backward RoPE on dq only, in place."""
+    d = make_desc(dq, None, cos, sin, **kw)
+    _check(lib().rope_bwd_q(dq.data_ptr(), ctypes.byref(d), _stream(stream)), "rope_bwd_q")
+    return dq
+
+
+def rope_build_table(table_rows: int, rotary_dim: int, theta: float = 10000.0):
+    """Host float32 cos/sin tables [table_rows, R/2] (CPU torch tensors)."""
+    import torch
+    half = rotary_dim // 2
+    cos = torch.empty((table_rows, half), dtype=torch.float32)
+    sin = torch.empty((table_rows, half), dtype=torch.float32)
+    _check(lib().rope_build_table(cos.data_ptr(), sin.data_ptr(), table_rows, rotary_dim,
+                                  float(theta)), "rope_build_table")
+    return cos, sin

@@ -1,0 +1,121 @@
+// librope.hip -- host side of the librope C ABI (declared in include/librope.h).
+//
+// Each entry point validates its descriptor without touching the GPU, picks
+// the access width and grid shape, and enqueues one kernel on the caller's
+// stream. Nothing here allocates device memory or waits for the GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "librope.h"
+#include "rope_kernels.hpp"
+#include "rope_plan.hpp"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kMaxDevices = 64;
+
+// Compute units per device, read once per device.
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Enqueues the planned kernel variant on a stream.
+struct GpuLauncher {
+  const rope::Plan& pl;
+  hipStream_t st;
+
+  template <typename T, int V, int PAIR, bool AL>
+  hipError_t run() {
+    const dim3 grid((unsigned)pl.grid), block((unsigned)pl.block);
+    if (pl.token)
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL>), grid, block, 0, st, pl.a);
+    else
+      hipLaunchKernelGGL((rope::rope_rows_kernel<T, V, PAIR, AL, 4>), grid, block, 0, st, pl.a);
+    return hipGetLastError();
+  }
+};
+
+rope_status_t run(void* q, void* k, const rope_desc_t* d, void* stream, bool with_k,
+                  float sin_sign) {
+  // validation first: it needs no device and touches no device memory
+  const rope_status_t vs = rope::validate(q, k, d, with_k);
+  if (vs != ROPE_OK) return vs;
+  if (rope::is_empty(d, with_k ? d->n_heads_k : 0)) return ROPE_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ROPE_ERR_HIP;
+  rope::Plan pl;
+  const rope_status_t ps = rope::make_plan(q, k, d, with_k, sin_sign, cu_count(dev), &pl);
+  if (ps != ROPE_OK || pl.empty) return ps;
+  GpuLauncher launcher{pl, static_cast<hipStream_t>(stream)};
+  return rope::dispatch(pl, launcher) == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+rope_status_t rope_fwd_qk(void* q, void* k, const rope_desc_t* d, void* stream) {
+  return run(q, k, d, stream, true, 1.0f);
+}
+
+rope_status_t rope_bwd_qk(void* dq, void* dk, const rope_desc_t* d, void* stream) {
+  return run(dq, dk, d, stream, true, -1.0f);
+}
+
+rope_status_t rope_fwd_q(void* q, const rope_desc_t* d, void* stream) {
+  return run(q, nullptr, d, stream, false, 1.0f);
+}
+
+rope_status_t rope_bwd_q(void* dq, const rope_desc_t* d, void* stream) {
+  return run(dq, nullptr, d, stream, false, -1.0f);
+}
+
+rope_status_t rope_build_table(float* cos_out, float* sin_out, int64_t table_rows,
+                               int64_t rotary_dim, double theta) {
+  if (table_rows < 0 || rotary_dim < 0 || (rotary_dim & 1) || !(theta > 0.0))
+    return ROPE_ERR_SHAPE;
+  const int64_t half = rotary_dim / 2;
+  if (table_rows == 0 || half == 0) return ROPE_OK;
+  if (!cos_out || !sin_out) return ROPE_ERR_NULL;
+  for (int64_t i = 0; i < half; ++i) {
+    // theta^(-2i/R), exponent and power in binary64
+    const double inv_freq = std::pow(theta, -(2.0 * (double)i) / (double)rotary_dim);
+    for (int64_t p = 0; p < table_rows; ++p) {
+      const double angle = (double)p * inv_freq;
+      cos_out[p * half + i] = (float)std::cos(angle);
+      sin_out[p * half + i] = (float)std::sin(angle);
+    }
+  }
+  return ROPE_OK;
+}
+
+const char* rope_status_string(rope_status_t s) {
+  switch (s) {
+    case ROPE_OK: return "ok";
+    case ROPE_ERR_NULL: return "a required pointer is NULL";
+    case ROPE_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case ROPE_ERR_DTYPE: return "unknown dtype";
+    case ROPE_ERR_LAYOUT: return "unknown layout, pairing or launch shape";
+    case ROPE_ERR_ALIGN: return "misaligned pointer";
+    case ROPE_ERR_ALIAS: return "q and k overlap";
+    case ROPE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int rope_version(void) { return kVersion; }
+
+}  // extern "C"

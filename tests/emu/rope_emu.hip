@@ -1,0 +1,138 @@
+// rope_emu.hip -- test harness: runs librope's kernel bodies on the host.
+//
+// Built for the host only (no device code is executed) and with
+// AddressSanitizer, it plans a call exactly as librope does, then runs every
+// workgroup and every lane of the planned grid one after another on host
+// buffers allocated to their exact sizes, so any out-of-bounds access of the
+// kernel index arithmetic is reported by the sanitizer. The Python tests
+// compare its outputs with the CPU oracle.
+//
+// usage: rope_emu JOB_DIR
+//   JOB_DIR/desc.txt : "key value" lines (see read_job)
+//   JOB_DIR/{q,k,cos,sin,pos}.bin : raw inputs (pos/k only when used)
+// writes JOB_DIR/{q_out,k_out}.bin and prints the plan on stdout.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "librope.h"
+#include "rope_kernels.hpp"
+#include "rope_plan.hpp"
+
+namespace {
+
+std::map<std::string, long long> read_job(const std::string& dir) {
+  std::map<std::string, long long> kv;
+  FILE* f = fopen((dir + "/desc.txt").c_str(), "r");
+  if (!f) {
+    perror("desc.txt");
+    exit(2);
+  }
+  char key[64];
+  long long val;
+  while (fscanf(f, "%63s %lld", key, &val) == 2) kv[key] = val;
+  fclose(f);
+  return kv;
+}
+
+// Exactly `bytes` long (the sanitizer guards both ends), 16-byte aligned.
+void* exact_alloc(size_t bytes) {
+  void* p = nullptr;
+  if (posix_memalign(&p, 16, bytes ? bytes : 1)) exit(3);
+  return p;
+}
+
+void* read_file(const std::string& path, size_t bytes, size_t offset_bytes) {
+  char* base = static_cast<char*>(exact_alloc(offset_bytes + bytes));
+  FILE* f = fopen(path.c_str(), "rb");
+  if (!f) {
+    perror(path.c_str());
+    exit(2);
+  }
+  if (bytes && fread(base + offset_bytes, 1, bytes, f) != bytes) {
+    fprintf(stderr, "short read %s\n", path.c_str());
+    exit(2);
+  }
+  fclose(f);
+  return base + offset_bytes;
+}
+
+void write_file(const std::string& path, const void* p, size_t bytes) {
+  FILE* f = fopen(path.c_str(), "wb");
+  if (!f || fwrite(p, 1, bytes, f) != bytes) exit(4);
+  fclose(f);
+}
+
+struct HostRunner {
+  const rope::Plan& pl;
+
+  template <typename T, int V, int PAIR, bool AL>
+  int run() {
+    for (int64_t blk = 0; blk < pl.grid; ++blk)
+      for (int t = 0; t < pl.block; ++t) {
+        if (pl.token)
+          rope::token_body<T, V, PAIR, AL>(pl.a, blk, pl.grid, t, pl.block);
+        else
+          rope::rows_body<T, V, PAIR, AL, 4>(pl.a, blk, t);
+      }
+    return 0;
+  }
+};
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc != 2) {
+    fprintf(stderr, "usage: rope_emu JOB_DIR\n");
+    return 2;
+  }
+  const std::string dir = argv[1];
+  auto kv = read_job(dir);
+  rope_desc_t d{};
+  d.batch = kv["batch"];
+  d.n_heads_q = kv["n_heads_q"];
+  d.n_heads_k = kv["n_heads_k"];
+  d.seq_len = kv["seq_len"];
+  d.head_dim = kv["head_dim"];
+  d.rotary_dim = kv["rotary_dim"];
+  d.dtype = (int32_t)kv["dtype"];
+  d.layout = (int32_t)kv["layout"];
+  d.pairing = (int32_t)kv["pairing"];
+  d.launch = (int32_t)kv["launch"];
+  d.table_rows = kv["table_rows"];
+  d.pos_batch_stride = kv["pos_batch_stride"];
+  const bool with_k = kv["with_k"] != 0;
+  const float sign = kv["direction"] < 0 ? -1.0f : 1.0f;
+  const int cus = kv.count("cus") ? (int)kv["cus"] : 256;
+  const size_t e = d.dtype == ROPE_F32 ? 4 : 2;
+  const size_t row = (size_t)(d.batch * d.seq_len * d.head_dim);
+  const size_t qb = row * d.n_heads_q * e, kb = with_k ? row * d.n_heads_k * e : 0;
+  const size_t tb = (size_t)(d.table_rows * (d.rotary_dim / 2)) * 4;
+
+  void* q = read_file(dir + "/q.bin", qb, (size_t)kv["q_offset"] * e);
+  void* k = with_k ? read_file(dir + "/k.bin", kb, (size_t)kv["k_offset"] * e) : nullptr;
+  d.cos = static_cast<const float*>(read_file(dir + "/cos.bin", tb, 0));
+  d.sin = static_cast<const float*>(read_file(dir + "/sin.bin", tb, 0));
+  if (kv["pos_count"] > 0)
+    d.pos = static_cast<const int32_t*>(
+        read_file(dir + "/pos.bin", (size_t)kv["pos_count"] * 4, 0));
+
+  rope::Plan pl;
+  const rope_status_t st = rope::make_plan(q, k, &d, with_k, sign, cus, &pl);
+  printf("status %d\n", (int)st);
+  if (st != ROPE_OK) return 0;
+  printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
+         "heads_per_group %d\nn_groups %d\n",
+         (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
+         pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups);
+  if (!pl.empty) {
+    HostRunner runner{pl};
+    rope::dispatch(pl, runner);
+  }
+  write_file(dir + "/q_out.bin", q, qb);
+  if (with_k) write_file(dir + "/k_out.bin", k, kb);
+  return 0;
+}

@@ -1,0 +1,181 @@
+"""The librope C ABI on the CPU: exports, validation, tables, status strings.
+
+No test here launches GPU work. Validation runs before any HIP call and never
+dereferences a device pointer, so the descriptors below use fake addresses.
+The one call with valid arguments runs only where no GPU is visible, where it
+must fail with ROPE_ERR_HIP instead of crashing.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import rotary_position_embedding_fwd_amd as rp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "librope.h")
+
+OK, NULL, SHAPE, DTYPE, LAYOUT, ALIGN, ALIAS, HIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[a-z_][a-z_0-9 ]*?[ *](rope_[a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    assert {"rope_fwd_qk", "rope_bwd_qk", "rope_fwd_q", "rope_bwd_q", "rope_build_table",
+            "rope_status_string", "rope_version"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    L = rp.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", rp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (rope_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+    # the C ABI exports no C++ (mangled) names of its own
+    assert not re.search(r" T _ZN4rope", out)
+
+
+def test_desc_layout_matches_header():
+    assert ctypes.sizeof(rp.RopeDesc) == 6 * 8 + 4 * 4 + 8 + 8 + 8 + 8 + 8
+    assert rp.RopeDesc.cos.offset == 64 and rp.RopeDesc.pos_batch_stride.offset == 96
+
+
+def test_version_and_status_strings():
+    assert rp.rope_version() >= 10000
+    for code in (OK, NULL, SHAPE, DTYPE, LAYOUT, ALIGN, ALIAS, HIP):
+        assert rp.status_string(code) and rp.status_string(code) != "unknown status"
+    assert rp.status_string(-99) == "unknown status"
+
+
+A16 = 1 << 20  # a fake, 16-byte aligned device address (never dereferenced)
+
+
+def good_desc(**kw):
+    d = rp.RopeDesc()
+    d.batch, d.n_heads_q, d.n_heads_k, d.seq_len, d.head_dim, d.rotary_dim = 2, 4, 2, 8, 64, 64
+    d.dtype, d.layout, d.pairing, d.launch = 2, 0, 0, 0
+    d.cos, d.sin, d.table_rows = A16 * 64, A16 * 65, 8
+    d.pos, d.pos_batch_stride = None, 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def call_qk(d, q=A16, k=A16 * 16, fn="rope_fwd_qk"):
+    return getattr(rp.lib(), fn)(q, k, ctypes.byref(d) if d is not None else None, None)
+
+
+@pytest.mark.parametrize("fn", ["rope_fwd_qk", "rope_bwd_qk"])
+@pytest.mark.parametrize("change,expected", [
+    (dict(dtype=3), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(layout=2), LAYOUT), (dict(pairing=2), LAYOUT), (dict(launch=3), LAYOUT),
+    (dict(rotary_dim=63), SHAPE), (dict(rotary_dim=66), SHAPE),
+    (dict(n_heads_k=5), SHAPE), (dict(batch=-1), SHAPE), (dict(seq_len=-2), SHAPE),
+    (dict(head_dim=-64), SHAPE), (dict(table_rows=7), SHAPE), (dict(n_heads_k=-1), SHAPE),
+    (dict(cos=None), NULL), (dict(sin=None), NULL),
+    (dict(cos=A16 * 64 + 4), ALIGN), (dict(sin=A16 * 65 + 8), ALIGN),
+    (dict(pos=A16 * 70 + 2, table_rows=4), ALIGN),
+    (dict(pos=A16 * 70, pos_batch_stride=-1), SHAPE),
+])
+def test_validation_errors(fn, change, expected):
+    assert call_qk(good_desc(**change), fn=fn) == expected
+
+
+def test_null_and_alias_and_alignment():
+    assert call_qk(None) == NULL
+    assert call_qk(good_desc(), q=None) == NULL
+    assert call_qk(good_desc(), k=None) == NULL
+    assert call_qk(good_desc(), q=A16 + 1) == ALIGN  # bf16 needs 2-byte alignment
+    assert call_qk(good_desc(dtype=0), k=A16 * 16 + 2) == ALIGN  # f32 needs 4
+    q_bytes = 2 * 4 * 8 * 64 * 2
+    assert call_qk(good_desc(), q=A16, k=A16 + q_bytes - 2) == ALIAS
+    k_bytes = 2 * 2 * 8 * 64 * 2
+    assert call_qk(good_desc(), q=A16, k=A16 - k_bytes + 16) == ALIAS  # k ends inside q
+    assert call_qk(good_desc(), q=A16, k=A16 + q_bytes) != ALIAS  # adjacent is fine
+
+
+def test_q_only_ignores_k_heads():
+    L = rp.lib()
+    d = good_desc(n_heads_k=99, dtype=7)
+    assert L.rope_fwd_q(A16, ctypes.byref(d), None) == DTYPE
+    d = good_desc(n_heads_k=99, rotary_dim=3)
+    assert L.rope_bwd_q(A16, ctypes.byref(d), None) == SHAPE
+
+
+@pytest.mark.parametrize("change", [dict(batch=0), dict(seq_len=0), dict(rotary_dim=0),
+                                    dict(n_heads_q=0, n_heads_k=0)])
+def test_empty_work_is_ok_without_touching_the_gpu(change):
+    # even with NULL data pointers: nothing is enqueued
+    assert call_qk(good_desc(**change), q=None, k=None) == OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks behaviour with no GPU present")
+def test_valid_call_without_gpu_reports_hip_error():
+    assert call_qk(good_desc()) == HIP
+    assert rp.lib().rope_fwd_q(A16, ctypes.byref(good_desc()), None) == HIP
+
+
+@pytest.mark.parametrize("theta,R,rows", [(10000.0, 64, 128), (10000.0, 128, 4096),
+                                          (10000.0, 32, 9216), (500000.0, 128, 32768),
+                                          (500000.0, 128, 131072), (3.0, 6, 17)])
+def test_host_table_matches_oracle_bitexact(orc, theta, R, rows):
+    """The product's table builder and the oracle's own table are two separate
+    implementations of RN32(cos/sin(p * theta^(-2i/R))); they must agree."""
+    c, s = rp.rope_build_table(rows, R, theta)
+    oc, os_ = orc.table(theta, R, rows)
+    assert np.array_equal(c.numpy().view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(s.numpy().view(np.uint32), os_.view(np.uint32))
+
+
+def test_table_builder_errors():
+    L = rp.lib()
+    buf = (ctypes.c_float * 8)()
+    assert L.rope_build_table(buf, buf, 2, 3, 10000.0) == SHAPE
+    assert L.rope_build_table(buf, buf, -1, 4, 10000.0) == SHAPE
+    assert L.rope_build_table(buf, buf, 2, 4, 0.0) == SHAPE
+    assert L.rope_build_table(None, None, 2, 4, 10000.0) == NULL
+    assert L.rope_build_table(None, None, 0, 4, 10000.0) == OK
+
+
+def test_binding_marshals_shapes():
+    q = torch.zeros(2, 32, 100, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 8, 100, 128, dtype=torch.bfloat16)
+    cos = torch.zeros(100, 64)
+    sin = torch.zeros(100, 64)
+    d = rp.make_desc(q, k, cos, sin)
+    assert (d.batch, d.n_heads_q, d.n_heads_k, d.seq_len, d.head_dim, d.rotary_dim) == \
+        (2, 32, 8, 100, 128, 128)
+    assert d.dtype == 2 and d.layout == 0 and d.table_rows == 100 and not d.pos
+    qs = torch.zeros(2, 100, 32, 64, dtype=torch.float16)
+    ks = torch.zeros(2, 100, 8, 64, dtype=torch.float16)
+    pos = torch.zeros(100, dtype=torch.int32)
+    d = rp.make_desc(qs, ks, cos[:, :16].contiguous(), sin[:, :16].contiguous(),
+                     layout="bshd", pairing="interleaved", rotary_dim=32, pos=pos)
+    assert (d.n_heads_q, d.n_heads_k, d.seq_len, d.head_dim, d.rotary_dim) == (32, 8, 100, 64, 32)
+    assert d.dtype == 1 and d.layout == 1 and d.pairing == 1 and d.pos_batch_stride == 0
+    dec = torch.zeros(7, 4, 1, 64, dtype=torch.bfloat16)
+    d = rp.make_desc(dec, None, cos[:, :32].contiguous(), sin[:, :32].contiguous(),
+                     pos=torch.zeros(7, dtype=torch.int32))
+    assert d.pos_batch_stride == 1 and d.n_heads_k == 0
+    with pytest.raises(ValueError):
+        rp.make_desc(q.transpose(1, 2), None, cos, sin)
+    with pytest.raises(ValueError):
+        rp.make_desc(q, k, cos[:, :10].contiguous(), sin[:, :10].contiguous())
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(rp, "_lib", None)
+    monkeypatch.setattr(rp, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        rp.lib()

@@ -1,0 +1,323 @@
+"""GPU parity: librope on an MI355X against the CPU oracle, through the C ABI.
+
+Every call goes through the ctypes binding to librope.so (the C entry points
+of include/librope.h). Tolerances are those of tests/_parity.py. Sizes:
+  - oracle-sized cases compare every element (several tiles, ragged tails);
+  - the full-size workloads run in the launch configuration that bench.py
+    times and are compared on sampled tokens (all heads and dims of each),
+    which the oracle computes one by one through its index path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import rotary_position_embedding_fwd_amd as rp
+import workloads as W
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def gpu_tables(w, rows=None):
+    c, s = rp.rope_build_table(w.table_rows if rows is None else rows, w.rotary_dim, w.theta)
+    return c.to(DEV), s.to(DEV)
+
+
+def opts(w, pos=None, launch="auto", pos_batch_stride=None):
+    return dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim,
+                pos=None if pos is None else pos.to(DEV),
+                pos_batch_stride=(w.pos_batch_stride if pos is not None and
+                                  pos_batch_stride is None else pos_batch_stride),
+                launch=launch)
+
+
+def run_qk(w, q, k, direction, pos=None, launch="auto", tables=None):
+    cos, sin = tables or gpu_tables(w)
+    qd, kd = q.to(DEV), k.to(DEV)
+    fn = rp.rope_fwd_qk if direction == 1 else rp.rope_bwd_qk
+    fn(qd, kd, cos, sin, **opts(w, pos, launch))
+    torch.cuda.synchronize()
+    return qd.cpu(), kd.cpu()
+
+
+def check_full(w, direction, launch="auto"):
+    names = ("q", "k") if direction == 1 else ("dq", "dk")
+    t = W.tensors(w, names)
+    x_q, x_k = t[names[0]], t[names[1]]
+    pos = W.positions(w)
+    say(f"[gpu] {w.name} dir={direction} launch={launch} q{tuple(x_q.shape)} {w.dtype}")
+    gq, gk = run_qk(w, x_q, x_k, direction, pos, launch)
+    masked = P.masked_tokens(w, pos)
+    stats = []
+    for g, x in ((gq, x_q), (gk, x_k)):
+        stats.append(P.assert_parity(P.storage(g), P.oracle_rope(w, x, direction, pos),
+                                     P.storage(x), w.dtype, w.layout, w.rotary_dim, masked,
+                                     f"{w.name} dir={direction}"))
+    return stats
+
+
+ORACLE_SIZED = {
+    "tiny_fp32": W.TINY_F32,
+    "llama_gqa_ragged": W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=300, table_rows=300),
+    "bshd_interleaved_ragged": W.BSHD_INTERLEAVED.scaled(batch=2, seq_len=333,
+                                                         table_rows=333),
+    "partial_rotary_indexed": W.PARTIAL_INDEXED,       # full size
+    "decode": W.DECODE,                                # full size
+    "long_context_slice": W.LONG_CONTEXT.scaled(seq_len=513, table_rows=131072),
+}
+
+
+@pytest.mark.parametrize("name", list(ORACLE_SIZED))
+@pytest.mark.parametrize("direction", [1, -1])
+def test_every_element_matches_oracle(name, direction):
+    check_full(ORACLE_SIZED[name], direction)
+
+
+@pytest.mark.parametrize("name", ["llama_gqa_ragged", "bshd_interleaved_ragged",
+                                  "partial_rotary_indexed", "decode", "tiny_fp32"])
+@pytest.mark.parametrize("launch", ["rows", "token"])
+def test_both_grid_shapes_match_oracle(name, launch):
+    check_full(ORACLE_SIZED[name], 1, launch)
+
+
+def test_tiny_fp32_backward_inverts_forward():
+    w = W.TINY_F32
+    t = W.tensors(w)
+    q, k = t["q"], t["k"]
+    cos, sin = gpu_tables(w)
+    qd, kd = q.to(DEV), k.to(DEV)
+    rp.rope_fwd_qk(qd, kd, cos, sin, **opts(w))
+    rp.rope_bwd_qk(qd, kd, cos, sin, **opts(w))
+    torch.cuda.synchronize()
+    assert (qd.cpu() - q).abs().max().item() <= 4e-6
+    assert (kd.cpu() - k).abs().max().item() <= 4e-6
+
+
+# ------------------------------------------------------------ cross checks
+
+def _bits(t):
+    return P.storage(t.cpu()).view(np.uint32) if t.dtype == torch.float32 else P.storage(t.cpu())
+
+
+def test_q_only_equals_q_part_of_fused_call():
+    w = ORACLE_SIZED["llama_gqa_ragged"]
+    t = W.tensors(w)
+    cos, sin = gpu_tables(w)
+    q1, k1 = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_fwd_qk(q1, k1, cos, sin, **opts(w))
+    q2 = t["q"].to(DEV)
+    rp.rope_fwd_q(q2, cos, sin, **opts(w))
+    k2 = t["k"].to(DEV)
+    rp.rope_fwd_q(k2, cos, sin, **opts(w))  # K alone, as a query tensor of Hk heads
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(q1), _bits(q2))
+    assert np.array_equal(_bits(k1), _bits(k2))
+    rp.rope_bwd_q(q2, cos, sin, **opts(w))
+    rp.rope_bwd_qk(q1, k1, cos, sin, **opts(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(q1), _bits(q2))
+
+
+def test_bshd_is_transposed_bhsd():
+    w = ORACLE_SIZED["llama_gqa_ragged"]
+    t = W.tensors(w)
+    cos, sin = gpu_tables(w)
+    a_q, a_k = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_fwd_qk(a_q, a_k, cos, sin, **opts(w))
+    b_q = t["q"].transpose(1, 2).contiguous().to(DEV)
+    b_k = t["k"].transpose(1, 2).contiguous().to(DEV)
+    rp.rope_fwd_qk(b_q, b_k, cos, sin, **opts(w.scaled(layout="bshd")))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(a_q), _bits(b_q.transpose(1, 2).contiguous()))
+    assert np.array_equal(_bits(a_k), _bits(b_k.transpose(1, 2).contiguous()))
+
+
+def test_interleaved_is_permuted_split_half():
+    w = ORACLE_SIZED["bshd_interleaved_ragged"]
+    R, D = w.rotary_dim, w.head_dim
+    perm = torch.arange(D)
+    for i in range(R // 2):
+        perm[2 * i], perm[2 * i + 1] = i, i + R // 2
+    t = W.tensors(w)
+    cos, sin = gpu_tables(w)
+    a_q, a_k = t["q"][..., perm].contiguous().to(DEV), t["k"][..., perm].contiguous().to(DEV)
+    rp.rope_fwd_qk(a_q, a_k, cos, sin, **opts(w))
+    b_q, b_k = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_fwd_qk(b_q, b_k, cos, sin, **opts(w.scaled(pairing="split_half")))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(a_q), _bits(b_q[..., perm].contiguous()))
+    assert np.array_equal(_bits(a_k), _bits(b_k[..., perm].contiguous()))
+
+
+def test_index_path_equals_plain_positions():
+    w = ORACLE_SIZED["llama_gqa_ragged"]
+    t = W.tensors(w)
+    cos, sin = gpu_tables(w)
+    a_q, a_k = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_fwd_qk(a_q, a_k, cos, sin, **opts(w))
+    b_q, b_k = t["q"].to(DEV), t["k"].to(DEV)
+    ar = torch.arange(w.seq_len, dtype=torch.int32)
+    rp.rope_fwd_qk(b_q, b_k, cos, sin, **opts(w, pos=ar))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(a_q), _bits(b_q))
+    assert np.array_equal(_bits(a_k), _bits(b_k))
+
+
+def test_decode_shape_equals_rows_shape_bitwise():
+    w = W.DECODE
+    t = W.tensors(w)
+    pos = W.positions(w)
+    r_q, r_k = run_qk(w, t["q"], t["k"], 1, pos, "rows")
+    k_q, k_k = run_qk(w, t["q"], t["k"], 1, pos, "token")
+    assert np.array_equal(_bits(r_q), _bits(k_q)) and np.array_equal(_bits(r_k), _bits(k_k))
+
+
+def test_guard_bands_untouched():
+    """Q and K sit inside larger buffers; every byte around them must survive."""
+    w = ORACLE_SIZED["partial_rotary_indexed"]
+    t = W.tensors(w)
+    pos = W.positions(w)
+    cos, sin = gpu_tables(w)
+    guard = 4096
+    nq, nk = t["q"].numel(), t["k"].numel()
+    buf = torch.full((guard + nq + guard + nk + guard,), -12345.0, dtype=torch.bfloat16,
+                     device=DEV)
+    q = buf[guard:guard + nq].view(t["q"].shape)
+    k = buf[2 * guard + nq:2 * guard + nq + nk].view(t["k"].shape)
+    q.copy_(t["q"].to(DEV))
+    k.copy_(t["k"].to(DEV))
+    before = buf.clone()
+    rp.rope_fwd_qk(q, k, cos, sin, **opts(w, pos=pos))
+    rp.rope_bwd_qk(q, k, cos, sin, **opts(w, pos=pos))
+    torch.cuda.synchronize()
+    for lo, hi in ((0, guard), (guard + nq, 2 * guard + nq), (2 * guard + nq + nk, buf.numel())):
+        assert torch.equal(buf[lo:hi].view(torch.int16), before[lo:hi].view(torch.int16))
+
+
+@pytest.mark.parametrize("offset", [1, 2, 4])
+def test_misaligned_views(offset):
+    """Base pointers off 16-byte alignment run narrower accesses, same results."""
+    w = ORACLE_SIZED["llama_gqa_ragged"].scaled(seq_len=37, table_rows=37)
+    t = W.tensors(w)
+    cos, sin = gpu_tables(w)
+    flat_q = torch.empty(t["q"].numel() + 8, dtype=torch.bfloat16, device=DEV)
+    flat_k = torch.empty(t["k"].numel() + 8, dtype=torch.bfloat16, device=DEV)
+    q = flat_q[offset:offset + t["q"].numel()].view(t["q"].shape)
+    k = flat_k[offset:offset + t["k"].numel()].view(t["k"].shape)
+    q.copy_(t["q"].to(DEV))
+    k.copy_(t["k"].to(DEV))
+    rp.rope_fwd_qk(q, k, cos, sin, **opts(w))
+    torch.cuda.synchronize()
+    for g, x in ((q, t["q"]), (k, t["k"])):
+        P.assert_parity(P.storage(g.cpu()), P.oracle_rope(w, x, 1, None), P.storage(x),
+                        w.dtype, w.layout, w.rotary_dim)
+
+
+@pytest.mark.parametrize("spec,pairing", [
+    (dict(head_dim=31, rotary_dim=30), "interleaved"),
+    (dict(head_dim=48, rotary_dim=48), "split_half"),
+    (dict(head_dim=130, rotary_dim=2), "split_half"),
+    (dict(head_dim=256, rotary_dim=128), "split_half"),
+])
+def test_unusual_dims(spec, pairing):
+    w = ORACLE_SIZED["llama_gqa_ragged"].scaled(seq_len=29, table_rows=29, pairing=pairing,
+                                                **spec)
+    check_full(w, 1)
+    check_full(w, -1, "token")
+
+
+def test_pass_through_specials_and_out_of_table_indices():
+    w = ORACLE_SIZED["partial_rotary_indexed"].scaled(seq_len=40, table_rows=100,
+                                                      pos_kind="none")
+    t = W.tensors(w)
+    q, k = t["q"], t["k"]
+    q.view(torch.int16)[..., w.rotary_dim:w.rotary_dim + 3] = torch.tensor(
+        [0x7fc1, 0x7f80, -128], dtype=torch.int16)  # NaN, +Inf, -Inf
+    pos = torch.randint(-50, 150, (w.seq_len,), generator=torch.Generator().manual_seed(3),
+                        dtype=torch.int32)
+    gq, gk = run_qk(w, q, k, 1, pos)
+    masked = P.masked_tokens(w, pos)
+    assert masked.any() and not masked.all()
+    for g, x in ((gq, q), (gk, k)):
+        P.assert_parity(P.storage(g), P.oracle_rope(w, x, 1, pos), P.storage(x), w.dtype,
+                        w.layout, w.rotary_dim, masked)
+
+
+def test_empty_inputs_are_noops():
+    w = ORACLE_SIZED["llama_gqa_ragged"]
+    cos, sin = gpu_tables(w)
+    for shape_q, shape_k in (((0, 32, 300, 128), (0, 8, 300, 128)),
+                             ((2, 32, 0, 128), (2, 8, 0, 128))):
+        q = torch.empty(shape_q, dtype=torch.bfloat16, device=DEV)
+        k = torch.empty(shape_k, dtype=torch.bfloat16, device=DEV)
+        rp.rope_fwd_qk(q, k, cos, sin, **opts(w))
+    q = torch.randn(1, 2, 5, 64, device=DEV).to(torch.bfloat16)
+    before = q.clone()
+    c0 = torch.empty(5, 0, device=DEV)
+    rp.rope_fwd_q(q, c0, c0, rotary_dim=0)
+    torch.cuda.synchronize()
+    assert torch.equal(q.view(torch.int16), before.view(torch.int16))
+
+
+def test_runs_on_the_callers_stream():
+    w = ORACLE_SIZED["bshd_interleaved_ragged"]
+    t = W.tensors(w)
+    cos, sin = gpu_tables(w)
+    q, k = t["q"].to(DEV), t["k"].to(DEV)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        rp.rope_fwd_qk(q, k, cos, sin, **opts(w))
+    s.synchronize()
+    for g, x in ((q, t["q"]), (k, t["k"])):
+        P.assert_parity(P.storage(g.cpu()), P.oracle_rope(w, x, 1, None), P.storage(x),
+                        w.dtype, w.layout, w.rotary_dim)
+
+
+# ------------------------------------------------ full sizes, sampled tokens
+
+def _sample_tokens(w, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    b = torch.randint(0, w.batch, (n,), generator=g)
+    s = torch.randint(0, w.seq_len, (n,), generator=g)
+    b = torch.cat([b, torch.tensor([0, w.batch - 1])])
+    s = torch.cat([s, torch.tensor([0, w.seq_len - 1])])
+    return b, s
+
+
+def _gather(x, b, s, layout):
+    """Rows of tokens (b[i], s[i]) as a [1, H, n, D] (bhsd) or [1, n, H, D] tensor."""
+    if layout == "bhsd":
+        return x[b, :, s, :].permute(1, 0, 2).unsqueeze(0).contiguous()
+    return x[b, s, :, :].unsqueeze(0).contiguous()
+
+
+@pytest.mark.parametrize("name", ["llama_gqa_prefill_bf16", "bshd_interleaved_fp16",
+                                  "long_context_bf16"])
+def test_full_size_sampled(name):
+    w = W.BY_NAME[name]
+    t = W.tensors(w)
+    say(f"[gpu] full-size {name}: q{tuple(w.q_shape)} k{tuple(w.k_shape)}")
+    cos, sin = gpu_tables(w)
+    qd, kd = t["q"].to(DEV), t["k"].to(DEV)
+    for direction in (1, -1):
+        fn = rp.rope_fwd_qk if direction == 1 else rp.rope_bwd_qk
+        fn(qd, kd, cos, sin, **opts(w))
+        torch.cuda.synchronize()
+        b, s = _sample_tokens(w, 48, 1000 + direction)
+        bd, sd = b.to(DEV), s.to(DEV)
+        for g, x in ((qd, t["q"]), (kd, t["k"])):
+            got = _gather(g, bd, sd, w.layout).cpu()
+            inp = _gather(x, b, s, w.layout)
+            ref = P.oracle_rope(w.scaled(batch=1, seq_len=len(s)), inp, direction,
+                                s.to(torch.int32), pos_batch_stride=0)
+            P.assert_parity(P.storage(got), ref, P.storage(inp), w.dtype, w.layout,
+                            w.rotary_dim, what=f"{name} dir={direction}")
+        # the next direction starts from the forward result
+        t = {"q": qd.cpu(), "k": kd.cpu()}

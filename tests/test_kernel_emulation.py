@@ -1,0 +1,222 @@
+"""librope's kernels run on the host, under AddressSanitizer, against the oracle.
+
+tests/emu/rope_emu.hip plans each call exactly as the library does and runs
+every workgroup and lane of the planned grid on host buffers of exact size.
+This checks, on the CPU and before any GPU run, that the index arithmetic
+of both grid shapes stays in bounds for every access width, pairing, layout
+and ragged size below, touches each element once, and computes what the
+oracle computes (same tolerances as the GPU parity tests).
+"""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import rotary_position_embedding_fwd_amd as rp
+import workloads as W
+from tests import _parity as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+EMU_SRC = os.path.join(ROOT, "tests", "emu", "rope_emu.hip")
+EMU_BIN = os.path.join(ROOT, "tests", "emu", "_build", "rope_emu")
+CSRC = os.path.join(ROOT, "rotary_position_embedding_fwd_amd", "csrc")
+DEPS = [EMU_SRC, os.path.join(CSRC, "rope_kernels.hpp"), os.path.join(CSRC, "rope_plan.hpp"),
+        os.path.join(ROOT, "include", "librope.h")]
+
+CODES = {"dtype": {"f32": 0, "f16": 1, "bf16": 2}, "layout": {"bhsd": 0, "bshd": 1},
+         "pairing": {"split_half": 0, "interleaved": 1},
+         "launch": {"auto": 0, "rows": 1, "token": 2}}
+
+
+@pytest.fixture(scope="module")
+def emu():
+    if (not os.path.exists(EMU_BIN) or
+            os.path.getmtime(EMU_BIN) < max(os.path.getmtime(p) for p in DEPS)):
+        os.makedirs(os.path.dirname(EMU_BIN), exist_ok=True)
+        cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-host-only", "-O1", "-g",
+               "-std=c++17", "-ffp-contract=off", "-Xarch_host", "-fsanitize=address",
+               "-fno-omit-frame-pointer", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+               "-o", EMU_BIN, EMU_SRC]
+        subprocess.run(cmd, check=True, capture_output=True)
+    return EMU_BIN
+
+
+def run_emu(emu, w, q, k, cos, sin, pos, direction=1, launch="auto", with_k=True,
+            q_offset=0, k_offset=0, cus=256, pos_batch_stride=None):
+    with tempfile.TemporaryDirectory() as job:
+        desc = dict(batch=w.batch, n_heads_q=w.n_heads_q, n_heads_k=w.n_heads_k,
+                    seq_len=w.seq_len, head_dim=w.head_dim, rotary_dim=w.rotary_dim,
+                    dtype=CODES["dtype"][w.dtype], layout=CODES["layout"][w.layout],
+                    pairing=CODES["pairing"][w.pairing], launch=CODES["launch"][launch],
+                    table_rows=cos.shape[0],
+                    pos_batch_stride=(w.pos_batch_stride if pos_batch_stride is None
+                                      else pos_batch_stride),
+                    with_k=int(with_k), direction=direction, cus=cus, q_offset=q_offset,
+                    k_offset=k_offset, pos_count=0 if pos is None else pos.numel())
+        with open(os.path.join(job, "desc.txt"), "w") as f:
+            for key, v in desc.items():
+                f.write(f"{key} {int(v)}\n")
+        P.storage(q).tofile(os.path.join(job, "q.bin"))
+        if with_k:
+            P.storage(k).tofile(os.path.join(job, "k.bin"))
+        cos.numpy().tofile(os.path.join(job, "cos.bin"))
+        sin.numpy().tofile(os.path.join(job, "sin.bin"))
+        if pos is not None:
+            pos.numpy().astype(np.int32).tofile(os.path.join(job, "pos.bin"))
+        env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
+        r = subprocess.run([emu, job], capture_output=True, text=True, timeout=300, env=env)
+        assert r.returncode == 0, r.stdout + r.stderr[-4000:]
+        plan = dict(line.split() for line in r.stdout.strip().splitlines())
+        plan = {key: int(v) for key, v in plan.items()}
+        if plan["status"] != 0:
+            return plan, None, None
+        st = P.storage(q)
+        qo = np.fromfile(os.path.join(job, "q_out.bin"), dtype=st.dtype).reshape(st.shape)
+        ko = None
+        if with_k:
+            sk = P.storage(k)
+            ko = np.fromfile(os.path.join(job, "k_out.bin"), dtype=sk.dtype).reshape(sk.shape)
+        return plan, qo, ko
+
+
+def _inputs(w, seed_shift=0):
+    t = W.tensors(w, ("q", "k"))
+    pos = W.positions(w)
+    cos, sin = rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
+    return t["q"], t["k"], pos, cos, sin
+
+
+def check(emu, w, direction=1, launch="auto", with_k=True, q_offset=0, k_offset=0, cus=256,
+          pos=None, use_workload_pos=True, expect=None):
+    q, k, wpos, cos, sin = _inputs(w)
+    if use_workload_pos:
+        pos = wpos
+    plan, qo, ko = run_emu(emu, w, q, k, cos, sin, pos, direction, launch, with_k, q_offset,
+                           k_offset, cus)
+    assert plan["status"] == 0, plan
+    for key, v in (expect or {}).items():
+        assert plan[key] == v, (key, plan)
+    masked = P.masked_tokens(w, pos)
+    P.assert_parity(qo, P.oracle_rope(w, q, direction, pos), P.storage(q), w.dtype, w.layout,
+                    w.rotary_dim, masked, "q")
+    if with_k:
+        P.assert_parity(ko, P.oracle_rope(w, k, direction, pos), P.storage(k), w.dtype,
+                        w.layout, w.rotary_dim, masked, "k")
+    return plan
+
+
+SMALL = {
+    "tiny_fp32": W.TINY_F32,
+    "llama_ragged": W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=77, table_rows=80),
+    "bshd_interleaved_ragged": W.BSHD_INTERLEAVED.scaled(batch=3, seq_len=45, table_rows=45),
+    "partial_indexed": W.PARTIAL_INDEXED.scaled(seq_len=130, pos_start_max=9000),
+    "decode": W.DECODE.scaled(batch=19),
+    "long_theta": W.LONG_CONTEXT.scaled(seq_len=64, table_rows=131072),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("direction", [1, -1])
+def test_emulated_workloads_match_oracle(emu, name, direction):
+    check(emu, SMALL[name], direction)
+
+
+@pytest.mark.parametrize("name", ["llama_ragged", "bshd_interleaved_ragged", "partial_indexed",
+                                  "decode", "tiny_fp32"])
+@pytest.mark.parametrize("launch", ["rows", "token"])
+def test_both_grid_shapes(emu, name, launch):
+    check(emu, SMALL[name], 1, launch, expect={"token": int(launch == "token")})
+
+
+def test_auto_shape_selection(emu):
+    assert check(emu, SMALL["decode"])["token"] == 1
+    assert check(emu, SMALL["llama_ragged"])["token"] == 0
+
+
+@pytest.mark.parametrize("cus", [1, 7, 256, 1000])
+def test_grid_heuristic_any_cu_count(emu, cus):
+    """Head grouping depends on the CU count; every choice must cover all work."""
+    check(emu, SMALL["llama_ragged"], 1, cus=cus)
+
+
+def test_q_only(emu):
+    check(emu, SMALL["llama_ragged"], 1, with_k=False)
+    check(emu, SMALL["decode"], -1, with_k=False)
+
+
+@pytest.mark.parametrize("q_off,k_off,vec", [(1, 0, 1), (2, 0, 2), (4, 4, 4), (0, 6, 2),
+                                             (8, 8, 8)])
+def test_misaligned_bases_use_narrower_accesses(emu, q_off, k_off, vec):
+    w = SMALL["llama_ragged"].scaled(seq_len=9, table_rows=9)
+    check(emu, w, 1, q_offset=q_off, k_offset=k_off, expect={"vec": vec})
+
+
+@pytest.mark.parametrize("spec,vec,aligned", [
+    (dict(head_dim=24, rotary_dim=24), 4, 1),            # R/2 = 12
+    (dict(head_dim=48, rotary_dim=48), 8, 1),            # lanes = 3 (not a power of 2)
+    (dict(head_dim=66, rotary_dim=64), 2, 1),            # D only 2-divisible
+    (dict(head_dim=130, rotary_dim=2), 1, 1),            # one pair per row
+    (dict(head_dim=256, rotary_dim=128), 8, 1),          # partial rotary, wide head
+    (dict(head_dim=256, rotary_dim=256), 8, 1),          # 16 lanes per row
+])
+def test_head_and_rotary_dims(emu, spec, vec, aligned):
+    w = SMALL["llama_ragged"].scaled(seq_len=11, table_rows=11, **spec)
+    check(emu, w, 1, expect={"vec": vec, "aligned": aligned})
+    check(emu, w, -1, launch="token")
+
+
+@pytest.mark.parametrize("spec,vec,aligned", [
+    (dict(head_dim=31, rotary_dim=30), 2, 0),  # odd D: rows not pair-aligned
+    (dict(head_dim=62, rotary_dim=62), 2, 1),
+    (dict(head_dim=40, rotary_dim=24), 8, 1),
+])
+def test_interleaved_dims(emu, spec, vec, aligned):
+    w = SMALL["bshd_interleaved_ragged"].scaled(seq_len=13, table_rows=13, **spec)
+    check(emu, w, 1, expect={"vec": vec, "aligned": aligned})
+    check(emu, w.scaled(layout="bhsd"), -1, launch="token")
+
+
+def test_many_heads_loop_in_token_shape(emu):
+    """(Hq + Hk) * lanes above 1024 lanes: the token shape loops within a workgroup."""
+    w = SMALL["decode"].scaled(n_heads_q=96, n_heads_k=8, head_dim=256, rotary_dim=256,
+                               batch=3)
+    plan = check(emu, w, 1, launch="token")
+    assert plan["block"] == 1024
+
+
+def test_mqa_single_kv_head(emu):
+    check(emu, SMALL["llama_ragged"].scaled(n_heads_k=1), 1)
+
+
+def test_out_of_table_indices_pass_through(emu):
+    w = SMALL["partial_indexed"].scaled(seq_len=20, table_rows=50)
+    pos = torch.tensor([-5, 0, 49, 50, 1 << 30, -(1 << 30), 7, 3, 2, 1, 0, 48, 51, 9, 8, 7,
+                        6, 5, 4, 3], dtype=torch.int32)
+    check(emu, w, 1, pos=pos, use_workload_pos=False)
+    check(emu, w, -1, launch="token", pos=pos, use_workload_pos=False)
+
+
+def test_per_sequence_positions_in_prefill(emu):
+    w = SMALL["llama_ragged"].scaled(seq_len=10, table_rows=1000, pos_kind="none")
+    pos = W.random_positions(w.batch * w.seq_len, 1000, 77)
+    q, k, _, cos, sin = _inputs(w)
+    plan, qo, ko = run_emu(emu, w, q, k, cos, sin, pos, 1, "auto", True,
+                           pos_batch_stride=w.seq_len)
+    for x, o in ((q, qo), (k, ko)):
+        ref = P.oracle_rope(w, x, 1, pos, pos_batch_stride=w.seq_len)
+        P.assert_parity(o, ref, P.storage(x), w.dtype, w.layout, w.rotary_dim,
+                        P.masked_tokens(w, pos, pos_batch_stride=w.seq_len))
+
+
+@pytest.mark.parametrize("change", [dict(batch=0), dict(seq_len=0), dict(rotary_dim=0)])
+def test_empty_work(emu, change):
+    w = SMALL["llama_ragged"].scaled(**change)
+    if w.rotary_dim == 0:
+        w = w.scaled(table_rows=w.seq_len)
+    q, k, pos, cos, sin = _inputs(w)
+    plan, qo, ko = run_emu(emu, w, q, k, cos, sin, pos)
+    assert plan["status"] == 0 and plan["empty"] == 1
+    assert np.array_equal(qo, P.storage(q))
