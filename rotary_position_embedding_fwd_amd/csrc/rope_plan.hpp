@@ -148,11 +148,13 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
   } else {
     a.n_items = a.n_tokens * a.lanes;
     const int64_t tiles = (a.n_items + kRowsBlock - 1) / kRowsBlock;
-    // Split the head loop into groups until there are enough waves to fill
-    // the chip about twice over; each group re-reads the token's cos/sin,
-    // which then comes from cache.
+    // One lane walks every head of its token when there are enough tokens
+    // for ~8 waves per CU (4 head rows in flight per lane cover the HBM
+    // latency; on MI355X this beat splitting the heads over more waves).
+    // Fewer tokens: split the heads into groups until that many waves exist;
+    // each group re-reads the token's cos/sin, which then comes from cache.
     const int64_t waves = tiles * (kRowsBlock / 64);
-    const int64_t target = (int64_t)cus * 64;
+    const int64_t target = (int64_t)cus * 8;
     int64_t groups = (target + waves - 1) / waves;
     if (groups < 1) groups = 1;
     if (groups > h_total) groups = h_total;
@@ -160,7 +162,6 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
     a.n_groups = (int32_t)((h_total + a.heads_per_group - 1) / a.heads_per_group);
     const int64_t n_wg = tiles * a.n_groups;
     if (n_wg > 0x7fffffff) return ROPE_ERR_SHAPE;
-    a.n_wg = (int32_t)n_wg;
     pl->grid = n_wg;
     pl->block = kRowsBlock;
   }
