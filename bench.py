@@ -85,6 +85,10 @@ def device_inputs(w, sets: int, which=("q", "k", "dq", "dk")):
 
 
 def time_prefill(w, steps: int, warmup: int, sets: int):
+    """Time `steps` steps back to back between two HIP events on the launch
+    stream. Forward and backward are the same kernel (the sign of sin is an
+    argument), so the region divided by 2 * steps is that kernel's average
+    launch duration, inter-launch gaps included."""
     import torch
     import rotary_position_embedding_fwd_amd as rp
     import workloads as W
@@ -92,40 +96,31 @@ def time_prefill(w, steps: int, warmup: int, sets: int):
     cos, sin = rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
     cos, sin = cos.cuda(), sin.cuda()
     host, bufs = device_inputs(w, sets)
-    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim,
-              pos=None if pos is None else pos.cuda())
     stream = torch.cuda.current_stream()
+    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim,
+              pos=None if pos is None else pos.cuda(), stream=stream)
+    fwd = [rp.prepare(b["q"], b["k"], cos, sin, **kw) for b in bufs]
+    bwd = [rp.prepare(b["dq"], b["dk"], cos, sin, **kw) for b in bufs]
 
-    def step(i, ev=None):
-        b = bufs[i % sets]
-        if ev is not None:
-            ev[0].record(stream)
-        rp.rope_fwd_qk(b["q"], b["k"], cos, sin, stream=stream, **kw)
-        if ev is not None:
-            ev[1].record(stream)
-        rp.rope_bwd_qk(b["dq"], b["dk"], cos, sin, stream=stream, **kw)
-        if ev is not None:
-            ev[2].record(stream)
+    def step(i):
+        fwd[i % sets].rope_fwd_qk()
+        bwd[i % sets].rope_bwd_qk()
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(steps):
-        step(warmup + i, evs[i])
+        step(warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    return dict(total_ms=total_ms, wall_s=wall, fwd_ms=fwd_ms, bwd_ms=bwd_ms, pos=pos,
-                host=host)
+
+    return dict(total_ms=total_ms, wall_s=wall, pos=pos, host=host)
 
 
 def time_decode(calls: int = 2000, warmup: int = 50):
@@ -138,25 +133,26 @@ def time_decode(calls: int = 2000, warmup: int = 50):
     cos, sin = cos.cuda(), sin.cuda()
     t = W.tensors(w)
     q, k = t["q"].cuda(), t["k"].cuda()
-    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, pos=pos)
     stream = torch.cuda.current_stream()
+    call = rp.prepare(q, k, cos, sin, layout=w.layout, pairing=w.pairing,
+                      rotary_dim=w.rotary_dim, pos=pos, stream=stream)
     for _ in range(warmup):
-        rp.rope_fwd_qk(q, k, cos, sin, stream=stream, **kw)
+        call.rope_fwd_qk()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(calls):
-        rp.rope_fwd_qk(q, k, cos, sin, stream=stream, **kw)
+        call.rope_fwd_qk()
     b.record(stream)
     torch.cuda.synchronize()
     per_call_us = a.elapsed_time(b) * 1000.0 / calls
-    # kernel-only duration: events around single launches
+    # one launch at a time, events around each
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(200)]
     for e0, e1 in evs:
         e0.record(stream)
-        rp.rope_fwd_qk(q, k, cos, sin, stream=stream, **kw)
+        call.rope_fwd_qk()
         e1.record(stream)
     torch.cuda.synchronize()
     kern = sorted(e0.elapsed_time(e1) * 1000.0 for e0, e1 in evs)
@@ -164,6 +160,36 @@ def time_decode(calls: int = 2000, warmup: int = 50):
     return {"workload": w.name, "us_per_call_back_to_back": round(per_call_us, 3),
             "us_kernel_event_median": round(kern[len(kern) // 2], 3),
             "algorithmic_bytes": nbytes, "calls": calls}
+
+
+def stream_ceiling(nbytes: int = 3 << 29, reps: int = 20):
+    """GB/s of a plain in-place read+write stream (libstream_probe.so) over a
+    buffer larger than the 256 MB Infinity Cache: the attainable HBM rate of
+    an operation that reads and writes every byte once."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "rotary_position_embedding_fwd_amd", "libstream_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.stream_rmw_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint,
+                                     ctypes.c_void_p]
+    lib.stream_rmw_probe.restype = ctypes.c_int
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        assert lib.stream_rmw_probe(buf.data_ptr(), nbytes, 0, stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        lib.stream_rmw_probe(buf.data_ptr(), nbytes, 0, stream.cuda_stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / reps
+    del buf
+    return {"kernel": "stream_rmw_kernel (16 B non-temporal load + store per lane)",
+            "bytes_per_launch": 2 * nbytes, "avg_launch_us": round(us, 2),
+            "GBps": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def cpu_baseline(w, host, pos):
@@ -241,7 +267,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str = TRAFFIC_FILE):
         return sum(vals) / len(vals) if vals else None
 
     is_fwd = lambda n: "rope_rows_kernel" in n and "bf16" in n.replace("DF16b", "bf16")  # noqa
-    is_copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()  # noqa
+    is_copy = lambda n: "copyBuffer" in n  # the runtime's device-to-device copy  # noqa
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
     f_k, w_k = pick(fetch, is_fwd), pick(write, is_fwd)
     f_c, w_c = pick(fetch, is_copy), pick(write, is_copy)
@@ -271,6 +297,7 @@ def main():
                     help="buffer sets cycled through (3 x 320 MiB > the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -298,10 +325,9 @@ def main():
     step_bytes = 2 * per_call
     total_s = r["total_ms"] / 1000.0
     gbs = args.steps * step_bytes / total_s / 1e9
-    fwd = sorted(r["fwd_ms"])
-    bwd = sorted(r["bwd_ms"])
-    fwd_avg_ms = sum(fwd) / len(fwd)
-    achieved = per_call / (fwd_avg_ms / 1000.0) / 1e9
+    launches = 2 * args.steps
+    avg_launch_us = r["total_ms"] * 1000.0 / launches
+    achieved = per_call / (avg_launch_us * 1e-6) / 1e9
     traffic = stored_traffic()
     out = {
         "metric": METRIC,
@@ -326,12 +352,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "rope_rows_kernel<__bf16, 8, split-half> forward",
-                     "avg_launch_us": round(fwd_avg_ms * 1000.0, 3),
-                     "median_launch_us": round(fwd[len(fwd) // 2] * 1000.0, 3),
-                     "bwd_avg_launch_us": round(sum(bwd) / len(bwd) * 1000.0, 3)},
+                     "kernel": "rope_rows_kernel<__bf16, 8, split-half> (fwd and bwd launches)",
+                     "algorithmic_bytes_per_launch": per_call,
+                     "avg_launch_us": round(avg_launch_us, 3),
+                     "launches_timed": launches},
         "wall_s_timed": round(r["wall_s"], 4),
     }
+    if not args.no_ceiling:
+        ceil = stream_ceiling()
+        ceil["frac_achieved_of_ceiling"] = round(achieved / ceil["GBps"], 4)
+        out["roofline"]["measured_stream_ceiling"] = ceil
     if not args.no_decode:
         out["decode"] = time_decode()
     if not args.no_cpu_baseline:

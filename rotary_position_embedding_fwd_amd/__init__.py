@@ -203,6 +203,38 @@ def rope_bwd_q(dq, cos, sin, *, stream=None, **kw):
     return dq
 
 
+class Prepared:
+    """A call whose descriptor is built once: for loops that issue the same
+    rotation many times (benchmarks, decode steps). Holds the tensors alive;
+    each method only forwards cached pointers to the C entry point."""
+
+    def __init__(self, q, k, cos, sin, stream=None, **kw):
+        self._keep = (q, k, cos, sin, kw.get("pos"))
+        self.desc = make_desc(q, k, cos, sin, **kw)
+        self._q = q.data_ptr()
+        self._k = k.data_ptr() if k is not None else None
+        self._stream = _stream(stream)
+        self._pdesc = ctypes.byref(self.desc)
+        self._lib = lib()
+
+    def rope_fwd_qk(self):
+        _check(self._lib.rope_fwd_qk(self._q, self._k, self._pdesc, self._stream), "rope_fwd_qk")
+
+    def rope_bwd_qk(self):
+        _check(self._lib.rope_bwd_qk(self._q, self._k, self._pdesc, self._stream), "rope_bwd_qk")
+
+    def rope_fwd_q(self):
+        _check(self._lib.rope_fwd_q(self._q, self._pdesc, self._stream), "rope_fwd_q")
+
+    def rope_bwd_q(self):
+        _check(self._lib.rope_bwd_q(self._q, self._pdesc, self._stream), "rope_bwd_q")
+
+
+def prepare(q, k, cos, sin, *, stream=None, **kw) -> Prepared:
+    """Build the descriptor of a rope_*_qk / rope_*_q call once (see Prepared)."""
+    return Prepared(q, k, cos, sin, stream=stream, **kw)
+
+
 def rope_build_table(table_rows: int, rotary_dim: int, theta: float = 10000.0):
     """Host float32 cos/sin tables [table_rows, R/2] (CPU torch tensors)."""
     import torch

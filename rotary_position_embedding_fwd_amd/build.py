@@ -14,6 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librope.so")
 SOURCES = [os.path.join(CSRC, "librope.hip")]
+PROBE_LIB = os.path.join(PKG, "libstream_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
 HEADERS = [os.path.join(CSRC, "rope_kernels.hpp"), os.path.join(INCLUDE, "librope.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,8 +36,9 @@ FLAGS = [
 ]
 
 
-def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
-    cmd = [HIPCC, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *extra, "-o", out, *SOURCES]
+def build(out: str = LIB, extra=(), verbose: bool = False, sources=None) -> str:
+    cmd = [HIPCC, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *extra, "-o", out,
+           *(SOURCES if sources is None else sources)]
     if verbose:
         print(" ".join(cmd), flush=True)
     tmp = out + ".tmp"
@@ -45,11 +48,20 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     return out
 
 
+def build_all(verbose: bool = False):
+    """librope.so and the benchmark's stream-bandwidth probe."""
+    build(LIB, verbose=verbose)
+    build(PROBE_LIB, verbose=verbose, sources=PROBE_SOURCES)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("-o", default=LIB)
     args = ap.parse_args()
-    build(args.o, verbose=True)
+    if args.o == LIB:
+        build_all(verbose=True)
+    else:
+        build(args.o, verbose=True)
 
 
 if __name__ == "__main__":
