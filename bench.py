@@ -192,6 +192,64 @@ def stream_ceiling(nbytes: int = 3 << 29, reps: int = 20):
             "GBps": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+def time_workload(w, launches=("auto", "rows", "token"), target_s: float = 0.15):
+    """µs per call and GB/s of rope_fwd_qk and rope_bwd_qk on workload w,
+    back to back on one stream, cycling through enough buffer sets to exceed
+    the 256 MB Infinity Cache when the workload allows."""
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    pos = W.positions(w)
+    cos, sin = rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
+    cos, sin = cos.cuda(), sin.cuda()
+    e = 4 if w.dtype == "f32" else 2
+    qk_bytes = e * w.head_dim * w.batch * w.seq_len * (w.n_heads_q + w.n_heads_k)
+    sets = max(1, min(8, -(-600_000_000 // max(qk_bytes, 1))))
+    host, bufs = device_inputs(w, sets)
+    stream = torch.cuda.current_stream()
+    nbytes = algorithmic_bytes(w, pos)
+    results = []
+    for launch in launches:
+        kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, launch=launch,
+                  pos=None if pos is None else pos.cuda(), stream=stream)
+        fwd = [rp.prepare(b["q"], b["k"], cos, sin, **kw) for b in bufs]
+        bwd = [rp.prepare(b["dq"], b["dk"], cos, sin, **kw) for b in bufs]
+        out = {"workload": w.name, "launch": launch, "buffer_sets": sets,
+               "algorithmic_bytes_per_call": nbytes}
+        _time_calls(out, fwd, bwd, sets, nbytes, target_s, stream)
+        results.append(out)
+    del bufs
+    torch.cuda.empty_cache()
+    return results
+
+
+def _time_calls(out, fwd, bwd, sets, nbytes, target_s, stream):
+    import torch
+    for name, calls in (("fwd", [c.rope_fwd_qk for c in fwd]),
+                        ("bwd", [c.rope_bwd_qk for c in bwd])):
+        for i in range(10):
+            calls[i % sets]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(5):
+            calls[i % sets]()
+        torch.cuda.synchronize()
+        est = max((time.perf_counter() - t0) / 5, 1e-6)
+        reps = int(min(5000, max(20, target_s / est)))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            calls[i % sets]()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1000.0 / reps
+        out[f"{name}_us_per_call"] = round(us, 3)
+        out[f"{name}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        out[f"{name}_pct_of_hbm_peak"] = round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)
+        out[f"{name}_reps"] = reps
+
+
 def cpu_baseline(w, host, pos):
     """The CPU oracle, as it stands, on one full step (fwd + bwd) of w, 1 thread."""
     import oracle
@@ -301,6 +359,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--workloads", action="store_true",
+                    help="time every workload (both grid shapes); one JSON line each")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -318,6 +378,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.workloads:
+        for wl in W.ALL:
+            for res in time_workload(wl):
+                print(json.dumps(res), flush=True)
+        return
 
     w = W.LLAMA_GQA_PREFILL
     r = time_prefill(w, args.steps, args.warmup, args.sets)
