@@ -60,6 +60,8 @@ struct Args {
   int32_t lanes;             // chunks per token row
   int32_t heads_per_group;   // rows kernel: heads walked by one lane
   int32_t n_groups;          // rows kernel: head groups
+  int32_t group_slow;        // rows kernel: workgroup ids run over tiles first
+  int64_t n_tiles;           // rows kernel: 256-item tiles
   float sin_sign;            // +1 forward, -1 backward
 };
 
@@ -276,8 +278,15 @@ constexpr int kRowsBlock = 256;
 
 template <typename T, int V, int PAIR, bool ALIGNED, int U>
 ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
-  const int64_t tile = block / a.n_groups;
-  const int group = (int)(block - tile * a.n_groups);
+  int64_t tile;
+  int group;
+  if (a.group_slow) {  // all tiles of head group 0, then of group 1, ...
+    group = (int)(block / a.n_tiles);
+    tile = block - (int64_t)group * a.n_tiles;
+  } else {  // all head groups of tile 0, then of tile 1, ...
+    tile = block / a.n_groups;
+    group = (int)(block - tile * a.n_groups);
+  }
   const int64_t item = tile * kRowsBlock + thread;
   if (item >= a.n_items) return;
   const int64_t n = item / a.lanes;

@@ -136,8 +136,19 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
   a.lanes = (int32_t)(span / v);
   const int h_total = a.n_heads_q + a.n_heads_k;
 
+  // Rows shape: 256 (token, chunk) items per workgroup, each lane walking a
+  // group of heads. Its waves per head group:
+  a.n_items = a.n_tokens * a.lanes;
+  const int64_t tiles = (a.n_items + kRowsBlock - 1) / kRowsBlock;
+  const int64_t waves_per_group = tiles * (kRowsBlock / 64);
+  const int64_t target_waves = (int64_t)cus * 8;
+
   pl->token = d->launch == ROPE_LAUNCH_TOKEN;
-  if (d->launch == ROPE_LAUNCH_AUTO) pl->token = d->seq_len == 1;
+  if (d->launch == ROPE_LAUNCH_AUTO) {
+    // decode, or too few tokens for the rows shape to fill the chip even
+    // with one head per lane: one token per workgroup instead
+    pl->token = d->seq_len == 1 || waves_per_group * h_total < target_waves;
+  }
 
   if (pl->token) {
     const int64_t per_token = (int64_t)h_total * a.lanes;
@@ -146,20 +157,30 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
     const int64_t max_grid = (int64_t)cus * 64;
     pl->grid = a.n_tokens < max_grid ? a.n_tokens : max_grid;
   } else {
-    a.n_items = a.n_tokens * a.lanes;
-    const int64_t tiles = (a.n_items + kRowsBlock - 1) / kRowsBlock;
-    // One lane walks every head of its token when there are enough tokens
-    // for ~8 waves per CU (4 head rows in flight per lane cover the HBM
-    // latency; on MI355X this beat splitting the heads over more waves).
-    // Fewer tokens: split the heads into groups until that many waves exist;
-    // each group re-reads the token's cos/sin, which then comes from cache.
-    const int64_t waves = tiles * (kRowsBlock / 64);
-    const int64_t target = (int64_t)cus * 8;
-    int64_t groups = (target + waves - 1) / waves;
-    if (groups < 1) groups = 1;
-    if (groups > h_total) groups = h_total;
-    a.heads_per_group = (int32_t)((h_total + groups - 1) / groups);
-    a.n_groups = (int32_t)((h_total + a.heads_per_group - 1) / a.heads_per_group);
+    // Head groups, walked in group-slow order (all tiles of group 0, then of
+    // group 1, ...): on MI355X this streams HBM best when a lane walks 4 heads
+    // (one unrolled batch). Each group reads the cos/sin rows of its tokens
+    // again, so groups grow in steps of 4 heads until those re-reads stay
+    // under 15% of the call's Q/K traffic (long sequences have big tables);
+    // they shrink below 4 heads only when there are too few waves.
+    const int64_t e = elem_bytes(d->dtype);
+    const int64_t rows_touched = d->pos ? (d->table_rows < a.n_tokens ? d->table_rows : a.n_tokens)
+                                        : d->seq_len;
+    const double table_pass = 4.0 * (double)d->rotary_dim * (double)rows_touched;
+    const double qk_bytes = 2.0 * (double)e * (double)d->rotary_dim * (double)a.n_tokens * h_total;
+    int g = 4;
+    while (g < h_total && (double)((h_total + g - 1) / g) * table_pass > 0.15 * qk_bytes) g += 4;
+    if (g > h_total) g = h_total;
+    int64_t groups = (h_total + g - 1) / g;
+    if (waves_per_group * groups < target_waves) {
+      groups = (target_waves + waves_per_group - 1) / waves_per_group;
+      if (groups > h_total) groups = h_total;
+      g = (int)((h_total + groups - 1) / groups);
+    }
+    a.heads_per_group = g;
+    a.n_groups = (int32_t)((h_total + g - 1) / g);
+    a.n_tiles = tiles;
+    a.group_slow = 1;
     const int64_t n_wg = tiles * a.n_groups;
     if (n_wg > 0x7fffffff) return ROPE_ERR_SHAPE;
     pl->grid = n_wg;

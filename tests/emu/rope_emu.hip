@@ -124,10 +124,18 @@ int main(int argc, char** argv) {
   const rope_status_t st = rope::make_plan(q, k, &d, with_k, sign, cus, &pl);
   printf("status %d\n", (int)st);
   if (st != ROPE_OK) return 0;
+  // test-only overrides of the rows-kernel grid (head-group size and order)
+  if (!pl.empty && !pl.token && kv["heads_per_group"] > 0) {
+    const int h_total = pl.a.n_heads_q + pl.a.n_heads_k;
+    pl.a.heads_per_group = (int32_t)kv["heads_per_group"];
+    pl.a.n_groups = (h_total + pl.a.heads_per_group - 1) / pl.a.heads_per_group;
+    pl.grid = pl.a.n_tiles * pl.a.n_groups;
+  }
+  if (!pl.empty && !pl.token && kv.count("group_slow")) pl.a.group_slow = (int32_t)kv["group_slow"];
   printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
-         "heads_per_group %d\nn_groups %d\n",
+         "heads_per_group %d\nn_groups %d\ngroup_slow %d\n",
          (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
-         pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups);
+         pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow);
   if (!pl.empty) {
     HostRunner runner{pl};
     rope::dispatch(pl, runner);

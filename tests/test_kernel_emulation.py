@@ -45,7 +45,7 @@ def emu():
 
 
 def run_emu(emu, w, q, k, cos, sin, pos, direction=1, launch="auto", with_k=True,
-            q_offset=0, k_offset=0, cus=256, pos_batch_stride=None):
+            q_offset=0, k_offset=0, cus=256, pos_batch_stride=None, overrides=None):
     with tempfile.TemporaryDirectory() as job:
         desc = dict(batch=w.batch, n_heads_q=w.n_heads_q, n_heads_k=w.n_heads_k,
                     seq_len=w.seq_len, head_dim=w.head_dim, rotary_dim=w.rotary_dim,
@@ -56,6 +56,7 @@ def run_emu(emu, w, q, k, cos, sin, pos, direction=1, launch="auto", with_k=True
                                       else pos_batch_stride),
                     with_k=int(with_k), direction=direction, cus=cus, q_offset=q_offset,
                     k_offset=k_offset, pos_count=0 if pos is None else pos.numel())
+        desc.update(overrides or {})
         with open(os.path.join(job, "desc.txt"), "w") as f:
             for key, v in desc.items():
                 f.write(f"{key} {int(v)}\n")
@@ -90,12 +91,12 @@ def _inputs(w, seed_shift=0):
 
 
 def check(emu, w, direction=1, launch="auto", with_k=True, q_offset=0, k_offset=0, cus=256,
-          pos=None, use_workload_pos=True, expect=None):
+          pos=None, use_workload_pos=True, expect=None, overrides=None):
     q, k, wpos, cos, sin = _inputs(w)
     if use_workload_pos:
         pos = wpos
     plan, qo, ko = run_emu(emu, w, q, k, cos, sin, pos, direction, launch, with_k, q_offset,
-                           k_offset, cus)
+                           k_offset, cus, overrides=overrides)
     assert plan["status"] == 0, plan
     for key, v in (expect or {}).items():
         assert plan[key] == v, (key, plan)
@@ -132,14 +133,29 @@ def test_both_grid_shapes(emu, name, launch):
 
 
 def test_auto_shape_selection(emu):
+    """Decode, and prefill too small to fill the chip with the rows shape even
+    at one head per lane, take the token shape; otherwise rows."""
     assert check(emu, SMALL["decode"])["token"] == 1
-    assert check(emu, SMALL["llama_ragged"])["token"] == 0
+    assert check(emu, SMALL["decode"], cus=1)["token"] == 1
+    assert check(emu, SMALL["llama_ragged"])["token"] == 1  # 154 tokens on 256 CUs
+    plan = check(emu, SMALL["llama_ragged"], cus=1)  # same tokens, a 1-CU device
+    assert plan["token"] == 0 and plan["group_slow"] == 1 and plan["heads_per_group"] == 4
 
 
 @pytest.mark.parametrize("cus", [1, 7, 256, 1000])
 def test_grid_heuristic_any_cu_count(emu, cus):
     """Head grouping depends on the CU count; every choice must cover all work."""
     check(emu, SMALL["llama_ragged"], 1, cus=cus)
+
+
+@pytest.mark.parametrize("name", ["llama_ragged", "bshd_interleaved_ragged", "partial_indexed"])
+@pytest.mark.parametrize("group_slow", [0, 1])
+@pytest.mark.parametrize("heads_per_group", [1, 3, 8, 100])
+def test_head_groups_in_either_order(emu, name, group_slow, heads_per_group):
+    """Every head-group size and both workgroup orders cover all rows once."""
+    plan = check(emu, SMALL[name], 1, "rows",
+                 overrides=dict(heads_per_group=heads_per_group, group_slow=group_slow))
+    assert plan["group_slow"] == group_slow
 
 
 def test_q_only(emu):
