@@ -40,8 +40,10 @@ struct GpuLauncher {
   template <typename T, int V, int PAIR, bool AL>
   hipError_t run() {
     const dim3 grid((unsigned)pl.grid), block((unsigned)pl.block);
-    if (pl.token)
-      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL>), grid, block, 0, st, pl.a);
+    if (pl.token && pl.single)
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, true>), grid, block, 0, st, pl.a);
+    else if (pl.token)
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, false>), grid, block, 0, st, pl.a);
     else
       hipLaunchKernelGGL((rope::rope_rows_kernel<T, V, PAIR, AL, 4>), grid, block, 0, st, pl.a);
     return hipGetLastError();

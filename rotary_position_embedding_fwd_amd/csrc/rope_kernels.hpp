@@ -58,6 +58,7 @@ struct Args {
   int32_t n_heads_q;
   int32_t n_heads_k;
   int32_t lanes;             // chunks per token row
+  int32_t lanes_shift;       // log2(lanes) when lanes is a power of two, else -1
   int32_t heads_per_group;   // rows kernel: heads walked by one lane
   int32_t n_groups;          // rows kernel: head groups
   int32_t group_slow;        // rows kernel: workgroup ids run over tiles first
@@ -323,34 +324,51 @@ __global__ void __launch_bounds__(kRowsBlock) rope_rows_kernel(Args a) {
 // One token per workgroup iteration; lanes cover (head, chunk) pairs of that
 // token. The head rows are requested before the position, so the row loads
 // overlap the dependent index -> cos/sin chain.
-template <typename T, int V, int PAIR, bool ALIGNED>
-ROPE_HD void token_body(const Args& a, int64_t block, int64_t grid, int thread,
-                        int block_dim) {
-  const int h_total = a.n_heads_q + a.n_heads_k;
-  const int per_token = h_total * a.lanes;
-  for (int64_t n = block; n < a.n_tokens; n += grid) {
-    const int64_t b = n / a.seq_len;
-    const int64_t s = n - b * a.seq_len;
-    for (int it = thread; it < per_token; it += block_dim) {
-      const int h = it / a.lanes;
-      const int c = it - h * a.lanes;
-      T* row = head_row<T>(a, h, b, s);
-      RowChunk<T, V, PAIR, ALIGNED> r;
-      r.load(row, c, a.half);
-      const int64_t p = token_pos(a, b, s);
-      if (p < 0) continue;
-      Trig<V, PAIR> t;
-      t.load(a.cos + p * a.half, a.sin + p * a.half, c * ChunkGeom<V, PAIR>::kPairs,
-             a.sin_sign);
-      r.rotate(t);
-      r.store(row, c, a.half);
-    }
+ROPE_HD void split_item(const Args& a, int it, int* h, int* c) {
+  if (a.lanes_shift >= 0) {
+    *h = it >> a.lanes_shift;
+    *c = it & ((1 << a.lanes_shift) - 1);
+  } else {
+    *h = it / a.lanes;
+    *c = it - *h * a.lanes;
   }
 }
 
 template <typename T, int V, int PAIR, bool ALIGNED>
+ROPE_HD void token_item(const Args& a, int64_t n, int it) {
+  const int64_t b = n / a.seq_len;
+  const int64_t s = n - b * a.seq_len;
+  int h, c;
+  split_item(a, it, &h, &c);
+  T* row = head_row<T>(a, h, b, s);
+  RowChunk<T, V, PAIR, ALIGNED> r;
+  r.load(row, c, a.half);
+  const int64_t p = token_pos(a, b, s);
+  if (p < 0) return;
+  Trig<V, PAIR> t;
+  t.load(a.cos + p * a.half, a.sin + p * a.half, c * ChunkGeom<V, PAIR>::kPairs, a.sin_sign);
+  r.rotate(t);
+  r.store(row, c, a.half);
+}
+
+// SINGLE: the grid has one workgroup per token and each workgroup one lane
+// per (head, chunk), so no loop is needed (the decode case).
+template <typename T, int V, int PAIR, bool ALIGNED, bool SINGLE>
+ROPE_HD void token_body(const Args& a, int64_t block, int64_t grid, int thread,
+                        int block_dim) {
+  const int per_token = (a.n_heads_q + a.n_heads_k) * a.lanes;
+  if constexpr (SINGLE) {
+    if (thread < per_token) token_item<T, V, PAIR, ALIGNED>(a, block, thread);
+  } else {
+    for (int64_t n = block; n < a.n_tokens; n += grid)
+      for (int it = thread; it < per_token; it += block_dim)
+        token_item<T, V, PAIR, ALIGNED>(a, n, it);
+  }
+}
+
+template <typename T, int V, int PAIR, bool ALIGNED, bool SINGLE>
 __global__ void __launch_bounds__(1024) rope_token_kernel(Args a) {
-  token_body<T, V, PAIR, ALIGNED>(a, blockIdx.x, gridDim.x, threadIdx.x, blockDim.x);
+  token_body<T, V, PAIR, ALIGNED, SINGLE>(a, blockIdx.x, gridDim.x, threadIdx.x, blockDim.x);
 }
 
 }  // namespace rope

@@ -21,6 +21,7 @@ struct Plan {
   int64_t grid;    // workgroups
   int block;       // lanes per workgroup
   bool empty;      // nothing to do
+  bool single;     // token shape: one workgroup per token, one lane per item
 };
 
 inline int64_t elem_bytes(int32_t dtype) { return dtype == ROPE_F32 ? 4 : 2; }
@@ -134,6 +135,9 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
   pl->vec = v;
   const int64_t span = d->pairing == ROPE_SPLIT_HALF ? d->rotary_dim / 2 : d->rotary_dim;
   a.lanes = (int32_t)(span / v);
+  a.lanes_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((int64_t)1 << sh == a.lanes) a.lanes_shift = sh;
   const int h_total = a.n_heads_q + a.n_heads_k;
 
   // Rows shape: 256 (token, chunk) items per workgroup, each lane walking a
@@ -156,6 +160,7 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
     pl->block = (int)(want < 1024 ? want : 1024);
     const int64_t max_grid = (int64_t)cus * 64;
     pl->grid = a.n_tokens < max_grid ? a.n_tokens : max_grid;
+    pl->single = pl->grid == a.n_tokens && pl->block >= per_token;
   } else {
     // Head groups, walked in group-slow order (all tiles of group 0, then of
     // group 1, ...): on MI355X this streams HBM best when a lane walks 4 heads

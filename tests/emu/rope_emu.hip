@@ -73,8 +73,10 @@ struct HostRunner {
   int run() {
     for (int64_t blk = 0; blk < pl.grid; ++blk)
       for (int t = 0; t < pl.block; ++t) {
-        if (pl.token)
-          rope::token_body<T, V, PAIR, AL>(pl.a, blk, pl.grid, t, pl.block);
+        if (pl.token && pl.single)
+          rope::token_body<T, V, PAIR, AL, true>(pl.a, blk, pl.grid, t, pl.block);
+        else if (pl.token)
+          rope::token_body<T, V, PAIR, AL, false>(pl.a, blk, pl.grid, t, pl.block);
         else
           rope::rows_body<T, V, PAIR, AL, 4>(pl.a, blk, t);
       }
@@ -133,9 +135,9 @@ int main(int argc, char** argv) {
   }
   if (!pl.empty && !pl.token && kv.count("group_slow")) pl.a.group_slow = (int32_t)kv["group_slow"];
   printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
-         "heads_per_group %d\nn_groups %d\ngroup_slow %d\n",
+         "heads_per_group %d\nn_groups %d\ngroup_slow %d\nsingle %d\n",
          (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
-         pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow);
+         pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow, (int)pl.single);
   if (!pl.empty) {
     HostRunner runner{pl};
     rope::dispatch(pl, runner);

@@ -280,6 +280,41 @@ def test_runs_on_the_callers_stream():
                         w.dtype, w.layout, w.rotary_dim)
 
 
+def test_graph_replays_match_eager():
+    """Calls captured into a HIP graph, replayed several times with eager work
+    and synchronizations in between; every replay must equal the eager call."""
+    w = W.DECODE
+    t = W.tensors(w)
+    pos = W.positions(w).to(DEV)
+    cos, sin = gpu_tables(w)
+    q, k = t["q"].to(DEV), t["k"].to(DEV)
+    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, pos=pos)
+    eq, ek = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_fwd_qk(eq, ek, cos, sin, **kw)
+    rp.rope_bwd_qk(eq, ek, cos, sin, **kw)
+    rp.rope_fwd_qk(eq, ek, cos, sin, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        call = rp.prepare(q, k, cos, sin, stream=side, **kw)
+        call.rope_fwd_qk()
+        call.rope_bwd_qk()
+        call.rope_fwd_qk()
+    torch.cuda.synchronize()
+    for replay in range(4):
+        q.copy_(t["q"].to(DEV))
+        k.copy_(t["k"].to(DEV))
+        junk = torch.randn(1 << 20, device=DEV).sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q.view(torch.int16), eq.view(torch.int16)), replay
+        assert torch.equal(k.view(torch.int16), ek.view(torch.int16)), replay
+        del junk
+
+
 # ------------------------------------------------ full sizes, sampled tokens
 
 def _sample_tokens(w, n, seed):

@@ -195,12 +195,21 @@ def test_interleaved_dims(emu, spec, vec, aligned):
     check(emu, w.scaled(layout="bhsd"), -1, launch="token")
 
 
+def test_single_pass_token_shape_only_when_the_grid_covers_everything(emu):
+    assert check(emu, SMALL["decode"])["single"] == 1
+    plan = check(emu, SMALL["decode"], cus=1)  # 64 workgroups for 19 tokens: still one each
+    assert plan["single"] == 1
+    w = SMALL["decode"].scaled(batch=100)
+    plan = check(emu, w, cus=1)  # 64 workgroups loop over 100 tokens
+    assert plan["token"] == 1 and plan["single"] == 0 and plan["grid"] == 64
+
+
 def test_many_heads_loop_in_token_shape(emu):
     """(Hq + Hk) * lanes above 1024 lanes: the token shape loops within a workgroup."""
     w = SMALL["decode"].scaled(n_heads_q=96, n_heads_k=8, head_dim=256, rotary_dim=256,
                                batch=3)
     plan = check(emu, w, 1, launch="token")
-    assert plan["block"] == 1024
+    assert plan["block"] == 1024 and plan["single"] == 0
 
 
 def test_mqa_single_kv_head(emu):
