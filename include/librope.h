@@ -133,6 +133,73 @@ rope_status_t rope_fwd_q(void *q, const rope_desc_t *d, void *stream);
 /* Backward of rope_fwd_q. */
 rope_status_t rope_bwd_q(void *dq, const rope_desc_t *d, void *stream);
 
+/* ------------------------------------------------------------------------
+ * General form: strided views, out-of-place, other table layouts.
+ *
+ * The usual call site rotates Q and K where a fused projection left them,
+ * e.g. as views into one packed QKV buffer, without first copying them to
+ * contiguous tensors (How Unsloth Optimizes RoPE ..., Manual Triton Kernel
+ * Invocation: the kernel takes explicit strides for the batch, head and
+ * sequence dims). rope_apply takes every tensor as a strided view and can
+ * write its result to separate outputs.
+ */
+
+/* A view of a 4-d tensor indexed [batch, head, seq, dim]. The dim axis is
+ * contiguous (stride 1); the other three strides are in elements, >= 0.
+ * Element (b, h, s, j) is at data + (b*stride_b + h*stride_h + s*stride_s + j)
+ * elements. */
+typedef struct rope_view {
+  void *data;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_s;
+} rope_view_t;
+
+typedef struct rope_apply_desc {
+  int64_t batch;        /* B >= 0 */
+  int64_t seq_len;      /* S >= 0 */
+  int64_t head_dim;     /* D >= 0 */
+  int64_t rotary_dim;   /* R, even, 0 <= R <= D */
+  int64_t n_heads_q;    /* Hq >= 0 */
+  int64_t n_heads_k;    /* 0 <= Hk <= Hq; 0 rotates Q only */
+  int32_t dtype;        /* rope_dtype_t */
+  int32_t pairing;      /* rope_pairing_t */
+  int32_t launch;       /* rope_launch_t */
+  int32_t direction;    /* +1 forward, -1 backward (sin negated) */
+  rope_view_t q_in;     /* device */
+  rope_view_t k_in;     /* device; ignored when n_heads_k == 0 */
+  rope_view_t q_out;    /* data NULL: write back into q_in (in place) */
+  rope_view_t k_out;    /* data NULL: write back into k_in (in place) */
+  const float *cos;     /* device, 16-byte aligned */
+  const float *sin;     /* device, 16-byte aligned */
+  int64_t table_rows;   /* rows of cos and sin */
+  /* Frequency i of position p is read at cos[p*table_row_stride + i*table_col_stride]:
+   *   [rows, R/2]                       row stride R/2 (or 0), col stride 1
+   *   [rows, R] halves duplicated       row stride R,          col stride 1
+   *     (cos(cat(f, f)), the split-half convention of many model codes)
+   *   [rows, R] each value repeated     row stride R,          col stride 2
+   *     (repeat_interleave, the interleaved convention)           */
+  int64_t table_row_stride;  /* floats; 0 means R/2 */
+  int64_t table_col_stride;  /* 1 or 2 */
+  const int32_t *pos;        /* device int32 indices or NULL (p = s) */
+  int64_t pos_batch_stride;
+} rope_apply_desc_t;
+
+/* Rotate Q (and K) as described by `d`, in place or out of place, on `stream`.
+ * Same arithmetic, pairing and index rules as rope_fwd_qk. Out of place, the
+ * outputs receive every element: rotated dims and, bit for bit, dims >= R
+ * and the rows of tokens whose index is out of range. Outputs must not
+ * overlap each other or any input, except that an output may be exactly its
+ * own input (same pointer and strides), which is the in-place case. Two
+ * views overlap when they could address a common element; Q and K views
+ * that interleave token by token (packed QKV) without sharing elements are
+ * accepted.
+ * Errors: as rope_fwd_qk; ROPE_ERR_SHAPE also for negative strides or a
+ * table stride that cannot hold R/2 frequencies; ROPE_ERR_LAYOUT for a
+ * direction other than +-1 or a table column stride other than 1 or 2;
+ * ROPE_ERR_ALIGN when a view's data is not aligned to its element size. */
+rope_status_t rope_apply(const rope_apply_desc_t *d, void *stream);
+
 /* Fill host float32 tables cos_out/sin_out, each [table_rows, R/2] row-major,
  * with cos and sin of p * theta^(-2i/R) for row p and column i: the exponent
  * -2i/R and the angle are formed in binary64 and each entry is rounded once

@@ -46,6 +46,40 @@ class RopeDesc(ctypes.Structure):
     ]
 
 
+class RopeView(ctypes.Structure):
+    """rope_view_t: data pointer and element strides of the batch, head and
+    sequence dims (the head_dim axis is contiguous)."""
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_s", ctypes.c_int64)]
+
+
+class RopeApplyDesc(ctypes.Structure):
+    """rope_apply_desc_t of include/librope.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seq_len", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("rotary_dim", ctypes.c_int64),
+        ("n_heads_q", ctypes.c_int64),
+        ("n_heads_k", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("pairing", ctypes.c_int32),
+        ("launch", ctypes.c_int32),
+        ("direction", ctypes.c_int32),
+        ("q_in", RopeView),
+        ("k_in", RopeView),
+        ("q_out", RopeView),
+        ("k_out", RopeView),
+        ("cos", ctypes.c_void_p),
+        ("sin", ctypes.c_void_p),
+        ("table_rows", ctypes.c_int64),
+        ("table_row_stride", ctypes.c_int64),
+        ("table_col_stride", ctypes.c_int64),
+        ("pos", ctypes.c_void_p),
+        ("pos_batch_stride", ctypes.c_int64),
+    ]
+
+
 class RopeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -71,6 +105,8 @@ def lib():
         for name in ("rope_fwd_q", "rope_bwd_q"):
             getattr(L, name).argtypes = [P, D, P]
             getattr(L, name).restype = ctypes.c_int
+        L.rope_apply.argtypes = [ctypes.POINTER(RopeApplyDesc), P]
+        L.rope_apply.restype = ctypes.c_int
         L.rope_build_table.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double]
         L.rope_build_table.restype = ctypes.c_int
         L.rope_status_string.argtypes = [ctypes.c_int]
@@ -201,6 +237,102 @@ def rope_bwd_q(dq, cos, sin, *, stream=None, **kw):
     d = make_desc(dq, None, cos, sin, **kw)
     _check(lib().rope_bwd_q(dq.data_ptr(), ctypes.byref(d), _stream(stream)), "rope_bwd_q")
     return dq
+
+
+TABLE_LAYOUTS = ("half", "duplicated", "interleaved")
+
+
+def _view(t, layout: str) -> RopeView:
+    """RopeView of a 4-d torch tensor in `layout` order with a contiguous last dim."""
+    if t.dim() != 4:
+        raise ValueError("q/k views must be 4-d")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError("the head_dim axis must be contiguous (stride 1)")
+    if layout == "bhsd":
+        sb, sh, ss = t.stride(0), t.stride(1), t.stride(2)
+    else:
+        sb, ss, sh = t.stride(0), t.stride(1), t.stride(2)
+    return RopeView(t.data_ptr(), sb, sh, ss)
+
+
+def make_apply_desc(q, k, cos, sin, *, q_out=None, k_out=None, direction: int = 1,
+                    layout: str = "bhsd", pairing: str = "split_half",
+                    rotary_dim: Optional[int] = None, pos=None,
+                    pos_batch_stride: Optional[int] = None, launch: str = "auto",
+                    table_layout: str = "half") -> RopeApplyDesc:
+    """rope_apply_desc_t for (possibly strided) torch views q, k (k may be None)
+    and optional outputs q_out, k_out of the same shapes.
+
+    table_layout: "half" = [rows, R/2]; "duplicated" = [rows, R] holding
+    cat(f, f); "interleaved" = [rows, R] holding each value twice in a row.
+    The table's row stride is taken from the tensor, so row-sliced views work.
+    """
+    B, Hq, S, D = _dims(q, layout)
+    Hk = 0
+    if k is not None:
+        Bk, Hk, Sk, Dk = _dims(k, layout)
+        if (Bk, Sk, Dk) != (B, S, D) or k.dtype != q.dtype:
+            raise ValueError("k must match q in batch, seq_len, head_dim and dtype")
+    for name, o, x in (("q_out", q_out, q), ("k_out", k_out, k)):
+        if o is not None and (x is None or o.shape != x.shape or o.dtype != x.dtype):
+            raise ValueError(f"{name} must match its input's shape and dtype")
+    R = D if rotary_dim is None else int(rotary_dim)
+    import torch
+    if cos.dtype != torch.float32 or sin.dtype != torch.float32 or cos.shape != sin.shape:
+        raise ValueError("cos and sin must be matching float32 tables")
+    if cos.dim() != 2 or cos.stride(1) != 1 or sin.stride(1) != 1 or cos.stride(0) != sin.stride(0):
+        raise ValueError("cos/sin must be 2-d with contiguous rows and equal strides")
+    if table_layout not in TABLE_LAYOUTS:
+        raise ValueError(f"table_layout must be one of {TABLE_LAYOUTS}")
+    want = R // 2 if table_layout == "half" else R
+    if cos.shape[1] != want:
+        raise ValueError(f"a {table_layout!r} table has {want} columns, got {cos.shape[1]}")
+    d = RopeApplyDesc()
+    d.batch, d.seq_len, d.head_dim, d.rotary_dim = B, S, D, R
+    d.n_heads_q, d.n_heads_k = Hq, Hk
+    d.dtype = _dtype_code(q)
+    d.pairing = PAIRINGS[pairing]
+    d.launch = LAUNCHES[launch]
+    d.direction = int(direction)
+    d.q_in = _view(q, layout)
+    if k is not None:
+        d.k_in = _view(k, layout)
+    if q_out is not None:
+        d.q_out = _view(q_out, layout)
+    if k_out is not None:
+        d.k_out = _view(k_out, layout)
+    d.cos, d.sin = cos.data_ptr(), sin.data_ptr()
+    d.table_rows = cos.shape[0]
+    d.table_row_stride = cos.stride(0)
+    d.table_col_stride = 2 if table_layout == "interleaved" else 1
+    if pos is not None:
+        if pos.dtype != torch.int32 or not pos.is_contiguous():
+            raise ValueError("pos must be a contiguous int32 tensor")
+        if pos_batch_stride is None:
+            if pos.dim() == 2:
+                pos_batch_stride = pos.stride(0)
+            elif pos.numel() == S:
+                pos_batch_stride = 0
+            elif pos.numel() == B * S:
+                pos_batch_stride = S
+            else:
+                raise ValueError("pos must hold seq_len or batch*seq_len indices")
+        need = (B - 1) * pos_batch_stride + S if B > 0 and S > 0 else 0
+        if pos.numel() < need:
+            raise ValueError(f"pos holds {pos.numel()} indices, needs {need}")
+        d.pos = pos.data_ptr()
+        d.pos_batch_stride = pos_batch_stride
+    return d
+
+
+def rope_apply(q, k, cos, sin, *, stream=None, **kw):
+    """General call: strided views, optional outputs (q_out, k_out), direction
+    +1/-1, table layouts. Returns the tensors that hold the result."""
+    d = make_apply_desc(q, k, cos, sin, **kw)
+    _check(lib().rope_apply(ctypes.byref(d), _stream(stream)), "rope_apply")
+    qo = kw.get("q_out")
+    ko = kw.get("k_out")
+    return (q if qo is None else qo), (k if ko is None else ko)
 
 
 class Prepared:

@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0: rope_apply
 constexpr int kMaxDevices = 64;
 
 // Compute units per device, read once per device.
@@ -37,32 +37,49 @@ struct GpuLauncher {
   const rope::Plan& pl;
   hipStream_t st;
 
-  template <typename T, int V, int PAIR, bool AL>
-  hipError_t run() {
+  template <typename T, int V, int PAIR, bool AL, bool OOP>
+  void launch() {
     const dim3 grid((unsigned)pl.grid), block((unsigned)pl.block);
     if (pl.token && pl.single)
-      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, true>), grid, block, 0, st, pl.a);
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, true, OOP>), grid, block, 0,
+                         st, pl.a);
     else if (pl.token)
-      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, false>), grid, block, 0, st, pl.a);
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, false, OOP>), grid, block, 0,
+                         st, pl.a);
     else
-      hipLaunchKernelGGL((rope::rope_rows_kernel<T, V, PAIR, AL, 4>), grid, block, 0, st, pl.a);
+      hipLaunchKernelGGL((rope::rope_rows_kernel<T, V, PAIR, AL, 4, OOP>), grid, block, 0, st,
+                         pl.a);
+  }
+
+  template <typename T, int V, int PAIR, bool AL>
+  hipError_t run() {
+    if (pl.oop)
+      launch<T, V, PAIR, AL, true>();
+    else
+      launch<T, V, PAIR, AL, false>();
     return hipGetLastError();
   }
 };
 
-rope_status_t run(void* q, void* k, const rope_desc_t* d, void* stream, bool with_k,
-                  float sin_sign) {
+rope_status_t run_apply(const rope_apply_desc_t* d, void* stream) {
   // validation first: it needs no device and touches no device memory
-  const rope_status_t vs = rope::validate(q, k, d, with_k);
+  const rope_status_t vs = rope::validate_apply(d);
   if (vs != ROPE_OK) return vs;
-  if (rope::is_empty(d, with_k ? d->n_heads_k : 0)) return ROPE_OK;
+  if (rope::apply_is_empty(d)) return ROPE_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ROPE_ERR_HIP;
   rope::Plan pl;
-  const rope_status_t ps = rope::make_plan(q, k, d, with_k, sin_sign, cu_count(dev), &pl);
+  const rope_status_t ps = rope::make_plan_apply(d, cu_count(dev), &pl);
   if (ps != ROPE_OK || pl.empty) return ps;
   GpuLauncher launcher{pl, static_cast<hipStream_t>(stream)};
   return rope::dispatch(pl, launcher) == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+}
+
+rope_status_t run(void* q, void* k, const rope_desc_t* d, void* stream, bool with_k,
+                  int direction) {
+  rope_apply_desc_t a;
+  const rope_status_t st = rope::desc_to_apply(q, k, d, with_k, direction, &a);
+  return st != ROPE_OK ? st : run_apply(&a, stream);
 }
 
 }  // namespace
@@ -70,20 +87,22 @@ rope_status_t run(void* q, void* k, const rope_desc_t* d, void* stream, bool wit
 extern "C" {
 
 rope_status_t rope_fwd_qk(void* q, void* k, const rope_desc_t* d, void* stream) {
-  return run(q, k, d, stream, true, 1.0f);
+  return run(q, k, d, stream, true, 1);
 }
 
 rope_status_t rope_bwd_qk(void* dq, void* dk, const rope_desc_t* d, void* stream) {
-  return run(dq, dk, d, stream, true, -1.0f);
+  return run(dq, dk, d, stream, true, -1);
 }
 
 rope_status_t rope_fwd_q(void* q, const rope_desc_t* d, void* stream) {
-  return run(q, nullptr, d, stream, false, 1.0f);
+  return run(q, nullptr, d, stream, false, 1);
 }
 
 rope_status_t rope_bwd_q(void* dq, const rope_desc_t* d, void* stream) {
-  return run(dq, nullptr, d, stream, false, -1.0f);
+  return run(dq, nullptr, d, stream, false, -1);
 }
+
+rope_status_t rope_apply(const rope_apply_desc_t* d, void* stream) { return run_apply(d, stream); }
 
 rope_status_t rope_build_table(float* cos_out, float* sin_out, int64_t table_rows,
                                int64_t rotary_dim, double theta) {

@@ -4,10 +4,10 @@
 // (16-bit) and does ~10 float ops on it, so it is bound by HBM bandwidth
 // ("Rotary Embedding Kernel", Overview: memory-bound, judged in GB/s). The
 // kernels therefore aim at three things only: whole-row 128-bit loads and
-// stores, cos/sin read once per token and reused for every Q and K head of
+// stores, cos/sin read once per token and reused for several Q and K heads of
 // that token (the reuse that head grouping buys in How Unsloth Optimizes RoPE
 // Embedding Computations in Triton Kernels, Triton Kernel Architecture for
-// RoPE), and enough loads in flight per CU to cover HBM latency.
+// RoPE), and an HBM access order that streams well on MI355X.
 //
 // Work unit. A token row of R rotated dims is cut into `lanes` chunks of V
 // contiguous elements per access:
@@ -16,12 +16,16 @@
 // ("Rotary Embedding Kernel", Paired Element Layout). A lane owns one chunk of
 // one token and holds that chunk's cos/sin in registers.
 //
-// Two grid shapes share the same per-chunk device function:
+// Tensors are strided views [batch, head, seq, dim] with a contiguous dim
+// axis, read from an input view and written to an output view; in place the
+// output is the input. Out of place (OOP), the lanes also copy the dims >= R
+// and the rows of skipped tokens, so the output is complete.
+//
+// Two grid shapes share the same per-chunk device functions:
 //   rope_rows_kernel  : lanes over (token, chunk); each lane walks a group of
 //                       heads (Q heads first, then K heads). For prefill.
 //   rope_token_kernel : one token per workgroup iteration, lanes over (head,
-//                       chunk). For decode (seq_len 1), where there are too
-//                       few tokens to fill the chip with the first shape.
+//                       chunk). For decode (seq_len 1) and small calls.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,14 +43,21 @@ enum Pairing : int { kSplitHalf = 0, kInterleaved = 1 };
 ROPE_HD int imin(int x, int y) { return x < y ? x : y; }
 ROPE_HD int imax(int x, int y) { return x > y ? x : y; }
 
+// A strided 4-d view: element (b, h, s, j) at base + b*sb + h*sh + s*ss + j.
+struct View {
+  char* base;
+  int64_t sb, sh, ss;  // element strides
+};
+
 // Everything a launch needs, passed by value as the kernel argument.
 struct Args {
-  char* q;  // Q base (bytes)
-  char* k;  // K base (bytes); unused when n_heads_k == 0
-  int64_t q_sb, q_sh, q_ss;  // Q element strides: batch, head, sequence
-  int64_t k_sb, k_sh, k_ss;  // K element strides
-  const float* cos;          // [table_rows, half]
+  View q_in, k_in;           // K views unused when n_heads_k == 0
+  View q_out, k_out;         // equal to the inputs in place
+  const float* cos;          // frequency i of position p at [p*t_row + i*t_col]
   const float* sin;
+  int64_t t_row;             // table row stride (floats)
+  int32_t t_col;             // table column stride (1 or 2)
+  int32_t t_vec;             // 1: a chunk's cos/sin are contiguous and aligned
   const int32_t* pos;        // nullptr: p = s
   int64_t pos_bs;            // index batch stride
   int64_t table_rows;
@@ -54,7 +65,8 @@ struct Args {
   int64_t seq_len;
   int64_t n_tokens;          // batch * seq_len
   int64_t n_items;           // n_tokens * lanes (rows kernel)
-  int32_t half;              // R / 2: cos/sin row length
+  int32_t head_dim;          // D (out-of-place copies)
+  int32_t half;              // R / 2
   int32_t n_heads_q;
   int32_t n_heads_k;
   int32_t lanes;             // chunks per token row
@@ -146,8 +158,7 @@ template <typename T, bool ALIGNED> struct Chunk<T, 1, ALIGNED> {
 // float32 result stays within about one float32 ulp of the exact value, so
 // the 16-bit rounding that follows lands on the nearest or an adjacent value.
 // sn already carries the direction: +sin forward, -sin backward.
-ROPE_HD void rotate_pair(float x1, float x2, float c, float sn,
-                                            float& y1, float& y2) {
+ROPE_HD void rotate_pair(float x1, float x2, float c, float sn, float& y1, float& y2) {
   const float p1 = x2 * sn;
   const float e1 = __builtin_fmaf(x2, sn, -p1);  // x2*sn - p1, exact
   y1 = __builtin_fmaf(x1, c, -p1) - e1;          // x1*c - x2*sn
@@ -156,38 +167,48 @@ ROPE_HD void rotate_pair(float x1, float x2, float c, float sn,
   y2 = __builtin_fmaf(x2, c, p2) + e2;           // x1*sn + x2*c
 }
 
-// Pairs per chunk and the chunk's column in the cos/sin row.
+// Pairs per chunk.
 template <int V, int PAIR> struct ChunkGeom {
   static constexpr int kPairs = PAIR == kSplitHalf ? V : V / 2;
 };
 
-// cos/sin of one chunk: kPairs consecutive floats of row p. The row length
-// (R/2) is a multiple of kPairs and the tables are 16-byte aligned, so the
-// slice is aligned to min(16, 4 * kPairs) bytes and moves in vector loads.
+// cos/sin of one chunk: frequencies first .. first+NP-1 of row p. With a
+// [rows, R/2] (or halves-duplicated [rows, R]) table these are NP contiguous
+// floats, aligned to min(16, 4*NP) bytes (the tables are 16-byte aligned and
+// the plan checks that the row stride keeps them so), and move in vector
+// loads; a repeat-interleaved table is read one value at a time.
 template <int V, int PAIR> struct Trig {
   static constexpr int NP = ChunkGeom<V, PAIR>::kPairs;
-  static constexpr int W = NP < 4 ? NP : 4;  // floats per load
+  static constexpr int W = NP < 4 ? NP : 4;  // floats per vector load
   typedef float vec_t __attribute__((ext_vector_type(W)));
   float c[NP], s[NP];
 
-  ROPE_HD void load(const float* cos_row, const float* sin_row, int col,
-                                       float sign) {
+  ROPE_HD void load(const Args& a, int64_t p, int first) {
+    const float* cr = a.cos + p * a.t_row;
+    const float* sr = a.sin + p * a.t_row;
+    if (a.t_vec) {
 #pragma unroll
-    for (int j = 0; j < NP; j += W) {
-      const vec_t cv = *reinterpret_cast<const vec_t*>(cos_row + col + j);
-      const vec_t sv = *reinterpret_cast<const vec_t*>(sin_row + col + j);
+      for (int j = 0; j < NP; j += W) {
+        const vec_t cv = *reinterpret_cast<const vec_t*>(cr + first + j);
+        const vec_t sv = *reinterpret_cast<const vec_t*>(sr + first + j);
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        c[j + w] = cv[w];
-        s[j + w] = sign * sv[w];
+        for (int w = 0; w < W; ++w) {
+          c[j + w] = cv[w];
+          s[j + w] = a.sin_sign * sv[w];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        c[j] = cr[(int64_t)(first + j) * a.t_col];
+        s[j] = a.sin_sign * sr[(int64_t)(first + j) * a.t_col];
       }
     }
   }
 };
 
-// Rotate one chunk of a row in place.
-//   row : first element of the head row
-//   c   : chunk index
+// One chunk of a row: load from the input row, rotate, store to the output row.
+//   c : chunk index; half = R/2
 template <typename T, int V, int PAIR, bool ALIGNED> struct RowChunk {
   static constexpr int NP = ChunkGeom<V, PAIR>::kPairs;
   Chunk<T, V, ALIGNED> a;  // split: first half; interleaved: the chunk
@@ -232,13 +253,24 @@ template <typename T, int V, int PAIR, bool ALIGNED> struct RowChunk {
   }
 };
 
-// Row start of head h (Q heads first, then K heads) for token (b, s).
+// Out of place only: copy dims [from, to) of a row, lane c of `lanes` taking
+// V-element chunks c, c+lanes, ... and lane 0 the elements past the last
+// whole chunk (only when V does not divide the span).
+template <typename T, int V, bool ALIGNED>
+ROPE_HD void copy_span(const T* in, T* out, int from, int to, int c, int lanes) {
+  const int n = (to - from) / V;
+  for (int k = c; k < n; k += lanes) {
+    Chunk<T, V, ALIGNED> x;
+    x.load(in + from + k * V);
+    x.store(out + from + k * V);
+  }
+  if (c == 0)
+    for (int j = from + n * V; j < to; ++j) stream_store(stream_load(in + j), out + j);
+}
+
 template <typename T>
-ROPE_HD T* head_row(const Args& a, int h, int64_t b, int64_t s) {
-  if (h < a.n_heads_q)
-    return reinterpret_cast<T*>(a.q) + (b * a.q_sb + (int64_t)h * a.q_sh + s * a.q_ss);
-  return reinterpret_cast<T*>(a.k) +
-         (b * a.k_sb + (int64_t)(h - a.n_heads_q) * a.k_sh + s * a.k_ss);
+ROPE_HD T* view_row(const View& v, int64_t h, int64_t b, int64_t s) {
+  return reinterpret_cast<T*>(v.base) + (b * v.sb + h * v.sh + s * v.ss);
 }
 
 // Position of token (b, s), or -1 when the token passes through.
@@ -248,36 +280,51 @@ ROPE_HD int64_t token_pos(const Args& a, int64_t b, int64_t s) {
 }
 
 // ------------------------------------------------------ rows (prefill) shape
-// Rotate one lane's chunk in heads [h_lo, h_hi) of one tensor whose rows for
-// this token start at `base` and are `stride` elements apart. U heads are
-// loaded before any is rotated so that U row loads are in flight at once.
-template <typename T, int V, int PAIR, bool ALIGNED, int U>
-ROPE_HD void rotate_heads(T* base, int64_t stride, int h_lo, int h_hi,
-                                             int c, int half, const Trig<V, PAIR>& t) {
+// Rotate one lane's chunk in heads [h_lo, h_hi) of one tensor, whose rows for
+// this token start at `in` / `out` and are `sh_in` / `sh_out` elements apart.
+// U heads are loaded before any is rotated so U row loads are in flight.
+template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP>
+ROPE_HD void rotate_heads(const Args& a, const T* in, int64_t sh_in, T* out, int64_t sh_out,
+                          int h_lo, int h_hi, int c, const Trig<V, PAIR>& t) {
   for (int h0 = h_lo; h0 < h_hi; h0 += U) {
     RowChunk<T, V, PAIR, ALIGNED> r[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (h0 + u < h_hi) r[u].load(base + (int64_t)(h0 + u) * stride, c, half);
+      if (h0 + u < h_hi) r[u].load(in + (int64_t)(h0 + u) * sh_in, c, a.half);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (h0 + u < h_hi) {
         r[u].rotate(t);
-        r[u].store(base + (int64_t)(h0 + u) * stride, c, half);
+        r[u].store(out + (int64_t)(h0 + u) * sh_out, c, a.half);
       }
     }
+    if constexpr (OOP) {
+      for (int u = 0; u < U && h0 + u < h_hi; ++u)
+        copy_span<T, V, ALIGNED>(in + (int64_t)(h0 + u) * sh_in,
+                                 out + (int64_t)(h0 + u) * sh_out, 2 * a.half, a.head_dim,
+                                 c, a.lanes);
+    }
   }
+}
+
+// Out of place, a skipped token's rows are copied whole.
+template <typename T, int V, bool ALIGNED>
+ROPE_HD void copy_heads(const Args& a, const T* in, int64_t sh_in, T* out, int64_t sh_out,
+                        int h_lo, int h_hi, int c) {
+  for (int h = h_lo; h < h_hi; ++h)
+    copy_span<T, V, ALIGNED>(in + (int64_t)h * sh_in, out + (int64_t)h * sh_out, 0,
+                             a.head_dim, c, a.lanes);
 }
 
 // Tokens are numbered in memory order (n = b * seq_len + s), so in the [B,H,S,D]
 // layout the 4 waves of a workgroup cover 32 consecutive rows (8 KiB at
 // D=128, bf16) of each head they visit. Workgroup ids run over (tile, head
-// group) with the group fastest, and are left in the hardware's round-robin
-// order over the XCDs: renumbering them so that each XCD owns one contiguous
-// range of tiles was measured ~10% slower.
+// group), in either order (group_slow: all tiles of group 0 first), and are
+// left in the hardware's round-robin order over the XCDs: renumbering them so
+// that each XCD owns one contiguous range of tiles was measured ~10% slower.
 constexpr int kRowsBlock = 256;
 
-template <typename T, int V, int PAIR, bool ALIGNED, int U>
+template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP>
 ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
   int64_t tile;
   int group;
@@ -295,29 +342,39 @@ ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
   const int64_t b = n / a.seq_len;
   const int64_t s = n - b * a.seq_len;
 
-  const int64_t p = token_pos(a, b, s);
-  if (p < 0) return;  // masked token: nothing is read or written
-
-  Trig<V, PAIR> t;
-  t.load(a.cos + p * a.half, a.sin + p * a.half, c * ChunkGeom<V, PAIR>::kPairs, a.sin_sign);
-
   const int h_begin = group * a.heads_per_group;
   const int h_end = imin(h_begin + a.heads_per_group, a.n_heads_q + a.n_heads_k);
-  if (h_begin < a.n_heads_q) {
-    T* qb = reinterpret_cast<T*>(a.q) + (b * a.q_sb + s * a.q_ss);
-    rotate_heads<T, V, PAIR, ALIGNED, U>(qb, a.q_sh, h_begin, imin(h_end, a.n_heads_q), c,
-                                         a.half, t);
+  const int q_lo = h_begin, q_hi = imin(h_end, a.n_heads_q);
+  const int k_lo = imax(h_begin - a.n_heads_q, 0), k_hi = h_end - a.n_heads_q;
+  const T* qi = view_row<T>(a.q_in, 0, b, s);
+  T* qo = view_row<T>(a.q_out, 0, b, s);
+  const T* ki = view_row<T>(a.k_in, 0, b, s);
+  T* ko = view_row<T>(a.k_out, 0, b, s);
+
+  const int64_t p = token_pos(a, b, s);
+  if (p < 0) {  // skipped token: in place nothing is read or written
+    if constexpr (OOP) {
+      if (q_lo < q_hi)
+        copy_heads<T, V, ALIGNED>(a, qi, a.q_in.sh, qo, a.q_out.sh, q_lo, q_hi, c);
+      if (k_lo < k_hi)
+        copy_heads<T, V, ALIGNED>(a, ki, a.k_in.sh, ko, a.k_out.sh, k_lo, k_hi, c);
+    }
+    return;
   }
-  if (h_end > a.n_heads_q) {
-    T* kb = reinterpret_cast<T*>(a.k) + (b * a.k_sb + s * a.k_ss);
-    rotate_heads<T, V, PAIR, ALIGNED, U>(kb, a.k_sh, imax(h_begin - a.n_heads_q, 0),
-                                         h_end - a.n_heads_q, c, a.half, t);
-  }
+
+  Trig<V, PAIR> t;
+  t.load(a, p, c * ChunkGeom<V, PAIR>::kPairs);
+  if (q_lo < q_hi)
+    rotate_heads<T, V, PAIR, ALIGNED, U, OOP>(a, qi, a.q_in.sh, qo, a.q_out.sh, q_lo, q_hi, c,
+                                              t);
+  if (k_lo < k_hi)
+    rotate_heads<T, V, PAIR, ALIGNED, U, OOP>(a, ki, a.k_in.sh, ko, a.k_out.sh, k_lo, k_hi, c,
+                                              t);
 }
 
-template <typename T, int V, int PAIR, bool ALIGNED, int U>
+template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP>
 __global__ void __launch_bounds__(kRowsBlock) rope_rows_kernel(Args a) {
-  rows_body<T, V, PAIR, ALIGNED, U>(a, blockIdx.x, threadIdx.x);
+  rows_body<T, V, PAIR, ALIGNED, U, OOP>(a, blockIdx.x, threadIdx.x);
 }
 
 // ------------------------------------------------------ token (decode) shape
@@ -334,41 +391,49 @@ ROPE_HD void split_item(const Args& a, int it, int* h, int* c) {
   }
 }
 
-template <typename T, int V, int PAIR, bool ALIGNED>
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP>
 ROPE_HD void token_item(const Args& a, int64_t n, int it) {
   const int64_t b = n / a.seq_len;
   const int64_t s = n - b * a.seq_len;
   int h, c;
   split_item(a, it, &h, &c);
-  T* row = head_row<T>(a, h, b, s);
+  const bool is_q = h < a.n_heads_q;
+  const int hh = is_q ? h : h - a.n_heads_q;
+  const T* in = view_row<T>(is_q ? a.q_in : a.k_in, hh, b, s);
+  T* out = view_row<T>(is_q ? a.q_out : a.k_out, hh, b, s);
   RowChunk<T, V, PAIR, ALIGNED> r;
-  r.load(row, c, a.half);
+  r.load(in, c, a.half);
   const int64_t p = token_pos(a, b, s);
-  if (p < 0) return;
+  if (p < 0) {
+    if constexpr (OOP) copy_span<T, V, ALIGNED>(in, out, 0, a.head_dim, c, a.lanes);
+    return;
+  }
   Trig<V, PAIR> t;
-  t.load(a.cos + p * a.half, a.sin + p * a.half, c * ChunkGeom<V, PAIR>::kPairs, a.sin_sign);
+  t.load(a, p, c * ChunkGeom<V, PAIR>::kPairs);
   r.rotate(t);
-  r.store(row, c, a.half);
+  r.store(out, c, a.half);
+  if constexpr (OOP) copy_span<T, V, ALIGNED>(in, out, 2 * a.half, a.head_dim, c, a.lanes);
 }
 
 // SINGLE: the grid has one workgroup per token and each workgroup one lane
 // per (head, chunk), so no loop is needed (the decode case).
-template <typename T, int V, int PAIR, bool ALIGNED, bool SINGLE>
+template <typename T, int V, int PAIR, bool ALIGNED, bool SINGLE, bool OOP>
 ROPE_HD void token_body(const Args& a, int64_t block, int64_t grid, int thread,
                         int block_dim) {
   const int per_token = (a.n_heads_q + a.n_heads_k) * a.lanes;
   if constexpr (SINGLE) {
-    if (thread < per_token) token_item<T, V, PAIR, ALIGNED>(a, block, thread);
+    if (thread < per_token) token_item<T, V, PAIR, ALIGNED, OOP>(a, block, thread);
   } else {
     for (int64_t n = block; n < a.n_tokens; n += grid)
       for (int it = thread; it < per_token; it += block_dim)
-        token_item<T, V, PAIR, ALIGNED>(a, n, it);
+        token_item<T, V, PAIR, ALIGNED, OOP>(a, n, it);
   }
 }
 
-template <typename T, int V, int PAIR, bool ALIGNED, bool SINGLE>
+template <typename T, int V, int PAIR, bool ALIGNED, bool SINGLE, bool OOP>
 __global__ void __launch_bounds__(1024) rope_token_kernel(Args a) {
-  token_body<T, V, PAIR, ALIGNED, SINGLE>(a, blockIdx.x, gridDim.x, threadIdx.x, blockDim.x);
+  token_body<T, V, PAIR, ALIGNED, SINGLE, OOP>(a, blockIdx.x, gridDim.x, threadIdx.x,
+                                               blockDim.x);
 }
 
 }  // namespace rope

@@ -2,6 +2,10 @@
 // access width, and the grid shape. No GPU calls happen here, so the same
 // plan drives the real launch (librope.hip) and the host emulation of the
 // kernels used to check index arithmetic and bounds on the CPU.
+//
+// Every call is first put in the general form of rope_apply (strided input
+// and output views, table strides, direction); the contiguous entry points
+// only fill that form from their layout.
 #pragma once
 
 #include <stdint.h>
@@ -22,110 +26,267 @@ struct Plan {
   int block;       // lanes per workgroup
   bool empty;      // nothing to do
   bool single;     // token shape: one workgroup per token, one lane per item
+  bool oop;        // some output differs from its input
 };
 
 inline int64_t elem_bytes(int32_t dtype) { return dtype == ROPE_F32 ? 4 : 2; }
 
-inline bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
-  if (na == 0 || nb == 0) return false;
-  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+inline bool apply_is_empty(const rope_apply_desc_t* d) {
+  return d->batch == 0 || d->seq_len == 0 || d->rotary_dim == 0 ||
+         d->n_heads_q + d->n_heads_k == 0;
 }
 
-inline bool is_empty(const rope_desc_t* d, int64_t hk) {
-  return d->batch == 0 || d->seq_len == 0 || d->rotary_dim == 0 || d->n_heads_q + hk == 0;
+// ------------------------------------------------------------------ views
+// A view with its extents [B, H, S, D], for the overlap and width checks.
+struct ViewX {
+  uintptr_t p;
+  int64_t sb, sh, ss;
+  int64_t B, H, S, D;
+};
+
+inline ViewX view_x(const rope_view_t& v, int64_t B, int64_t H, int64_t S, int64_t D) {
+  return ViewX{reinterpret_cast<uintptr_t>(v.data), v.stride_b, v.stride_h, v.stride_s,
+               B, H, S, D};
 }
 
+inline bool view_empty(const ViewX& v) { return !v.B || !v.H || !v.S || !v.D; }
+
+// Elements from the first to one past the last addressed element.
+inline int64_t view_span(const ViewX& v) {
+  if (view_empty(v)) return 0;
+  return (v.B - 1) * v.sb + (v.H - 1) * v.sh + (v.S - 1) * v.ss + v.D;
+}
+
+// Sufficient condition for no two (b, h, s, j) to share an element: ordered
+// by stride, every dim of extent > 1 steps over everything the smaller ones
+// cover. All the usual layouts ([B,H,S,D], [B,S,H,D], views into packed QKV)
+// satisfy it.
+inline bool view_injective(const ViewX& v) {
+  if (view_empty(v)) return true;
+  int64_t st[3] = {v.sb, v.sh, v.ss}, ex[3] = {v.B, v.H, v.S};
+  for (int i = 0; i < 3; ++i)  // sort the three dims by stride
+    for (int j = i + 1; j < 3; ++j)
+      if (st[j] < st[i]) {
+        const int64_t t0 = st[i], t1 = ex[i];
+        st[i] = st[j], ex[i] = ex[j];
+        st[j] = t0, ex[j] = t1;
+      }
+  int64_t covered = v.D;
+  for (int i = 0; i < 3; ++i) {
+    if (ex[i] <= 1) continue;
+    if (st[i] < covered) return false;
+    covered += (ex[i] - 1) * st[i];
+  }
+  return true;
+}
+
+inline bool same_view(const ViewX& a, const ViewX& b) {
+  return a.p == b.p && a.sb == b.sb && a.sh == b.sh && a.ss == b.ss && a.B == b.B &&
+         a.H == b.H && a.S == b.S && a.D == b.D;
+}
+
+// Token period of a view: the stride between consecutive tokens' cells, or 0
+// when its tokens do not tile memory with one period.
+inline int64_t token_period(const ViewX& v) {
+  if (v.S > 1) {
+    if (v.B > 1 && (v.ss <= 0 || v.sb % v.ss != 0)) return 0;
+    return v.ss;
+  }
+  return v.B > 1 ? v.sb : 0;
+}
+
+// True when the two views cannot address a common element. Byte ranges that
+// do not meet are disjoint; so are views that interleave token by token
+// (packed QKV): same token period P, each view's heads inside a cell of P
+// elements, and the second view's cell span falling entirely beside the
+// first's.
+inline bool views_disjoint(const ViewX& a, const ViewX& b, int64_t e) {
+  if (view_empty(a) || view_empty(b)) return true;
+  const uintptr_t a0 = a.p, a1 = a.p + (uintptr_t)(view_span(a) * e);
+  const uintptr_t b0 = b.p, b1 = b.p + (uintptr_t)(view_span(b) * e);
+  if (a1 <= b0 || b1 <= a0) return true;
+  const int64_t P = token_period(a);
+  if (P <= 0 || P != token_period(b)) return false;
+  const int64_t ext_a = (a.H - 1) * a.sh + a.D, ext_b = (b.H - 1) * b.sh + b.D;
+  if (ext_a > P || ext_b > P) return false;
+  const int64_t delta_bytes = (int64_t)(b.p - a.p);  // two's complement wrap is fine
+  if (delta_bytes % e) return false;
+  int64_t r = (delta_bytes / e) % P;
+  if (r < 0) r += P;
+  return r >= ext_a && r + ext_b <= P;
+}
+
+// ------------------------------------------------------------ validation
 // Checks that need no GPU and never dereference a device pointer.
-inline rope_status_t validate(const void* q, const void* k, const rope_desc_t* d, bool with_k) {
+inline rope_status_t validate_apply(const rope_apply_desc_t* d) {
   if (!d) return ROPE_ERR_NULL;
   if (d->dtype < ROPE_F32 || d->dtype > ROPE_BF16) return ROPE_ERR_DTYPE;
-  if (d->layout != ROPE_BHSD && d->layout != ROPE_BSHD) return ROPE_ERR_LAYOUT;
   if (d->pairing != ROPE_SPLIT_HALF && d->pairing != ROPE_INTERLEAVED) return ROPE_ERR_LAYOUT;
   if (d->launch < ROPE_LAUNCH_AUTO || d->launch > ROPE_LAUNCH_TOKEN) return ROPE_ERR_LAYOUT;
-  const int64_t hk = with_k ? d->n_heads_k : 0;
+  if (d->direction != 1 && d->direction != -1) return ROPE_ERR_LAYOUT;
+  if (d->table_col_stride != 1 && d->table_col_stride != 2) return ROPE_ERR_LAYOUT;
+  const int64_t hk = d->n_heads_k;
   if (d->batch < 0 || d->n_heads_q < 0 || d->seq_len < 0 || d->head_dim < 0 ||
       d->rotary_dim < 0 || d->table_rows < 0 || hk < 0)
     return ROPE_ERR_SHAPE;
   if ((d->rotary_dim & 1) || d->rotary_dim > d->head_dim) return ROPE_ERR_SHAPE;
-  if (with_k && hk > d->n_heads_q) return ROPE_ERR_SHAPE;
+  if (hk > d->n_heads_q) return ROPE_ERR_SHAPE;
   // heads and dims index with 32-bit integers inside the kernels
-  if (d->n_heads_q + hk > ((int64_t)1 << 30) || d->rotary_dim > ((int64_t)1 << 30))
+  if (d->n_heads_q + hk > ((int64_t)1 << 30) || d->head_dim > ((int64_t)1 << 30))
     return ROPE_ERR_SHAPE;
-  if (is_empty(d, hk)) return ROPE_OK;
+  if (apply_is_empty(d)) return ROPE_OK;
   if (!d->pos && d->seq_len > d->table_rows) return ROPE_ERR_SHAPE;
   if (d->pos && d->pos_batch_stride < 0) return ROPE_ERR_SHAPE;
-  if ((d->n_heads_q > 0 && !q) || (hk > 0 && !k) || !d->cos || !d->sin) return ROPE_ERR_NULL;
+  const rope_view_t* views[4] = {&d->q_in, &d->k_in, &d->q_out, &d->k_out};
+  for (const rope_view_t* v : views)
+    if (v->stride_b < 0 || v->stride_h < 0 || v->stride_s < 0) return ROPE_ERR_SHAPE;
+  const int64_t half = d->rotary_dim / 2;
+  const int64_t t_row = d->table_row_stride ? d->table_row_stride : half;
+  if (t_row < 0 || t_row < (half - 1) * d->table_col_stride + 1) return ROPE_ERR_SHAPE;
+  if ((d->n_heads_q > 0 && !d->q_in.data) || (hk > 0 && !d->k_in.data) || !d->cos || !d->sin)
+    return ROPE_ERR_NULL;
   const int64_t e = elem_bytes(d->dtype);
-  if ((reinterpret_cast<uintptr_t>(q) % e) || (hk > 0 && reinterpret_cast<uintptr_t>(k) % e))
-    return ROPE_ERR_ALIGN;
+  for (const rope_view_t* v : views)
+    if (reinterpret_cast<uintptr_t>(v->data) % e) return ROPE_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(d->cos) % 16) || (reinterpret_cast<uintptr_t>(d->sin) % 16) ||
       (reinterpret_cast<uintptr_t>(d->pos) % 4))
     return ROPE_ERR_ALIGN;
-  const int64_t row = d->batch * d->seq_len * d->head_dim * e;
-  if (with_k && ranges_overlap(q, row * d->n_heads_q, k, row * hk)) return ROPE_ERR_ALIAS;
+
+  // Written views (an output, or the input itself in place) must not address
+  // one element twice, must not overlap each other, and must not overlap any
+  // input other than their own identical input.
+  const int64_t B = d->batch, S = d->seq_len, D = d->head_dim;
+  const ViewX qi = view_x(d->q_in, B, d->n_heads_q, S, D);
+  const ViewX ki = view_x(d->k_in, B, hk, S, D);
+  const ViewX qo = d->q_out.data ? view_x(d->q_out, B, d->n_heads_q, S, D) : qi;
+  const ViewX ko = d->k_out.data ? view_x(d->k_out, B, hk, S, D) : ki;
+  if (!view_injective(qo) || !view_injective(ko)) return ROPE_ERR_ALIAS;
+  if (!views_disjoint(qo, ko, e)) return ROPE_ERR_ALIAS;
+  if (!same_view(qo, qi) && !views_disjoint(qo, qi, e)) return ROPE_ERR_ALIAS;
+  if (!same_view(ko, ki) && !views_disjoint(ko, ki, e)) return ROPE_ERR_ALIAS;
+  if (!views_disjoint(qo, ki, e) || !views_disjoint(ko, qi, e)) return ROPE_ERR_ALIAS;
   return ROPE_OK;
 }
 
+// The contiguous entry points in the general form: strides from the layout,
+// outputs in place, a [table_rows, R/2] table.
+inline rope_status_t desc_to_apply(const void* q, const void* k, const rope_desc_t* d,
+                                   bool with_k, int direction, rope_apply_desc_t* out) {
+  if (!d) return ROPE_ERR_NULL;
+  if (d->dtype < ROPE_F32 || d->dtype > ROPE_BF16) return ROPE_ERR_DTYPE;
+  if (d->layout != ROPE_BHSD && d->layout != ROPE_BSHD) return ROPE_ERR_LAYOUT;
+  rope_apply_desc_t a{};
+  a.batch = d->batch;
+  a.seq_len = d->seq_len;
+  a.head_dim = d->head_dim;
+  a.rotary_dim = d->rotary_dim;
+  a.n_heads_q = d->n_heads_q;
+  a.n_heads_k = with_k ? d->n_heads_k : 0;
+  a.dtype = d->dtype;
+  a.pairing = d->pairing;
+  a.launch = d->launch;
+  a.direction = direction;
+  const int64_t S = d->seq_len, D = d->head_dim;
+  const int64_t heads[2] = {d->n_heads_q, a.n_heads_k};
+  rope_view_t* views[2] = {&a.q_in, &a.k_in};
+  const void* data[2] = {q, with_k ? k : nullptr};
+  for (int i = 0; i < 2; ++i) {
+    rope_view_t& v = *views[i];
+    v.data = const_cast<void*>(data[i]);
+    if (d->layout == ROPE_BHSD) {  // [B, H, S, D]
+      v.stride_b = heads[i] * S * D;
+      v.stride_h = S * D;
+      v.stride_s = D;
+    } else {  // [B, S, H, D]
+      v.stride_b = S * heads[i] * D;
+      v.stride_s = heads[i] * D;
+      v.stride_h = D;
+    }
+  }
+  a.cos = d->cos;
+  a.sin = d->sin;
+  a.table_rows = d->table_rows;
+  a.table_row_stride = 0;
+  a.table_col_stride = 1;
+  a.pos = d->pos;
+  a.pos_batch_stride = d->pos_batch_stride;
+  *out = a;
+  return ROPE_OK;
+}
+
+inline rope_status_t validate(const void* q, const void* k, const rope_desc_t* d, bool with_k) {
+  rope_apply_desc_t a;
+  const rope_status_t st = desc_to_apply(q, k, d, with_k, 1, &a);
+  return st != ROPE_OK ? st : validate_apply(&a);
+}
+
+// ------------------------------------------------------------------ plan
 // Largest access width V (elements, a power of two, at most 16 bytes) that
-// keeps every chunk access V-aligned: V must divide the head dim, the span
-// that chunks tile (R/2 for split-half, R for interleaved) and the element
-// offset of each base pointer.
-inline int pick_vec(const rope_desc_t* d, const void* q, const void* k, int64_t hk) {
+// keeps every chunk access V-aligned: V must divide the span that chunks
+// tile (R/2 for split-half, R for interleaved), the element offset of every
+// view and every stride of a dim with more than one index.
+inline int pick_vec(const rope_apply_desc_t* d) {
   const int64_t e = elem_bytes(d->dtype);
   const int64_t span = d->pairing == ROPE_SPLIT_HALF ? d->rotary_dim / 2 : d->rotary_dim;
-  const uintptr_t qa = reinterpret_cast<uintptr_t>(q) / e;
-  const uintptr_t ka = hk > 0 ? reinterpret_cast<uintptr_t>(k) / e : 0;
+  const int64_t heads[4] = {d->n_heads_q, d->n_heads_k, d->n_heads_q, d->n_heads_k};
+  const rope_view_t* views[4] = {&d->q_in, &d->k_in, &d->q_out, &d->k_out};
   int v = (int)(16 / e);
-  while (v > 1 && (d->head_dim % v || span % v || qa % v || ka % v)) v >>= 1;
+  auto fits = [&](int w) {
+    if (span % w) return false;
+    for (int i = 0; i < 4; ++i) {
+      const rope_view_t& x = *views[i];
+      if (!x.data || heads[i] == 0) continue;
+      if ((reinterpret_cast<uintptr_t>(x.data) / e) % w) return false;
+      if ((d->batch > 1 && x.stride_b % w) || (heads[i] > 1 && x.stride_h % w) ||
+          (d->seq_len > 1 && x.stride_s % w))
+        return false;
+    }
+    return true;
+  };
+  while (v > 1 && !fits(v)) v >>= 1;
   return v;
 }
 
-inline void set_strides(const rope_desc_t* d, int64_t heads, int64_t* sb, int64_t* sh,
-                        int64_t* ss) {
-  const int64_t S = d->seq_len, D = d->head_dim;
-  if (d->layout == ROPE_BHSD) {  // [B, H, S, D]
-    *sb = heads * S * D;
-    *sh = S * D;
-    *ss = D;
-  } else {  // [B, S, H, D]
-    *sb = S * heads * D;
-    *ss = heads * D;
-    *sh = D;
-  }
+inline View to_view(const rope_view_t& v) {
+  return View{static_cast<char*>(v.data), v.stride_b, v.stride_h, v.stride_s};
 }
 
 // Validate and plan one call. `cus` is the device's compute-unit count.
-inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with_k,
-                               float sin_sign, int cus, Plan* pl) {
-  const rope_status_t vs = validate(q, k, d, with_k);
+inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* pl) {
+  const rope_status_t vs = validate_apply(d);
   if (vs != ROPE_OK) return vs;
   *pl = Plan{};
-  const int64_t hk = with_k ? d->n_heads_k : 0;
-  pl->empty = is_empty(d, hk);
+  pl->empty = apply_is_empty(d);
   if (pl->empty) return ROPE_OK;
 
   Args& a = pl->a;
-  a.q = static_cast<char*>(q);
-  a.k = static_cast<char*>(k);
-  set_strides(d, d->n_heads_q, &a.q_sb, &a.q_sh, &a.q_ss);
-  set_strides(d, hk, &a.k_sb, &a.k_sh, &a.k_ss);
+  a.q_in = to_view(d->q_in);
+  a.k_in = to_view(d->k_in);
+  a.q_out = d->q_out.data ? to_view(d->q_out) : a.q_in;
+  a.k_out = d->k_out.data ? to_view(d->k_out) : a.k_in;
+  auto same = [](const View& x, const View& y) {
+    return x.base == y.base && x.sb == y.sb && x.sh == y.sh && x.ss == y.ss;
+  };
+  pl->oop = !same(a.q_in, a.q_out) || (d->n_heads_k > 0 && !same(a.k_in, a.k_out));
   a.cos = d->cos;
   a.sin = d->sin;
+  a.half = (int32_t)(d->rotary_dim / 2);
+  a.t_row = d->table_row_stride ? d->table_row_stride : a.half;
+  a.t_col = (int32_t)d->table_col_stride;
   a.pos = d->pos;
   a.pos_bs = d->pos_batch_stride;
   a.table_rows = d->table_rows;
   a.batch = d->batch;
   a.seq_len = d->seq_len;
   a.n_tokens = d->batch * d->seq_len;
-  a.half = (int32_t)(d->rotary_dim / 2);
+  a.head_dim = (int32_t)d->head_dim;
   a.n_heads_q = (int32_t)d->n_heads_q;
-  a.n_heads_k = (int32_t)hk;
-  a.sin_sign = sin_sign;
+  a.n_heads_k = (int32_t)d->n_heads_k;
+  a.sin_sign = (float)d->direction;
 
   pl->dtype = d->dtype;
   pl->pairing = d->pairing;
-  int v = pick_vec(d, q, k, hk);
+  int v = pick_vec(d);
   pl->aligned = true;
   if (d->pairing == ROPE_INTERLEAVED && v < 2) {
     // interleaved pairs that are not 2-element aligned: element-wise pairs
@@ -138,6 +299,11 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
   a.lanes_shift = -1;
   for (int sh = 0; sh < 31; ++sh)
     if ((int64_t)1 << sh == a.lanes) a.lanes_shift = sh;
+  // cos/sin of a chunk in vector loads: contiguous frequencies, and a row
+  // stride that keeps each chunk's slice aligned to the load width
+  const int np = d->pairing == ROPE_SPLIT_HALF ? v : v / 2;
+  const int tw = np < 4 ? np : 4;
+  a.t_vec = (a.t_col == 1 && a.t_row % tw == 0) ? 1 : 0;
   const int h_total = a.n_heads_q + a.n_heads_k;
 
   // Rows shape: 256 (token, chunk) items per workgroup, each lane walking a
@@ -169,10 +335,11 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
     // under 15% of the call's Q/K traffic (long sequences have big tables);
     // they shrink below 4 heads only when there are too few waves.
     const int64_t e = elem_bytes(d->dtype);
-    const int64_t rows_touched = d->pos ? (d->table_rows < a.n_tokens ? d->table_rows : a.n_tokens)
-                                        : d->seq_len;
+    const int64_t rows_touched =
+        d->pos ? (d->table_rows < a.n_tokens ? d->table_rows : a.n_tokens) : d->seq_len;
     const double table_pass = 4.0 * (double)d->rotary_dim * (double)rows_touched;
-    const double qk_bytes = 2.0 * (double)e * (double)d->rotary_dim * (double)a.n_tokens * h_total;
+    const double qk_bytes =
+        2.0 * (double)e * (double)d->rotary_dim * (double)a.n_tokens * h_total;
     int g = 4;
     while (g < h_total && (double)((h_total + g - 1) / g) * table_pass > 0.15 * qk_bytes) g += 4;
     if (g > h_total) g = h_total;
@@ -194,8 +361,16 @@ inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with
   return ROPE_OK;
 }
 
-// Call f.template run<T, V, PAIR, ALIGNED>() for the plan's kernel variant.
-// The variants instantiated here are all the plans above can produce.
+inline rope_status_t make_plan(void* q, void* k, const rope_desc_t* d, bool with_k,
+                               float sin_sign, int cus, Plan* pl) {
+  rope_apply_desc_t a;
+  const rope_status_t st = desc_to_apply(q, k, d, with_k, sin_sign < 0 ? -1 : 1, &a);
+  return st != ROPE_OK ? st : make_plan_apply(&a, cus, pl);
+}
+
+// Call f.template run<T, V, PAIR, ALIGNED>() for the plan's kernel variant
+// (the functor picks grid shape and in/out-of-place from the plan). The
+// variants instantiated here are all the plans above can produce.
 template <class F>
 auto dispatch(const Plan& pl, F& f) -> decltype(f.template run<float, 1, kSplitHalf, true>()) {
   const bool split = pl.pairing == ROPE_SPLIT_HALF;

@@ -69,20 +69,107 @@ void write_file(const std::string& path, const void* p, size_t bytes) {
 struct HostRunner {
   const rope::Plan& pl;
 
-  template <typename T, int V, int PAIR, bool AL>
-  int run() {
+  template <typename T, int V, int PAIR, bool AL, bool OOP>
+  void go() {
     for (int64_t blk = 0; blk < pl.grid; ++blk)
       for (int t = 0; t < pl.block; ++t) {
         if (pl.token && pl.single)
-          rope::token_body<T, V, PAIR, AL, true>(pl.a, blk, pl.grid, t, pl.block);
+          rope::token_body<T, V, PAIR, AL, true, OOP>(pl.a, blk, pl.grid, t, pl.block);
         else if (pl.token)
-          rope::token_body<T, V, PAIR, AL, false>(pl.a, blk, pl.grid, t, pl.block);
+          rope::token_body<T, V, PAIR, AL, false, OOP>(pl.a, blk, pl.grid, t, pl.block);
         else
-          rope::rows_body<T, V, PAIR, AL, 4>(pl.a, blk, t);
+          rope::rows_body<T, V, PAIR, AL, 4, OOP>(pl.a, blk, t);
       }
+  }
+
+  template <typename T, int V, int PAIR, bool AL>
+  int run() {
+    if (pl.oop)
+      go<T, V, PAIR, AL, true>();
+    else
+      go<T, V, PAIR, AL, false>();
     return 0;
   }
 };
+
+void print_plan(const rope::Plan& pl) {
+  printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
+         "heads_per_group %d\nn_groups %d\ngroup_slow %d\nsingle %d\noop %d\nt_vec %d\n",
+         (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
+         pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow, (int)pl.single,
+         (int)pl.oop, pl.a.t_vec);
+}
+
+// test-only overrides of the rows-kernel grid (head-group size and order)
+void apply_overrides(rope::Plan& pl, std::map<std::string, long long>& kv) {
+  if (!pl.empty && !pl.token && kv["heads_per_group"] > 0) {
+    const int h_total = pl.a.n_heads_q + pl.a.n_heads_k;
+    pl.a.heads_per_group = (int32_t)kv["heads_per_group"];
+    pl.a.n_groups = (h_total + pl.a.heads_per_group - 1) / pl.a.heads_per_group;
+    pl.grid = pl.a.n_tiles * pl.a.n_groups;
+  }
+  if (!pl.empty && !pl.token && kv.count("group_slow")) pl.a.group_slow = (int32_t)kv["group_slow"];
+}
+
+rope_view_t read_view(std::map<std::string, long long>& kv, const std::string& name, char* base,
+                      size_t e) {
+  rope_view_t v{};
+  if (kv[name + "_off"] < 0) return v;  // absent (in place)
+  v.data = base + (size_t)kv[name + "_off"] * e;
+  v.stride_b = kv[name + "_sb"];
+  v.stride_h = kv[name + "_sh"];
+  v.stride_s = kv[name + "_ss"];
+  return v;
+}
+
+// General form: JOB_DIR/in.bin (in_elems) holds the Q and K input views,
+// JOB_DIR/out.bin (out_elems, may be 0) the output views; cos/sin.bin hold
+// table_elems floats. Writes in_after.bin and out_after.bin.
+int apply_mode(const std::string& dir, std::map<std::string, long long>& kv) {
+  rope_apply_desc_t d{};
+  d.batch = kv["batch"];
+  d.seq_len = kv["seq_len"];
+  d.head_dim = kv["head_dim"];
+  d.rotary_dim = kv["rotary_dim"];
+  d.n_heads_q = kv["n_heads_q"];
+  d.n_heads_k = kv["n_heads_k"];
+  d.dtype = (int32_t)kv["dtype"];
+  d.pairing = (int32_t)kv["pairing"];
+  d.launch = (int32_t)kv["launch"];
+  d.direction = (int32_t)kv["direction"];
+  const size_t e = d.dtype == ROPE_F32 ? 4 : 2;
+  const size_t in_bytes = (size_t)kv["in_elems"] * e, out_bytes = (size_t)kv["out_elems"] * e;
+  char* in = static_cast<char*>(read_file(dir + "/in.bin", in_bytes, 0));
+  char* out = out_bytes ? static_cast<char*>(read_file(dir + "/out.bin", out_bytes, 0)) : nullptr;
+  d.q_in = read_view(kv, "q_in", in, e);
+  d.k_in = read_view(kv, "k_in", in, e);
+  d.q_out = read_view(kv, "q_out", out, e);
+  d.k_out = read_view(kv, "k_out", out, e);
+  const size_t tb = (size_t)kv["table_elems"] * 4;
+  d.cos = static_cast<const float*>(read_file(dir + "/cos.bin", tb, 0));
+  d.sin = static_cast<const float*>(read_file(dir + "/sin.bin", tb, 0));
+  d.table_rows = kv["table_rows"];
+  d.table_row_stride = kv["t_row"];
+  d.table_col_stride = kv["t_col"];
+  if (kv["pos_count"] > 0)
+    d.pos = static_cast<const int32_t*>(
+        read_file(dir + "/pos.bin", (size_t)kv["pos_count"] * 4, 0));
+  d.pos_batch_stride = kv["pos_batch_stride"];
+  rope::Plan pl;
+  const int cus = kv.count("cus") ? (int)kv["cus"] : 256;
+  const rope_status_t st = rope::make_plan_apply(&d, cus, &pl);
+  printf("status %d\n", (int)st);
+  if (st != ROPE_OK) return 0;
+  apply_overrides(pl, kv);
+  print_plan(pl);
+  if (!pl.empty) {
+    HostRunner runner{pl};
+    rope::dispatch(pl, runner);
+  }
+  write_file(dir + "/in_after.bin", in, in_bytes);
+  if (out_bytes) write_file(dir + "/out_after.bin", out, out_bytes);
+  return 0;
+}
 
 }  // namespace
 
@@ -93,6 +180,7 @@ int main(int argc, char** argv) {
   }
   const std::string dir = argv[1];
   auto kv = read_job(dir);
+  if (kv["apply"]) return apply_mode(dir, kv);
   rope_desc_t d{};
   d.batch = kv["batch"];
   d.n_heads_q = kv["n_heads_q"];
@@ -126,18 +214,8 @@ int main(int argc, char** argv) {
   const rope_status_t st = rope::make_plan(q, k, &d, with_k, sign, cus, &pl);
   printf("status %d\n", (int)st);
   if (st != ROPE_OK) return 0;
-  // test-only overrides of the rows-kernel grid (head-group size and order)
-  if (!pl.empty && !pl.token && kv["heads_per_group"] > 0) {
-    const int h_total = pl.a.n_heads_q + pl.a.n_heads_k;
-    pl.a.heads_per_group = (int32_t)kv["heads_per_group"];
-    pl.a.n_groups = (h_total + pl.a.heads_per_group - 1) / pl.a.heads_per_group;
-    pl.grid = pl.a.n_tiles * pl.a.n_groups;
-  }
-  if (!pl.empty && !pl.token && kv.count("group_slow")) pl.a.group_slow = (int32_t)kv["group_slow"];
-  printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
-         "heads_per_group %d\nn_groups %d\ngroup_slow %d\nsingle %d\n",
-         (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
-         pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow, (int)pl.single);
+  apply_overrides(pl, kv);
+  print_plan(pl);
   if (!pl.empty) {
     HostRunner runner{pl};
     rope::dispatch(pl, runner);

@@ -179,3 +179,104 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(rp, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         rp.lib()
+
+
+def test_struct_layouts_match_the_c_compiler(tmp_path):
+    """ctypes mirrors of rope_desc_t and rope_apply_desc_t have the C layout."""
+    src = tmp_path / "layout.c"
+    src.write_text('''#include <stddef.h>
+#include <stdio.h>
+#include "librope.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(rope_desc_t), offsetof(rope_desc_t, cos),
+         offsetof(rope_desc_t, pos_batch_stride), sizeof(rope_apply_desc_t),
+         offsetof(rope_apply_desc_t, q_in), offsetof(rope_apply_desc_t, k_out),
+         offsetof(rope_apply_desc_t, cos), offsetof(rope_apply_desc_t, pos_batch_stride));
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", f"-I{os.path.join(ROOT, 'include')}", "-o", str(exe),
+                    str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    D, A = rp.RopeDesc, rp.RopeApplyDesc
+    assert got == [ctypes.sizeof(D), D.cos.offset, D.pos_batch_stride.offset,
+                   ctypes.sizeof(A), A.q_in.offset, A.k_out.offset, A.cos.offset,
+                   A.pos_batch_stride.offset]
+
+
+def apply_desc(**kw):
+    d = rp.RopeApplyDesc()
+    d.batch, d.seq_len, d.head_dim, d.rotary_dim, d.n_heads_q, d.n_heads_k = 2, 8, 64, 64, 4, 2
+    d.dtype, d.pairing, d.launch, d.direction = 2, 0, 0, 1
+    W = (4 + 2 * 2) * 64  # packed [B, S, (Hq + 2Hk) * D]
+    d.q_in = rp.RopeView(A16, 8 * W, 64, W)
+    d.k_in = rp.RopeView(A16 + 4 * 64 * 2, 8 * W, 64, W)
+    d.cos, d.sin, d.table_rows = A16 * 64, A16 * 65, 8
+    d.table_row_stride, d.table_col_stride = 0, 1
+    for key, v in kw.items():
+        setattr(d, key, v)
+    return d
+
+
+def call_apply(d):
+    return rp.lib().rope_apply(ctypes.byref(d) if d is not None else None, None)
+
+
+@pytest.mark.parametrize("change,expected", [
+    (dict(direction=0), LAYOUT), (dict(direction=2), LAYOUT), (dict(table_col_stride=3), LAYOUT),
+    (dict(table_row_stride=31), SHAPE), (dict(table_row_stride=-1), SHAPE),
+    (dict(table_col_stride=2, table_row_stride=62), SHAPE),
+    (dict(q_in=rp.RopeView(A16 + 1, 8 * 512, 64, 512)), ALIGN),
+    (dict(q_out=rp.RopeView(A16 * 3 + 1, 0, 0, 0)), ALIGN),
+    (dict(k_in=rp.RopeView(A16 + 3 * 64 * 2, 8 * 512, 64, 512)), ALIAS),   # K inside Q's heads
+    (dict(q_in=rp.RopeView(A16, 8 * 512, 0, 512)), ALIAS),                  # heads share rows
+    (dict(q_out=rp.RopeView(A16 + 4 * 64 * 2, 8 * 512, 64, 512)), ALIAS),  # Q out onto K in
+    (dict(k_in=rp.RopeView(A16 + 4 * 64 * 2, 8 * 512, 64, -512)), SHAPE),
+    (dict(k_in=rp.RopeView(None, 0, 0, 0)), NULL),
+])
+def test_apply_validation_errors(change, expected):
+    assert call_apply(apply_desc(**change)) == expected
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks behaviour with no GPU present")
+@pytest.mark.parametrize("change", [
+    dict(),                                                        # packed QKV, in place
+    dict(q_out=rp.RopeView(A16 * 8, 4 * 8 * 64, 8 * 64, 64),       # out of place, [B,H,S,D]
+         k_out=rp.RopeView(A16 * 9, 2 * 8 * 64, 8 * 64, 64)),
+    dict(table_row_stride=64, table_col_stride=2),                 # repeat-interleaved table
+    dict(n_heads_k=0, k_in=rp.RopeView(None, 0, 0, 0),             # broadcast input, Q only
+         q_in=rp.RopeView(A16, 0, 64, 512), q_out=rp.RopeView(A16 * 8, 4 * 8 * 64, 8 * 64, 64)),
+])
+def test_apply_accepts_valid_views(change):
+    """Accepted descriptors get past validation; with no GPU the call then
+    fails at the HIP runtime instead."""
+    assert call_apply(apply_desc(**change)) == HIP
+
+
+def test_apply_empty_and_null():
+    assert call_apply(None) == NULL
+    assert call_apply(apply_desc(batch=0, q_in=rp.RopeView(None, 0, 0, 0))) == OK
+
+
+def test_binding_marshals_strided_views():
+    B, S, Hq, Hk, D = 2, 16, 8, 2, 128
+    qkv = torch.zeros(B, S, (Hq + 2 * Hk) * D, dtype=torch.bfloat16)
+    q = qkv[..., :Hq * D].view(B, S, Hq, D)
+    k = qkv[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D)
+    c = torch.zeros(S, D)  # duplicated halves, [S, R]
+    d = rp.make_apply_desc(q, k, c, c, layout="bshd", table_layout="duplicated", direction=-1)
+    W = (Hq + 2 * Hk) * D
+    assert (d.q_in.stride_b, d.q_in.stride_h, d.q_in.stride_s) == (S * W, D, W)
+    assert d.k_in.data == q.data_ptr() + Hq * D * 2
+    assert d.table_row_stride == D and d.table_col_stride == 1 and d.direction == -1
+    assert not d.q_out.data and not d.k_out.data
+    d = rp.make_apply_desc(q, k, c, c, layout="bshd", table_layout="interleaved",
+                           q_out=torch.empty(B, S, Hq, D, dtype=torch.bfloat16))
+    assert d.table_col_stride == 2 and d.q_out.data
+    with pytest.raises(ValueError):
+        rp.make_apply_desc(q, k, c[:, :64].contiguous(), c[:, :64].contiguous(), layout="bshd",
+                           table_layout="duplicated")
+    with pytest.raises(ValueError):
+        rp.make_apply_desc(q.transpose(2, 3), None, c, c, table_layout="duplicated")

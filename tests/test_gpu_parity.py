@@ -356,3 +356,112 @@ def test_full_size_sampled(name):
                             w.rotary_dim, what=f"{name} dir={direction}")
         # the next direction starts from the forward result
         t = {"q": qd.cpu(), "k": kd.cpu()}
+
+
+# ------------------------------------------------ general form: rope_apply
+
+def _packed_views(B, S, Hq, Hk, D, dtype, seed):
+    qkv = W.normal((B, S, (Hq + 2 * Hk) * D), dtype, seed)
+    q = qkv[..., :Hq * D].view(B, S, Hq, D)
+    k = qkv[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D)
+    return qkv, q, k
+
+
+def _check_view(w, got_bshd, x_bshd, direction, pos, pos_batch_stride=None, what=""):
+    """got/x are [B,S,H,D] views (any strides); compare through the oracle."""
+    ws = w.scaled(layout="bshd", n_heads_q=x_bshd.shape[2])
+    ref = P.oracle_rope(ws, x_bshd.contiguous(), direction, pos,
+                        pos_batch_stride=pos_batch_stride)
+    masked = P.masked_tokens(ws, pos, pos_batch_stride=pos_batch_stride)
+    return P.assert_parity(P.storage(got_bshd.contiguous().cpu()), ref,
+                           P.storage(x_bshd.contiguous()), w.dtype, "bshd", w.rotary_dim,
+                           masked, what)
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_packed_qkv_in_place(direction):
+    """Q and K rotated where a fused projection left them: views into one
+    [B, S, (Hq + 2 Hk) * D] buffer; the V part stays bit-exact."""
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=1000, table_rows=1000)
+    B, S, Hq, Hk, D = w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim
+    qkv, q, k = _packed_views(B, S, Hq, Hk, D, w.dtype, 31)
+    say(f"[gpu] packed qkv {tuple(qkv.shape)} dir={direction}")
+    cos, sin = gpu_tables(w)
+    g = qkv.to(DEV)
+    gq = g[..., :Hq * D].view(B, S, Hq, D)
+    gk = g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D)
+    rp.rope_apply(gq, gk, cos, sin, layout="bshd", direction=direction)
+    torch.cuda.synchronize()
+    gc = g.cpu()
+    _check_view(w, gc[..., :Hq * D].view(B, S, Hq, D), q, direction, None, what="q")
+    _check_view(w, gc[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D), k, direction, None, what="k")
+    assert torch.equal(gc[..., (Hq + Hk) * D:].view(torch.int16),
+                       qkv[..., (Hq + Hk) * D:].view(torch.int16))
+
+
+@pytest.mark.parametrize("launch", ["rows", "token"])
+def test_out_of_place_partial_rotary_skipped_tokens(launch):
+    w = W.PARTIAL_INDEXED.scaled(seq_len=300, table_rows=9216)
+    B, S, H, D = w.batch, w.seq_len, w.n_heads_q, w.head_dim
+    qkv, q, k = _packed_views(B, S, H, H, D, w.dtype, 32)
+    pos = torch.cat([torch.tensor([-1, -1, 9300], dtype=torch.int32),
+                     W.random_positions(S - 3, 9216, 33)])
+    cos, sin = gpu_tables(w)
+    g = qkv.to(DEV)
+    gq = g[..., :H * D].view(B, S, H, D)
+    gk = g[..., H * D:2 * H * D].view(B, S, H, D)
+    oq = torch.full((B, S, H, D), 7.0, dtype=torch.bfloat16, device=DEV)
+    ok = torch.full((B, S, H, D), 7.0, dtype=torch.bfloat16, device=DEV)
+    rp.rope_apply(gq, gk, cos, sin, q_out=oq, k_out=ok, layout="bshd", rotary_dim=w.rotary_dim,
+                  pos=pos.to(DEV), pos_batch_stride=0, launch=launch)
+    torch.cuda.synchronize()
+    assert torch.equal(g.cpu().view(torch.int16), qkv.view(torch.int16))  # inputs untouched
+    _check_view(w, oq, q, 1, pos, 0, "q_out")
+    _check_view(w, ok, k, 1, pos, 0, "k_out")
+
+
+@pytest.mark.parametrize("table_layout", ["half", "duplicated", "interleaved"])
+@pytest.mark.parametrize("pairing", ["split_half", "interleaved"])
+def test_table_layouts_agree(table_layout, pairing):
+    w = W.BSHD_INTERLEAVED.scaled(batch=2, seq_len=129, table_rows=129, pairing=pairing)
+    t = W.tensors(w)
+    c, s = rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
+    if table_layout == "duplicated":
+        c, s = torch.cat([c, c], 1), torch.cat([s, s], 1)
+    elif table_layout == "interleaved":
+        c, s = c.repeat_interleave(2, 1), s.repeat_interleave(2, 1)
+    q, k = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_apply(q, k, c.to(DEV), s.to(DEV), layout="bshd", pairing=pairing,
+                  table_layout=table_layout)
+    torch.cuda.synchronize()
+    _check_view(w, q, t["q"], 1, None, what="q")
+    _check_view(w, k, t["k"], 1, None, what="k")
+
+
+def test_broadcast_input_out_of_place():
+    """One sequence (batch stride 0) rotated into every batch of the output."""
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=3, seq_len=64, n_heads_q=8, table_rows=64)
+    one = W.normal((1, 64, 8, 128), w.dtype, 34)
+    src = one.to(DEV).expand(3, 64, 8, 128)
+    out = torch.empty(3, 64, 8, 128, dtype=torch.bfloat16, device=DEV)
+    cos, sin = gpu_tables(w)
+    rp.rope_apply(src, None, cos, sin, q_out=out, layout="bshd", direction=-1)
+    torch.cuda.synchronize()
+    _check_view(w, out, one.expand(3, 64, 8, 128), -1, None, what="broadcast")
+
+
+def test_apply_matches_contiguous_entry_points_bitwise():
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=300, table_rows=300)
+    t = W.tensors(w)
+    cos, sin = gpu_tables(w)
+    a_q, a_k = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_fwd_qk(a_q, a_k, cos, sin, **opts(w))
+    b_q, b_k = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_apply(b_q, b_k, cos, sin, layout="bhsd")
+    c_q = torch.empty_like(b_q)
+    c_k = torch.empty_like(b_k)
+    rp.rope_apply(t["q"].to(DEV), t["k"].to(DEV), cos, sin, q_out=c_q, k_out=c_k)
+    torch.cuda.synchronize()
+    for x, y, z in ((a_q, b_q, c_q), (a_k, b_k, c_k)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+        assert torch.equal(x.view(torch.int16), z.view(torch.int16))

@@ -245,3 +245,241 @@ def test_empty_work(emu, change):
     plan, qo, ko = run_emu(emu, w, q, k, cos, sin, pos)
     assert plan["status"] == 0 and plan["empty"] == 1
     assert np.array_equal(qo, P.storage(q))
+
+
+# ------------------------------------------------ the general form (rope_apply)
+
+def _strided(buf, spec, shape):
+    """View [B,H,S,D] of 1-d storage `buf` at (offset, sb, sh, ss)."""
+    off, sb, sh, ss = spec
+    return torch.as_strided(buf, shape, (sb, sh, ss, 1), off)
+
+
+def run_emu_apply(emu, w, in_buf, q_in, k_in, cos, sin, *, out_buf=None, q_out=None,
+                  k_out=None, pos=None, direction=1, launch="auto", t_row=0, t_col=1,
+                  cus=256, pos_batch_stride=None):
+    """Run rope_apply's plan in the emulator. Views are (offset, sb, sh, ss)
+    element specs into in_buf / out_buf (1-d torch storage)."""
+    with tempfile.TemporaryDirectory() as job:
+        desc = dict(apply=1, batch=w.batch, seq_len=w.seq_len, head_dim=w.head_dim,
+                    rotary_dim=w.rotary_dim, n_heads_q=w.n_heads_q,
+                    n_heads_k=0 if k_in is None else w.n_heads_k,
+                    dtype=CODES["dtype"][w.dtype], pairing=CODES["pairing"][w.pairing],
+                    launch=CODES["launch"][launch], direction=direction,
+                    in_elems=in_buf.numel(), out_elems=0 if out_buf is None else out_buf.numel(),
+                    table_elems=cos.numel(), table_rows=cos.shape[0], t_row=t_row, t_col=t_col,
+                    pos_count=0 if pos is None else pos.numel(),
+                    pos_batch_stride=(w.pos_batch_stride if pos_batch_stride is None
+                                      else pos_batch_stride), cus=cus)
+        for name, spec in (("q_in", q_in), ("k_in", k_in), ("q_out", q_out), ("k_out", k_out)):
+            if spec is None:
+                desc[name + "_off"] = -1
+            else:
+                for key, v in zip(("off", "sb", "sh", "ss"), spec):
+                    desc[f"{name}_{key}"] = v
+        with open(os.path.join(job, "desc.txt"), "w") as f:
+            for key, v in desc.items():
+                f.write(f"{key} {int(v)}\n")
+        P.storage(in_buf).tofile(os.path.join(job, "in.bin"))
+        if out_buf is not None:
+            P.storage(out_buf).tofile(os.path.join(job, "out.bin"))
+        cos.contiguous().numpy().tofile(os.path.join(job, "cos.bin"))
+        sin.contiguous().numpy().tofile(os.path.join(job, "sin.bin"))
+        if pos is not None:
+            pos.numpy().astype(np.int32).tofile(os.path.join(job, "pos.bin"))
+        env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
+        r = subprocess.run([emu, job], capture_output=True, text=True, timeout=300, env=env)
+        assert r.returncode == 0, r.stdout + r.stderr[-4000:]
+        plan = {key: int(v) for key, v in
+                (line.split() for line in r.stdout.strip().splitlines())}
+        if plan["status"] != 0:
+            return plan, None, None
+        dt = W.TORCH_DTYPES[w.dtype]
+
+        def back(path, like):
+            st = P.storage(like)
+            arr = np.fromfile(path, dtype=st.dtype)
+            t = torch.from_numpy(arr.copy())
+            return t if dt == torch.float32 else t.view(dt)
+        in_after = back(os.path.join(job, "in_after.bin"), in_buf)
+        out_after = None if out_buf is None else back(os.path.join(job, "out_after.bin"), out_buf)
+        return plan, in_after, out_after
+
+
+def _half_tables(w):
+    return rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
+
+
+def _oracle_view(w, x, direction, pos, heads, pos_batch_stride=None):
+    wv = w.scaled(layout="bhsd", n_heads_q=heads)
+    return P.oracle_rope(wv, x.contiguous(), direction, pos, pos_batch_stride=pos_batch_stride)
+
+
+def _assert_view(w, got, x, direction, pos, heads, pos_batch_stride=None):
+    ref = _oracle_view(w, x, direction, pos, heads, pos_batch_stride)
+    masked = P.masked_tokens(w, pos, pos_batch_stride=pos_batch_stride)
+    P.assert_parity(P.storage(got.contiguous()), ref, P.storage(x.contiguous()), w.dtype,
+                    "bhsd", w.rotary_dim, masked)
+
+
+PACKED = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=37, n_heads_q=8, n_heads_k=2,
+                                    table_rows=40)
+
+
+def _packed(w, seed=5):
+    """[B, S, (Hq + 2 Hk) * D] packed QKV storage and the Q, K view specs."""
+    B, S, D, Hq, Hk = w.batch, w.seq_len, w.head_dim, w.n_heads_q, w.n_heads_k
+    Wd = (Hq + 2 * Hk) * D
+    buf = W.normal((B * S * Wd,), w.dtype, seed)
+    q = (0, S * Wd, D, Wd)
+    k = (Hq * D, S * Wd, D, Wd)
+    v_region = (B, S, Wd)
+    return buf, q, k, v_region
+
+
+@pytest.mark.parametrize("launch", ["auto", "rows", "token"])
+@pytest.mark.parametrize("direction", [1, -1])
+def test_packed_qkv_in_place(emu, launch, direction):
+    w = PACKED
+    buf, qs, ks, _ = _packed(w)
+    cos, sin = _half_tables(w)
+    plan, after, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, launch=launch,
+                                   direction=direction)
+    assert plan["status"] == 0 and plan["oop"] == 0
+    qshape = (w.batch, w.n_heads_q, w.seq_len, w.head_dim)
+    kshape = (w.batch, w.n_heads_k, w.seq_len, w.head_dim)
+    _assert_view(w, _strided(after, qs, qshape), _strided(buf, qs, qshape), direction, None,
+                 w.n_heads_q)
+    _assert_view(w, _strided(after, ks, kshape), _strided(buf, ks, kshape), direction, None,
+                 w.n_heads_k)
+    # the V part of every token is untouched, bit for bit
+    B, S, D, Hq, Hk = w.batch, w.seq_len, w.head_dim, w.n_heads_q, w.n_heads_k
+    v0 = buf.view(B, S, -1)[..., (Hq + Hk) * D:]
+    v1 = after.view(B, S, -1)[..., (Hq + Hk) * D:]
+    assert np.array_equal(P.storage(v0.contiguous()), P.storage(v1.contiguous()))
+
+
+@pytest.mark.parametrize("launch", ["rows", "token"])
+def test_packed_qkv_out_of_place_partial_rotary_with_skipped_tokens(emu, launch):
+    w = PACKED.scaled(rotary_dim=64, table_rows=100)
+    buf, qs, ks, _ = _packed(w, seed=6)
+    cos, sin = _half_tables(w)
+    B, S, D, Hq, Hk = w.batch, w.seq_len, w.head_dim, w.n_heads_q, w.n_heads_k
+    out = torch.zeros(B * (Hq + Hk) * S * D, dtype=W.TORCH_DTYPES[w.dtype])
+    qo = (0, Hq * S * D, S * D, D)
+    ko = (B * Hq * S * D, Hk * S * D, S * D, D)
+    pos = W.random_positions(S, 130, 9, low=-20)  # some negative, some past the table
+    plan, after, out_after = run_emu_apply(emu, w, buf, qs, ks, cos, sin, out_buf=out,
+                                           q_out=qo, k_out=ko, pos=pos, launch=launch,
+                                           pos_batch_stride=0)
+    assert plan["oop"] == 1
+    assert np.array_equal(P.storage(after), P.storage(buf))  # inputs untouched
+    qshape, kshape = (B, Hq, S, D), (B, Hk, S, D)
+    _assert_view(w, _strided(out_after, qo, qshape), _strided(buf, qs, qshape), 1, pos, Hq,
+                 pos_batch_stride=0)
+    _assert_view(w, _strided(out_after, ko, kshape), _strided(buf, ks, kshape), 1, pos, Hk,
+                 pos_batch_stride=0)
+
+
+@pytest.mark.parametrize("table_layout", ["duplicated", "interleaved", "padded"])
+@pytest.mark.parametrize("pairing", ["split_half", "interleaved"])
+def test_table_layouts(emu, table_layout, pairing):
+    w = PACKED.scaled(pairing=pairing)
+    buf, qs, ks, _ = _packed(w, seed=7)
+    c, s = _half_tables(w)
+    if table_layout == "duplicated":
+        cos, sin, t_row, t_col = torch.cat([c, c], 1), torch.cat([s, s], 1), w.rotary_dim, 1
+    elif table_layout == "interleaved":
+        cos, sin = c.repeat_interleave(2, 1), s.repeat_interleave(2, 1)
+        t_row, t_col = w.rotary_dim, 2
+    else:  # rows padded to R/2 + 4 floats
+        pad = torch.full((c.shape[0], 4), float("nan"))
+        cos, sin = torch.cat([c, pad], 1), torch.cat([s, pad], 1)
+        t_row, t_col = w.rotary_dim // 2 + 4, 1
+    plan, after, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, t_row=t_row, t_col=t_col)
+    assert plan["t_vec"] == (1 if t_col == 1 else 0)
+    qshape = (w.batch, w.n_heads_q, w.seq_len, w.head_dim)
+    _assert_view(w, _strided(after, qs, qshape), _strided(buf, qs, qshape), 1, None,
+                 w.n_heads_q)
+
+
+def test_padded_rows_and_broadcast_input_out_of_place(emu):
+    """[B,H,S,D] rows padded to D + 8 elements, rotated in place; and one
+    sequence broadcast (batch stride 0) into a [B,H,S,D] output."""
+    w = PACKED.scaled(n_heads_k=0, seq_len=21, table_rows=21)
+    B, H, S, D = w.batch, w.n_heads_q, w.seq_len, w.head_dim
+    cos, sin = _half_tables(w)
+    rs = D + 8
+    buf = W.normal((B * H * S * rs,), w.dtype, 11)
+    spec = (0, H * S * rs, S * rs, rs)
+    plan, after, _ = run_emu_apply(emu, w, buf, spec, None, cos, sin)
+    shape = (B, H, S, D)
+    _assert_view(w, _strided(after, spec, shape), _strided(buf, spec, shape), 1, None, H)
+    pads = torch.as_strided(after, (B * H * S, 8), (rs, 1), D)
+    pads0 = torch.as_strided(buf, (B * H * S, 8), (rs, 1), D)
+    assert np.array_equal(P.storage(pads.contiguous()), P.storage(pads0.contiguous()))
+    # broadcast: every batch reads the same sequence
+    one = W.normal((H * S * D,), w.dtype, 12)
+    out = torch.zeros(B * H * S * D, dtype=W.TORCH_DTYPES[w.dtype])
+    ispec, ospec = (0, 0, S * D, D), (0, H * S * D, S * D, D)
+    plan, after, out_after = run_emu_apply(emu, w, one, ispec, None, cos, sin, out_buf=out,
+                                           q_out=ospec, direction=-1)
+    assert plan["status"] == 0 and plan["oop"] == 1
+    _assert_view(w, _strided(out_after, ospec, shape), _strided(one, ispec, shape), -1, None, H)
+
+
+def test_odd_head_dim_interleaved_out_of_place(emu):
+    w = W.BSHD_INTERLEAVED.scaled(batch=2, seq_len=9, n_heads_q=3, n_heads_k=2, head_dim=31,
+                                  rotary_dim=30, table_rows=9, layout="bhsd")
+    B, S, D = w.batch, w.seq_len, w.head_dim
+    cos, sin = _half_tables(w)
+    buf = W.normal((B * 5 * S * D,), w.dtype, 13)
+    qs, ks = (0, 3 * S * D, S * D, D), (B * 3 * S * D, 2 * S * D, S * D, D)
+    out = torch.zeros_like(buf)
+    plan, _, out_after = run_emu_apply(emu, w, buf, qs, ks, cos, sin, out_buf=out, q_out=qs,
+                                       k_out=ks)
+    assert plan["aligned"] == 0 and plan["oop"] == 1
+    _assert_view(w, _strided(out_after, qs, (B, 3, S, D)), _strided(buf, qs, (B, 3, S, D)), 1,
+                 None, 3)
+    _assert_view(w, _strided(out_after, ks, (B, 2, S, D)), _strided(buf, ks, (B, 2, S, D)), 1,
+                 None, 2)
+
+
+@pytest.mark.parametrize("case,expected", [
+    ("outputs_overlap", -6), ("k_inside_q_heads", -6), ("output_not_injective", -6),
+    ("direction_zero", -4), ("col_stride_three", -4), ("negative_stride", -2),
+    ("table_row_stride_too_small", -2), ("q_shifted_into_k", -6), ("packed_ok", 0)])
+def test_apply_validation(emu, case, expected):
+    w = PACKED
+    buf, qs, ks, _ = _packed(w)
+    cos, sin = _half_tables(w)
+    kw = {}
+    if case == "outputs_overlap":
+        # outputs live in a second buffer; with identical offsets the validator
+        # cannot tell the buffers apart only if the pointers coincide, so place
+        # Q's output exactly over K's input by writing into the input buffer
+        plan, _, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, out_buf=None, q_out=None)
+        assert plan["status"] == 0
+        d_out = torch.zeros_like(buf)
+        plan, _, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, out_buf=d_out, q_out=qs,
+                                   k_out=qs)
+        assert plan["status"] == expected  # both outputs on the same elements
+        assert plan["status"] == expected
+        return
+    if case == "k_inside_q_heads":
+        ks = (w.head_dim * 3, *ks[1:])
+    if case == "output_not_injective":
+        qs = (0, qs[1], 0, qs[3])
+    if case == "direction_zero":
+        kw["direction"] = 0
+    if case == "col_stride_three":
+        kw["t_col"] = 3
+    if case == "negative_stride":
+        qs = (qs[0] + qs[1], -qs[1], qs[2], qs[3])
+    if case == "table_row_stride_too_small":
+        kw["t_row"] = w.rotary_dim // 2 - 1
+    if case == "q_shifted_into_k":  # Q's last head now shares elements with K's first
+        buf = torch.cat([buf, buf[:1]])
+        qs = (1, *qs[1:])
+    plan, _, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, **kw)
+    assert plan["status"] == expected
