@@ -245,10 +245,12 @@ def time_workload(w, launches=("auto", "rows", "token"), target_s: float = 0.15)
     return results
 
 
-def _time_calls(out, fwd, bwd, sets, nbytes, target_s, stream):
+def _time_calls(out, fwd, bwd, sets, nbytes, target_s, stream, method=None):
     import torch
-    for name, calls in (("fwd", [c.rope_fwd_qk for c in fwd]),
-                        ("bwd", [c.rope_bwd_qk for c in bwd])):
+    fm = method or "rope_fwd_qk"
+    bm = method or "rope_bwd_qk"
+    for name, calls in (("fwd", [getattr(c, fm) for c in fwd]),
+                        ("bwd", [getattr(c, bm) for c in bwd])):
         for i in range(10):
             calls[i % sets]()
         torch.cuda.synchronize()
@@ -270,6 +272,107 @@ def _time_calls(out, fwd, bwd, sets, nbytes, target_s, stream):
         out[f"{name}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         out[f"{name}_pct_of_hbm_peak"] = round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)
         out[f"{name}_reps"] = reps
+
+
+def time_general_form(w, target_s: float = 0.15):
+    """rope_apply on workload w's shapes laid out as one packed QKV buffer
+    [B, S, (Hq + 2 Hk) * D] (Q and K rotated in place where they sit), and
+    out of place from the packed buffer into separate [B, S, H, D] outputs.
+    GB/s over the same algorithmic bytes as the contiguous call (R = D here,
+    so out of place moves the same bytes)."""
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    B, S, Hq, Hk, D = w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim
+    cos, sin = rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
+    cos, sin = cos.cuda(), sin.cuda()
+    dt = W.TORCH_DTYPES[w.dtype]
+    e = 4 if w.dtype == "f32" else 2
+    qkv_bytes = B * S * (Hq + 2 * Hk) * D * e
+    sets = max(1, min(4, -(-600_000_000 // qkv_bytes)))
+    host = W.normal((B, S, (Hq + 2 * Hk) * D), w.dtype, w.seed("q"))
+    bufs = [host.cuda() for _ in range(sets)]
+    outs = [(torch.empty(B, S, Hq, D, dtype=dt, device="cuda"),
+             torch.empty(B, S, Hk, D, dtype=dt, device="cuda")) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+    nbytes = algorithmic_bytes(w, None)
+    kw = dict(layout="bshd", pairing=w.pairing, rotary_dim=w.rotary_dim, stream=stream)
+
+    def views(g):
+        return (g[..., :Hq * D].view(B, S, Hq, D),
+                g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D))
+    results = []
+    for mode in ("packed_qkv_in_place", "packed_qkv_out_of_place"):
+        calls = []
+        for i, g in enumerate(bufs):
+            q, k = views(g)
+            extra = {} if mode.endswith("in_place") else dict(q_out=outs[i][0], k_out=outs[i][1])
+            f = rp.prepare_apply(q, k, cos, sin, **kw, **extra)
+            b = rp.prepare_apply(q, k, cos, sin, direction=-1, **kw, **extra)
+            calls.append((f, b))
+        out = {"workload": w.name, "launch": mode, "buffer_sets": sets,
+               "algorithmic_bytes_per_call": nbytes}
+        _time_calls(out, [c[0] for c in calls], [c[1] for c in calls], sets, nbytes, target_s,
+                    stream, method="rope_apply")
+        results.append(out)
+    del bufs, outs
+    torch.cuda.empty_cache()
+    return results
+
+
+# [B, S, Hq, Hk, D, dtype] shapes for the token-major launch-shape comparison
+LAYOUT_MATRIX_SHAPES = {
+    "[4, 4096, 32+8, 128] bf16": (4, 4096, 32, 8, 128, "bf16"),
+    "[8, 2048, 16+16, 64] fp16": (8, 2048, 16, 16, 64, "f16"),
+    "[4, 4096, 32+32, 64] bf16": (4, 4096, 32, 32, 64, "bf16"),
+    "[2, 4096, 16+4, 256] bf16": (2, 4096, 16, 4, 256, "bf16"),
+}
+
+
+def time_layout_matrix(reps: int = 400):
+    """rows vs token launch on token-major views ([B,S,H,D] tensors and Q/K
+    views into a packed QKV buffer), both pairings: forward rope_apply in
+    place, reps calls over 3 buffer sets between two HIP events."""
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    stream = torch.cuda.current_stream()
+    for name, (B, S, Hq, Hk, D, dt) in LAYOUT_MATRIX_SHAPES.items():
+        cos, sin = rp.rope_build_table(S, D, 10000.0)
+        cos, sin = cos.cuda(), sin.cuda()
+        nbytes = 2 * (2 if dt != "f32" else 4) * B * S * (Hq + Hk) * D + 8 * S * (D // 2)
+        for view in ("bshd", "packed"):
+            sets = []
+            for i in range(3):
+                if view == "bshd":
+                    sets.append((W.normal((B, S, Hq, D), dt, 9000 + i).cuda(),
+                                 W.normal((B, S, Hk, D), dt, 9100 + i).cuda()))
+                else:
+                    g = W.normal((B, S, (Hq + 2 * Hk) * D), dt, 9200 + i).cuda()
+                    sets.append((g[..., :Hq * D].view(B, S, Hq, D),
+                                 g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D), g))
+            for pairing in ("split_half", "interleaved"):
+                res = {"shape": name, "view": view, "pairing": pairing}
+                for launch in ("rows", "token"):
+                    calls = [rp.prepare_apply(x[0], x[1], cos, sin, layout="bshd",
+                                              pairing=pairing, launch=launch,
+                                              stream=stream).rope_apply for x in sets]
+                    for c in calls:
+                        c()
+                    torch.cuda.synchronize()
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    for i in range(reps):
+                        calls[i % len(calls)]()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    us = a.elapsed_time(b) * 1000.0 / reps
+                    res[f"{launch}_us"] = round(us, 2)
+                    res[f"{launch}_GBps"] = round(nbytes / us / 1e3, 1)
+                yield res
+            del sets
+            torch.cuda.empty_cache()
 
 
 def cpu_baseline(w, host, pos):
@@ -383,6 +486,11 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--workloads", action="store_true",
                     help="time every workload (both grid shapes); one JSON line each")
+    ap.add_argument("--general-form", action="store_true",
+                    help="time only rope_apply on the Llama prefill shape as packed QKV, "
+                         "in place and out of place")
+    ap.add_argument("--layout-matrix", action="store_true",
+                    help="rows vs token launch on token-major views, by shape and pairing")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -401,10 +509,20 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.layout_matrix:
+        for res in time_layout_matrix():
+            print(json.dumps(res), flush=True)
+        return
+    if args.general_form:
+        for res in time_general_form(W.LLAMA_GQA_PREFILL):
+            print(json.dumps(res), flush=True)
+        return
     if args.workloads:
         for wl in W.ALL:
             for res in time_workload(wl):
                 print(json.dumps(res), flush=True)
+        for res in time_general_form(W.LLAMA_GQA_PREFILL):
+            print(json.dumps(res), flush=True)
         return
 
     w = W.LLAMA_GQA_PREFILL

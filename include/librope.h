@@ -37,8 +37,8 @@
  *                 (Unsloth page, Usage Examples)
  *     ROPE_BSHD : Q [batch, seq_len, n_heads_q, head_dim] (rotary-embedding-torch
  *                 docs, seq_before_head_dim)
- * Both dense and contiguous. GQA: 1 <= n_heads_k <= n_heads_q (Unsloth page,
- * Manual Triton Kernel Invocation, separate n_heads_K).
+ * Both dense and contiguous. GQA: 0 <= n_heads_k <= n_heads_q (Unsloth page,
+ * Manual Triton Kernel Invocation, separate n_heads_K); 0 rotates Q only.
  *
  * Tables (How Unsloth Optimizes RoPE ..., Usage Examples: precomputed cos and
  * sin; "Rotary Embedding Kernel", Common Pitfalls: [seq_len, D/2], broadcast
@@ -49,7 +49,8 @@
  * Ownership and lifetime. Every pointer in a call is caller-owned. q, k, cos,
  * sin and pos are device memory on the current HIP device and must stay valid
  * until the enqueued work completes. q and k are modified in place and must
- * not overlap each other. The library keeps no mutable global state beyond a
+ * not overlap each other, nor the cos, sin and pos arrays, which must not
+ * change while the work runs. The library keeps no mutable global state beyond a
  * per-device cache of the compute-unit count, filled once; calls are
  * reentrant and may be issued from several threads on different streams.
  *
@@ -74,8 +75,9 @@ typedef enum rope_status {
   ROPE_ERR_SHAPE = -2,  /* a size is negative or inconsistent */
   ROPE_ERR_DTYPE = -3,  /* unknown dtype code */
   ROPE_ERR_LAYOUT = -4, /* unknown layout, pairing or launch-shape code */
-  ROPE_ERR_ALIGN = -5,  /* a pointer is not aligned to its element size */
-  ROPE_ERR_ALIAS = -6,  /* the q and k byte ranges overlap */
+  ROPE_ERR_ALIGN = -5,  /* q/k data not aligned to its element size, cos or sin
+                           not 16-byte aligned, or pos not 4-byte aligned */
+  ROPE_ERR_ALIAS = -6,  /* written data overlaps other operands (see the calls) */
   ROPE_ERR_HIP = -7     /* the HIP runtime reported an error */
 } rope_status_t;
 
@@ -96,7 +98,7 @@ typedef enum rope_launch {
 typedef struct rope_desc {
   int64_t batch;       /* B >= 0 */
   int64_t n_heads_q;   /* Hq >= 0 */
-  int64_t n_heads_k;   /* Hk, 1 <= Hk <= Hq for the _qk calls; ignored by the _q calls */
+  int64_t n_heads_k;   /* Hk, 0 <= Hk <= Hq for the _qk calls; ignored by the _q calls */
   int64_t seq_len;     /* S >= 0 */
   int64_t head_dim;    /* D >= 0 */
   int64_t rotary_dim;  /* R, even, 0 <= R <= D */
@@ -104,8 +106,8 @@ typedef struct rope_desc {
   int32_t layout;      /* rope_layout_t */
   int32_t pairing;     /* rope_pairing_t */
   int32_t launch;      /* rope_launch_t; 0 = automatic */
-  const float *cos;    /* device, float32 [table_rows, R/2], 4-byte aligned */
-  const float *sin;    /* device, float32 [table_rows, R/2], 4-byte aligned */
+  const float *cos;    /* device, float32 [table_rows, R/2], 16-byte aligned */
+  const float *sin;    /* device, float32 [table_rows, R/2], 16-byte aligned */
   int64_t table_rows;  /* rows of cos and sin (the largest position + 1) */
   const int32_t *pos;  /* device int32 indices, or NULL for p = s */
   int64_t pos_batch_stride; /* index of token (b, s) is pos[b * stride + s]; 0 shares one row */
@@ -114,6 +116,8 @@ typedef struct rope_desc {
 /* Forward RoPE on Q and K in one launch, in place.
  * q: device, d->dtype elements in d->layout, shape with n_heads_q heads.
  * k: device, same with n_heads_k heads; must not overlap q.
+ * ROPE_ERR_ALIAS when q and k overlap, or either overlaps cos, sin or the
+ * index entries the call reads.
  * stream: a hipStream_t, or NULL for the null stream.
  * Returns ROPE_OK, a validation error (nothing enqueued) or ROPE_ERR_HIP.
  * Empty work (batch, seq_len, all heads or rotary_dim zero) returns ROPE_OK
@@ -193,11 +197,13 @@ typedef struct rope_apply_desc {
  * own input (same pointer and strides), which is the in-place case. Two
  * views overlap when they could address a common element; Q and K views
  * that interleave token by token (packed QKV) without sharing elements are
- * accepted.
+ * accepted. No written view may meet the byte range of cos, sin or the index
+ * entries the call reads. Any of these is ROPE_ERR_ALIAS.
  * Errors: as rope_fwd_qk; ROPE_ERR_SHAPE also for negative strides or a
  * table stride that cannot hold R/2 frequencies; ROPE_ERR_LAYOUT for a
  * direction other than +-1 or a table column stride other than 1 or 2;
- * ROPE_ERR_ALIGN when a view's data is not aligned to its element size. */
+ * ROPE_ERR_ALIGN when a view's data is not aligned to its element size, cos
+ * or sin is not 16-byte aligned, or pos is not 4-byte aligned. */
 rope_status_t rope_apply(const rope_apply_desc_t *d, void *stream);
 
 /* Fill host float32 tables cos_out/sin_out, each [table_rows, R/2] row-major,

@@ -362,6 +362,25 @@ class Prepared:
         _check(self._lib.rope_bwd_q(self._q, self._pdesc, self._stream), "rope_bwd_q")
 
 
+class PreparedApply:
+    """A rope_apply call whose descriptor is built once (see Prepared)."""
+
+    def __init__(self, q, k, cos, sin, stream=None, **kw):
+        self._keep = (q, k, cos, sin, kw.get("pos"), kw.get("q_out"), kw.get("k_out"))
+        self.desc = make_apply_desc(q, k, cos, sin, **kw)
+        self._stream = _stream(stream)
+        self._pdesc = ctypes.byref(self.desc)
+        self._lib = lib()
+
+    def rope_apply(self):
+        _check(self._lib.rope_apply(self._pdesc, self._stream), "rope_apply")
+
+
+def prepare_apply(q, k, cos, sin, *, stream=None, **kw) -> PreparedApply:
+    """Build the descriptor of a rope_apply call once."""
+    return PreparedApply(q, k, cos, sin, stream=stream, **kw)
+
+
 def prepare(q, k, cos, sin, *, stream=None, **kw) -> Prepared:
     """Build the descriptor of a rope_*_qk / rope_*_q call once (see Prepared)."""
     return Prepared(q, k, cos, sin, stream=stream, **kw)

@@ -40,12 +40,16 @@ struct GpuLauncher {
   template <typename T, int V, int PAIR, bool AL, bool OOP>
   void launch() {
     const dim3 grid((unsigned)pl.grid), block((unsigned)pl.block);
-    if (pl.token && pl.single)
-      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, true, OOP>), grid, block, 0,
-                         st, pl.a);
-    else if (pl.token)
-      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, false, OOP>), grid, block, 0,
-                         st, pl.a);
+    const int mode = pl.token ? pl.token_mode() : -1;
+    if (mode == rope::kTokenOne)
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenOne, OOP>), grid,
+                         block, 0, st, pl.a);
+    else if (mode == rope::kTokenPacked)
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenPacked, OOP>),
+                         grid, block, 0, st, pl.a);
+    else if (mode == rope::kTokenLoop)
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenLoop, OOP>), grid,
+                         block, 0, st, pl.a);
     else
       hipLaunchKernelGGL((rope::rope_rows_kernel<T, V, PAIR, AL, 4, OOP>), grid, block, 0, st,
                          pl.a);

@@ -24,8 +24,10 @@
 // Two grid shapes share the same per-chunk device functions:
 //   rope_rows_kernel  : lanes over (token, chunk); each lane walks a group of
 //                       heads (Q heads first, then K heads). For prefill.
-//   rope_token_kernel : one token per workgroup iteration, lanes over (head,
-//                       chunk). For decode (seq_len 1) and small calls.
+//   rope_token_kernel : a few consecutive tokens per workgroup, lanes over
+//                       (token, head, chunk). For decode (seq_len 1), views
+//                       whose heads of a token are adjacent ([B,S,H,D], packed
+//                       QKV) and calls too small for the rows shape.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -75,6 +77,7 @@ struct Args {
   int32_t n_groups;          // rows kernel: head groups
   int32_t group_slow;        // rows kernel: workgroup ids run over tiles first
   int64_t n_tiles;           // rows kernel: 256-item tiles
+  int32_t tokens_per_block;  // token kernel: consecutive tokens per workgroup
   float sin_sign;            // +1 forward, -1 backward
 };
 
@@ -176,17 +179,23 @@ template <int V, int PAIR> struct ChunkGeom {
 // [rows, R/2] (or halves-duplicated [rows, R]) table these are NP contiguous
 // floats, aligned to min(16, 4*NP) bytes (the tables are 16-byte aligned and
 // the plan checks that the row stride keeps them so), and move in vector
-// loads; a repeat-interleaved table is read one value at a time.
+// loads (TVEC); a repeat-interleaved table is read one value at a time. TVEC
+// is chosen once at the top of each kernel, so each copy of the body is
+// straight-line code whose loads the compiler can wait for one by one.
 template <int V, int PAIR> struct Trig {
   static constexpr int NP = ChunkGeom<V, PAIR>::kPairs;
   static constexpr int W = NP < 4 ? NP : 4;  // floats per vector load
   typedef float vec_t __attribute__((ext_vector_type(W)));
   float c[NP], s[NP];
+  float sign;  // +1 forward, -1 backward; applied in the rotation, so that no
+               // arithmetic waits on the loads here
 
+  template <bool TVEC>
   ROPE_HD void load(const Args& a, int64_t p, int first) {
+    sign = a.sin_sign;
     const float* cr = a.cos + p * a.t_row;
     const float* sr = a.sin + p * a.t_row;
-    if (a.t_vec) {
+    if constexpr (TVEC) {
 #pragma unroll
       for (int j = 0; j < NP; j += W) {
         const vec_t cv = *reinterpret_cast<const vec_t*>(cr + first + j);
@@ -194,14 +203,14 @@ template <int V, int PAIR> struct Trig {
 #pragma unroll
         for (int w = 0; w < W; ++w) {
           c[j + w] = cv[w];
-          s[j + w] = a.sin_sign * sv[w];
+          s[j + w] = sv[w];
         }
       }
     } else {
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
         c[j] = cr[(int64_t)(first + j) * a.t_col];
-        s[j] = a.sin_sign * sr[(int64_t)(first + j) * a.t_col];
+        s[j] = sr[(int64_t)(first + j) * a.t_col];
       }
     }
   }
@@ -228,7 +237,7 @@ template <typename T, int V, int PAIR, bool ALIGNED> struct RowChunk {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         float y1, y2;
-        rotate_pair(to_f32(a.v[j]), to_f32(b.v[j]), t.c[j], t.s[j], y1, y2);
+        rotate_pair(to_f32(a.v[j]), to_f32(b.v[j]), t.c[j], t.sign * t.s[j], y1, y2);
         a.v[j] = from_f32<T>(y1);
         b.v[j] = from_f32<T>(y2);
       }
@@ -236,7 +245,8 @@ template <typename T, int V, int PAIR, bool ALIGNED> struct RowChunk {
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
         float y1, y2;
-        rotate_pair(to_f32(a.v[2 * j]), to_f32(a.v[2 * j + 1]), t.c[j], t.s[j], y1, y2);
+        rotate_pair(to_f32(a.v[2 * j]), to_f32(a.v[2 * j + 1]), t.c[j], t.sign * t.s[j], y1,
+                    y2);
         a.v[2 * j] = from_f32<T>(y1);
         a.v[2 * j + 1] = from_f32<T>(y2);
       }
@@ -273,9 +283,20 @@ ROPE_HD T* view_row(const View& v, int64_t h, int64_t b, int64_t s) {
   return reinterpret_cast<T*>(v.base) + (b * v.sb + h * v.sh + s * v.ss);
 }
 
-// Position of token (b, s), or -1 when the token passes through.
+// Position of token (b, s), or -1 when the token passes through. The index
+// array does not change during a launch (no written view overlaps it), so on
+// the device it is read through the constant address space: where (b, s) is
+// the same for the whole wave, that is one scalar load, whose wait does not
+// hold up the row loads already in flight.
 ROPE_HD int64_t token_pos(const Args& a, int64_t b, int64_t s) {
-  const int64_t p = a.pos ? (int64_t)a.pos[b * a.pos_bs + s] : s;
+  if (!a.pos) return s < a.table_rows ? s : -1;
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const const_i32* idx = reinterpret_cast<const const_i32*>(reinterpret_cast<uintptr_t>(a.pos));
+  const int64_t p = idx[b * a.pos_bs + s];
+#else
+  const int64_t p = a.pos[b * a.pos_bs + s];
+#endif
   return (p < 0 || p >= a.table_rows) ? -1 : p;
 }
 
@@ -324,7 +345,7 @@ ROPE_HD void copy_heads(const Args& a, const T* in, int64_t sh_in, T* out, int64
 // that each XCD owns one contiguous range of tiles was measured ~10% slower.
 constexpr int kRowsBlock = 256;
 
-template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP>
+template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP, bool TVEC>
 ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
   int64_t tile;
   int group;
@@ -347,9 +368,10 @@ ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
   const int q_lo = h_begin, q_hi = imin(h_end, a.n_heads_q);
   const int k_lo = imax(h_begin - a.n_heads_q, 0), k_hi = h_end - a.n_heads_q;
   const T* qi = view_row<T>(a.q_in, 0, b, s);
-  T* qo = view_row<T>(a.q_out, 0, b, s);
   const T* ki = view_row<T>(a.k_in, 0, b, s);
-  T* ko = view_row<T>(a.k_out, 0, b, s);
+  // in place the output views are the input views
+  T* qo = OOP ? view_row<T>(a.q_out, 0, b, s) : const_cast<T*>(qi);
+  T* ko = OOP ? view_row<T>(a.k_out, 0, b, s) : const_cast<T*>(ki);
 
   const int64_t p = token_pos(a, b, s);
   if (p < 0) {  // skipped token: in place nothing is read or written
@@ -363,7 +385,7 @@ ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
   }
 
   Trig<V, PAIR> t;
-  t.load(a, p, c * ChunkGeom<V, PAIR>::kPairs);
+  t.template load<TVEC>(a, p, c * ChunkGeom<V, PAIR>::kPairs);
   if (q_lo < q_hi)
     rotate_heads<T, V, PAIR, ALIGNED, U, OOP>(a, qi, a.q_in.sh, qo, a.q_out.sh, q_lo, q_hi, c,
                                               t);
@@ -372,15 +394,24 @@ ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
                                               t);
 }
 
+// The kernel entry, also run on the host by the emulator.
 template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP>
-__global__ void __launch_bounds__(kRowsBlock) rope_rows_kernel(Args a) {
-  rows_body<T, V, PAIR, ALIGNED, U, OOP>(a, blockIdx.x, threadIdx.x);
+ROPE_HD void rows_entry(const Args& a, int64_t block, int thread) {
+  if (a.t_vec)
+    rows_body<T, V, PAIR, ALIGNED, U, OOP, true>(a, block, thread);
+  else
+    rows_body<T, V, PAIR, ALIGNED, U, OOP, false>(a, block, thread);
 }
 
-// ------------------------------------------------------ token (decode) shape
-// One token per workgroup iteration; lanes cover (head, chunk) pairs of that
-// token. The head rows are requested before the position, so the row loads
-// overlap the dependent index -> cos/sin chain.
+template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP>
+__global__ void __launch_bounds__(kRowsBlock) rope_rows_kernel(Args a) {
+  rows_entry<T, V, PAIR, ALIGNED, U, OOP>(a, blockIdx.x, threadIdx.x);
+}
+
+// ------------------------------------------------------------- token shape
+// Lanes cover (head, chunk) items of a token. Each lane's head rows are
+// requested before the position, so the row loads overlap the dependent
+// index -> cos/sin chain.
 ROPE_HD void split_item(const Args& a, int it, int* h, int* c) {
   if (a.lanes_shift >= 0) {
     *h = it >> a.lanes_shift;
@@ -391,49 +422,150 @@ ROPE_HD void split_item(const Args& a, int it, int* h, int* c) {
   }
 }
 
-template <typename T, int V, int PAIR, bool ALIGNED, bool OOP>
-ROPE_HD void token_item(const Args& a, int64_t n, int it) {
-  const int64_t b = n / a.seq_len;
-  const int64_t s = n - b * a.seq_len;
-  int h, c;
-  split_item(a, it, &h, &c);
-  const bool is_q = h < a.n_heads_q;
-  const int hh = is_q ? h : h - a.n_heads_q;
-  const T* in = view_row<T>(is_q ? a.q_in : a.k_in, hh, b, s);
-  T* out = view_row<T>(is_q ? a.q_out : a.k_out, hh, b, s);
-  RowChunk<T, V, PAIR, ALIGNED> r;
-  r.load(in, c, a.half);
-  const int64_t p = token_pos(a, b, s);
-  if (p < 0) {
-    if constexpr (OOP) copy_span<T, V, ALIGNED>(in, out, 0, a.head_dim, c, a.lanes);
-    return;
+// Items per lane in the single-pass token kernel: enough that a lane keeps two
+// 16-byte row accesses in flight. A split-half chunk is already two accesses
+// (one per half); an interleaved chunk is one, so its lanes take two items.
+// (Measured on MI355X with interleaved pairs, [B,S,H,D] bf16: 67.7 -> 54.5 us
+// at [4,4096,32+8,128], 34.4 -> 28.7 us at [2,4096,16+4,256]; a second
+// split-half item per lane was 3-6 % slower.)
+constexpr int token_items_per_lane(int pairing) { return pairing == kInterleaved ? 2 : 1; }
+
+// K items of the token shape, run together: all row loads, then the
+// positions and cos/sin, then rotate and store. Item k is (head, chunk) item
+// it[k] of token n[k] and is stored only if live[k]; a lane whose item 0 is
+// not live has nothing to do. A dead item k > 0 loads item 0's row and
+// cos/sin instead of branching around its loads, so every load of the lane is
+// issued in one straight run. SAME: every item is of token n[0] (one token per
+// workgroup), so the token's position is read once.
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, bool TVEC, int K, bool SAME>
+ROPE_HD void token_items(const Args& a, const int64_t* n_in, const int* it_in,
+                         const bool* live) {
+  if (!live[0]) return;
+  int64_t n[K];
+  int it[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    n[k] = (k == 0 || live[k]) ? n_in[k] : n_in[0];
+    it[k] = (k == 0 || live[k]) ? it_in[k] : it_in[0];
   }
-  Trig<V, PAIR> t;
-  t.load(a, p, c * ChunkGeom<V, PAIR>::kPairs);
-  r.rotate(t);
-  r.store(out, c, a.half);
-  if constexpr (OOP) copy_span<T, V, ALIGNED>(in, out, 2 * a.half, a.head_dim, c, a.lanes);
+  const T* in[K];
+  T* out[K];
+  int c[K];
+  int64_t b[K], s[K], p[K];
+  RowChunk<T, V, PAIR, ALIGNED> r[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (SAME && k > 0) {
+      b[k] = b[0];
+      s[k] = s[0];
+    } else {
+      b[k] = a.seq_len == 1 ? n[k] : n[k] / a.seq_len;  // decode: no division
+      s[k] = n[k] - b[k] * a.seq_len;
+    }
+    int h;
+    split_item(a, it[k], &h, &c[k]);
+    const bool is_q = h < a.n_heads_q;
+    const int hh = is_q ? h : h - a.n_heads_q;
+    in[k] = view_row<T>(is_q ? a.q_in : a.k_in, hh, b[k], s[k]);
+    // in place the output view is the input view
+    out[k] = OOP ? view_row<T>(is_q ? a.q_out : a.k_out, hh, b[k], s[k]) : const_cast<T*>(in[k]);
+    r[k].load(in[k], c[k], a.half);
+  }
+  Trig<V, PAIR> t[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    p[k] = (SAME && k > 0) ? p[0] : token_pos(a, b[k], s[k]);
+    if (p[k] >= 0) t[k].template load<TVEC>(a, p[k], c[k] * ChunkGeom<V, PAIR>::kPairs);
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (k > 0 && !live[k]) continue;
+    if (p[k] < 0) {  // skipped token: in place nothing is written
+      if constexpr (OOP) copy_span<T, V, ALIGNED>(in[k], out[k], 0, a.head_dim, c[k], a.lanes);
+      continue;
+    }
+    r[k].rotate(t[k]);
+    r[k].store(out[k], c[k], a.half);
+    if constexpr (OOP)
+      copy_span<T, V, ALIGNED>(in[k], out[k], 2 * a.half, a.head_dim, c[k], a.lanes);
+  }
 }
 
-// SINGLE: the grid has one workgroup per token and each workgroup one lane
-// per (head, chunk), so no loop is needed (the decode case).
-template <typename T, int V, int PAIR, bool ALIGNED, bool SINGLE, bool OOP>
+// A workgroup owns tokens_per_block consecutive tokens at a time; its items
+// are numbered (token, head, chunk) with the chunk fastest, so that when the
+// heads of a token are adjacent in memory the workgroup walks one contiguous
+// stretch. Three instantiations, chosen by the planner:
+//   kTokenOne    : one token per workgroup, the grid covers every token, and
+//                  each lane holds at most token_items_per_lane(PAIR) items,
+//                  i and i + L for L lanes. The token index is uniform across
+//                  the wave, so the index load is a scalar load. Decode and
+//                  token-major prefill; kept apart so that its code is short.
+//   kTokenPacked : the same with tokens_per_block > 1 tokens per workgroup.
+//   kTokenLoop   : workgroups loop over tokens, one item per lane at a time.
+enum TokenMode : int { kTokenLoop = 0, kTokenPacked = 1, kTokenOne = 2 };
+
+template <typename T, int V, int PAIR, bool ALIGNED, int MODE, bool OOP, bool TVEC>
 ROPE_HD void token_body(const Args& a, int64_t block, int64_t grid, int thread,
                         int block_dim) {
   const int per_token = (a.n_heads_q + a.n_heads_k) * a.lanes;
-  if constexpr (SINGLE) {
-    if (thread < per_token) token_item<T, V, PAIR, ALIGNED, OOP>(a, block, thread);
+  const int tpb = a.tokens_per_block;
+  constexpr int K = token_items_per_lane(PAIR);
+  if constexpr (MODE == kTokenOne) {
+    const int L = (per_token + K - 1) / K;
+    if (thread >= L) return;  // the block is rounded up to whole waves
+    int64_t n[K];
+    int it[K];
+    bool live[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      n[k] = block;
+      it[k] = thread + k * L;
+      live[k] = it[k] < per_token;
+    }
+    token_items<T, V, PAIR, ALIGNED, OOP, TVEC, K, true>(a, n, it, live);
+  } else if constexpr (MODE == kTokenPacked) {
+    const int items = tpb * per_token;
+    const int L = (items + K - 1) / K;
+    if (thread >= L) return;
+    int64_t n[K];
+    int it[K];
+    bool live[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i = thread + k * L;
+      const int tl = i / per_token;
+      n[k] = block * tpb + tl;
+      it[k] = i - tl * per_token;
+      live[k] = i < items && n[k] < a.n_tokens;
+    }
+    token_items<T, V, PAIR, ALIGNED, OOP, TVEC, K, false>(a, n, it, live);
   } else {
-    for (int64_t n = block; n < a.n_tokens; n += grid)
-      for (int it = thread; it < per_token; it += block_dim)
-        token_item<T, V, PAIR, ALIGNED, OOP>(a, n, it);
+    const int per_block = tpb * per_token;
+    for (int64_t n0 = block * tpb; n0 < a.n_tokens; n0 += grid * tpb)
+      for (int i = thread; i < per_block; i += block_dim) {
+        const int tl = tpb == 1 ? 0 : i / per_token;
+        const int64_t n = n0 + tl;
+        const int it = i - tl * per_token;
+        const bool live = n < a.n_tokens;
+        token_items<T, V, PAIR, ALIGNED, OOP, TVEC, 1, true>(a, &n, &it, &live);
+      }
   }
 }
 
-template <typename T, int V, int PAIR, bool ALIGNED, bool SINGLE, bool OOP>
+// The kernel entry, also run on the host by the emulator.
+template <typename T, int V, int PAIR, bool ALIGNED, int MODE, bool OOP>
+ROPE_HD void token_entry(const Args& a, int64_t block, int64_t grid, int thread,
+                         int block_dim) {
+  if (a.t_vec)
+    token_body<T, V, PAIR, ALIGNED, MODE, OOP, true>(a, block, grid, thread, block_dim);
+  else
+    token_body<T, V, PAIR, ALIGNED, MODE, OOP, false>(a, block, grid, thread, block_dim);
+}
+
+template <typename T, int V, int PAIR, bool ALIGNED, int MODE, bool OOP>
 __global__ void __launch_bounds__(1024) rope_token_kernel(Args a) {
-  token_body<T, V, PAIR, ALIGNED, SINGLE, OOP>(a, blockIdx.x, gridDim.x, threadIdx.x,
-                                               blockDim.x);
+  token_entry<T, V, PAIR, ALIGNED, MODE, OOP>(a, blockIdx.x, gridDim.x, threadIdx.x,
+                                              blockDim.x);
 }
 
 }  // namespace rope

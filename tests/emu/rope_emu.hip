@@ -73,12 +73,17 @@ struct HostRunner {
   void go() {
     for (int64_t blk = 0; blk < pl.grid; ++blk)
       for (int t = 0; t < pl.block; ++t) {
-        if (pl.token && pl.single)
-          rope::token_body<T, V, PAIR, AL, true, OOP>(pl.a, blk, pl.grid, t, pl.block);
+        if (pl.token && pl.token_mode() == rope::kTokenOne)
+          rope::token_entry<T, V, PAIR, AL, rope::kTokenOne, OOP>(pl.a, blk, pl.grid, t,
+                                                                   pl.block);
+        else if (pl.token && pl.token_mode() == rope::kTokenPacked)
+          rope::token_entry<T, V, PAIR, AL, rope::kTokenPacked, OOP>(pl.a, blk, pl.grid, t,
+                                                                      pl.block);
         else if (pl.token)
-          rope::token_body<T, V, PAIR, AL, false, OOP>(pl.a, blk, pl.grid, t, pl.block);
+          rope::token_entry<T, V, PAIR, AL, rope::kTokenLoop, OOP>(pl.a, blk, pl.grid, t,
+                                                                    pl.block);
         else
-          rope::rows_body<T, V, PAIR, AL, 4, OOP>(pl.a, blk, t);
+          rope::rows_entry<T, V, PAIR, AL, 4, OOP>(pl.a, blk, t);
       }
   }
 
@@ -94,10 +99,11 @@ struct HostRunner {
 
 void print_plan(const rope::Plan& pl) {
   printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
-         "heads_per_group %d\nn_groups %d\ngroup_slow %d\nsingle %d\noop %d\nt_vec %d\n",
+         "heads_per_group %d\nn_groups %d\ngroup_slow %d\nsingle %d\noop %d\nt_vec %d\n"
+         "tokens_per_block %d\n",
          (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
          pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow, (int)pl.single,
-         (int)pl.oop, pl.a.t_vec);
+         (int)pl.oop, pl.a.t_vec, pl.a.tokens_per_block);
 }
 
 // test-only overrides of the rows-kernel grid (head-group size and order)
@@ -109,6 +115,11 @@ void apply_overrides(rope::Plan& pl, std::map<std::string, long long>& kv) {
     pl.grid = pl.a.n_tiles * pl.a.n_groups;
   }
   if (!pl.empty && !pl.token && kv.count("group_slow")) pl.a.group_slow = (int32_t)kv["group_slow"];
+  // token shape: a smaller grid than planned runs the grid-stride loop
+  if (!pl.empty && pl.token && kv["token_grid"] > 0 && kv["token_grid"] < pl.grid) {
+    pl.grid = kv["token_grid"];
+    pl.single = false;
+  }
 }
 
 rope_view_t read_view(std::map<std::string, long long>& kv, const std::string& name, char* base,

@@ -235,6 +235,9 @@ def call_apply(d):
     (dict(q_out=rp.RopeView(A16 + 4 * 64 * 2, 8 * 512, 64, 512)), ALIAS),  # Q out onto K in
     (dict(k_in=rp.RopeView(A16 + 4 * 64 * 2, 8 * 512, 64, -512)), SHAPE),
     (dict(k_in=rp.RopeView(None, 0, 0, 0)), NULL),
+    (dict(pos=A16 + 1024, pos_batch_stride=8), ALIAS),   # index entries inside written Q
+    (dict(cos=A16 + 2 * 512 * 2), ALIAS),                # cos table inside written rows
+    (dict(sin=A16 - 16), ALIAS),                         # sin table runs into written Q
 ])
 def test_apply_validation_errors(change, expected):
     assert call_apply(apply_desc(**change)) == expected
@@ -248,6 +251,9 @@ def test_apply_validation_errors(change, expected):
     dict(table_row_stride=64, table_col_stride=2),                 # repeat-interleaved table
     dict(n_heads_k=0, k_in=rp.RopeView(None, 0, 0, 0),             # broadcast input, Q only
          q_in=rp.RopeView(A16, 0, 64, 512), q_out=rp.RopeView(A16 * 8, 4 * 8 * 64, 8 * 64, 64)),
+    dict(q_out=rp.RopeView(A16 * 8, 4 * 8 * 64, 8 * 64, 64),       # tables and index may share
+         k_out=rp.RopeView(A16 * 9, 2 * 8 * 64, 8 * 64, 64),       # memory with inputs that are
+         cos=A16 + 2 * 512 * 2, pos=A16 + 1024, pos_batch_stride=8),  # only read
 ])
 def test_apply_accepts_valid_views(change):
     """Accepted descriptors get past validation; with no GPU the call then

@@ -465,3 +465,44 @@ def test_apply_matches_contiguous_entry_points_bitwise():
     for x, y, z in ((a_q, b_q, c_q), (a_k, b_k, c_k)):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
         assert torch.equal(x.view(torch.int16), z.view(torch.int16))
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_small_tokens_share_a_workgroup(direction):
+    """[2, 8192, 2+1, 64] as [B,S,H,D]: 12 lanes per token, so the token shape
+    packs 4 consecutive tokens into each workgroup on a 256-CU chip."""
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=8192, n_heads_q=2, n_heads_k=1,
+                                   head_dim=64, rotary_dim=64, table_rows=8192,
+                                   layout="bshd")
+    say(f"[gpu] small tokens {tuple(w.q_shape)} dir={direction}")
+    check_full(w, direction)
+
+
+def test_packed_qkv_full_size_sampled():
+    """The Llama prefill shape as one packed [4, 4096, 48 * 128] QKV buffer,
+    rotated in place forward then backward (the launches bench.py times),
+    checked on sampled tokens; the V part stays bit-exact."""
+    w = W.LLAMA_GQA_PREFILL
+    B, S, Hq, Hk, D = w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim
+    qkv, q, k = _packed_views(B, S, Hq, Hk, D, w.dtype, 35)
+    say(f"[gpu] packed qkv full size {tuple(qkv.shape)}")
+    cos, sin = gpu_tables(w)
+    g = qkv.to(DEV)
+    gq = g[..., :Hq * D].view(B, S, Hq, D)
+    gk = g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D)
+    prev = {"q": q, "k": k}
+    for direction in (1, -1):
+        rp.rope_apply(gq, gk, cos, sin, layout="bshd", direction=direction)
+        torch.cuda.synchronize()
+        b, s = _sample_tokens(w, 48, 2000 + direction)
+        bd, sd = b.to(DEV), s.to(DEV)
+        for name, gv in (("q", gq), ("k", gk)):
+            got = _gather(gv, bd, sd, "bshd").cpu()
+            inp = _gather(prev[name], b, s, "bshd")
+            ws = w.scaled(batch=1, seq_len=len(s), layout="bshd", n_heads_q=gv.shape[2])
+            ref = P.oracle_rope(ws, inp, direction, s.to(torch.int32), pos_batch_stride=0)
+            P.assert_parity(P.storage(got), ref, P.storage(inp), w.dtype, "bshd",
+                            w.rotary_dim, what=f"packed {name} dir={direction}")
+        prev = {"q": gq.cpu(), "k": gk.cpu()}
+    assert torch.equal(g[..., (Hq + Hk) * D:].cpu().view(torch.int16),
+                       qkv[..., (Hq + Hk) * D:].view(torch.int16))

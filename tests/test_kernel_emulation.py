@@ -8,6 +8,7 @@ and ragged size below, touches each element once, and computes what the
 oracle computes (same tolerances as the GPU parity tests).
 """
 import os
+import fcntl
 import subprocess
 import tempfile
 
@@ -31,16 +32,26 @@ CODES = {"dtype": {"f32": 0, "f16": 1, "bf16": 2}, "layout": {"bhsd": 0, "bshd":
          "launch": {"auto": 0, "rows": 1, "token": 2}}
 
 
+def _emu_stale():
+    return (not os.path.exists(EMU_BIN) or
+            os.path.getmtime(EMU_BIN) < max(os.path.getmtime(p) for p in DEPS))
+
+
 @pytest.fixture(scope="module")
 def emu():
-    if (not os.path.exists(EMU_BIN) or
-            os.path.getmtime(EMU_BIN) < max(os.path.getmtime(p) for p in DEPS)):
-        os.makedirs(os.path.dirname(EMU_BIN), exist_ok=True)
-        cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-host-only", "-O1", "-g",
-               "-std=c++17", "-ffp-contract=off", "-Xarch_host", "-fsanitize=address",
-               "-fno-omit-frame-pointer", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
-               "-o", EMU_BIN, EMU_SRC]
-        subprocess.run(cmd, check=True, capture_output=True)
+    # several pytest-xdist workers may get here at once: build under a lock,
+    # into a private file that is renamed into place when complete
+    os.makedirs(os.path.dirname(EMU_BIN), exist_ok=True)
+    with open(EMU_BIN + ".lock", "w") as lock:
+        fcntl.flock(lock, fcntl.LOCK_EX)
+        if _emu_stale():
+            tmp = f"{EMU_BIN}.{os.getpid()}"
+            cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-host-only", "-O1",
+                   "-g", "-std=c++17", "-ffp-contract=off", "-Xarch_host", "-fsanitize=address",
+                   "-fno-omit-frame-pointer", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+                   "-o", tmp, EMU_SRC]
+            subprocess.run(cmd, check=True, capture_output=True)
+            os.replace(tmp, EMU_BIN)
     return EMU_BIN
 
 
@@ -133,13 +144,21 @@ def test_both_grid_shapes(emu, name, launch):
 
 
 def test_auto_shape_selection(emu):
-    """Decode, and prefill too small to fill the chip with the rows shape even
-    at one head per lane, take the token shape; otherwise rows."""
+    """Decode, views whose heads of a token are adjacent ([B,S,H,D]), and
+    [B,H,S,D] prefill too small to fill the chip with the rows shape even at
+    one head per lane, take the token shape; otherwise rows."""
     assert check(emu, SMALL["decode"])["token"] == 1
     assert check(emu, SMALL["decode"], cus=1)["token"] == 1
     assert check(emu, SMALL["llama_ragged"])["token"] == 1  # 154 tokens on 256 CUs
     plan = check(emu, SMALL["llama_ragged"], cus=1)  # same tokens, a 1-CU device
     assert plan["token"] == 0 and plan["group_slow"] == 1 and plan["heads_per_group"] == 4
+    # the same tokens as [B,S,H,D]: token shape on any device
+    assert check(emu, SMALL["llama_ragged"].scaled(layout="bshd"), cus=1)["token"] == 1
+    assert check(emu, SMALL["bshd_interleaved_ragged"], cus=1)["token"] == 1
+    # one Q head: [B,S,1,D] is [B,1,S,D]; rows on a device it fills
+    plan = check(emu, SMALL["llama_ragged"].scaled(layout="bshd", n_heads_q=1, n_heads_k=1),
+                 cus=1)
+    assert plan["token"] == 0
 
 
 @pytest.mark.parametrize("cus", [1, 7, 256, 1000])
@@ -197,11 +216,51 @@ def test_interleaved_dims(emu, spec, vec, aligned):
 
 def test_single_pass_token_shape_only_when_the_grid_covers_everything(emu):
     assert check(emu, SMALL["decode"])["single"] == 1
-    plan = check(emu, SMALL["decode"], cus=1)  # 64 workgroups for 19 tokens: still one each
-    assert plan["single"] == 1
+    plan = check(emu, SMALL["decode"], cus=1)  # one workgroup per token on any device
+    assert plan["single"] == 1 and plan["grid"] == 19 and plan["tokens_per_block"] == 1
     w = SMALL["decode"].scaled(batch=100)
-    plan = check(emu, w, cus=1)  # 64 workgroups loop over 100 tokens
-    assert plan["token"] == 1 and plan["single"] == 0 and plan["grid"] == 64
+    plan = check(emu, w, cus=1, overrides=dict(token_grid=7))  # 7 workgroups loop over 100
+    assert plan["token"] == 1 and plan["single"] == 0 and plan["grid"] == 7
+
+
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("token_grid", [0, 3])
+@pytest.mark.parametrize("direction", [1, -1])
+def test_small_tokens_share_a_workgroup(emu, layout, token_grid, direction):
+    """3 heads x 4 lanes = 12 lanes per token: 21 consecutive tokens per
+    workgroup (252 of 256 lanes), one pass or a grid-stride loop, with a
+    ragged last group of tokens (400 = 19 * 21 + 1)."""
+    w = SMALL["llama_ragged"].scaled(n_heads_q=2, n_heads_k=1, head_dim=64, rotary_dim=64,
+                                     seq_len=200, table_rows=200, layout=layout)
+    plan = check(emu, w, direction, launch="token", cus=1,
+                 overrides=dict(token_grid=token_grid))
+    assert plan["tokens_per_block"] == 21 and plan["block"] == 256
+    assert plan["grid"] == (3 if token_grid else 20)
+    assert plan["single"] == (0 if token_grid else 1)
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_interleaved_lanes_take_two_items(emu, direction):
+    """Interleaved pairs: each token-shape lane takes items i and i + L. 32
+    heads x 8 chunks = 256 items on 128 lanes; then 15 items per token (odd)
+    packed 8 tokens to a workgroup: 120 items on 60 lanes, and a ragged last
+    workgroup of tokens."""
+    w = SMALL["bshd_interleaved_ragged"]
+    plan = check(emu, w, direction, launch="token")
+    assert plan["block"] == 128 and plan["single"] == 1 and plan["tokens_per_block"] == 1
+    w = w.scaled(n_heads_q=3, n_heads_k=2, head_dim=40, rotary_dim=24)
+    plan = check(emu, w, direction, launch="token", cus=1)
+    assert plan["lanes"] == 3 and plan["tokens_per_block"] == 8 and plan["block"] == 64
+    assert plan["single"] == 1 and plan["grid"] == 17  # ceil(135 / 8)
+    check(emu, w, direction, launch="token", cus=1, overrides=dict(token_grid=5))
+
+
+def test_token_packing_keeps_the_chip_filled(emu):
+    """Tokens per workgroup shrink so the grid keeps 16 workgroups per CU."""
+    w = SMALL["llama_ragged"].scaled(n_heads_q=2, n_heads_k=1, head_dim=64, rotary_dim=64,
+                                     layout="bshd")
+    assert check(emu, w, cus=1)["tokens_per_block"] == 9  # 154 // 16
+    assert check(emu, w, cus=256)["tokens_per_block"] == 1
 
 
 def test_many_heads_loop_in_token_shape(emu):
