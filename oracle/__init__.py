@@ -51,15 +51,15 @@ def _bind(lib):
     lib.oracle_freq.restype = ctypes.c_double
     lib.oracle_freq.argtypes = [ctypes.c_double, _I64, _I64]
     lib.oracle_table.restype = None
-    lib.oracle_table.argtypes = [ctypes.c_double, _I64, _I64, _P, _P]
+    lib.oracle_table.argtypes = [ctypes.c_double, ctypes.c_double, _I64, _I64, _P, _P]
     lib.oracle_rope.restype = ctypes.c_int
     lib.oracle_rope.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, _I64, _I64, _I64, _I64, _I64,
-                                ctypes.c_double, _P, _I64, _I64]
+                                ctypes.c_double, ctypes.c_double, _P, _I64, _I64]
     lib.oracle_rope_exact.restype = ctypes.c_int
     lib.oracle_rope_exact.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       _I64, _I64, _I64, _I64, _I64, ctypes.c_double,
-                                      _P, _I64, _I64]
+                                      ctypes.c_double, _P, _I64, _I64]
     lib.oracle_to_bf16_bits.restype = ctypes.c_uint16
     lib.oracle_to_bf16_bits.argtypes = [ctypes.c_double]
     lib.oracle_to_f16_bits.restype = ctypes.c_uint16
@@ -113,21 +113,24 @@ def freq(theta: float, rotary_dim: int, i: int, lib=None) -> float:
     return (lib or load()).oracle_freq(theta, rotary_dim, i)
 
 
-def table(theta: float, rotary_dim: int, rows: int, lib=None):
-    """The oracle's own fp32 cos/sin tables, each [rows, R/2]."""
+def table(theta: float, rotary_dim: int, rows: int, interpolate_factor: float = 1.0,
+          lib=None):
+    """The oracle's own fp32 cos/sin tables, each [rows, R/2]: row p holds
+    cos/sin of (p / interpolate_factor) * freq_i."""
     half = rotary_dim // 2
     c = np.empty((rows, half), np.float32)
     s = np.empty((rows, half), np.float32)
-    (lib or load()).oracle_table(theta, rotary_dim, rows, _ptr(c), _ptr(s))
+    (lib or load()).oracle_table(theta, interpolate_factor, rotary_dim, rows, _ptr(c), _ptr(s))
     return c, s
 
 
 def rope(x: np.ndarray, dtype: str, *, layout: str = "bhsd", pairing: str = "split_half",
          direction: int = 1, rotary_dim: Optional[int] = None, theta: float = 10000.0,
          pos=None, pos_batch_stride: int = 0, table_rows: Optional[int] = None,
-         lib=None) -> np.ndarray:
+         interpolate_factor: float = 1.0, lib=None) -> np.ndarray:
     """Table-mode RoPE of storage array `x` (float32, or uint16 bits for f16/bf16).
 
+    Positions are divided by `interpolate_factor` before the angle is formed.
     Returns a new array of the same storage type and shape.
     """
     x = np.ascontiguousarray(x, dtype=NP_STORAGE[dtype])
@@ -138,7 +141,7 @@ def rope(x: np.ndarray, dtype: str, *, layout: str = "bhsd", pairing: str = "spl
     y = np.empty_like(x)
     rc = (lib or load()).oracle_rope(_ptr(x), _ptr(y), DTYPES[dtype], LAYOUTS[layout],
                                      PAIRINGS[pairing], direction, B, H, S, D, R, theta,
-                                     _ptr(p), pos_batch_stride, rows)
+                                     interpolate_factor, _ptr(p), pos_batch_stride, rows)
     if rc:
         raise OracleError(f"oracle_rope rejected its arguments (code {rc})")
     return y
@@ -147,7 +150,8 @@ def rope(x: np.ndarray, dtype: str, *, layout: str = "bhsd", pairing: str = "spl
 def rope_exact(x: np.ndarray, *, layout: str = "bhsd", pairing: str = "split_half",
                direction: int = 1, rotary_dim: Optional[int] = None,
                theta: float = 10000.0, pos=None, pos_batch_stride: int = 0,
-               table_rows: Optional[int] = None, lib=None) -> np.ndarray:
+               table_rows: Optional[int] = None, interpolate_factor: float = 1.0,
+               lib=None) -> np.ndarray:
     """Exact-mode RoPE in binary64 (unrounded cos/sin), for invariant checks."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     B, H, S, D = _dims(x.shape, layout)
@@ -157,7 +161,8 @@ def rope_exact(x: np.ndarray, *, layout: str = "bhsd", pairing: str = "split_hal
     y = np.empty_like(x)
     rc = (lib or load()).oracle_rope_exact(_ptr(x), _ptr(y), LAYOUTS[layout],
                                            PAIRINGS[pairing], direction, B, H, S, D, R,
-                                           theta, _ptr(p), pos_batch_stride, rows)
+                                           theta, interpolate_factor, _ptr(p),
+                                           pos_batch_stride, rows)
     if rc:
         raise OracleError(f"oracle_rope_exact rejected its arguments (code {rc})")
     return y

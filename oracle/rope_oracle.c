@@ -12,9 +12,13 @@
  *       rotary-embedding-torch docs, Key Parameters: `theta` is the base of
  *       the frequencies (default 10000) and `dim` is the width of the part
  *       being rotated, so the exponent runs over the rotary dim R.
- *   angle  = p * freq_i for the token's position p
+ *   angle  = (p / interpolate_factor) * freq_i for the token's position p
  *       "Rotary Embedding Kernel", Overview: applied per position along the
- *       sequence.
+ *       sequence. rotary-embedding-torch docs, Key Parameters:
+ *       `interpolate_factor` scales sequence positions (default 1.0); read
+ *       here as a divisor (a factor k > 1 squeezes k times more positions
+ *       into the same angles, i.e. position interpolation). The division is
+ *       one binary64 operation, exact for factor 1.
  *   (x1, x2) -> (x1*cos - x2*sin, x1*sin + x2*cos)
  *       "Rotary Embedding Kernel", Overview (the rotation of one pair).
  *   pairs (x[i], x[i + R/2]) or (x[2i], x[2i+1])
@@ -149,22 +153,28 @@ double oracle_freq(double theta, int64_t rotary_dim, int64_t i) {
   return pow(theta, expo);
 }
 
-/* Table entries of row `p`, column `i`: cos and sin of p*freq_i, each
+/* The angle of position p at frequency i. */
+static double angle_of(double theta, double interp, int64_t rotary_dim, int64_t p,
+                       int64_t i) {
+  return ((double)p / interp) * oracle_freq(theta, rotary_dim, i);
+}
+
+/* Table entries of row `p`, column `i`: cos and sin of the angle, each
  * rounded once to float32. */
-void oracle_table_entry(double theta, int64_t rotary_dim, int64_t p, int64_t i,
-                        float *c32, float *s32) {
-  double angle = (double)p * oracle_freq(theta, rotary_dim, i);
+void oracle_table_entry(double theta, double interp, int64_t rotary_dim, int64_t p,
+                        int64_t i, float *c32, float *s32) {
+  double angle = angle_of(theta, interp, rotary_dim, p, i);
   *c32 = (float)cos(angle);
   *s32 = (float)sin(angle);
 }
 
 /* The whole [rows, R/2] table, row-major (for the table pins). */
-void oracle_table(double theta, int64_t rotary_dim, int64_t rows, float *cos_out,
-                  float *sin_out) {
+void oracle_table(double theta, double interp, int64_t rotary_dim, int64_t rows,
+                  float *cos_out, float *sin_out) {
   int64_t half = rotary_dim / 2;
   for (int64_t p = 0; p < rows; ++p)
     for (int64_t i = 0; i < half; ++i)
-      oracle_table_entry(theta, rotary_dim, p, i, &cos_out[p * half + i],
+      oracle_table_entry(theta, interp, rotary_dim, p, i, &cos_out[p * half + i],
                          &sin_out[p * half + i]);
 }
 
@@ -196,8 +206,9 @@ static int64_t token_position(const int32_t *pos, int64_t pos_batch_stride,
 
 static int check_args(int dtype, int layout, int pairing, int direction, int64_t B,
                       int64_t H, int64_t S, int64_t D, int64_t R, int64_t table_rows,
-                      const int32_t *pos) {
+                      const int32_t *pos, double interp) {
   if (dtype < ORC_F32 || dtype > ORC_BF16) return -3;
+  if (!(interp > 0.0) || !isfinite(interp)) return -2;
   if (layout != ORC_BHSD && layout != ORC_BSHD) return -4;
   if (pairing != ORC_SPLIT_HALF && pairing != ORC_INTERLEAVED) return -4;
   if (direction != 1 && direction != -1) return -2;
@@ -214,9 +225,10 @@ static int check_args(int dtype, int layout, int pairing, int direction, int64_t
  */
 int oracle_rope(const void *x, void *y, int dtype, int layout, int pairing,
                 int direction, int64_t B, int64_t H, int64_t S, int64_t D, int64_t R,
-                double theta, const int32_t *pos, int64_t pos_batch_stride,
+                double theta, double interp, const int32_t *pos, int64_t pos_batch_stride,
                 int64_t table_rows) {
-  int rc = check_args(dtype, layout, pairing, direction, B, H, S, D, R, table_rows, pos);
+  int rc = check_args(dtype, layout, pairing, direction, B, H, S, D, R, table_rows, pos,
+                      interp);
   if (rc) return rc;
   int64_t es = elem_size(dtype);
   if (x != y) memcpy(y, x, (size_t)(B * H * S * D * es)); /* untouched lanes */
@@ -228,7 +240,7 @@ int oracle_rope(const void *x, void *y, int dtype, int layout, int pairing,
         int64_t row = row_offset(layout, H, S, D, b, h, s);
         for (int64_t i = 0; i < R / 2; ++i) {
           float c32, s32;
-          oracle_table_entry(theta, R, p, i, &c32, &s32);
+          oracle_table_entry(theta, interp, R, p, i, &c32, &s32);
           double c = c32, sn = (double)direction * (double)s32;
           int64_t j1, j2;
           pair_dims(pairing, R, i, &j1, &j2);
@@ -246,8 +258,10 @@ int oracle_rope(const void *x, void *y, int dtype, int layout, int pairing,
 /* Exact mode: binary64 in and out, unrounded cos/sin of the binary64 angle. */
 int oracle_rope_exact(const double *x, double *y, int layout, int pairing, int direction,
                       int64_t B, int64_t H, int64_t S, int64_t D, int64_t R, double theta,
-                      const int32_t *pos, int64_t pos_batch_stride, int64_t table_rows) {
-  int rc = check_args(ORC_F32, layout, pairing, direction, B, H, S, D, R, table_rows, pos);
+                      double interp, const int32_t *pos, int64_t pos_batch_stride,
+                      int64_t table_rows) {
+  int rc = check_args(ORC_F32, layout, pairing, direction, B, H, S, D, R, table_rows, pos,
+                      interp);
   if (rc) return rc;
   if (x != y) memcpy(y, x, (size_t)(B * H * S * D) * sizeof(double));
   for (int64_t b = 0; b < B; ++b)
@@ -257,7 +271,7 @@ int oracle_rope_exact(const double *x, double *y, int layout, int pairing, int d
         if (p < 0) continue;
         int64_t row = row_offset(layout, H, S, D, b, h, s);
         for (int64_t i = 0; i < R / 2; ++i) {
-          double angle = (double)p * oracle_freq(theta, R, i);
+          double angle = angle_of(theta, interp, R, p, i);
           double c = cos(angle), sn = (double)direction * sin(angle);
           int64_t j1, j2;
           pair_dims(pairing, R, i, &j1, &j2);

@@ -38,13 +38,15 @@ def ord16(bits: np.ndarray) -> np.ndarray:
 
 def oracle_rope(w: W.Workload, x: torch.Tensor, direction: int,
                 pos: Optional[torch.Tensor], pos_batch_stride: Optional[int] = None,
-                table_rows: Optional[int] = None) -> np.ndarray:
+                table_rows: Optional[int] = None,
+                interpolate_factor: float = 1.0) -> np.ndarray:
     return orc.rope(storage(x), w.dtype, layout=w.layout, pairing=w.pairing,
                     direction=direction, rotary_dim=w.rotary_dim, theta=w.theta,
                     pos=None if pos is None else pos.numpy(),
                     pos_batch_stride=w.pos_batch_stride if pos_batch_stride is None
                     else pos_batch_stride,
-                    table_rows=w.table_rows if table_rows is None else table_rows)
+                    table_rows=w.table_rows if table_rows is None else table_rows,
+                    interpolate_factor=interpolate_factor)
 
 
 def masked_tokens(w: W.Workload, pos: Optional[torch.Tensor], table_rows=None,

@@ -49,6 +49,10 @@ MUTANTS = {
     "exact_mode_sign": ("y[row + j1] = x1 * c - x2 * sn;", "y[row + j1] = x1 * c + x2 * sn;"),
     "exact_mode_pairs_crossed": ("double x1 = y[row + j1], x2 = y[row + j2];",
                                  "double x1 = y[row + j2], x2 = y[row + j1];"),
+    "interp_multiplies": ("return ((double)p / interp) * oracle_freq(theta, rotary_dim, i);",
+                          "return ((double)p * interp) * oracle_freq(theta, rotary_dim, i);"),
+    "interp_ignored": ("return ((double)p / interp) * oracle_freq(theta, rotary_dim, i);",
+                       "return (double)p * oracle_freq(theta, rotary_dim, i);"),
     "pass_through_dims_rotated": ("for (int64_t i = 0; i < R / 2; ++i) {\n          float c32, s32;",
                                   "for (int64_t i = 0; i < D / 2; ++i) {\n          float c32, s32;"),
 }

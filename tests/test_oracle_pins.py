@@ -423,3 +423,74 @@ def test_rejects_bad_arguments(orc):
         orc.rope(x, "f32", rotary_dim=3)  # odd R
     with pytest.raises(orc.OracleError):
         orc.rope(x, "f32", table_rows=2)  # S > table rows without an index
+
+
+# ---------------------------------------------------------------- interpolate_factor
+# rotary-embedding-torch docs, Key Parameters: `interpolate_factor` scales the
+# sequence positions (default 1.0). Read as a divisor: angle = (p / s) * freq_i.
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_interpolate_factor_one_is_no_scaling(orc, dtype):
+    w = W.TINY_F32.scaled(dtype=dtype)
+    x = W.tensors(w)["q"]
+    from tests import _parity as P
+    xs = P.storage(x)
+    assert np.array_equal(orc.rope(xs, dtype, theta=w.theta),
+                          orc.rope(xs, dtype, theta=w.theta, interpolate_factor=1.0))
+
+
+@pytest.mark.parametrize("s,scale", [(2.0, 2), (4.0, 4), (0.5, None)])
+def test_interpolate_factor_divides_positions(orc, s, scale):
+    """With factor s, position p rotates as position p / s does with factor 1,
+    bit for bit when p / s is exact: s = 2 at 2q equals 1 at q, and s = 1/2
+    at q equals 1 at 2q."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((1, 3, 17, 32)).astype(np.float32)
+    q = rng.integers(0, 3000, 17).astype(np.int32)
+    kw = dict(theta=10000.0, table_rows=20000)
+    if scale is not None:
+        got = orc.rope(x, "f32", pos=(q * scale).astype(np.int32), interpolate_factor=s, **kw)
+        ref = orc.rope(x, "f32", pos=q, **kw)
+    else:
+        got = orc.rope(x, "f32", pos=q, interpolate_factor=s, **kw)
+        ref = orc.rope(x, "f32", pos=(2 * q).astype(np.int32), **kw)
+    assert np.array_equal(got, ref)
+
+
+def test_interpolated_table_matches_mpmath(orc):
+    """A non-dyadic factor: entries equal cos/sin of (p / 3) * freq_i in
+    binary64, evaluated in 60-digit arithmetic and rounded once to float32."""
+    rng = np.random.default_rng(43)
+    theta, R, rows, s = 10000.0, 64, 5000, 3.0
+    c, sn = orc.table(theta, R, rows, interpolate_factor=s)
+    c1, _ = orc.table(theta, R, rows)
+    assert not np.array_equal(c, c1)
+    for _ in range(300):
+        p = int(rng.integers(0, rows))
+        i = int(rng.integers(0, R // 2))
+        angle = (float(p) / s) * orc.freq(theta, R, i)  # the binary64 angle
+        with mpmath.workdps(60):
+            a = mpmath.mpf(angle)
+            mc, ms = mpmath.cos(a), mpmath.sin(a)
+        for got, ref in ((c[p, i], mc), (sn[p, i], ms)):
+            if float(got) != X.rn24_mp(ref):
+                assert X.near_f32_midpoint(ref), (p, i, got, ref)
+
+
+def test_exact_mode_interpolation_composes(orc):
+    """Exact mode with factor s at positions m equals factor 1 at the real
+    positions m / s (checked through composition: s = 4, positions 4q)."""
+    rng = np.random.default_rng(45)
+    x = rng.standard_normal((1, 2, 9, 16))
+    q = rng.integers(0, 800, 9).astype(np.int32)
+    kw = dict(theta=10000.0, table_rows=5000)
+    y = orc.rope_exact(x, pos=(4 * q).astype(np.int32), interpolate_factor=4.0, **kw)
+    z = orc.rope_exact(x, pos=q, **kw)
+    np.testing.assert_allclose(y, z, rtol=0, atol=1e-12)
+
+
+def test_rejects_bad_interpolate_factor(orc):
+    x = np.zeros((1, 1, 4, 8), np.float32)
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(orc.OracleError):
+            orc.rope(x, "f32", interpolate_factor=s)
