@@ -47,11 +47,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, pos) -> int:
+def algorithmic_bytes(w, pos, tables: bool = True) -> int:
     """Bytes the method must move for one call on workload w.
 
     read + write of the first R dims of every rotated Q and K row, each
-    distinct cos/sin row once (2 tables x R/2 x 4 B), each index once.
+    distinct cos/sin row once (2 tables x R/2 x 4 B; none when the angles are
+    computed from theta), each index once.
     """
     import numpy as np
     e = 4 if w.dtype == "f32" else 2
@@ -71,7 +72,7 @@ def algorithmic_bytes(w, pos) -> int:
         distinct = int(np.unique(pv[valid]).size)
         idx_bytes = 4 * int(np.unique(idx).size)
     rotated = e * R * n_tok * rows_h
-    return 2 * rotated + 4 * R * distinct + idx_bytes
+    return 2 * rotated + (4 * R * distinct if tables else 0) + idx_bytes
 
 
 def device_inputs(w, sets: int, which=("q", "k", "dq", "dk")):
@@ -123,7 +124,10 @@ def time_prefill(w, steps: int, warmup: int, sets: int):
     return dict(total_ms=total_ms, wall_s=wall, pos=pos, host=host)
 
 
-def time_decode(calls: int = 2000, warmup: int = 50):
+def time_decode(calls: int = 2000, warmup: int = 50, theta: bool = False):
+    """Decode-shape forward calls: back to back from Python, one at a time
+    between events, and replayed from a captured HIP graph. theta: angles
+    computed from theta through rope_apply instead of read from tables."""
     import torch
     import rotary_position_embedding_fwd_amd as rp
     import workloads as W
@@ -134,16 +138,23 @@ def time_decode(calls: int = 2000, warmup: int = 50):
     t = W.tensors(w)
     q, k = t["q"].cuda(), t["k"].cuda()
     stream = torch.cuda.current_stream()
-    call = rp.prepare(q, k, cos, sin, layout=w.layout, pairing=w.pairing,
-                      rotary_dim=w.rotary_dim, pos=pos, stream=stream)
+    def make(st):
+        if theta:
+            c = rp.prepare_apply(q, k, None, None, layout=w.layout, pairing=w.pairing,
+                                 rotary_dim=w.rotary_dim, pos=pos, theta=w.theta,
+                                 max_positions=w.table_rows, stream=st)
+            return c.rope_apply
+        return rp.prepare(q, k, cos, sin, layout=w.layout, pairing=w.pairing,
+                          rotary_dim=w.rotary_dim, pos=pos, stream=st).rope_fwd_qk
+    call = make(stream)
     for _ in range(warmup):
-        call.rope_fwd_qk()
+        call()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(calls):
-        call.rope_fwd_qk()
+        call()
     b.record(stream)
     torch.cuda.synchronize()
     per_call_us = a.elapsed_time(b) * 1000.0 / calls
@@ -152,7 +163,7 @@ def time_decode(calls: int = 2000, warmup: int = 50):
            for _ in range(200)]
     for e0, e1 in evs:
         e0.record(stream)
-        call.rope_fwd_qk()
+        call()
         e1.record(stream)
     torch.cuda.synchronize()
     kern = sorted(e0.elapsed_time(e1) * 1000.0 for e0, e1 in evs)
@@ -162,10 +173,9 @@ def time_decode(calls: int = 2000, warmup: int = 50):
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.graph(g, stream=side):
-        gcall = rp.prepare(q, k, cos, sin, layout=w.layout, pairing=w.pairing,
-                           rotary_dim=w.rotary_dim, pos=pos, stream=side)
+        gcall = make(side)
         for _ in range(per_graph):
-            gcall.rope_fwd_qk()
+            gcall()
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
@@ -175,8 +185,9 @@ def time_decode(calls: int = 2000, warmup: int = 50):
     b.record(stream)
     torch.cuda.synchronize()
     graph_us = a.elapsed_time(b) * 1000.0 / (per_graph * replays)
-    nbytes = algorithmic_bytes(w, pos.cpu())
-    return {"workload": w.name, "us_per_call_graph_replay": round(graph_us, 3),
+    nbytes = algorithmic_bytes(w, pos.cpu(), tables=not theta)
+    return {"workload": w.name, "angles": "theta" if theta else "tables",
+            "us_per_call_graph_replay": round(graph_us, 3),
             "us_per_call_back_to_back": round(per_call_us, 3),
             "us_kernel_event_median": round(kern[len(kern) // 2], 3),
             "algorithmic_bytes": nbytes, "calls": calls,
@@ -272,6 +283,46 @@ def _time_calls(out, fwd, bwd, sets, nbytes, target_s, stream, method=None):
         out[f"{name}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         out[f"{name}_pct_of_hbm_peak"] = round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)
         out[f"{name}_reps"] = reps
+
+
+def time_theta(target_s: float = 0.15):
+    """Angles computed from theta (no cos/sin tables): rope_apply on the Llama
+    prefill workload ([B,H,S,D], rows shape) and on its packed-QKV form (token
+    shape), forward and backward in place; and decode calls replayed from a
+    captured HIP graph."""
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    results = []
+    stream = torch.cuda.current_stream()
+    w = W.LLAMA_GQA_PREFILL
+    nbytes = algorithmic_bytes(w, None, tables=False)
+    _, sets = device_inputs(w, 3, ("q", "k"))
+    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, theta=w.theta,
+              max_positions=w.table_rows, stream=stream)
+    fwd = [rp.prepare_apply(x["q"], x["k"], None, None, **kw) for x in sets]
+    bwd = [rp.prepare_apply(x["q"], x["k"], None, None, direction=-1, **kw) for x in sets]
+    out = {"workload": w.name, "launch": "theta_angles", "buffer_sets": len(sets),
+           "algorithmic_bytes_per_call": nbytes}
+    _time_calls(out, fwd, bwd, len(sets), nbytes, target_s, stream, method="rope_apply")
+    results.append(out)
+    del sets, fwd, bwd
+    B, S, Hq, Hk, D = w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim
+    host = W.normal((B, S, (Hq + 2 * Hk) * D), w.dtype, w.seed("q"))
+    bufs = [host.cuda() for _ in range(3)]
+    views = [(g[..., :Hq * D].view(B, S, Hq, D), g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D))
+             for g in bufs]
+    kw["layout"] = "bshd"
+    fwd = [rp.prepare_apply(q, k, None, None, **kw) for q, k in views]
+    bwd = [rp.prepare_apply(q, k, None, None, direction=-1, **kw) for q, k in views]
+    out = {"workload": w.name, "launch": "theta_angles_packed_qkv_in_place", "buffer_sets": 3,
+           "algorithmic_bytes_per_call": nbytes}
+    _time_calls(out, fwd, bwd, 3, nbytes, target_s, stream, method="rope_apply")
+    results.append(out)
+    del bufs, views, fwd, bwd
+    torch.cuda.empty_cache()
+    results.append(time_decode(theta=True))
+    return results
 
 
 def time_general_form(w, target_s: float = 0.15):
@@ -489,6 +540,8 @@ def main():
     ap.add_argument("--general-form", action="store_true",
                     help="time only rope_apply on the Llama prefill shape as packed QKV, "
                          "in place and out of place")
+    ap.add_argument("--theta", action="store_true",
+                    help="time the path with cos/sin computed from theta (no tables)")
     ap.add_argument("--layout-matrix", action="store_true",
                     help="rows vs token launch on token-major views, by shape and pairing")
     args = ap.parse_args()
@@ -509,6 +562,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.theta:
+        for res in time_theta():
+            print(json.dumps(res), flush=True)
+        return
     if args.layout_matrix:
         for res in time_layout_matrix():
             print(json.dumps(res), flush=True)

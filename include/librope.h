@@ -85,15 +85,22 @@ typedef enum rope_dtype { ROPE_F32 = 0, ROPE_F16 = 1, ROPE_BF16 = 2 } rope_dtype
 typedef enum rope_layout { ROPE_BHSD = 0, ROPE_BSHD = 1 } rope_layout_t;
 typedef enum rope_pairing { ROPE_SPLIT_HALF = 0, ROPE_INTERLEAVED = 1 } rope_pairing_t;
 
-/* Which grid shape to launch. AUTO picks by size: one token per workgroup
- * (lanes over heads) when there are few tokens, as at decode (seq_len 1);
- * otherwise token rows across lanes with a loop over heads. The two shapes
- * run the same per-pair arithmetic and give bit-identical results. */
+/* Which grid shape to launch. AUTO walks memory in order: the token shape
+ * when a token's heads are adjacent ([B,S,H,D], packed QKV) and at decode
+ * (seq_len 1), the rows shape for [B,H,S,D] unless there are too few tokens
+ * to fill the device. The two shapes run the same per-pair arithmetic and
+ * give bit-identical results. */
 typedef enum rope_launch {
   ROPE_LAUNCH_AUTO = 0,
   ROPE_LAUNCH_ROWS = 1,  /* lanes over (token, chunk), loop over heads */
-  ROPE_LAUNCH_TOKEN = 2  /* one token per workgroup, lanes over (head, chunk) */
+  ROPE_LAUNCH_TOKEN = 2  /* a few tokens per workgroup, lanes over (token, head, chunk) */
 } rope_launch_t;
+
+/* Where rope_apply takes cos and sin from. */
+typedef enum rope_angles {
+  ROPE_ANGLES_TABLE = 0, /* the caller's cos/sin tables */
+  ROPE_ANGLES_THETA = 1  /* computed in the kernel from theta and interpolate_factor */
+} rope_angles_t;
 
 typedef struct rope_desc {
   int64_t batch;       /* B >= 0 */
@@ -187,6 +194,19 @@ typedef struct rope_apply_desc {
   int64_t table_col_stride;  /* 1 or 2 */
   const int32_t *pos;        /* device int32 indices or NULL (p = s) */
   int64_t pos_batch_stride;
+  /* angles == ROPE_ANGLES_THETA: no tables. cos, sin and the table strides
+   * are ignored (cos and sin may be NULL); table_rows only bounds the
+   * positions (an index >= table_rows passes through, as with tables).
+   * Frequency i of position p is cos/sin of (p / interpolate_factor) *
+   * theta^(-2i/R) (rotary-embedding-torch docs, Key Parameters: `theta` is
+   * the frequency base, `interpolate_factor` scales the positions, here as a
+   * divisor), computed in binary64 and rounded once to float32 per value:
+   * the values rope_build_table would store, except where an exact value
+   * lies within ~1e-15 relative of a float32 rounding boundary. */
+  double theta;              /* > 0, finite */
+  double interpolate_factor; /* > 0, finite; 1 = positions as given */
+  int32_t angles;            /* rope_angles_t */
+  int32_t reserved;          /* set to 0 */
 } rope_apply_desc_t;
 
 /* Rotate Q (and K) as described by `d`, in place or out of place, on `stream`.
@@ -199,23 +219,28 @@ typedef struct rope_apply_desc {
  * that interleave token by token (packed QKV) without sharing elements are
  * accepted. No written view may meet the byte range of cos, sin or the index
  * entries the call reads. Any of these is ROPE_ERR_ALIAS.
- * Errors: as rope_fwd_qk; ROPE_ERR_SHAPE also for negative strides or a
- * table stride that cannot hold R/2 frequencies; ROPE_ERR_LAYOUT for a
- * direction other than +-1 or a table column stride other than 1 or 2;
+ * Errors: as rope_fwd_qk; ROPE_ERR_SHAPE also for negative strides, a table
+ * stride that cannot hold R/2 frequencies, or (ROPE_ANGLES_THETA) a theta
+ * or interpolate_factor that is not finite and > 0, or R > 8192;
+ * ROPE_ERR_LAYOUT for a direction other than +-1, a table column stride
+ * other than 1 or 2, or an unknown `angles`;
  * ROPE_ERR_ALIGN when a view's data is not aligned to its element size, cos
  * or sin is not 16-byte aligned, or pos is not 4-byte aligned. */
 rope_status_t rope_apply(const rope_apply_desc_t *d, void *stream);
 
 /* Fill host float32 tables cos_out/sin_out, each [table_rows, R/2] row-major,
- * with cos and sin of p * theta^(-2i/R) for row p and column i: the exponent
- * -2i/R and the angle are formed in binary64 and each entry is rounded once
- * to float32 (rotary-embedding-torch docs, Key Parameters: `theta` is the base
- * of the frequencies, default 10000; "Rotary Embedding Kernel": cos/sin are
- * precomputed). Host memory, caller-owned; runs on the calling thread.
+ * with cos and sin of (p / interpolate_factor) * theta^(-2i/R) for row p and
+ * column i: the exponent -2i/R, the scaled position and the angle are formed
+ * in binary64 and each entry is rounded once to float32 (rotary-embedding-torch
+ * docs, Key Parameters: `theta` is the base of the frequencies, default
+ * 10000; `interpolate_factor` scales the positions, default 1; "Rotary
+ * Embedding Kernel": cos/sin are precomputed). Host memory, caller-owned;
+ * runs on the calling thread.
  * Returns ROPE_ERR_NULL for NULL outputs with non-empty work and
- * ROPE_ERR_SHAPE for a negative size, an odd rotary_dim or theta <= 0. */
+ * ROPE_ERR_SHAPE for a negative size, an odd rotary_dim, or a theta or
+ * interpolate_factor that is not finite and > 0. */
 rope_status_t rope_build_table(float *cos_out, float *sin_out, int64_t table_rows,
-                               int64_t rotary_dim, double theta);
+                               int64_t rotary_dim, double theta, double interpolate_factor);
 
 /* A static, human-readable name for a status code ("unknown status" for
  * codes this library never returns). */

@@ -77,7 +77,14 @@ class RopeApplyDesc(ctypes.Structure):
         ("table_col_stride", ctypes.c_int64),
         ("pos", ctypes.c_void_p),
         ("pos_batch_stride", ctypes.c_int64),
+        ("theta", ctypes.c_double),
+        ("interpolate_factor", ctypes.c_double),
+        ("angles", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
+
+
+ANGLES_TABLE, ANGLES_THETA = 0, 1
 
 
 class RopeError(RuntimeError):
@@ -107,7 +114,8 @@ def lib():
             getattr(L, name).restype = ctypes.c_int
         L.rope_apply.argtypes = [ctypes.POINTER(RopeApplyDesc), P]
         L.rope_apply.restype = ctypes.c_int
-        L.rope_build_table.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double]
+        L.rope_build_table.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                       ctypes.c_double]
         L.rope_build_table.restype = ctypes.c_int
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_status_string.restype = ctypes.c_char_p
@@ -259,13 +267,20 @@ def make_apply_desc(q, k, cos, sin, *, q_out=None, k_out=None, direction: int = 
                     layout: str = "bhsd", pairing: str = "split_half",
                     rotary_dim: Optional[int] = None, pos=None,
                     pos_batch_stride: Optional[int] = None, launch: str = "auto",
-                    table_layout: str = "half") -> RopeApplyDesc:
+                    table_layout: str = "half", theta: Optional[float] = None,
+                    interpolate_factor: float = 1.0,
+                    max_positions: Optional[int] = None) -> RopeApplyDesc:
     """rope_apply_desc_t for (possibly strided) torch views q, k (k may be None)
     and optional outputs q_out, k_out of the same shapes.
 
     table_layout: "half" = [rows, R/2]; "duplicated" = [rows, R] holding
     cat(f, f); "interleaved" = [rows, R] holding each value twice in a row.
     The table's row stride is taken from the tensor, so row-sliced views work.
+
+    theta: compute cos/sin in the kernel from theta and interpolate_factor
+    instead of reading tables (cos and sin must then be None);
+    max_positions bounds the positions as table_rows does (default: seq_len
+    without an index, else 2^31 - 1).
     """
     B, Hq, S, D = _dims(q, layout)
     Hk = 0
@@ -278,15 +293,22 @@ def make_apply_desc(q, k, cos, sin, *, q_out=None, k_out=None, direction: int = 
             raise ValueError(f"{name} must match its input's shape and dtype")
     R = D if rotary_dim is None else int(rotary_dim)
     import torch
-    if cos.dtype != torch.float32 or sin.dtype != torch.float32 or cos.shape != sin.shape:
-        raise ValueError("cos and sin must be matching float32 tables")
-    if cos.dim() != 2 or cos.stride(1) != 1 or sin.stride(1) != 1 or cos.stride(0) != sin.stride(0):
-        raise ValueError("cos/sin must be 2-d with contiguous rows and equal strides")
-    if table_layout not in TABLE_LAYOUTS:
-        raise ValueError(f"table_layout must be one of {TABLE_LAYOUTS}")
-    want = R // 2 if table_layout == "half" else R
-    if cos.shape[1] != want:
-        raise ValueError(f"a {table_layout!r} table has {want} columns, got {cos.shape[1]}")
+    if theta is not None:
+        if cos is not None or sin is not None:
+            raise ValueError("pass either cos/sin tables or theta, not both")
+    else:
+        if cos is None or sin is None:
+            raise ValueError("cos and sin tables are required unless theta is given")
+        if cos.dtype != torch.float32 or sin.dtype != torch.float32 or cos.shape != sin.shape:
+            raise ValueError("cos and sin must be matching float32 tables")
+        if (cos.dim() != 2 or cos.stride(1) != 1 or sin.stride(1) != 1 or
+                cos.stride(0) != sin.stride(0)):
+            raise ValueError("cos/sin must be 2-d with contiguous rows and equal strides")
+        if table_layout not in TABLE_LAYOUTS:
+            raise ValueError(f"table_layout must be one of {TABLE_LAYOUTS}")
+        want = R // 2 if table_layout == "half" else R
+        if cos.shape[1] != want:
+            raise ValueError(f"a {table_layout!r} table has {want} columns, got {cos.shape[1]}")
     d = RopeApplyDesc()
     d.batch, d.seq_len, d.head_dim, d.rotary_dim = B, S, D, R
     d.n_heads_q, d.n_heads_k = Hq, Hk
@@ -301,10 +323,18 @@ def make_apply_desc(q, k, cos, sin, *, q_out=None, k_out=None, direction: int = 
         d.q_out = _view(q_out, layout)
     if k_out is not None:
         d.k_out = _view(k_out, layout)
-    d.cos, d.sin = cos.data_ptr(), sin.data_ptr()
-    d.table_rows = cos.shape[0]
-    d.table_row_stride = cos.stride(0)
-    d.table_col_stride = 2 if table_layout == "interleaved" else 1
+    if theta is not None:
+        d.angles = ANGLES_THETA
+        d.theta, d.interpolate_factor = float(theta), float(interpolate_factor)
+        if max_positions is None:
+            max_positions = S if pos is None else 2 ** 31 - 1
+        d.table_rows = int(max_positions)
+        d.table_col_stride = 1
+    else:
+        d.cos, d.sin = cos.data_ptr(), sin.data_ptr()
+        d.table_rows = cos.shape[0]
+        d.table_row_stride = cos.stride(0)
+        d.table_col_stride = 2 if table_layout == "interleaved" else 1
     if pos is not None:
         if pos.dtype != torch.int32 or not pos.is_contiguous():
             raise ValueError("pos must be a contiguous int32 tensor")
@@ -386,12 +416,14 @@ def prepare(q, k, cos, sin, *, stream=None, **kw) -> Prepared:
     return Prepared(q, k, cos, sin, stream=stream, **kw)
 
 
-def rope_build_table(table_rows: int, rotary_dim: int, theta: float = 10000.0):
-    """Host float32 cos/sin tables [table_rows, R/2] (CPU torch tensors)."""
+def rope_build_table(table_rows: int, rotary_dim: int, theta: float = 10000.0,
+                     interpolate_factor: float = 1.0):
+    """Host float32 cos/sin tables [table_rows, R/2] (CPU torch tensors); row p
+    holds the angles of position p / interpolate_factor."""
     import torch
     half = rotary_dim // 2
     cos = torch.empty((table_rows, half), dtype=torch.float32)
     sin = torch.empty((table_rows, half), dtype=torch.float32)
     _check(lib().rope_build_table(cos.data_ptr(), sin.data_ptr(), table_rows, rotary_dim,
-                                  float(theta)), "rope_build_table")
+                                  float(theta), float(interpolate_factor)), "rope_build_table")
     return cos, sin

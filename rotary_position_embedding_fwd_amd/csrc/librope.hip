@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0: rope_apply
+constexpr int kVersion = 10200;  // 1.2.0: angles computed from theta, interpolate_factor
 constexpr int kMaxDevices = 64;
 
 // Compute units per device, read once per device.
@@ -41,15 +41,26 @@ struct GpuLauncher {
   void launch() {
     const dim3 grid((unsigned)pl.grid), block((unsigned)pl.block);
     const int mode = pl.token ? pl.token_mode() : -1;
-    if (mode == rope::kTokenOne)
-      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenOne, OOP>), grid,
-                         block, 0, st, pl.a);
+    const unsigned lds = (unsigned)pl.lds_bytes;
+    constexpr int RT = rope::kSrcRuntime;
+    if (mode == rope::kTokenOne && pl.a.angles)
+      hipLaunchKernelGGL(
+          (rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenOne, OOP, rope::kTrigTheta>), grid,
+          block, lds, st, pl.a);
+    else if (mode == rope::kTokenOne && pl.a.t_vec)
+      hipLaunchKernelGGL(
+          (rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenOne, OOP, rope::kTrigVec>), grid,
+          block, 0, st, pl.a);
+    else if (mode == rope::kTokenOne)
+      hipLaunchKernelGGL(
+          (rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenOne, OOP, rope::kTrigScalar>),
+          grid, block, 0, st, pl.a);
     else if (mode == rope::kTokenPacked)
-      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenPacked, OOP>),
-                         grid, block, 0, st, pl.a);
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenPacked, OOP, RT>),
+                         grid, block, lds, st, pl.a);
     else if (mode == rope::kTokenLoop)
-      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenLoop, OOP>), grid,
-                         block, 0, st, pl.a);
+      hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenLoop, OOP, RT>),
+                         grid, block, 0, st, pl.a);
     else
       hipLaunchKernelGGL((rope::rope_rows_kernel<T, V, PAIR, AL, 4, OOP>), grid, block, 0, st,
                          pl.a);
@@ -109,8 +120,9 @@ rope_status_t rope_bwd_q(void* dq, const rope_desc_t* d, void* stream) {
 rope_status_t rope_apply(const rope_apply_desc_t* d, void* stream) { return run_apply(d, stream); }
 
 rope_status_t rope_build_table(float* cos_out, float* sin_out, int64_t table_rows,
-                               int64_t rotary_dim, double theta) {
-  if (table_rows < 0 || rotary_dim < 0 || (rotary_dim & 1) || !(theta > 0.0))
+                               int64_t rotary_dim, double theta, double interpolate_factor) {
+  if (table_rows < 0 || rotary_dim < 0 || (rotary_dim & 1) || !(theta > 0.0) ||
+      !std::isfinite(theta) || !(interpolate_factor > 0.0) || !std::isfinite(interpolate_factor))
     return ROPE_ERR_SHAPE;
   const int64_t half = rotary_dim / 2;
   if (table_rows == 0 || half == 0) return ROPE_OK;
@@ -119,7 +131,7 @@ rope_status_t rope_build_table(float* cos_out, float* sin_out, int64_t table_row
     // theta^(-2i/R), exponent and power in binary64
     const double inv_freq = std::pow(theta, -(2.0 * (double)i) / (double)rotary_dim);
     for (int64_t p = 0; p < table_rows; ++p) {
-      const double angle = (double)p * inv_freq;
+      const double angle = ((double)p / interpolate_factor) * inv_freq;
       cos_out[p * half + i] = (float)std::cos(angle);
       sin_out[p * half + i] = (float)std::sin(angle);
     }
@@ -131,11 +143,11 @@ const char* rope_status_string(rope_status_t s) {
   switch (s) {
     case ROPE_OK: return "ok";
     case ROPE_ERR_NULL: return "a required pointer is NULL";
-    case ROPE_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case ROPE_ERR_SHAPE: return "invalid or inconsistent sizes, or a number out of range";
     case ROPE_ERR_DTYPE: return "unknown dtype";
-    case ROPE_ERR_LAYOUT: return "unknown layout, pairing or launch shape";
+    case ROPE_ERR_LAYOUT: return "unknown layout, pairing, launch shape or angle source";
     case ROPE_ERR_ALIGN: return "misaligned pointer";
-    case ROPE_ERR_ALIAS: return "q and k overlap";
+    case ROPE_ERR_ALIAS: return "written data overlaps other operands";
     case ROPE_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";

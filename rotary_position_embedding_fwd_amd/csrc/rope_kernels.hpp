@@ -51,34 +51,45 @@ struct View {
   int64_t sb, sh, ss;  // element strides
 };
 
-// Everything a launch needs, passed by value as the kernel argument.
+// Everything a launch needs, passed by value as the kernel argument. Fields
+// are ordered so that an in-place token-shape call (decode) reads only the
+// first three 64-byte lines of the argument block, which the scalar cache
+// fetches in few round trips; fields of the rows kernel and of out-of-place
+// calls come last.
 struct Args {
-  View q_in, k_in;           // K views unused when n_heads_k == 0
-  View q_out, k_out;         // equal to the inputs in place
+  // line 0: input views
+  View q_in, k_in;           // K view unused when n_heads_k == 0
+  // line 1: pointers and 64-bit sizes
   const float* cos;          // frequency i of position p at [p*t_row + i*t_col]
   const float* sin;
-  int64_t t_row;             // table row stride (floats)
-  int32_t t_col;             // table column stride (1 or 2)
-  int32_t t_vec;             // 1: a chunk's cos/sin are contiguous and aligned
   const int32_t* pos;        // nullptr: p = s
+  int64_t t_row;             // table row stride (floats)
   int64_t pos_bs;            // index batch stride
   int64_t table_rows;
-  int64_t batch;
   int64_t seq_len;
   int64_t n_tokens;          // batch * seq_len
-  int64_t n_items;           // n_tokens * lanes (rows kernel)
-  int32_t head_dim;          // D (out-of-place copies)
+  // line 2: 32-bit fields
   int32_t half;              // R / 2
   int32_t n_heads_q;
   int32_t n_heads_k;
   int32_t lanes;             // chunks per token row
   int32_t lanes_shift;       // log2(lanes) when lanes is a power of two, else -1
+  float sin_sign;            // +1 forward, -1 backward
+  int32_t t_col;             // table column stride (1 or 2)
+  int32_t t_vec;             // 1: a chunk's cos/sin are contiguous and aligned
+  int32_t angles;            // 0: cos/sin tables; 1: computed from theta
+  int32_t tokens_per_block;  // token kernel: consecutive tokens per workgroup
+  int32_t head_dim;          // D (out-of-place copies)
   int32_t heads_per_group;   // rows kernel: heads walked by one lane
   int32_t n_groups;          // rows kernel: head groups
   int32_t group_slow;        // rows kernel: workgroup ids run over tiles first
+  // the rest
   int64_t n_tiles;           // rows kernel: 256-item tiles
-  int32_t tokens_per_block;  // token kernel: consecutive tokens per workgroup
-  float sin_sign;            // +1 forward, -1 backward
+  int64_t n_items;           // rows kernel: n_tokens * lanes
+  int64_t batch;
+  View q_out, k_out;         // equal to the inputs in place
+  double l2_step;            // angles from theta: -2 log2(theta) / R
+  double interp;             // angles from theta: positions are divided by it
 };
 
 // ------------------------------------------------------------ storage I/O
@@ -175,13 +186,80 @@ template <int V, int PAIR> struct ChunkGeom {
   static constexpr int kPairs = PAIR == kSplitHalf ? V : V / 2;
 };
 
-// cos/sin of one chunk: frequencies first .. first+NP-1 of row p. With a
+// ------------------------------------------------- angles from theta
+// cos and sin of the binary64 angle x, each rounded once to float32.
+// Argument reduction after W. J. Cody and W. Waite (Software Manual for the
+// Elementary Functions, 1980): x = k (pi/2) + r with k the integer nearest to
+// x (2/pi) and pi/2 carried as two binary64 parts (hi + lo = pi/2 to within
+// 1.5e-33), so that r is within ~1e-16 of its exact value for |x| < 2^40
+// (the planner keeps angles below that). Then the Taylor series of sin and
+// cos about 0 on |r| <= pi/4 (+ a sliver), through the r^15 and r^16 terms:
+// the first terms dropped are below 5e-17. Everything before the final
+// rounding is binary64, so the float32 results are the correctly rounded
+// cos(x) and sin(x) except within ~1e-16 of a rounding boundary. The quadrant
+// k mod 4 then swaps and negates the pair.
+ROPE_HD void sincos_f32(double x, float* c_out, float* s_out) {
+  constexpr double kTwoOverPi = 0x1.45f306dc9c883p-1;  // 2/pi
+  constexpr double kPio2Hi = 0x1.921fb54442d18p+0;     // pi/2 rounded to binary64
+  constexpr double kPio2Lo = 0x1.1a62633145c07p-54;    // pi/2 - kPio2Hi, rounded
+  const double k = __builtin_rint(x * kTwoOverPi);
+  double r = __builtin_fma(-k, kPio2Hi, x);
+  r = __builtin_fma(-k, kPio2Lo, r);
+  const double r2 = r * r;
+  // sin r = r + r^3 (-1/3! + r^2/5! - r^4/7! + ... - r^12/15!)
+  double ps = -1.0 / 1307674368000.0;
+  ps = __builtin_fma(ps, r2, 1.0 / 6227020800.0);
+  ps = __builtin_fma(ps, r2, -1.0 / 39916800.0);
+  ps = __builtin_fma(ps, r2, 1.0 / 362880.0);
+  ps = __builtin_fma(ps, r2, -1.0 / 5040.0);
+  ps = __builtin_fma(ps, r2, 1.0 / 120.0);
+  ps = __builtin_fma(ps, r2, -1.0 / 6.0);
+  const double sr = __builtin_fma(r * r2, ps, r);
+  // cos r = 1 + r^2 (-1/2! + r^2/4! - r^4/6! + ... + r^14/16!)
+  double pc = 1.0 / 20922789888000.0;
+  pc = __builtin_fma(pc, r2, -1.0 / 87178291200.0);
+  pc = __builtin_fma(pc, r2, 1.0 / 479001600.0);
+  pc = __builtin_fma(pc, r2, -1.0 / 3628800.0);
+  pc = __builtin_fma(pc, r2, 1.0 / 40320.0);
+  pc = __builtin_fma(pc, r2, -1.0 / 720.0);
+  pc = __builtin_fma(pc, r2, 1.0 / 24.0);
+  pc = __builtin_fma(pc, r2, -0.5);
+  const double cr = __builtin_fma(r2, pc, 1.0);
+  // x = k pi/2 + r: quadrant 1 gives (-sin r, cos r), 2 (-cos r, -sin r),
+  // 3 (sin r, -cos r)
+  const int q = (int)((int64_t)k & 3);
+  const double cv = (q & 1) ? sr : cr;
+  const double sv = (q & 1) ? cr : sr;
+  *c_out = (float)((q == 1 || q == 2) ? -cv : cv);
+  *s_out = (float)((q & 2) ? -sv : sv);
+}
+
+// The angle of frequency i at position p: (p / interpolate_factor) * theta^(-2i/R),
+// the power formed as exp2(i * (-2 log2(theta) / R)), all in binary64. The
+// frequency does not depend on p, so callers can form it before the position
+// arrives; a factor of 1 skips the division (whose result would be p).
+ROPE_HD double theta_freq(const Args& a, int i) { return exp2((double)i * a.l2_step); }
+ROPE_HD double theta_pos(const Args& a, int64_t p) {
+  return a.interp == 1.0 ? (double)p : (double)p / a.interp;
+}
+ROPE_HD double theta_angle(const Args& a, int64_t p, int i) {
+  return theta_pos(a, p) * theta_freq(a, i);
+}
+
+// Where a chunk's cos/sin come from.
+enum TrigSource : int {
+  kTrigVec = 0,     // [rows, R/2]-style table, NP contiguous floats per chunk
+  kTrigScalar = 1,  // any other table layout, one value at a time
+  kTrigTheta = 2,   // computed from theta by this lane
+};
+
+// cos/sin of one chunk: frequencies first .. first+NP-1 at position p. With a
 // [rows, R/2] (or halves-duplicated [rows, R]) table these are NP contiguous
 // floats, aligned to min(16, 4*NP) bytes (the tables are 16-byte aligned and
 // the plan checks that the row stride keeps them so), and move in vector
-// loads (TVEC); a repeat-interleaved table is read one value at a time. TVEC
-// is chosen once at the top of each kernel, so each copy of the body is
-// straight-line code whose loads the compiler can wait for one by one.
+// loads (kTrigVec); a repeat-interleaved table is read one value at a time.
+// The source is chosen once at the top of each kernel, so each copy of the
+// body is straight-line code whose loads the compiler can wait for one by one.
 template <int V, int PAIR> struct Trig {
   static constexpr int NP = ChunkGeom<V, PAIR>::kPairs;
   static constexpr int W = NP < 4 ? NP : 4;  // floats per vector load
@@ -190,28 +268,45 @@ template <int V, int PAIR> struct Trig {
   float sign;  // +1 forward, -1 backward; applied in the rotation, so that no
                // arithmetic waits on the loads here
 
-  template <bool TVEC>
+  template <int SRC>
   ROPE_HD void load(const Args& a, int64_t p, int first) {
     sign = a.sin_sign;
-    const float* cr = a.cos + p * a.t_row;
-    const float* sr = a.sin + p * a.t_row;
-    if constexpr (TVEC) {
+    if constexpr (SRC == kTrigTheta) {
 #pragma unroll
-      for (int j = 0; j < NP; j += W) {
-        const vec_t cv = *reinterpret_cast<const vec_t*>(cr + first + j);
-        const vec_t sv = *reinterpret_cast<const vec_t*>(sr + first + j);
+      for (int j = 0; j < NP; ++j) sincos_f32(theta_angle(a, p, first + j), &c[j], &s[j]);
+      return;
+    } else {
+      const float* cr = a.cos + p * a.t_row;
+      const float* sr = a.sin + p * a.t_row;
+      if constexpr (SRC == kTrigVec) {
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-          c[j + w] = cv[w];
-          s[j + w] = sv[w];
+        for (int j = 0; j < NP; j += W) {
+          const vec_t cv = *reinterpret_cast<const vec_t*>(cr + first + j);
+          const vec_t sv = *reinterpret_cast<const vec_t*>(sr + first + j);
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            c[j + w] = cv[w];
+            s[j + w] = sv[w];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          c[j] = cr[(int64_t)(first + j) * a.t_col];
+          s[j] = sr[(int64_t)(first + j) * a.t_col];
         }
       }
-    } else {
+    }
+  }
+
+  // From the workgroup's shared cos/sin: (cos, sin) pairs of one token's
+  // frequencies, starting at float index 2 * first.
+  ROPE_HD void from_shared(const Args& a, const float* lds, int first) {
+    sign = a.sin_sign;
 #pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        c[j] = cr[(int64_t)(first + j) * a.t_col];
-        s[j] = sr[(int64_t)(first + j) * a.t_col];
-      }
+    for (int j = 0; j < NP; ++j) {
+      c[j] = lds[2 * (first + j)];
+      s[j] = lds[2 * (first + j) + 1];
     }
   }
 };
@@ -345,7 +440,7 @@ ROPE_HD void copy_heads(const Args& a, const T* in, int64_t sh_in, T* out, int64
 // that each XCD owns one contiguous range of tiles was measured ~10% slower.
 constexpr int kRowsBlock = 256;
 
-template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP, bool TVEC>
+template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP, int SRC>
 ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
   int64_t tile;
   int group;
@@ -385,7 +480,7 @@ ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
   }
 
   Trig<V, PAIR> t;
-  t.template load<TVEC>(a, p, c * ChunkGeom<V, PAIR>::kPairs);
+  t.template load<SRC>(a, p, c * ChunkGeom<V, PAIR>::kPairs);
   if (q_lo < q_hi)
     rotate_heads<T, V, PAIR, ALIGNED, U, OOP>(a, qi, a.q_in.sh, qo, a.q_out.sh, q_lo, q_hi, c,
                                               t);
@@ -397,10 +492,12 @@ ROPE_HD void rows_body(const Args& a, int64_t block, int thread) {
 // The kernel entry, also run on the host by the emulator.
 template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP>
 ROPE_HD void rows_entry(const Args& a, int64_t block, int thread) {
-  if (a.t_vec)
-    rows_body<T, V, PAIR, ALIGNED, U, OOP, true>(a, block, thread);
+  if (a.angles)
+    rows_body<T, V, PAIR, ALIGNED, U, OOP, kTrigTheta>(a, block, thread);
+  else if (a.t_vec)
+    rows_body<T, V, PAIR, ALIGNED, U, OOP, kTrigVec>(a, block, thread);
   else
-    rows_body<T, V, PAIR, ALIGNED, U, OOP, false>(a, block, thread);
+    rows_body<T, V, PAIR, ALIGNED, U, OOP, kTrigScalar>(a, block, thread);
 }
 
 template <typename T, int V, int PAIR, bool ALIGNED, int U, bool OOP>
@@ -430,66 +527,94 @@ ROPE_HD void split_item(const Args& a, int it, int* h, int* c) {
 // split-half item per lane was 3-6 % slower.)
 constexpr int token_items_per_lane(int pairing) { return pairing == kInterleaved ? 2 : 1; }
 
-// K items of the token shape, run together: all row loads, then the
-// positions and cos/sin, then rotate and store. Item k is (head, chunk) item
-// it[k] of token n[k] and is stored only if live[k]; a lane whose item 0 is
-// not live has nothing to do. A dead item k > 0 loads item 0's row and
-// cos/sin instead of branching around its loads, so every load of the lane is
-// issued in one straight run. SAME: every item is of token n[0] (one token per
-// workgroup), so the token's position is read once.
-template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, bool TVEC, int K, bool SAME>
-ROPE_HD void token_items(const Args& a, const int64_t* n_in, const int* it_in,
-                         const bool* live) {
-  if (!live[0]) return;
-  int64_t n[K];
-  int it[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    n[k] = (k == 0 || live[k]) ? n_in[k] : n_in[0];
-    it[k] = (k == 0 || live[k]) ? it_in[k] : it_in[0];
-  }
+// K items of the token shape, run together, as one lane's state: begin()
+// issues all row loads; positions() reads the tokens' positions; then either
+// finish<SRC>() loads or computes the cos/sin and rotates and stores, or, for
+// angles computed once per workgroup into shared memory, finish_shared()
+// reads them there. Item k is (head, chunk) item it[k] of token n[k] (local
+// token tl[k] of the workgroup) and is stored only if live[k]; a lane whose
+// item 0 is not live has nothing to do. A dead item k > 0 loads item 0's row
+// and cos/sin instead of branching around its loads, so every load of the
+// lane is issued in one straight run. SAME: every item is of token n[0] (one
+// token per workgroup), so the token's position is read once.
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, int K, bool SAME>
+struct TokenWork {
+  static constexpr int NP = ChunkGeom<V, PAIR>::kPairs;
   const T* in[K];
   T* out[K];
-  int c[K];
+  int c[K], tl[K];
   int64_t b[K], s[K], p[K];
+  bool live[K];
   RowChunk<T, V, PAIR, ALIGNED> r[K];
+
+  ROPE_HD bool begin(const Args& a, const int64_t* n_in, const int* it_in, const int* tl_in,
+                     const bool* live_in) {
+    if (!live_in[0]) return false;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    if (SAME && k > 0) {
-      b[k] = b[0];
-      s[k] = s[0];
-    } else {
-      b[k] = a.seq_len == 1 ? n[k] : n[k] / a.seq_len;  // decode: no division
-      s[k] = n[k] - b[k] * a.seq_len;
+    for (int k = 0; k < K; ++k) {
+      live[k] = live_in[k];
+      const bool own = k == 0 || live[k];
+      const int64_t n = own ? n_in[k] : n_in[0];
+      const int it = own ? it_in[k] : it_in[0];
+      tl[k] = own ? tl_in[k] : tl_in[0];
+      if (SAME && k > 0) {
+        b[k] = b[0];
+        s[k] = s[0];
+      } else {
+        b[k] = a.seq_len == 1 ? n : n / a.seq_len;  // decode: no division
+        s[k] = n - b[k] * a.seq_len;
+      }
+      int h;
+      split_item(a, it, &h, &c[k]);
+      const bool is_q = h < a.n_heads_q;
+      const int hh = is_q ? h : h - a.n_heads_q;
+      in[k] = view_row<T>(is_q ? a.q_in : a.k_in, hh, b[k], s[k]);
+      // in place the output view is the input view
+      out[k] = OOP ? view_row<T>(is_q ? a.q_out : a.k_out, hh, b[k], s[k]) : const_cast<T*>(in[k]);
+      r[k].load(in[k], c[k], a.half);
     }
-    int h;
-    split_item(a, it[k], &h, &c[k]);
-    const bool is_q = h < a.n_heads_q;
-    const int hh = is_q ? h : h - a.n_heads_q;
-    in[k] = view_row<T>(is_q ? a.q_in : a.k_in, hh, b[k], s[k]);
-    // in place the output view is the input view
-    out[k] = OOP ? view_row<T>(is_q ? a.q_out : a.k_out, hh, b[k], s[k]) : const_cast<T*>(in[k]);
-    r[k].load(in[k], c[k], a.half);
+    return true;
   }
-  Trig<V, PAIR> t[K];
+
+  ROPE_HD void positions(const Args& a) {
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    p[k] = (SAME && k > 0) ? p[0] : token_pos(a, b[k], s[k]);
-    if (p[k] >= 0) t[k].template load<TVEC>(a, p[k], c[k] * ChunkGeom<V, PAIR>::kPairs);
+    for (int k = 0; k < K; ++k) p[k] = (SAME && k > 0) ? p[0] : token_pos(a, b[k], s[k]);
   }
+
+  ROPE_HD void store(const Args& a, const Trig<V, PAIR>* t) {
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    if (k > 0 && !live[k]) continue;
-    if (p[k] < 0) {  // skipped token: in place nothing is written
-      if constexpr (OOP) copy_span<T, V, ALIGNED>(in[k], out[k], 0, a.head_dim, c[k], a.lanes);
-      continue;
+    for (int k = 0; k < K; ++k) {
+      if (k > 0 && !live[k]) continue;
+      if (p[k] < 0) {  // skipped token: in place nothing is written
+        if constexpr (OOP) copy_span<T, V, ALIGNED>(in[k], out[k], 0, a.head_dim, c[k], a.lanes);
+        continue;
+      }
+      r[k].rotate(t[k]);
+      r[k].store(out[k], c[k], a.half);
+      if constexpr (OOP)
+        copy_span<T, V, ALIGNED>(in[k], out[k], 2 * a.half, a.head_dim, c[k], a.lanes);
     }
-    r[k].rotate(t[k]);
-    r[k].store(out[k], c[k], a.half);
-    if constexpr (OOP)
-      copy_span<T, V, ALIGNED>(in[k], out[k], 2 * a.half, a.head_dim, c[k], a.lanes);
   }
-}
+
+  template <int SRC>
+  ROPE_HD void finish(const Args& a) {
+    positions(a);
+    Trig<V, PAIR> t[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (p[k] >= 0) t[k].template load<SRC>(a, p[k], c[k] * NP);
+    store(a, t);
+  }
+
+  // lds: the workgroup's (cos, sin) pairs, [token][frequency] (see theta_fill)
+  ROPE_HD void finish_shared(const Args& a, const float* lds) {
+    Trig<V, PAIR> t[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (p[k] >= 0) t[k].from_shared(a, lds, tl[k] * a.half + c[k] * NP);
+    store(a, t);
+  }
+};
 
 // A workgroup owns tokens_per_block consecutive tokens at a time; its items
 // are numbered (token, head, chunk) with the chunk fastest, so that when the
@@ -504,42 +629,48 @@ ROPE_HD void token_items(const Args& a, const int64_t* n_in, const int* it_in,
 //   kTokenLoop   : workgroups loop over tokens, one item per lane at a time.
 enum TokenMode : int { kTokenLoop = 0, kTokenPacked = 1, kTokenOne = 2 };
 
-template <typename T, int V, int PAIR, bool ALIGNED, int MODE, bool OOP, bool TVEC>
+// The items of lane `thread` in the single-pass modes (kTokenOne,
+// kTokenPacked): L lanes, lane t holding items t and t + L of the
+// workgroup's tokens_per_block * (Hq + Hk) * lanes items.
+template <int MODE, int K>
+ROPE_HD int single_pass_items(const Args& a, int64_t block, int thread, int64_t* n, int* it,
+                              int* tl, bool* live) {
+  const int per_token = (a.n_heads_q + a.n_heads_k) * a.lanes;
+  const int tpb = MODE == kTokenOne ? 1 : a.tokens_per_block;
+  const int items = tpb * per_token;
+  const int L = (items + K - 1) / K;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int i = thread + k * L;
+    if constexpr (MODE == kTokenOne) {
+      n[k] = block;
+      it[k] = i;
+      tl[k] = 0;
+      live[k] = thread < L && i < items;
+    } else {
+      tl[k] = i / per_token;
+      n[k] = block * tpb + tl[k];
+      it[k] = i - tl[k] * per_token;
+      live[k] = thread < L && i < items && n[k] < a.n_tokens;
+    }
+  }
+  return L;
+}
+
+template <typename T, int V, int PAIR, bool ALIGNED, int MODE, bool OOP, int SRC>
 ROPE_HD void token_body(const Args& a, int64_t block, int64_t grid, int thread,
                         int block_dim) {
-  const int per_token = (a.n_heads_q + a.n_heads_k) * a.lanes;
-  const int tpb = a.tokens_per_block;
   constexpr int K = token_items_per_lane(PAIR);
-  if constexpr (MODE == kTokenOne) {
-    const int L = (per_token + K - 1) / K;
-    if (thread >= L) return;  // the block is rounded up to whole waves
+  if constexpr (MODE == kTokenOne || MODE == kTokenPacked) {
     int64_t n[K];
-    int it[K];
+    int it[K], tl[K];
     bool live[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      n[k] = block;
-      it[k] = thread + k * L;
-      live[k] = it[k] < per_token;
-    }
-    token_items<T, V, PAIR, ALIGNED, OOP, TVEC, K, true>(a, n, it, live);
-  } else if constexpr (MODE == kTokenPacked) {
-    const int items = tpb * per_token;
-    const int L = (items + K - 1) / K;
-    if (thread >= L) return;
-    int64_t n[K];
-    int it[K];
-    bool live[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int i = thread + k * L;
-      const int tl = i / per_token;
-      n[k] = block * tpb + tl;
-      it[k] = i - tl * per_token;
-      live[k] = i < items && n[k] < a.n_tokens;
-    }
-    token_items<T, V, PAIR, ALIGNED, OOP, TVEC, K, false>(a, n, it, live);
+    single_pass_items<MODE, K>(a, block, thread, n, it, tl, live);
+    TokenWork<T, V, PAIR, ALIGNED, OOP, K, MODE == kTokenOne> w;
+    if (w.begin(a, n, it, tl, live)) w.template finish<SRC>(a);
   } else {
+    const int per_token = (a.n_heads_q + a.n_heads_k) * a.lanes;
+    const int tpb = a.tokens_per_block;
     const int per_block = tpb * per_token;
     for (int64_t n0 = block * tpb; n0 < a.n_tokens; n0 += grid * tpb)
       for (int i = thread; i < per_block; i += block_dim) {
@@ -547,25 +678,121 @@ ROPE_HD void token_body(const Args& a, int64_t block, int64_t grid, int thread,
         const int64_t n = n0 + tl;
         const int it = i - tl * per_token;
         const bool live = n < a.n_tokens;
-        token_items<T, V, PAIR, ALIGNED, OOP, TVEC, 1, true>(a, &n, &it, &live);
+        TokenWork<T, V, PAIR, ALIGNED, OOP, 1, true> w;
+        if (w.begin(a, &n, &it, &tl, &live)) w.template finish<SRC>(a);
       }
   }
 }
 
-// The kernel entry, also run on the host by the emulator.
+// The kernel entry for cos/sin read from tables, or computed per lane (the
+// loop mode), also run on the host by the emulator.
 template <typename T, int V, int PAIR, bool ALIGNED, int MODE, bool OOP>
 ROPE_HD void token_entry(const Args& a, int64_t block, int64_t grid, int thread,
                          int block_dim) {
-  if (a.t_vec)
-    token_body<T, V, PAIR, ALIGNED, MODE, OOP, true>(a, block, grid, thread, block_dim);
+  if (a.angles)
+    token_body<T, V, PAIR, ALIGNED, MODE, OOP, kTrigTheta>(a, block, grid, thread, block_dim);
+  else if (a.t_vec)
+    token_body<T, V, PAIR, ALIGNED, MODE, OOP, kTrigVec>(a, block, grid, thread, block_dim);
   else
-    token_body<T, V, PAIR, ALIGNED, MODE, OOP, false>(a, block, grid, thread, block_dim);
+    token_body<T, V, PAIR, ALIGNED, MODE, OOP, kTrigScalar>(a, block, grid, thread, block_dim);
 }
 
+// Angles computed from theta in the single-pass modes: the workgroup's
+// tokens_per_block * R/2 (cos, sin) pairs are computed once, one pair per
+// lane and pass, into shared memory laid out [token][frequency][cos, sin],
+// instead of by every head's lane. Skipped tokens' pairs are left unset; no
+// item reads them.
+template <int MODE>
+ROPE_HD void theta_fill(const Args& a, int64_t block, int thread, int block_dim, float* lds) {
+  const int tpb = MODE == kTokenOne ? 1 : a.tokens_per_block;
+  const int values = tpb * a.half;
+  if constexpr (MODE == kTokenOne) {
+    // One token: its position is read once (uniform: a scalar load). Each
+    // lane forms its frequency before the position arrives, and computes the
+    // pair even for a skipped token (as position 0) so that no branch sits
+    // between the position and the arithmetic; only the store is skipped.
+    const int64_t b = a.seq_len == 1 ? block : block / a.seq_len;
+    const int64_t p = token_pos(a, b, block - b * a.seq_len);
+    for (int v = thread; v < values; v += block_dim) {
+      const double f = theta_freq(a, v);
+      float c, sn;
+      sincos_f32(theta_pos(a, p < 0 ? 0 : p) * f, &c, &sn);
+      if (p >= 0) {
+        lds[2 * v] = c;
+        lds[2 * v + 1] = sn;
+      }
+    }
+  } else {
+    for (int v = thread; v < values; v += block_dim) {
+      const int tl = v / a.half;
+      const int i = v - tl * a.half;
+      const int64_t n = block * tpb + tl;
+      if (n >= a.n_tokens) continue;
+      const double f = theta_freq(a, i);
+      const int64_t b = a.seq_len == 1 ? n : n / a.seq_len;
+      const int64_t p = token_pos(a, b, n - b * a.seq_len);
+      float c, sn;
+      sincos_f32(theta_pos(a, p < 0 ? 0 : p) * f, &c, &sn);
+      if (p >= 0) {
+        lds[2 * v] = c;
+        lds[2 * v + 1] = sn;
+      }
+    }
+  }
+}
+
+// Shared memory of the single-pass modes with angles from theta, in bytes.
+ROPE_HD int64_t theta_shared_bytes(int64_t tokens_per_block, int64_t half) {
+  return tokens_per_block * half * 2 * (int64_t)sizeof(float);
+}
+
+// The angles-from-theta path of the single-pass modes (device only: it holds
+// a workgroup barrier). Every lane reaches the barrier: lanes without items
+// still compute shared cos/sin.
 template <typename T, int V, int PAIR, bool ALIGNED, int MODE, bool OOP>
+__device__ __forceinline__ void token_theta_single(const Args& a) {
+  extern __shared__ float lds[];
+  constexpr int K = token_items_per_lane(PAIR);
+  int64_t n[K];
+  int it[K], tl[K];
+  bool live[K];
+  single_pass_items<MODE, K>(a, blockIdx.x, threadIdx.x, n, it, tl, live);
+  TokenWork<T, V, PAIR, ALIGNED, OOP, K, MODE == kTokenOne> w;
+  const bool has = w.begin(a, n, it, tl, live);  // row loads in flight
+  if (has) w.positions(a);
+  theta_fill<MODE>(a, blockIdx.x, threadIdx.x, blockDim.x, lds);
+  __syncthreads();
+  if (has) w.finish_shared(a, lds);
+}
+
+// SRC: a TrigSource fixed at compile time, or kSrcRuntime to choose from the
+// arguments. The one-token mode (decode) gets one instantiation per source, so
+// that each loads its arguments once, up front: a runtime branch on the
+// source made the compiler fetch the table path's arguments only after the
+// branch, a second round trip on the decode latency path (~0.1 us measured).
+constexpr int kSrcRuntime = -1;
+
+template <typename T, int V, int PAIR, bool ALIGNED, int MODE, bool OOP, int SRC>
 __global__ void __launch_bounds__(1024) rope_token_kernel(Args a) {
-  token_entry<T, V, PAIR, ALIGNED, MODE, OOP>(a, blockIdx.x, gridDim.x, threadIdx.x,
-                                              blockDim.x);
+  constexpr bool single = MODE == kTokenOne || MODE == kTokenPacked;
+  // Ask for one field of each of the argument block's first three 64-byte
+  // lines before anything else, so that the scalar cache fetches all three in
+  // one round trip; left to itself the compiler fetches them one after
+  // another as they are first used, each a round trip on the decode latency
+  // path (measured: 2.42 -> 2.34 us per graph-replayed decode call).
+  asm volatile("" ::"s"(a.q_in.base), "s"(a.cos), "s"(a.half));
+  if constexpr (SRC == kTrigTheta && single) {
+    token_theta_single<T, V, PAIR, ALIGNED, MODE, OOP>(a);
+  } else if constexpr (SRC != kSrcRuntime) {
+    token_body<T, V, PAIR, ALIGNED, MODE, OOP, SRC>(a, blockIdx.x, gridDim.x, threadIdx.x,
+                                                    blockDim.x);
+  } else {
+    if (single && a.angles)
+      token_theta_single<T, V, PAIR, ALIGNED, MODE, OOP>(a);
+    else
+      token_entry<T, V, PAIR, ALIGNED, MODE, OOP>(a, blockIdx.x, gridDim.x, threadIdx.x,
+                                                  blockDim.x);
+  }
 }
 
 }  // namespace rope

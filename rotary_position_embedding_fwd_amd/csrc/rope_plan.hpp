@@ -10,6 +10,8 @@
 
 #include <stdint.h>
 
+#include <cmath>
+
 #include "librope.h"
 #include "rope_kernels.hpp"
 
@@ -27,6 +29,7 @@ struct Plan {
   bool empty;      // nothing to do
   bool single;     // token shape: the grid covers every token, no loops
   bool oop;        // some output differs from its input
+  int64_t lds_bytes;  // dynamic shared memory per workgroup
 
   // token shape: which rope_token_kernel instantiation runs the plan
   int token_mode() const {
@@ -34,6 +37,12 @@ struct Plan {
     return a.tokens_per_block == 1 ? kTokenOne : kTokenPacked;
   }
 };
+
+// Angles computed from theta: the largest rotary dim (the token kernel keeps a
+// token's R/2 cos/sin pairs in shared memory) and the largest angle, in
+// radians, for which the kernels' argument reduction keeps |r| <= pi/4 + 1e-4.
+constexpr int64_t kMaxThetaRotaryDim = 8192;
+constexpr double kMaxThetaAngle = 1099511627776.0;  // 2^40
 
 // Token shape: (head, chunk) items a workgroup aims for when tokens are small.
 constexpr int64_t kTokenItems = 256;
@@ -133,7 +142,9 @@ inline rope_status_t validate_apply(const rope_apply_desc_t* d) {
   if (d->pairing != ROPE_SPLIT_HALF && d->pairing != ROPE_INTERLEAVED) return ROPE_ERR_LAYOUT;
   if (d->launch < ROPE_LAUNCH_AUTO || d->launch > ROPE_LAUNCH_TOKEN) return ROPE_ERR_LAYOUT;
   if (d->direction != 1 && d->direction != -1) return ROPE_ERR_LAYOUT;
-  if (d->table_col_stride != 1 && d->table_col_stride != 2) return ROPE_ERR_LAYOUT;
+  if (d->angles != ROPE_ANGLES_TABLE && d->angles != ROPE_ANGLES_THETA) return ROPE_ERR_LAYOUT;
+  const bool tables = d->angles == ROPE_ANGLES_TABLE;
+  if (tables && d->table_col_stride != 1 && d->table_col_stride != 2) return ROPE_ERR_LAYOUT;
   const int64_t hk = d->n_heads_k;
   if (d->batch < 0 || d->n_heads_q < 0 || d->seq_len < 0 || d->head_dim < 0 ||
       d->rotary_dim < 0 || d->table_rows < 0 || hk < 0)
@@ -143,6 +154,16 @@ inline rope_status_t validate_apply(const rope_apply_desc_t* d) {
   // heads and dims index with 32-bit integers inside the kernels
   if (d->n_heads_q + hk > ((int64_t)1 << 30) || d->head_dim > ((int64_t)1 << 30))
     return ROPE_ERR_SHAPE;
+  if (!tables) {
+    if (!(d->theta > 0.0) || !std::isfinite(d->theta) || !(d->interpolate_factor > 0.0) ||
+        !std::isfinite(d->interpolate_factor) || d->rotary_dim > kMaxThetaRotaryDim)
+      return ROPE_ERR_SHAPE;
+    // The largest angle must stay inside the range where the kernels' sin/cos
+    // argument reduction is accurate.
+    const double max_freq = d->theta >= 1.0 ? 1.0 : 1.0 / d->theta;
+    const double max_pos = d->table_rows > 0 ? (double)(d->table_rows - 1) : 0.0;
+    if (max_pos / d->interpolate_factor * max_freq > kMaxThetaAngle) return ROPE_ERR_SHAPE;
+  }
   if (apply_is_empty(d)) return ROPE_OK;
   if (!d->pos && d->seq_len > d->table_rows) return ROPE_ERR_SHAPE;
   if (d->pos && d->pos_batch_stride < 0) return ROPE_ERR_SHAPE;
@@ -151,13 +172,16 @@ inline rope_status_t validate_apply(const rope_apply_desc_t* d) {
     if (v->stride_b < 0 || v->stride_h < 0 || v->stride_s < 0) return ROPE_ERR_SHAPE;
   const int64_t half = d->rotary_dim / 2;
   const int64_t t_row = d->table_row_stride ? d->table_row_stride : half;
-  if (t_row < 0 || t_row < (half - 1) * d->table_col_stride + 1) return ROPE_ERR_SHAPE;
-  if ((d->n_heads_q > 0 && !d->q_in.data) || (hk > 0 && !d->k_in.data) || !d->cos || !d->sin)
+  if (tables && (t_row < 0 || t_row < (half - 1) * d->table_col_stride + 1))
+    return ROPE_ERR_SHAPE;
+  if ((d->n_heads_q > 0 && !d->q_in.data) || (hk > 0 && !d->k_in.data) ||
+      (tables && (!d->cos || !d->sin)))
     return ROPE_ERR_NULL;
   const int64_t e = elem_bytes(d->dtype);
   for (const rope_view_t* v : views)
     if (reinterpret_cast<uintptr_t>(v->data) % e) return ROPE_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(d->cos) % 16) || (reinterpret_cast<uintptr_t>(d->sin) % 16) ||
+  if ((tables && ((reinterpret_cast<uintptr_t>(d->cos) % 16) ||
+                  (reinterpret_cast<uintptr_t>(d->sin) % 16))) ||
       (reinterpret_cast<uintptr_t>(d->pos) % 4))
     return ROPE_ERR_ALIGN;
 
@@ -189,7 +213,7 @@ inline rope_status_t validate_apply(const rope_apply_desc_t* d) {
   };
   if (d->pos && meets_written(d->pos, 4 * ((B - 1) * d->pos_batch_stride + S)))
     return ROPE_ERR_ALIAS;
-  if (d->table_rows > 0) {
+  if (tables && d->table_rows > 0) {
     const int64_t table_bytes = 4 * ((d->table_rows - 1) * t_row + (half - 1) * d->table_col_stride + 1);
     if (meets_written(d->cos, table_bytes) || meets_written(d->sin, table_bytes))
       return ROPE_ERR_ALIAS;
@@ -312,6 +336,11 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
   a.n_heads_q = (int32_t)d->n_heads_q;
   a.n_heads_k = (int32_t)d->n_heads_k;
   a.sin_sign = (float)d->direction;
+  a.angles = d->angles == ROPE_ANGLES_THETA ? 1 : 0;
+  if (a.angles) {
+    a.l2_step = -2.0 * std::log2(d->theta) / (double)d->rotary_dim;
+    a.interp = d->interpolate_factor;
+  }
 
   pl->dtype = d->dtype;
   pl->pairing = d->pairing;
@@ -383,6 +412,7 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
     const int64_t max_grid = (int64_t)1 << 30;
     pl->grid = blocks < max_grid ? blocks : max_grid;
     pl->single = pl->grid == blocks && pl->block >= lanes_needed;
+    if (a.angles && pl->single) pl->lds_bytes = theta_shared_bytes(tpb, a.half);
   } else {
     // Head groups, walked in group-slow order (all tiles of group 0, then of
     // group 1, ...): on MI355X this streams HBM best when a lane walks 4 heads

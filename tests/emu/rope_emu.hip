@@ -11,6 +11,7 @@
 //   JOB_DIR/desc.txt : "key value" lines (see read_job)
 //   JOB_DIR/{q,k,cos,sin,pos}.bin : raw inputs (pos/k only when used)
 // writes JOB_DIR/{q_out,k_out}.bin and prints the plan on stdout.
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -69,8 +70,41 @@ void write_file(const std::string& path, const void* p, size_t bytes) {
 struct HostRunner {
   const rope::Plan& pl;
 
+  // Token kernel, single-pass modes, angles from theta: the kernel's three
+  // phases around its barrier, each run for every lane of the workgroup
+  // before the next. Shared memory is an exact-size buffer of NaNs, so a
+  // read of an entry no lane wrote shows up in the outputs.
+  template <typename T, int V, int PAIR, bool AL, bool OOP, int MODE>
+  void theta_block(int64_t blk) {
+    constexpr int K = rope::token_items_per_lane(PAIR);
+    using Work = rope::TokenWork<T, V, PAIR, AL, OOP, K, MODE == rope::kTokenOne>;
+    std::vector<Work> ws(pl.block);
+    std::vector<char> has(pl.block);
+    std::vector<float> lds((size_t)pl.lds_bytes / sizeof(float), std::nanf(""));
+    for (int t = 0; t < pl.block; ++t) {
+      int64_t n[K];
+      int it[K], tl[K];
+      bool live[K];
+      rope::single_pass_items<MODE, K>(pl.a, blk, t, n, it, tl, live);
+      has[t] = ws[t].begin(pl.a, n, it, tl, live);
+      if (has[t]) ws[t].positions(pl.a);
+    }
+    for (int t = 0; t < pl.block; ++t) rope::theta_fill<MODE>(pl.a, blk, t, pl.block, lds.data());
+    for (int t = 0; t < pl.block; ++t)
+      if (has[t]) ws[t].finish_shared(pl.a, lds.data());
+  }
+
   template <typename T, int V, int PAIR, bool AL, bool OOP>
   void go() {
+    if (pl.token && pl.a.angles && pl.token_mode() != rope::kTokenLoop) {
+      for (int64_t blk = 0; blk < pl.grid; ++blk) {
+        if (pl.token_mode() == rope::kTokenOne)
+          theta_block<T, V, PAIR, AL, OOP, rope::kTokenOne>(blk);
+        else
+          theta_block<T, V, PAIR, AL, OOP, rope::kTokenPacked>(blk);
+      }
+      return;
+    }
     for (int64_t blk = 0; blk < pl.grid; ++blk)
       for (int t = 0; t < pl.block; ++t) {
         if (pl.token && pl.token_mode() == rope::kTokenOne)
@@ -100,10 +134,11 @@ struct HostRunner {
 void print_plan(const rope::Plan& pl) {
   printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
          "heads_per_group %d\nn_groups %d\ngroup_slow %d\nsingle %d\noop %d\nt_vec %d\n"
-         "tokens_per_block %d\n",
+         "tokens_per_block %d\nangles %d\nlds_bytes %lld\n",
          (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
          pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow, (int)pl.single,
-         (int)pl.oop, pl.a.t_vec, pl.a.tokens_per_block);
+         (int)pl.oop, pl.a.t_vec, pl.a.tokens_per_block, pl.a.angles,
+         (long long)pl.lds_bytes);
 }
 
 // test-only overrides of the rows-kernel grid (head-group size and order)
@@ -119,6 +154,7 @@ void apply_overrides(rope::Plan& pl, std::map<std::string, long long>& kv) {
   if (!pl.empty && pl.token && kv["token_grid"] > 0 && kv["token_grid"] < pl.grid) {
     pl.grid = kv["token_grid"];
     pl.single = false;
+    pl.lds_bytes = 0;  // the loop mode computes angles per lane
   }
 }
 
@@ -157,8 +193,15 @@ int apply_mode(const std::string& dir, std::map<std::string, long long>& kv) {
   d.q_out = read_view(kv, "q_out", out, e);
   d.k_out = read_view(kv, "k_out", out, e);
   const size_t tb = (size_t)kv["table_elems"] * 4;
-  d.cos = static_cast<const float*>(read_file(dir + "/cos.bin", tb, 0));
-  d.sin = static_cast<const float*>(read_file(dir + "/sin.bin", tb, 0));
+  if (tb) {
+    d.cos = static_cast<const float*>(read_file(dir + "/cos.bin", tb, 0));
+    d.sin = static_cast<const float*>(read_file(dir + "/sin.bin", tb, 0));
+  }
+  d.angles = (int32_t)kv["angles"];
+  // binary64 arguments travel as their bit patterns
+  const long long theta_bits = kv["theta_bits"], interp_bits = kv["interp_bits"];
+  memcpy(&d.theta, &theta_bits, sizeof(double));
+  memcpy(&d.interpolate_factor, &interp_bits, sizeof(double));
   d.table_rows = kv["table_rows"];
   d.table_row_stride = kv["t_row"];
   d.table_col_stride = kv["t_col"];
@@ -192,6 +235,17 @@ int main(int argc, char** argv) {
   const std::string dir = argv[1];
   auto kv = read_job(dir);
   if (kv["apply"]) return apply_mode(dir, kv);
+  if (kv["sincos"]) {
+    // the kernels' cos/sin of binary64 angles: angles.bin (count doubles) ->
+    // sincos.bin (count (cos, sin) float pairs)
+    const size_t count = (size_t)kv["count"];
+    const double* x = static_cast<const double*>(read_file(dir + "/angles.bin", count * 8, 0));
+    std::vector<float> out(2 * count);
+    for (size_t i = 0; i < count; ++i) rope::sincos_f32(x[i], &out[2 * i], &out[2 * i + 1]);
+    write_file(dir + "/sincos.bin", out.data(), out.size() * sizeof(float));
+    printf("status 0\n");
+    return 0;
+  }
   rope_desc_t d{};
   d.batch = kv["batch"];
   d.n_heads_q = kv["n_heads_q"];

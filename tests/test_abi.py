@@ -126,14 +126,18 @@ def test_valid_call_without_gpu_reports_hip_error():
     assert rp.lib().rope_fwd_q(A16, ctypes.byref(good_desc()), None) == HIP
 
 
-@pytest.mark.parametrize("theta,R,rows", [(10000.0, 64, 128), (10000.0, 128, 4096),
-                                          (10000.0, 32, 9216), (500000.0, 128, 32768),
-                                          (500000.0, 128, 131072), (3.0, 6, 17)])
-def test_host_table_matches_oracle_bitexact(orc, theta, R, rows):
+@pytest.mark.parametrize("theta,R,rows,interp", [(10000.0, 64, 128, 1.0),
+                                                 (10000.0, 128, 4096, 1.0),
+                                                 (10000.0, 32, 9216, 1.0),
+                                                 (500000.0, 128, 32768, 1.0),
+                                                 (500000.0, 128, 131072, 1.0), (3.0, 6, 17, 1.0),
+                                                 (10000.0, 64, 3000, 3.0),
+                                                 (500000.0, 128, 8192, 0.25)])
+def test_host_table_matches_oracle_bitexact(orc, theta, R, rows, interp):
     """The product's table builder and the oracle's own table are two separate
-    implementations of RN32(cos/sin(p * theta^(-2i/R))); they must agree."""
-    c, s = rp.rope_build_table(rows, R, theta)
-    oc, os_ = orc.table(theta, R, rows)
+    implementations of RN32(cos/sin((p / s) * theta^(-2i/R))); they must agree."""
+    c, s = rp.rope_build_table(rows, R, theta, interp)
+    oc, os_ = orc.table(theta, R, rows, interp)
     assert np.array_equal(c.numpy().view(np.uint32), oc.view(np.uint32))
     assert np.array_equal(s.numpy().view(np.uint32), os_.view(np.uint32))
 
@@ -141,11 +145,14 @@ def test_host_table_matches_oracle_bitexact(orc, theta, R, rows):
 def test_table_builder_errors():
     L = rp.lib()
     buf = (ctypes.c_float * 8)()
-    assert L.rope_build_table(buf, buf, 2, 3, 10000.0) == SHAPE
-    assert L.rope_build_table(buf, buf, -1, 4, 10000.0) == SHAPE
-    assert L.rope_build_table(buf, buf, 2, 4, 0.0) == SHAPE
-    assert L.rope_build_table(None, None, 2, 4, 10000.0) == NULL
-    assert L.rope_build_table(None, None, 0, 4, 10000.0) == OK
+    assert L.rope_build_table(buf, buf, 2, 3, 10000.0, 1.0) == SHAPE
+    assert L.rope_build_table(buf, buf, -1, 4, 10000.0, 1.0) == SHAPE
+    assert L.rope_build_table(buf, buf, 2, 4, 0.0, 1.0) == SHAPE
+    for bad in (0.0, -2.0, float("inf"), float("nan")):
+        assert L.rope_build_table(buf, buf, 2, 4, 10000.0, bad) == SHAPE
+        assert L.rope_build_table(buf, buf, 2, 4, bad if bad != 0.0 else -1.0, 1.0) == SHAPE
+    assert L.rope_build_table(None, None, 2, 4, 10000.0, 1.0) == NULL
+    assert L.rope_build_table(None, None, 0, 4, 10000.0, 1.0) == OK
 
 
 def test_binding_marshals_shapes():

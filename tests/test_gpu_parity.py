@@ -506,3 +506,94 @@ def test_packed_qkv_full_size_sampled():
         prev = {"q": gq.cpu(), "k": gk.cpu()}
     assert torch.equal(g[..., (Hq + Hk) * D:].cpu().view(torch.int16),
                        qkv[..., (Hq + Hk) * D:].view(torch.int16))
+
+
+# ------------------------------------------------- angles computed from theta
+
+def _theta_run(w, x_q, x_k, direction, pos=None, interp=1.0, launch="auto",
+               max_positions=None, pos_batch_stride=None):
+    qd, kd = x_q.to(DEV), x_k.to(DEV)
+    rp.rope_apply(qd, kd, None, None, layout=w.layout, pairing=w.pairing,
+                  rotary_dim=w.rotary_dim, direction=direction, launch=launch,
+                  pos=None if pos is None else pos.to(DEV),
+                  pos_batch_stride=(w.pos_batch_stride if pos is not None and
+                                    pos_batch_stride is None else pos_batch_stride),
+                  theta=w.theta, interpolate_factor=interp,
+                  max_positions=w.table_rows if max_positions is None else max_positions)
+    torch.cuda.synchronize()
+    return qd.cpu(), kd.cpu()
+
+
+THETA_CASES = {
+    "llama_gqa_ragged": (ORACLE_SIZED["llama_gqa_ragged"], "auto", 1.0),
+    "llama_gqa_ragged_rows_interp3": (ORACLE_SIZED["llama_gqa_ragged"], "rows", 3.0),
+    "llama_gqa_ragged_token_interp2": (ORACLE_SIZED["llama_gqa_ragged"], "token", 2.0),
+    "bshd_interleaved_ragged": (ORACLE_SIZED["bshd_interleaved_ragged"], "auto", 1.0),
+    "partial_rotary_indexed": (ORACLE_SIZED["partial_rotary_indexed"], "auto", 1.0),
+    "decode": (ORACLE_SIZED["decode"], "auto", 1.0),
+    "long_context_slice": (ORACLE_SIZED["long_context_slice"], "auto", 1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(THETA_CASES))
+@pytest.mark.parametrize("direction", [1, -1])
+def test_theta_matches_oracle(name, direction):
+    """cos/sin computed in the kernel from theta (and interpolate_factor):
+    every element against the oracle with the same theta and factor."""
+    w, launch, interp = THETA_CASES[name]
+    t = W.tensors(w)
+    pos = W.positions(w)
+    if name == "long_context_slice":  # the slice's own positions are small: use the top ones
+        pos = torch.arange(w.table_rows - w.seq_len, w.table_rows, dtype=torch.int32)
+    say(f"[gpu] theta {name} dir={direction} launch={launch} interp={interp}")
+    pbs = 0 if name == "long_context_slice" else None
+    gq, gk = _theta_run(w, t["q"], t["k"], direction, pos, interp, launch,
+                        pos_batch_stride=pbs)
+    pbs_o = w.pos_batch_stride if pbs is None else pbs
+    masked = P.masked_tokens(w, pos, pos_batch_stride=pbs_o)
+    for g, x in ((gq, t["q"]), (gk, t["k"])):
+        ref = P.oracle_rope(w.scaled(n_heads_q=x.shape[1] if w.layout == "bhsd" else x.shape[2]),
+                            x, direction, pos, pos_batch_stride=pbs_o, interpolate_factor=interp)
+        P.assert_parity(P.storage(g), ref, P.storage(x), w.dtype, w.layout, w.rotary_dim,
+                        masked, f"theta {name}")
+
+
+@pytest.mark.parametrize("name", ["llama_gqa_prefill_bf16", "long_context_bf16"])
+def test_theta_full_size_equals_table_path(name):
+    """At full size in the bench's launch configuration, the theta path gives
+    the table path's bits except on a vanishing fraction of elements (where a
+    cos/sin value lies within ~1e-15 of a float32 rounding boundary), and
+    those stay within one 16-bit unit."""
+    w = W.BY_NAME[name]
+    t = W.tensors(w)
+    say(f"[gpu] theta vs table full size {name}")
+    cos, sin = gpu_tables(w)
+    a_q, a_k = t["q"].to(DEV), t["k"].to(DEV)
+    rp.rope_fwd_qk(a_q, a_k, cos, sin, **opts(w))
+    b_q, b_k = _theta_run(w, t["q"], t["k"], 1)
+    torch.cuda.synchronize()
+    for a, b in ((a_q.cpu(), b_q), (a_k.cpu(), b_k)):
+        sa, sb = P.storage(a), P.storage(b)
+        diff = sa != sb
+        frac = diff.mean()
+        say(f"[gpu]   differing elements: {int(diff.sum())} of {diff.size}")
+        assert frac <= 1e-5, frac
+        if diff.any():
+            assert np.all(np.abs(P.ord16(sa[diff]) - P.ord16(sb[diff])) <= 1)
+
+
+def test_theta_packed_qkv_in_place():
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=500, table_rows=500)
+    B, S, Hq, Hk, D = w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim
+    qkv, q, k = _packed_views(B, S, Hq, Hk, D, w.dtype, 36)
+    say(f"[gpu] theta packed qkv {tuple(qkv.shape)}")
+    g = qkv.to(DEV)
+    gq = g[..., :Hq * D].view(B, S, Hq, D)
+    gk = g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D)
+    rp.rope_apply(gq, gk, None, None, layout="bshd", theta=w.theta, max_positions=S)
+    torch.cuda.synchronize()
+    gc = g.cpu()
+    _check_view(w, gc[..., :Hq * D].view(B, S, Hq, D), q, 1, None, what="q")
+    _check_view(w, gc[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D), k, 1, None, what="k")
+    assert torch.equal(gc[..., (Hq + Hk) * D:].view(torch.int16),
+                       qkv[..., (Hq + Hk) * D:].view(torch.int16))

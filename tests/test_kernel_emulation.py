@@ -9,6 +9,7 @@ oracle computes (same tolerances as the GPU parity tests).
 """
 import os
 import fcntl
+import struct
 import subprocess
 import tempfile
 
@@ -18,6 +19,7 @@ import torch
 
 import rotary_position_embedding_fwd_amd as rp
 import workloads as W
+from tests import _exact as X
 from tests import _parity as P
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -314,11 +316,17 @@ def _strided(buf, spec, shape):
     return torch.as_strided(buf, shape, (sb, sh, ss, 1), off)
 
 
+def _f64_bits(x: float) -> int:
+    return struct.unpack("<q", struct.pack("<d", float(x)))[0]
+
+
 def run_emu_apply(emu, w, in_buf, q_in, k_in, cos, sin, *, out_buf=None, q_out=None,
                   k_out=None, pos=None, direction=1, launch="auto", t_row=0, t_col=1,
-                  cus=256, pos_batch_stride=None):
+                  cus=256, pos_batch_stride=None, theta=None, interpolate_factor=1.0,
+                  table_rows=None, overrides=None):
     """Run rope_apply's plan in the emulator. Views are (offset, sb, sh, ss)
-    element specs into in_buf / out_buf (1-d torch storage)."""
+    element specs into in_buf / out_buf (1-d torch storage). With `theta`,
+    angles are computed from theta (cos/sin may then be None)."""
     with tempfile.TemporaryDirectory() as job:
         desc = dict(apply=1, batch=w.batch, seq_len=w.seq_len, head_dim=w.head_dim,
                     rotary_dim=w.rotary_dim, n_heads_q=w.n_heads_q,
@@ -326,10 +334,16 @@ def run_emu_apply(emu, w, in_buf, q_in, k_in, cos, sin, *, out_buf=None, q_out=N
                     dtype=CODES["dtype"][w.dtype], pairing=CODES["pairing"][w.pairing],
                     launch=CODES["launch"][launch], direction=direction,
                     in_elems=in_buf.numel(), out_elems=0 if out_buf is None else out_buf.numel(),
-                    table_elems=cos.numel(), table_rows=cos.shape[0], t_row=t_row, t_col=t_col,
+                    table_elems=0 if cos is None else cos.numel(),
+                    table_rows=(cos.shape[0] if table_rows is None else table_rows),
+                    t_row=t_row, t_col=t_col,
                     pos_count=0 if pos is None else pos.numel(),
                     pos_batch_stride=(w.pos_batch_stride if pos_batch_stride is None
-                                      else pos_batch_stride), cus=cus)
+                                      else pos_batch_stride), cus=cus,
+                    angles=0 if theta is None else 1,
+                    theta_bits=_f64_bits(0.0 if theta is None else theta),
+                    interp_bits=_f64_bits(interpolate_factor))
+        desc.update(overrides or {})
         for name, spec in (("q_in", q_in), ("k_in", k_in), ("q_out", q_out), ("k_out", k_out)):
             if spec is None:
                 desc[name + "_off"] = -1
@@ -342,8 +356,9 @@ def run_emu_apply(emu, w, in_buf, q_in, k_in, cos, sin, *, out_buf=None, q_out=N
         P.storage(in_buf).tofile(os.path.join(job, "in.bin"))
         if out_buf is not None:
             P.storage(out_buf).tofile(os.path.join(job, "out.bin"))
-        cos.contiguous().numpy().tofile(os.path.join(job, "cos.bin"))
-        sin.contiguous().numpy().tofile(os.path.join(job, "sin.bin"))
+        if cos is not None:
+            cos.contiguous().numpy().tofile(os.path.join(job, "cos.bin"))
+            sin.contiguous().numpy().tofile(os.path.join(job, "sin.bin"))
         if pos is not None:
             pos.numpy().astype(np.int32).tofile(os.path.join(job, "pos.bin"))
         env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
@@ -542,3 +557,185 @@ def test_apply_validation(emu, case, expected):
         qs = (1, *qs[1:])
     plan, _, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, **kw)
     assert plan["status"] == expected
+
+
+# ------------------------------------------------- angles computed from theta
+
+def _qk_views(w, layout):
+    """Q and K of workload w stored back to back in one buffer, as (offset,
+    sb, sh, ss) view specs in the given layout; returns buf, specs, tensors."""
+    t = W.tensors(w)
+    q, k = t["q"], t["k"]  # in w.layout
+    B, S, D, Hq, Hk = w.batch, w.seq_len, w.head_dim, w.n_heads_q, w.n_heads_k
+    buf = torch.cat([q.reshape(-1), k.reshape(-1)])
+    if layout == "bhsd":
+        qs, ks = (0, Hq * S * D, S * D, D), (q.numel(), Hk * S * D, S * D, D)
+    else:
+        qs, ks = (0, S * Hq * D, D, Hq * D), (q.numel(), S * Hk * D, D, Hk * D)
+    return buf, qs, ks, q, k
+
+
+def _theta_case(emu, w, *, launch="auto", direction=1, interp=1.0, pos=None,
+                pos_batch_stride=None, max_positions=None, cus=256, overrides=None):
+    """Run w with angles computed from theta and compare with the oracle
+    (table mode with the same theta and interpolate_factor) and with the
+    table path of the emulated library on the same inputs."""
+    buf, qs, ks, q, k = _qk_views(w, w.layout)
+    rows = max_positions if max_positions is not None else w.table_rows
+    pbs = w.pos_batch_stride if pos_batch_stride is None else pos_batch_stride
+    plan, after, _ = run_emu_apply(emu, w, buf, qs, ks, None, None, pos=pos, direction=direction,
+                                   launch=launch, cus=cus, pos_batch_stride=pbs,
+                                   theta=w.theta, interpolate_factor=interp, table_rows=rows,
+                                   overrides=overrides)
+    assert plan["status"] == 0 and plan["angles"] == 1, plan
+    qa, ka = after[:q.numel()].view(q.shape), after[q.numel():].view(k.shape)
+    masked = P.masked_tokens(w, pos, table_rows=rows, pos_batch_stride=pbs)
+    for got, x in ((qa, q), (ka, k)):
+        ref = P.oracle_rope(w.scaled(n_heads_q=x.shape[1] if w.layout == "bhsd" else x.shape[2]),
+                            x, direction, pos, pos_batch_stride=pbs, table_rows=rows,
+                            interpolate_factor=interp)
+        P.assert_parity(P.storage(got), ref, P.storage(x), w.dtype, w.layout, w.rotary_dim,
+                        masked)
+    # the table path on the same call: cos/sin agree to the last bit except
+    # where a value lies within ~1e-15 of a float32 rounding boundary
+    cos, sin = rp.rope_build_table(rows, w.rotary_dim, w.theta, interp)
+    _, after_t, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, pos=pos, direction=direction,
+                                  launch=launch, cus=cus, pos_batch_stride=pbs,
+                                  overrides=overrides)
+    same = np.mean(P.storage(after) == P.storage(after_t))
+    assert same >= 0.999, same
+    return plan
+
+
+@pytest.mark.parametrize("launch", ["rows", "token"])
+@pytest.mark.parametrize("direction", [1, -1])
+def test_theta_matches_oracle_both_shapes(emu, launch, direction):
+    plan = _theta_case(emu, SMALL["llama_ragged"], launch=launch, direction=direction)
+    assert plan["token"] == (launch == "token")
+    # single-pass token shape: the token's R/2 (cos, sin) pairs in shared memory
+    assert plan["lds_bytes"] == (SMALL["llama_ragged"].rotary_dim // 2 * 8 if launch == "token"
+                                 else 0)
+
+
+@pytest.mark.parametrize("interp", [1.0, 3.0, 0.5])
+def test_theta_interpolate_factor(emu, interp):
+    w = SMALL["llama_ragged"]
+    _theta_case(emu, w, interp=interp, launch="rows")
+    _theta_case(emu, w, interp=interp, launch="token", direction=-1)
+
+
+def test_theta_interleaved_two_items_per_lane(emu):
+    plan = _theta_case(emu, SMALL["bshd_interleaved_ragged"], launch="token")
+    assert plan["block"] == 128 and plan["single"] == 1
+
+
+def test_theta_packed_tokens_and_loop(emu):
+    w = SMALL["llama_ragged"].scaled(n_heads_q=2, n_heads_k=1, head_dim=64, rotary_dim=64,
+                                     seq_len=200, table_rows=200, layout="bshd")
+    plan = _theta_case(emu, w, launch="token", cus=1, interp=2.0)
+    # 12 items per token: 21 tokens per workgroup (400 // 16 = 25 allows it)
+    assert plan["tokens_per_block"] == 21 and plan["single"] == 1
+    assert plan["lds_bytes"] == 21 * 32 * 8  # [token][frequency] (cos, sin) pairs
+    plan = _theta_case(emu, w, launch="token", cus=1, overrides=dict(token_grid=3))
+    assert plan["single"] == 0 and plan["lds_bytes"] == 0
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_theta_decode_large_positions(emu, direction):
+    """Decode: one token per workgroup, positions up to 32767 with theta = 5e5."""
+    w = SMALL["decode"]
+    pos = W.positions(w)
+    plan = _theta_case(emu, w, direction=direction, pos=pos)
+    assert plan["token"] == 1 and plan["tokens_per_block"] == 1
+
+
+def test_theta_long_positions(emu):
+    """Positions near 131071 (angles ~1.3e5 rad at the lowest frequency)."""
+    w = SMALL["long_theta"]
+    pos = torch.arange(131071 - 63, 131072, dtype=torch.int32)
+    _theta_case(emu, w, pos=pos, pos_batch_stride=0, max_positions=131072, launch="rows")
+    _theta_case(emu, w, pos=pos, pos_batch_stride=0, max_positions=131072, launch="token")
+
+
+def test_theta_skipped_tokens_partial_rotary(emu):
+    w = SMALL["partial_indexed"]
+    pos = W.positions(w)
+    for launch in ("rows", "token"):
+        _theta_case(emu, w, pos=pos, launch=launch)
+
+
+def _theta_status(emu, **kw):
+    w = SMALL["llama_ragged"].scaled(seq_len=4, table_rows=4)
+    buf, qs, ks, q, k = _qk_views(w, w.layout)
+    args = dict(theta=w.theta, interpolate_factor=1.0, table_rows=4)
+    overrides = {}
+    for key, v in kw.items():
+        if key in ("theta", "interpolate_factor", "table_rows"):
+            args[key] = v
+        else:
+            overrides[key] = v
+    plan, _, _ = run_emu_apply(emu, w, buf, qs, ks, None, None, overrides=overrides, **args)
+    return plan["status"]
+
+
+def test_theta_validation(emu):
+    SHAPE, LAYOUT = -2, -4
+    assert _theta_status(emu) == 0  # no tables needed
+    for bad in (0.0, -10.0, float("inf"), float("nan")):
+        assert _theta_status(emu, theta=bad) == SHAPE
+        assert _theta_status(emu, interpolate_factor=bad) == SHAPE
+    assert _theta_status(emu, angles=2) == LAYOUT
+    # the largest angle, (table_rows - 1) / interpolate_factor, must stay <= 2^40
+    assert _theta_status(emu, table_rows=2 ** 31 - 1, interpolate_factor=1e-3) == SHAPE
+    assert _theta_status(emu, table_rows=2 ** 31 - 1, interpolate_factor=1.0) == 0
+
+
+def _kernel_sincos(emu, angles):
+    with tempfile.TemporaryDirectory() as job:
+        with open(os.path.join(job, "desc.txt"), "w") as f:
+            f.write(f"sincos 1\ncount {len(angles)}\n")
+        np.asarray(angles, np.float64).tofile(os.path.join(job, "angles.bin"))
+        env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
+        r = subprocess.run([emu, job], capture_output=True, text=True, timeout=300, env=env)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return np.fromfile(os.path.join(job, "sincos.bin"), np.float32).reshape(-1, 2)
+
+
+def test_kernel_sincos_is_correctly_rounded(emu):
+    """The kernels' cos/sin (Cody-Waite reduction by pi/2, Taylor series in
+    binary64, one rounding) against 60-digit mpmath rounded once to float32:
+    equal except for values within ~1e-15 of a float32 rounding boundary. The
+    angles cover the kernels' range: RoPE angles p * theta^(-2i/R) up to 1.3e5,
+    angles within 1e-9 of multiples of pi/2 (where the reduction cancels),
+    negative angles, tiny angles and the 2^40 limit."""
+    import mpmath
+    rng = np.random.default_rng(77)
+    ang = [0.0, -0.0, 1e-20, 1e-8, -1e-8, 0.5, 1.0, 2.0 ** 40, -(2.0 ** 40)]
+    ang += list(rng.uniform(-10, 10, 2000))
+    ang += list(rng.uniform(0, 131072, 3000))
+    ang += list(np.exp(rng.uniform(np.log(1e-6), np.log(2.0 ** 40), 3000)))
+    with mpmath.workdps(60):
+        halfpi = mpmath.pi / 2
+        for k in rng.integers(1, 2 ** 30, 1000):
+            near = float(halfpi * int(k))  # nearest binary64 to k pi/2
+            ang += [near, np.nextafter(near, np.inf), np.nextafter(near, -np.inf)]
+        theta, R = 500000.0, 128
+        for p in (1, 7, 4095, 32767, 131071):
+            for i in range(R // 2):
+                ang.append(float(p) * (theta ** (-(2.0 * i) / R)))
+    ang = np.asarray(ang, np.float64)
+    got = _kernel_sincos(emu, ang)
+    bad = 0
+    with mpmath.workdps(60):
+        for x, (gc, gs) in zip(ang, got):
+            a = mpmath.mpf(float(x))
+            for g, ref in ((gc, mpmath.cos(a)), (gs, mpmath.sin(a))):
+                r = X.rn24_mp(ref)
+                if float(g) != r:
+                    bad += 1
+                    # only a value within 1e-15 (absolute) of the midpoint
+                    # between the two float32 neighbours may round the other way
+                    mid = (mpmath.mpf(r) + mpmath.mpf(float(g))) / 2
+                    assert abs(float(g) - r) <= abs(np.spacing(np.float32(r))) * 1.01, (x, g, r)
+                    assert abs(ref - mid) <= mpmath.mpf("1e-15"), (x, g, ref)
+    assert bad <= 2, bad
