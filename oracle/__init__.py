@@ -60,6 +60,11 @@ def _bind(lib):
     lib.oracle_rope_exact.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       _I64, _I64, _I64, _I64, _I64, ctypes.c_double,
                                       ctypes.c_double, _P, _I64, _I64]
+    lib.oracle_rope_attention.restype = ctypes.c_int
+    lib.oracle_rope_attention.argtypes = [_P, _P, _P, _P, ctypes.c_int, ctypes.c_int,
+                                          _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                          ctypes.c_double, ctypes.c_double, _P, _I64, _P, _I64,
+                                          _I64, ctypes.c_int, ctypes.c_double]
     lib.oracle_to_bf16_bits.restype = ctypes.c_uint16
     lib.oracle_to_bf16_bits.argtypes = [ctypes.c_double]
     lib.oracle_to_f16_bits.restype = ctypes.c_uint16
@@ -166,6 +171,36 @@ def rope_exact(x: np.ndarray, *, layout: str = "bhsd", pairing: str = "split_hal
     if rc:
         raise OracleError(f"oracle_rope_exact rejected its arguments (code {rc})")
     return y
+
+
+def rope_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: str, *,
+                   pairing: str = "split_half", rotary_dim: Optional[int] = None,
+                   theta: float = 10000.0, interpolate_factor: float = 1.0, qpos=None,
+                   qpos_batch_stride: int = 0, kpos=None, kpos_batch_stride: int = 0,
+                   table_rows: Optional[int] = None, causal: bool = False,
+                   scale: Optional[float] = None, lib=None) -> np.ndarray:
+    """Attention over RoPE-rotated Q and K (see rope_oracle.c), binary64 output.
+
+    q [B,Hq,Sq,D], k and v [B,Hk,Sk,D] storage arrays (float32, or uint16 bits
+    for f16/bf16). scale defaults to 1/sqrt(D); positions default to s for
+    keys and s + Sk - Sq for queries.
+    """
+    st = NP_STORAGE[dtype]
+    q, k, v = (np.ascontiguousarray(a, dtype=st) for a in (q, k, v))
+    B, Hq, Sq, D = q.shape
+    _, Hk, Sk, _ = k.shape
+    R = D if rotary_dim is None else rotary_dim
+    rows = max(Sq, Sk) if table_rows is None else table_rows
+    sc = 1.0 / np.sqrt(D) if scale is None else scale
+    o = np.empty((B, Hq, Sq, D), np.float64)
+    qp, kp = _pos_arr(qpos), _pos_arr(kpos)
+    rc = (lib or load()).oracle_rope_attention(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), DTYPES[dtype], PAIRINGS[pairing], B, Hq, Hk, Sq,
+        Sk, D, R, theta, interpolate_factor, _ptr(qp), qpos_batch_stride, _ptr(kp),
+        kpos_batch_stride, rows, int(causal), float(sc))
+    if rc:
+        raise OracleError(f"oracle_rope_attention rejected its arguments (code {rc})")
+    return o
 
 
 def to_bits(y: float, dtype: str, lib=None) -> int:

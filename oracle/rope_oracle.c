@@ -45,6 +45,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* Codes of this file's own interface (mirrored in oracle/__init__.py). */
@@ -281,6 +282,91 @@ int oracle_rope_exact(const double *x, double *y, int layout, int pairing, int d
         }
       }
   return 0;
+}
+
+/*
+ * Attention with RoPE applied to the loaded Q and K (rotary-embedding-torch
+ * docs, flash_attn_with_rotary: the rotation is applied to Q and K inside the
+ * attention computation instead of as a separate pass; GQA repeats the K/V
+ * heads; is_causal). Written as the unfused composition it replaces:
+ *
+ *   Qr = oracle_rope(Q), Kr = oracle_rope(K)      table mode, each element
+ *       rounded to the storage dtype, as a separate rotation pass would leave
+ *       them (query positions: qpos, or row i at i + Sk - Sq; key positions:
+ *       kpos, or row j at j)
+ *   s_ij = scale * sum_d Qr[i][d] * Kr[j][d]       binary64
+ *   causal: key j is visible to query i when j <= i + (Sk - Sq)
+ *       (the last query row lines up with the last key row)
+ *   o_i = sum_j softmax_j(s_ij) * V[j]             binary64, max subtracted
+ *
+ * Query head h uses K/V head h / (Hq / Hk). q [B,Hq,Sq,D], k and v
+ * [B,Hk,Sk,D] in `dtype` storage; o [B,Hq,Sq,D] binary64. Returns 0, or a
+ * negative code (also for Hq not a multiple of Hk, or causal with Sq > Sk).
+ */
+int oracle_rope_attention(const void *q, const void *k, const void *v, double *o, int dtype,
+                          int pairing, int64_t B, int64_t Hq, int64_t Hk, int64_t Sq,
+                          int64_t Sk, int64_t D, int64_t R, double theta, double interp,
+                          const int32_t *qpos, int64_t qpos_batch_stride, const int32_t *kpos,
+                          int64_t kpos_batch_stride, int64_t table_rows, int causal,
+                          double scale) {
+  if (Hk <= 0 || Hq % Hk || (causal && Sq > Sk) || Sq < 0 || Sk < 0) return -2;
+  int64_t es = elem_size(dtype);
+  void *qr = malloc((size_t)(B * Hq * Sq * D * es));
+  void *kr = malloc((size_t)(B * Hk * Sk * D * es));
+  int32_t *qp = NULL;
+  int rc = -5;
+  if (!qr || !kr) goto done;
+  if (!qpos && Sk != Sq) { /* default query positions i + Sk - Sq, as an index row */
+    qp = malloc((size_t)(Sq > 0 ? Sq : 1) * sizeof(int32_t));
+    if (!qp) goto done;
+    for (int64_t i = 0; i < Sq; ++i) qp[i] = (int32_t)(i + Sk - Sq);
+    qpos = qp;
+    qpos_batch_stride = 0;
+  }
+  rc = oracle_rope(q, qr, dtype, ORC_BHSD, pairing, 1, B, Hq, Sq, D, R, theta, interp, qpos,
+                   qpos_batch_stride, table_rows);
+  if (!rc)
+    rc = oracle_rope(k, kr, dtype, ORC_BHSD, pairing, 1, B, Hk, Sk, D, R, theta, interp, kpos,
+                     kpos_batch_stride, table_rows);
+  if (rc) goto done;
+  {
+    double *w = malloc((size_t)(Sk > 0 ? Sk : 1) * sizeof(double));
+    if (!w) { rc = -5; goto done; }
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t h = 0; h < Hq; ++h) {
+        int64_t hk = h / (Hq / Hk);
+        for (int64_t i = 0; i < Sq; ++i) {
+          int64_t qrow = ((b * Hq + h) * Sq + i) * D;
+          int64_t last = causal ? i + (Sk - Sq) : Sk - 1; /* last visible key */
+          double m = -INFINITY;
+          for (int64_t j = 0; j <= last; ++j) {
+            int64_t krow = ((b * Hk + hk) * Sk + j) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+              dot += load_elem(qr, qrow + d, dtype) * load_elem(kr, krow + d, dtype);
+            w[j] = scale * dot;
+            if (w[j] > m) m = w[j];
+          }
+          double l = 0.0;
+          for (int64_t j = 0; j <= last; ++j) {
+            w[j] = exp(w[j] - m);
+            l += w[j];
+          }
+          for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int64_t j = 0; j <= last; ++j)
+              acc += w[j] * load_elem(v, ((b * Hk + hk) * Sk + j) * D + d, dtype);
+            o[qrow + d] = last >= 0 ? acc / l : 0.0;
+          }
+        }
+      }
+    free(w);
+  }
+done:
+  free(qr);
+  free(kr);
+  free(qp);
+  return rc;
 }
 
 /* Rounding helpers exposed for the pins on the dtype conversions. */

@@ -53,6 +53,14 @@ MUTANTS = {
                           "return ((double)p * interp) * oracle_freq(theta, rotary_dim, i);"),
     "interp_ignored": ("return ((double)p / interp) * oracle_freq(theta, rotary_dim, i);",
                        "return (double)p * oracle_freq(theta, rotary_dim, i);"),
+    "attn_no_scale": ("            w[j] = scale * dot;", "            w[j] = dot;"),
+    "attn_causal_off_by_one": ("int64_t last = causal ? i + (Sk - Sq) : Sk - 1;",
+                               "int64_t last = causal ? i + (Sk - Sq) - 1 : Sk - 1;"),
+    "attn_gqa_map": ("int64_t hk = h / (Hq / Hk);", "int64_t hk = h % Hk;"),
+    "attn_k_unrotated": ("rc = oracle_rope(k, kr, dtype, ORC_BHSD, pairing, 1,",
+                         "rc = oracle_rope(k, kr, dtype, ORC_BHSD, pairing, -1,"),
+    "attn_values_from_keys": ("acc += w[j] * load_elem(v, ", "acc += w[j] * load_elem(kr, "),
+    "attn_query_offset": ("qp[i] = (int32_t)(i + Sk - Sq);", "qp[i] = (int32_t)i;"),
     "pass_through_dims_rotated": ("for (int64_t i = 0; i < R / 2; ++i) {\n          float c32, s32;",
                                   "for (int64_t i = 0; i < D / 2; ++i) {\n          float c32, s32;"),
 }
@@ -69,7 +77,8 @@ def _run_mutant(name, old, new, tmp):
                     "-o", lib, path, "-lm"], check=True)
     env = dict(os.environ, ROPE_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_attention_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-2000:]
 
