@@ -228,6 +228,61 @@ typedef struct rope_apply_desc {
  * or sin is not 16-byte aligned, or pos is not 4-byte aligned. */
 rope_status_t rope_apply(const rope_apply_desc_t *d, void *stream);
 
+/* ---------------------------------------------- attention with RoPE fused
+ * Attention whose Q and K are rotated inside the kernel, on the blocks it
+ * loads, so no rotated Q or K is written to memory (rotary-embedding-torch
+ * docs, flash_attn_with_rotary; GQA repeats the K/V heads; is_causal):
+ *   O[b,h] = softmax(scale * rope(Q[b,h]) rope(K[b,h'])^T  [causal mask]) V[b,h']
+ * with h' = h / (Hq / Hk). rope() is the rotation of rope_fwd_qk (same
+ * table, pairing, positions and float32 arithmetic), its results rounded to
+ * bf16 as that call would store them: the output equals rope_fwd_qk on Q and
+ * K followed by the same attention with `rotate` = 0.
+ *   - Q [B, Hq, Sq, D], K and V [B, Hk, Sk, D], O [B, Hq, Sq, D]: dense,
+ *     contiguous, bf16, 16-byte aligned. O must not overlap any input.
+ *   - positions: q_pos / k_pos as in rope_desc_t (per batch stride), or NULL:
+ *     key j at j, query i at i + Sk - Sq; out-of-table indices pass through.
+ *   - causal: key j is visible to query i when j <= i + Sk - Sq (needs
+ *     Sq <= Sk). A query with no visible key (Sk = 0) gets zeros; K and V
+ *     may then be NULL.
+ *   - scale: 0 means 1 / sqrt(head_dim).
+ * Matrix-core kernel: the products run as bf16 with float32 accumulation and
+ * the softmax weights are rounded to bf16 before they multiply V.
+ * Limits: head_dim 64 or 128; split-half pairs need R % 32 == 0 and
+ * interleaved pairs R % 8 == 0 (R = 0: no rotation). */
+typedef struct rope_attn_desc {
+  int64_t batch;
+  int64_t n_heads_q;    /* Hq >= 1 */
+  int64_t n_heads_k;    /* Hk >= 1, Hq % Hk == 0 */
+  int64_t seq_len_q;    /* Sq >= 0 */
+  int64_t seq_len_k;    /* Sk >= 0 */
+  int64_t head_dim;     /* D: 64 or 128 */
+  int64_t rotary_dim;   /* R, even, <= D (see the limits above) */
+  int32_t dtype;        /* ROPE_BF16 */
+  int32_t pairing;      /* rope_pairing_t */
+  int32_t causal;       /* 0 or 1 */
+  int32_t rotate;       /* 1: rotate Q and K; 0: plain attention */
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;
+  const float *cos;     /* [table_rows, R/2], 16-byte aligned; unused if rotate == 0 */
+  const float *sin;
+  int64_t table_rows;
+  const int32_t *q_pos;
+  int64_t q_pos_batch_stride;
+  const int32_t *k_pos;
+  int64_t k_pos_batch_stride;
+  double scale;
+} rope_attn_desc_t;
+
+/* Enqueue the fused attention on `stream`. Errors as rope_apply:
+ * ROPE_ERR_DTYPE for a dtype other than bf16, ROPE_ERR_SHAPE for sizes
+ * outside the limits above (or Hq % Hk != 0, or causal with Sq > Sk, or a
+ * non-finite scale, or positions without an index reaching table_rows),
+ * ROPE_ERR_LAYOUT for an unknown pairing, ROPE_ERR_ALIGN, ROPE_ERR_ALIAS when
+ * O overlaps an input. */
+rope_status_t rope_attention_fwd(const rope_attn_desc_t *d, void *stream);
+
 /* Fill host float32 tables cos_out/sin_out, each [table_rows, R/2] row-major,
  * with cos and sin of (p / interpolate_factor) * theta^(-2i/R) for row p and
  * column i: the exponent -2i/R, the scaled position and the angle are formed

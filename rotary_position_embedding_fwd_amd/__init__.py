@@ -87,6 +87,24 @@ class RopeApplyDesc(ctypes.Structure):
 ANGLES_TABLE, ANGLES_THETA = 0, 1
 
 
+class RopeAttnDesc(ctypes.Structure):
+    """rope_attn_desc_t of include/librope.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("n_heads_q", ctypes.c_int64),
+        ("n_heads_k", ctypes.c_int64), ("seq_len_q", ctypes.c_int64),
+        ("seq_len_k", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+        ("rotary_dim", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("pairing", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("rotate", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p),
+        ("table_rows", ctypes.c_int64),
+        ("q_pos", ctypes.c_void_p), ("q_pos_batch_stride", ctypes.c_int64),
+        ("k_pos", ctypes.c_void_p), ("k_pos_batch_stride", ctypes.c_int64),
+        ("scale", ctypes.c_double),
+    ]
+
+
 class RopeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -117,6 +135,8 @@ def lib():
         L.rope_build_table.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                        ctypes.c_double]
         L.rope_build_table.restype = ctypes.c_int
+        L.rope_attention_fwd.argtypes = [ctypes.POINTER(RopeAttnDesc), P]
+        L.rope_attention_fwd.restype = ctypes.c_int
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_status_string.restype = ctypes.c_char_p
         L.rope_version.argtypes = []
@@ -427,3 +447,91 @@ def rope_build_table(table_rows: int, rotary_dim: int, theta: float = 10000.0,
     _check(lib().rope_build_table(cos.data_ptr(), sin.data_ptr(), table_rows, rotary_dim,
                                   float(theta), float(interpolate_factor)), "rope_build_table")
     return cos, sin
+
+
+def _index(pos, batch: int, seq: int, batch_stride: Optional[int], what: str):
+    """(pointer, batch stride) of an optional int32 index of `seq` entries per batch."""
+    if pos is None:
+        return None, 0
+    import torch
+    if pos.dtype != torch.int32 or not pos.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous int32 tensor")
+    bs = (seq if pos.numel() >= batch * seq else 0) if batch_stride is None else batch_stride
+    need = (batch - 1) * bs + seq if batch > 0 and seq > 0 else 0
+    if pos.numel() < need:
+        raise ValueError(f"{what} holds {pos.numel()} indices, needs {need}")
+    return pos.data_ptr(), bs
+
+
+def make_attn_desc(q, k, v, cos, sin, o, *, pairing: str = "split_half",
+                   rotary_dim: Optional[int] = None, causal: bool = False,
+                   rotate: bool = True, q_pos=None, k_pos=None,
+                   q_pos_batch_stride: Optional[int] = None,
+                   k_pos_batch_stride: Optional[int] = None, scale: float = 0.0) -> RopeAttnDesc:
+    """rope_attn_desc_t for q [B,Hq,Sq,D], k and v [B,Hk,Sk,D], o like q (all
+    contiguous bf16). rotary_dim defaults to 2 * cos.shape[1]; positions
+    default to key j at j and query i at i + Sk - Sq. An index with at least
+    B*S entries is taken per batch (stride S), otherwise shared (stride 0)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d tensor")
+    B, Hq, Sq, D = q.shape
+    Hk, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hk, Sk, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hk, Sk, D] with q's B and D")
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    d = RopeAttnDesc()
+    d.batch, d.n_heads_q, d.n_heads_k = B, Hq, Hk
+    d.seq_len_q, d.seq_len_k, d.head_dim = Sq, Sk, D
+    d.dtype = _dtype_code(q)
+    for t in (k, v, o):
+        if _dtype_code(t) != d.dtype:
+            raise ValueError("q, k, v and o must share one dtype")
+    d.pairing = PAIRINGS[pairing]
+    d.causal = int(bool(causal))
+    d.rotate = int(bool(rotate))
+    d.q, d.k, d.v, d.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    if cos is not None:
+        if cos.dim() != 2 or tuple(sin.shape) != tuple(cos.shape):
+            raise ValueError("cos and sin must be [table_rows, R/2]")
+        d.rotary_dim = 2 * cos.shape[1] if rotary_dim is None else rotary_dim
+        d.cos, d.sin = cos.data_ptr(), sin.data_ptr()
+        d.table_rows = cos.shape[0]
+    else:
+        d.rotary_dim = 0 if rotary_dim is None else rotary_dim
+    d.q_pos, d.q_pos_batch_stride = _index(q_pos, B, Sq, q_pos_batch_stride, "q_pos")
+    d.k_pos, d.k_pos_batch_stride = _index(k_pos, B, Sk, k_pos_batch_stride, "k_pos")
+    d.scale = float(scale)
+    return d
+
+
+def rope_attention(q, k, v, cos, sin, *, o=None, stream=None, **kw):
+    """Attention over RoPE-rotated q and k in one launch (rope_attention_fwd):
+    softmax(scale * rope(q) rope(k)^T [causal]) v, GQA by head groups. The
+    rotated q and k are never written. Returns o (allocated if not given)."""
+    import torch
+    if o is None:
+        o = torch.empty_like(q)
+    d = make_attn_desc(q, k, v, cos, sin, o, **kw)
+    _check(lib().rope_attention_fwd(ctypes.byref(d), _stream(stream)), "rope_attention_fwd")
+    return o
+
+
+class PreparedAttention:
+    """A rope_attention_fwd call whose descriptor is built once (see Prepared)."""
+
+    def __init__(self, q, k, v, cos, sin, o, stream=None, **kw):
+        self._keep = (q, k, v, cos, sin, o, kw.get("q_pos"), kw.get("k_pos"))
+        self.desc = make_attn_desc(q, k, v, cos, sin, o, **kw)
+        self._stream = _stream(stream)
+        self._pdesc = ctypes.byref(self.desc)
+        self._lib = lib()
+
+    def rope_attention_fwd(self):
+        _check(self._lib.rope_attention_fwd(self._pdesc, self._stream), "rope_attention_fwd")
+
+
+def prepare_attention(q, k, v, cos, sin, o, *, stream=None, **kw) -> PreparedAttention:
+    """Build the descriptor of a rope_attention_fwd call once."""
+    return PreparedAttention(q, k, v, cos, sin, o, stream=stream, **kw)

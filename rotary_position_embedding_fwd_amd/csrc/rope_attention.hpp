@@ -1,0 +1,367 @@
+// rope_attention.hpp -- attention with RoPE applied to the loaded Q and K
+// blocks, for gfx950 matrix cores (rotary-embedding-torch docs,
+// flash_attn_with_rotary: the rotation happens on the Q and K blocks inside
+// the attention kernel, so no rotated Q or K is written to memory; GQA; causal
+// masking; per-token positions with skipped tokens).
+//
+// O = softmax(scale * rope(Q) rope(K)^T [+ causal mask]) V, per (batch, query
+// head), with K/V head h / (Hq / Hk). rope() is the same pair rotation, in the
+// same float32 arithmetic, as the stand-alone kernels (rope_kernels.hpp), and
+// the rotated values are rounded to bf16 as the stand-alone pass would store
+// them, so the fused result equals rope_fwd_qk followed by attention.
+//
+// Shape of the computation (one workgroup = 4 waves = 128 query rows of one
+// (batch, head); each lane owns one query row, two lanes per row):
+//   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16. Each lane's accumulators hold
+//                 its query's scores against 32 of a 64-key tile, so the
+//                 softmax statistics are per lane plus one exchange with the
+//                 partner lane (lane ^ 32).
+//   O^T += V^T P^T  with the same instruction; the score registers are the
+//                 P^T operand directly, under a fixed permutation of the keys
+//                 inside each 16-key step that V^T's reads follow.
+// Q is loaded and rotated once into the registers of the B operand of S^T.
+// Each 64-key tile of K is rotated while it is staged into LDS ([key][dim],
+// rows padded by 16 bytes); V is staged transposed ([dim][key], padded) so
+// that the A operand of O^T is two 8-byte LDS reads per lane and step.
+// The softmax runs in base 2 with the scale folded into log2(e).
+//
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (checked on the device by a
+// probe): A (32x16): lane l, slot i holds A[l%32][(l/32)*8 + i]; B (16x32):
+// B[(l/32)*8 + i][l%32]; C/D (32x32 float): accumulator j of lane l holds
+// C[8*(j/4) + 4*(l/32) + j%4][l%32].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rope_kernels.hpp"
+
+namespace rope {
+namespace attn {
+
+constexpr int kWaves = 4;
+constexpr int kBlock = 64 * kWaves;         // lanes per workgroup
+constexpr int kQueries = 32 * kWaves;       // query rows per workgroup
+constexpr int kKeys = 64;                   // keys per tile
+constexpr int kKPad = 8;                    // K tile row padding (bf16)
+constexpr int kVPad = 8;                    // V^T tile row padding (bf16)
+
+struct AttnArgs {
+  const __bf16* q;    // [B, Hq, Sq, D]
+  const __bf16* k;    // [B, Hk, Sk, D]
+  const __bf16* v;    // [B, Hk, Sk, D]
+  __bf16* o;          // [B, Hq, Sq, D]
+  const float* cos;   // [table_rows, R/2]
+  const float* sin;
+  const int32_t* q_pos;  // nullptr: query row i at i + Sk - Sq
+  const int32_t* k_pos;  // nullptr: key row j at j
+  int64_t q_pos_bs, k_pos_bs;
+  int64_t table_rows;
+  int32_t batch, n_heads_q, n_heads_k, seq_q, seq_k;
+  int32_t half;          // R / 2
+  int32_t rotate;        // 0: no rotation (plain attention, for the unfused path)
+  int32_t causal;
+  int32_t q_tiles;       // ceil(Sq / kQueries)
+  float scale_log2e;     // softmax scale * log2(e)
+};
+
+// ------------------------------------------------------------- addresses
+// Everything that forms an address is a plain function of the indices, so
+// the host can enumerate the whole grid and check every access against the
+// buffers before the kernel first runs on a device.
+
+template <int D> ROPE_HD int64_t row_of(const AttnArgs& a, int b, int h, int heads, int seq,
+                                        int s) {
+  return (((int64_t)b * heads + h) * seq + s) * D;
+}
+
+// K tile staging: item it of a 64-key tile. Split-half: items [0, R/16) of a
+// key rotate the chunk pair (c, c + R/16) of 8 dims each; interleaved: items
+// [0, R/8) rotate chunk c in place; the rest copy the unrotated chunks >= R/8.
+template <int D, int PAIR> struct KItems {
+  static ROPE_HD int per_key(const AttnArgs& a) {
+    const int rchunks = 2 * a.half / 8;  // chunks holding rotated dims
+    return (PAIR == kSplitHalf ? rchunks / 2 : rchunks) + (D / 8 - rchunks);
+  }
+};
+
+// LDS layout, in bf16 elements: K tile [kKeys][D + kKPad], then V^T tile
+// [D][kKeys + kVPad].
+template <int D> constexpr int k_lds_elems() { return kKeys * (D + kKPad); }
+template <int D> constexpr int v_lds_elems() { return D * (kKeys + kVPad); }
+template <int D> constexpr int lds_bytes() { return 2 * (k_lds_elems<D>() + v_lds_elems<D>()); }
+template <int D> ROPE_HD int k_lds(int key, int dim) { return key * (D + kKPad) + dim; }
+template <int D> ROPE_HD int v_lds(int dim, int key) {
+  return k_lds_elems<D>() + dim * (kKeys + kVPad) + key;
+}
+
+// Position of query row i / key row j (or -1: not rotated).
+ROPE_HD int64_t query_pos(const AttnArgs& a, int b, int i) {
+  int64_t p = a.q_pos ? (int64_t)a.q_pos[(int64_t)b * a.q_pos_bs + i]
+                      : (int64_t)i + (a.seq_k - a.seq_q);
+  return (p < 0 || p >= a.table_rows) ? -1 : p;
+}
+ROPE_HD int64_t key_pos(const AttnArgs& a, int b, int j) {
+  int64_t p = a.k_pos ? (int64_t)a.k_pos[(int64_t)b * a.k_pos_bs + j] : (int64_t)j;
+  return (p < 0 || p >= a.table_rows) ? -1 : p;
+}
+
+// Key tiles a workgroup visits: all of them, or (causal) up to the last key
+// visible to its last query row.
+ROPE_HD int key_tiles(const AttnArgs& a, int q_tile) {
+  int last_key = a.seq_k - 1;
+  if (a.causal) {
+    const int q_last = imin(a.seq_q - 1, q_tile * kQueries + kQueries - 1);
+    last_key = imin(last_key, q_last + (a.seq_k - a.seq_q));
+  }
+  return last_key < 0 ? 0 : last_key / kKeys + 1;
+}
+
+// --------------------------------------------------------------- helpers
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Rotate two 8-element chunks (x1 = first halves of 8 pairs, x2 = second
+// halves) with NP = 8 frequencies, or one chunk of 4 interleaved pairs.
+ROPE_HD void rotate_split8(bf16x8& x1, bf16x8& x2, const float* c, const float* s) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float y1, y2;
+    rotate_pair(to_f32(x1[j]), to_f32(x2[j]), c[j], s[j], y1, y2);
+    x1[j] = from_f32<__bf16>(y1);
+    x2[j] = from_f32<__bf16>(y2);
+  }
+}
+ROPE_HD void rotate_inter8(bf16x8& x, const float* c, const float* s) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float y1, y2;
+    rotate_pair(to_f32(x[2 * j]), to_f32(x[2 * j + 1]), c[j], s[j], y1, y2);
+    x[2 * j] = from_f32<__bf16>(y1);
+    x[2 * j + 1] = from_f32<__bf16>(y2);
+  }
+}
+
+ROPE_HD void load_cs(const AttnArgs& a, int64_t p, int first, int n, float* c, float* s) {
+  const float* cr = a.cos + p * a.half + first;
+  const float* sr = a.sin + p * a.half + first;
+  for (int j = 0; j < n; ++j) {
+    c[j] = cr[j];
+    s[j] = sr[j];
+  }
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ float wave_xor32(float x) {
+  // the partner lane l ^ 32 (ds_bpermute addresses are byte lane indices)
+  const int src = (int)((__lane_id() ^ 32) << 2);
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x)));
+}
+#endif
+
+// ---------------------------------------------------------------- kernel
+// H16: split-half pairs, (R/2)/16 (the register distance between the two
+// chunks of a pair; a compile-time constant so the registers stay registers);
+// 0 for interleaved pairs.
+template <int D, int PAIR, int H16>
+__global__ void __launch_bounds__(kBlock) rope_attention_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  extern __shared__ __bf16 lds[];
+  const int q_tile = blockIdx.x % a.q_tiles;
+  const int h = (blockIdx.x / a.q_tiles) % a.n_heads_q;
+  const int b = blockIdx.x / (a.q_tiles * a.n_heads_q);
+  const int hk = h / (a.n_heads_q / a.n_heads_k);
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int hs = lane >> 5;  // which half of the wave: k slots 0-7 or 8-15
+  const int qi = q_tile * kQueries + wave * 32 + (lane & 31);  // this lane's query row
+  constexpr int kSteps = D / 16;  // k-steps of S^T over the head dim
+  const int R = 2 * a.half;
+
+  // ---- Q: this lane's half of its query row, rotated, as B operands.
+  bf16x8 qreg[kSteps];
+  {
+    const bool q_ok = qi < a.seq_q;
+    const __bf16* qrow = a.q + row_of<D>(a, b, h, a.n_heads_q, a.seq_q, q_ok ? qi : 0);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      bf16x8 z = {};
+      qreg[s] = q_ok ? *reinterpret_cast<const bf16x8*>(qrow + s * 16 + hs * 8) : z;
+    }
+    const int64_t p = (q_ok && a.rotate) ? query_pos(a, b, qi) : -1;
+    if (p >= 0) {
+      float c[8], sn[8];
+      if constexpr (PAIR == kSplitHalf) {
+        // chunk s (dims s*16 + hs*8 .. +7, all < R/2 = 16*H16) pairs with
+        // chunk s + H16 of this lane (dims + R/2)
+#pragma unroll
+        for (int s = 0; s < H16; ++s) {
+          load_cs(a, p, s * 16 + hs * 8, 8, c, sn);
+          rotate_split8(qreg[s], qreg[s + H16], c, sn);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          const int d = s * 16 + hs * 8;  // 4 interleaved pairs, freqs d/2 ..
+          if (d < R) {
+            load_cs(a, p, d / 2, 4, c, sn);
+            rotate_inter8(qreg[s], c, sn);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- running softmax state and O^T accumulators (D/32 tiles of 32 dims)
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  floatx16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = (floatx16){};
+
+  const int n_tiles = key_tiles(a, q_tile);
+  const int per_key = KItems<D, PAIR>::per_key(a);
+  const int rchunks = R / 8;
+  const __bf16* kbase = a.k + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
+  const __bf16* vbase = a.v + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
+  const int causal_shift = a.seq_k - a.seq_q;
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int k0 = kt * kKeys;
+    __syncthreads();  // the previous tile's reads are done
+    // -- K tile: rotate while staging
+    for (int it = t; it < kKeys * per_key; it += kBlock) {
+      const int kk = it / per_key, item = it - kk * per_key;
+      const int key = k0 + kk;
+      const bool ok = key < a.seq_k;
+      const __bf16* krow = kbase + (int64_t)(ok ? key : 0) * D;
+      const int64_t p = (ok && a.rotate) ? key_pos(a, b, key) : -1;
+      bf16x8 z = {};
+      if constexpr (PAIR == kSplitHalf) {
+        const int npair = rchunks / 2;
+        if (item < npair) {
+          const int d1 = item * 8, d2 = a.half + item * 8;
+          bf16x8 x1 = ok ? *reinterpret_cast<const bf16x8*>(krow + d1) : z;
+          bf16x8 x2 = ok ? *reinterpret_cast<const bf16x8*>(krow + d2) : z;
+          if (p >= 0) {
+            float c[8], sn[8];
+            load_cs(a, p, d1, 8, c, sn);
+            rotate_split8(x1, x2, c, sn);
+          }
+          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d1)]) = x1;
+          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d2)]) = x2;
+        } else {
+          const int d = R + (item - npair) * 8;
+          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d)]) =
+              ok ? *reinterpret_cast<const bf16x8*>(krow + d) : z;
+        }
+      } else {
+        const int d = item * 8;
+        bf16x8 x = ok ? *reinterpret_cast<const bf16x8*>(krow + d) : z;
+        if (item < rchunks && p >= 0) {
+          float c[4], sn[4];
+          load_cs(a, p, d / 2, 4, c, sn);
+          rotate_inter8(x, c, sn);
+        }
+        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d)]) = x;
+      }
+    }
+    // -- V tile, transposed: consecutive lanes take consecutive keys
+    for (int it = t; it < kKeys * (D / 8); it += kBlock) {
+      const int kk = it % kKeys, c = it / kKeys;
+      const int key = k0 + kk;
+      bf16x8 x = {};
+      if (key < a.seq_k) x = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)key * D + c * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lds[v_lds<D>(c * 8 + i, kk)] = x[i];
+    }
+    __syncthreads();
+
+    // -- S^T = K Q^T for the two 32-key halves of the tile
+    floatx16 sc[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      floatx16 s = {};
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(&lds[k_lds<D>(half * 32 + (lane & 31), st * 16 + hs * 8)]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[st], s, 0, 0, 0);
+      }
+      sc[half] = s;
+    }
+    // -- mask, then the online softmax in base 2
+    float m_tile = -__builtin_inff();
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = k0 + half * 32 + 8 * (j / 4) + 4 * hs + (j % 4);
+        const bool vis = key < a.seq_k && (!a.causal || key <= qi + causal_shift);
+        const float x = vis ? sc[half][j] * a.scale_log2e : -__builtin_inff();
+        sc[half][j] = x;
+        m_tile = fmaxf(m_tile, x);
+      }
+    m_tile = fmaxf(m_tile, wave_xor32(m_tile));
+    const float m_new = fmaxf(m_run, m_tile);
+    const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float l_tile = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float x = sc[half][j];
+        const float pj = x == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(x - m_new);
+        sc[half][j] = pj;
+        l_tile += pj;
+      }
+    l_tile += wave_xor32(l_tile);
+    l_run = l_run * alpha + l_tile;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
+
+    // -- O^T += V^T P^T: k-steps of 16 keys; step (half, u) covers keys
+    // half*32 + 16u .. +15, lane's slots j = 8u .. 8u+7 of sc[half], which
+    // hold keys 16u + 8*(i/4) + 4*hs + i%4 for slot i
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = from_f32<__bf16>(sc[half][8 * u + i]);
+        const int kb = half * 32 + 16 * u + 4 * hs;  // keys kb..kb+3 and kb+8..kb+11
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int dim = dt * 32 + (lane & 31);
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&lds[v_lds<D>(dim, kb)]);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&lds[v_lds<D>(dim, kb + 8)]);
+          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[dt], 0, 0, 0);
+        }
+      }
+  }
+
+  // ---- O = acc / l: lane holds dims dt*32 + 8*(j/4) + 4*hs + j%4 of its row
+  if (qi < a.seq_q) {
+    __bf16* orow = a.o + row_of<D>(a, b, h, a.n_heads_q, a.seq_q, qi);
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = from_f32<__bf16>(acc[dt][4 * g + i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * g + 4 * hs) = out;
+      }
+  }
+#endif
+}
+
+}  // namespace attn
+}  // namespace rope

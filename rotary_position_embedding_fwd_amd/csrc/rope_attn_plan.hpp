@@ -1,0 +1,105 @@
+// rope_attn_plan.hpp -- host-side checks and launch plan of the fused
+// attention (rope_attention.hpp). Never touches device memory.
+#pragma once
+
+#include <stdint.h>
+
+#include <cmath>
+
+#include "librope.h"
+#include "rope_attention.hpp"
+
+namespace rope {
+namespace attn {
+
+struct AttnPlan {
+  AttnArgs a;
+  bool empty;
+  int64_t grid;
+  int head_dim;
+  int pairing;
+  int h16;  // split-half: (R/2)/16; 0 otherwise
+  int64_t lds;
+};
+
+inline bool ranges_meet(const void* p, int64_t bytes, const void* q, int64_t qbytes) {
+  if (!p || !q || bytes <= 0 || qbytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (uintptr_t)bytes;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + (uintptr_t)qbytes;
+  return a0 < b1 && b0 < a1;
+}
+
+inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
+  if (!d || !pl) return ROPE_ERR_NULL;
+  *pl = AttnPlan{};
+  if (d->dtype != ROPE_BF16) return ROPE_ERR_DTYPE;
+  if (d->pairing != ROPE_SPLIT_HALF && d->pairing != ROPE_INTERLEAVED) return ROPE_ERR_LAYOUT;
+  const int64_t B = d->batch, Hq = d->n_heads_q, Hk = d->n_heads_k, Sq = d->seq_len_q,
+                Sk = d->seq_len_k, D = d->head_dim, R = d->rotary_dim;
+  if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hk < 1 || Hq % Hk) return ROPE_ERR_SHAPE;
+  if (D != 64 && D != 128) return ROPE_ERR_SHAPE;
+  if (R < 0 || R > D || (R & 1)) return ROPE_ERR_SHAPE;
+  if (d->pairing == ROPE_SPLIT_HALF ? (R % 32) : (R % 8)) return ROPE_ERR_SHAPE;
+  if (d->causal && Sq > Sk) return ROPE_ERR_SHAPE;
+  if (!std::isfinite(d->scale) || d->table_rows < 0) return ROPE_ERR_SHAPE;
+  if (d->q_pos_batch_stride < 0 || d->k_pos_batch_stride < 0) return ROPE_ERR_SHAPE;
+  // 32-bit index arithmetic inside the kernel
+  const int64_t lim = (int64_t)1 << 30;
+  if (B > lim || Hq > lim || Sq > lim || Sk > lim) return ROPE_ERR_SHAPE;
+  pl->empty = B == 0 || Sq == 0;
+  if (pl->empty) return ROPE_OK;
+  const bool rotate = d->rotate && R > 0;
+  if (rotate && ((!d->q_pos || !d->k_pos) && Sk > d->table_rows)) return ROPE_ERR_SHAPE;
+  if (!d->q || !d->o || (Sk > 0 && (!d->k || !d->v))) return ROPE_ERR_NULL;
+  if (rotate && (!d->cos || !d->sin)) return ROPE_ERR_NULL;
+  auto mis = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) % m) != 0; };
+  if (mis(d->q, 16) || mis(d->k, 16) || mis(d->v, 16) || mis(d->o, 16)) return ROPE_ERR_ALIGN;
+  if (rotate && (mis(d->cos, 16) || mis(d->sin, 16))) return ROPE_ERR_ALIGN;
+  if (mis(d->q_pos, 4) || mis(d->k_pos, 4)) return ROPE_ERR_ALIGN;
+  const int64_t qbytes = B * Hq * Sq * D * 2, kvbytes = B * Hk * Sk * D * 2;
+  if (ranges_meet(d->o, qbytes, d->q, qbytes) || ranges_meet(d->o, qbytes, d->k, kvbytes) ||
+      ranges_meet(d->o, qbytes, d->v, kvbytes))
+    return ROPE_ERR_ALIAS;
+  const int64_t tbytes = d->table_rows * (R / 2) * 4;
+  if (rotate && (ranges_meet(d->o, qbytes, d->cos, tbytes) ||
+                 ranges_meet(d->o, qbytes, d->sin, tbytes)))
+    return ROPE_ERR_ALIAS;
+  if (d->q_pos && ranges_meet(d->o, qbytes, d->q_pos, 4 * ((B - 1) * d->q_pos_batch_stride + Sq)))
+    return ROPE_ERR_ALIAS;
+  if (d->k_pos && ranges_meet(d->o, qbytes, d->k_pos, 4 * ((B - 1) * d->k_pos_batch_stride + Sk)))
+    return ROPE_ERR_ALIAS;
+
+  AttnArgs& a = pl->a;
+  a.q = static_cast<const __bf16*>(d->q);
+  a.k = static_cast<const __bf16*>(d->k);
+  a.v = static_cast<const __bf16*>(d->v);
+  a.o = static_cast<__bf16*>(d->o);
+  a.cos = d->cos;
+  a.sin = d->sin;
+  a.q_pos = d->q_pos;
+  a.k_pos = d->k_pos;
+  a.q_pos_bs = d->q_pos_batch_stride;
+  a.k_pos_bs = d->k_pos_batch_stride;
+  a.table_rows = d->table_rows;
+  a.batch = (int32_t)B;
+  a.n_heads_q = (int32_t)Hq;
+  a.n_heads_k = (int32_t)Hk;
+  a.seq_q = (int32_t)Sq;
+  a.seq_k = (int32_t)Sk;
+  a.half = rotate ? (int32_t)(R / 2) : 0;
+  a.rotate = rotate ? 1 : 0;
+  a.causal = d->causal ? 1 : 0;
+  a.q_tiles = (int32_t)((Sq + kQueries - 1) / kQueries);
+  const double scale = d->scale != 0.0 ? d->scale : 1.0 / std::sqrt((double)D);
+  a.scale_log2e = (float)(scale * 1.4426950408889634);  // log2(e)
+  pl->grid = (int64_t)a.q_tiles * Hq * B;
+  if (pl->grid > 0x7fffffff) return ROPE_ERR_SHAPE;
+  pl->head_dim = (int)D;
+  pl->pairing = d->pairing;
+  pl->h16 = (rotate && d->pairing == ROPE_SPLIT_HALF) ? (int)(R / 32) : 0;
+  pl->lds = D == 64 ? lds_bytes<64>() : lds_bytes<128>();
+  return ROPE_OK;
+}
+
+}  // namespace attn
+}  // namespace rope

@@ -293,3 +293,112 @@ def test_binding_marshals_strided_views():
                            table_layout="duplicated")
     with pytest.raises(ValueError):
         rp.make_apply_desc(q.transpose(2, 3), None, c, c, table_layout="duplicated")
+
+
+# ------------------------------------------------- attention with RoPE fused
+def attn_desc(**kw):
+    d = rp.RopeAttnDesc()
+    d.batch, d.n_heads_q, d.n_heads_k, d.seq_len_q, d.seq_len_k = 2, 8, 2, 100, 100
+    d.head_dim, d.rotary_dim, d.dtype, d.pairing, d.causal, d.rotate = 128, 128, 2, 0, 1, 1
+    qb, kb = 2 * 8 * 100 * 128 * 2, 2 * 2 * 100 * 128 * 2
+    d.q, d.k, d.v, d.o = A16 * 1024, A16 * 1024 + qb, A16 * 1024 + qb + kb, A16 * 4096
+    d.cos, d.sin, d.table_rows = A16 * 8192, A16 * 9000, 100
+    for key, v in kw.items():
+        setattr(d, key, v)
+    return d
+
+
+def call_attn(d):
+    return rp.lib().rope_attention_fwd(ctypes.byref(d) if d is not None else None, None)
+
+
+@pytest.mark.parametrize("change,expected", [
+    (dict(dtype=1), DTYPE), (dict(dtype=0), DTYPE), (dict(dtype=7), DTYPE),
+    (dict(pairing=2), LAYOUT),
+    (dict(head_dim=96, rotary_dim=96), SHAPE), (dict(head_dim=256, rotary_dim=128), SHAPE),
+    (dict(rotary_dim=48), SHAPE),                     # split-half R % 32
+    (dict(pairing=1, rotary_dim=20), SHAPE),          # interleaved R % 8
+    (dict(rotary_dim=130), SHAPE), (dict(rotary_dim=-2), SHAPE),
+    (dict(n_heads_k=3), SHAPE), (dict(n_heads_k=0), SHAPE), (dict(n_heads_q=0), SHAPE),
+    (dict(seq_len_q=101), SHAPE),                     # causal needs Sq <= Sk
+    (dict(table_rows=99), SHAPE),                     # default positions leave the table
+    (dict(scale=float("nan")), SHAPE), (dict(scale=float("inf")), SHAPE),
+    (dict(batch=-1), SHAPE), (dict(q_pos_batch_stride=-1), SHAPE),
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(v=None), NULL), (dict(cos=None), NULL),
+    (dict(q=A16 * 1024 + 2), ALIGN), (dict(o=A16 * 4096 + 8), ALIGN),
+    (dict(sin=A16 * 9000 + 4), ALIGN),
+    (dict(q_pos=A16 * 10000 + 2, k_pos=A16 * 10000), ALIGN),
+    (dict(o=A16 * 1024), ALIAS),                      # O onto Q
+    (dict(o=A16 * 1024 + 2 * 8 * 100 * 128 * 2 - 32), ALIAS),   # O runs into K
+    (dict(cos=A16 * 4096 + 64), ALIAS),               # table inside O
+    (dict(q_pos=A16 * 4096, k_pos=A16 * 10000), ALIAS),
+])
+def test_attention_validation_errors(change, expected):
+    assert call_attn(attn_desc(**change)) == expected
+
+
+def test_attention_empty_and_null():
+    assert call_attn(None) == NULL
+    # no queries: nothing to do, even with NULL data pointers
+    assert call_attn(attn_desc(seq_len_q=0, q=None, k=None, v=None, o=None)) == OK
+    assert call_attn(attn_desc(batch=0, q=None, o=None)) == OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks behaviour with no GPU present")
+@pytest.mark.parametrize("change", [
+    dict(),
+    dict(causal=0, seq_len_q=130),                       # non-causal, Sq > Sk
+    dict(seq_len_k=0, k=None, v=None, seq_len_q=0),      # (empty: OK, checked above)
+    dict(seq_len_k=0, k=None, v=None, causal=0),         # no keys: K and V may be NULL
+    dict(rotate=0, cos=None, sin=None, table_rows=0),    # plain attention needs no table
+    dict(rotary_dim=0, cos=None, sin=None),
+    dict(pairing=1, rotary_dim=8, head_dim=64),
+    dict(q_pos=A16 * 10000, k_pos=A16 * 10100, q_pos_batch_stride=100, k_pos_batch_stride=100,
+         table_rows=4),                                  # index positions: any table size
+    dict(cos=A16 * 1024, sin=A16 * 1024 + 64),           # tables may share memory with inputs
+])
+def test_attention_accepts_valid_descriptors(change):
+    rc = call_attn(attn_desc(**change))
+    assert rc in ((OK,) if change.get("seq_len_q") == 0 else (HIP,))
+
+
+def test_attention_desc_layout_matches_the_c_compiler(tmp_path):
+    src = tmp_path / "attn_layout.c"
+    src.write_text('''#include <stddef.h>
+#include <stdio.h>
+#include "librope.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(rope_attn_desc_t), offsetof(rope_attn_desc_t, q),
+         offsetof(rope_attn_desc_t, table_rows), offsetof(rope_attn_desc_t, q_pos),
+         offsetof(rope_attn_desc_t, k_pos_batch_stride), offsetof(rope_attn_desc_t, scale));
+  return 0;
+}
+''')
+    exe = tmp_path / "attn_layout"
+    subprocess.run(["gcc", "-std=c11", f"-I{os.path.join(ROOT, 'include')}", "-o", str(exe),
+                    str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    D = rp.RopeAttnDesc
+    assert got == [ctypes.sizeof(D), D.q.offset, D.table_rows.offset, D.q_pos.offset,
+                   D.k_pos_batch_stride.offset, D.scale.offset]
+
+
+def test_binding_marshals_attention():
+    q = torch.zeros(2, 8, 50, 64, dtype=torch.bfloat16)
+    k = torch.zeros(2, 2, 70, 64, dtype=torch.bfloat16)
+    c = torch.zeros(70, 16)
+    o = torch.empty_like(q)
+    d = rp.make_attn_desc(q, k, k, c, c, o, causal=True)
+    assert (d.batch, d.n_heads_q, d.n_heads_k, d.seq_len_q, d.seq_len_k, d.head_dim,
+            d.rotary_dim, d.table_rows, d.causal, d.rotate) == (2, 8, 2, 50, 70, 64, 32, 70, 1, 1)
+    kp = torch.arange(140, dtype=torch.int32)
+    qp = torch.arange(50, dtype=torch.int32)
+    d = rp.make_attn_desc(q, k, k, c, c, o, q_pos=qp, k_pos=kp)
+    assert d.q_pos_batch_stride == 0 and d.k_pos_batch_stride == 70
+    with pytest.raises(ValueError):
+        rp.make_attn_desc(q, k, k, c, c, o, k_pos=kp[:69])
+    with pytest.raises(ValueError):
+        rp.make_attn_desc(q, k, k[:, :1].contiguous(), c, c, o)
+    with pytest.raises(ValueError):
+        rp.make_attn_desc(q, k, k, c, c, o[:, :, :10])

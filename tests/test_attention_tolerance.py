@@ -1,0 +1,157 @@
+"""The error bound of tests/_attn.py, checked on the CPU.
+
+Two directions:
+  - a numerical model of the kernel's arithmetic (float32 scores, online
+    softmax over 64-key tiles in base 2, weights rounded to bf16 before they
+    multiply V, float32 accumulation, bf16 output), written here in numpy
+    from that description, stays inside the bound;
+  - mistakes planted in the oracle (a key dropped, the causal diagonal moved
+    by one, the wrong pairing, positions off by one, K left unrotated, the
+    wrong K/V head for a query head) land outside it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import _attn as A
+
+
+def _inputs(B, Hq, Hk, Sq, Sk, D, seed):
+    q = W.normal((B, Hq, Sq, D), "bf16", seed)
+    k = W.normal((B, Hk, Sk, D), "bf16", seed + 1)
+    v = W.normal((B, Hk, Sk, D), "bf16", seed + 2)
+    return q, k, v
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k_pos=None):
+    """The kernel's arithmetic in numpy float32 (see the module docstring)."""
+    qs, ks, vs = (oracle.torch_to_storage(t) for t in (q, k, v))
+    B, Hq, Sq, D = qs.shape
+    Hk, Sk = ks.shape[1], ks.shape[2]
+    qp = A._positions(q_pos, B, Sq, Sk - Sq).astype(np.int32)
+    kp = A._positions(k_pos, B, Sk, 0).astype(np.int32)
+    qr = A.bf16_values(oracle.rope(qs, "bf16", pairing=pairing, rotary_dim=R, theta=theta,
+                                   pos=qp, pos_batch_stride=Sq, table_rows=cos.shape[0]))
+    kr = A.bf16_values(oracle.rope(ks, "bf16", pairing=pairing, rotary_dim=R, theta=theta,
+                                   pos=kp, pos_batch_stride=Sk, table_rows=cos.shape[0]))
+    vv = A.bf16_values(vs).astype(np.float32)
+    c = np.float32(1.0 / np.sqrt(D) * 1.4426950408889634)
+    out = np.zeros((B, Hq, Sq, D), np.float64)
+    g = Hq // Hk
+    for b in range(B):
+        for h in range(Hq):
+            Q = qr[b, h].astype(np.float32)
+            K = kr[b, h // g].astype(np.float32)
+            V = vv[b, h // g]
+            m = np.full(Sq, -np.inf, np.float32)
+            l = np.zeros(Sq, np.float32)
+            acc = np.zeros((Sq, D), np.float32)
+            for k0 in range(0, Sk, 64):
+                kk = np.arange(k0, min(k0 + 64, Sk))
+                x = (Q @ K[kk].T) * c
+                if causal:
+                    x = np.where(kk[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq), x, -np.inf)
+                m_new = np.maximum(m, x.max(axis=1))
+                alpha = np.where(m_new == m, np.float32(1), np.exp2(m - m_new)).astype(np.float32)
+                p = np.where(np.isneginf(x), np.float32(0), np.exp2(x - m_new[:, None]))
+                p = p.astype(np.float32)
+                l = l * alpha + p.sum(axis=1, dtype=np.float32)
+                acc = acc * alpha[:, None] + _bf16(p) @ V[kk]
+                m = m_new
+            inv = np.where(l > 0, 1 / l, 0).astype(np.float32)
+            out[b, h] = _bf16(acc * inv[:, None])
+    return out
+
+
+CASES = [
+    # B Hq Hk Sq Sk D R pairing causal
+    (1, 2, 1, 130, 130, 64, 64, "split_half", True),
+    (2, 4, 2, 77, 200, 128, 128, "split_half", False),
+    (1, 2, 2, 129, 129, 64, 32, "interleaved", True),
+    (1, 1, 1, 1, 257, 128, 96, "split_half", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_kernel_model_inside_bound(orc, case):
+    B, Hq, Hk, Sq, Sk, D, R, pairing, causal = case
+    q, k, v = _inputs(B, Hq, Hk, Sq, Sk, D, 7100 + Sq)
+    cos, sin = oracle.table(10000.0, R, max(Sq, Sk))
+    ref, tol = A.reference(q, k, v, cos, sin, pairing=pairing, rotary_dim=R, causal=causal)
+    got = _kernel_model(q, k, v, cos, sin, pairing=pairing, R=R, theta=10000.0, causal=causal)
+    err = np.abs(got - ref)
+    assert (err <= tol).all(), float((err / tol).max())
+    # the bound is not vacuous: well under the size of the outputs
+    assert np.median(tol) < 0.02 * np.median(np.abs(A.bf16_values(
+        oracle.torch_to_storage(v)))) + 0.01
+
+
+def _mutant_violates(ref, tol, mut, min_frac=0.01):
+    bad = np.abs(mut - ref) > tol
+    return bad.mean() >= min_frac
+
+
+def test_planted_mistakes_fall_outside(orc):
+    B, Hq, Hk, Sq, Sk, D, R = 1, 4, 2, 130, 130, 64, 64
+    q, k, v = _inputs(B, Hq, Hk, Sq, Sk, D, 7300)
+    cos, sin = oracle.table(10000.0, R, Sk)
+    qs, ks, vs = (oracle.torch_to_storage(t) for t in (q, k, v))
+    qp = np.arange(Sq, dtype=np.int32)
+    kp = np.arange(Sk, dtype=np.int32)
+    ref, tol = A.reference(q, k, v, cos, sin, causal=True)
+    ref_nc, tol_nc = A.reference(q, k, v, cos, sin, causal=False)
+    base = dict(pairing="split_half", rotary_dim=R, theta=10000.0, table_rows=Sk, scale=None)
+
+    def orc_att(qa, ka, va, qpos, kpos, causal=True, **over):
+        kw = dict(base, **over)
+        return oracle.rope_attention(qa, ka, va, "bf16", qpos=qpos, qpos_batch_stride=0,
+                                     kpos=kpos, kpos_batch_stride=0, causal=causal, **kw)
+
+    # the same call reproduces the expected values exactly
+    assert np.array_equal(orc_att(qs, ks, vs, qp, kp), ref)
+    mutants = {
+        # the last key of every query row dropped (non-causal)
+        "dropped key": (orc_att(qs, ks[:, :, :-1].copy(), vs[:, :, :-1].copy(), qp, kp[:-1],
+                                causal=False), ref_nc, tol_nc),
+        # the causal diagonal moved by one: each query loses its own key (rows
+        # 1.. against keys 0..Sk-2 keep the shape causal attention accepts)
+        "causal off by one": (orc_att(qs[:, :, 1:].copy(), ks[:, :, :-1].copy(),
+                                      vs[:, :, :-1].copy(), qp[1:], kp[:-1]),
+                              ref[:, :, 1:], tol[:, :, 1:]),
+        "wrong pairing": (orc_att(qs, ks, vs, qp, kp, pairing="interleaved"), ref, tol),
+        "query positions off by one": (orc_att(qs, ks, vs, qp + 1, kp), ref, tol),
+        "keys not rotated": (orc_att(qs, ks, vs, qp, np.full(Sk, -1, np.int32)), ref, tol),
+        "wrong kv head": (orc_att(qs, ks[:, ::-1].copy(), vs[:, ::-1].copy(), qp, kp), ref, tol),
+    }
+    for name, (mut, r, t) in mutants.items():
+        assert _mutant_violates(r, t, mut), name
+
+
+def test_unrounded_weights_are_distinguishable(orc):
+    # the bound is tight enough that a kernel which skipped the bf16 rounding
+    # of its weights would still pass, but one that rounded them twice (to
+    # 4 bits) would not
+    B, Hq, Hk, Sq, Sk, D, R = 1, 1, 1, 64, 200, 64, 64
+    q, k, v = _inputs(B, Hq, Hk, Sq, Sk, D, 7400)
+    cos, sin = oracle.table(10000.0, R, Sk)
+    ref, tol = A.reference(q, k, v, cos, sin)
+    qs, ks, vs = (oracle.torch_to_storage(t) for t in (q, k, v))
+    qr = A.bf16_values(oracle.rope(qs, "bf16", rotary_dim=R, pos=np.arange(Sq, dtype=np.int32)
+                                   + (Sk - Sq), table_rows=Sk))[0, 0]
+    kr = A.bf16_values(oracle.rope(ks, "bf16", rotary_dim=R, table_rows=Sk))[0, 0]
+    vv = A.bf16_values(vs)[0, 0]
+    s = qr @ kr.T / np.sqrt(D)
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    l = w.sum(axis=1, keepdims=True)
+    exact = (w @ vv) / l
+    assert (np.abs(exact - ref[0, 0]) <= tol[0, 0]).all()
+    coarse = w / w.max(axis=1, keepdims=True)
+    e = np.floor(np.log2(np.maximum(coarse, 1e-300)))
+    coarse = np.round(coarse / 2.0 ** (e - 3)) * 2.0 ** (e - 3) * w.max(axis=1, keepdims=True)
+    assert _mutant_violates(ref[0, 0], tol[0, 0], (coarse @ vv) / l)

@@ -38,7 +38,7 @@ INTERLEAVED = "interleaved"
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
-SEED_OFFSETS = {"q": 0, "k": 1, "dq": 2, "dk": 3, "pos": 4}
+SEED_OFFSETS = {"q": 0, "k": 1, "dq": 2, "dk": 3, "pos": 4, "v": 5, "kpos": 6}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -116,6 +116,65 @@ ALL = (TINY_F32, LLAMA_GQA_PREFILL, BSHD_INTERLEAVED, PARTIAL_INDEXED, DECODE,
 BY_NAME = {w.name: w for w in ALL}
 
 
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """One synthetic problem for attention over rotated Q and K: Q
+    [batch, n_heads_q, seq_len_q, head_dim], K and V [batch, n_heads_k,
+    seq_len_k, head_dim] (rotary-embedding-torch docs, flash_attn_with_rotary,
+    Input Tensor Shapes), bf16 storage.
+
+    pos_kind "none": key j at position j, query i at i + seq_len_k - seq_len_q;
+    "cls_offset": one shared index row for queries and keys (seq_len_q ==
+    seq_len_k), the first `n_masked` tokens at -1 (not rotated), the rest
+    start + 0, 1, ... with a seeded start in [0, pos_start_max] (the docs'
+    example skips two CLS/register tokens and rotates the rest from 0).
+    """
+
+    name: str
+    index: int
+    batch: int
+    n_heads_q: int
+    n_heads_k: int
+    seq_len_q: int
+    seq_len_k: int
+    head_dim: int
+    rotary_dim: int
+    pairing: str
+    theta: float
+    table_rows: int
+    causal: bool
+    pos_kind: str = "none"
+    n_masked: int = 0
+    pos_start_max: int = 0
+    dtype: str = "bf16"
+
+    @property
+    def q_shape(self) -> tuple:
+        return (self.batch, self.n_heads_q, self.seq_len_q, self.head_dim)
+
+    @property
+    def kv_shape(self) -> tuple:
+        return (self.batch, self.n_heads_k, self.seq_len_k, self.head_dim)
+
+    def seed(self, what: str) -> int:
+        return 1000 * self.index + SEED_OFFSETS[what]
+
+    def scaled(self, **changes) -> "AttnWorkload":
+        return dataclasses.replace(self, **changes)
+
+
+# Causal GQA prefill attention at the Llama shape of the RoPE workloads above.
+ATTN_LLAMA_PREFILL = AttnWorkload("attn_llama_gqa_prefill_bf16", 7, 4, 32, 8, 4096, 4096,
+                                  128, 128, SPLIT_HALF, 10000.0, 4096, True)
+# The docs' example: 1024 rotated tokens after two unrotated ones, R = 32 of
+# head dim 64, causal.
+ATTN_CLS_SKIP = AttnWorkload("attn_cls_skip_partial_bf16", 8, 1, 8, 8, 1026, 1026, 64, 32,
+                             SPLIT_HALF, 10000.0, 1024, True, pos_kind="cls_offset",
+                             n_masked=2, pos_start_max=0)
+
+ATTN_ALL = (ATTN_LLAMA_PREFILL, ATTN_CLS_SKIP)
+
+
 def _gen(seed: int) -> torch.Generator:
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
@@ -158,3 +217,26 @@ def positions(w: Workload) -> Optional[torch.Tensor]:
 def random_positions(n: int, high: int, seed: int, low: int = 0) -> torch.Tensor:
     """Uniform int32 positions in [low, high) for edge-case tests."""
     return torch.randint(low, high, (n,), generator=_gen(seed), dtype=torch.int32)
+
+
+def attn_tensors(w: AttnWorkload) -> dict:
+    """Seeded CPU q, k, v of attention workload `w`."""
+    return {"q": normal(w.q_shape, w.dtype, w.seed("q")),
+            "k": normal(w.kv_shape, w.dtype, w.seed("k")),
+            "v": normal(w.kv_shape, w.dtype, w.seed("v"))}
+
+
+def attn_positions(w: AttnWorkload) -> Optional[torch.Tensor]:
+    """The shared int32 index row of attention workload `w`, or None."""
+    if w.pos_kind == "none":
+        return None
+    if w.pos_kind == "cls_offset":
+        if w.seq_len_q != w.seq_len_k:
+            raise ValueError("a shared index row needs seq_len_q == seq_len_k")
+        g = _gen(w.seed("pos"))
+        start = int(torch.randint(0, w.pos_start_max + 1, (1,), generator=g))
+        n = w.seq_len_k - w.n_masked
+        body = torch.arange(n, dtype=torch.int32) + start
+        head = torch.full((w.n_masked,), -1, dtype=torch.int32)
+        return torch.cat([head, body])
+    raise ValueError(f"unknown pos_kind {w.pos_kind!r}")
