@@ -325,6 +325,95 @@ def time_theta(target_s: float = 0.15):
     return results
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, published
+
+
+def attention_flops(w) -> int:
+    """Algorithmic flops of one attention call: 2 D for each visible (query,
+    key) pair in S = Q K^T and 2 D more in O = P V, for every (batch, head)."""
+    Sq, Sk = w.seq_len_q, w.seq_len_k
+    if w.causal:
+        # query i sees keys 0 .. i + Sk - Sq
+        pairs = sum(min(Sk, i + Sk - Sq + 1) for i in range(Sq))
+    else:
+        pairs = Sq * Sk
+    return 4 * w.head_dim * pairs * w.batch * w.n_heads_q
+
+
+def _time_event(fn, stream, target_s: float):
+    """Average µs per call of fn() on `stream`, between HIP events."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t0, 1e-6)
+    reps = int(min(2000, max(10, target_s / est)))
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1000.0 / reps, reps
+
+
+def time_attention(target_s: float = 0.5):
+    """Attention over rotated Q and K: the fused call (rope_attention_fwd,
+    rotation inside the kernel) against the unfused sequence (rope_apply
+    writing rotated copies of Q and K, then the same attention kernel with
+    rotation off), on the causal Llama GQA prefill shape and on the
+    CLS-skipping partial-rotary example. One JSON object per workload."""
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    stream = torch.cuda.current_stream()
+    results = []
+    for w in W.ATTN_ALL:
+        t = {k: v.cuda() for k, v in W.attn_tensors(w).items()}
+        pos = W.attn_positions(w)
+        pos = None if pos is None else pos.cuda()
+        c, s = (x.cuda() for x in rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta))
+        o = torch.empty_like(t["q"])
+        kw = dict(pairing=w.pairing, rotary_dim=w.rotary_dim, causal=w.causal, q_pos=pos,
+                  k_pos=pos, stream=stream)
+        fused = rp.prepare_attention(t["q"], t["k"], t["v"], c, s, o, **kw)
+        qr, kr = torch.empty_like(t["q"]), torch.empty_like(t["k"])
+        rot = rp.prepare_apply(t["q"], t["k"], c, s, q_out=qr, k_out=kr, pairing=w.pairing,
+                               rotary_dim=w.rotary_dim, pos=pos, stream=stream)
+        plain = rp.prepare_attention(qr, kr, t["v"], c, s, o, rotate=False, **kw)
+        flops = attention_flops(w)
+        fused_us, reps = _time_event(fused.rope_attention_fwd, stream, target_s)
+        plain_us, _ = _time_event(plain.rope_attention_fwd, stream, target_s)
+        rot_us, _ = _time_event(rot.rope_apply, stream, target_s / 4)
+
+        def unfused():
+            rot.rope_apply()
+            plain.rope_attention_fwd()
+        unfused_us, _ = _time_event(unfused, stream, target_s)
+        tf = flops / (fused_us * 1e-6) / 1e12
+        results.append({
+            "workload": w.name, "q_shape": list(w.q_shape), "kv_shape": list(w.kv_shape),
+            "rotary_dim": w.rotary_dim, "pairing": w.pairing, "causal": w.causal,
+            "positions": w.pos_kind, "algorithmic_flops_per_call": flops,
+            "fused_us_per_call": round(fused_us, 2),
+            "fused_TFLOPs": round(tf, 1),
+            "fused_frac_of_mfma_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "attention_without_rotation_us": round(plain_us, 2),
+            "rotation_out_of_place_us": round(rot_us, 2),
+            "unfused_us_per_call": round(unfused_us, 2),
+            "fused_saves_us": round(unfused_us - fused_us, 2),
+            "reps": reps,
+            "kernel": "rope_attention_kernel (v_mfma_f32_32x32x16_bf16)",
+        })
+        del t, o, qr, kr, fused, rot, plain
+        torch.cuda.empty_cache()
+    return results
+
+
 def time_general_form(w, target_s: float = 0.15):
     """rope_apply on workload w's shapes laid out as one packed QKV buffer
     [B, S, (Hq + 2 Hk) * D] (Q and K rotated in place where they sit), and
@@ -544,6 +633,9 @@ def main():
                     help="time the path with cos/sin computed from theta (no tables)")
     ap.add_argument("--layout-matrix", action="store_true",
                     help="rows vs token launch on token-major views, by shape and pairing")
+    ap.add_argument("--attention", action="store_true",
+                    help="time attention with RoPE fused on the loaded Q/K blocks, against "
+                         "rotation followed by attention")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -564,6 +656,10 @@ def main():
 
     if args.theta:
         for res in time_theta():
+            print(json.dumps(res), flush=True)
+        return
+    if args.attention:
+        for res in time_attention():
             print(json.dumps(res), flush=True)
         return
     if args.layout_matrix:

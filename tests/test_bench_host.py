@@ -64,3 +64,14 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_attention_flops_count_visible_pairs():
+    # causal with Sq == Sk: query i sees i + 1 keys, S (S + 1) / 2 pairs per head
+    w = W.ATTN_LLAMA_PREFILL
+    S = w.seq_len_q
+    assert bench.attention_flops(w) == 4 * w.head_dim * (S * (S + 1) // 2) * w.batch * w.n_heads_q
+    # non-causal: every pair; causal with Sq < Sk: the last Sq rows of the square
+    assert bench.attention_flops(w.scaled(causal=False)) == 4 * 128 * S * S * 4 * 32
+    v = w.scaled(seq_len_q=3, seq_len_k=10, batch=1, n_heads_q=1)
+    assert bench.attention_flops(v) == 4 * 128 * (8 + 9 + 10)
