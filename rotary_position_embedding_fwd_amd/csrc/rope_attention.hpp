@@ -45,6 +45,7 @@ constexpr int kQueries = 32 * kWaves;       // query rows per workgroup
 constexpr int kKeys = 64;                   // keys per tile
 constexpr int kKPad = 8;                    // K tile row padding (bf16)
 constexpr int kVPad = 8;                    // V^T tile row padding (bf16)
+constexpr int kXcds = 8;                    // accelerator dies, one L2 each
 
 struct AttnArgs {
   const __bf16* q;    // [B, Hq, Sq, D]
@@ -95,6 +96,36 @@ template <int D> ROPE_HD int v_lds(int dim, int key) {
   return k_lds_elems<D>() + dim * (kKeys + kVPad) + key;
 }
 
+// Workgroup -> (batch, query head, query tile). Workgroups are handed to the
+// dies round-robin (workgroup w to die w % 8), so the work list is cut into
+// 8 contiguous ranges and die x walks range x: the query tiles of one head,
+// and the heads of one K/V group, run on one die and share its L2. Within a
+// head the tiles go from the last (most keys when causal) to the first, so
+// the short ones fill the tail of the launch.
+struct Work {
+  int b, h, q_tile;
+};
+ROPE_HD Work work_of(const AttnArgs& a, int64_t blk) {
+  const int64_t n = (int64_t)a.q_tiles * a.n_heads_q * a.batch;
+  const int64_t full = n / kXcds, rem = n % kXcds;
+  const int64_t x = blk % kXcds, local = blk / kXcds;
+  const int64_t w = x * full + (x < rem ? x : rem) + local;
+  Work r;
+  r.q_tile = a.q_tiles - 1 - (int)(w % a.q_tiles);
+  r.h = (int)((w / a.q_tiles) % a.n_heads_q);
+  r.b = (int)(w / ((int64_t)a.q_tiles * a.n_heads_q));
+  return r;
+}
+
+// V tile staging: item it holds 4 consecutive keys (4 k4 .. 4 k4 + 3) of 8
+// dims (8 c .. 8 c + 7); consecutive lanes take consecutive key quads, so the
+// transposed tile is written 8 bytes (4 keys of one dim) at a time.
+template <int D> constexpr int v_items() { return (kKeys / 4) * (D / 8); }
+struct VItem {
+  int k4, c;
+};
+ROPE_HD VItem v_item(int it) { return VItem{it % (kKeys / 4), it / (kKeys / 4)}; }
+
 // Position of query row i / key row j (or -1: not rotated).
 ROPE_HD int64_t query_pos(const AttnArgs& a, int b, int i) {
   int64_t p = a.q_pos ? (int64_t)a.q_pos[(int64_t)b * a.q_pos_bs + i]
@@ -144,12 +175,21 @@ ROPE_HD void rotate_inter8(bf16x8& x, const float* c, const float* s) {
   }
 }
 
+// n (4 or 8) table entries from `first` (a multiple of 4) of row p: 16-byte
+// loads (tables are 16-byte aligned and R/2 is a multiple of 4).
 ROPE_HD void load_cs(const AttnArgs& a, int64_t p, int first, int n, float* c, float* s) {
-  const float* cr = a.cos + p * a.half + first;
-  const float* sr = a.sin + p * a.half + first;
-  for (int j = 0; j < n; ++j) {
-    c[j] = cr[j];
-    s[j] = sr[j];
+  const float4* cr = reinterpret_cast<const float4*>(a.cos + p * a.half + first);
+  const float4* sr = reinterpret_cast<const float4*>(a.sin + p * a.half + first);
+  for (int j = 0; j < n / 4; ++j) {
+    const float4 cv = cr[j], sv = sr[j];
+    c[4 * j] = cv.x;
+    c[4 * j + 1] = cv.y;
+    c[4 * j + 2] = cv.z;
+    c[4 * j + 3] = cv.w;
+    s[4 * j] = sv.x;
+    s[4 * j + 1] = sv.y;
+    s[4 * j + 2] = sv.z;
+    s[4 * j + 3] = sv.w;
   }
 }
 
@@ -166,12 +206,11 @@ __device__ __forceinline__ float wave_xor32(float x) {
 // chunks of a pair; a compile-time constant so the registers stay registers);
 // 0 for interleaved pairs.
 template <int D, int PAIR, int H16>
-__global__ void __launch_bounds__(kBlock) rope_attention_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __bf16 lds[];
-  const int q_tile = blockIdx.x % a.q_tiles;
-  const int h = (blockIdx.x / a.q_tiles) % a.n_heads_q;
-  const int b = blockIdx.x / (a.q_tiles * a.n_heads_q);
+  const Work wk = work_of(a, blockIdx.x);
+  const int q_tile = wk.q_tile, h = wk.h, b = wk.b;
   const int hk = h / (a.n_heads_q / a.n_heads_k);
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -226,6 +265,9 @@ __global__ void __launch_bounds__(kBlock) rope_attention_kernel(AttnArgs a) {
   const __bf16* kbase = a.k + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
   const __bf16* vbase = a.v + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
   const int causal_shift = a.seq_k - a.seq_q;
+  // this wave's query rows, for the masking decisions (uniform per wave)
+  const int wq_first = q_tile * kQueries + wave * 32;
+  const int wq_last = imin(wq_first + 31, a.seq_q - 1);
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int k0 = kt * kKeys;
@@ -267,16 +309,29 @@ __global__ void __launch_bounds__(kBlock) rope_attention_kernel(AttnArgs a) {
         *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d)]) = x;
       }
     }
-    // -- V tile, transposed: consecutive lanes take consecutive keys
-    for (int it = t; it < kKeys * (D / 8); it += kBlock) {
-      const int kk = it % kKeys, c = it / kKeys;
-      const int key = k0 + kk;
-      bf16x8 x = {};
-      if (key < a.seq_k) x = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)key * D + c * 8);
+    // -- V tile, transposed: 4 keys x 8 dims per item, 8-byte LDS writes
+    for (int it = t; it < v_items<D>(); it += kBlock) {
+      const VItem vi = v_item(it);
+      bf16x8 x[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) lds[v_lds<D>(c * 8 + i, kk)] = x[i];
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 4 * vi.k4 + r;
+        bf16x8 z = {};
+        x[r] = key < a.seq_k
+                   ? *reinterpret_cast<const bf16x8*>(vbase + (int64_t)key * D + vi.c * 8)
+                   : z;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x4 col = {x[0][i], x[1][i], x[2][i], x[3][i]};
+        *reinterpret_cast<bf16x4*>(&lds[v_lds<D>(vi.c * 8 + i, 4 * vi.k4)]) = col;
+      }
     }
     __syncthreads();
+    // a tile wholly after this wave's causal diagonal adds nothing: its
+    // scores are all masked, so the running max, sum and output stay as
+    // they are (the wave still takes part in staging and the barriers)
+    if (a.causal && k0 > wq_last + causal_shift) continue;
 
     // -- S^T = K Q^T for the two 32-key halves of the tile
     floatx16 sc[2];
@@ -291,38 +346,51 @@ __global__ void __launch_bounds__(kBlock) rope_attention_kernel(AttnArgs a) {
       }
       sc[half] = s;
     }
-    // -- mask, then the online softmax in base 2
+    // -- mask (only where the tile reaches past Sk or this wave's causal
+    // diagonal), then the online softmax in base 2 on the raw scores: the
+    // running max m is kept unscaled and each weight is
+    // exp2(s * scale_log2e - m * scale_log2e), one fused multiply-add
+    const bool edge = k0 + kKeys > a.seq_k || (a.causal && k0 + kKeys - 1 > wq_first + causal_shift);
+    if (edge) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + half * 32 + 8 * (j / 4) + 4 * hs + (j % 4);
+          const bool vis = key < a.seq_k && (!a.causal || key <= qi + causal_shift);
+          if (!vis) sc[half][j] = -__builtin_inff();
+        }
+    }
     float m_tile = -__builtin_inff();
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = k0 + half * 32 + 8 * (j / 4) + 4 * hs + (j % 4);
-        const bool vis = key < a.seq_k && (!a.causal || key <= qi + causal_shift);
-        const float x = vis ? sc[half][j] * a.scale_log2e : -__builtin_inff();
-        sc[half][j] = x;
-        m_tile = fmaxf(m_tile, x);
-      }
+      for (int j = 0; j < 16; ++j) m_tile = fmaxf(m_tile, sc[half][j]);
     m_tile = fmaxf(m_tile, wave_xor32(m_tile));
     const float m_new = fmaxf(m_run, m_tile);
-    const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float c = a.scale_log2e;
+    const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    // an all-masked row so far (m_new = -inf) keeps weights 0
+    const float mc = m_new == -__builtin_inff() ? 0.0f : m_new * c;
     float l_tile = 0.0f;
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float x = sc[half][j];
-        const float pj = x == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(x - m_new);
+        const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half][j], c, -mc));
         sc[half][j] = pj;
         l_tile += pj;
       }
     l_tile += wave_xor32(l_tile);
     l_run = l_run * alpha + l_tile;
     m_run = m_new;
+    // rescale the output only when some lane's max moved
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+      for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
+        for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
+    }
 
     // -- O^T += V^T P^T: k-steps of 16 keys; step (half, u) covers keys
     // half*32 + 16u .. +15, lane's slots j = 8u .. 8u+7 of sc[half], which

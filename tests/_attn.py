@@ -16,7 +16,11 @@ arithmetic, element by element, built from oracle results only:
      moves by at most eps_i, every weight moves by a factor within
      exp(+-2 eps_i), so the output moves by at most (exp(2 eps_i) - 1) * A.
   3. float32 running sums over Sk keys (weights, output accumulators and the
-     rescales between key tiles): 2 (Sk + 128) 2^-24 * A.
+     rescales between key tiles): 2 (Sk + 128) 2^-24 * A; and the rescale
+     factor exp2((m_old - m_new) * scale log2 e) applied at up to one key tile
+     in each of the ceil(Sk / 64), each off by its argument's rounding and
+     exp2's error, which adds ceil(Sk / 64) * ln2 * (2^-23 |x|max + 2^-22) to
+     eps_i.
   4. The final rounding of O to bf16: u * |O|.
 """
 from __future__ import annotations
@@ -137,7 +141,10 @@ def reference(q, k, v, cos: Optional[np.ndarray], sin: Optional[np.ndarray], *,
             s = np.abs(Q @ K.T) * sc * log2e
             e = sc * e + np.log(2.0) * (2.0 ** -22 * s + 2.0 ** -21)
             e = np.where(visible, e, 0.0)
-            eps[b, h] = e.max(axis=1) if Sk else 0.0
+            if Sk:
+                xmax = np.where(visible, s, 0.0).max(axis=1)
+                rescale = -(-Sk // 64) * np.log(2.0) * (2.0 ** -23 * xmax + 2.0 ** -22)
+                eps[b, h] = e.max(axis=1) + rescale
     grow = np.exp(2.0 * eps)[..., None]
     pre = a_abs * grow * (U16 + 2.0 * (Sk + 128) * 2.0 ** -24) + (grow - 1.0) * a_abs
     tol = pre + U16 * (np.abs(ref) + pre)

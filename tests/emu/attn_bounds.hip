@@ -67,10 +67,21 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
     if (a.k_pos) ck.check((int64_t)b * a.k_pos_bs + j, 1, kpos_elems, "k_pos");
     return key_pos(a, b, j);
   };
+  // the workgroup -> work map is a bijection onto (batch, head, query tile)
+  std::vector<char> seen((size_t)pl.grid, 0);
   for (int64_t blk = 0; blk < pl.grid; ++blk) {
-    const int q_tile = (int)(blk % a.q_tiles);
-    const int h = (int)((blk / a.q_tiles) % a.n_heads_q);
-    const int b = (int)(blk / ((int64_t)a.q_tiles * a.n_heads_q));
+    const Work wk = work_of(a, blk);
+    const bool inside = wk.b >= 0 && wk.b < a.batch && wk.h >= 0 && wk.h < a.n_heads_q &&
+                        wk.q_tile >= 0 && wk.q_tile < a.q_tiles;
+    ck.check(inside ? 0 : -1, 1, 1, "work item outside the problem");
+    if (inside) {
+      const int64_t id = ((int64_t)wk.b * a.n_heads_q + wk.h) * a.q_tiles + wk.q_tile;
+      ck.check(seen[id]++ ? -1 : 0, 1, 1, "work item given twice");
+    }
+  }
+  for (int64_t blk = 0; blk < pl.grid; ++blk) {
+    const Work wk = work_of(a, blk);
+    const int q_tile = wk.q_tile, h = wk.h, b = wk.b;
     const int hk = h / (a.n_heads_q / a.n_heads_k);
     const int n_tiles = key_tiles(a, q_tile);
     const int64_t kbase = row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
@@ -131,14 +142,18 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
             ck.wrote(k_lds<D>(kk, d), 8);
           }
         }
-        for (int it = t; it < kKeys * (D / 8); it += kBlock) {
-          const int kk = it % kKeys, c = it / kKeys;
-          const int key = k0 + kk;
-          if (key < a.seq_k) ck.check(kbase + (int64_t)key * D + c * 8, 8, kv_elems, "v load");
+        for (int it = t; it < v_items<D>(); it += kBlock) {
+          const VItem vi = v_item(it);
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + 4 * vi.k4 + r;
+            if (key < a.seq_k)
+              ck.check(kbase + (int64_t)key * D + vi.c * 8, 8, kv_elems, "v load");
+          }
           for (int i = 0; i < 8; ++i) {
-            const int off = v_lds<D>(c * 8 + i, kk);
-            ck.check(off, 1, lds_elems, "v lds");
-            ck.wrote(off, 1);
+            const int off = v_lds<D>(vi.c * 8 + i, 4 * vi.k4);
+            ck.check(off, 4, lds_elems, "v lds");
+            ck.check(off % 4 == 0 ? 0 : -1, 1, 1, "v lds write not 8-byte aligned");
+            ck.wrote(off, 4);
             if (off < k_lds_elems<D>()) ck.check(0, 1, 0, "v lds inside the k tile");
           }
         }
