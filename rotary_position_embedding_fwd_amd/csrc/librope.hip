@@ -105,9 +105,16 @@ namespace {
 
 template <int D, int PAIR, int H16>
 hipError_t launch_attention(const rope::attn::AttnPlan& pl, hipStream_t st) {
-  hipLaunchKernelGGL((rope::attn::rope_attention_kernel<D, PAIR, H16>),
-                     dim3((unsigned)pl.grid), dim3(rope::attn::kBlock), (unsigned)pl.lds, st,
-                     pl.a);
+  auto kernel = rope::attn::rope_attention_kernel<D, PAIR, H16>;
+  // the double-buffered tiles take more than the default 64 KiB of dynamic
+  // LDS at head dim 128: raise the kernel's limit once (per process; the
+  // attribute belongs to the kernel, not to a device)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+      rope::attn::lds_bytes<D>());
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)pl.grid), dim3(rope::attn::kBlock), (unsigned)pl.lds,
+                     st, pl.a);
   return hipGetLastError();
 }
 

@@ -10,8 +10,9 @@
 // the rotated values are rounded to bf16 as the stand-alone pass would store
 // them, so the fused result equals rope_fwd_qk followed by attention.
 //
-// Shape of the computation (one workgroup = 4 waves = 128 query rows of one
-// (batch, head); each lane owns one query row, two lanes per row):
+// Shape of the computation (one workgroup = 8 waves = 256 query rows: 32
+// rows per wave, from hw query heads that share one K/V head, 256 / hw rows
+// of each; each lane owns one query row, two lanes per row):
 //   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16. Each lane's accumulators hold
 //                 its query's scores against 32 of a 64-key tile, so the
 //                 softmax statistics are per lane plus one exchange with the
@@ -20,9 +21,12 @@
 //                 P^T operand directly, under a fixed permutation of the keys
 //                 inside each 16-key step that V^T's reads follow.
 // Q is loaded and rotated once into the registers of the B operand of S^T.
-// Each 64-key tile of K is rotated while it is staged into LDS ([key][dim],
-// rows padded by 16 bytes); V is staged transposed ([dim][key], padded) so
-// that the A operand of O^T is two 8-byte LDS reads per lane and step.
+// Each 64-key tile of K is rotated once per workgroup, for all its 256 rows,
+// while it is staged into LDS ([key][dim], rows padded by 16 bytes); V is
+// staged transposed ([dim][key], padded) so that the A operand of O^T is two
+// 8-byte LDS reads per lane and step. Tiles are double-buffered: the next
+// tile is fetched before the current one's products and staged into the
+// other buffer after them, with one barrier per tile.
 // The softmax runs in base 2 with the scale folded into log2(e).
 //
 // Operand layouts of v_mfma_f32_32x32x16_bf16 (checked on the device by a
@@ -39,9 +43,9 @@
 namespace rope {
 namespace attn {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kBlock = 64 * kWaves;         // lanes per workgroup
-constexpr int kQueries = 32 * kWaves;       // query rows per workgroup
+constexpr int kRows = 32 * kWaves;          // query rows per workgroup
 constexpr int kKeys = 64;                   // keys per tile
 constexpr int kKPad = 8;                    // K tile row padding (bf16)
 constexpr int kVPad = 8;                    // V^T tile row padding (bf16)
@@ -62,7 +66,10 @@ struct AttnArgs {
   int32_t half;          // R / 2
   int32_t rotate;        // 0: no rotation (plain attention, for the unfused path)
   int32_t causal;
-  int32_t q_tiles;       // ceil(Sq / kQueries)
+  int32_t hw;            // query heads per workgroup (a power of 2 dividing Hq / Hk)
+  int32_t rows;          // query rows of each head per workgroup: kRows / hw
+  int32_t head_groups;   // Hq / hw
+  int32_t q_tiles;       // ceil(Sq / rows)
   float scale_log2e;     // softmax scale * log2(e)
 };
 
@@ -86,35 +93,48 @@ template <int D, int PAIR> struct KItems {
   }
 };
 
-// LDS layout, in bf16 elements: K tile [kKeys][D + kKPad], then V^T tile
-// [D][kKeys + kVPad].
+// LDS layout, in bf16 elements: two buffers, each a K tile
+// [kKeys][D + kKPad] followed by a V^T tile [D][kKeys + kVPad].
 template <int D> constexpr int k_lds_elems() { return kKeys * (D + kKPad); }
 template <int D> constexpr int v_lds_elems() { return D * (kKeys + kVPad); }
-template <int D> constexpr int lds_bytes() { return 2 * (k_lds_elems<D>() + v_lds_elems<D>()); }
-template <int D> ROPE_HD int k_lds(int key, int dim) { return key * (D + kKPad) + dim; }
-template <int D> ROPE_HD int v_lds(int dim, int key) {
-  return k_lds_elems<D>() + dim * (kKeys + kVPad) + key;
+template <int D> constexpr int buf_elems() { return k_lds_elems<D>() + v_lds_elems<D>(); }
+template <int D> constexpr int lds_bytes() { return 2 * 2 * buf_elems<D>(); }
+template <int D> ROPE_HD int k_lds(int buf, int key, int dim) {
+  return buf * buf_elems<D>() + key * (D + kKPad) + dim;
+}
+template <int D> ROPE_HD int v_lds(int buf, int dim, int key) {
+  return buf * buf_elems<D>() + k_lds_elems<D>() + dim * (kKeys + kVPad) + key;
 }
 
-// Workgroup -> (batch, query head, query tile). Workgroups are handed to the
-// dies round-robin (workgroup w to die w % 8), so the work list is cut into
-// 8 contiguous ranges and die x walks range x: the query tiles of one head,
-// and the heads of one K/V group, run on one die and share its L2. Within a
-// head the tiles go from the last (most keys when causal) to the first, so
-// the short ones fill the tail of the launch.
+// Workgroup -> (batch, head group, query tile). Workgroups are handed to
+// the dies round-robin (workgroup w to die w % 8), so the work list is cut
+// into 8 contiguous ranges and die x walks range x: the query tiles of one
+// head group, and the groups of one K/V head, run on one die and share its
+// L2. Within a group the tiles go from the last (most keys when causal) to
+// the first, so the short ones fill the tail of the launch.
 struct Work {
-  int b, h, q_tile;
+  int b, hg, q_tile;
 };
 ROPE_HD Work work_of(const AttnArgs& a, int64_t blk) {
-  const int64_t n = (int64_t)a.q_tiles * a.n_heads_q * a.batch;
+  const int64_t n = (int64_t)a.q_tiles * a.head_groups * a.batch;
   const int64_t full = n / kXcds, rem = n % kXcds;
   const int64_t x = blk % kXcds, local = blk / kXcds;
   const int64_t w = x * full + (x < rem ? x : rem) + local;
   Work r;
   r.q_tile = a.q_tiles - 1 - (int)(w % a.q_tiles);
-  r.h = (int)((w / a.q_tiles) % a.n_heads_q);
-  r.b = (int)(w / ((int64_t)a.q_tiles * a.n_heads_q));
+  r.hg = (int)((w / a.q_tiles) % a.head_groups);
+  r.b = (int)(w / ((int64_t)a.q_tiles * a.head_groups));
   return r;
+}
+
+// Wave w of a workgroup: query head hg * hw + w / (kWaves / hw), rows
+// q_tile * rows + (w % (kWaves / hw)) * 32 .. + 31.
+struct WaveRole {
+  int h, row0;
+};
+ROPE_HD WaveRole wave_role(const AttnArgs& a, const Work& wk, int wave) {
+  const int per_head = kWaves / a.hw;
+  return WaveRole{wk.hg * a.hw + wave / per_head, wk.q_tile * a.rows + (wave % per_head) * 32};
 }
 
 // V tile staging: item it holds 4 consecutive keys (4 k4 .. 4 k4 + 3) of 8
@@ -142,7 +162,7 @@ ROPE_HD int64_t key_pos(const AttnArgs& a, int b, int j) {
 ROPE_HD int key_tiles(const AttnArgs& a, int q_tile) {
   int last_key = a.seq_k - 1;
   if (a.causal) {
-    const int q_last = imin(a.seq_q - 1, q_tile * kQueries + kQueries - 1);
+    const int q_last = imin(a.seq_q - 1, q_tile * a.rows + a.rows - 1);
     last_key = imin(last_key, q_last + (a.seq_k - a.seq_q));
   }
   return last_key < 0 ? 0 : last_key / kKeys + 1;
@@ -153,6 +173,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Rotate two 8-element chunks (x1 = first halves of 8 pairs, x2 = second
 // halves) with NP = 8 frequencies, or one chunk of 4 interleaved pairs.
@@ -201,6 +223,149 @@ __device__ __forceinline__ float wave_xor32(float x) {
 }
 #endif
 
+// ------------------------------------------------------- tile staging
+// K staging items per key, fixed by the instantiation: split-half rotates
+// R/16 = 2 H16 chunk pairs and copies D/8 - 4 H16 chunks; interleaved has
+// one item per 8-dim chunk. (Equal to KItems::per_key of the plan's args.)
+template <int D, int PAIR, int H16> constexpr int k_per_key() {
+  return PAIR == kSplitHalf ? D / 8 - 2 * H16 : D / 8;
+}
+// Most K / V staging items one lane handles per tile.
+template <int D, int PAIR, int H16> constexpr int k_items_max() {
+  return (kKeys * k_per_key<D, PAIR, H16>() + kBlock - 1) / kBlock;
+}
+template <int D> constexpr int v_items_max() { return (v_items<D>() + kBlock - 1) / kBlock; }
+
+// Raw rows of one tile held in registers between fetch and staging. Item n
+// of a lane is item t + n * kBlock of the tile (the same items, in the same
+// order, as a loop over it = t, t + kBlock, ...).
+template <int D, int PAIR, int H16> struct KStage {
+  static constexpr int kN = k_items_max<D, PAIR, H16>();
+  bf16x8 x1[kN], x2[kN];
+  int p[kN];  // table row, or -1: not rotated
+};
+template <int D> struct VStage {
+  u32x4 x[v_items_max<D>()][4];  // 4 key rows x 8 dims, as bf16 pairs
+};
+
+#if defined(__HIP_DEVICE_COMPILE__)
+template <int D, int PAIR, int H16>
+__device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* kbase, int k0,
+                                        int t, KStage<D, PAIR, H16>& ks) {
+  constexpr int per_key = k_per_key<D, PAIR, H16>(), npair = 2 * H16;
+  const int R = 2 * a.half;
+#pragma unroll
+  for (int n = 0; n < KStage<D, PAIR, H16>::kN; ++n) {
+    const int it = t + n * kBlock;
+    bf16x8 z = {};
+    ks.x1[n] = z;
+    ks.x2[n] = z;
+    ks.p[n] = -1;
+    if (it < kKeys * per_key) {
+      const int kk = it / per_key, item = it - kk * per_key;
+      const int key = k0 + kk;
+      if (key < a.seq_k) {
+        const __bf16* krow = kbase + (int64_t)key * D;
+        if (a.rotate) ks.p[n] = (int)key_pos(a, b, key);
+        if constexpr (PAIR == kSplitHalf) {
+          if (item < npair) {
+            ks.x1[n] = *reinterpret_cast<const bf16x8*>(krow + item * 8);
+            ks.x2[n] = *reinterpret_cast<const bf16x8*>(krow + a.half + item * 8);
+          } else {
+            ks.x1[n] = *reinterpret_cast<const bf16x8*>(krow + R + (item - npair) * 8);
+          }
+        } else {
+          ks.x1[n] = *reinterpret_cast<const bf16x8*>(krow + item * 8);
+        }
+      }
+    }
+  }
+}
+
+// Rotate the fetched K items (split-half: items [0, R/16) of a key rotate
+// the chunk pair (c, c + R/16); interleaved: items [0, R/8) rotate chunk c
+// in place; the rest are copied) and write them to the K tile.
+template <int D, int PAIR, int H16>
+__device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR, H16>& ks,
+                                        __bf16* lds, int buf) {
+  constexpr int per_key = k_per_key<D, PAIR, H16>(), npair = 2 * H16;
+  const int R = 2 * a.half, rchunks = R / 8;
+#pragma unroll
+  for (int n = 0; n < KStage<D, PAIR, H16>::kN; ++n) {
+    const int it = t + n * kBlock;
+    if (it < kKeys * per_key) {
+      const int kk = it / per_key, item = it - kk * per_key;
+      if constexpr (PAIR == kSplitHalf) {
+        if (item < npair) {
+          const int d1 = item * 8, d2 = a.half + item * 8;
+          if (ks.p[n] >= 0) {
+            float c[8], sn[8];
+            load_cs(a, ks.p[n], d1, 8, c, sn);
+            rotate_split8(ks.x1[n], ks.x2[n], c, sn);
+          }
+          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, d1)]) = ks.x1[n];
+          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, d2)]) = ks.x2[n];
+        } else {
+          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, R + (item - npair) * 8)]) = ks.x1[n];
+        }
+      } else {
+        const int d = item * 8;
+        if (item < rchunks && ks.p[n] >= 0) {
+          float c[4], sn[4];
+          load_cs(a, ks.p[n], d / 2, 4, c, sn);
+          rotate_inter8(ks.x1[n], c, sn);
+        }
+        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, d)]) = ks.x1[n];
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void fetch_v(const AttnArgs& a, const __bf16* vbase, int k0, int t,
+                                        VStage<D>& vs) {
+#pragma unroll
+  for (int n = 0; n < v_items_max<D>(); ++n) {
+    const int it = t + n * kBlock;
+    if (it < v_items<D>()) {
+      const VItem vi = v_item(it);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 4 * vi.k4 + r;
+        u32x4 z = {};
+        vs.x[n][r] = key < a.seq_k
+                         ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * D + vi.c * 8)
+                         : z;
+      }
+    }
+  }
+}
+
+// V tile, transposed: 4 keys x 8 dims per item, 8-byte LDS writes. Word w
+// of a row holds dims 2w (low half) and 2w + 1 (high half); a byte permute
+// pairs the same half of two rows.
+template <int D>
+__device__ __forceinline__ void stage_v(int t, const VStage<D>& vs, __bf16* lds, int buf) {
+  constexpr uint32_t kLow = 0x05040100u, kHigh = 0x07060302u;
+#pragma unroll
+  for (int n = 0; n < v_items_max<D>(); ++n) {
+    const int it = t + n * kBlock;
+    if (it < v_items<D>()) {
+      const VItem vi = v_item(it);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const u32x2 even = {__builtin_amdgcn_perm(vs.x[n][1][w], vs.x[n][0][w], kLow),
+                            __builtin_amdgcn_perm(vs.x[n][3][w], vs.x[n][2][w], kLow)};
+        const u32x2 odd = {__builtin_amdgcn_perm(vs.x[n][1][w], vs.x[n][0][w], kHigh),
+                           __builtin_amdgcn_perm(vs.x[n][3][w], vs.x[n][2][w], kHigh)};
+        *reinterpret_cast<u32x2*>(&lds[v_lds<D>(buf, vi.c * 8 + 2 * w, 4 * vi.k4)]) = even;
+        *reinterpret_cast<u32x2*>(&lds[v_lds<D>(buf, vi.c * 8 + 2 * w + 1, 4 * vi.k4)]) = odd;
+      }
+    }
+  }
+}
+#endif
+
 // ---------------------------------------------------------------- kernel
 // H16: split-half pairs, (R/2)/16 (the register distance between the two
 // chunks of a pair; a compile-time constant so the registers stay registers);
@@ -210,12 +375,14 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __bf16 lds[];
   const Work wk = work_of(a, blockIdx.x);
-  const int q_tile = wk.q_tile, h = wk.h, b = wk.b;
-  const int hk = h / (a.n_heads_q / a.n_heads_k);
+  const int q_tile = wk.q_tile, b = wk.b;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
+  const WaveRole role = wave_role(a, wk, wave);
+  const int h = role.h;
+  const int hk = h / (a.n_heads_q / a.n_heads_k);  // the same for every wave
   const int hs = lane >> 5;  // which half of the wave: k slots 0-7 or 8-15
-  const int qi = q_tile * kQueries + wave * 32 + (lane & 31);  // this lane's query row
+  const int qi = role.row0 + (lane & 31);  // this lane's query row
   constexpr int kSteps = D / 16;  // k-steps of S^T over the head dim
   const int R = 2 * a.half;
 
@@ -260,158 +427,145 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   for (int i = 0; i < D / 32; ++i) acc[i] = (floatx16){};
 
   const int n_tiles = key_tiles(a, q_tile);
-  const int per_key = KItems<D, PAIR>::per_key(a);
-  const int rchunks = R / 8;
   const __bf16* kbase = a.k + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
   const __bf16* vbase = a.v + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
   const int causal_shift = a.seq_k - a.seq_q;
   // this wave's query rows, for the masking decisions (uniform per wave)
-  const int wq_first = q_tile * kQueries + wave * 32;
+  const int wq_first = role.row0;
   const int wq_last = imin(wq_first + 31, a.seq_q - 1);
 
+  // Tile kt sits in LDS buffer kt & 1 while its products run. The raw K and
+  // V rows (and key positions) of tile kt + 1 are fetched into registers
+  // before them, so their memory latency passes under the matrix work, and
+  // are staged into the other buffer after them: that buffer's last readers
+  // (tile kt - 1) all passed the previous barrier, and its next readers wait
+  // for this iteration's barrier. The fetched registers never cross an
+  // iteration.
+  if (n_tiles > 0) {
+    KStage<D, PAIR, H16> ks;
+    VStage<D> vs;
+    fetch_k<D, PAIR, H16>(a, b, kbase, 0, t, ks);
+    fetch_v<D>(a, vbase, 0, t, vs);
+    stage_k<D, PAIR, H16>(a, t, ks, lds, 0);
+    stage_v<D>(t, vs, lds, 0);
+  }
+  __syncthreads();
+  // a wave whose rows all lie past Sq computes nothing (it still stages)
+  const bool live = wq_first < a.seq_q;
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int k0 = kt * kKeys;
-    __syncthreads();  // the previous tile's reads are done
-    // -- K tile: rotate while staging
-    for (int it = t; it < kKeys * per_key; it += kBlock) {
-      const int kk = it / per_key, item = it - kk * per_key;
-      const int key = k0 + kk;
-      const bool ok = key < a.seq_k;
-      const __bf16* krow = kbase + (int64_t)(ok ? key : 0) * D;
-      const int64_t p = (ok && a.rotate) ? key_pos(a, b, key) : -1;
-      bf16x8 z = {};
-      if constexpr (PAIR == kSplitHalf) {
-        const int npair = rchunks / 2;
-        if (item < npair) {
-          const int d1 = item * 8, d2 = a.half + item * 8;
-          bf16x8 x1 = ok ? *reinterpret_cast<const bf16x8*>(krow + d1) : z;
-          bf16x8 x2 = ok ? *reinterpret_cast<const bf16x8*>(krow + d2) : z;
-          if (p >= 0) {
-            float c[8], sn[8];
-            load_cs(a, p, d1, 8, c, sn);
-            rotate_split8(x1, x2, c, sn);
-          }
-          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d1)]) = x1;
-          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d2)]) = x2;
-        } else {
-          const int d = R + (item - npair) * 8;
-          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d)]) =
-              ok ? *reinterpret_cast<const bf16x8*>(krow + d) : z;
-        }
-      } else {
-        const int d = item * 8;
-        bf16x8 x = ok ? *reinterpret_cast<const bf16x8*>(krow + d) : z;
-        if (item < rchunks && p >= 0) {
-          float c[4], sn[4];
-          load_cs(a, p, d / 2, 4, c, sn);
-          rotate_inter8(x, c, sn);
-        }
-        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(kk, d)]) = x;
-      }
+    const int buf = kt & 1;
+    const bool more = kt + 1 < n_tiles;
+    KStage<D, PAIR, H16> ks;
+    VStage<D> vs;
+    if (more) {
+      fetch_k<D, PAIR, H16>(a, b, kbase, k0 + kKeys, t, ks);
+      fetch_v<D>(a, vbase, k0 + kKeys, t, vs);
     }
-    // -- V tile, transposed: 4 keys x 8 dims per item, 8-byte LDS writes
-    for (int it = t; it < v_items<D>(); it += kBlock) {
-      const VItem vi = v_item(it);
-      bf16x8 x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * vi.k4 + r;
-        bf16x8 z = {};
-        x[r] = key < a.seq_k
-                   ? *reinterpret_cast<const bf16x8*>(vbase + (int64_t)key * D + vi.c * 8)
-                   : z;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x4 col = {x[0][i], x[1][i], x[2][i], x[3][i]};
-        *reinterpret_cast<bf16x4*>(&lds[v_lds<D>(vi.c * 8 + i, 4 * vi.k4)]) = col;
-      }
-    }
-    __syncthreads();
     // a tile wholly after this wave's causal diagonal adds nothing: its
     // scores are all masked, so the running max, sum and output stay as
-    // they are (the wave still takes part in staging and the barriers)
-    if (a.causal && k0 > wq_last + causal_shift) continue;
-
-    // -- S^T = K Q^T for the two 32-key halves of the tile
-    floatx16 sc[2];
+    // they are (the wave still stages the next tile and meets the barriers)
+    if (live && (!a.causal || k0 <= wq_last + causal_shift)) {
+      // -- S^T = K Q^T for the two 32-key halves of the tile; each half's
+      // K fragments are read from LDS before its chain of products
+      floatx16 sc[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      floatx16 s = {};
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 kf[kSteps];
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&lds[k_lds<D>(half * 32 + (lane & 31), st * 16 + hs * 8)]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[st], s, 0, 0, 0);
+        for (int st = 0; st < kSteps; ++st)
+          kf[st] = *reinterpret_cast<const bf16x8*>(
+              &lds[k_lds<D>(buf, half * 32 + (lane & 31), st * 16 + hs * 8)]);
+        floatx16 sh = {};
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st)
+          sh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qreg[st], sh, 0, 0, 0);
+        sc[half] = sh;
+        // keep the reads ahead of the products: all kSteps LDS reads, then
+        // the chain of kSteps matrix instructions
+        __builtin_amdgcn_sched_group_barrier(0x100, kSteps, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kSteps, 0);
       }
-      sc[half] = s;
-    }
-    // -- mask (only where the tile reaches past Sk or this wave's causal
-    // diagonal), then the online softmax in base 2 on the raw scores: the
-    // running max m is kept unscaled and each weight is
-    // exp2(s * scale_log2e - m * scale_log2e), one fused multiply-add
-    const bool edge = k0 + kKeys > a.seq_k || (a.causal && k0 + kKeys - 1 > wq_first + causal_shift);
-    if (edge) {
+      // -- mask (only where the tile reaches past Sk or this wave's causal
+      // diagonal), then the online softmax in base 2 on the raw scores: the
+      // running max m is kept unscaled and each weight is
+      // exp2(s * scale_log2e - m * scale_log2e), one fused multiply-add
+      const bool edge = k0 + kKeys > a.seq_k || (a.causal && k0 + kKeys - 1 > wq_first + causal_shift);
+      if (edge) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + half * 32 + 8 * (j / 4) + 4 * hs + (j % 4);
+            const bool vis = key < a.seq_k && (!a.causal || key <= qi + causal_shift);
+            if (!vis) sc[half][j] = -__builtin_inff();
+          }
+      }
+      float m_tile = -__builtin_inff();
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) m_tile = fmaxf(m_tile, sc[half][j]);
+      m_tile = fmaxf(m_tile, wave_xor32(m_tile));
+      const float m_new = fmaxf(m_run, m_tile);
+      const float c = a.scale_log2e;
+      const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      // an all-masked row so far (m_new = -inf) keeps weights 0
+      const float mc = m_new == -__builtin_inff() ? 0.0f : m_new * c;
+      float l_tile = 0.0f;
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = k0 + half * 32 + 8 * (j / 4) + 4 * hs + (j % 4);
-          const bool vis = key < a.seq_k && (!a.causal || key <= qi + causal_shift);
-          if (!vis) sc[half][j] = -__builtin_inff();
+          const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half][j], c, -mc));
+          sc[half][j] = pj;
+          l_tile += pj;
         }
-    }
-    float m_tile = -__builtin_inff();
+      l_tile += wave_xor32(l_tile);
+      l_run = l_run * alpha + l_tile;
+      m_run = m_new;
+      // rescale the output only when some lane's max moved
+      if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
+        for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) m_tile = fmaxf(m_tile, sc[half][j]);
-    m_tile = fmaxf(m_tile, wave_xor32(m_tile));
-    const float m_new = fmaxf(m_run, m_tile);
-    const float c = a.scale_log2e;
-    const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    // an all-masked row so far (m_new = -inf) keeps weights 0
-    const float mc = m_new == -__builtin_inff() ? 0.0f : m_new * c;
-    float l_tile = 0.0f;
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half][j], c, -mc));
-        sc[half][j] = pj;
-        l_tile += pj;
+          for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
       }
-    l_tile += wave_xor32(l_tile);
-    l_run = l_run * alpha + l_tile;
-    m_run = m_new;
-    // rescale the output only when some lane's max moved
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
-    }
 
-    // -- O^T += V^T P^T: k-steps of 16 keys; step (half, u) covers keys
-    // half*32 + 16u .. +15, lane's slots j = 8u .. 8u+7 of sc[half], which
-    // hold keys 16u + 8*(i/4) + 4*hs + i%4 for slot i
+      // -- O^T += V^T P^T: k-steps of 16 keys; step (half, u) covers keys
+      // half*32 + 16u .. +15, lane's slots j = 8u .. 8u+7 of sc[half], which
+      // hold keys 16u + 8*(i/4) + 4*hs + i%4 for slot i. Each step's V^T
+      // fragments are read before its products.
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 pb;
+        for (int u = 0; u < 2; ++u) {
+          bf16x8 pb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = from_f32<__bf16>(sc[half][8 * u + i]);
-        const int kb = half * 32 + 16 * u + 4 * hs;  // keys kb..kb+3 and kb+8..kb+11
+          for (int i = 0; i < 8; ++i) pb[i] = from_f32<__bf16>(sc[half][8 * u + i]);
+          const int kb = half * 32 + 16 * u + 4 * hs;  // keys kb..kb+3 and kb+8..kb+11
+          u32x4 va[D / 32];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int dim = dt * 32 + (lane & 31);
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&lds[v_lds<D>(dim, kb)]);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&lds[v_lds<D>(dim, kb + 8)]);
-          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[dt], 0, 0, 0);
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const int dim = dt * 32 + (lane & 31);
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(&lds[v_lds<D>(buf, dim, kb)]);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(&lds[v_lds<D>(buf, dim, kb + 8)]);
+            va[dt] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+          }
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, va[dt]), pb, acc[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
         }
-      }
+
+    }
+    if (more) {
+      stage_k<D, PAIR, H16>(a, t, ks, lds, buf ^ 1);
+      stage_v<D>(t, vs, lds, buf ^ 1);
+    }
+    __syncthreads();
   }
 
   // ---- O = acc / l: lane holds dims dt*32 + 8*(j/4) + 4*hs + j%4 of its row

@@ -89,10 +89,19 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   a.half = rotate ? (int32_t)(R / 2) : 0;
   a.rotate = rotate ? 1 : 0;
   a.causal = d->causal ? 1 : 0;
-  a.q_tiles = (int32_t)((Sq + kQueries - 1) / kQueries);
+  // query heads per workgroup: the largest power of two (at most the 8
+  // waves) dividing the group of query heads that share a K/V head, so one
+  // staged K/V tile serves all 256 rows of the workgroup
+  const int64_t group = Hq / Hk;
+  int32_t hw = 1;
+  while (hw < kWaves && group % (2 * hw) == 0) hw *= 2;
+  a.hw = hw;
+  a.rows = kRows / hw;
+  a.head_groups = (int32_t)(Hq / hw);
+  a.q_tiles = (int32_t)((Sq + a.rows - 1) / a.rows);
   const double scale = d->scale != 0.0 ? d->scale : 1.0 / std::sqrt((double)D);
   a.scale_log2e = (float)(scale * 1.4426950408889634);  // log2(e)
-  pl->grid = (int64_t)a.q_tiles * Hq * B;
+  pl->grid = (int64_t)a.q_tiles * a.head_groups * B;
   if (pl->grid > 0x7fffffff) return ROPE_ERR_SHAPE;
   pl->head_dim = (int)D;
   pl->pairing = d->pairing;

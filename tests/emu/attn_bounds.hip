@@ -4,12 +4,18 @@
 // The kernel (rope_attention.hpp) runs on matrix cores and cannot execute on
 // the host, so this walks its loops instead: every workgroup, lane and key
 // tile of the planned grid, forming each address with the kernel's own index
-// functions (row_of, k_lds, v_lds, query_pos, key_pos, key_tiles, KItems) and
-// counting any that falls outside the exact extent of its buffer.
+// functions (work_of, wave_role, row_of, k_lds, v_lds, query_pos, key_pos,
+// key_tiles, KItems) and counting any that falls outside the exact extent of
+// its buffer. The tile pipeline is simulated phase by phase (stage tile 0;
+// then per tile, the reads of its buffer and the staging of the next tile
+// into the other one): each staging write must land in its tile's buffer,
+// no LDS cell may be written by two lanes in one phase, and every cell read
+// for tile kt must hold tile kt.
 //
 // usage: attn_bounds B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos
 //   (qpos / kpos: 0 = no index, 1 = an index of Sq / Sk entries per batch)
 // prints "plan <status>" then "violations <n>" and "accesses <n>".
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -24,20 +30,6 @@ namespace {
 
 struct Checker {
   long long violations = 0, accesses = 0;
-  // LDS cells written / read by the first key tile of the first workgroup
-  // (the staging pattern is the same for every tile and workgroup)
-  std::vector<int> written, read;
-  bool track = false;
-  void wrote(int first, int count) {
-    if (track)
-      for (int i = first; i < first + count; ++i)
-        if (i >= 0 && i < (int)written.size()) ++written[i];
-  }
-  void reads(int first, int count) {
-    if (track)
-      for (int i = first; i < first + count; ++i)
-        if (i >= 0 && i < (int)read.size()) ++read[i];
-  }
   void check(long long first, long long count, long long extent, const char* what) {
     ++accesses;
     if (first < 0 || first + count > extent) {
@@ -46,6 +38,14 @@ struct Checker {
       ++violations;
     }
   }
+  void fail(bool bad, const char* what) { check(bad ? -1 : 0, 1, 1, what); }
+};
+
+// LDS cell ownership of one workgroup: the tile whose staging last wrote
+// each cell, and the lane that wrote it in the current staging phase.
+struct LdsModel {
+  std::vector<int> tile, writer;
+  explicit LdsModel(int n) : tile(n, -1), writer(n, -1) {}
 };
 
 template <int D, int PAIR>
@@ -55,10 +55,10 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
   const int lds_elems = lds_bytes<D>() / 2;
   const int R = 2 * a.half;
   const int per_key = KItems<D, PAIR>::per_key(a);
+  // the kernel instantiation's compile-time count must equal the plan's
+  const int h16 = pl.h16;
+  ck.fail(per_key != (PAIR == kSplitHalf ? D / 8 - 2 * h16 : D / 8), "items per key");
   const int rchunks = R / 8;
-  ck.written.assign(lds_elems, 0);
-  ck.read.assign(lds_elems, 0);
-  // positions through the kernel's own functions, with the index reads checked
   auto qpos = [&](int b, int i) {
     if (a.q_pos) ck.check((int64_t)b * a.q_pos_bs + i, 1, qpos_elems, "q_pos");
     return query_pos(a, b, i);
@@ -67,47 +67,87 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
     if (a.k_pos) ck.check((int64_t)b * a.k_pos_bs + j, 1, kpos_elems, "k_pos");
     return key_pos(a, b, j);
   };
-  // the workgroup -> work map is a bijection onto (batch, head, query tile)
+  // the workgroup -> work map is a bijection onto (batch, head group, query tile)
   std::vector<char> seen((size_t)pl.grid, 0);
   for (int64_t blk = 0; blk < pl.grid; ++blk) {
     const Work wk = work_of(a, blk);
-    const bool inside = wk.b >= 0 && wk.b < a.batch && wk.h >= 0 && wk.h < a.n_heads_q &&
+    const bool inside = wk.b >= 0 && wk.b < a.batch && wk.hg >= 0 && wk.hg < a.head_groups &&
                         wk.q_tile >= 0 && wk.q_tile < a.q_tiles;
-    ck.check(inside ? 0 : -1, 1, 1, "work item outside the problem");
+    ck.fail(!inside, "work item outside the problem");
     if (inside) {
-      const int64_t id = ((int64_t)wk.b * a.n_heads_q + wk.h) * a.q_tiles + wk.q_tile;
-      ck.check(seen[id]++ ? -1 : 0, 1, 1, "work item given twice");
+      const int64_t id = ((int64_t)wk.b * a.head_groups + wk.hg) * a.q_tiles + wk.q_tile;
+      ck.fail(seen[id]++ != 0, "work item given twice");
     }
   }
+  // every (batch, head, row) is some wave's row exactly once
+  ck.fail((int64_t)a.head_groups * a.hw != a.n_heads_q, "head groups cover the heads");
+  ck.fail(a.rows * a.hw != kRows || (int64_t)a.q_tiles * a.rows < a.seq_q, "rows cover Sq");
+  ck.fail((a.n_heads_q / a.n_heads_k) % a.hw != 0, "a workgroup spans two K/V heads");
+  // every (batch, query head, row < Sq) belongs to exactly one lane's query
+  std::vector<char> owned((size_t)a.batch * a.n_heads_q * a.seq_q, 0);
   for (int64_t blk = 0; blk < pl.grid; ++blk) {
     const Work wk = work_of(a, blk);
-    const int q_tile = wk.q_tile, h = wk.h, b = wk.b;
-    const int hk = h / (a.n_heads_q / a.n_heads_k);
-    const int n_tiles = key_tiles(a, q_tile);
-    const int64_t kbase = row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
+    for (int wave = 0; wave < kWaves; ++wave) {
+      const WaveRole role = wave_role(a, wk, wave);
+      for (int r = 0; r < 32; ++r) {  // lanes r and r + 32 share row row0 + r
+        const int qi = role.row0 + r;
+        if (qi < a.seq_q && role.h >= 0 && role.h < a.n_heads_q)
+          ck.fail(owned[((size_t)wk.b * a.n_heads_q + role.h) * a.seq_q + qi]++ != 0,
+                  "query row owned twice");
+      }
+    }
+  }
+  for (char c : owned) ck.fail(c != 1, "query row owned by no lane");
+  for (int64_t blk = 0; blk < pl.grid; ++blk) {
+    const Work wk = work_of(a, blk);
+    const int b = wk.b;
+    const int n_tiles = key_tiles(a, wk.q_tile);
+    const int hk0 = wave_role(a, wk, 0).h / (a.n_heads_q / a.n_heads_k);
+    const int64_t kbase = row_of<D>(a, b, hk0, a.n_heads_k, a.seq_k, 0);
+    // Q loads and rotation, O stores
     for (int t = 0; t < kBlock; ++t) {
       const int lane = t & 63, wave = t >> 6, hs = lane >> 5;
-      const int qi = q_tile * kQueries + wave * 32 + (lane & 31);
+      const WaveRole role = wave_role(a, wk, wave);
+      ck.fail(role.h < 0 || role.h >= a.n_heads_q, "wave head");
+      ck.fail(role.h / (a.n_heads_q / a.n_heads_k) != hk0, "waves of one workgroup share K/V");
+      const int qi = role.row0 + (lane & 31);
       const bool q_ok = qi < a.seq_q;
-      const int64_t qrow = row_of<D>(a, b, h, a.n_heads_q, a.seq_q, q_ok ? qi : 0);
-      for (int s = 0; s < D / 16; ++s)
-        if (q_ok) ck.check(qrow + s * 16 + hs * 8, 8, q_elems, "q load");
-      const int64_t p = (q_ok && a.rotate) ? qpos(b, qi) : -1;
+      if (!q_ok) continue;
+      const int64_t qrow = row_of<D>(a, b, role.h, a.n_heads_q, a.seq_q, qi);
+      for (int s = 0; s < D / 16; ++s) ck.check(qrow + s * 16 + hs * 8, 8, q_elems, "q load");
+      const int64_t p = a.rotate ? qpos(b, qi) : -1;
       if (p >= 0) {
         if (PAIR == kSplitHalf) {
           for (int s = 0; s < a.half / 16; ++s) {
             ck.check(p * a.half + s * 16 + hs * 8, 8, table_elems, "q cos/sin");
-            if (s + a.half / 16 >= D / 16) ck.check(0, 1, 0, "q pair register");
+            ck.fail(s + a.half / 16 >= D / 16, "q pair register");
           }
         } else {
           for (int s = 0; s < D / 16; ++s)
-            if (s * 16 + hs * 8 < R) ck.check(p * a.half + (s * 16 + hs * 8) / 2, 4, table_elems,
-                                              "q cos/sin");
+            if (s * 16 + hs * 8 < R)
+              ck.check(p * a.half + (s * 16 + hs * 8) / 2, 4, table_elems, "q cos/sin");
         }
       }
-      for (int kt = 0; kt < n_tiles; ++kt) {
-        const int k0 = kt * kKeys;
-        ck.track = blk == 0 && kt == 0;
+      for (int dt = 0; dt < D / 32; ++dt)
+        for (int g = 0; g < 4; ++g) ck.check(qrow + dt * 32 + 8 * g + 4 * hs, 4, q_elems, "o store");
+    }
+    // the tile pipeline: stage tile 0 into buffer 0; then per tile kt,
+    // reads of buffer kt & 1, staging of tile kt + 1 into the other buffer
+    LdsModel m(lds_elems);
+    auto stage = [&](int tile) {
+      const int buf = tile & 1, k0 = tile * kKeys;
+      std::fill(m.writer.begin(), m.writer.end(), -1);
+      auto wrote = [&](int off, int n, int t, const char* what) {
+        ck.check(off, n, lds_elems, what);
+        const int lo = buf * buf_elems<D>(), hi = lo + buf_elems<D>();
+        ck.fail(off < lo || off + n > hi, "staging outside its buffer");
+        for (int i = off; i < off + n && i >= 0 && i < lds_elems; ++i) {
+          ck.fail(m.writer[i] != -1 && m.writer[i] != t, "lds cell written by two lanes");
+          m.writer[i] = t;
+          m.tile[i] = tile;
+        }
+      };
+      for (int t = 0; t < kBlock; ++t) {
         for (int it = t; it < kKeys * per_key; it += kBlock) {
           const int kk = it / per_key, item = it - kk * per_key;
           const int key = k0 + kk;
@@ -123,74 +163,71 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
                 ck.check(krow + d2, 8, kv_elems, "k load");
               }
               if (kp >= 0) ck.check(kp * a.half + d1, 8, table_elems, "k cos/sin");
-              ck.check(k_lds<D>(kk, d1), 8, k_lds_elems<D>(), "k lds");
-              ck.check(k_lds<D>(kk, d2), 8, k_lds_elems<D>(), "k lds");
-              ck.wrote(k_lds<D>(kk, d1), 8);
-              ck.wrote(k_lds<D>(kk, d2), 8);
+              wrote(k_lds<D>(buf, kk, d1), 8, t, "k lds");
+              wrote(k_lds<D>(buf, kk, d2), 8, t, "k lds");
             } else {
               const int d = R + (item - npair) * 8;
               if (ok) ck.check(krow + d, 8, kv_elems, "k load");
-              ck.check(k_lds<D>(kk, d), 8, k_lds_elems<D>(), "k lds");
-              ck.wrote(k_lds<D>(kk, d), 8);
+              wrote(k_lds<D>(buf, kk, d), 8, t, "k lds");
             }
           } else {
             const int d = item * 8;
             if (ok) ck.check(krow + d, 8, kv_elems, "k load");
-            if (item < rchunks && kp >= 0)
-              ck.check(kp * a.half + d / 2, 4, table_elems, "k cos/sin");
-            ck.check(k_lds<D>(kk, d), 8, k_lds_elems<D>(), "k lds");
-            ck.wrote(k_lds<D>(kk, d), 8);
+            if (item < rchunks && kp >= 0) ck.check(kp * a.half + d / 2, 4, table_elems, "k cos/sin");
+            wrote(k_lds<D>(buf, kk, d), 8, t, "k lds");
           }
         }
         for (int it = t; it < v_items<D>(); it += kBlock) {
           const VItem vi = v_item(it);
           for (int r = 0; r < 4; ++r) {
             const int key = k0 + 4 * vi.k4 + r;
-            if (key < a.seq_k)
-              ck.check(kbase + (int64_t)key * D + vi.c * 8, 8, kv_elems, "v load");
+            if (key < a.seq_k) ck.check(kbase + (int64_t)key * D + vi.c * 8, 8, kv_elems, "v load");
           }
           for (int i = 0; i < 8; ++i) {
-            const int off = v_lds<D>(vi.c * 8 + i, 4 * vi.k4);
-            ck.check(off, 4, lds_elems, "v lds");
-            ck.check(off % 4 == 0 ? 0 : -1, 1, 1, "v lds write not 8-byte aligned");
-            ck.wrote(off, 4);
-            if (off < k_lds_elems<D>()) ck.check(0, 1, 0, "v lds inside the k tile");
+            const int off = v_lds<D>(buf, vi.c * 8 + i, 4 * vi.k4);
+            ck.fail(off % 4 != 0, "v lds write not 8-byte aligned");
+            ck.fail(off < buf * buf_elems<D>() + k_lds_elems<D>(), "v lds inside the k tile");
+            wrote(off, 4, t, "v lds");
           }
         }
+      }
+    };
+    auto read = [&](int off, int n, int tile, const char* what) {
+      ck.check(off, n, lds_elems, what);
+      for (int i = off; i < off + n && i >= 0 && i < lds_elems; ++i)
+        ck.fail(m.tile[i] != tile, "lds read of a cell not staged for this tile");
+    };
+    if (n_tiles > 0) stage(0);
+    for (int kt = 0; kt < n_tiles; ++kt) {
+      const int buf = kt & 1, k0 = kt * kKeys;
+      for (int t = 0; t < kBlock; ++t) {
+        const int lane = t & 63, wave = t >> 6, hs = lane >> 5;
+        const WaveRole role = wave_role(a, wk, wave);
+        const int wq_last = imin(role.row0 + 31, a.seq_q - 1);
+        if (role.row0 >= a.seq_q) continue;
+        if (a.causal && k0 > wq_last + (a.seq_k - a.seq_q)) continue;
         for (int half = 0; half < 2; ++half)
           for (int st = 0; st < D / 16; ++st)
-          {
-            const int off = k_lds<D>(half * 32 + (lane & 31), st * 16 + hs * 8);
-            ck.check(off, 8, k_lds_elems<D>(), "k lds read");
-            ck.reads(off, 8);
-          }
+            read(k_lds<D>(buf, half * 32 + (lane & 31), st * 16 + hs * 8), 8, kt, "k lds read");
         for (int half = 0; half < 2; ++half)
           for (int u = 0; u < 2; ++u) {
             const int kb = half * 32 + 16 * u + 4 * hs;
+            ck.fail(kb + 8 + 4 > kKeys, "v key beyond the tile");
             for (int dt = 0; dt < D / 32; ++dt) {
               const int dim = dt * 32 + (lane & 31);
-              ck.check(v_lds<D>(dim, kb), 4, lds_elems, "v lds read");
-              ck.check(v_lds<D>(dim, kb + 8), 4, lds_elems, "v lds read");
-              ck.reads(v_lds<D>(dim, kb), 4);
-              ck.reads(v_lds<D>(dim, kb + 8), 4);
-              if (kb + 8 + 4 > kKeys) ck.check(0, 1, 0, "v key beyond the tile");
+              read(v_lds<D>(buf, dim, kb), 4, kt, "v lds read");
+              read(v_lds<D>(buf, dim, kb + 8), 4, kt, "v lds read");
             }
           }
       }
-      if (q_ok) {
-        const int64_t orow = row_of<D>(a, b, h, a.n_heads_q, a.seq_q, qi);
-        for (int dt = 0; dt < D / 32; ++dt)
-          for (int g = 0; g < 4; ++g) ck.check(orow + dt * 32 + 8 * g + 4 * hs, 4, q_elems, "o store");
-      }
+      if (kt + 1 < n_tiles) stage(kt + 1);
     }
   }
-  // every cell is written at most once per tile, and every cell read was written
-  ck.track = false;
-  for (int i = 0; i < lds_elems; ++i) {
-    ck.check(ck.written[i] > 1 ? -1 : 0, 1, 1, "lds cell written twice");
-    if (ck.read[i] > 0) ck.check(ck.written[i] == 1 ? 0 : -1, 1, 1, "lds cell read, never written");
-  }
 }
+
+}  // namespace
+
+namespace {
 
 // the first entries hold the positions at the edges of the table: the last
 // row, one past it (passes through) and -1 (passes through)

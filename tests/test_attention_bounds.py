@@ -3,8 +3,9 @@
 tests/emu/attn_bounds.hip plans each call exactly as the library does and
 walks every workgroup, lane and key tile of the planned grid through the
 kernel's own index functions: each Q/K/V/O, cos/sin and position access must
-fall inside its buffer, each LDS cell of a tile must be written by one lane
-only, and every LDS cell the matrix-core reads touch must have been written.
+fall inside its buffer. The double-buffered tile pipeline is simulated phase
+by phase: staging writes land in their tile's buffer, no LDS cell is written
+by two lanes in one phase, and every cell read for tile kt holds tile kt.
 The walk runs under AddressSanitizer, so the position reads are real reads
 of index arrays of exact size.
 """
@@ -37,6 +38,9 @@ CASES = [
     (1, 2, 1, 64, 64, 128, 32, SPLIT, 0, 64, 0, 0),         # H16 = 1
     (1, 2, 1, 64, 64, 128, 96, SPLIT, 0, 64, 0, 0),         # H16 = 3
     (1, 2, 1, 64, 64, 64, 64, INTER, 1, 64, 0, 0),
+    (2, 16, 2, 100, 300, 128, 128, SPLIT, 1, 300, 0, 1),    # 8 heads per workgroup
+    (1, 6, 3, 70, 70, 64, 64, SPLIT, 0, 70, 0, 0),          # GQA 2:1
+    (1, 12, 1, 40, 520, 128, 64, INTER, 1, 520, 1, 0),      # MQA 12:1 (4 heads per group)
 ]
 
 
