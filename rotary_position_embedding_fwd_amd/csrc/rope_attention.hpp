@@ -83,18 +83,27 @@ template <int D> ROPE_HD int64_t row_of(const AttnArgs& a, int b, int h, int hea
   return (((int64_t)b * heads + h) * seq + s) * D;
 }
 
-// K tile staging: item it of a 64-key tile. Split-half: items [0, R/16) of a
-// key rotate the chunk pair (c, c + R/16) of 8 dims each; interleaved: items
-// [0, R/8) rotate chunk c in place; the rest copy the unrotated chunks >= R/8.
-template <int D, int PAIR> struct KItems {
-  static ROPE_HD int per_key(const AttnArgs& a) {
-    const int rchunks = 2 * a.half / 8;  // chunks holding rotated dims
-    return (PAIR == kSplitHalf ? rchunks / 2 : rchunks) + (D / 8 - rchunks);
-  }
+// K tile staging items, in three classes; item n of lane t in a class is
+// class item t + n * kBlock, and class item it covers key it / per_key,
+// chunk it % per_key:
+//   - split-half pair items (R/16 = 2 H16 per key): chunk j rotates the
+//     pairs of dims 8j .. 8j + 7 with R/2 + 8j .. R/2 + 8j + 7;
+//   - split-half copy items ((D - R)/8 per key): chunk j copies dims
+//     R + 8j .. R + 8j + 7;
+//   - interleaved items (D/8 per key): chunk j holds dims 8j .. 8j + 7,
+//     rotated (4 pairs) when 8j < R.
+// The counts are fixed by the instantiation (R = 32 H16 for split-half).
+template <int D, int PAIR, int H16> struct KPlan {
+  static constexpr int kPair = PAIR == kSplitHalf ? 2 * H16 : 0;
+  static constexpr int kCopy = PAIR == kSplitHalf ? D / 8 - 4 * H16 : 0;
+  static constexpr int kInter = PAIR == kSplitHalf ? 0 : D / 8;
+  static constexpr int lanes(int per_key) { return (kKeys * per_key + kBlock - 1) / kBlock; }
+  static constexpr int kPairN = lanes(kPair), kCopyN = lanes(kCopy), kInterN = lanes(kInter);
 };
 
 // LDS layout, in bf16 elements: two buffers, each a K tile
-// [kKeys][D + kKPad] followed by a V^T tile [D][kKeys + kVPad].
+// [kKeys][D + kKPad] followed by a V^T tile [D][kKeys + kVPad] (keys in
+// v_slot order).
 template <int D> constexpr int k_lds_elems() { return kKeys * (D + kKPad); }
 template <int D> constexpr int v_lds_elems() { return D * (kKeys + kVPad); }
 template <int D> constexpr int buf_elems() { return k_lds_elems<D>() + v_lds_elems<D>(); }
@@ -102,8 +111,17 @@ template <int D> constexpr int lds_bytes() { return 2 * 2 * buf_elems<D>(); }
 template <int D> ROPE_HD int k_lds(int buf, int key, int dim) {
   return buf * buf_elems<D>() + key * (D + kKPad) + dim;
 }
-template <int D> ROPE_HD int v_lds(int buf, int dim, int key) {
-  return buf * buf_elems<D>() + k_lds_elems<D>() + dim * (kKeys + kVPad) + key;
+// V^T slot of key `key` (0 .. kKeys-1) of a tile: inside each 16-key group
+// the second and third quads trade places, so the 8 keys one lane feeds a
+// product step (keys 4 hs .. 4 hs + 3 and 8 + 4 hs .. 11 + 4 hs of the
+// group) sit in the 8 consecutive slots 8 hs .. 8 hs + 7: one 16-byte read.
+ROPE_HD int v_slot(int key) {
+  const int q = (key >> 2) & 3;
+  const int qs = q == 1 ? 2 : (q == 2 ? 1 : q);
+  return (key & ~15) | (qs << 2) | (key & 3);
+}
+template <int D> ROPE_HD int v_lds(int buf, int dim, int slot) {
+  return buf * buf_elems<D>() + k_lds_elems<D>() + dim * (kKeys + kVPad) + slot;
 }
 
 // Workgroup -> (batch, head group, query tile). Workgroups are handed to
@@ -224,25 +242,20 @@ __device__ __forceinline__ float wave_xor32(float x) {
 #endif
 
 // ------------------------------------------------------- tile staging
-// K staging items per key, fixed by the instantiation: split-half rotates
-// R/16 = 2 H16 chunk pairs and copies D/8 - 4 H16 chunks; interleaved has
-// one item per 8-dim chunk. (Equal to KItems::per_key of the plan's args.)
-template <int D, int PAIR, int H16> constexpr int k_per_key() {
-  return PAIR == kSplitHalf ? D / 8 - 2 * H16 : D / 8;
-}
-// Most K / V staging items one lane handles per tile.
-template <int D, int PAIR, int H16> constexpr int k_items_max() {
-  return (kKeys * k_per_key<D, PAIR, H16>() + kBlock - 1) / kBlock;
-}
 template <int D> constexpr int v_items_max() { return (v_items<D>() + kBlock - 1) / kBlock; }
+constexpr int at_least_1(int n) { return n > 0 ? n : 1; }
 
-// Raw rows of one tile held in registers between fetch and staging. Item n
-// of a lane is item t + n * kBlock of the tile (the same items, in the same
-// order, as a loop over it = t, t + kBlock, ...).
+// Raw rows of one tile (and the cos/sin of its rotated items) held in
+// registers between fetch and staging.
 template <int D, int PAIR, int H16> struct KStage {
-  static constexpr int kN = k_items_max<D, PAIR, H16>();
-  bf16x8 x1[kN], x2[kN];
-  int p[kN];  // table row, or -1: not rotated
+  using P = KPlan<D, PAIR, H16>;
+  bf16x8 px1[at_least_1(P::kPairN)], px2[at_least_1(P::kPairN)];
+  float pc[at_least_1(P::kPairN)][8], ps[at_least_1(P::kPairN)][8];
+  bool prot[at_least_1(P::kPairN)];
+  bf16x8 cx[at_least_1(P::kCopyN)];
+  bf16x8 ix[at_least_1(P::kInterN)];
+  float ic[at_least_1(P::kInterN)][4], is[at_least_1(P::kInterN)][4];
+  bool irot[at_least_1(P::kInterN)];
 };
 template <int D> struct VStage {
   u32x4 x[v_items_max<D>()][4];  // 4 key rows x 8 dims, as bf16 pairs
@@ -252,71 +265,92 @@ template <int D> struct VStage {
 template <int D, int PAIR, int H16>
 __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* kbase, int k0,
                                         int t, KStage<D, PAIR, H16>& ks) {
-  constexpr int per_key = k_per_key<D, PAIR, H16>(), npair = 2 * H16;
+  using P = KPlan<D, PAIR, H16>;
   const int R = 2 * a.half;
+  const bf16x8 z = {};
 #pragma unroll
-  for (int n = 0; n < KStage<D, PAIR, H16>::kN; ++n) {
+  for (int n = 0; n < P::kPairN; ++n) {
     const int it = t + n * kBlock;
-    bf16x8 z = {};
-    ks.x1[n] = z;
-    ks.x2[n] = z;
-    ks.p[n] = -1;
-    if (it < kKeys * per_key) {
-      const int kk = it / per_key, item = it - kk * per_key;
-      const int key = k0 + kk;
+    ks.px1[n] = z;
+    ks.px2[n] = z;
+    ks.prot[n] = false;
+    if (it < kKeys * P::kPair) {
+      const int key = k0 + it / P::kPair, j = it % P::kPair;
       if (key < a.seq_k) {
         const __bf16* krow = kbase + (int64_t)key * D;
-        if (a.rotate) ks.p[n] = (int)key_pos(a, b, key);
-        if constexpr (PAIR == kSplitHalf) {
-          if (item < npair) {
-            ks.x1[n] = *reinterpret_cast<const bf16x8*>(krow + item * 8);
-            ks.x2[n] = *reinterpret_cast<const bf16x8*>(krow + a.half + item * 8);
-          } else {
-            ks.x1[n] = *reinterpret_cast<const bf16x8*>(krow + R + (item - npair) * 8);
+        ks.px1[n] = *reinterpret_cast<const bf16x8*>(krow + 8 * j);
+        ks.px2[n] = *reinterpret_cast<const bf16x8*>(krow + a.half + 8 * j);
+        const int64_t p = key_pos(a, b, key);
+        if (p >= 0) {
+          load_cs(a, p, 8 * j, 8, ks.pc[n], ks.ps[n]);
+          ks.prot[n] = true;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < P::kCopyN; ++n) {
+    const int it = t + n * kBlock;
+    ks.cx[n] = z;
+    if (it < kKeys * P::kCopy) {
+      const int key = k0 + it / P::kCopy, j = it % P::kCopy;
+      if (key < a.seq_k)
+        ks.cx[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + R + 8 * j);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < P::kInterN; ++n) {
+    const int it = t + n * kBlock;
+    ks.ix[n] = z;
+    ks.irot[n] = false;
+    if (it < kKeys * P::kInter) {
+      const int key = k0 + it / P::kInter, j = it % P::kInter;
+      if (key < a.seq_k) {
+        ks.ix[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + 8 * j);
+        if (8 * j < R) {
+          const int64_t p = a.rotate ? key_pos(a, b, key) : -1;
+          if (p >= 0) {
+            load_cs(a, p, 4 * j, 4, ks.ic[n], ks.is[n]);
+            ks.irot[n] = true;
           }
-        } else {
-          ks.x1[n] = *reinterpret_cast<const bf16x8*>(krow + item * 8);
         }
       }
     }
   }
 }
 
-// Rotate the fetched K items (split-half: items [0, R/16) of a key rotate
-// the chunk pair (c, c + R/16); interleaved: items [0, R/8) rotate chunk c
-// in place; the rest are copied) and write them to the K tile.
+// Rotate the fetched K items with the cos/sin fetched beside them and write
+// them to the K tile of buffer `buf`.
 template <int D, int PAIR, int H16>
 __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR, H16>& ks,
                                         __bf16* lds, int buf) {
-  constexpr int per_key = k_per_key<D, PAIR, H16>(), npair = 2 * H16;
-  const int R = 2 * a.half, rchunks = R / 8;
+  using P = KPlan<D, PAIR, H16>;
+  const int R = 2 * a.half;
 #pragma unroll
-  for (int n = 0; n < KStage<D, PAIR, H16>::kN; ++n) {
+  for (int n = 0; n < P::kPairN; ++n) {
     const int it = t + n * kBlock;
-    if (it < kKeys * per_key) {
-      const int kk = it / per_key, item = it - kk * per_key;
-      if constexpr (PAIR == kSplitHalf) {
-        if (item < npair) {
-          const int d1 = item * 8, d2 = a.half + item * 8;
-          if (ks.p[n] >= 0) {
-            float c[8], sn[8];
-            load_cs(a, ks.p[n], d1, 8, c, sn);
-            rotate_split8(ks.x1[n], ks.x2[n], c, sn);
-          }
-          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, d1)]) = ks.x1[n];
-          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, d2)]) = ks.x2[n];
-        } else {
-          *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, R + (item - npair) * 8)]) = ks.x1[n];
-        }
-      } else {
-        const int d = item * 8;
-        if (item < rchunks && ks.p[n] >= 0) {
-          float c[4], sn[4];
-          load_cs(a, ks.p[n], d / 2, 4, c, sn);
-          rotate_inter8(ks.x1[n], c, sn);
-        }
-        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, d)]) = ks.x1[n];
-      }
+    if (it < kKeys * P::kPair) {
+      const int kk = it / P::kPair, j = it % P::kPair;
+      if (ks.prot[n]) rotate_split8(ks.px1[n], ks.px2[n], ks.pc[n], ks.ps[n]);
+      *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.px1[n];
+      *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, a.half + 8 * j)]) = ks.px2[n];
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < P::kCopyN; ++n) {
+    const int it = t + n * kBlock;
+    if (it < kKeys * P::kCopy) {
+      const int kk = it / P::kCopy, j = it % P::kCopy;
+      *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, R + 8 * j)]) = ks.cx[n];
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < P::kInterN; ++n) {
+    const int it = t + n * kBlock;
+    if (it < kKeys * P::kInter) {
+      const int kk = it / P::kInter, j = it % P::kInter;
+      if (ks.irot[n]) rotate_inter8(ks.ix[n], ks.ic[n], ks.is[n]);
+      *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.ix[n];
     }
   }
 }
@@ -358,8 +392,9 @@ __device__ __forceinline__ void stage_v(int t, const VStage<D>& vs, __bf16* lds,
                             __builtin_amdgcn_perm(vs.x[n][3][w], vs.x[n][2][w], kLow)};
         const u32x2 odd = {__builtin_amdgcn_perm(vs.x[n][1][w], vs.x[n][0][w], kHigh),
                            __builtin_amdgcn_perm(vs.x[n][3][w], vs.x[n][2][w], kHigh)};
-        *reinterpret_cast<u32x2*>(&lds[v_lds<D>(buf, vi.c * 8 + 2 * w, 4 * vi.k4)]) = even;
-        *reinterpret_cast<u32x2*>(&lds[v_lds<D>(buf, vi.c * 8 + 2 * w + 1, 4 * vi.k4)]) = odd;
+        const int slot = v_slot(4 * vi.k4);  // the quad stays contiguous
+        *reinterpret_cast<u32x2*>(&lds[v_lds<D>(buf, vi.c * 8 + 2 * w, slot)]) = even;
+        *reinterpret_cast<u32x2*>(&lds[v_lds<D>(buf, vi.c * 8 + 2 * w + 1, slot)]) = odd;
       }
     }
   }
@@ -543,14 +578,14 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
           bf16x8 pb;
 #pragma unroll
           for (int i = 0; i < 8; ++i) pb[i] = from_f32<__bf16>(sc[half][8 * u + i]);
-          const int kb = half * 32 + 16 * u + 4 * hs;  // keys kb..kb+3 and kb+8..kb+11
+          // keys 16u + 4hs .. +3 and 16u + 8 + 4hs .. +3 of this half: V^T
+          // slots half*32 + 16u + 8hs .. +7
+          const int slot = half * 32 + 16 * u + 8 * hs;
           u32x4 va[D / 32];
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
             const int dim = dt * 32 + (lane & 31);
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(&lds[v_lds<D>(buf, dim, kb)]);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(&lds[v_lds<D>(buf, dim, kb + 8)]);
-            va[dt] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+            va[dt] = *reinterpret_cast<const u32x4*>(&lds[v_lds<D>(buf, dim, slot)]);
           }
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)

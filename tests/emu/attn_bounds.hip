@@ -4,8 +4,8 @@
 // The kernel (rope_attention.hpp) runs on matrix cores and cannot execute on
 // the host, so this walks its loops instead: every workgroup, lane and key
 // tile of the planned grid, forming each address with the kernel's own index
-// functions (work_of, wave_role, row_of, k_lds, v_lds, query_pos, key_pos,
-// key_tiles, KItems) and counting any that falls outside the exact extent of
+// functions (work_of, wave_role, row_of, k_lds, v_lds, v_slot, query_pos,
+// key_pos, key_tiles, KPlan) and counting any that falls outside the exact extent of
 // its buffer. The tile pipeline is simulated phase by phase (stage tile 0;
 // then per tile, the reads of its buffer and the staging of the next tile
 // into the other one): each staging write must land in its tile's buffer,
@@ -16,6 +16,7 @@
 //   (qpos / kpos: 0 = no index, 1 = an index of Sq / Sk entries per batch)
 // prints "plan <status>" then "violations <n>" and "accesses <n>".
 #include <algorithm>
+#include <type_traits>
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -48,17 +49,16 @@ struct LdsModel {
   explicit LdsModel(int n) : tile(n, -1), writer(n, -1) {}
 };
 
-template <int D, int PAIR>
+template <int D, int PAIR, int H16>
 void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_elems,
           int64_t qpos_elems, int64_t kpos_elems, Checker& ck) {
   const AttnArgs& a = pl.a;
   const int lds_elems = lds_bytes<D>() / 2;
   const int R = 2 * a.half;
-  const int per_key = KItems<D, PAIR>::per_key(a);
-  // the kernel instantiation's compile-time count must equal the plan's
-  const int h16 = pl.h16;
-  ck.fail(per_key != (PAIR == kSplitHalf ? D / 8 - 2 * h16 : D / 8), "items per key");
-  const int rchunks = R / 8;
+  using P = KPlan<D, PAIR, H16>;
+  // the instantiation's item classes cover each key's D dims exactly once
+  ck.fail(PAIR == kSplitHalf && R != 32 * H16, "split-half R is 32 H16");
+  ck.fail(16 * P::kPair + 8 * P::kCopy + 8 * P::kInter != D, "items cover the head dim");
   auto qpos = [&](int b, int i) {
     if (a.q_pos) ck.check((int64_t)b * a.q_pos_bs + i, 1, qpos_elems, "q_pos");
     return query_pos(a, b, i);
@@ -148,35 +148,42 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
         }
       };
       for (int t = 0; t < kBlock; ++t) {
-        for (int it = t; it < kKeys * per_key; it += kBlock) {
-          const int kk = it / per_key, item = it - kk * per_key;
+        // split-half pair items: rotate dims 8j.. with R/2 + 8j..
+        for (int it = t; it < kKeys * P::kPair; it += kBlock) {
+          const int kk = it / P::kPair, j = it % P::kPair;
           const int key = k0 + kk;
-          const bool ok = key < a.seq_k;
-          const int64_t krow = kbase + (int64_t)(ok ? key : 0) * D;
-          const int64_t kp = (ok && a.rotate) ? kpos(b, key) : -1;
-          if (PAIR == kSplitHalf) {
-            const int npair = rchunks / 2;
-            if (item < npair) {
-              const int d1 = item * 8, d2 = a.half + item * 8;
-              if (ok) {
-                ck.check(krow + d1, 8, kv_elems, "k load");
-                ck.check(krow + d2, 8, kv_elems, "k load");
-              }
-              if (kp >= 0) ck.check(kp * a.half + d1, 8, table_elems, "k cos/sin");
-              wrote(k_lds<D>(buf, kk, d1), 8, t, "k lds");
-              wrote(k_lds<D>(buf, kk, d2), 8, t, "k lds");
-            } else {
-              const int d = R + (item - npair) * 8;
-              if (ok) ck.check(krow + d, 8, kv_elems, "k load");
-              wrote(k_lds<D>(buf, kk, d), 8, t, "k lds");
-            }
-          } else {
-            const int d = item * 8;
-            if (ok) ck.check(krow + d, 8, kv_elems, "k load");
-            if (item < rchunks && kp >= 0) ck.check(kp * a.half + d / 2, 4, table_elems, "k cos/sin");
-            wrote(k_lds<D>(buf, kk, d), 8, t, "k lds");
+          if (key < a.seq_k) {
+            const int64_t krow = kbase + (int64_t)key * D;
+            ck.check(krow + 8 * j, 8, kv_elems, "k load");
+            ck.check(krow + a.half + 8 * j, 8, kv_elems, "k load");
+            const int64_t kp = kpos(b, key);
+            if (kp >= 0) ck.check(kp * a.half + 8 * j, 8, table_elems, "k cos/sin");
           }
+          wrote(k_lds<D>(buf, kk, 8 * j), 8, t, "k lds");
+          wrote(k_lds<D>(buf, kk, a.half + 8 * j), 8, t, "k lds");
         }
+        // split-half copy items: dims R + 8j..
+        for (int it = t; it < kKeys * P::kCopy; it += kBlock) {
+          const int kk = it / P::kCopy, j = it % P::kCopy;
+          const int key = k0 + kk;
+          if (key < a.seq_k) ck.check(kbase + (int64_t)key * D + R + 8 * j, 8, kv_elems, "k load");
+          wrote(k_lds<D>(buf, kk, R + 8 * j), 8, t, "k lds");
+        }
+        // interleaved items: dims 8j.., rotated when 8j < R
+        for (int it = t; it < kKeys * P::kInter; it += kBlock) {
+          const int kk = it / P::kInter, j = it % P::kInter;
+          const int key = k0 + kk;
+          if (key < a.seq_k) {
+            ck.check(kbase + (int64_t)key * D + 8 * j, 8, kv_elems, "k load");
+            const int64_t kp = (8 * j < R && a.rotate) ? kpos(b, key) : -1;
+            if (kp >= 0) ck.check(kp * a.half + 4 * j, 4, table_elems, "k cos/sin");
+          }
+          wrote(k_lds<D>(buf, kk, 8 * j), 8, t, "k lds");
+        }
+        // the lanes' item counts stay within the registers the kernel keeps
+        ck.fail((t + P::kPairN * kBlock) < kKeys * P::kPair, "pair items per lane");
+        ck.fail((t + P::kCopyN * kBlock) < kKeys * P::kCopy, "copy items per lane");
+        ck.fail((t + P::kInterN * kBlock) < kKeys * P::kInter, "interleaved items per lane");
         for (int it = t; it < v_items<D>(); it += kBlock) {
           const VItem vi = v_item(it);
           for (int r = 0; r < 4; ++r) {
@@ -184,7 +191,7 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
             if (key < a.seq_k) ck.check(kbase + (int64_t)key * D + vi.c * 8, 8, kv_elems, "v load");
           }
           for (int i = 0; i < 8; ++i) {
-            const int off = v_lds<D>(buf, vi.c * 8 + i, 4 * vi.k4);
+            const int off = v_lds<D>(buf, vi.c * 8 + i, v_slot(4 * vi.k4));
             ck.fail(off % 4 != 0, "v lds write not 8-byte aligned");
             ck.fail(off < buf * buf_elems<D>() + k_lds_elems<D>(), "v lds inside the k tile");
             wrote(off, 4, t, "v lds");
@@ -211,12 +218,16 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
             read(k_lds<D>(buf, half * 32 + (lane & 31), st * 16 + hs * 8), 8, kt, "k lds read");
         for (int half = 0; half < 2; ++half)
           for (int u = 0; u < 2; ++u) {
+            const int slot = half * 32 + 16 * u + 8 * hs;
+            // the 8 slots hold the keys this lane's P^T slots stand for
             const int kb = half * 32 + 16 * u + 4 * hs;
-            ck.fail(kb + 8 + 4 > kKeys, "v key beyond the tile");
+            for (int i = 0; i < 8; ++i)
+              ck.fail(v_slot(i < 4 ? kb + i : kb + 8 + (i - 4)) != slot + i, "v slot order");
             for (int dt = 0; dt < D / 32; ++dt) {
               const int dim = dt * 32 + (lane & 31);
-              read(v_lds<D>(buf, dim, kb), 4, kt, "v lds read");
-              read(v_lds<D>(buf, dim, kb + 8), 4, kt, "v lds read");
+              const int off = v_lds<D>(buf, dim, slot);
+              ck.fail(off % 8 != 0, "v lds read not 16-byte aligned");
+              read(off, 8, kt, "v lds read");
             }
           }
       }
@@ -294,16 +305,38 @@ int main(int argc, char** argv) {
   }
   Checker ck;
   const int64_t qpos_elems = d.batch * d.seq_len_q, kpos_elems = d.batch * d.seq_len_k;
-  if (pl.head_dim == 64) {
-    if (pl.pairing == ROPE_SPLIT_HALF)
-      walk<64, kSplitHalf>(pl, q_elems, kv_elems, table_elems, qpos_elems, kpos_elems, ck);
-    else
-      walk<64, kInterleaved>(pl, q_elems, kv_elems, table_elems, qpos_elems, kpos_elems, ck);
+  const int64_t a1 = qpos_elems, a2 = kpos_elems;
+  auto run = [&](auto d_tag, auto pair_tag, auto h_tag) {
+    walk<decltype(d_tag)::value, decltype(pair_tag)::value, decltype(h_tag)::value>(
+        pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
+  using SP = std::integral_constant<int, kSplitHalf>;
+  using IN = std::integral_constant<int, kInterleaved>;
+  if (pl.pairing == ROPE_INTERLEAVED) {
+    if (pl.head_dim == 64) run(D64{}, IN{}, I0{}); else run(D128{}, IN{}, I0{});
+  } else if (pl.head_dim == 64) {
+    switch (pl.h16) {
+      case 0: run(D64{}, SP{}, I0{}); break;
+      case 1: run(D64{}, SP{}, I1{}); break;
+      case 2: run(D64{}, SP{}, I2{}); break;
+      default: ck.fail(true, "h16 beyond head dim 64");
+    }
   } else {
-    if (pl.pairing == ROPE_SPLIT_HALF)
-      walk<128, kSplitHalf>(pl, q_elems, kv_elems, table_elems, qpos_elems, kpos_elems, ck);
-    else
-      walk<128, kInterleaved>(pl, q_elems, kv_elems, table_elems, qpos_elems, kpos_elems, ck);
+    switch (pl.h16) {
+      case 0: run(D128{}, SP{}, I0{}); break;
+      case 1: run(D128{}, SP{}, I1{}); break;
+      case 2: run(D128{}, SP{}, I2{}); break;
+      case 3: run(D128{}, SP{}, I3{}); break;
+      case 4: run(D128{}, SP{}, I4{}); break;
+      default: ck.fail(true, "h16 beyond head dim 128");
+    }
   }
   printf("violations %lld\naccesses %lld\n", ck.violations, ck.accesses);
   return 0;
