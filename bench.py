@@ -711,7 +711,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "rope_rows_kernel<__bf16, 8, split-half> (fwd and bwd launches)",
+                     "kernel": "rope_pair_lanes_kernel<__bf16, 8, 4> (fwd and bwd launches)",
                      "algorithmic_bytes_per_launch": per_call,
                      "avg_launch_us": round(avg_launch_us, 3),
                      "launches_timed": launches},

@@ -62,9 +62,21 @@ struct GpuLauncher {
     else if (mode == rope::kTokenLoop)
       hipLaunchKernelGGL((rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenLoop, OOP, RT>),
                          grid, block, 0, st, pl.a);
-    else
+    else if (!launch_pair<T, V, PAIR, AL, OOP>(grid, block))
       hipLaunchKernelGGL((rope::rope_rows_kernel<T, V, PAIR, AL, 4, OOP>), grid, block, 0, st,
                          pl.a);
+  }
+
+  // the one-chunk-per-lane rows kernel, for the plans that chose it
+  template <typename T, int V, int PAIR, bool AL, bool OOP>
+  bool launch_pair(dim3 grid, dim3 block) {
+    if constexpr (PAIR == rope::kSplitHalf && AL && !OOP && V * sizeof(T) == 16) {
+      if (pl.pair) {
+        hipLaunchKernelGGL((rope::rope_pair_lanes_kernel<T, V, 4>), grid, block, 0, st, pl.a);
+        return true;
+      }
+    }
+    return false;
   }
 
   template <typename T, int V, int PAIR, bool AL>

@@ -268,50 +268,56 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
   using P = KPlan<D, PAIR, H16>;
   const int R = 2 * a.half;
   const bf16x8 z = {};
+  if constexpr (P::kPair > 0) {
 #pragma unroll
-  for (int n = 0; n < P::kPairN; ++n) {
-    const int it = t + n * kBlock;
-    ks.px1[n] = z;
-    ks.px2[n] = z;
-    ks.prot[n] = false;
-    if (it < kKeys * P::kPair) {
-      const int key = k0 + it / P::kPair, j = it % P::kPair;
-      if (key < a.seq_k) {
-        const __bf16* krow = kbase + (int64_t)key * D;
-        ks.px1[n] = *reinterpret_cast<const bf16x8*>(krow + 8 * j);
-        ks.px2[n] = *reinterpret_cast<const bf16x8*>(krow + a.half + 8 * j);
-        const int64_t p = key_pos(a, b, key);
-        if (p >= 0) {
-          load_cs(a, p, 8 * j, 8, ks.pc[n], ks.ps[n]);
-          ks.prot[n] = true;
+    for (int n = 0; n < P::kPairN; ++n) {
+      const int it = t + n * kBlock;
+      ks.px1[n] = z;
+      ks.px2[n] = z;
+      ks.prot[n] = false;
+      if (it < kKeys * P::kPair) {
+        const int key = k0 + it / P::kPair, j = it % P::kPair;
+        if (key < a.seq_k) {
+          const __bf16* krow = kbase + (int64_t)key * D;
+          ks.px1[n] = *reinterpret_cast<const bf16x8*>(krow + 8 * j);
+          ks.px2[n] = *reinterpret_cast<const bf16x8*>(krow + a.half + 8 * j);
+          const int64_t p = key_pos(a, b, key);
+          if (p >= 0) {
+            load_cs(a, p, 8 * j, 8, ks.pc[n], ks.ps[n]);
+            ks.prot[n] = true;
+          }
         }
       }
     }
   }
+  if constexpr (P::kCopy > 0) {
 #pragma unroll
-  for (int n = 0; n < P::kCopyN; ++n) {
-    const int it = t + n * kBlock;
-    ks.cx[n] = z;
-    if (it < kKeys * P::kCopy) {
-      const int key = k0 + it / P::kCopy, j = it % P::kCopy;
-      if (key < a.seq_k)
-        ks.cx[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + R + 8 * j);
+    for (int n = 0; n < P::kCopyN; ++n) {
+      const int it = t + n * kBlock;
+      ks.cx[n] = z;
+      if (it < kKeys * P::kCopy) {
+        const int key = k0 + it / P::kCopy, j = it % P::kCopy;
+        if (key < a.seq_k)
+          ks.cx[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + R + 8 * j);
+      }
     }
   }
+  if constexpr (P::kInter > 0) {
 #pragma unroll
-  for (int n = 0; n < P::kInterN; ++n) {
-    const int it = t + n * kBlock;
-    ks.ix[n] = z;
-    ks.irot[n] = false;
-    if (it < kKeys * P::kInter) {
-      const int key = k0 + it / P::kInter, j = it % P::kInter;
-      if (key < a.seq_k) {
-        ks.ix[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + 8 * j);
-        if (8 * j < R) {
-          const int64_t p = a.rotate ? key_pos(a, b, key) : -1;
-          if (p >= 0) {
-            load_cs(a, p, 4 * j, 4, ks.ic[n], ks.is[n]);
-            ks.irot[n] = true;
+    for (int n = 0; n < P::kInterN; ++n) {
+      const int it = t + n * kBlock;
+      ks.ix[n] = z;
+      ks.irot[n] = false;
+      if (it < kKeys * P::kInter) {
+        const int key = k0 + it / P::kInter, j = it % P::kInter;
+        if (key < a.seq_k) {
+          ks.ix[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + 8 * j);
+          if (8 * j < R) {
+            const int64_t p = a.rotate ? key_pos(a, b, key) : -1;
+            if (p >= 0) {
+              load_cs(a, p, 4 * j, 4, ks.ic[n], ks.is[n]);
+              ks.irot[n] = true;
+            }
           }
         }
       }
@@ -326,31 +332,37 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
                                         __bf16* lds, int buf) {
   using P = KPlan<D, PAIR, H16>;
   const int R = 2 * a.half;
+  if constexpr (P::kPair > 0) {
 #pragma unroll
-  for (int n = 0; n < P::kPairN; ++n) {
-    const int it = t + n * kBlock;
-    if (it < kKeys * P::kPair) {
-      const int kk = it / P::kPair, j = it % P::kPair;
-      if (ks.prot[n]) rotate_split8(ks.px1[n], ks.px2[n], ks.pc[n], ks.ps[n]);
-      *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.px1[n];
-      *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, a.half + 8 * j)]) = ks.px2[n];
+    for (int n = 0; n < P::kPairN; ++n) {
+      const int it = t + n * kBlock;
+      if (it < kKeys * P::kPair) {
+        const int kk = it / P::kPair, j = it % P::kPair;
+        if (ks.prot[n]) rotate_split8(ks.px1[n], ks.px2[n], ks.pc[n], ks.ps[n]);
+        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.px1[n];
+        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, a.half + 8 * j)]) = ks.px2[n];
+      }
     }
   }
+  if constexpr (P::kCopy > 0) {
 #pragma unroll
-  for (int n = 0; n < P::kCopyN; ++n) {
-    const int it = t + n * kBlock;
-    if (it < kKeys * P::kCopy) {
-      const int kk = it / P::kCopy, j = it % P::kCopy;
-      *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, R + 8 * j)]) = ks.cx[n];
+    for (int n = 0; n < P::kCopyN; ++n) {
+      const int it = t + n * kBlock;
+      if (it < kKeys * P::kCopy) {
+        const int kk = it / P::kCopy, j = it % P::kCopy;
+        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, R + 8 * j)]) = ks.cx[n];
+      }
     }
   }
+  if constexpr (P::kInter > 0) {
 #pragma unroll
-  for (int n = 0; n < P::kInterN; ++n) {
-    const int it = t + n * kBlock;
-    if (it < kKeys * P::kInter) {
-      const int kk = it / P::kInter, j = it % P::kInter;
-      if (ks.irot[n]) rotate_inter8(ks.ix[n], ks.ic[n], ks.is[n]);
-      *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.ix[n];
+    for (int n = 0; n < P::kInterN; ++n) {
+      const int it = t + n * kBlock;
+      if (it < kKeys * P::kInter) {
+        const int kk = it / P::kInter, j = it % P::kInter;
+        if (ks.irot[n]) rotate_inter8(ks.ix[n], ks.ic[n], ks.is[n]);
+        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.ix[n];
+      }
     }
   }
 }

@@ -505,6 +505,147 @@ __global__ void __launch_bounds__(kRowsBlock) rope_rows_kernel(Args a) {
   rows_entry<T, V, PAIR, ALIGNED, U, OOP>(a, blockIdx.x, threadIdx.x);
 }
 
+// -------------------------------------- rows shape, one chunk per lane
+// Split-half pairs, in place, 16-byte aligned chunks, and L = R / (2 V) a
+// power of two no larger than kPairLanesMax. The 2L lanes of a token hold
+// its 2L chunks, lane c2 the chunk c2 % L of half c2 / L, so each row access
+// of a wave covers the whole rotated span of 64 / (2L) tokens. A lane takes
+// the chunk of its pair partner (lane c2 ^ L: the same chunk of the other
+// half) from that lane's registers and writes only its own chunk:
+//   lower half  y = x1 c - x2 s  = own c + other (-s)
+//   upper half  y = x2 c + x1 s  = own c + other (+s)
+// in the steps of rotate_pair, which it reproduces bit for bit (negating s
+// is exact and commutes with every rounding there).
+constexpr int kPairLanesMax = 16;
+
+ROPE_HD float rotate_own(float own, float other, float c, float s_eff) {
+  const float p = other * s_eff;
+  const float e = __builtin_fmaf(other, s_eff, -p);  // other*s_eff - p, exact
+  return __builtin_fmaf(own, c, p) + e;
+}
+
+template <typename T, int V, int U, int SRC> struct PairLaneWork {
+  using C = Chunk<T, V, true>;
+  Trig<V, kSplitHalf> t;
+  T* row[2];         // Q and K rows of this token at head 0, at this lane's chunk
+  int64_t sh[2];     // head strides
+  int lo[2], hi[2];  // head ranges of this workgroup's group, per tensor
+  bool upper;        // this lane holds the second half's chunk
+  C own[U], other[U];
+
+  // false: this lane has nothing to do (past the last token, or a skipped
+  // token; the partner lane then has nothing to do either)
+  ROPE_HD bool begin(const Args& a, int64_t block, int thread) {
+    int64_t tile;
+    int group;
+    if (a.group_slow) {
+      group = (int)(block / a.n_tiles);
+      tile = block - (int64_t)group * a.n_tiles;
+    } else {
+      tile = block / a.n_groups;
+      group = (int)(block - tile * a.n_groups);
+    }
+    const int64_t item = tile * kRowsBlock + thread;
+    if (item >= a.n_items) return false;
+    const int64_t n = item >> a.lanes_shift;
+    const int c2 = (int)(item & (a.lanes - 1));
+    const int L = a.lanes >> 1;
+    upper = (c2 & L) != 0;
+    const int c = c2 & (L - 1);
+    const int64_t b = n / a.seq_len;
+    const int64_t s = n - b * a.seq_len;
+    const int64_t p = token_pos(a, b, s);
+    if (p < 0) return false;
+    const int h_begin = group * a.heads_per_group;
+    const int h_end = imin(h_begin + a.heads_per_group, a.n_heads_q + a.n_heads_k);
+    lo[0] = h_begin;
+    hi[0] = imin(h_end, a.n_heads_q);
+    lo[1] = imax(h_begin - a.n_heads_q, 0);
+    hi[1] = h_end - a.n_heads_q;
+    const int off = (upper ? a.half : 0) + c * V;
+    row[0] = view_row<T>(a.q_in, 0, b, s) + off;
+    row[1] = view_row<T>(a.k_in, 0, b, s) + off;
+    sh[0] = a.q_in.sh;
+    sh[1] = a.k_in.sh;
+    t.template load<SRC>(a, p, c * V);
+    return true;
+  }
+  ROPE_HD void load(int x, int h0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (h0 + u < hi[x]) own[u].load(row[x] + (int64_t)(h0 + u) * sh[x]);
+  }
+  // rotate the own chunks with the partner chunks in other[], store
+  ROPE_HD void finish(int x, int h0) {
+    const float sg = upper ? t.sign : -t.sign;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (h0 + u < hi[x]) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          own[u].v[j] = from_f32<T>(
+              rotate_own(to_f32(own[u].v[j]), to_f32(other[u].v[j]), t.c[j], sg * t.s[j]));
+        own[u].store(row[x] + (int64_t)(h0 + u) * sh[x]);
+      }
+    }
+  }
+};
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// The 32-bit word w of lane (this lane ^ L), L a power of two <= 16: a DPP
+// row rotation by 8 for L = 8 (within each row of 16 lanes, rotating by 8 is
+// xor 8), the LDS crossbar's swizzle (xor within 32 lanes) otherwise.
+__device__ __forceinline__ uint32_t partner_word(uint32_t w, int L) {
+  const int x = (int)w;
+  switch (L) {
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xf, 0xf, false);
+    case 1: return (uint32_t)__builtin_amdgcn_ds_swizzle(x, (1 << 10) | 0x1f);
+    case 2: return (uint32_t)__builtin_amdgcn_ds_swizzle(x, (2 << 10) | 0x1f);
+    case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle(x, (4 << 10) | 0x1f);
+    default: return (uint32_t)__builtin_amdgcn_ds_swizzle(x, (16 << 10) | 0x1f);
+  }
+}
+
+template <typename T, int V>
+__device__ __forceinline__ void partner_chunk(const Chunk<T, V, true>& own,
+                                              Chunk<T, V, true>& other, int L) {
+  static_assert(V * sizeof(T) == 16, "pair lanes move 16-byte chunks");
+  uint32_t w[4];
+  __builtin_memcpy(w, own.v, 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = partner_word(w[i], L);
+  __builtin_memcpy(other.v, w, 16);
+}
+
+template <typename T, int V, int U, int SRC>
+__device__ __forceinline__ void pair_lanes_body(const Args& a) {
+  PairLaneWork<T, V, U, SRC> w;
+  if (!w.begin(a, blockIdx.x, threadIdx.x)) return;
+  const int L = a.lanes >> 1;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    for (int h0 = w.lo[x]; h0 < w.hi[x]; h0 += U) {
+      w.load(x, h0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (h0 + u < w.hi[x]) partner_chunk<T, V>(w.own[u], w.other[u], L);
+      w.finish(x, h0);
+    }
+}
+#endif
+
+template <typename T, int V, int U>
+__global__ void __launch_bounds__(kRowsBlock) rope_pair_lanes_kernel(Args a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (a.angles)
+    pair_lanes_body<T, V, U, kTrigTheta>(a);
+  else if (a.t_vec)
+    pair_lanes_body<T, V, U, kTrigVec>(a);
+  else
+    pair_lanes_body<T, V, U, kTrigScalar>(a);
+#endif
+}
+
 // ------------------------------------------------------------- token shape
 // Lanes cover (head, chunk) items of a token. Each lane's head rows are
 // requested before the position, so the row loads overlap the dependent

@@ -29,6 +29,7 @@ struct Plan {
   bool empty;      // nothing to do
   bool single;     // token shape: the grid covers every token, no loops
   bool oop;        // some output differs from its input
+  bool pair;       // rows shape, one chunk per lane (rope_pair_lanes_kernel)
   int64_t lds_bytes;  // dynamic shared memory per workgroup
 
   // token shape: which rope_token_kernel instantiation runs the plan
@@ -367,7 +368,7 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
   // Rows shape: 256 (token, chunk) items per workgroup, each lane walking a
   // group of heads. Its waves per head group:
   a.n_items = a.n_tokens * a.lanes;
-  const int64_t tiles = (a.n_items + kRowsBlock - 1) / kRowsBlock;
+  int64_t tiles = (a.n_items + kRowsBlock - 1) / kRowsBlock;
   const int64_t waves_per_group = tiles * (kRowsBlock / 64);
   const int64_t target_waves = (int64_t)cus * 8;
 
@@ -434,6 +435,22 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
       groups = (target_waves + waves_per_group - 1) / waves_per_group;
       if (groups > h_total) groups = h_total;
       g = (int)((h_total + groups - 1) / groups);
+    }
+    // One chunk per lane (rope_pair_lanes_kernel) where it applies:
+    // split-half, in place, 16-byte chunks, L = R / (2V) a power of two
+    // <= kPairLanesMax, and a lane walking at most 4 heads (one unrolled
+    // batch). Measured on MI355X, in place: Llama [4,32+8,4096,128] bf16,
+    // 4-head groups, 54.9 us against 56.4 us with a chunk pair per lane;
+    // long context [1,32+8,131072,128], 8-head groups, 600 us against 472 us.
+    // Lanes then count both halves' chunks: twice the items.
+    pl->pair = d->pairing == ROPE_SPLIT_HALF && !pl->oop && pl->aligned &&
+               (int64_t)v * elem_bytes(d->dtype) == 16 && a.lanes_shift >= 0 &&
+               a.lanes <= kPairLanesMax && g <= 4;
+    if (pl->pair) {
+      a.lanes *= 2;
+      a.lanes_shift += 1;
+      a.n_items = a.n_tokens * a.lanes;
+      tiles = (a.n_items + kRowsBlock - 1) / kRowsBlock;
     }
     a.heads_per_group = g;
     a.n_groups = (int32_t)((h_total + g - 1) / g);

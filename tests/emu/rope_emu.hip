@@ -94,8 +94,63 @@ struct HostRunner {
       if (has[t]) ws[t].finish_shared(pl.a, lds.data());
   }
 
+  // Rows shape, one chunk per lane: the kernel's phases (load, partner
+  // exchange, rotate and store) run for every lane of the workgroup before
+  // the next, as the wave runs them in lockstep; each lane takes its
+  // partner's loaded chunk from that lane's registers.
+  template <typename T, int V, int SRC>
+  void pair_block(int64_t blk) {
+    using Work = rope::PairLaneWork<T, V, 4, SRC>;
+    std::vector<Work> ws(pl.block);
+    std::vector<char> live(pl.block);
+    int first = -1;
+    for (int t = 0; t < pl.block; ++t) {
+      live[t] = ws[t].begin(pl.a, blk, t);
+      if (live[t] && first < 0) first = t;
+    }
+    if (first < 0) return;
+    const int L = pl.a.lanes >> 1;
+    for (int t = 0; t < pl.block; ++t) {
+      if (!live[t]) continue;
+      // a live lane's partner is live, in the same wave, with the same heads
+      const int q = t ^ L;
+      if (q >= pl.block || !live[q] || (q >> 6) != (t >> 6) || ws[q].upper == ws[t].upper) {
+        fprintf(stderr, "pair lanes: lane %d has no partner\n", t);
+        exit(5);
+      }
+      for (int x = 0; x < 2; ++x)
+        if (ws[t].lo[x] != ws[first].lo[x] || ws[t].hi[x] != ws[first].hi[x]) {
+          fprintf(stderr, "pair lanes: head ranges differ within a workgroup\n");
+          exit(5);
+        }
+    }
+    for (int x = 0; x < 2; ++x)
+      for (int h0 = ws[first].lo[x]; h0 < ws[first].hi[x]; h0 += 4) {
+        for (int t = 0; t < pl.block; ++t)
+          if (live[t]) ws[t].load(x, h0);
+        for (int t = 0; t < pl.block; ++t)
+          if (live[t])
+            for (int u = 0; u < 4; ++u) ws[t].other[u] = ws[t ^ L].own[u];
+        for (int t = 0; t < pl.block; ++t)
+          if (live[t]) ws[t].finish(x, h0);
+      }
+  }
+
   template <typename T, int V, int PAIR, bool AL, bool OOP>
   void go() {
+    if constexpr (PAIR == rope::kSplitHalf && AL && !OOP && V * sizeof(T) == 16) {
+      if (!pl.token && pl.pair) {
+        for (int64_t blk = 0; blk < pl.grid; ++blk) {
+          if (pl.a.angles)
+            pair_block<T, V, rope::kTrigTheta>(blk);
+          else if (pl.a.t_vec)
+            pair_block<T, V, rope::kTrigVec>(blk);
+          else
+            pair_block<T, V, rope::kTrigScalar>(blk);
+        }
+        return;
+      }
+    }
     if (pl.token && pl.a.angles && pl.token_mode() != rope::kTokenLoop) {
       for (int64_t blk = 0; blk < pl.grid; ++blk) {
         if (pl.token_mode() == rope::kTokenOne)
@@ -134,15 +189,25 @@ struct HostRunner {
 void print_plan(const rope::Plan& pl) {
   printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
          "heads_per_group %d\nn_groups %d\ngroup_slow %d\nsingle %d\noop %d\nt_vec %d\n"
-         "tokens_per_block %d\nangles %d\nlds_bytes %lld\n",
+         "tokens_per_block %d\nangles %d\nlds_bytes %lld\npair %d\n",
          (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
          pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow, (int)pl.single,
          (int)pl.oop, pl.a.t_vec, pl.a.tokens_per_block, pl.a.angles,
-         (long long)pl.lds_bytes);
+         (long long)pl.lds_bytes, (int)pl.pair);
 }
 
-// test-only overrides of the rows-kernel grid (head-group size and order)
+// test-only overrides of the rows-kernel grid (one chunk or a chunk pair per
+// lane, head-group size and order)
 void apply_overrides(rope::Plan& pl, std::map<std::string, long long>& kv) {
+  if (!pl.empty && !pl.token && pl.pair && kv["no_pair"] > 0) {
+    // the pair-per-lane form of the same plan: half the lanes per token
+    pl.pair = false;
+    pl.a.lanes /= 2;
+    pl.a.lanes_shift -= 1;
+    pl.a.n_items = pl.a.n_tokens * pl.a.lanes;
+    pl.a.n_tiles = (pl.a.n_items + rope::kRowsBlock - 1) / rope::kRowsBlock;
+    pl.grid = pl.a.n_tiles * pl.a.n_groups;
+  }
   if (!pl.empty && !pl.token && kv["heads_per_group"] > 0) {
     const int h_total = pl.a.n_heads_q + pl.a.n_heads_k;
     pl.a.heads_per_group = (int32_t)kv["heads_per_group"];
@@ -235,6 +300,32 @@ int main(int argc, char** argv) {
   const std::string dir = argv[1];
   auto kv = read_job(dir);
   if (kv["apply"]) return apply_mode(dir, kv);
+  if (kv["plan_only"]) {
+    // the plan of a rope_fwd_qk call at any size, for 16-byte aligned Q and
+    // K (fake addresses: nothing runs, nothing is dereferenced)
+    rope_desc_t d{};
+    d.batch = kv["batch"];
+    d.n_heads_q = kv["n_heads_q"];
+    d.n_heads_k = kv["n_heads_k"];
+    d.seq_len = kv["seq_len"];
+    d.head_dim = kv["head_dim"];
+    d.rotary_dim = kv["rotary_dim"];
+    d.dtype = (int32_t)kv["dtype"];
+    d.layout = (int32_t)kv["layout"];
+    d.pairing = (int32_t)kv["pairing"];
+    d.launch = (int32_t)kv["launch"];
+    d.table_rows = kv["table_rows"];
+    d.cos = reinterpret_cast<const float*>((uintptr_t)1 << 44);
+    d.sin = reinterpret_cast<const float*>((uintptr_t)2 << 44);
+    void* q = reinterpret_cast<void*>((uintptr_t)3 << 44);
+    void* k = reinterpret_cast<void*>((uintptr_t)4 << 44);
+    rope::Plan pl;
+    const int cus = kv.count("cus") ? (int)kv["cus"] : 256;
+    const rope_status_t st = rope::make_plan(q, k, &d, true, 1.0f, cus, &pl);
+    printf("status %d\n", (int)st);
+    if (st == ROPE_OK) print_plan(pl);
+    return 0;
+  }
   if (kv["sincos"]) {
     // the kernels' cos/sin of binary64 angles: angles.bin (count doubles) ->
     // sincos.bin (count (cos, sin) float pairs)

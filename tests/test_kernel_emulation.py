@@ -739,3 +739,89 @@ def test_kernel_sincos_is_correctly_rounded(emu):
                     assert abs(float(g) - r) <= abs(np.spacing(np.float32(r))) * 1.01, (x, g, r)
                     assert abs(ref - mid) <= mpmath.mpf("1e-15"), (x, g, ref)
     assert bad <= 2, bad
+
+
+# -------------------------------------------- rows shape, one chunk per lane
+# Split-half, in place, 16-byte chunks, L = (R/2)/V chunks per half a power
+# of two <= 16: each lane holds one chunk and takes its pair partner's chunk
+# from lane ^ L. The emulator runs the wave's phases in lockstep. The results
+# must equal the pair-per-lane form of the same plan bit for bit (and the
+# oracle, through check()).
+PAIR_CASES = {
+    # name: workload, expected L
+    "bf16_R128_L8": (W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=77, table_rows=80), 8),
+    "bf16_R64_L4": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=50, head_dim=64, rotary_dim=64,
+                                                table_rows=50, n_heads_q=6, n_heads_k=2), 4),
+    "f32_R64_L8": (W.TINY_F32.scaled(seq_len=70, table_rows=70), 8),
+    "f16_R32_L2": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=33, head_dim=64, rotary_dim=32,
+                                               dtype="f16", table_rows=33, n_heads_q=4,
+                                               n_heads_k=4), 2),
+    "bf16_R256_L16": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=40, head_dim=256,
+                                                  rotary_dim=256, table_rows=40, n_heads_q=5,
+                                                  n_heads_k=1), 16),
+    "bf16_R16_L1": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=45, head_dim=64, rotary_dim=16,
+                                                table_rows=45, n_heads_q=3, n_heads_k=3), 1),
+    "indexed_partial": (W.PARTIAL_INDEXED.scaled(seq_len=130, pos_start_max=9000), 2),
+}
+
+
+@pytest.mark.parametrize("name", list(PAIR_CASES))
+@pytest.mark.parametrize("direction", [1, -1])
+def test_one_chunk_per_lane_equals_chunk_pairs(emu, name, direction):
+    w, L = PAIR_CASES[name]
+    plan = check(emu, w, direction, launch="rows",
+                 expect=dict(pair=1, lanes=2 * L))
+    q, k, wpos, cos, sin = _inputs(w)
+    _, q1, k1 = run_emu(emu, w, q, k, cos, sin, wpos, direction, "rows")
+    plan0, q0, k0 = run_emu(emu, w, q, k, cos, sin, wpos, direction, "rows",
+                            overrides=dict(no_pair=1))
+    assert plan0["pair"] == 0 and plan0["lanes"] == L, plan0
+    assert np.array_equal(q1, q0) and np.array_equal(k1, k0)
+    assert plan["grid"] >= plan0["grid"]
+
+
+@pytest.mark.parametrize("group_slow", [0, 1])
+@pytest.mark.parametrize("heads_per_group", [1, 3, 40])
+def test_one_chunk_per_lane_any_head_groups(emu, group_slow, heads_per_group):
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=37, table_rows=40)
+    check(emu, w, launch="rows", expect=dict(pair=1),
+          overrides=dict(heads_per_group=heads_per_group, group_slow=group_slow))
+
+
+def test_one_chunk_per_lane_only_where_it_applies(emu):
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=40, table_rows=40)
+    assert check(emu, w, launch="rows")["pair"] == 1
+    # interleaved pairs, 8-byte chunks (misaligned base), or L = 3 (R = 48)
+    assert check(emu, w.scaled(pairing=W.INTERLEAVED), launch="rows")["pair"] == 0
+    assert check(emu, w, launch="rows", q_offset=4)["pair"] == 0
+    assert check(emu, w.scaled(rotary_dim=48, head_dim=64), launch="rows")["pair"] == 0
+    # the token shape never uses it
+    assert check(emu, w, launch="token")["pair"] == 0
+
+
+def plan_of(emu, w, launch="auto", cus=256):
+    """The library's plan for rope_fwd_qk on workload w at full size (nothing runs)."""
+    with tempfile.TemporaryDirectory() as job:
+        desc = dict(plan_only=1, batch=w.batch, n_heads_q=w.n_heads_q, n_heads_k=w.n_heads_k,
+                    seq_len=w.seq_len, head_dim=w.head_dim, rotary_dim=w.rotary_dim,
+                    dtype=CODES["dtype"][w.dtype], layout=CODES["layout"][w.layout],
+                    pairing=CODES["pairing"][w.pairing], launch=CODES["launch"][launch],
+                    table_rows=w.table_rows, cus=cus)
+        with open(os.path.join(job, "desc.txt"), "w") as f:
+            for key, v in desc.items():
+                f.write(f"{key} {int(v)}\n")
+        r = subprocess.run([emu, job], capture_output=True, text=True, timeout=60)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return {k: int(v) for k, v in (line.split() for line in r.stdout.strip().splitlines())}
+
+
+def test_full_size_plans(emu):
+    # Llama prefill: rows shape, 4-head groups, one chunk per lane (16 lanes
+    # per token); long context: 8-head groups (its cos/sin table is re-read
+    # per group), a chunk pair per lane
+    p = plan_of(emu, W.LLAMA_GQA_PREFILL)
+    assert (p["token"], p["heads_per_group"], p["pair"], p["lanes"]) == (0, 4, 1, 16), p
+    p = plan_of(emu, W.LONG_CONTEXT)
+    assert (p["token"], p["heads_per_group"], p["pair"], p["lanes"]) == (0, 8, 0, 8), p
+    assert plan_of(emu, W.DECODE)["token"] == 1
+    assert plan_of(emu, W.BSHD_INTERLEAVED)["token"] == 1
