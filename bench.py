@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "rotary_position_embedding_fwd_amd", "csrc", f)
                   for f in ("rope_kernels.hpp", "rope_plan.hpp", "librope.hip")]
-TRAFFIC_FILE = os.path.join(PROFILES, "traffic_rope_rows_bf16_llama_gqa_prefill.json")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_rope_pair_lanes_kernel_bf16_llama_gqa_prefill.json")
 
 
 def kernel_source_hash() -> str:
@@ -589,13 +589,14 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str = TRAFFIC_FILE):
         vals = [v for n, v in rows if pred(n)]
         return sum(vals) / len(vals) if vals else None
 
-    is_fwd = lambda n: "rope_rows_kernel" in n and "bf16" in n.replace("DF16b", "bf16")  # noqa
+    # the kernel the bench's step runs (the one-chunk-per-lane rows kernel)
+    is_fwd = lambda n: "rope_pair_lanes_kernel" in n and "bf16" in n.replace("DF16b", "bf16")  # noqa
     is_copy = lambda n: "copyBuffer" in n  # the runtime's device-to-device copy  # noqa
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
     f_k, w_k = pick(fetch, is_fwd), pick(write, is_fwd)
     f_c, w_c = pick(fetch, is_copy), pick(write, is_copy)
     copy_bytes = 1 << 30
-    res = {"kernel": "rope_rows_kernel<__bf16, 8, split-half> (forward and backward launches)",
+    res = {"kernel": "rope_pair_lanes_kernel<__bf16, 8, 4> (forward and backward launches)",
            "workload": W.LLAMA_GQA_PREFILL.name,
            "fetch_kib_per_launch": f_k, "write_kib_per_launch": w_k,
            "copy_fetch_kib": f_c, "copy_write_kib": w_c}

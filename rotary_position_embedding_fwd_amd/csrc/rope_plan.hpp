@@ -438,12 +438,14 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
     }
     // One chunk per lane (rope_pair_lanes_kernel) where it applies:
     // split-half, in place, 16-byte chunks, L = R / (2V) a power of two
-    // <= kPairLanesMax, and a lane walking at most 4 heads (one unrolled
-    // batch). Measured on MI355X, in place: Llama [4,32+8,4096,128] bf16,
-    // 4-head groups, 54.9 us against 56.4 us with a chunk pair per lane;
-    // long context [1,32+8,131072,128], 8-head groups, 600 us against 472 us.
+    // <= kPairLanesMax, cos/sin read from tables, and a lane walking at
+    // most 4 heads (one unrolled batch). Measured on MI355X, in place:
+    // Llama [4,32+8,4096,128] bf16, 4-head groups, 54.9 us against 56.4 us
+    // with a chunk pair per lane; long context [1,32+8,131072,128], 8-head
+    // groups, 600 us against 472 us; angles from theta, where both lanes of
+    // a pair would evaluate the same sin/cos, 73.3 us against 58.3 us.
     // Lanes then count both halves' chunks: twice the items.
-    pl->pair = d->pairing == ROPE_SPLIT_HALF && !pl->oop && pl->aligned &&
+    pl->pair = d->pairing == ROPE_SPLIT_HALF && !pl->oop && pl->aligned && !a.angles &&
                (int64_t)v * elem_bytes(d->dtype) == 16 && a.lanes_shift >= 0 &&
                a.lanes <= kPairLanesMax && g <= 4;
     if (pl->pair) {

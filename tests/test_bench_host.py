@@ -38,7 +38,7 @@ def test_pmc_summary_scales_by_the_copy(tmp_path, monkeypatch):
               "Kernel_Id,Kernel_Name,Workgroup_Size,LDS_Block_Size,Scratch_Size,VGPR_Count,"
               "Accum_VGPR_Count,SGPR_Count,Counter_Name,Counter_Value,Start_Timestamp,"
               "End_Timestamp\n")
-    kern = "_ZN4rope16rope_rows_kernelIDF16bLi8ELi0ELb1ELi4EEEvNS_4ArgsE"
+    kern = "_ZN4rope22rope_pair_lanes_kernelIDF16bLi8ELi4EEEvNS_4ArgsE"
 
     def write(d, counter, rows):
         os.makedirs(d / "host", exist_ok=True)

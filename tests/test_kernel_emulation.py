@@ -825,3 +825,11 @@ def test_full_size_plans(emu):
     assert (p["token"], p["heads_per_group"], p["pair"], p["lanes"]) == (0, 8, 0, 8), p
     assert plan_of(emu, W.DECODE)["token"] == 1
     assert plan_of(emu, W.BSHD_INTERLEAVED)["token"] == 1
+
+
+def test_theta_angles_keep_chunk_pairs(emu):
+    # both lanes of a pair would evaluate the same sin/cos: the plan keeps a
+    # chunk pair per lane when angles come from theta
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=40, table_rows=40)
+    plan = _theta_case(emu, w, launch="rows")
+    assert plan["pair"] == 0 and plan["lanes"] == 8, plan
