@@ -41,6 +41,10 @@ CASES = [
     (2, 16, 2, 100, 300, 128, 128, SPLIT, 1, 300, 0, 1),    # 8 heads per workgroup
     (1, 6, 3, 70, 70, 64, 64, SPLIT, 0, 70, 0, 0),          # GQA 2:1
     (1, 12, 1, 40, 520, 128, 64, INTER, 1, 520, 1, 0),      # MQA 12:1 (4 heads per group)
+    (1, 16, 2, 70, 140, 128, 128, SPLIT, 1, 140, 0, 0),     # GQA 8:1 (8 heads per group)
+    (2, 16, 1, 40, 97, 64, 64, INTER, 0, 97, 1, 1),         # GQA 16:1
+    (1, 6, 2, 300, 100, 128, 64, SPLIT, 0, 300, 0, 0),      # GQA 3:1, Sq > Sk
+    (8, 4, 2, 33, 65, 64, 32, SPLIT, 1, 65, 1, 1),          # batch 8
 ]
 
 

@@ -80,6 +80,12 @@ CASES = {
     "decode_like_sq1": (3, 8, 2, 1, 300, 128, 128, "split_half", True, "none"),
     "short_sq3": (1, 4, 1, 3, 129, 64, 64, "split_half", True, "none"),
     "no_rotation": (1, 2, 1, 96, 96, 128, 0, "split_half", True, "none"),
+    # 8 query heads per workgroup (32 rows each) and 16 per K/V head
+    "gqa_8_heads_per_workgroup": (1, 16, 2, 70, 140, 128, 128, "split_half", True, "none"),
+    "gqa_16_to_1": (2, 16, 1, 40, 97, 64, 64, "interleaved", False, "random"),
+    # GQA 3:1 (one head per workgroup), more queries than keys, not causal
+    "gqa_3_to_1_sq_gt_sk": (1, 6, 2, 300, 100, 128, 64, "split_half", False, "none"),
+    "batch_8_short": (8, 4, 2, 33, 65, 64, 32, "split_half", True, "random"),
 }
 
 
