@@ -2,7 +2,7 @@
 //
 // The operation is an elementwise map that moves ~4 bytes per rotated pair
 // (16-bit) and does ~10 float ops on it, so it is bound by HBM bandwidth
-// ("Rotary Embedding Kernel", Overview: memory-bound, judged in GB/s). The
+// ("Rotary Embedding Kernel", Overview: memory-bound, measured in GB/s). The
 // kernels therefore aim at three things only: whole-row 128-bit loads and
 // stores, cos/sin read once per token and reused for several Q and K heads of
 // that token (the reuse that head grouping buys in How Unsloth Optimizes RoPE
