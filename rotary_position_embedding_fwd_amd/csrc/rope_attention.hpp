@@ -234,10 +234,20 @@ ROPE_HD void load_cs(const AttnArgs& a, int64_t p, int first, int n, float* c, f
 }
 
 #if defined(__HIP_DEVICE_COMPILE__)
-__device__ __forceinline__ float wave_xor32(float x) {
-  // the partner lane l ^ 32 (ds_bpermute addresses are byte lane indices)
-  const int src = (int)((__lane_id() ^ 32) << 2);
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x)));
+// Combine x with the partner lane l ^ 32 (the other half of the row): gfx950's
+// v_permlane32_swap exchanges the two 32-lane halves of a register in the
+// vector ALU. Swapping x with itself leaves (lower half's value, upper half's
+// value) in the two results of every lane, so max and sum come out the same,
+// bit for bit, in both lanes of a row.
+__device__ __forceinline__ float wave_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 #endif
 
@@ -553,7 +563,7 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int j = 0; j < 16; ++j) m_tile = fmaxf(m_tile, sc[half][j]);
-      m_tile = fmaxf(m_tile, wave_xor32(m_tile));
+      m_tile = wave_max32(m_tile);
       const float m_new = fmaxf(m_run, m_tile);
       const float c = a.scale_log2e;
       const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
@@ -568,7 +578,7 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
           sc[half][j] = pj;
           l_tile += pj;
         }
-      l_tile += wave_xor32(l_tile);
+      l_tile = wave_sum32(l_tile);
       l_run = l_run * alpha + l_tile;
       m_run = m_new;
       // rescale the output only when some lane's max moved

@@ -46,6 +46,13 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   // 32-bit index arithmetic inside the kernel
   const int64_t lim = (int64_t)1 << 30;
   if (B > lim || Hq > lim || Sq > lim || Sk > lim) return ROPE_ERR_SHAPE;
+  // byte counts of Q/O and K/V (and the table) must not overflow
+  int64_t qbytes = 0, kvbytes = 0, tbytes = 0;
+  if (__builtin_mul_overflow(B * Hq, Sq, &qbytes) || __builtin_mul_overflow(qbytes, D * 2, &qbytes) ||
+      __builtin_mul_overflow(B * Hk, Sk, &kvbytes) ||
+      __builtin_mul_overflow(kvbytes, D * 2, &kvbytes) ||
+      __builtin_mul_overflow(d->table_rows, R * 2, &tbytes))
+    return ROPE_ERR_SHAPE;
   pl->empty = B == 0 || Sq == 0;
   if (pl->empty) return ROPE_OK;
   const bool rotate = d->rotate && R > 0;
@@ -56,18 +63,24 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   if (mis(d->q, 16) || mis(d->k, 16) || mis(d->v, 16) || mis(d->o, 16)) return ROPE_ERR_ALIGN;
   if (rotate && (mis(d->cos, 16) || mis(d->sin, 16))) return ROPE_ERR_ALIGN;
   if (mis(d->q_pos, 4) || mis(d->k_pos, 4)) return ROPE_ERR_ALIGN;
-  const int64_t qbytes = B * Hq * Sq * D * 2, kvbytes = B * Hk * Sk * D * 2;
   if (ranges_meet(d->o, qbytes, d->q, qbytes) || ranges_meet(d->o, qbytes, d->k, kvbytes) ||
       ranges_meet(d->o, qbytes, d->v, kvbytes))
     return ROPE_ERR_ALIAS;
-  const int64_t tbytes = d->table_rows * (R / 2) * 4;
   if (rotate && (ranges_meet(d->o, qbytes, d->cos, tbytes) ||
                  ranges_meet(d->o, qbytes, d->sin, tbytes)))
     return ROPE_ERR_ALIAS;
-  if (d->q_pos && ranges_meet(d->o, qbytes, d->q_pos, 4 * ((B - 1) * d->q_pos_batch_stride + Sq)))
-    return ROPE_ERR_ALIAS;
-  if (d->k_pos && ranges_meet(d->o, qbytes, d->k_pos, 4 * ((B - 1) * d->k_pos_batch_stride + Sk)))
-    return ROPE_ERR_ALIAS;
+  // the index arrays' extents: ((B - 1) * stride + S) int32 entries
+  auto index_bytes = [&](int64_t stride, int64_t S, int64_t* out) {
+    int64_t n = 0;
+    return !__builtin_mul_overflow(B - 1, stride, &n) && !__builtin_add_overflow(n, S, &n) &&
+           !__builtin_mul_overflow(n, (int64_t)4, out);
+  };
+  int64_t qpb = 0, kpb = 0;
+  if ((d->q_pos && !index_bytes(d->q_pos_batch_stride, Sq, &qpb)) ||
+      (d->k_pos && !index_bytes(d->k_pos_batch_stride, Sk, &kpb)))
+    return ROPE_ERR_SHAPE;
+  if (d->q_pos && ranges_meet(d->o, qbytes, d->q_pos, qpb)) return ROPE_ERR_ALIAS;
+  if (d->k_pos && ranges_meet(d->o, qbytes, d->k_pos, kpb)) return ROPE_ERR_ALIAS;
 
   AttnArgs& a = pl->a;
   a.q = static_cast<const __bf16*>(d->q);

@@ -76,6 +76,19 @@ inline int64_t view_span(const ViewX& v) {
   return (v.B - 1) * v.sb + (v.H - 1) * v.sh + (v.S - 1) * v.ss + v.D;
 }
 
+// view_span in bytes, false when it does not fit in int64 (absurd strides or
+// sizes would otherwise wrap the overlap checks below)
+inline bool view_bytes(const ViewX& v, int64_t e, int64_t* out) {
+  *out = 0;
+  if (view_empty(v)) return true;
+  int64_t t = 0, n = v.D;
+  const int64_t ext[3] = {v.B, v.H, v.S}, st[3] = {v.sb, v.sh, v.ss};
+  for (int i = 0; i < 3; ++i)
+    if (__builtin_mul_overflow(ext[i] - 1, st[i], &t) || __builtin_add_overflow(n, t, &n))
+      return false;
+  return !__builtin_mul_overflow(n, e, out);
+}
+
 // Sufficient condition for no two (b, h, s, j) to share an element: ordered
 // by stride, every dim of extent > 1 steps over everything the smaller ones
 // cover. All the usual layouts ([B,H,S,D], [B,S,H,D], views into packed QKV)
@@ -194,6 +207,21 @@ inline rope_status_t validate_apply(const rope_apply_desc_t* d) {
   const ViewX ki = view_x(d->k_in, B, hk, S, D);
   const ViewX qo = d->q_out.data ? view_x(d->q_out, B, d->n_heads_q, S, D) : qi;
   const ViewX ko = d->k_out.data ? view_x(d->k_out, B, hk, S, D) : ki;
+  // every extent below fits in int64
+  int64_t span = 0, tokens = 0;
+  for (const ViewX* x : {&qi, &ki, &qo, &ko})
+    if (!view_bytes(*x, e, &span)) return ROPE_ERR_SHAPE;
+  if (__builtin_mul_overflow(B, S, &tokens)) return ROPE_ERR_SHAPE;
+  int64_t pos_bytes = 0, table_bytes = 0;
+  if (d->pos && (__builtin_mul_overflow(B - 1, d->pos_batch_stride, &pos_bytes) ||
+                 __builtin_add_overflow(pos_bytes, S, &pos_bytes) ||
+                 __builtin_mul_overflow(pos_bytes, (int64_t)4, &pos_bytes)))
+    return ROPE_ERR_SHAPE;
+  if (tables && d->table_rows > 0 &&
+      (__builtin_mul_overflow(d->table_rows - 1, t_row, &table_bytes) ||
+       __builtin_add_overflow(table_bytes, (half - 1) * d->table_col_stride + 1, &table_bytes) ||
+       __builtin_mul_overflow(table_bytes, (int64_t)4, &table_bytes)))
+    return ROPE_ERR_SHAPE;
   if (!view_injective(qo) || !view_injective(ko)) return ROPE_ERR_ALIAS;
   if (!views_disjoint(qo, ko, e)) return ROPE_ERR_ALIAS;
   if (!same_view(qo, qi) && !views_disjoint(qo, qi, e)) return ROPE_ERR_ALIAS;
@@ -212,13 +240,10 @@ inline rope_status_t validate_apply(const rope_apply_desc_t* d) {
     }
     return false;
   };
-  if (d->pos && meets_written(d->pos, 4 * ((B - 1) * d->pos_batch_stride + S)))
+  if (d->pos && meets_written(d->pos, pos_bytes)) return ROPE_ERR_ALIAS;
+  if (tables && d->table_rows > 0 &&
+      (meets_written(d->cos, table_bytes) || meets_written(d->sin, table_bytes)))
     return ROPE_ERR_ALIAS;
-  if (tables && d->table_rows > 0) {
-    const int64_t table_bytes = 4 * ((d->table_rows - 1) * t_row + (half - 1) * d->table_col_stride + 1);
-    if (meets_written(d->cos, table_bytes) || meets_written(d->sin, table_bytes))
-      return ROPE_ERR_ALIAS;
-  }
   return ROPE_OK;
 }
 

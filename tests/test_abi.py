@@ -402,3 +402,23 @@ def test_binding_marshals_attention():
         rp.make_attn_desc(q, k, k[:, :1].contiguous(), c, c, o)
     with pytest.raises(ValueError):
         rp.make_attn_desc(q, k, k, c, c, o[:, :, :10])
+
+
+def test_attention_sizes_whose_byte_counts_overflow():
+    # each size within the 32-bit index limit, their product past int64
+    big = 1 << 30
+    assert call_attn(attn_desc(batch=big, n_heads_q=big, n_heads_k=big, seq_len_q=big,
+                               seq_len_k=big, causal=0)) == SHAPE
+    assert call_attn(attn_desc(table_rows=(1 << 62))) == SHAPE
+    # an index batch stride whose extent overflows
+    assert call_attn(attn_desc(q_pos=A16 * 10000, k_pos=A16 * 10100,
+                               q_pos_batch_stride=(1 << 62), k_pos_batch_stride=100)) == SHAPE
+
+
+@pytest.mark.parametrize("change", [
+    dict(q_in=rp.RopeView(A16, 1 << 62, 64, 512)),           # batch stride past int64
+    dict(table_row_stride=1 << 61),                           # table extent past int64
+    dict(pos=A16 * 1000, pos_batch_stride=1 << 62),           # index extent past int64
+])
+def test_apply_extents_that_overflow_are_rejected(change):
+    assert call_apply(apply_desc(**change)) == SHAPE
