@@ -12,21 +12,22 @@
 //
 // Shape of the computation (one workgroup = 8 waves = 256 query rows: 32
 // rows per wave, from hw query heads that share one K/V head, 256 / hw rows
-// of each; each lane owns one query row, two lanes per row):
+// of each; the two lanes l and l + 32 of a wave share one query row):
 //   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16. Each lane's accumulators hold
 //                 its query's scores against 32 of a 64-key tile, so the
 //                 softmax statistics are per lane plus one exchange with the
-//                 partner lane (lane ^ 32).
+//                 partner lane (lane ^ 32, v_permlane32_swap).
 //   O^T += V^T P^T  with the same instruction; the score registers are the
 //                 P^T operand directly, under a fixed permutation of the keys
 //                 inside each 16-key step that V^T's reads follow.
 // Q is loaded and rotated once into the registers of the B operand of S^T.
 // Each 64-key tile of K is rotated once per workgroup, for all its 256 rows,
 // while it is staged into LDS ([key][dim], rows padded by 16 bytes); V is
-// staged transposed ([dim][key], padded) so that the A operand of O^T is two
-// 8-byte LDS reads per lane and step. Tiles are double-buffered: the next
-// tile is fetched before the current one's products and staged into the
-// other buffer after them, with one barrier per tile.
+// staged transposed ([dim][key], padded, keys in v_slot order) so that the A
+// operand of O^T is one 16-byte LDS read per lane and step. Tiles are
+// double-buffered: the next tile is fetched before the current one's
+// products and staged into the other buffer after them, with one barrier per
+// tile.
 // The softmax runs in base 2 with the scale folded into log2(e).
 //
 // Operand layouts of v_mfma_f32_32x32x16_bf16 (checked on the device by a
