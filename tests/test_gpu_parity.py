@@ -468,6 +468,26 @@ def test_apply_matches_contiguous_entry_points_bitwise():
 
 
 @pytest.mark.parametrize("direction", [1, -1])
+def test_one_chunk_per_lane_equals_chunk_pairs_full_size(direction):
+    """In place the Llama prefill call runs the one-chunk-per-lane rows
+    kernel (partner halves exchanged across lanes); out of place the same
+    rows shape runs one chunk pair per lane. Same bits, every element."""
+    w = W.LLAMA_GQA_PREFILL
+    names = ("q", "k") if direction == 1 else ("dq", "dk")
+    t = W.tensors(w, names)
+    cos, sin = gpu_tables(w)
+    say(f"[gpu] {w.name} dir={direction}: one chunk per lane vs chunk pairs")
+    iq, ik = t[names[0]].to(DEV), t[names[1]].to(DEV)
+    rp.rope_apply(iq, ik, cos, sin, layout="bhsd", launch="rows", direction=direction)
+    oq, ok = torch.empty_like(iq), torch.empty_like(ik)
+    rp.rope_apply(t[names[0]].to(DEV), t[names[1]].to(DEV), cos, sin, q_out=oq, k_out=ok,
+                  layout="bhsd", launch="rows", direction=direction)
+    torch.cuda.synchronize()
+    assert torch.equal(iq.view(torch.int16), oq.view(torch.int16))
+    assert torch.equal(ik.view(torch.int16), ok.view(torch.int16))
+
+
+@pytest.mark.parametrize("direction", [1, -1])
 def test_small_tokens_share_a_workgroup(direction):
     """[2, 8192, 2+1, 64] as [B,S,H,D]: 12 lanes per token, so the token shape
     packs 4 consecutive tokens into each workgroup on a 256-CU chip."""
