@@ -244,7 +244,8 @@ rope_status_t rope_apply(const rope_apply_desc_t *d, void *stream);
  *   - causal: key j is visible to query i when j <= i + Sk - Sq (needs
  *     Sq <= Sk). A query with no visible key (Sk = 0) gets zeros; K and V
  *     may then be NULL.
- *   - scale: 0 means 1 / sqrt(head_dim).
+ *   - scale: 0 means 1 / sqrt(head_dim). Any sign; |scale| * log2(e) must
+ *     be a normal float32, and the scaled scores must stay finite in float32.
  * Matrix-core kernel: the products run as bf16 with float32 accumulation and
  * the softmax weights are rounded to bf16 before they multiply V.
  * Limits: head_dim 64 or 128; split-half pairs need R % 32 == 0 and
@@ -278,7 +279,8 @@ typedef struct rope_attn_desc {
 /* Enqueue the fused attention on `stream`. Errors as rope_apply:
  * ROPE_ERR_DTYPE for a dtype other than bf16, ROPE_ERR_SHAPE for sizes
  * outside the limits above (or Hq % Hk != 0, or causal with Sq > Sk, or a
- * non-finite scale, or positions without an index reaching table_rows),
+ * scale that is not finite or whose |scale| * log2(e) is not a normal float32,
+ * or positions without an index reaching table_rows),
  * ROPE_ERR_LAYOUT for an unknown pairing, ROPE_ERR_ALIGN, ROPE_ERR_ALIAS when
  * O overlaps an input. */
 rope_status_t rope_attention_fwd(const rope_attn_desc_t *d, void *stream);

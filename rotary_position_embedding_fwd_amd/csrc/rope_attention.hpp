@@ -25,10 +25,15 @@
 // while it is staged into LDS ([key][dim], rows padded by 16 bytes); V is
 // staged transposed ([dim][key], padded, keys in v_slot order) so that the A
 // operand of O^T is one 16-byte LDS read per lane and step. Tiles are
-// double-buffered: the next tile is fetched before the current one's
-// products and staged into the other buffer after them, with one barrier per
-// tile.
-// The softmax runs in base 2 with the scale folded into log2(e).
+// double-buffered: the next tile is fetched while the current one is worked
+// on and staged into the other buffer after its products, with one barrier
+// per tile.
+// The softmax runs in base 2 with the scale folded into log2(e), one online
+// step per 32-key half of a tile; the halves are software-pipelined so that
+// one half's softmax sits beside the other half's matrix instructions. Each
+// row's reference max moves only when a step's max passes it by more than 8
+// in the base-2 exponent, which keeps the weights below 2^8 and the output
+// rescales rare. A negative scale is taken as |scale| with Q negated.
 //
 // Operand layouts of v_mfma_f32_32x32x16_bf16 (checked on the device by a
 // probe): A (32x16): lane l, slot i holds A[l%32][(l/32)*8 + i]; B (16x32):
@@ -71,7 +76,8 @@ struct AttnArgs {
   int32_t rows;          // query rows of each head per workgroup: kRows / hw
   int32_t head_groups;   // Hq / hw
   int32_t q_tiles;       // ceil(Sq / rows)
-  float scale_log2e;     // softmax scale * log2(e)
+  int32_t negate_q;      // 1: the scale is negative; the scores are taken with -Q
+  float scale_log2e;     // |softmax scale| * log2(e), a normal float
 };
 
 // ------------------------------------------------------------- addresses
@@ -478,6 +484,14 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
     }
   }
 
+  // A negative scale: -Q with |scale|. Negating bf16 is exact and so is
+  // negating every product and partial sum, so the scores are exactly -S.
+  if (a.negate_q) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      qreg[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qreg[s]) ^ 0x80008000u);
+  }
+
   // ---- running softmax state and O^T accumulators (D/32 tiles of 32 dims)
   float m_run = -__builtin_inff(), l_run = 0.0f;
   floatx16 acc[D / 32];
@@ -494,11 +508,10 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
 
   // Tile kt sits in LDS buffer kt & 1 while its products run. The raw K and
   // V rows (and key positions) of tile kt + 1 are fetched into registers
-  // before them, so their memory latency passes under the matrix work, and
-  // are staged into the other buffer after them: that buffer's last readers
-  // (tile kt - 1) all passed the previous barrier, and its next readers wait
-  // for this iteration's barrier. The fetched registers never cross an
-  // iteration.
+  // while tile kt is worked on, and staged into the other buffer after its
+  // products: that buffer's last readers (tile kt - 1) all passed the
+  // previous barrier, and its next readers wait for this iteration's
+  // barrier. The fetched registers never cross an iteration.
   if (n_tiles > 0) {
     KStage<D, PAIR, H16> ks;
     VStage<D> vs;
@@ -510,114 +523,128 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   __syncthreads();
   // a wave whose rows all lie past Sq computes nothing (it still stages)
   const bool live = wq_first < a.seq_q;
+  const float c = a.scale_log2e;
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int k0 = kt * kKeys;
     const int buf = kt & 1;
     const bool more = kt + 1 < n_tiles;
-    KStage<D, PAIR, H16> ks;
-    VStage<D> vs;
-    if (more) {
-      fetch_k<D, PAIR, H16>(a, b, kbase, k0 + kKeys, t, ks);
-      fetch_v<D>(a, vbase, k0 + kKeys, t, vs);
-    }
     // a tile wholly after this wave's causal diagonal adds nothing: its
     // scores are all masked, so the running max, sum and output stay as
     // they are (the wave still stages the next tile and meets the barriers)
-    if (live && (!a.causal || k0 <= wq_last + causal_shift)) {
-      // -- S^T = K Q^T for the two 32-key halves of the tile; each half's
-      // K fragments are read from LDS before its chain of products
-      floatx16 sc[2];
+    const bool work = live && (!a.causal || k0 <= wq_last + causal_shift);
+    // masks only where the tile reaches past Sk or this wave's diagonal
+    const bool edge = k0 + kKeys > a.seq_k || (a.causal && k0 + kKeys - 1 > wq_first + causal_shift);
+
+    // S^T = K Q^T for one 32-key half of the tile: the half's K fragments are
+    // read from LDS, then its chain of products. Lane slot j holds key
+    // half*32 + 8*(j/4) + 4*hs + j%4 of its query row.
+    auto scores = [&](int half) {
+      bf16x8 kf[kSteps];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 kf[kSteps];
+      for (int st = 0; st < kSteps; ++st)
+        kf[st] = *reinterpret_cast<const bf16x8*>(
+            &lds[k_lds<D>(buf, half * 32 + (lane & 31), st * 16 + hs * 8)]);
+      floatx16 sh = {};
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st)
-          kf[st] = *reinterpret_cast<const bf16x8*>(
-              &lds[k_lds<D>(buf, half * 32 + (lane & 31), st * 16 + hs * 8)]);
-        floatx16 sh = {};
+      for (int st = 0; st < kSteps; ++st)
+        sh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qreg[st], sh, 0, 0, 0);
+      return sh;
+    };
+    auto mask = [&](floatx16& sh, int half) {
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st)
-          sh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qreg[st], sh, 0, 0, 0);
-        sc[half] = sh;
-        // keep the reads ahead of the products: all kSteps LDS reads, then
-        // the chain of kSteps matrix instructions
-        __builtin_amdgcn_sched_group_barrier(0x100, kSteps, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, kSteps, 0);
+      for (int j = 0; j < 16; ++j) {
+        const int key = k0 + half * 32 + 8 * (j / 4) + 4 * hs + (j % 4);
+        const bool vis = key < a.seq_k && (!a.causal || key <= qi + causal_shift);
+        if (!vis) sh[j] = -__builtin_inff();
       }
-      // -- mask (only where the tile reaches past Sk or this wave's causal
-      // diagonal), then the online softmax in base 2 on the raw scores: the
-      // running max m is kept unscaled and each weight is
-      // exp2(s * scale_log2e - m * scale_log2e), one fused multiply-add
-      const bool edge = k0 + kKeys > a.seq_k || (a.causal && k0 + kKeys - 1 > wq_first + causal_shift);
-      if (edge) {
+    };
+    // Online softmax over one 32-key half, in base 2 on the raw scores: each
+    // weight is exp2(s * c - m * c), one fused multiply-add, with m the
+    // row's reference max. m moves to the half's max only when that passes
+    // it by more than 8 in the base-2 exponent, so weights stay below 2^8
+    // and the output is rarely rescaled. Returns the rescale factor; the
+    // weights come back as bf16, two 16-key k-steps.
+    auto softmax = [&](floatx16& sh, bf16x8* pb) {
+      float m_t = -__builtin_inff();
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + half * 32 + 8 * (j / 4) + 4 * hs + (j % 4);
-            const bool vis = key < a.seq_k && (!a.causal || key <= qi + causal_shift);
-            if (!vis) sc[half][j] = -__builtin_inff();
-          }
-      }
-      float m_tile = -__builtin_inff();
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) m_tile = fmaxf(m_tile, sc[half][j]);
-      m_tile = wave_max32(m_tile);
-      const float m_new = fmaxf(m_run, m_tile);
-      const float c = a.scale_log2e;
-      const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      // an all-masked row so far (m_new = -inf) keeps weights 0
+      for (int j = 0; j < 16; ++j) m_t = fmaxf(m_t, sh[j]);
+      m_t = wave_max32(m_t);
+      // false when both are -inf (a row with no visible key so far)
+      const bool move = (m_t - m_run) * c > 8.0f;
+      const float m_new = move ? m_t : m_run;
+      const float alpha = move ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+      // a row with no visible key so far (m_new = -inf) keeps weights 0
       const float mc = m_new == -__builtin_inff() ? 0.0f : m_new * c;
-      float l_tile = 0.0f;
+      float l_t = 0.0f;
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int j = 0; j < 16; ++j) {
+        const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[j], c, -mc));
+        sh[j] = pj;
+        l_t += pj;
+      }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half][j], c, -mc));
-          sc[half][j] = pj;
-          l_tile += pj;
-        }
-      l_tile = wave_sum32(l_tile);
-      l_run = l_run * alpha + l_tile;
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[u][i] = from_f32<__bf16>(sh[8 * u + i]);
+      l_t = wave_sum32(l_t);
+      l_run = l_run * alpha + l_t;
       m_run = m_new;
-      // rescale the output only when some lane's max moved
+      return alpha;
+    };
+    // rescale the output only when some lane's reference max moved
+    auto rescale = [&](float alpha) {
       if (__ballot(alpha != 1.0f)) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i)
 #pragma unroll
           for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
       }
-
-      // -- O^T += V^T P^T: k-steps of 16 keys; step (half, u) covers keys
-      // half*32 + 16u .. +15, lane's slots j = 8u .. 8u+7 of sc[half], which
-      // hold keys 16u + 8*(i/4) + 4*hs + i%4 for slot i. Each step's V^T
-      // fragments are read before its products.
+    };
+    // O^T += V^T P^T over one half: k-step u covers keys half*32 + 16u ..
+    // +15, the lane's weights pb[u] (slots 8u .. 8u+7 of its scores, keys
+    // 16u + 8*(i/4) + 4*hs + i%4), against V^T slots half*32 + 16u + 8hs ..
+    // +7, which hold the same keys in that order. Each step's V^T fragments
+    // are read before its products.
+    auto output = [&](int half, const bf16x8* pb) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int u = 0; u < 2; ++u) {
+        const int slot = half * 32 + 16 * u + 8 * hs;
+        u32x4 va[D / 32];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8 pb;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pb[i] = from_f32<__bf16>(sc[half][8 * u + i]);
-          // keys 16u + 4hs .. +3 and 16u + 8 + 4hs .. +3 of this half: V^T
-          // slots half*32 + 16u + 8hs .. +7
-          const int slot = half * 32 + 16 * u + 8 * hs;
-          u32x4 va[D / 32];
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const int dim = dt * 32 + (lane & 31);
-            va[dt] = *reinterpret_cast<const u32x4*>(&lds[v_lds<D>(buf, dim, slot)]);
-          }
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, va[dt]), pb, acc[dt], 0, 0, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int dim = dt * 32 + (lane & 31);
+          va[dt] = *reinterpret_cast<const u32x4*>(&lds[v_lds<D>(buf, dim, slot)]);
         }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, va[dt]), pb[u], acc[dt], 0, 0, 0);
+      }
+    };
 
+    // The two halves are software-pipelined: the second half's score
+    // products run beside the first half's softmax, and the first half's
+    // output products beside the second half's softmax. The next tile's
+    // fetch is issued between the two, after the score products.
+    floatx16 s0, s1;
+    bf16x8 p0[2], p1[2];
+    if (work) {
+      s0 = scores(0);
+      if (edge) mask(s0, 0);
+      s1 = scores(1);
+      rescale(softmax(s0, p0));
+      if (edge) mask(s1, 1);
+    }
+    KStage<D, PAIR, H16> ks;
+    VStage<D> vs;
+    if (more) {
+      fetch_k<D, PAIR, H16>(a, b, kbase, k0 + kKeys, t, ks);
+      fetch_v<D>(a, vbase, k0 + kKeys, t, vs);
+    }
+    if (work) {
+      output(0, p0);
+      rescale(softmax(s1, p1));
+      output(1, p1);
     }
     if (more) {
       stage_k<D, PAIR, H16>(a, t, ks, lds, buf ^ 1);

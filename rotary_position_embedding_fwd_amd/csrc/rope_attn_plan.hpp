@@ -4,6 +4,7 @@
 
 #include <stdint.h>
 
+#include <cfloat>
 #include <cmath>
 
 #include "librope.h"
@@ -42,6 +43,11 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   if (d->pairing == ROPE_SPLIT_HALF ? (R % 32) : (R % 8)) return ROPE_ERR_SHAPE;
   if (d->causal && Sq > Sk) return ROPE_ERR_SHAPE;
   if (!std::isfinite(d->scale) || d->table_rows < 0) return ROPE_ERR_SHAPE;
+  // the kernel works with |scale| * log2(e) as a normal float32 (a negative
+  // scale enters as a sign flip of Q)
+  const double scale = d->scale != 0.0 ? d->scale : 1.0 / std::sqrt((double)D);
+  const float scale_log2e = (float)(std::fabs(scale) * 1.4426950408889634);  // log2(e)
+  if (!(scale_log2e >= FLT_MIN && scale_log2e <= FLT_MAX)) return ROPE_ERR_SHAPE;
   if (d->q_pos_batch_stride < 0 || d->k_pos_batch_stride < 0) return ROPE_ERR_SHAPE;
   // 32-bit index arithmetic inside the kernel
   const int64_t lim = (int64_t)1 << 30;
@@ -112,8 +118,8 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   a.rows = kRows / hw;
   a.head_groups = (int32_t)(Hq / hw);
   a.q_tiles = (int32_t)((Sq + a.rows - 1) / a.rows);
-  const double scale = d->scale != 0.0 ? d->scale : 1.0 / std::sqrt((double)D);
-  a.scale_log2e = (float)(scale * 1.4426950408889634);  // log2(e)
+  a.scale_log2e = scale_log2e;
+  a.negate_q = scale < 0.0;
   pl->grid = (int64_t)a.q_tiles * a.head_groups * B;
   if (pl->grid > 0x7fffffff) return ROPE_ERR_SHAPE;
   pl->head_dim = (int)D;

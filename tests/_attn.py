@@ -16,11 +16,13 @@ arithmetic, element by element, built from oracle results only:
      moves by at most eps_i, every weight moves by a factor within
      exp(+-2 eps_i), so the output moves by at most (exp(2 eps_i) - 1) * A.
   3. float32 running sums over Sk keys (weights, output accumulators and the
-     rescales between key tiles): 2 (Sk + 128) 2^-24 * A; and the rescale
-     factor exp2((m_old - m_new) * scale log2 e) applied at up to one key tile
-     in each of the ceil(Sk / 64), each off by its argument's rounding and
-     exp2's error, which adds ceil(Sk / 64) * ln2 * (2^-23 |x|max + 2^-22) to
-     eps_i.
+     rescales between key steps): 2 (Sk + 128) 2^-24 * A; and the rescale
+     factor exp2((m_old - m_new) * |scale| log2 e), applied at most once per
+     32-key step (the kernel moves its reference max only when the new max
+     passes it by more than 8 in the base-2 exponent, so the weights stay
+     below 2^8; a bf16 weight's relative rounding does not depend on its
+     size), each off by its argument's rounding and exp2's error, which adds
+     ceil(Sk / 32) * ln2 * (2^-23 |x|max + 2^-22) to eps_i.
   4. The final rounding of O to bf16: u * |O|.
 """
 from __future__ import annotations
@@ -103,6 +105,7 @@ def reference(q, k, v, cos: Optional[np.ndarray], sin: Optional[np.ndarray], *,
     R = 0 if not rotate else (D if rotary_dim is None else rotary_dim)
     rows = 0 if cos is None else cos.shape[0]
     sc = 1.0 / np.sqrt(D) if not scale else scale
+    asc = abs(sc)
     qp = _positions(q_pos, B, Sq, Sk - Sq)
     kp = _positions(k_pos, B, Sk, 0)
     qp32 = np.ascontiguousarray(qp, dtype=np.int32)
@@ -138,12 +141,12 @@ def reference(q, k, v, cos: Optional[np.ndarray], sin: Optional[np.ndarray], *,
             K, dK = kr[b, h // group], dk[b, h // group]
             aq, ak = np.abs(Q), np.abs(K)
             e = dQ @ (ak + dK).T + aq @ dK.T + gamma * (aq @ ak.T)
-            s = np.abs(Q @ K.T) * sc * log2e
-            e = sc * e + np.log(2.0) * (2.0 ** -22 * s + 2.0 ** -21)
+            s = np.abs(Q @ K.T) * asc * log2e
+            e = asc * e + np.log(2.0) * (2.0 ** -22 * s + 2.0 ** -21)
             e = np.where(visible, e, 0.0)
             if Sk:
                 xmax = np.where(visible, s, 0.0).max(axis=1)
-                rescale = -(-Sk // 64) * np.log(2.0) * (2.0 ** -23 * xmax + 2.0 ** -22)
+                rescale = -(-Sk // 32) * np.log(2.0) * (2.0 ** -23 * xmax + 2.0 ** -22)
                 eps[b, h] = e.max(axis=1) + rescale
     grow = np.exp(2.0 * eps)[..., None]
     pre = a_abs * grow * (U16 + 2.0 * (Sk + 128) * 2.0 ** -24) + (grow - 1.0) * a_abs

@@ -323,6 +323,8 @@ def call_attn(d):
     (dict(seq_len_q=101), SHAPE),                     # causal needs Sq <= Sk
     (dict(table_rows=99), SHAPE),                     # default positions leave the table
     (dict(scale=float("nan")), SHAPE), (dict(scale=float("inf")), SHAPE),
+    (dict(scale=1e-40), SHAPE), (dict(scale=-1e-45), SHAPE),   # |scale| log2 e not normal
+    (dict(scale=1e39), SHAPE), (dict(scale=-1e300), SHAPE),    # ... or past float32
     (dict(batch=-1), SHAPE), (dict(q_pos_batch_stride=-1), SHAPE),
     (dict(q=None), NULL), (dict(o=None), NULL), (dict(v=None), NULL), (dict(cos=None), NULL),
     (dict(q=A16 * 1024 + 2), ALIGN), (dict(o=A16 * 4096 + 8), ALIGN),
@@ -356,6 +358,7 @@ def test_attention_empty_and_null():
     dict(q_pos=A16 * 10000, k_pos=A16 * 10100, q_pos_batch_stride=100, k_pos_batch_stride=100,
          table_rows=4),                                  # index positions: any table size
     dict(cos=A16 * 1024, sin=A16 * 1024 + 64),           # tables may share memory with inputs
+    dict(scale=-0.125), dict(scale=1e-30),               # any sign; small but normal
 ])
 def test_attention_accepts_valid_descriptors(change):
     rc = call_attn(attn_desc(**change))

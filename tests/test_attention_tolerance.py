@@ -2,9 +2,10 @@
 
 Two directions:
   - a numerical model of the kernel's arithmetic (float32 scores, online
-    softmax over 64-key tiles in base 2, weights rounded to bf16 before they
-    multiply V, float32 accumulation, bf16 output), written here in numpy
-    from that description, stays inside the bound;
+    softmax over 32-key steps in base 2 whose reference max moves only when
+    a step's max passes it by more than 8, weights rounded to bf16 before
+    they multiply V, float32 accumulation, bf16 output), written here in
+    numpy from that description, stays inside the bound;
   - mistakes planted in the oracle (a key dropped, the causal diagonal moved
     by one, the wrong pairing, positions off by one, K left unrotated, the
     wrong K/V head for a query head) land outside it.
@@ -29,7 +30,8 @@ def _bf16(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy()
 
 
-def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k_pos=None):
+def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k_pos=None,
+                  scale=None):
     """The kernel's arithmetic in numpy float32 (see the module docstring)."""
     qs, ks, vs = (oracle.torch_to_storage(t) for t in (q, k, v))
     B, Hq, Sq, D = qs.shape
@@ -41,7 +43,7 @@ def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k
     kr = A.bf16_values(oracle.rope(ks, "bf16", pairing=pairing, rotary_dim=R, theta=theta,
                                    pos=kp, pos_batch_stride=Sk, table_rows=cos.shape[0]))
     vv = A.bf16_values(vs).astype(np.float32)
-    c = np.float32(1.0 / np.sqrt(D) * 1.4426950408889634)
+    c = np.float32((1.0 / np.sqrt(D) if scale is None else scale) * 1.4426950408889634)
     out = np.zeros((B, Hq, Sq, D), np.float64)
     g = Hq // Hk
     for b in range(B):
@@ -52,13 +54,16 @@ def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k
             m = np.full(Sq, -np.inf, np.float32)
             l = np.zeros(Sq, np.float32)
             acc = np.zeros((Sq, D), np.float32)
-            for k0 in range(0, Sk, 64):
-                kk = np.arange(k0, min(k0 + 64, Sk))
+            for k0 in range(0, Sk, 32):
+                kk = np.arange(k0, min(k0 + 32, Sk))
                 x = (Q @ K[kk].T) * c
                 if causal:
                     x = np.where(kk[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq), x, -np.inf)
-                m_new = np.maximum(m, x.max(axis=1))
-                alpha = np.where(m_new == m, np.float32(1), np.exp2(m - m_new)).astype(np.float32)
+                m_t = x.max(axis=1)
+                with np.errstate(invalid="ignore"):
+                    move = m_t - m > 8
+                m_new = np.where(move, m_t, m).astype(np.float32)
+                alpha = np.where(move, np.exp2(m - m_new), np.float32(1)).astype(np.float32)
                 p = np.where(np.isneginf(x), np.float32(0), np.exp2(x - m_new[:, None]))
                 p = p.astype(np.float32)
                 l = l * alpha + p.sum(axis=1, dtype=np.float32)
@@ -90,6 +95,21 @@ def test_kernel_model_inside_bound(orc, case):
     # the bound is not vacuous: well under the size of the outputs
     assert np.median(tol) < 0.02 * np.median(np.abs(A.bf16_values(
         oracle.torch_to_storage(v)))) + 0.01
+
+
+@pytest.mark.parametrize("scale", [-0.3, 2.0, -2.0])
+def test_kernel_model_inside_bound_any_scale(orc, scale):
+    # large |scale|: the row max jumps by more than 8 in the base-2 exponent
+    # between many 32-key steps, so the model rescales often; negative: the
+    # softmax of -|scale| S
+    B, Hq, Hk, Sq, Sk, D, R = 1, 2, 1, 100, 300, 64, 64
+    q, k, v = _inputs(B, Hq, Hk, Sq, Sk, D, 7200)
+    cos, sin = oracle.table(10000.0, R, Sk)
+    ref, tol = A.reference(q, k, v, cos, sin, rotary_dim=R, causal=True, scale=scale)
+    got = _kernel_model(q, k, v, cos, sin, pairing="split_half", R=R, theta=10000.0,
+                        causal=True, scale=scale)
+    err = np.abs(got - ref)
+    assert (err <= tol).all(), float((err / tol).max())
 
 
 def _mutant_violates(ref, tol, mut, min_frac=0.01):

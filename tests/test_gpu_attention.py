@@ -209,3 +209,19 @@ def test_explicit_scale_matches_oracle():
     got = run(q, k, v, gt, rotary_dim=R, causal=True, scale=0.3)
     ref, tol = A.reference(q, k, v, *ot, rotary_dim=R, causal=True, scale=0.3)
     A.check(got, ref, tol, "explicit scale")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 2.0, -2.0, 1e-3])
+def test_any_scale_matches_oracle(scale):
+    # negative: the softmax of -|scale| S (the kernel takes -Q); |scale| 2:
+    # the row max jumps by more than 8 in the base-2 exponent between many
+    # 32-key steps, so the output is rescaled often, and weights far below
+    # the max underflow to 0; 1e-3: nearly uniform weights, the reference max
+    # never moves after the first step
+    B, Hq, Hk, Sq, Sk, D, R = 1, 4, 2, 150, 300, 128, 128
+    say(f"scale {scale}")
+    q, k, v = inputs(B, Hq, Hk, Sq, Sk, D, 8950)
+    gt, ot = tables(Sk, R)
+    got = run(q, k, v, gt, rotary_dim=R, causal=True, scale=scale)
+    ref, tol = A.reference(q, k, v, *ot, rotary_dim=R, causal=True, scale=scale)
+    A.check(got, ref, tol, f"scale {scale}")
