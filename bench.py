@@ -515,21 +515,23 @@ def time_layout_matrix(reps: int = 400):
             torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, host, pos):
-    """The CPU oracle, as it stands, on one full step (fwd + bwd) of w, 1 thread."""
+def cpu_baseline(w, host, pos, steps: int = 2):
+    """The CPU oracle, as it stands, on `steps` full steps (fwd + bwd) of w,
+    1 thread: about 10 s of CPU work on the Llama prefill workload."""
     import oracle
     orc = oracle
     orc.load()
-    nbytes = 2 * algorithmic_bytes(w, pos)
+    nbytes = steps * 2 * algorithmic_bytes(w, pos)
     kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, theta=w.theta,
               pos=None if pos is None else pos.numpy(), pos_batch_stride=w.pos_batch_stride,
               table_rows=w.table_rows)
     arrs = {k: orc.torch_to_storage(v) for k, v in host.items()}
     t0 = time.perf_counter()
-    orc.rope(arrs["q"], w.dtype, direction=1, **kw)
-    orc.rope(arrs["k"], w.dtype, direction=1, **kw)
-    orc.rope(arrs["dq"], w.dtype, direction=-1, **kw)
-    orc.rope(arrs["dk"], w.dtype, direction=-1, **kw)
+    for _ in range(steps):
+        orc.rope(arrs["q"], w.dtype, direction=1, **kw)
+        orc.rope(arrs["k"], w.dtype, direction=1, **kw)
+        orc.rope(arrs["dq"], w.dtype, direction=-1, **kw)
+        orc.rope(arrs["dk"], w.dtype, direction=-1, **kw)
     dt = time.perf_counter() - t0
     cpu_model = ""
     try:
@@ -542,7 +544,7 @@ def cpu_baseline(w, host, pos):
         pass
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"one full step (fwd of Q,K + bwd of dQ,dK) of {w.name}, "
+            "sample": f"{steps} full steps (fwd of Q,K + bwd of dQ,dK) of {w.name}, "
                       f"single-threaded scalar binary64 oracle",
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model}
 
