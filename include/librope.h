@@ -228,6 +228,44 @@ typedef struct rope_apply_desc {
  * or sin is not 16-byte aligned, or pos is not 4-byte aligned. */
 rope_status_t rope_apply(const rope_apply_desc_t *d, void *stream);
 
+/* ------------------------------------------------------ XPOS scaling
+ * rope_apply with XPOS scaling (rotary-embedding-torch docs, Key Parameters:
+ * `use_xpos`, Extrapolatable Positional Encoding for length extrapolation).
+ * After the rotation, both elements of pair i of a query row at position p
+ * are multiplied by xpos_q[p*row + i*col] and those of a key row by
+ * xpos_k[...], with row/col the table strides of cos and sin; for the xPos
+ * paper's scales these hold zeta_i^e and zeta_i^-e (rope_build_xpos_table),
+ * so a query at n and a key at m meet with the factor zeta_i^((n-m)/B). The
+ * pages name XPOS without its formula; the one used is the xPos paper's
+ * (Sun et al., "A Length-Extrapolatable Transformer", ACL 2023).
+ *   - y = RN32(RN32(rotation) * factor), then rounded to the dtype; the
+ *     rotation is rope_apply's. A factor does not change within a pair, so
+ *     it commutes with the rotation: direction = -1 (the backward) uses the
+ *     same tables.
+ *   - d as for rope_apply, with angles = ROPE_ANGLES_TABLE and launch =
+ *     ROPE_LAUNCH_AUTO (ROPE_ERR_LAYOUT otherwise). xpos_q / xpos_k: device
+ *     float32, 4-byte aligned, laid out like cos and sin; NULL only when
+ *     there are no Q (resp. K) heads. A skipped token (index out of the
+ *     table) is not scaled either.
+ * Errors as rope_apply, and ROPE_ERR_NULL / ROPE_ERR_ALIGN / ROPE_ERR_ALIAS
+ * for the factor tables (a written view may not overlap them). */
+rope_status_t rope_apply_xpos(const rope_apply_desc_t *d, const float *xpos_q,
+                              const float *xpos_k, void *stream);
+
+/* Fill host float32 tables xpos_q / xpos_k, each [table_rows, R/2] row-major:
+ * row p, column i holds zeta_i^e and zeta_i^-e with
+ * zeta_i = (2i/R + gamma) / (1 + gamma) and e = (p - center) / scale_base,
+ * formed in binary64 and rounded once to float32 (the xPos paper uses
+ * gamma = 0.4, scale_base = 512; center 0 gives its exponent p / B, and a
+ * center near the middle of the positions keeps both tables in range for
+ * long sequences). Host memory, caller-owned. ROPE_ERR_SHAPE for a negative
+ * size, an odd rotary_dim, or a scale_base or gamma that is not finite and
+ * > 0, or a center that is not finite; ROPE_ERR_NULL for NULL outputs with
+ * non-empty work. */
+rope_status_t rope_build_xpos_table(float *xpos_q, float *xpos_k, int64_t table_rows,
+                                    int64_t rotary_dim, double scale_base, double gamma,
+                                    double center);
+
 /* ---------------------------------------------- attention with RoPE fused
  * Attention whose Q and K are rotated inside the kernel, on the blocks it
  * loads, so no rotated Q or K is written to memory (rotary-embedding-torch

@@ -65,6 +65,18 @@ def _bind(lib):
                                           _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                           ctypes.c_double, ctypes.c_double, _P, _I64, _P, _I64,
                                           _I64, ctypes.c_int, ctypes.c_double]
+    lib.oracle_xpos_zeta.restype = ctypes.c_double
+    lib.oracle_xpos_zeta.argtypes = [ctypes.c_double, _I64, _I64]
+    lib.oracle_xpos_table.restype = None
+    lib.oracle_xpos_table.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, _I64,
+                                      _I64, _P, _P]
+    xpos_args = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                 _I64, _I64, _I64, _I64, _I64, ctypes.c_double, ctypes.c_double, _P, _I64,
+                 _I64, ctypes.c_double, ctypes.c_double, ctypes.c_double]
+    lib.oracle_rope_xpos.restype = ctypes.c_int
+    lib.oracle_rope_xpos.argtypes = [_P, _P, ctypes.c_int] + xpos_args
+    lib.oracle_rope_xpos_exact.restype = ctypes.c_int
+    lib.oracle_rope_xpos_exact.argtypes = [_P, _P] + xpos_args
     lib.oracle_to_bf16_bits.restype = ctypes.c_uint16
     lib.oracle_to_bf16_bits.argtypes = [ctypes.c_double]
     lib.oracle_to_f16_bits.restype = ctypes.c_uint16
@@ -170,6 +182,69 @@ def rope_exact(x: np.ndarray, *, layout: str = "bhsd", pairing: str = "split_hal
                                            pos_batch_stride, rows)
     if rc:
         raise OracleError(f"oracle_rope_exact rejected its arguments (code {rc})")
+    return y
+
+
+def xpos_zeta(gamma: float, rotary_dim: int, i: int, lib=None) -> float:
+    """zeta_i = (i / (R/2) + gamma) / (1 + gamma) in binary64 (xPos)."""
+    return (lib or load()).oracle_xpos_zeta(gamma, rotary_dim, i)
+
+
+def xpos_table(rotary_dim: int, rows: int, scale_base: float = 512.0, gamma: float = 0.4,
+               center: float = 0.0, lib=None):
+    """The oracle's own fp32 XPOS factor tables (query, key), each [rows, R/2]:
+    row p holds zeta_i^((p - center)/B) and its reciprocal power."""
+    half = rotary_dim // 2
+    zq = np.empty((rows, half), np.float32)
+    zk = np.empty((rows, half), np.float32)
+    (lib or load()).oracle_xpos_table(scale_base, gamma, center, rotary_dim, rows, _ptr(zq),
+                                      _ptr(zk))
+    return zq, zk
+
+
+def rope_xpos(x: np.ndarray, dtype: str, *, is_key: bool, layout: str = "bhsd",
+              pairing: str = "split_half", direction: int = 1,
+              rotary_dim: Optional[int] = None, theta: float = 10000.0, pos=None,
+              pos_batch_stride: int = 0, table_rows: Optional[int] = None,
+              interpolate_factor: float = 1.0, scale_base: float = 512.0, gamma: float = 0.4,
+              center: float = 0.0, lib=None) -> np.ndarray:
+    """Table-mode RoPE with XPOS factors (query rows, or key rows when
+    is_key) of storage array `x`. Returns a new array."""
+    x = np.ascontiguousarray(x, dtype=NP_STORAGE[dtype])
+    B, H, S, D = _dims(x.shape, layout)
+    R = D if rotary_dim is None else rotary_dim
+    rows = S if table_rows is None else table_rows
+    p = _pos_arr(pos)
+    y = np.empty_like(x)
+    rc = (lib or load()).oracle_rope_xpos(_ptr(x), _ptr(y), DTYPES[dtype], LAYOUTS[layout],
+                                          PAIRINGS[pairing], direction, int(is_key), B, H, S,
+                                          D, R, theta, interpolate_factor, _ptr(p),
+                                          pos_batch_stride, rows, scale_base, gamma, center)
+    if rc:
+        raise OracleError(f"oracle_rope_xpos rejected its arguments (code {rc})")
+    return y
+
+
+def rope_xpos_exact(x: np.ndarray, *, is_key: bool, layout: str = "bhsd",
+                    pairing: str = "split_half", direction: int = 1,
+                    rotary_dim: Optional[int] = None, theta: float = 10000.0, pos=None,
+                    pos_batch_stride: int = 0, table_rows: Optional[int] = None,
+                    interpolate_factor: float = 1.0, scale_base: float = 512.0,
+                    gamma: float = 0.4, center: float = 0.0, lib=None) -> np.ndarray:
+    """Exact-mode RoPE with XPOS factors in binary64, for invariant checks."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    B, H, S, D = _dims(x.shape, layout)
+    R = D if rotary_dim is None else rotary_dim
+    rows = S if table_rows is None else table_rows
+    p = _pos_arr(pos)
+    y = np.empty_like(x)
+    rc = (lib or load()).oracle_rope_xpos_exact(_ptr(x), _ptr(y), LAYOUTS[layout],
+                                                PAIRINGS[pairing], direction, int(is_key), B,
+                                                H, S, D, R, theta, interpolate_factor,
+                                                _ptr(p), pos_batch_stride, rows, scale_base,
+                                                gamma, center)
+    if rc:
+        raise OracleError(f"oracle_rope_xpos_exact rejected its arguments (code {rc})")
     return y
 
 

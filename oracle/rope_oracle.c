@@ -285,6 +285,113 @@ int oracle_rope_exact(const double *x, double *y, int layout, int pairing, int d
 }
 
 /*
+ * XPOS scaling (rotary-embedding-torch docs, Key Parameters: `use_xpos`,
+ * Extrapolatable Positional Encoding). The pages name the option and nothing
+ * more; its definition is the xPos paper's (Sun et al., "A
+ * Length-Extrapolatable Transformer", ACL 2023): after the rotation, pair i
+ * of a query at position n is scaled by zeta_i^(n/B) and pair i of a key at m
+ * by zeta_i^(-m/B), with zeta_i = (i / (R/2) + gamma) / (1 + gamma), so the
+ * query-key product of that pair carries zeta_i^((n - m)/B), a decay in the
+ * relative distance. Positions are taken relative to `center` (n - center).
+ *
+ * Table contract, as for cos/sin: each factor is rounded once to float32;
+ * the output is (x1*c32 - s*x2*s32) * z32 evaluated in binary64 and rounded
+ * once into the storage dtype.
+ */
+double oracle_xpos_zeta(double gamma, int64_t rotary_dim, int64_t i) {
+  return ((double)i / ((double)rotary_dim / 2.0) + gamma) / (1.0 + gamma);
+}
+
+/* The factor of pair i at position p: zeta_i^((p - center)/B) for a query row,
+ * the reciprocal power for a key row (binary64, unrounded). */
+static double xpos_factor(double scale_base, double gamma, double center, int64_t rotary_dim,
+                          int64_t p, int64_t i, int is_key) {
+  double e = ((double)p - center) / scale_base;
+  return pow(oracle_xpos_zeta(gamma, rotary_dim, i), is_key ? -e : e);
+}
+
+/* [rows, R/2] float32 factor tables for query and key rows. */
+void oracle_xpos_table(double scale_base, double gamma, double center, int64_t rotary_dim,
+                       int64_t rows, float *zq_out, float *zk_out) {
+  int64_t half = rotary_dim / 2;
+  for (int64_t p = 0; p < rows; ++p)
+    for (int64_t i = 0; i < half; ++i) {
+      zq_out[p * half + i] = (float)xpos_factor(scale_base, gamma, center, rotary_dim, p, i, 0);
+      zk_out[p * half + i] = (float)xpos_factor(scale_base, gamma, center, rotary_dim, p, i, 1);
+    }
+}
+
+static int check_xpos(double scale_base, double gamma, double center) {
+  if (!(scale_base > 0.0) || !isfinite(scale_base)) return -2;
+  if (!(gamma > 0.0) || !isfinite(gamma) || !isfinite(center)) return -2;
+  return 0;
+}
+
+/* Table mode with XPOS factors; is_key selects the key rows' factors. */
+int oracle_rope_xpos(const void *x, void *y, int dtype, int layout, int pairing, int direction,
+                     int is_key, int64_t B, int64_t H, int64_t S, int64_t D, int64_t R,
+                     double theta, double interp, const int32_t *pos, int64_t pos_batch_stride,
+                     int64_t table_rows, double scale_base, double gamma, double center) {
+  int rc = check_args(dtype, layout, pairing, direction, B, H, S, D, R, table_rows, pos,
+                      interp);
+  if (!rc) rc = check_xpos(scale_base, gamma, center);
+  if (rc) return rc;
+  int64_t es = elem_size(dtype);
+  if (x != y) memcpy(y, x, (size_t)(B * H * S * D * es)); /* untouched lanes */
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t s = 0; s < S; ++s) {
+        int64_t p = token_position(pos, pos_batch_stride, table_rows, b, s);
+        if (p < 0) continue; /* skipped token: neither rotated nor scaled */
+        int64_t row = row_offset(layout, H, S, D, b, h, s);
+        for (int64_t i = 0; i < R / 2; ++i) {
+          float c32, s32;
+          oracle_table_entry(theta, interp, R, p, i, &c32, &s32);
+          double z = (float)xpos_factor(scale_base, gamma, center, R, p, i, is_key);
+          double c = c32, sn = (double)direction * (double)s32;
+          int64_t j1, j2;
+          pair_dims(pairing, R, i, &j1, &j2);
+          double x1 = load_elem(x, row + j1, dtype);
+          double x2 = load_elem(x, row + j2, dtype);
+          store_elem(y, row + j1, dtype, (x1 * c - x2 * sn) * z);
+          store_elem(y, row + j2, dtype, (x1 * sn + x2 * c) * z);
+        }
+      }
+  return 0;
+}
+
+/* Exact mode with XPOS: binary64 in and out, unrounded cos, sin and factors. */
+int oracle_rope_xpos_exact(const double *x, double *y, int layout, int pairing, int direction,
+                           int is_key, int64_t B, int64_t H, int64_t S, int64_t D, int64_t R,
+                           double theta, double interp, const int32_t *pos,
+                           int64_t pos_batch_stride, int64_t table_rows, double scale_base,
+                           double gamma, double center) {
+  int rc = check_args(ORC_F32, layout, pairing, direction, B, H, S, D, R, table_rows, pos,
+                      interp);
+  if (!rc) rc = check_xpos(scale_base, gamma, center);
+  if (rc) return rc;
+  if (x != y) memcpy(y, x, (size_t)(B * H * S * D) * sizeof(double));
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t s = 0; s < S; ++s) {
+        int64_t p = token_position(pos, pos_batch_stride, table_rows, b, s);
+        if (p < 0) continue;
+        int64_t row = row_offset(layout, H, S, D, b, h, s);
+        for (int64_t i = 0; i < R / 2; ++i) {
+          double angle = angle_of(theta, interp, R, p, i);
+          double c = cos(angle), sn = (double)direction * sin(angle);
+          double z = xpos_factor(scale_base, gamma, center, R, p, i, is_key);
+          int64_t j1, j2;
+          pair_dims(pairing, R, i, &j1, &j2);
+          double x1 = y[row + j1], x2 = y[row + j2];
+          y[row + j1] = (x1 * c - x2 * sn) * z;
+          y[row + j2] = (x1 * sn + x2 * c) * z;
+        }
+      }
+  return 0;
+}
+
+/*
  * Attention with RoPE applied to the loaded Q and K (rotary-embedding-torch
  * docs, flash_attn_with_rotary: the rotation is applied to Q and K inside the
  * attention computation instead of as a separate pass; GQA repeats the K/V

@@ -135,6 +135,11 @@ def lib():
         L.rope_build_table.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                        ctypes.c_double]
         L.rope_build_table.restype = ctypes.c_int
+        L.rope_apply_xpos.argtypes = [ctypes.POINTER(RopeApplyDesc), P, P, P]
+        L.rope_apply_xpos.restype = ctypes.c_int
+        L.rope_build_xpos_table.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        L.rope_build_xpos_table.restype = ctypes.c_int
         L.rope_attention_fwd.argtypes = [ctypes.POINTER(RopeAttnDesc), P]
         L.rope_attention_fwd.restype = ctypes.c_int
         L.rope_status_string.argtypes = [ctypes.c_int]
@@ -385,6 +390,35 @@ def rope_apply(q, k, cos, sin, *, stream=None, **kw):
     return (q if qo is None else qo), (k if ko is None else ko)
 
 
+def _xpos_ptrs(xpos_q, xpos_k, cos):
+    import torch
+    out = []
+    for name, z in (("xpos_q", xpos_q), ("xpos_k", xpos_k)):
+        if z is None:
+            out.append(None)
+            continue
+        if z.dtype != torch.float32 or z.shape != cos.shape or z.stride() != cos.stride():
+            raise ValueError(f"{name} must be a float32 table laid out like cos")
+        out.append(z.data_ptr())
+    return out
+
+
+def rope_apply_xpos(q, k, cos, sin, xpos_q, xpos_k, *, stream=None, **kw):
+    """rope_apply with XPOS factors: after the rotation, pair i of a query row
+    at position p is multiplied by xpos_q[p, i], of a key row by xpos_k[p, i]
+    (tables laid out like cos and sin, e.g. from rope_build_xpos_table).
+    Same keywords as rope_apply, tables only (no theta). Returns the tensors
+    that hold the result."""
+    if kw.get("theta") is not None:
+        raise ValueError("XPOS factors come with cos/sin tables, not theta")
+    d = make_apply_desc(q, k, cos, sin, **kw)
+    zq, zk = _xpos_ptrs(xpos_q, xpos_k, cos)
+    _check(lib().rope_apply_xpos(ctypes.byref(d), zq, zk, _stream(stream)), "rope_apply_xpos")
+    qo = kw.get("q_out")
+    ko = kw.get("k_out")
+    return (q if qo is None else qo), (k if ko is None else ko)
+
+
 class Prepared:
     """A call whose descriptor is built once: for loops that issue the same
     rotation many times (benchmarks, decode steps). Holds the tensors alive;
@@ -410,6 +444,31 @@ class Prepared:
 
     def rope_bwd_q(self):
         _check(self._lib.rope_bwd_q(self._q, self._pdesc, self._stream), "rope_bwd_q")
+
+
+class PreparedApplyXpos:
+    """A rope_apply_xpos call whose descriptor is built once (see Prepared)."""
+
+    def __init__(self, q, k, cos, sin, xpos_q, xpos_k, stream=None, **kw):
+        self._keep = (q, k, cos, sin, xpos_q, xpos_k, kw.get("pos"), kw.get("q_out"),
+                      kw.get("k_out"))
+        if kw.get("theta") is not None:
+            raise ValueError("XPOS factors come with cos/sin tables, not theta")
+        self.desc = make_apply_desc(q, k, cos, sin, **kw)
+        self._zq, self._zk = _xpos_ptrs(xpos_q, xpos_k, cos)
+        self._stream = _stream(stream)
+        self._pdesc = ctypes.byref(self.desc)
+        self._lib = lib()
+
+    def rope_apply_xpos(self):
+        _check(self._lib.rope_apply_xpos(self._pdesc, self._zq, self._zk, self._stream),
+               "rope_apply_xpos")
+
+
+def prepare_apply_xpos(q, k, cos, sin, xpos_q, xpos_k, *, stream=None,
+                       **kw) -> PreparedApplyXpos:
+    """Build the descriptor of a rope_apply_xpos call once."""
+    return PreparedApplyXpos(q, k, cos, sin, xpos_q, xpos_k, stream=stream, **kw)
 
 
 class PreparedApply:
@@ -447,6 +506,21 @@ def rope_build_table(table_rows: int, rotary_dim: int, theta: float = 10000.0,
     _check(lib().rope_build_table(cos.data_ptr(), sin.data_ptr(), table_rows, rotary_dim,
                                   float(theta), float(interpolate_factor)), "rope_build_table")
     return cos, sin
+
+
+def rope_build_xpos_table(table_rows: int, rotary_dim: int, scale_base: float = 512.0,
+                          gamma: float = 0.4, center: float = 0.0):
+    """Host float32 XPOS factor tables (query, key), each [table_rows, R/2]:
+    zeta_i^((p - center)/scale_base) and its reciprocal power,
+    zeta_i = (2i/R + gamma) / (1 + gamma)."""
+    import torch
+    half = rotary_dim // 2
+    zq = torch.empty((table_rows, half), dtype=torch.float32)
+    zk = torch.empty((table_rows, half), dtype=torch.float32)
+    _check(lib().rope_build_xpos_table(zq.data_ptr(), zk.data_ptr(), table_rows, rotary_dim,
+                                       float(scale_base), float(gamma), float(center)),
+           "rope_build_xpos_table")
+    return zq, zk
 
 
 def _index(pos, batch: int, seq: int, batch_stride: Optional[int], what: str):

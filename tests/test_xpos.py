@@ -1,0 +1,471 @@
+"""RoPE with XPOS scaling (rope_apply_xpos): oracle pins, host emulation, GPU parity.
+
+The pages name XPOS (rotary-embedding-torch docs, Key Parameters: use_xpos)
+without its formula; the oracle follows the xPos paper's scales (Sun et al.,
+"A Length-Extrapolatable Transformer"): pair i of a query at n is scaled by
+zeta_i^((n-c)/B), of a key at m by zeta_i^(-(m-c)/B), with
+zeta_i = (i/(R/2) + gamma)/(1 + gamma).
+
+Pins of the oracle (CPU, independent of it):
+  - zeta and the factor tables against mpmath at 60 digits, each entry
+    rounded once to float32 (skipping entries within binary64 error of a
+    float32 rounding boundary); closed forms zeta_0 = gamma/(1+gamma), the
+    factor 1 at p = c, zeta_i and 1/zeta_i one scale base away;
+  - table-mode outputs against exact rational arithmetic on Fractions,
+    rounded to the storage format by tests/_exact.py;
+  - in exact mode, a query and a key at the same position keep their plain
+    dot product (the factors cancel and the rotation is orthogonal), and
+    moving both positions by the same amount leaves every pairwise product
+    unchanged (only n - m matters);
+  - with every position at c the result is plain RoPE, bit for bit.
+Kernel tolerance: 16-bit outputs within 1 unit of the monotone order (as
+rope_apply); float32 outputs within 2 float32 ulps (the kernel rounds the
+rotation and the product with the factor to float32, the oracle rounds the
+binary64 value once).
+"""
+import fcntl
+import os
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotary_position_embedding_fwd_amd as rp
+import workloads as W
+from tests import _exact as X
+from tests import _parity as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+EMU_SRC = os.path.join(ROOT, "tests", "emu", "xpos_emu.hip")
+EMU_BIN = os.path.join(ROOT, "tests", "emu", "_build", "xpos_emu")
+CSRC = os.path.join(ROOT, "rotary_position_embedding_fwd_amd", "csrc")
+DEPS = [EMU_SRC, os.path.join(CSRC, "rope_xpos.hpp"), os.path.join(CSRC, "rope_kernels.hpp"),
+        os.path.join(CSRC, "rope_plan.hpp"), os.path.join(ROOT, "include", "librope.h")]
+DT = {"f32": 0, "f16": 1, "bf16": 2}
+PAIR = {"split_half": 0, "interleaved": 1}
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+# ------------------------------------------------------------ oracle pins
+
+def _zeta_mp(gamma, R, i):
+    g = mpmath.mpf(gamma)
+    return (mpmath.mpf(i) / (mpmath.mpf(R) / 2) + g) / (1 + g)
+
+
+@pytest.mark.parametrize("gamma,R", [(0.4, 128), (0.4, 32), (1.5, 64)])
+def test_zeta_closed_forms(orc, gamma, R):
+    assert oracle.xpos_zeta(gamma, R, 0) == gamma / (1 + gamma)
+    with mpmath.workdps(60):
+        for i in range(R // 2):
+            z = oracle.xpos_zeta(gamma, R, i)
+            assert abs(mpmath.mpf(z) - _zeta_mp(gamma, R, i)) <= mpmath.mpf(2) ** -52 * z
+    # zeta grows with i and stays in (0, 1)
+    zs = [oracle.xpos_zeta(gamma, R, i) for i in range(R // 2)]
+    assert all(0 < a < b < 1 for a, b in zip(zs, zs[1:]))
+
+
+@pytest.mark.parametrize("B,gamma,center", [(512.0, 0.4, 0.0), (64.0, 0.4, 100.0),
+                                            (128.0, 0.9, 37.0)])
+def test_factor_tables_against_mpmath(orc, B, gamma, center):
+    R, rows = 32, 300
+    zq, zk = oracle.xpos_table(R, rows, scale_base=B, gamma=gamma, center=center)
+    checked = 0
+    with mpmath.workdps(60):
+        for p in list(range(0, rows, 7)) + [int(center)]:
+            e = (mpmath.mpf(p) - mpmath.mpf(center)) / mpmath.mpf(B)
+            for i in range(R // 2):
+                z = _zeta_mp(gamma, R, i)
+                for got, ex in ((zq[p, i], z ** e), (zk[p, i], z ** -e)):
+                    if X.near_f32_midpoint(ex):
+                        continue
+                    assert float(got) == X.rn24_mp(ex), (p, i)
+                    checked += 1
+    assert checked > 1000
+    c = int(center)
+    assert (zq[c] == 1).all() and (zk[c] == 1).all()
+    # one scale base away: zeta_i and its reciprocal, rounded once
+    if c + int(B) < rows:
+        for i in range(R // 2):
+            z = oracle.xpos_zeta(gamma, R, i)
+            assert zq[c + int(B), i] == np.float32(z) or abs(
+                float(zq[c + int(B), i]) - z) <= 2 ** -24 * z
+            assert abs(float(zk[c + int(B), i]) - 1 / z) <= 2 ** -23 / z
+
+
+def test_library_table_builder_matches_oracle(orc):
+    for R, rows, B, g, c in [(128, 4096, 512.0, 0.4, 2048.0), (64, 100, 32.0, 0.4, 0.0)]:
+        zq, zk = rp.rope_build_xpos_table(rows, R, B, g, c)
+        oq, ok = oracle.xpos_table(R, rows, scale_base=B, gamma=g, center=c)
+        assert np.array_equal(zq.numpy(), oq) and np.array_equal(zk.numpy(), ok)
+
+
+def _near_mid(y: Fraction, fmt: str) -> bool:
+    prec, emin, _ = X.FORMATS[fmt]
+    if y == 0:
+        return False
+    a = abs(y)
+    e = max(X._floor_log2(a), emin)
+    q = Fraction(2) ** (e - prec + 1)
+    frac = a / q - int(a / q)
+    return abs(frac - Fraction(1, 2)) * q <= a * Fraction(2) ** -50
+
+
+@pytest.mark.parametrize("dtype,pairing,is_key,direction", [
+    ("bf16", "split_half", False, 1), ("f16", "interleaved", True, -1),
+    ("f32", "split_half", True, 1), ("bf16", "interleaved", False, -1)])
+def test_table_mode_against_exact_rationals(orc, dtype, pairing, is_key, direction):
+    B_, H, S, D, R = 1, 2, 9, 24, 16
+    scale_base, gamma, center, rows = 4.0, 0.4, 3.0, 12
+    x = W.normal((B_, H, S, D), dtype, 9100 + DT[dtype])
+    xs = oracle.torch_to_storage(x)
+    pos = np.array([0, 5, -1, 11, 3, 12, 7, 2, 9], np.int32)
+    got = oracle.rope_xpos(xs, dtype, is_key=is_key, pairing=pairing, direction=direction,
+                           rotary_dim=R, pos=pos, table_rows=rows, scale_base=scale_base,
+                           gamma=gamma, center=center)
+    cos, sin = oracle.table(10000.0, R, rows)
+    zq, zk = oracle.xpos_table(R, rows, scale_base=scale_base, gamma=gamma, center=center)
+    z = zk if is_key else zq
+    fmt = dtype
+    bits = xs.view(np.uint32) if dtype == "f32" else xs
+    gbits = got.view(np.uint32) if dtype == "f32" else got
+    for h in range(H):
+        for s in range(S):
+            p = int(pos[s])
+            if p < 0 or p >= rows:
+                assert np.array_equal(gbits[0, h, s], bits[0, h, s])
+                continue
+            for i in range(R // 2):
+                j1, j2 = (i, i + R // 2) if pairing == "split_half" else (2 * i, 2 * i + 1)
+                x1 = X.value_of(int(bits[0, h, s, j1]), fmt)
+                x2 = X.value_of(int(bits[0, h, s, j2]), fmt)
+                c, sn = Fraction(float(cos[p, i])), direction * Fraction(float(sin[p, i]))
+                f = Fraction(float(z[p, i]))
+                for j, y in ((j1, (x1 * c - x2 * sn) * f), (j2, (x1 * sn + x2 * c) * f)):
+                    if _near_mid(y, fmt):
+                        continue
+                    assert int(gbits[0, h, s, j]) == X.bits_of(X.round_ne(y, fmt), fmt), \
+                        (h, s, j)
+            assert np.array_equal(gbits[0, h, s, R:], bits[0, h, s, R:])
+
+
+def test_same_position_keeps_the_dot_product(orc):
+    rng = np.random.default_rng(5)
+    S, D = 40, 64
+    q = rng.standard_normal((1, 1, S, D))
+    k = rng.standard_normal((1, 1, S, D))
+    kw = dict(rotary_dim=D, scale_base=16.0, center=7.0, table_rows=S)
+    qx = oracle.rope_xpos_exact(q, is_key=False, **kw)
+    kx = oracle.rope_xpos_exact(k, is_key=True, **kw)
+    plain = (q * k).sum(-1)
+    assert np.allclose((qx * kx).sum(-1), plain, rtol=1e-12, atol=1e-12)
+    # while each row on its own is scaled away from its input
+    assert not np.allclose(np.abs(qx).sum(-1), np.abs(q).sum(-1), rtol=1e-3)
+
+
+def test_only_relative_positions_matter(orc):
+    rng = np.random.default_rng(6)
+    D, n = 32, 12
+    q = rng.standard_normal((1, 1, n, D))
+    k = rng.standard_normal((1, 1, n, D))
+    base = rng.integers(0, 50, n).astype(np.int32)
+    kw = dict(rotary_dim=D, scale_base=8.0, gamma=0.4, table_rows=400)
+
+    def scores(shift):
+        p = base + shift
+        qx = oracle.rope_xpos_exact(q, is_key=False, pos=p, **kw)[0, 0]
+        kx = oracle.rope_xpos_exact(k, is_key=True, pos=p[::-1].copy(), **kw)[0, 0]
+        return qx @ kx.T
+
+    s0 = scores(0)
+    for shift in (1, 37, 250):
+        assert np.allclose(scores(shift), s0, rtol=1e-9, atol=1e-9)
+
+
+@pytest.mark.parametrize("n,m", [(40, 0), (3, 90), (17, 17)])
+def test_one_pair_decays_by_zeta_to_the_distance(orc, n, m):
+    # R = 2: one pair, whose product with XPOS is plain RoPE's times
+    # zeta_0^((n - m)/B), zeta_0 = gamma / (1 + gamma)
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 1, 1, 2))
+    k = rng.standard_normal((1, 1, 1, 2))
+    kw = dict(rotary_dim=2, table_rows=100)
+    qx = oracle.rope_xpos_exact(q, is_key=False, pos=np.array([n], np.int32), scale_base=8.0,
+                                center=5.0, **kw)
+    kx = oracle.rope_xpos_exact(k, is_key=True, pos=np.array([m], np.int32), scale_base=8.0,
+                                center=5.0, **kw)
+    qp = oracle.rope_exact(q, pos=np.array([n], np.int32), **kw)
+    kp = oracle.rope_exact(k, pos=np.array([m], np.int32), **kw)
+    ratio = (qx * kx).sum() / (qp * kp).sum()
+    assert abs(ratio - (0.4 / 1.4) ** ((n - m) / 8.0)) <= 1e-12 * ratio
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_factor_one_is_plain_rope(orc, dtype):
+    x = oracle.torch_to_storage(W.normal((2, 3, 10, 64), dtype, 9300))
+    pos = np.full(20, 77, np.int32)
+    a = oracle.rope_xpos(x, dtype, is_key=True, pos=pos, pos_batch_stride=10, table_rows=100,
+                         center=77.0)
+    b = oracle.rope(x, dtype, pos=pos, pos_batch_stride=10, table_rows=100)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------- host emulation
+
+@pytest.fixture(scope="module")
+def emu():
+    os.makedirs(os.path.dirname(EMU_BIN), exist_ok=True)
+    with open(EMU_BIN + ".lock", "w") as lock:
+        fcntl.flock(lock, fcntl.LOCK_EX)
+        if (not os.path.exists(EMU_BIN) or
+                os.path.getmtime(EMU_BIN) < max(os.path.getmtime(p) for p in DEPS)):
+            tmp = f"{EMU_BIN}.{os.getpid()}"
+            cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-host-only", "-O1",
+                   "-g", "-std=c++17", "-ffp-contract=off", "-Xarch_host", "-fsanitize=address",
+                   "-fno-omit-frame-pointer", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+                   "-o", tmp, EMU_SRC]
+            subprocess.run(cmd, check=True, capture_output=True)
+            os.replace(tmp, EMU_BIN)
+    return EMU_BIN
+
+
+# B S Hq Hk D R dtype pairing layout oop pos_kind direction scale_base center
+CASES = [
+    (1, 37, 3, 1, 64, 64, "bf16", "split_half", "bhsd", False, "none", 1, 512.0, 0.0),
+    (2, 19, 4, 2, 128, 96, "f16", "split_half", "bshd", True, "none", -1, 16.0, 9.0),
+    (1, 50, 2, 2, 64, 32, "f32", "interleaved", "bhsd", True, "skip", 1, 8.0, 25.0),
+    (2, 7, 5, 0, 72, 40, "bf16", "interleaved", "bshd", False, "skip", 1, 4.0, 0.0),
+    (1, 30, 2, 1, 65, 64, "f32", "split_half", "bhsd", True, "none", -1, 32.0, 15.0),
+    (3, 1, 8, 2, 128, 128, "bf16", "split_half", "bhsd", False, "decode", 1, 512.0, 1000.0),
+    (1, 300, 1, 1, 256, 256, "f16", "split_half", "bshd", True, "none", 1, 64.0, 150.0),
+]
+
+
+def case_id(c):
+    return "-".join(str(x) for x in c[:12])
+
+
+def _positions(kind, B, S, rows, seed):
+    if kind == "none":
+        return None, 0
+    g = np.random.default_rng(seed)
+    if kind == "skip":  # a shared row with skipped and out-of-table entries
+        p = g.integers(0, rows, S).astype(np.int32)
+        p[::5] = -1
+        p[3::7] = rows + 2
+        return p, 0
+    if kind == "decode":  # one position per batch row
+        return g.integers(0, rows, B).astype(np.int32), 1
+    raise ValueError(kind)
+
+
+def _case_data(c, seed=9500):
+    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c
+    shape_q = (B, Hq, S, D) if layout == "bhsd" else (B, S, Hq, D)
+    shape_k = (B, Hk, S, D) if layout == "bhsd" else (B, S, Hk, D)
+    q = W.normal(shape_q, dtype, seed)
+    k = W.normal(shape_k, dtype, seed + 1) if Hk else None
+    rows = max(S, 64) + 3
+    pos, pbs = _positions(pkind, B, S, rows, seed + 2)
+    cos, sin = oracle.table(10000.0, R, rows)
+    zq, zk = oracle.xpos_table(R, rows, scale_base=sb, gamma=0.4, center=center)
+    return q, k, pos, pbs, rows, cos, sin, zq, zk
+
+
+def _expected(c, q, k, pos, pbs, rows):
+    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c
+    kw = dict(layout=layout, pairing=pairing, direction=direction, rotary_dim=R, pos=pos,
+              pos_batch_stride=pbs, table_rows=rows, scale_base=sb, gamma=0.4, center=center)
+    eq = oracle.rope_xpos(oracle.torch_to_storage(q), dtype, is_key=False, **kw)
+    ek = None if k is None else oracle.rope_xpos(oracle.torch_to_storage(k), dtype,
+                                                 is_key=True, **kw)
+    return eq, ek
+
+
+def _strides(shape, layout):
+    B, A, C, D = shape
+    if layout == "bhsd":   # [B,H,S,D]: (sb, sh, ss)
+        return A * C * D, C * D, D
+    return A * C * D, D, C * D  # [B,S,H,D]: sb, sh = D, ss = H*D
+
+
+def _ord32(bits):
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFFFFFF
+    return np.where(b & 0x80000000, -mag, mag)
+
+
+def check(got, ref, dtype, what):
+    if dtype == "f32":
+        d = np.abs(_ord32(got.view(np.uint32)) - _ord32(ref.view(np.uint32)))
+        assert int(d.max()) <= 2, f"{what}: {int(d.max())} float32 ulps apart"
+    else:
+        d = np.abs(P.ord16(got) - P.ord16(ref))
+        assert int(d.max()) <= P.ORD_TOL, f"{what}: {int(d.max())} units apart"
+
+
+def run_emu(emu, c, q, k, pos, pbs, rows, cos, sin, zq, zk):
+    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c
+    qs = oracle.torch_to_storage(q)
+    ks = None if k is None else oracle.torch_to_storage(k)
+    with tempfile.TemporaryDirectory() as job:
+        qsb, qsh, qss = _strides(q.shape, layout)
+        desc = dict(B=B, S=S, D=D, R=R, Hq=Hq, Hk=Hk, dtype=DT[dtype], pairing=PAIR[pairing],
+                    direction=direction, oop=int(oop), qn=qs.size, kn=0 if ks is None else ks.size,
+                    tn=cos.size, pn=0 if pos is None else pos.size, table_rows=rows,
+                    t_row=R // 2, t_col=1, pos_bs=pbs, qsb=qsb, qsh=qsh, qss=qss)
+        if ks is not None:
+            desc.update(zip(("ksb", "ksh", "kss"), _strides(k.shape, layout)))
+        with open(os.path.join(job, "desc.txt"), "w") as f:
+            for key, v in desc.items():
+                f.write(f"{key} {int(v)}\n")
+        qs.tofile(os.path.join(job, "q.bin"))
+        if ks is not None:
+            ks.tofile(os.path.join(job, "k.bin"))
+        for name, arr in (("cos", cos), ("sin", sin), ("zq", zq), ("zk", zk)):
+            arr.tofile(os.path.join(job, f"{name}.bin"))
+        if pos is not None:
+            pos.tofile(os.path.join(job, "pos.bin"))
+        env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
+        r = subprocess.run([emu, job], capture_output=True, text=True, timeout=300, env=env)
+        assert r.returncode == 0, r.stdout + r.stderr[-4000:]
+        status = int(r.stdout.split()[1])
+        if status:
+            return status, None, None
+        go = np.fromfile(os.path.join(job, "q_out.bin"), dtype=qs.dtype).reshape(qs.shape)
+        gk = None if ks is None else np.fromfile(os.path.join(job, "k_out.bin"),
+                                                 dtype=ks.dtype).reshape(ks.shape)
+        return 0, go, gk
+
+
+@pytest.mark.parametrize("c", CASES, ids=case_id)
+def test_emulated_kernel_matches_oracle(orc, emu, c):
+    q, k, pos, pbs, rows, cos, sin, zq, zk = _case_data(c)
+    status, gq, gk = run_emu(emu, c, q, k, pos, pbs, rows, cos, sin, zq, zk)
+    assert status == 0
+    eq, ek = _expected(c, q, k, pos, pbs, rows)
+    dtype = c[6]
+    check(gq, eq, dtype, "q")
+    if ek is not None:
+        check(gk, ek, dtype, "k")
+    # pass-through lanes are bit-exact (dims >= R; skipped tokens)
+    R = c[5]
+    for g, e in ((gq, eq), (gk, ek)):
+        if g is None:
+            continue
+        gb = g.view(np.uint32) if dtype == "f32" else g
+        eb = e.view(np.uint32) if dtype == "f32" else e
+        assert np.array_equal(gb[..., R:], eb[..., R:])
+
+
+# ------------------------------------------------------------ the C ABI
+
+def _abi_desc(**over):
+    """A valid rope_apply descriptor for a [1, 2, 8, 64] bf16 Q/K pair at fake
+    16-byte aligned addresses (nothing is dereferenced on the error paths)."""
+    A = 1 << 40
+    d = rp.RopeApplyDesc()
+    d.batch, d.seq_len, d.head_dim, d.rotary_dim = 1, 8, 64, 64
+    d.n_heads_q, d.n_heads_k = 2, 1
+    d.dtype, d.pairing, d.launch, d.direction = 2, 0, 0, 1
+    d.q_in = rp.RopeView(A, 2 * 8 * 64, 8 * 64, 64)
+    d.k_in = rp.RopeView(A + 65536, 8 * 64, 8 * 64, 64)
+    d.cos, d.sin = A + 2 * 65536, A + 3 * 65536
+    d.table_rows = 8
+    d.table_col_stride = 1
+    d.angles = 0
+    for key, v in over.items():
+        setattr(d, key, v)
+    return d
+
+
+def _call(d, zq=(1 << 40) + 4 * 65536, zk=(1 << 40) + 5 * 65536):
+    import ctypes
+    return rp.lib().rope_apply_xpos(ctypes.byref(d), zq, zk, None)
+
+
+def test_abi_validation():
+    OK, NULL, SHAPE, LAYOUT, ALIGN, ALIAS = 0, -1, -2, -4, -5, -6
+    assert _call(_abi_desc(angles=1, theta=10000.0, interpolate_factor=1.0)) == LAYOUT
+    assert _call(_abi_desc(launch=1)) == LAYOUT
+    assert _call(_abi_desc(), zq=None) == NULL
+    assert _call(_abi_desc(), zk=None) == NULL
+    assert _call(_abi_desc(), zq=(1 << 40) + 4 * 65536 + 2) == ALIGN
+    # no K heads: no key table needed (the next check to fail is Q's table)
+    assert _call(_abi_desc(n_heads_k=0), zq=(1 << 40) + 4 * 65536 + 2, zk=None) == ALIGN
+    assert _call(_abi_desc(), zk=(1 << 40) + 64) == ALIAS    # inside Q, written in place
+    assert _call(_abi_desc(rotary_dim=63)) == SHAPE
+    assert _call(_abi_desc(seq_len=0), zq=None, zk=None) == OK   # empty: nothing to do
+    import ctypes
+    assert rp.lib().rope_apply_xpos(None, None, None, None) == NULL
+
+
+def test_abi_table_builder_errors():
+    import ctypes
+    L = rp.lib()
+    buf = (ctypes.c_float * 64)()
+    SHAPE, NULL = -2, -1
+    for args in [(4, 17, 512.0, 0.4, 0.0), (4, 16, 0.0, 0.4, 0.0), (4, 16, 512.0, -1.0, 0.0),
+                 (4, 16, float("inf"), 0.4, 0.0), (4, 16, 512.0, 0.4, float("nan")),
+                 (-1, 16, 512.0, 0.4, 0.0)]:
+        assert L.rope_build_xpos_table(buf, buf, *args) == SHAPE, args
+    assert L.rope_build_xpos_table(None, buf, 4, 16, 512.0, 0.4, 0.0) == NULL
+    assert L.rope_build_xpos_table(None, None, 0, 16, 512.0, 0.4, 0.0) == 0
+
+
+# ------------------------------------------------------------ on the GPU
+
+def _gpu_call(c, q, k, pos, pbs, rows, cos, sin, zq, zk, stream=None):
+    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c
+    dev = "cuda"
+    qd = q.to(dev)
+    kd = None if k is None else k.to(dev)
+    kw = dict(layout=layout, pairing=pairing, rotary_dim=R, direction=direction)
+    if pos is not None:
+        kw["pos"] = torch.from_numpy(pos).to(dev)
+        kw["pos_batch_stride"] = pbs
+    if oop:
+        kw["q_out"] = torch.empty_like(qd)
+        if kd is not None:
+            kw["k_out"] = torch.empty_like(kd)
+    t = [torch.from_numpy(a).to(dev) for a in (cos, sin, zq, zk)]
+    oq, ok = rp.rope_apply_xpos(qd, kd, t[0], t[1], t[2], t[3], **kw)
+    torch.cuda.synchronize()
+    return (oracle.torch_to_storage(oq.cpu()),
+            None if ok is None else oracle.torch_to_storage(ok.cpu()))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("c", CASES, ids=case_id)
+def test_gpu_matches_oracle(orc, c):
+    print(f"xpos case {case_id(c)}", flush=True)
+    q, k, pos, pbs, rows, cos, sin, zq, zk = _case_data(c)
+    gq, gk = _gpu_call(c, q, k, pos, pbs, rows, cos, sin, zq, zk)
+    eq, ek = _expected(c, q, k, pos, pbs, rows)
+    check(gq, eq, c[6], "q")
+    if ek is not None:
+        check(gk, ek, c[6], "k")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("direction", [1, -1])
+def test_gpu_full_llama_size(orc, direction):
+    # the Llama GQA prefill shape in place, every element against the oracle
+    w = W.LLAMA_GQA_PREFILL
+    c = (w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim, w.rotary_dim, w.dtype,
+         w.pairing, w.layout, False, "none", direction, 512.0, w.seq_len / 2)
+    print(f"xpos full size, direction {direction}", flush=True)
+    t = W.tensors(w, ("q", "k"))
+    rows = w.table_rows
+    cos, sin = oracle.table(w.theta, w.rotary_dim, rows)
+    zq, zk = oracle.xpos_table(w.rotary_dim, rows, scale_base=512.0, gamma=0.4,
+                               center=w.seq_len / 2)
+    gq, gk = _gpu_call(c, t["q"], t["k"], None, 0, rows, cos, sin, zq, zk)
+    eq, ek = _expected(c, t["q"], t["k"], None, 0, rows)
+    check(gq, eq, w.dtype, "q")
+    check(gk, ek, w.dtype, "k")
