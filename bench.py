@@ -325,6 +325,51 @@ def time_theta(target_s: float = 0.15):
     return results
 
 
+def time_xpos(target_s: float = 0.15):
+    """RoPE with XPOS factors (rope_apply_xpos) on the Llama prefill workload,
+    forward and backward in place, [B,H,S,D] and packed QKV; beside it the
+    same rotation without factors (rope_apply), on the same buffers."""
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    results = []
+    stream = torch.cuda.current_stream()
+    w = W.LLAMA_GQA_PREFILL
+    # the factor tables add two more [S, R/2] float32 rows per position
+    nbytes = algorithmic_bytes(w, None) + 4 * w.rotary_dim * w.seq_len
+    cos, sin = (t.cuda() for t in rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta))
+    zq, zk = (t.cuda() for t in rp.rope_build_xpos_table(w.table_rows, w.rotary_dim, 512.0, 0.4,
+                                                          w.seq_len / 2))
+    _, sets = device_inputs(w, 3, ("q", "k"))
+    B, S, Hq, Hk, D = w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim
+    host = W.normal((B, S, (Hq + 2 * Hk) * D), w.dtype, w.seed("q"))
+    bufs = [host.cuda() for _ in range(3)]
+    packed = [(g[..., :Hq * D].view(B, S, Hq, D), g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D))
+              for g in bufs]
+    for layout, views in (("bhsd", [(x["q"], x["k"]) for x in sets]), ("bshd", packed)):
+        kw = dict(layout=layout, pairing=w.pairing, rotary_dim=w.rotary_dim, stream=stream)
+        fwd = [rp.prepare_apply_xpos(q, k, cos, sin, zq, zk, **kw) for q, k in views]
+        bwd = [rp.prepare_apply_xpos(q, k, cos, sin, zq, zk, direction=-1, **kw)
+               for q, k in views]
+        out = {"workload": w.name, "call": "rope_apply_xpos",
+               "views": "[B,H,S,D]" if layout == "bhsd" else "packed QKV [B,S,H,D]",
+               "xpos": {"scale_base": 512.0, "gamma": 0.4, "center": w.seq_len / 2},
+               "buffer_sets": 3, "algorithmic_bytes_per_call": nbytes,
+               "kernel": "rope_xpos_kernel (16-byte chunks, 4 heads per lane)"}
+        _time_calls(out, fwd, bwd, 3, nbytes, target_s, stream, method="rope_apply_xpos")
+        results.append(out)
+        plain_bytes = algorithmic_bytes(w, None)
+        fwd = [rp.prepare_apply(q, k, cos, sin, **kw) for q, k in views]
+        bwd = [rp.prepare_apply(q, k, cos, sin, direction=-1, **kw) for q, k in views]
+        out = {"workload": w.name, "call": "rope_apply (no XPOS, for comparison)",
+               "views": "[B,H,S,D]" if layout == "bhsd" else "packed QKV [B,S,H,D]",
+               "buffer_sets": 3, "algorithmic_bytes_per_call": plain_bytes}
+        _time_calls(out, fwd, bwd, 3, plain_bytes, target_s, stream, method="rope_apply")
+        results.append(out)
+        del fwd, bwd
+    return results
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, published
 
 
@@ -636,6 +681,8 @@ def main():
                     help="time the path with cos/sin computed from theta (no tables)")
     ap.add_argument("--layout-matrix", action="store_true",
                     help="rows vs token launch on token-major views, by shape and pairing")
+    ap.add_argument("--xpos", action="store_true",
+                    help="RoPE with XPOS factors (rope_apply_xpos) against plain rope_apply")
     ap.add_argument("--attention", action="store_true",
                     help="time attention with RoPE fused on the loaded Q/K blocks, against "
                          "rotation followed by attention")
@@ -659,6 +706,10 @@ def main():
 
     if args.theta:
         for res in time_theta():
+            print(json.dumps(res), flush=True)
+        return
+    if args.xpos:
+        for res in time_xpos():
             print(json.dumps(res), flush=True)
         return
     if args.attention:

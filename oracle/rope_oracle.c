@@ -345,16 +345,17 @@ int oracle_rope_xpos(const void *x, void *y, int dtype, int layout, int pairing,
         if (p < 0) continue; /* skipped token: neither rotated nor scaled */
         int64_t row = row_offset(layout, H, S, D, b, h, s);
         for (int64_t i = 0; i < R / 2; ++i) {
-          float c32, s32;
-          oracle_table_entry(theta, interp, R, p, i, &c32, &s32);
-          double z = (float)xpos_factor(scale_base, gamma, center, R, p, i, is_key);
-          double c = c32, sn = (double)direction * (double)s32;
-          int64_t j1, j2;
-          pair_dims(pairing, R, i, &j1, &j2);
-          double x1 = load_elem(x, row + j1, dtype);
-          double x2 = load_elem(x, row + j2, dtype);
-          store_elem(y, row + j1, dtype, (x1 * c - x2 * sn) * z);
-          store_elem(y, row + j2, dtype, (x1 * sn + x2 * c) * z);
+          float cos32, sin32;
+          oracle_table_entry(theta, interp, R, p, i, &cos32, &sin32);
+          /* the factor as the float32 table holds it */
+          double f32 = (float)xpos_factor(scale_base, gamma, center, R, p, i, is_key);
+          double cs = cos32, sg = (double)direction * (double)sin32;
+          int64_t ja, jb;
+          pair_dims(pairing, R, i, &ja, &jb);
+          double a1 = load_elem(x, row + ja, dtype);
+          double a2 = load_elem(x, row + jb, dtype);
+          store_elem(y, row + ja, dtype, (a1 * cs - a2 * sg) * f32);
+          store_elem(y, row + jb, dtype, (a1 * sg + a2 * cs) * f32);
         }
       }
   return 0;
@@ -378,14 +379,14 @@ int oracle_rope_xpos_exact(const double *x, double *y, int layout, int pairing, 
         if (p < 0) continue;
         int64_t row = row_offset(layout, H, S, D, b, h, s);
         for (int64_t i = 0; i < R / 2; ++i) {
-          double angle = angle_of(theta, interp, R, p, i);
-          double c = cos(angle), sn = (double)direction * sin(angle);
-          double z = xpos_factor(scale_base, gamma, center, R, p, i, is_key);
-          int64_t j1, j2;
-          pair_dims(pairing, R, i, &j1, &j2);
-          double x1 = y[row + j1], x2 = y[row + j2];
-          y[row + j1] = (x1 * c - x2 * sn) * z;
-          y[row + j2] = (x1 * sn + x2 * c) * z;
+          double ang = angle_of(theta, interp, R, p, i);
+          double cs = cos(ang), sg = (double)direction * sin(ang);
+          double f = xpos_factor(scale_base, gamma, center, R, p, i, is_key);
+          int64_t ja, jb;
+          pair_dims(pairing, R, i, &ja, &jb);
+          double a1 = y[row + ja], a2 = y[row + jb];
+          y[row + ja] = (a1 * cs - a2 * sg) * f;
+          y[row + jb] = (a1 * sg + a2 * cs) * f;
         }
       }
   return 0;

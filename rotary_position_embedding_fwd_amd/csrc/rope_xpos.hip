@@ -6,18 +6,32 @@
 
 namespace {
 
-template <typename T>
+template <typename T, int V, int PAIR>
 __global__ void __launch_bounds__(rope::xpos::kBlock)
     rope_xpos_kernel(rope::xpos::XArgs a) {
-  rope::xpos::xpos_token<T>(a, blockIdx.x, (int)threadIdx.x);
+  rope::xpos::xpos_block<T, V, PAIR>(a, blockIdx.x, (int)threadIdx.x);
 }
 
 template <typename T>
-hipError_t launch_xpos(const rope::xpos::XPlan& pl, hipStream_t st) {
-  hipLaunchKernelGGL(rope_xpos_kernel<T>, dim3((unsigned)pl.a.n_tokens),
-                     dim3(rope::xpos::kBlock), 0, st, pl.a);
-  return hipGetLastError();
+__global__ void __launch_bounds__(rope::xpos::kBlock)
+    rope_xpos_element_kernel(rope::xpos::XArgs a) {
+  rope::xpos::xpos_token<T>(a, blockIdx.x, (int)threadIdx.x);
 }
+
+struct Launcher {
+  const rope::xpos::XPlan& pl;
+  hipStream_t st;
+  template <typename T, int V, int PAIR>
+  void chunked() {
+    hipLaunchKernelGGL((rope_xpos_kernel<T, V, PAIR>), dim3((unsigned)pl.grid),
+                       dim3(rope::xpos::kBlock), 0, st, pl.a);
+  }
+  template <typename T>
+  void element() {
+    hipLaunchKernelGGL(rope_xpos_element_kernel<T>, dim3((unsigned)pl.grid),
+                       dim3(rope::xpos::kBlock), 0, st, pl.a);
+  }
+};
 
 }  // namespace
 
@@ -28,14 +42,9 @@ rope_status_t rope_apply_xpos(const rope_apply_desc_t* d, const float* xpos_q,
   rope::xpos::XPlan pl;
   const rope_status_t st = rope::xpos::make_xpos_plan(d, xpos_q, xpos_k, &pl);
   if (st != ROPE_OK || pl.empty) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipErrorInvalidValue;
-  switch (pl.dtype) {
-    case ROPE_F32: e = launch_xpos<float>(pl, s); break;
-    case ROPE_F16: e = launch_xpos<_Float16>(pl, s); break;
-    case ROPE_BF16: e = launch_xpos<__bf16>(pl, s); break;
-  }
-  return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
+  Launcher launch{pl, static_cast<hipStream_t>(stream)};
+  if (!rope::xpos::dispatch(pl, launch)) return ROPE_ERR_HIP;  // no plan produces this
+  return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
 }
 
 rope_status_t rope_build_xpos_table(float* xpos_q, float* xpos_k, int64_t table_rows,

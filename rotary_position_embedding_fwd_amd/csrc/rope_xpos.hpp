@@ -13,13 +13,18 @@
 // so it commutes with the pair's rotation: the backward (sin negated) uses
 // the same tables.
 //
-// One workgroup per token; its lanes walk (head, slot) items, slot k < R/2
-// being pair k of the row (split-half: dims k and k + R/2; interleaved: 2k
-// and 2k + 1) and, out of place, slots past R/2 copying two of the dims >= R.
-// Within a head row consecutive lanes take consecutive slots, so each half of
-// a split-half row (and an interleaved row) is read and written coalesced.
-// The body is a plain function of (token, lane) so that the host can run it
-// over every lane of a grid and check every access.
+// Chunked shape (xpos_block): a lane owns one chunk of one token and walks
+// it over a group of heads, loading the chunk's cos, sin and factors once. A
+// chunk is V contiguous elements moved as one access, V the widest that
+// every view's alignment allows (as for rope_apply): split-half chunk c
+// covers pairs cV .. cV+V-1 (dims cV.. and R/2+cV..), interleaved chunk c the
+// V/2 pairs of dims cV .. cV+V-1; out of place, further chunks copy the dims
+// >= R. Consecutive lanes take consecutive chunks of a row, then the next
+// token, so rows stream coalesced.
+// Element shape (xpos_token), for interleaved views that are not even
+// 2-element aligned: one workgroup per token, lanes over (head, pair) items.
+// Both bodies are plain functions of (workgroup, lane) so that the host can
+// run them over every lane of a grid and check every access.
 #pragma once
 
 #include <stdint.h>
@@ -34,7 +39,7 @@
 namespace rope {
 namespace xpos {
 
-constexpr int kBlock = 256;  // lanes per workgroup (one token)
+constexpr int kBlock = 256;  // lanes per workgroup
 
 struct XArgs {
   View q_in, k_in, q_out, k_out;  // outputs equal the inputs in place
@@ -52,6 +57,14 @@ struct XArgs {
   int32_t interleaved;
   int32_t oop;                    // some output differs from its input
   float sin_sign;                 // +1 forward, -1 backward
+  // chunked shape
+  int32_t chunks;                 // pair chunks per head row
+  int32_t row_items;              // chunks per head row, copies included
+  int32_t heads_per_group;        // rows one lane walks
+  int32_t n_groups;               // ceil((Hq + Hk) / heads_per_group)
+  int32_t token_major;            // 1: lanes run token-slow (views with adjacent heads)
+  int32_t t_vec;                  // 1: a chunk's table entries load as float4s
+  int64_t n_items;                // lanes: head groups x tokens x row_items
 };
 
 // All items of one token that lane t of its workgroup owns.
@@ -94,10 +107,138 @@ ROPE_HD void xpos_token(const XArgs& a, int64_t token, int t) {
   }
 }
 
+// Factor, cos and sin of NP consecutive pairs from pair `first` of row p.
+template <int NP>
+ROPE_HD void load_tables(const XArgs& a, int64_t p, int first, bool key, float* c, float* sn,
+                         float* z) {
+  const float* zt = key ? a.zk : a.zq;
+  const int64_t base = p * a.t_row + (int64_t)first * a.t_col;
+  if constexpr (NP % 4 == 0) {
+    if (a.t_vec) {
+#pragma unroll
+      for (int j = 0; j < NP; j += 4) {
+        const float4 cv = *reinterpret_cast<const float4*>(a.cos + base + j);
+        const float4 sv = *reinterpret_cast<const float4*>(a.sin + base + j);
+        const float4 zv = *reinterpret_cast<const float4*>(zt + base + j);
+        c[j] = cv.x; c[j + 1] = cv.y; c[j + 2] = cv.z; c[j + 3] = cv.w;
+        sn[j] = sv.x; sn[j + 1] = sv.y; sn[j + 2] = sv.z; sn[j + 3] = sv.w;
+        z[j] = zv.x; z[j + 1] = zv.y; z[j + 2] = zv.z; z[j + 3] = zv.w;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int64_t ti = base + (int64_t)j * a.t_col;
+    c[j] = a.cos[ti];
+    sn[j] = a.sin[ti];
+    z[j] = zt[ti];
+  }
+}
+
+// The item of lane t of workgroup `blk` (chunked shape): one chunk of one
+// token, walked over a group of G heads (Q heads first, then K heads), so
+// the chunk's cos, sin and factors are loaded once for G rows. Items run
+// chunk fastest, then token, then head group.
+template <typename T, int V, int PAIR>
+ROPE_HD void xpos_block(const XArgs& a, int64_t blk, int t) {
+  constexpr int NP = PAIR == kSplitHalf ? V : V / 2;  // pairs per chunk
+  static_assert(NP >= 1, "an interleaved chunk holds at least one pair");
+  const int64_t item = blk * kBlock + t;
+  if (item >= a.n_items) return;
+  int64_t g, token;
+  int c;
+  if (a.token_major) {  // token, head group, chunk: a token's rows are adjacent
+    const int64_t per_token = (int64_t)a.n_groups * a.row_items;
+    token = item / per_token;
+    const int64_t rest = item - token * per_token;
+    g = rest / a.row_items;
+    c = (int)(rest - g * a.row_items);
+  } else {  // head group, token, chunk
+    const int64_t per_group = a.n_tokens * a.row_items;
+    g = item / per_group;
+    const int64_t rest = item - g * per_group;
+    token = rest / a.row_items;
+    c = (int)(rest - token * a.row_items);
+  }
+  const int64_t b = token / a.seq_len, s = token - b * a.seq_len;
+  const int h_total = a.n_heads_q + a.n_heads_k;
+  const int h0 = (int)g * a.heads_per_group;
+  const int h1 = imin(h_total, h0 + a.heads_per_group);
+  auto row = [&](int head, bool out) {
+    const bool is_k = head >= a.n_heads_q;
+    const int h = is_k ? head - a.n_heads_q : head;
+    const View& v = out ? (is_k ? a.k_out : a.q_out) : (is_k ? a.k_in : a.q_in);
+    return reinterpret_cast<T*>(v.base) + b * v.sb + h * v.sh + s * v.ss;
+  };
+  if (c >= a.chunks) {  // out of place only: dims >= R, V at a time
+    const int j0 = 2 * a.half + (c - a.chunks) * V;
+    for (int head = h0; head < h1; ++head) {
+      const T* in = row(head, false);
+      T* out = row(head, true);
+      if (j0 + V <= a.head_dim) {
+        Chunk<T, V, true> x;
+        x.load(in + j0);
+        x.store(out + j0);
+      } else {
+        for (int j = j0; j < a.head_dim; ++j) out[j] = in[j];
+      }
+    }
+    return;
+  }
+  const int64_t p = a.pos ? (int64_t)a.pos[b * a.pos_bs + s] : s;
+  const bool rot = p >= 0 && p < a.table_rows;
+  if (!rot && !a.oop) return;  // a skipped token: untouched in place
+  const int first = PAIR == kSplitHalf ? c * V : c * NP;  // first pair of the chunk
+  float cs[NP], sn[NP], zq[NP], zk[NP];
+  if (rot) {
+    if (h0 < a.n_heads_q) load_tables<NP>(a, p, first, false, cs, sn, zq);
+    if (h1 > a.n_heads_q) load_tables<NP>(a, p, first, true, cs, sn, zk);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) sn[j] *= a.sin_sign;
+  }
+  for (int head = h0; head < h1; ++head) {
+    const float* z = head >= a.n_heads_q ? zk : zq;
+    const T* in = row(head, false);
+    T* out = row(head, true);
+    if constexpr (PAIR == kSplitHalf) {
+      Chunk<T, V, true> x1, x2;
+      x1.load(in + c * V);
+      x2.load(in + a.half + c * V);
+      if (rot) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          float y1, y2;
+          rotate_pair(to_f32(x1.v[j]), to_f32(x2.v[j]), cs[j], sn[j], y1, y2);
+          x1.v[j] = from_f32<T>(y1 * z[j]);
+          x2.v[j] = from_f32<T>(y2 * z[j]);
+        }
+      }
+      x1.store(out + c * V);
+      x2.store(out + a.half + c * V);
+    } else {
+      Chunk<T, V, true> x;
+      x.load(in + c * V);
+      if (rot) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          float y1, y2;
+          rotate_pair(to_f32(x.v[2 * j]), to_f32(x.v[2 * j + 1]), cs[j], sn[j], y1, y2);
+          x.v[2 * j] = from_f32<T>(y1 * z[j]);
+          x.v[2 * j + 1] = from_f32<T>(y2 * z[j]);
+        }
+      }
+      x.store(out + c * V);
+    }
+  }
+}
+
 struct XPlan {
   XArgs a;
   bool empty;
   int dtype;
+  int vec;         // chunk width V; 0: element shape
+  int64_t grid;    // workgroups
 };
 
 // Validate a rope_apply_xpos call and plan it. Never touches device memory.
@@ -150,6 +291,41 @@ inline rope_status_t make_xpos_plan(const rope_apply_desc_t* d, const float* zq,
   a.sin_sign = (float)d->direction;
   pl->dtype = d->dtype;
 
+  // chunked shape unless interleaved pairs are not 2-element aligned
+  const int v = pick_vec(d);
+  const bool chunked = !(a.interleaved && v < 2);
+  if (chunked) {
+    pl->vec = v;
+    a.chunks = (int32_t)((a.interleaved ? d->rotary_dim : d->rotary_dim / 2) / v);
+    const int64_t copies = oop ? (d->head_dim - d->rotary_dim + v - 1) / v : 0;
+    a.row_items = (int32_t)(a.chunks + copies);
+    // 4 heads per lane (the rows kernel's measured best for the Llama shape),
+    // fewer when that would leave the chip short of lanes. Views whose heads
+    // of a token are adjacent in memory ([B,S,H,D], packed QKV) run one head
+    // per lane, token-slow, so a wave's lanes sweep each token's rows in
+    // memory order (measured on MI355X, Llama shape as packed QKV: 72 us
+    // that way, 88 us with 4 heads per lane).
+    const int64_t h_total = d->n_heads_q + d->n_heads_k;
+    a.token_major = (d->n_heads_q > 1 && d->q_in.stride_h < d->q_in.stride_s) ? 1 : 0;
+    int64_t g = a.token_major ? 1 : (h_total < 4 ? h_total : 4);
+    while (g > 1 && ((h_total + g - 1) / g) * a.n_tokens * a.row_items < 256 * 256) g /= 2;
+    a.heads_per_group = (int32_t)g;
+    a.n_groups = (int32_t)((h_total + g - 1) / g);
+    int64_t items = 0;
+    if (__builtin_mul_overflow((int64_t)a.n_groups, a.n_tokens * a.row_items, &items))
+      return ROPE_ERR_SHAPE;
+    a.n_items = items;
+    const int np = a.interleaved ? v / 2 : v;
+    a.t_vec = (np % 4 == 0 && a.t_col == 1 && a.t_row % 4 == 0 &&
+               reinterpret_cast<uintptr_t>(zq) % 16 == 0 &&
+               reinterpret_cast<uintptr_t>(zk) % 16 == 0) ? 1 : 0;
+    pl->grid = (a.n_items + kBlock - 1) / kBlock;
+    if (pl->grid > 0x7fffffff) return ROPE_ERR_SHAPE;
+  } else {
+    pl->vec = 0;
+    pl->grid = a.n_tokens;
+  }
+
   // The factor tables span what cos and sin span, and no written view may
   // meet them (they are read for the whole launch).
   int64_t tbytes = 0;
@@ -176,6 +352,54 @@ inline rope_status_t make_xpos_plan(const rope_apply_desc_t* d, const float* zq,
   if ((d->n_heads_q > 0 && meets_written(zq)) || (d->n_heads_k > 0 && meets_written(zk)))
     return ROPE_ERR_ALIAS;
   return ROPE_OK;
+}
+
+// Calls f.template chunked<T, V, PAIR>() or f.template element<T>() for the
+// plan's shape (F: the GPU launcher, or the host emulation). False for a
+// combination no plan produces.
+template <typename T, int VMAX, class F>
+bool dispatch_vec(const XPlan& pl, F& f) {
+  const bool inter = pl.a.interleaved != 0;
+  switch (pl.vec) {
+    case 1:
+      if (inter) return false;
+      f.template chunked<T, 1, kSplitHalf>();
+      return true;
+    case 2:
+      if (inter) f.template chunked<T, 2, kInterleaved>();
+      else f.template chunked<T, 2, kSplitHalf>();
+      return true;
+    case 4:
+      if (inter) f.template chunked<T, 4, kInterleaved>();
+      else f.template chunked<T, 4, kSplitHalf>();
+      return true;
+    case 8:
+      if constexpr (VMAX >= 8) {
+        if (inter) f.template chunked<T, 8, kInterleaved>();
+        else f.template chunked<T, 8, kSplitHalf>();
+        return true;
+      }
+      return false;
+  }
+  return false;
+}
+
+template <class F>
+bool dispatch(const XPlan& pl, F& f) {
+  if (pl.vec == 0) {
+    switch (pl.dtype) {
+      case ROPE_F32: f.template element<float>(); return true;
+      case ROPE_F16: f.template element<_Float16>(); return true;
+      case ROPE_BF16: f.template element<__bf16>(); return true;
+    }
+    return false;
+  }
+  switch (pl.dtype) {
+    case ROPE_F32: return dispatch_vec<float, 4>(pl, f);
+    case ROPE_F16: return dispatch_vec<_Float16, 8>(pl, f);
+    case ROPE_BF16: return dispatch_vec<__bf16, 8>(pl, f);
+  }
+  return false;
 }
 
 // zeta_i^((p - center) / scale_base) for query rows and its inverse power for

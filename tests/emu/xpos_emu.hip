@@ -60,11 +60,21 @@ void write_file(const std::string& path, const void* p, size_t bytes) {
   fclose(f);
 }
 
-template <typename T>
-void run_all(const rope::xpos::XPlan& pl) {
-  for (int64_t token = 0; token < pl.a.n_tokens; ++token)
-    for (int t = 0; t < rope::xpos::kBlock; ++t) rope::xpos::xpos_token<T>(pl.a, token, t);
-}
+// Every lane of every workgroup of the planned grid, one after another.
+struct HostRunner {
+  const rope::xpos::XPlan& pl;
+  template <typename T, int V, int PAIR>
+  void chunked() {
+    for (int64_t blk = 0; blk < pl.grid; ++blk)
+      for (int t = 0; t < rope::xpos::kBlock; ++t)
+        rope::xpos::xpos_block<T, V, PAIR>(pl.a, blk, t);
+  }
+  template <typename T>
+  void element() {
+    for (int64_t blk = 0; blk < pl.grid; ++blk)
+      for (int t = 0; t < rope::xpos::kBlock; ++t) rope::xpos::xpos_token<T>(pl.a, blk, t);
+  }
+};
 
 }  // namespace
 
@@ -129,11 +139,13 @@ int main(int argc, char** argv) {
   const rope_status_t st = rope::xpos::make_xpos_plan(&d, zq, kn ? zk : nullptr, &pl);
   printf("status %d\n", (int)st);
   if (st != ROPE_OK) return 0;
+  printf("vec %d\ngrid %lld\nheads_per_group %d\n", pl.vec, (long long)pl.grid,
+         (int)pl.a.heads_per_group);
   if (!pl.empty) {
-    switch (pl.dtype) {
-      case ROPE_F32: run_all<float>(pl); break;
-      case ROPE_F16: run_all<_Float16>(pl); break;
-      case ROPE_BF16: run_all<__bf16>(pl); break;
+    HostRunner run{pl};
+    if (!rope::xpos::dispatch(pl, run)) {
+      fprintf(stderr, "no kernel for this plan\n");
+      return 5;
     }
   }
   write_file(dir + "/q_out.bin", oop ? qo : q, qn * e);

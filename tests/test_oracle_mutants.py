@@ -1,5 +1,6 @@
 """Plant plausible mistakes in copies of the CPU oracle and check that the
-pins in test_oracle_pins.py catch every one.
+pins (test_oracle_pins.py, test_oracle_attention_pins.py,
+test_oracle_xpos_pins.py) catch every one.
 
 Each mutant is one textual change of rope_oracle.c (which must match exactly
 once), compiled with gcc into a temporary library and run under the pin suite
@@ -63,6 +64,16 @@ MUTANTS = {
     "attn_query_offset": ("qp[i] = (int32_t)(i + Sk - Sq);", "qp[i] = (int32_t)i;"),
     "pass_through_dims_rotated": ("for (int64_t i = 0; i < R / 2; ++i) {\n          float c32, s32;",
                                   "for (int64_t i = 0; i < D / 2; ++i) {\n          float c32, s32;"),
+    "xpos_key_sign": ("return pow(oracle_xpos_zeta(gamma, rotary_dim, i), is_key ? -e : e);",
+                      "return pow(oracle_xpos_zeta(gamma, rotary_dim, i), e);"),
+    "xpos_second_unscaled": ("store_elem(y, row + jb, dtype, (a1 * sg + a2 * cs) * f32);",
+                             "store_elem(y, row + jb, dtype, (a1 * sg + a2 * cs));"),
+    "xpos_zeta_over_r": ("return ((double)i / ((double)rotary_dim / 2.0) + gamma) / (1.0 + gamma);",
+                         "return ((double)i / (double)rotary_dim + gamma) / (1.0 + gamma);"),
+    "xpos_center_ignored": ("double e = ((double)p - center) / scale_base;",
+                            "double e = (double)p / scale_base;"),
+    "xpos_exact_unscaled": ("y[row + ja] = (a1 * cs - a2 * sg) * f;",
+                            "y[row + ja] = (a1 * cs - a2 * sg);"),
 }
 
 
@@ -78,7 +89,8 @@ def _run_mutant(name, old, new, tmp):
     env = dict(os.environ, ROPE_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_attention_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_attention_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_xpos_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-2000:]
 

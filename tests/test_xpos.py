@@ -1,23 +1,11 @@
-"""RoPE with XPOS scaling (rope_apply_xpos): oracle pins, host emulation, GPU parity.
+"""RoPE with XPOS scaling (rope_apply_xpos): host emulation and GPU parity.
 
-The pages name XPOS (rotary-embedding-torch docs, Key Parameters: use_xpos)
-without its formula; the oracle follows the xPos paper's scales (Sun et al.,
-"A Length-Extrapolatable Transformer"): pair i of a query at n is scaled by
-zeta_i^((n-c)/B), of a key at m by zeta_i^(-(m-c)/B), with
-zeta_i = (i/(R/2) + gamma)/(1 + gamma).
+The oracle (oracle_rope_xpos) and its pins are in test_oracle_xpos_pins.py.
+Here: the library's host table builder equals the oracle's tables bit for
+bit; the kernel body runs on the CPU under AddressSanitizer over every lane
+of the planned grid (tests/emu/xpos_emu.hip) and through the C ABI on the
+GPU, each against the oracle; and the C ABI's argument checks.
 
-Pins of the oracle (CPU, independent of it):
-  - zeta and the factor tables against mpmath at 60 digits, each entry
-    rounded once to float32 (skipping entries within binary64 error of a
-    float32 rounding boundary); closed forms zeta_0 = gamma/(1+gamma), the
-    factor 1 at p = c, zeta_i and 1/zeta_i one scale base away;
-  - table-mode outputs against exact rational arithmetic on Fractions,
-    rounded to the storage format by tests/_exact.py;
-  - in exact mode, a query and a key at the same position keep their plain
-    dot product (the factors cancel and the rotation is orthogonal), and
-    moving both positions by the same amount leaves every pairwise product
-    unchanged (only n - m matters);
-  - with every position at c the result is plain RoPE, bit for bit.
 Kernel tolerance: 16-bit outputs within 1 unit of the monotone order (as
 rope_apply); float32 outputs within 2 float32 ulps (the kernel rounds the
 rotation and the product with the factor to float32, the oracle rounds the
@@ -27,9 +15,6 @@ import fcntl
 import os
 import subprocess
 import tempfile
-from fractions import Fraction
-
-import mpmath
 import numpy as np
 import pytest
 import torch
@@ -37,7 +22,6 @@ import torch
 import oracle
 import rotary_position_embedding_fwd_amd as rp
 import workloads as W
-from tests import _exact as X
 from tests import _parity as P
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -51,168 +35,13 @@ PAIR = {"split_half": 0, "interleaved": 1}
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
-# ------------------------------------------------------------ oracle pins
-
-def _zeta_mp(gamma, R, i):
-    g = mpmath.mpf(gamma)
-    return (mpmath.mpf(i) / (mpmath.mpf(R) / 2) + g) / (1 + g)
-
-
-@pytest.mark.parametrize("gamma,R", [(0.4, 128), (0.4, 32), (1.5, 64)])
-def test_zeta_closed_forms(orc, gamma, R):
-    assert oracle.xpos_zeta(gamma, R, 0) == gamma / (1 + gamma)
-    with mpmath.workdps(60):
-        for i in range(R // 2):
-            z = oracle.xpos_zeta(gamma, R, i)
-            assert abs(mpmath.mpf(z) - _zeta_mp(gamma, R, i)) <= mpmath.mpf(2) ** -52 * z
-    # zeta grows with i and stays in (0, 1)
-    zs = [oracle.xpos_zeta(gamma, R, i) for i in range(R // 2)]
-    assert all(0 < a < b < 1 for a, b in zip(zs, zs[1:]))
-
-
-@pytest.mark.parametrize("B,gamma,center", [(512.0, 0.4, 0.0), (64.0, 0.4, 100.0),
-                                            (128.0, 0.9, 37.0)])
-def test_factor_tables_against_mpmath(orc, B, gamma, center):
-    R, rows = 32, 300
-    zq, zk = oracle.xpos_table(R, rows, scale_base=B, gamma=gamma, center=center)
-    checked = 0
-    with mpmath.workdps(60):
-        for p in list(range(0, rows, 7)) + [int(center)]:
-            e = (mpmath.mpf(p) - mpmath.mpf(center)) / mpmath.mpf(B)
-            for i in range(R // 2):
-                z = _zeta_mp(gamma, R, i)
-                for got, ex in ((zq[p, i], z ** e), (zk[p, i], z ** -e)):
-                    if X.near_f32_midpoint(ex):
-                        continue
-                    assert float(got) == X.rn24_mp(ex), (p, i)
-                    checked += 1
-    assert checked > 1000
-    c = int(center)
-    assert (zq[c] == 1).all() and (zk[c] == 1).all()
-    # one scale base away: zeta_i and its reciprocal, rounded once
-    if c + int(B) < rows:
-        for i in range(R // 2):
-            z = oracle.xpos_zeta(gamma, R, i)
-            assert zq[c + int(B), i] == np.float32(z) or abs(
-                float(zq[c + int(B), i]) - z) <= 2 ** -24 * z
-            assert abs(float(zk[c + int(B), i]) - 1 / z) <= 2 ** -23 / z
-
+# ------------------------------------------------------ table builder
 
 def test_library_table_builder_matches_oracle(orc):
     for R, rows, B, g, c in [(128, 4096, 512.0, 0.4, 2048.0), (64, 100, 32.0, 0.4, 0.0)]:
         zq, zk = rp.rope_build_xpos_table(rows, R, B, g, c)
         oq, ok = oracle.xpos_table(R, rows, scale_base=B, gamma=g, center=c)
         assert np.array_equal(zq.numpy(), oq) and np.array_equal(zk.numpy(), ok)
-
-
-def _near_mid(y: Fraction, fmt: str) -> bool:
-    prec, emin, _ = X.FORMATS[fmt]
-    if y == 0:
-        return False
-    a = abs(y)
-    e = max(X._floor_log2(a), emin)
-    q = Fraction(2) ** (e - prec + 1)
-    frac = a / q - int(a / q)
-    return abs(frac - Fraction(1, 2)) * q <= a * Fraction(2) ** -50
-
-
-@pytest.mark.parametrize("dtype,pairing,is_key,direction", [
-    ("bf16", "split_half", False, 1), ("f16", "interleaved", True, -1),
-    ("f32", "split_half", True, 1), ("bf16", "interleaved", False, -1)])
-def test_table_mode_against_exact_rationals(orc, dtype, pairing, is_key, direction):
-    B_, H, S, D, R = 1, 2, 9, 24, 16
-    scale_base, gamma, center, rows = 4.0, 0.4, 3.0, 12
-    x = W.normal((B_, H, S, D), dtype, 9100 + DT[dtype])
-    xs = oracle.torch_to_storage(x)
-    pos = np.array([0, 5, -1, 11, 3, 12, 7, 2, 9], np.int32)
-    got = oracle.rope_xpos(xs, dtype, is_key=is_key, pairing=pairing, direction=direction,
-                           rotary_dim=R, pos=pos, table_rows=rows, scale_base=scale_base,
-                           gamma=gamma, center=center)
-    cos, sin = oracle.table(10000.0, R, rows)
-    zq, zk = oracle.xpos_table(R, rows, scale_base=scale_base, gamma=gamma, center=center)
-    z = zk if is_key else zq
-    fmt = dtype
-    bits = xs.view(np.uint32) if dtype == "f32" else xs
-    gbits = got.view(np.uint32) if dtype == "f32" else got
-    for h in range(H):
-        for s in range(S):
-            p = int(pos[s])
-            if p < 0 or p >= rows:
-                assert np.array_equal(gbits[0, h, s], bits[0, h, s])
-                continue
-            for i in range(R // 2):
-                j1, j2 = (i, i + R // 2) if pairing == "split_half" else (2 * i, 2 * i + 1)
-                x1 = X.value_of(int(bits[0, h, s, j1]), fmt)
-                x2 = X.value_of(int(bits[0, h, s, j2]), fmt)
-                c, sn = Fraction(float(cos[p, i])), direction * Fraction(float(sin[p, i]))
-                f = Fraction(float(z[p, i]))
-                for j, y in ((j1, (x1 * c - x2 * sn) * f), (j2, (x1 * sn + x2 * c) * f)):
-                    if _near_mid(y, fmt):
-                        continue
-                    assert int(gbits[0, h, s, j]) == X.bits_of(X.round_ne(y, fmt), fmt), \
-                        (h, s, j)
-            assert np.array_equal(gbits[0, h, s, R:], bits[0, h, s, R:])
-
-
-def test_same_position_keeps_the_dot_product(orc):
-    rng = np.random.default_rng(5)
-    S, D = 40, 64
-    q = rng.standard_normal((1, 1, S, D))
-    k = rng.standard_normal((1, 1, S, D))
-    kw = dict(rotary_dim=D, scale_base=16.0, center=7.0, table_rows=S)
-    qx = oracle.rope_xpos_exact(q, is_key=False, **kw)
-    kx = oracle.rope_xpos_exact(k, is_key=True, **kw)
-    plain = (q * k).sum(-1)
-    assert np.allclose((qx * kx).sum(-1), plain, rtol=1e-12, atol=1e-12)
-    # while each row on its own is scaled away from its input
-    assert not np.allclose(np.abs(qx).sum(-1), np.abs(q).sum(-1), rtol=1e-3)
-
-
-def test_only_relative_positions_matter(orc):
-    rng = np.random.default_rng(6)
-    D, n = 32, 12
-    q = rng.standard_normal((1, 1, n, D))
-    k = rng.standard_normal((1, 1, n, D))
-    base = rng.integers(0, 50, n).astype(np.int32)
-    kw = dict(rotary_dim=D, scale_base=8.0, gamma=0.4, table_rows=400)
-
-    def scores(shift):
-        p = base + shift
-        qx = oracle.rope_xpos_exact(q, is_key=False, pos=p, **kw)[0, 0]
-        kx = oracle.rope_xpos_exact(k, is_key=True, pos=p[::-1].copy(), **kw)[0, 0]
-        return qx @ kx.T
-
-    s0 = scores(0)
-    for shift in (1, 37, 250):
-        assert np.allclose(scores(shift), s0, rtol=1e-9, atol=1e-9)
-
-
-@pytest.mark.parametrize("n,m", [(40, 0), (3, 90), (17, 17)])
-def test_one_pair_decays_by_zeta_to_the_distance(orc, n, m):
-    # R = 2: one pair, whose product with XPOS is plain RoPE's times
-    # zeta_0^((n - m)/B), zeta_0 = gamma / (1 + gamma)
-    rng = np.random.default_rng(7)
-    q = rng.standard_normal((1, 1, 1, 2))
-    k = rng.standard_normal((1, 1, 1, 2))
-    kw = dict(rotary_dim=2, table_rows=100)
-    qx = oracle.rope_xpos_exact(q, is_key=False, pos=np.array([n], np.int32), scale_base=8.0,
-                                center=5.0, **kw)
-    kx = oracle.rope_xpos_exact(k, is_key=True, pos=np.array([m], np.int32), scale_base=8.0,
-                                center=5.0, **kw)
-    qp = oracle.rope_exact(q, pos=np.array([n], np.int32), **kw)
-    kp = oracle.rope_exact(k, pos=np.array([m], np.int32), **kw)
-    ratio = (qx * kx).sum() / (qp * kp).sum()
-    assert abs(ratio - (0.4 / 1.4) ** ((n - m) / 8.0)) <= 1e-12 * ratio
-
-
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_factor_one_is_plain_rope(orc, dtype):
-    x = oracle.torch_to_storage(W.normal((2, 3, 10, 64), dtype, 9300))
-    pos = np.full(20, 77, np.int32)
-    a = oracle.rope_xpos(x, dtype, is_key=True, pos=pos, pos_batch_stride=10, table_rows=100,
-                         center=77.0)
-    b = oracle.rope(x, dtype, pos=pos, pos_batch_stride=10, table_rows=100)
-    assert np.array_equal(a, b)
 
 
 # ------------------------------------------------------- host emulation
@@ -235,14 +64,24 @@ def emu():
 
 
 # B S Hq Hk D R dtype pairing layout oop pos_kind direction scale_base center
+# and the chunk width the plan picks (0: element shape)
 CASES = [
-    (1, 37, 3, 1, 64, 64, "bf16", "split_half", "bhsd", False, "none", 1, 512.0, 0.0),
-    (2, 19, 4, 2, 128, 96, "f16", "split_half", "bshd", True, "none", -1, 16.0, 9.0),
-    (1, 50, 2, 2, 64, 32, "f32", "interleaved", "bhsd", True, "skip", 1, 8.0, 25.0),
-    (2, 7, 5, 0, 72, 40, "bf16", "interleaved", "bshd", False, "skip", 1, 4.0, 0.0),
-    (1, 30, 2, 1, 65, 64, "f32", "split_half", "bhsd", True, "none", -1, 32.0, 15.0),
-    (3, 1, 8, 2, 128, 128, "bf16", "split_half", "bhsd", False, "decode", 1, 512.0, 1000.0),
-    (1, 300, 1, 1, 256, 256, "f16", "split_half", "bshd", True, "none", 1, 64.0, 150.0),
+    (1, 37, 3, 1, 64, 64, "bf16", "split_half", "bhsd", False, "none", 1, 512.0, 0.0, 8),
+    (2, 19, 4, 2, 128, 96, "f16", "split_half", "bshd", True, "none", -1, 16.0, 9.0, 8),
+    (1, 50, 2, 2, 64, 32, "f32", "interleaved", "bhsd", True, "skip", 1, 8.0, 25.0, 4),
+    (2, 7, 5, 0, 72, 40, "bf16", "interleaved", "bshd", False, "skip", 1, 4.0, 0.0, 8),
+    (1, 30, 2, 1, 65, 64, "f32", "split_half", "bhsd", True, "none", -1, 32.0, 15.0, 1),
+    (3, 1, 8, 2, 128, 128, "bf16", "split_half", "bhsd", False, "decode", 1, 512.0, 1000.0, 8),
+    (1, 300, 1, 1, 256, 256, "f16", "split_half", "bshd", True, "none", 1, 64.0, 150.0, 8),
+    (1, 11, 2, 1, 66, 36, "bf16", "interleaved", "bhsd", True, "skip", -1, 16.0, 3.0, 2),
+    (1, 5, 2, 2, 33, 20, "f16", "interleaved", "bshd", False, "none", 1, 8.0, 2.0, 0),
+    (2, 9, 3, 1, 34, 32, "bf16", "split_half", "bhsd", True, "none", 1, 64.0, 4.0, 2),
+    (1, 13, 2, 2, 68, 64, "f16", "split_half", "bhsd", False, "skip", 1, 32.0, 6.0, 4),
+    (1, 200, 3, 0, 12, 12, "f32", "interleaved", "bshd", True, "skip", 1, 2.0, 50.0, 4),
+    # enough lanes for 4 heads per lane: one group spans Q and K, the last is
+    # ragged; and the token-slow order of views with adjacent heads
+    (1, 16384, 3, 3, 64, 64, "bf16", "split_half", "bhsd", False, "none", 1, 512.0, 8192.0, 8),
+    (1, 9000, 5, 2, 64, 48, "f16", "interleaved", "bshd", True, "skip", -1, 512.0, 100.0, 8),
 ]
 
 
@@ -265,7 +104,7 @@ def _positions(kind, B, S, rows, seed):
 
 
 def _case_data(c, seed=9500):
-    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c
+    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c[:14]
     shape_q = (B, Hq, S, D) if layout == "bhsd" else (B, S, Hq, D)
     shape_k = (B, Hk, S, D) if layout == "bhsd" else (B, S, Hk, D)
     q = W.normal(shape_q, dtype, seed)
@@ -278,7 +117,7 @@ def _case_data(c, seed=9500):
 
 
 def _expected(c, q, k, pos, pbs, rows):
-    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c
+    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c[:14]
     kw = dict(layout=layout, pairing=pairing, direction=direction, rotary_dim=R, pos=pos,
               pos_batch_stride=pbs, table_rows=rows, scale_base=sb, gamma=0.4, center=center)
     eq = oracle.rope_xpos(oracle.torch_to_storage(q), dtype, is_key=False, **kw)
@@ -310,7 +149,7 @@ def check(got, ref, dtype, what):
 
 
 def run_emu(emu, c, q, k, pos, pbs, rows, cos, sin, zq, zk):
-    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c
+    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c[:14]
     qs = oracle.torch_to_storage(q)
     ks = None if k is None else oracle.torch_to_storage(k)
     with tempfile.TemporaryDirectory() as job:
@@ -334,9 +173,12 @@ def run_emu(emu, c, q, k, pos, pbs, rows, cos, sin, zq, zk):
         env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
         r = subprocess.run([emu, job], capture_output=True, text=True, timeout=300, env=env)
         assert r.returncode == 0, r.stdout + r.stderr[-4000:]
-        status = int(r.stdout.split()[1])
+        out = dict(line.split() for line in r.stdout.strip().splitlines())
+        status = int(out["status"])
         if status:
             return status, None, None
+        run_emu.last_vec = int(out["vec"])
+        run_emu.last_group = int(out["heads_per_group"])
         go = np.fromfile(os.path.join(job, "q_out.bin"), dtype=qs.dtype).reshape(qs.shape)
         gk = None if ks is None else np.fromfile(os.path.join(job, "k_out.bin"),
                                                  dtype=ks.dtype).reshape(ks.shape)
@@ -348,6 +190,10 @@ def test_emulated_kernel_matches_oracle(orc, emu, c):
     q, k, pos, pbs, rows, cos, sin, zq, zk = _case_data(c)
     status, gq, gk = run_emu(emu, c, q, k, pos, pbs, rows, cos, sin, zq, zk)
     assert status == 0
+    assert run_emu.last_vec == c[14]  # the shape this case is meant to cover
+    if c[1] * c[4] >= 9000 * 64:
+        # 4 heads per lane; views with adjacent heads run one head per lane
+        assert run_emu.last_group == (1 if c[8] == "bshd" else 4)
     eq, ek = _expected(c, q, k, pos, pbs, rows)
     dtype = c[6]
     check(gq, eq, dtype, "q")
@@ -421,7 +267,7 @@ def test_abi_table_builder_errors():
 # ------------------------------------------------------------ on the GPU
 
 def _gpu_call(c, q, k, pos, pbs, rows, cos, sin, zq, zk, stream=None):
-    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c
+    B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center = c[:14]
     dev = "cuda"
     qd = q.to(dev)
     kd = None if k is None else k.to(dev)
@@ -458,7 +304,7 @@ def test_gpu_full_llama_size(orc, direction):
     # the Llama GQA prefill shape in place, every element against the oracle
     w = W.LLAMA_GQA_PREFILL
     c = (w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim, w.rotary_dim, w.dtype,
-         w.pairing, w.layout, False, "none", direction, 512.0, w.seq_len / 2)
+         w.pairing, w.layout, False, "none", direction, 512.0, w.seq_len / 2, 8)
     print(f"xpos full size, direction {direction}", flush=True)
     t = W.tensors(w, ("q", "k"))
     rows = w.table_rows
