@@ -355,7 +355,7 @@ def time_xpos(target_s: float = 0.15):
                "views": "[B,H,S,D]" if layout == "bhsd" else "packed QKV [B,S,H,D]",
                "xpos": {"scale_base": 512.0, "gamma": 0.4, "center": w.seq_len / 2},
                "buffer_sets": 3, "algorithmic_bytes_per_call": nbytes,
-               "kernel": "rope_xpos_kernel (16-byte chunks, 4 heads per lane)"}
+               "kernel": "rope_xpos_kernel (16-byte chunks, 8 heads per lane)"}
         _time_calls(out, fwd, bwd, 3, nbytes, target_s, stream, method="rope_apply_xpos")
         results.append(out)
         plain_bytes = algorithmic_bytes(w, None)

@@ -6,10 +6,10 @@
 
 namespace {
 
-template <typename T, int V, int PAIR>
+template <typename T, int V, int PAIR, int U>
 __global__ void __launch_bounds__(rope::xpos::kBlock)
     rope_xpos_kernel(rope::xpos::XArgs a) {
-  rope::xpos::xpos_block<T, V, PAIR>(a, blockIdx.x, (int)threadIdx.x);
+  rope::xpos::xpos_block<T, V, PAIR, U>(a, blockIdx.x, (int)threadIdx.x);
 }
 
 template <typename T>
@@ -21,9 +21,9 @@ __global__ void __launch_bounds__(rope::xpos::kBlock)
 struct Launcher {
   const rope::xpos::XPlan& pl;
   hipStream_t st;
-  template <typename T, int V, int PAIR>
+  template <typename T, int V, int PAIR, int U>
   void chunked() {
-    hipLaunchKernelGGL((rope_xpos_kernel<T, V, PAIR>), dim3((unsigned)pl.grid),
+    hipLaunchKernelGGL((rope_xpos_kernel<T, V, PAIR, U>), dim3((unsigned)pl.grid),
                        dim3(rope::xpos::kBlock), 0, st, pl.a);
   }
   template <typename T>

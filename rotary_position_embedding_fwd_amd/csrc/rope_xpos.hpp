@@ -14,7 +14,8 @@
 // the same tables.
 //
 // Chunked shape (xpos_block): a lane owns one chunk of one token and walks
-// it over a group of heads, loading the chunk's cos, sin and factors once. A
+// it over a group of heads, loading the chunk's cos, sin and factors once and
+// issuing several heads' loads before their stores. A
 // chunk is V contiguous elements moved as one access, V the widest that
 // every view's alignment allows (as for rope_apply): split-half chunk c
 // covers pairs cV .. cV+V-1 (dims cV.. and R/2+cV..), interleaved chunk c the
@@ -140,7 +141,7 @@ ROPE_HD void load_tables(const XArgs& a, int64_t p, int first, bool key, float* 
 // token, walked over a group of G heads (Q heads first, then K heads), so
 // the chunk's cos, sin and factors are loaded once for G rows. Items run
 // chunk fastest, then token, then head group.
-template <typename T, int V, int PAIR>
+template <typename T, int V, int PAIR, int U>
 ROPE_HD void xpos_block(const XArgs& a, int64_t blk, int t) {
   constexpr int NP = PAIR == kSplitHalf ? V : V / 2;  // pairs per chunk
   static_assert(NP >= 1, "an interleaved chunk holds at least one pair");
@@ -197,38 +198,59 @@ ROPE_HD void xpos_block(const XArgs& a, int64_t blk, int t) {
 #pragma unroll
     for (int j = 0; j < NP; ++j) sn[j] *= a.sin_sign;
   }
-  for (int head = h0; head < h1; ++head) {
-    const float* z = head >= a.n_heads_q ? zk : zq;
-    const T* in = row(head, false);
-    T* out = row(head, true);
+  // U heads at a time: all their loads are issued before the first store
+  constexpr int kU = U;
+  for (int hb = h0; hb < h1; hb += kU) {
     if constexpr (PAIR == kSplitHalf) {
-      Chunk<T, V, true> x1, x2;
-      x1.load(in + c * V);
-      x2.load(in + a.half + c * V);
-      if (rot) {
+      Chunk<T, V, true> x1[kU], x2[kU];
 #pragma unroll
-        for (int j = 0; j < NP; ++j) {
-          float y1, y2;
-          rotate_pair(to_f32(x1.v[j]), to_f32(x2.v[j]), cs[j], sn[j], y1, y2);
-          x1.v[j] = from_f32<T>(y1 * z[j]);
-          x2.v[j] = from_f32<T>(y2 * z[j]);
+      for (int u = 0; u < kU; ++u) {
+        if (hb + u < h1) {
+          const T* in = row(hb + u, false);
+          x1[u].load(in + c * V);
+          x2[u].load(in + a.half + c * V);
         }
       }
-      x1.store(out + c * V);
-      x2.store(out + a.half + c * V);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (hb + u < h1) {
+          const float* z = hb + u >= a.n_heads_q ? zk : zq;
+          if (rot) {
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+              float y1, y2;
+              rotate_pair(to_f32(x1[u].v[j]), to_f32(x2[u].v[j]), cs[j], sn[j], y1, y2);
+              x1[u].v[j] = from_f32<T>(y1 * z[j]);
+              x2[u].v[j] = from_f32<T>(y2 * z[j]);
+            }
+          }
+          T* out = row(hb + u, true);
+          x1[u].store(out + c * V);
+          x2[u].store(out + a.half + c * V);
+        }
+      }
     } else {
-      Chunk<T, V, true> x;
-      x.load(in + c * V);
-      if (rot) {
+      Chunk<T, V, true> x[kU];
 #pragma unroll
-        for (int j = 0; j < NP; ++j) {
-          float y1, y2;
-          rotate_pair(to_f32(x.v[2 * j]), to_f32(x.v[2 * j + 1]), cs[j], sn[j], y1, y2);
-          x.v[2 * j] = from_f32<T>(y1 * z[j]);
-          x.v[2 * j + 1] = from_f32<T>(y2 * z[j]);
+      for (int u = 0; u < kU; ++u)
+        if (hb + u < h1) x[u].load(row(hb + u, false) + c * V);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (hb + u < h1) {
+          const float* z = hb + u >= a.n_heads_q ? zk : zq;
+          if (rot) {
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+              float y1, y2;
+              rotate_pair(to_f32(x[u].v[2 * j]), to_f32(x[u].v[2 * j + 1]), cs[j], sn[j], y1,
+                          y2);
+              x[u].v[2 * j] = from_f32<T>(y1 * z[j]);
+              x[u].v[2 * j + 1] = from_f32<T>(y2 * z[j]);
+            }
+          }
+          x[u].store(row(hb + u, true) + c * V);
         }
       }
-      x.store(out + c * V);
     }
   }
 }
@@ -299,15 +321,15 @@ inline rope_status_t make_xpos_plan(const rope_apply_desc_t* d, const float* zq,
     a.chunks = (int32_t)((a.interleaved ? d->rotary_dim : d->rotary_dim / 2) / v);
     const int64_t copies = oop ? (d->head_dim - d->rotary_dim + v - 1) / v : 0;
     a.row_items = (int32_t)(a.chunks + copies);
-    // 4 heads per lane (the rows kernel's measured best for the Llama shape),
-    // fewer when that would leave the chip short of lanes. Views whose heads
-    // of a token are adjacent in memory ([B,S,H,D], packed QKV) run one head
-    // per lane, token-slow, so a wave's lanes sweep each token's rows in
-    // memory order (measured on MI355X, Llama shape as packed QKV: 72 us
-    // that way, 88 us with 4 heads per lane).
+    // 8 heads per lane, fewer when that would leave the chip short of lanes
+    // (measured on MI355X, Llama prefill [B,H,S,D]: 62.1 us with 8, 64.4 us
+    // with 4, 73.5 us with 2). Views whose heads of a token are adjacent in
+    // memory ([B,S,H,D], packed QKV) run one head per lane, token-slow, so a
+    // wave's lanes sweep each token's rows in memory order (Llama shape as
+    // packed QKV: 72 us that way, 88 us with 4 heads per lane).
     const int64_t h_total = d->n_heads_q + d->n_heads_k;
     a.token_major = (d->n_heads_q > 1 && d->q_in.stride_h < d->q_in.stride_s) ? 1 : 0;
-    int64_t g = a.token_major ? 1 : (h_total < 4 ? h_total : 4);
+    int64_t g = a.token_major ? 1 : (h_total < 8 ? h_total : 8);
     while (g > 1 && ((h_total + g - 1) / g) * a.n_tokens * a.row_items < 256 * 256) g /= 2;
     a.heads_per_group = (int32_t)g;
     a.n_groups = (int32_t)((h_total + g - 1) / g);
@@ -354,29 +376,38 @@ inline rope_status_t make_xpos_plan(const rope_apply_desc_t* d, const float* zq,
   return ROPE_OK;
 }
 
-// Calls f.template chunked<T, V, PAIR>() or f.template element<T>() for the
-// plan's shape (F: the GPU launcher, or the host emulation). False for a
-// combination no plan produces.
+// Calls f.template chunked<T, V, PAIR, U>() or f.template element<T>() for
+// the plan's shape (F: the GPU launcher, or the host emulation). U: heads
+// whose loads go out together, 4 when a lane walks several heads (one head
+// per lane keeps the register count, and occupancy, of a single head:
+// measured on MI355X, packed QKV Llama, 79 us with U = 4 against 72 us).
+// False for a combination no plan produces.
+template <typename T, int V, int PAIR, class F>
+void dispatch_u(const XPlan& pl, F& f) {
+  if (pl.a.heads_per_group > 1) f.template chunked<T, V, PAIR, 4>();
+  else f.template chunked<T, V, PAIR, 1>();
+}
+
 template <typename T, int VMAX, class F>
 bool dispatch_vec(const XPlan& pl, F& f) {
   const bool inter = pl.a.interleaved != 0;
   switch (pl.vec) {
     case 1:
       if (inter) return false;
-      f.template chunked<T, 1, kSplitHalf>();
+      dispatch_u<T, 1, kSplitHalf>(pl, f);
       return true;
     case 2:
-      if (inter) f.template chunked<T, 2, kInterleaved>();
-      else f.template chunked<T, 2, kSplitHalf>();
+      if (inter) dispatch_u<T, 2, kInterleaved>(pl, f);
+      else dispatch_u<T, 2, kSplitHalf>(pl, f);
       return true;
     case 4:
-      if (inter) f.template chunked<T, 4, kInterleaved>();
-      else f.template chunked<T, 4, kSplitHalf>();
+      if (inter) dispatch_u<T, 4, kInterleaved>(pl, f);
+      else dispatch_u<T, 4, kSplitHalf>(pl, f);
       return true;
     case 8:
       if constexpr (VMAX >= 8) {
-        if (inter) f.template chunked<T, 8, kInterleaved>();
-        else f.template chunked<T, 8, kSplitHalf>();
+        if (inter) dispatch_u<T, 8, kInterleaved>(pl, f);
+        else dispatch_u<T, 8, kSplitHalf>(pl, f);
         return true;
       }
       return false;

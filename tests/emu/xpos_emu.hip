@@ -63,11 +63,11 @@ void write_file(const std::string& path, const void* p, size_t bytes) {
 // Every lane of every workgroup of the planned grid, one after another.
 struct HostRunner {
   const rope::xpos::XPlan& pl;
-  template <typename T, int V, int PAIR>
+  template <typename T, int V, int PAIR, int U>
   void chunked() {
     for (int64_t blk = 0; blk < pl.grid; ++blk)
       for (int t = 0; t < rope::xpos::kBlock; ++t)
-        rope::xpos::xpos_block<T, V, PAIR>(pl.a, blk, t);
+        rope::xpos::xpos_block<T, V, PAIR, U>(pl.a, blk, t);
   }
   template <typename T>
   void element() {

@@ -78,9 +78,9 @@ CASES = [
     (2, 9, 3, 1, 34, 32, "bf16", "split_half", "bhsd", True, "none", 1, 64.0, 4.0, 2),
     (1, 13, 2, 2, 68, 64, "f16", "split_half", "bhsd", False, "skip", 1, 32.0, 6.0, 4),
     (1, 200, 3, 0, 12, 12, "f32", "interleaved", "bshd", True, "skip", 1, 2.0, 50.0, 4),
-    # enough lanes for 4 heads per lane: one group spans Q and K, the last is
+    # enough lanes for 8 heads per lane: one group spans Q and K, the last is
     # ragged; and the token-slow order of views with adjacent heads
-    (1, 16384, 3, 3, 64, 64, "bf16", "split_half", "bhsd", False, "none", 1, 512.0, 8192.0, 8),
+    (1, 16384, 5, 5, 64, 64, "bf16", "split_half", "bhsd", False, "none", 1, 512.0, 8192.0, 8),
     (1, 9000, 5, 2, 64, 48, "f16", "interleaved", "bshd", True, "skip", -1, 512.0, 100.0, 8),
 ]
 
@@ -192,8 +192,8 @@ def test_emulated_kernel_matches_oracle(orc, emu, c):
     assert status == 0
     assert run_emu.last_vec == c[14]  # the shape this case is meant to cover
     if c[1] * c[4] >= 9000 * 64:
-        # 4 heads per lane; views with adjacent heads run one head per lane
-        assert run_emu.last_group == (1 if c[8] == "bshd" else 4)
+        # 8 heads per lane; views with adjacent heads run one head per lane
+        assert run_emu.last_group == (1 if c[8] == "bshd" else 8)
     eq, ek = _expected(c, q, k, pos, pbs, rows)
     dtype = c[6]
     check(gq, eq, dtype, "q")
