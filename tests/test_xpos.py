@@ -82,6 +82,11 @@ CASES = [
     # ragged; and the token-slow order of views with adjacent heads
     (1, 16384, 5, 5, 64, 64, "bf16", "split_half", "bhsd", False, "none", 1, 512.0, 8192.0, 8),
     (1, 9000, 5, 2, 64, 48, "f16", "interleaved", "bshd", True, "skip", -1, 512.0, 100.0, 8),
+    # split-half in place with 16-byte chunks: 4 (f32), 16 and 1 chunks per
+    # half, skipped tokens, backward
+    (2, 40, 4, 2, 32, 32, "f32", "split_half", "bhsd", False, "skip", -1, 16.0, 10.0, 4),
+    (1, 20, 2, 1, 256, 256, "bf16", "split_half", "bhsd", False, "none", 1, 64.0, 5.0, 8),
+    (1, 30, 3, 3, 64, 16, "bf16", "split_half", "bhsd", False, "skip", 1, 8.0, 3.0, 8),
 ]
 
 
