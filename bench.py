@@ -410,8 +410,10 @@ def time_attention(target_s: float = 0.5):
     """Attention over rotated Q and K: the fused call (rope_attention_fwd,
     rotation inside the kernel) against the unfused sequence (rope_apply
     writing rotated copies of Q and K, then the same attention kernel with
-    rotation off), on the causal Llama GQA prefill shape and on the
-    CLS-skipping partial-rotary example. One JSON object per workload."""
+    rotation off) and the K-once call (rope_attention_fwd_k_once: rope(K)
+    into a workspace, Q rotated in the kernel), on the causal Llama GQA
+    prefill shape and on the CLS-skipping partial-rotary example. One JSON
+    object per workload."""
     import torch
     import rotary_position_embedding_fwd_amd as rp
     import workloads as W
@@ -430,8 +432,11 @@ def time_attention(target_s: float = 0.5):
         rot = rp.prepare_apply(t["q"], t["k"], c, s, q_out=qr, k_out=kr, pairing=w.pairing,
                                rotary_dim=w.rotary_dim, pos=pos, stream=stream)
         plain = rp.prepare_attention(qr, kr, t["v"], c, s, o, rotate=False, **kw)
+        # K rotated once into a workspace, only Q rotated in the kernel
+        k_once = rp.prepare_attention(t["q"], t["k"], t["v"], c, s, o, k_workspace=kr, **kw)
         flops = attention_flops(w)
         fused_us, reps = _time_event(fused.rope_attention_fwd, stream, target_s)
+        k_once_us, _ = _time_event(k_once.rope_attention_fwd, stream, target_s)
         plain_us, _ = _time_event(plain.rope_attention_fwd, stream, target_s)
         rot_us, _ = _time_event(rot.rope_apply, stream, target_s / 4)
 
@@ -451,10 +456,14 @@ def time_attention(target_s: float = 0.5):
             "rotation_out_of_place_us": round(rot_us, 2),
             "unfused_us_per_call": round(unfused_us, 2),
             "fused_saves_us": round(unfused_us - fused_us, 2),
+            "k_once_us_per_call": round(k_once_us, 2),
+            "k_once_TFLOPs": round(flops / (k_once_us * 1e-6) / 1e12, 1),
+            "k_once_frac_of_mfma_bf16_peak": round(
+                flops / (k_once_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "reps": reps,
             "kernel": "rope_attention_kernel (v_mfma_f32_32x32x16_bf16)",
         })
-        del t, o, qr, kr, fused, rot, plain
+        del t, o, qr, kr, fused, rot, plain, k_once
         torch.cuda.empty_cache()
     return results
 

@@ -312,6 +312,9 @@ typedef struct rope_attn_desc {
   const int32_t *k_pos;
   int64_t k_pos_batch_stride;
   double scale;
+  int32_t k_rotated;    /* 1: K already holds rope(K) (e.g. from rope_fwd_qk); only Q
+                           is rotated in the kernel. 0: both (the fused form) */
+  int32_t reserved;     /* set to 0 */
 } rope_attn_desc_t;
 
 /* Enqueue the fused attention on `stream`. Errors as rope_apply:
@@ -322,6 +325,20 @@ typedef struct rope_attn_desc {
  * ROPE_ERR_LAYOUT for an unknown pairing, ROPE_ERR_ALIGN, ROPE_ERR_ALIAS when
  * O overlaps an input. */
 rope_status_t rope_attention_fwd(const rope_attn_desc_t *d, void *stream);
+
+/* The same attention with K rotated once instead of once per workgroup:
+ * rope_apply writes rope(K) into the caller's `k_workspace` (device,
+ * 16-byte aligned, B*Hk*Sk*D bf16 elements, laid out like K), then
+ * rope_attention_fwd runs on it with k_rotated = 1, both on `stream`. The
+ * result equals rope_attention_fwd's bit for bit. On long sequences, where
+ * many workgroups read each K tile, this is the faster form. For callers
+ * that can spare a K-sized buffer; the library still allocates nothing.
+ * Errors as rope_attention_fwd (d->k_rotated must be 0), and ROPE_ERR_NULL /
+ * ROPE_ERR_ALIGN / ROPE_ERR_ALIAS for a missing or misaligned workspace or
+ * one that overlaps any operand. With no rotation (rotate = 0 or R = 0) the
+ * workspace is not touched. */
+rope_status_t rope_attention_fwd_k_once(const rope_attn_desc_t *d, void *k_workspace,
+                                        void *stream);
 
 /* Fill host float32 tables cos_out/sin_out, each [table_rows, R/2] row-major,
  * with cos and sin of (p / interpolate_factor) * theta^(-2i/R) for row p and

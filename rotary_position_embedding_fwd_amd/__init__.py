@@ -102,6 +102,7 @@ class RopeAttnDesc(ctypes.Structure):
         ("q_pos", ctypes.c_void_p), ("q_pos_batch_stride", ctypes.c_int64),
         ("k_pos", ctypes.c_void_p), ("k_pos_batch_stride", ctypes.c_int64),
         ("scale", ctypes.c_double),
+        ("k_rotated", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -141,6 +142,8 @@ def lib():
                                             ctypes.c_double, ctypes.c_double, ctypes.c_double]
         L.rope_build_xpos_table.restype = ctypes.c_int
         L.rope_attention_fwd.argtypes = [ctypes.POINTER(RopeAttnDesc), P]
+        L.rope_attention_fwd_k_once.argtypes = [ctypes.POINTER(RopeAttnDesc), P, P]
+        L.rope_attention_fwd_k_once.restype = ctypes.c_int
         L.rope_attention_fwd.restype = ctypes.c_int
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_status_string.restype = ctypes.c_char_p
@@ -541,7 +544,8 @@ def make_attn_desc(q, k, v, cos, sin, o, *, pairing: str = "split_half",
                    rotary_dim: Optional[int] = None, causal: bool = False,
                    rotate: bool = True, q_pos=None, k_pos=None,
                    q_pos_batch_stride: Optional[int] = None,
-                   k_pos_batch_stride: Optional[int] = None, scale: float = 0.0) -> RopeAttnDesc:
+                   k_pos_batch_stride: Optional[int] = None, scale: float = 0.0,
+                   k_rotated: bool = False) -> RopeAttnDesc:
     """rope_attn_desc_t for q [B,Hq,Sq,D], k and v [B,Hk,Sk,D], o like q (all
     contiguous bf16). rotary_dim defaults to 2 * cos.shape[1]; positions
     default to key j at j and query i at i + Sk - Sq. An index with at least
@@ -577,33 +581,57 @@ def make_attn_desc(q, k, v, cos, sin, o, *, pairing: str = "split_half",
     d.q_pos, d.q_pos_batch_stride = _index(q_pos, B, Sq, q_pos_batch_stride, "q_pos")
     d.k_pos, d.k_pos_batch_stride = _index(k_pos, B, Sk, k_pos_batch_stride, "k_pos")
     d.scale = float(scale)
+    d.k_rotated = int(bool(k_rotated))
     return d
 
 
-def rope_attention(q, k, v, cos, sin, *, o=None, stream=None, **kw):
-    """Attention over RoPE-rotated q and k in one launch (rope_attention_fwd):
-    softmax(scale * rope(q) rope(k)^T [causal]) v, GQA by head groups. The
-    rotated q and k are never written. Returns o (allocated if not given)."""
+def _k_workspace(k_workspace, k):
+    if k_workspace is None:
+        return None
+    if (k_workspace.dtype != k.dtype or tuple(k_workspace.shape) != tuple(k.shape) or
+            not k_workspace.is_contiguous()):
+        raise ValueError("k_workspace must be a contiguous tensor like k")
+    return k_workspace.data_ptr()
+
+
+def rope_attention(q, k, v, cos, sin, *, o=None, stream=None, k_workspace=None, **kw):
+    """Attention over RoPE-rotated q and k (rope_attention_fwd):
+    softmax(scale * rope(q) rope(k)^T [causal]) v, GQA by head groups, in one
+    launch, the rotated q and k never written. With k_workspace (a tensor
+    like k), rope(k) is written there once and the attention rotates only q
+    (rope_attention_fwd_k_once): the same result, faster on long sequences.
+    Returns o (allocated if not given)."""
     import torch
     if o is None:
         o = torch.empty_like(q)
     d = make_attn_desc(q, k, v, cos, sin, o, **kw)
-    _check(lib().rope_attention_fwd(ctypes.byref(d), _stream(stream)), "rope_attention_fwd")
+    ws = _k_workspace(k_workspace, k)
+    if ws is None:
+        _check(lib().rope_attention_fwd(ctypes.byref(d), _stream(stream)), "rope_attention_fwd")
+    else:
+        _check(lib().rope_attention_fwd_k_once(ctypes.byref(d), ws, _stream(stream)),
+               "rope_attention_fwd_k_once")
     return o
 
 
 class PreparedAttention:
     """A rope_attention_fwd call whose descriptor is built once (see Prepared)."""
 
-    def __init__(self, q, k, v, cos, sin, o, stream=None, **kw):
-        self._keep = (q, k, v, cos, sin, o, kw.get("q_pos"), kw.get("k_pos"))
+    def __init__(self, q, k, v, cos, sin, o, stream=None, k_workspace=None, **kw):
+        self._keep = (q, k, v, cos, sin, o, kw.get("q_pos"), kw.get("k_pos"), k_workspace)
         self.desc = make_attn_desc(q, k, v, cos, sin, o, **kw)
+        self._ws = _k_workspace(k_workspace, k)
         self._stream = _stream(stream)
         self._pdesc = ctypes.byref(self.desc)
         self._lib = lib()
 
     def rope_attention_fwd(self):
-        _check(self._lib.rope_attention_fwd(self._pdesc, self._stream), "rope_attention_fwd")
+        """The fused call, or with a workspace the K-once call."""
+        if self._ws is None:
+            _check(self._lib.rope_attention_fwd(self._pdesc, self._stream), "rope_attention_fwd")
+        else:
+            _check(self._lib.rope_attention_fwd_k_once(self._pdesc, self._ws, self._stream),
+                   "rope_attention_fwd_k_once")
 
 
 def prepare_attention(q, k, v, cos, sin, o, *, stream=None, **kw) -> PreparedAttention:

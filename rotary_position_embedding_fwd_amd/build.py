@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librope.so")
-SOURCES = [os.path.join(CSRC, "librope.hip"), os.path.join(CSRC, "rope_xpos.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("librope.hip", "rope_attention.hip",
+                                            "rope_xpos.hip")]
 PROBE_LIB = os.path.join(PKG, "libstream_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]
 HEADERS = [os.path.join(CSRC, "rope_kernels.hpp"), os.path.join(INCLUDE, "librope.h")]

@@ -11,7 +11,6 @@
 
 #include "librope.h"
 #include "rope_kernels.hpp"
-#include "rope_attn_plan.hpp"
 #include "rope_plan.hpp"
 
 namespace {
@@ -112,44 +111,6 @@ rope_status_t run(void* q, void* k, const rope_desc_t* d, void* stream, bool wit
 
 }  // namespace
 
-// ------------------------------------------------------- fused attention
-namespace {
-
-template <int D, int PAIR, int H16>
-hipError_t launch_attention(const rope::attn::AttnPlan& pl, hipStream_t st) {
-  auto kernel = rope::attn::rope_attention_kernel<D, PAIR, H16>;
-  // the double-buffered tiles take more than the default 64 KiB of dynamic
-  // LDS at head dim 128: raise the kernel's limit once (per process; the
-  // attribute belongs to the kernel, not to a device)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      rope::attn::lds_bytes<D>());
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)pl.grid), dim3(rope::attn::kBlock), (unsigned)pl.lds,
-                     st, pl.a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_attention_d(const rope::attn::AttnPlan& pl, hipStream_t st) {
-  using rope::kInterleaved;
-  using rope::kSplitHalf;
-  if (pl.pairing == ROPE_INTERLEAVED) return launch_attention<D, kInterleaved, 0>(pl, st);
-  switch (pl.h16) {
-    case 0: return launch_attention<D, kSplitHalf, 0>(pl, st);
-    case 1: return launch_attention<D, kSplitHalf, 1>(pl, st);
-    case 2: return launch_attention<D, kSplitHalf, 2>(pl, st);
-  }
-  if constexpr (D == 128) {
-    switch (pl.h16) {
-      case 3: return launch_attention<D, kSplitHalf, 3>(pl, st);
-      case 4: return launch_attention<D, kSplitHalf, 4>(pl, st);
-    }
-  }
-  return hipErrorInvalidValue;  // unreachable: the plan bounds h16 by D / 32
-}
-
-}  // namespace
 
 extern "C" {
 
@@ -189,18 +150,6 @@ rope_status_t rope_build_table(float* cos_out, float* sin_out, int64_t table_row
     }
   }
   return ROPE_OK;
-}
-
-rope_status_t rope_attention_fwd(const rope_attn_desc_t* d, void* stream) {
-  rope::attn::AttnPlan pl;
-  const rope_status_t st = rope::attn::make_attn_plan(d, &pl);
-  if (st != ROPE_OK || pl.empty) return st;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ROPE_ERR_HIP;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = pl.head_dim == 64 ? launch_attention_d<64>(pl, s)
-                                         : launch_attention_d<128>(pl, s);
-  return e == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
 }
 
 const char* rope_status_string(rope_status_t s) {

@@ -71,6 +71,7 @@ struct AttnArgs {
   int32_t batch, n_heads_q, n_heads_k, seq_q, seq_k;
   int32_t half;          // R / 2
   int32_t rotate;        // 0: no rotation (plain attention, for the unfused path)
+  int32_t rotate_k;      // 0: K arrives rotated (or no rotation): stage it as it is
   int32_t causal;
   int32_t hw;            // query heads per workgroup (a power of 2 dividing Hq / Hk)
   int32_t rows;          // query rows of each head per workgroup: kRows / hw
@@ -283,7 +284,8 @@ template <int D, int PAIR, int H16>
 __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* kbase, int k0,
                                         int t, KStage<D, PAIR, H16>& ks) {
   using P = KPlan<D, PAIR, H16>;
-  const int R = 2 * a.half;
+  const int R = 2 * a.half;      // interleaved: the rotated dims
+  constexpr int kR = 32 * H16;   // split-half: the rotated dims, fixed by the instantiation
   const bf16x8 z = {};
   if constexpr (P::kPair > 0) {
 #pragma unroll
@@ -297,8 +299,8 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
         if (key < a.seq_k) {
           const __bf16* krow = kbase + (int64_t)key * D;
           ks.px1[n] = *reinterpret_cast<const bf16x8*>(krow + 8 * j);
-          ks.px2[n] = *reinterpret_cast<const bf16x8*>(krow + a.half + 8 * j);
-          const int64_t p = key_pos(a, b, key);
+          ks.px2[n] = *reinterpret_cast<const bf16x8*>(krow + 16 * H16 + 8 * j);
+          const int64_t p = a.rotate_k ? key_pos(a, b, key) : -1;
           if (p >= 0) {
             load_cs(a, p, 8 * j, 8, ks.pc[n], ks.ps[n]);
             ks.prot[n] = true;
@@ -315,7 +317,7 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
       if (it < kKeys * P::kCopy) {
         const int key = k0 + it / P::kCopy, j = it % P::kCopy;
         if (key < a.seq_k)
-          ks.cx[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + R + 8 * j);
+          ks.cx[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + kR + 8 * j);
       }
     }
   }
@@ -330,7 +332,7 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
         if (key < a.seq_k) {
           ks.ix[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + 8 * j);
           if (8 * j < R) {
-            const int64_t p = a.rotate ? key_pos(a, b, key) : -1;
+            const int64_t p = a.rotate_k ? key_pos(a, b, key) : -1;
             if (p >= 0) {
               load_cs(a, p, 4 * j, 4, ks.ic[n], ks.is[n]);
               ks.irot[n] = true;
@@ -348,7 +350,7 @@ template <int D, int PAIR, int H16>
 __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR, H16>& ks,
                                         __bf16* lds, int buf) {
   using P = KPlan<D, PAIR, H16>;
-  const int R = 2 * a.half;
+  constexpr int kR = 32 * H16;   // split-half: the rotated dims, fixed by the instantiation
   if constexpr (P::kPair > 0) {
 #pragma unroll
     for (int n = 0; n < P::kPairN; ++n) {
@@ -357,7 +359,7 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
         const int kk = it / P::kPair, j = it % P::kPair;
         if (ks.prot[n]) rotate_split8(ks.px1[n], ks.px2[n], ks.pc[n], ks.ps[n]);
         *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.px1[n];
-        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, a.half + 8 * j)]) = ks.px2[n];
+        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 16 * H16 + 8 * j)]) = ks.px2[n];
       }
     }
   }
@@ -367,7 +369,7 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
       const int it = t + n * kBlock;
       if (it < kKeys * P::kCopy) {
         const int kk = it / P::kCopy, j = it % P::kCopy;
-        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, R + 8 * j)]) = ks.cx[n];
+        *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, kR + 8 * j)]) = ks.cx[n];
       }
     }
   }
@@ -434,8 +436,13 @@ __device__ __forceinline__ void stage_v(int t, const VStage<D>& vs, __bf16* lds,
 // H16: split-half pairs, (R/2)/16 (the register distance between the two
 // chunks of a pair; a compile-time constant so the registers stay registers);
 // 0 for interleaved pairs.
-template <int D, int PAIR, int H16>
+template <int D, int PAIR, int H16, bool KR>
 __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
+  // K staging: rotated while staged (KR, the fused form), or copied as it
+  // arrives (K already rotated; the copy-only plan keeps no cos/sin
+  // registers for it)
+  constexpr int KP = KR ? PAIR : kSplitHalf;
+  constexpr int KH = KR ? H16 : 0;
 #if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __bf16 lds[];
   const Work wk = work_of(a, blockIdx.x);
@@ -449,6 +456,10 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   const int qi = role.row0 + (lane & 31);  // this lane's query row
   constexpr int kSteps = D / 16;  // k-steps of S^T over the head dim
   const int R = 2 * a.half;
+
+  const int n_tiles = key_tiles(a, q_tile);
+  const __bf16* kbase = a.k + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
+  const __bf16* vbase = a.v + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
 
   // ---- Q: this lane's half of its query row, rotated, as B operands.
   bf16x8 qreg[kSteps];
@@ -498,9 +509,6 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (floatx16){};
 
-  const int n_tiles = key_tiles(a, q_tile);
-  const __bf16* kbase = a.k + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
-  const __bf16* vbase = a.v + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
   const int causal_shift = a.seq_k - a.seq_q;
   // this wave's query rows, for the masking decisions (uniform per wave)
   const int wq_first = role.row0;
@@ -513,12 +521,12 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   // previous barrier, and its next readers wait for this iteration's
   // barrier. The fetched registers never cross an iteration.
   if (n_tiles > 0) {
-    KStage<D, PAIR, H16> ks;
-    VStage<D> vs;
-    fetch_k<D, PAIR, H16>(a, b, kbase, 0, t, ks);
-    fetch_v<D>(a, vbase, 0, t, vs);
-    stage_k<D, PAIR, H16>(a, t, ks, lds, 0);
-    stage_v<D>(t, vs, lds, 0);
+    KStage<D, KP, KH> ks0;
+    VStage<D> vs0;
+    fetch_k<D, KP, KH>(a, b, kbase, 0, t, ks0);
+    fetch_v<D>(a, vbase, 0, t, vs0);
+    stage_k<D, KP, KH>(a, t, ks0, lds, 0);
+    stage_v<D>(t, vs0, lds, 0);
   }
   __syncthreads();
   // a wave whose rows all lie past Sq computes nothing (it still stages)
@@ -635,10 +643,10 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
       rescale(softmax(s0, p0));
       if (edge) mask(s1, 1);
     }
-    KStage<D, PAIR, H16> ks;
+    KStage<D, KP, KH> ks;
     VStage<D> vs;
     if (more) {
-      fetch_k<D, PAIR, H16>(a, b, kbase, k0 + kKeys, t, ks);
+      fetch_k<D, KP, KH>(a, b, kbase, k0 + kKeys, t, ks);
       fetch_v<D>(a, vbase, k0 + kKeys, t, vs);
     }
     if (work) {
@@ -647,7 +655,7 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
       output(1, p1);
     }
     if (more) {
-      stage_k<D, PAIR, H16>(a, t, ks, lds, buf ^ 1);
+      stage_k<D, KP, KH>(a, t, ks, lds, buf ^ 1);
       stage_v<D>(t, vs, lds, buf ^ 1);
     }
     __syncthreads();

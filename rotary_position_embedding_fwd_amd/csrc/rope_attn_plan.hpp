@@ -43,6 +43,7 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   if (d->pairing == ROPE_SPLIT_HALF ? (R % 32) : (R % 8)) return ROPE_ERR_SHAPE;
   if (d->causal && Sq > Sk) return ROPE_ERR_SHAPE;
   if (!std::isfinite(d->scale) || d->table_rows < 0) return ROPE_ERR_SHAPE;
+  if (d->k_rotated != 0 && d->k_rotated != 1) return ROPE_ERR_SHAPE;
   // the kernel works with |scale| * log2(e) as a normal float32 (a negative
   // scale enters as a sign flip of Q)
   const double scale = d->scale != 0.0 ? d->scale : 1.0 / std::sqrt((double)D);
@@ -107,6 +108,7 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   a.seq_k = (int32_t)Sk;
   a.half = rotate ? (int32_t)(R / 2) : 0;
   a.rotate = rotate ? 1 : 0;
+  a.rotate_k = (rotate && !d->k_rotated) ? 1 : 0;
   a.causal = d->causal ? 1 : 0;
   // query heads per workgroup: the largest power of two (at most the 8
   // waves) dividing the group of query heads that share a K/V head, so one

@@ -12,8 +12,9 @@
 // no LDS cell may be written by two lanes in one phase, and every cell read
 // for tile kt must hold tile kt.
 //
-// usage: attn_bounds B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos
-//   (qpos / kpos: 0 = no index, 1 = an index of Sq / Sk entries per batch)
+// usage: attn_bounds B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos [k_rotated]
+//   (qpos / kpos: 0 = no index, 1 = an index of Sq / Sk entries per batch;
+//   k_rotated: 1 = K arrives rotated and is staged by the copy-only plan)
 // prints "plan <status>" then "violations <n>" and "accesses <n>".
 #include <algorithm>
 #include <type_traits>
@@ -49,13 +50,17 @@ struct LdsModel {
   explicit LdsModel(int n) : tile(n, -1), writer(n, -1) {}
 };
 
-template <int D, int PAIR, int H16>
+template <int D, int PAIR, int H16, bool KR>
 void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_elems,
           int64_t qpos_elems, int64_t kpos_elems, Checker& ck) {
   const AttnArgs& a = pl.a;
   const int lds_elems = lds_bytes<D>() / 2;
   const int R = 2 * a.half;
-  using P = KPlan<D, PAIR, H16>;
+  // K staging: the kernel's plan for this instantiation (rotated while
+  // staged, or the copy-only plan when K arrives rotated)
+  using P = KPlan<D, KR ? PAIR : kSplitHalf, KR ? H16 : 0>;
+  constexpr int kRK = KR ? 32 * H16 : 0;  // split-half: dims the pair items cover
+  ck.fail(KR != (a.rotate_k != 0) && a.rotate, "instantiation matches rotate_k");
   // the instantiation's item classes cover each key's D dims exactly once
   ck.fail(PAIR == kSplitHalf && R != 32 * H16, "split-half R is 32 H16");
   ck.fail(16 * P::kPair + 8 * P::kCopy + 8 * P::kInter != D, "items cover the head dim");
@@ -155,19 +160,19 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
           if (key < a.seq_k) {
             const int64_t krow = kbase + (int64_t)key * D;
             ck.check(krow + 8 * j, 8, kv_elems, "k load");
-            ck.check(krow + a.half + 8 * j, 8, kv_elems, "k load");
+            ck.check(krow + kRK / 2 + 8 * j, 8, kv_elems, "k load");
             const int64_t kp = kpos(b, key);
             if (kp >= 0) ck.check(kp * a.half + 8 * j, 8, table_elems, "k cos/sin");
           }
           wrote(k_lds<D>(buf, kk, 8 * j), 8, t, "k lds");
-          wrote(k_lds<D>(buf, kk, a.half + 8 * j), 8, t, "k lds");
+          wrote(k_lds<D>(buf, kk, kRK / 2 + 8 * j), 8, t, "k lds");
         }
         // split-half copy items: dims R + 8j..
         for (int it = t; it < kKeys * P::kCopy; it += kBlock) {
           const int kk = it / P::kCopy, j = it % P::kCopy;
           const int key = k0 + kk;
-          if (key < a.seq_k) ck.check(kbase + (int64_t)key * D + R + 8 * j, 8, kv_elems, "k load");
-          wrote(k_lds<D>(buf, kk, R + 8 * j), 8, t, "k lds");
+          if (key < a.seq_k) ck.check(kbase + (int64_t)key * D + kRK + 8 * j, 8, kv_elems, "k load");
+          wrote(k_lds<D>(buf, kk, kRK + 8 * j), 8, t, "k lds");
         }
         // interleaved items: dims 8j.., rotated when 8j < R
         for (int it = t; it < kKeys * P::kInter; it += kBlock) {
@@ -175,7 +180,7 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
           const int key = k0 + kk;
           if (key < a.seq_k) {
             ck.check(kbase + (int64_t)key * D + 8 * j, 8, kv_elems, "k load");
-            const int64_t kp = (8 * j < R && a.rotate) ? kpos(b, key) : -1;
+            const int64_t kp = (8 * j < R && a.rotate_k) ? kpos(b, key) : -1;
             if (kp >= 0) ck.check(kp * a.half + 4 * j, 4, table_elems, "k cos/sin");
           }
           wrote(k_lds<D>(buf, kk, 8 * j), 8, t, "k lds");
@@ -250,12 +255,14 @@ void edge_positions(std::vector<int32_t>& p, int64_t rows) {
 }  // namespace
 
 int main(int argc, char** argv) {
-  if (argc != 13) {
-    fprintf(stderr, "usage: attn_bounds B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos\n");
+  if (argc != 13 && argc != 14) {
+    fprintf(stderr,
+            "usage: attn_bounds B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos "
+            "[k_rotated]\n");
     return 2;
   }
-  long long v[12];
-  for (int i = 0; i < 12; ++i) v[i] = atoll(argv[i + 1]);
+  long long v[13] = {};
+  for (int i = 0; i < argc - 1; ++i) v[i] = atoll(argv[i + 1]);
   rope_attn_desc_t d{};
   d.batch = v[0];
   d.n_heads_q = v[1];
@@ -269,6 +276,7 @@ int main(int argc, char** argv) {
   d.table_rows = v[9];
   d.dtype = ROPE_BF16;
   d.rotate = 1;
+  d.k_rotated = (int32_t)v[12];
   // fake, 16-byte aligned, disjoint addresses: the walk never dereferences them
   const uintptr_t base = (uintptr_t)1 << 40;
   const int64_t q_elems = d.batch * d.n_heads_q * d.seq_len_q * d.head_dim;
@@ -307,8 +315,14 @@ int main(int argc, char** argv) {
   const int64_t qpos_elems = d.batch * d.seq_len_q, kpos_elems = d.batch * d.seq_len_k;
   const int64_t a1 = qpos_elems, a2 = kpos_elems;
   auto run = [&](auto d_tag, auto pair_tag, auto h_tag) {
-    walk<decltype(d_tag)::value, decltype(pair_tag)::value, decltype(h_tag)::value>(
-        pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+    constexpr int DD = decltype(d_tag)::value, PP = decltype(pair_tag)::value,
+                  HH = decltype(h_tag)::value;
+    // the launcher's choice: K rotated in the kernel unless it arrives rotated
+    // (a plan without rotation uses the rotating instantiation, H16 = 0)
+    if (pl.a.rotate_k || (PP == kSplitHalf && HH == 0))
+      walk<DD, PP, HH, true>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+    else
+      walk<DD, PP, HH, false>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;

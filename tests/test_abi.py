@@ -334,9 +334,39 @@ def call_attn(d):
     (dict(o=A16 * 1024 + 2 * 8 * 100 * 128 * 2 - 32), ALIAS),   # O runs into K
     (dict(cos=A16 * 4096 + 64), ALIAS),               # table inside O
     (dict(q_pos=A16 * 4096, k_pos=A16 * 10000), ALIAS),
+    (dict(k_rotated=2), SHAPE),
 ])
 def test_attention_validation_errors(change, expected):
     assert call_attn(attn_desc(**change)) == expected
+
+
+def call_k_once(d, ws):
+    return rp.lib().rope_attention_fwd_k_once(ctypes.byref(d) if d is not None else None, ws,
+                                              None)
+
+
+WS = A16 * 20000  # a workspace address clear of every operand of attn_desc()
+
+
+@pytest.mark.parametrize("change,ws,expected", [
+    (dict(), None, NULL),                               # rotation needs the workspace
+    (dict(), WS + 8, ALIGN),
+    (dict(k_rotated=1), WS, SHAPE),                     # the call rotates K itself
+    (dict(), A16 * 1024, ALIAS),                        # onto Q
+    (dict(), A16 * 1024 + 2 * 8 * 100 * 128 * 2 + 64, ALIAS),   # onto K
+    (dict(), A16 * 4096 + 16, ALIAS),                   # onto O
+    (dict(), A16 * 8192 - 16, ALIAS),                   # runs into cos
+    (dict(q_pos=WS + 4096, k_pos=A16 * 30000), WS, ALIAS),       # over an index row
+    (dict(dtype=1), WS, DTYPE),                         # the attention's own checks first
+    (dict(scale=float("nan")), WS, SHAPE),
+])
+def test_attention_k_once_validation_errors(change, ws, expected):
+    assert call_k_once(attn_desc(**change), ws) == expected
+
+
+def test_attention_k_once_empty_and_null():
+    assert call_k_once(None, WS) == NULL
+    assert call_k_once(attn_desc(seq_len_q=0, q=None, k=None, v=None, o=None), None) == OK
 
 
 def test_attention_empty_and_null():

@@ -24,7 +24,7 @@ DEPS = [SRC, os.path.join(CSRC, "rope_attention.hpp"), os.path.join(CSRC, "rope_
 
 SPLIT, INTER = 0, 1
 
-# B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos
+# B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos [k_rotated]
 CASES = [
     (1, 2, 1, 130, 130, 128, 128, SPLIT, 0, 200, 0, 0),     # ragged tiles
     (2, 4, 2, 77, 200, 64, 64, SPLIT, 1, 256, 0, 0),        # causal, Sq < Sk
@@ -45,6 +45,12 @@ CASES = [
     (2, 16, 1, 40, 97, 64, 64, INTER, 0, 97, 1, 1),         # GQA 16:1
     (1, 6, 2, 300, 100, 128, 64, SPLIT, 0, 300, 0, 0),      # GQA 3:1, Sq > Sk
     (8, 4, 2, 33, 65, 64, 32, SPLIT, 1, 65, 1, 1),          # batch 8
+    # K arrives rotated (rope_attention_fwd_k_once): the copy-only K staging
+    # with Q still rotated in the kernel
+    (2, 32, 8, 300, 300, 128, 128, SPLIT, 1, 300, 0, 0, 1),
+    (1, 2, 2, 129, 129, 128, 64, INTER, 1, 130, 1, 1, 1),
+    (2, 8, 2, 257, 300, 128, 96, SPLIT, 1, 300, 1, 0, 1),
+    (1, 8, 8, 1026, 1026, 64, 32, SPLIT, 1, 1024, 1, 1, 1),
 ]
 
 

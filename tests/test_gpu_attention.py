@@ -186,6 +186,50 @@ def test_fused_equals_rotation_then_attention(name):
     assert torch.equal(fused.view(torch.int16), unfused.view(torch.int16))
 
 
+K_ONCE_CASES = dict(FUSED_CASES, **{
+    "cls_positions_d64": (1, 4, 4, 258, 258, 64, 32, "split_half", True, "cls"),
+    "gqa_16_to_1_interleaved": (2, 16, 1, 40, 97, 64, 64, "interleaved", False, "random"),
+})
+
+
+@pytest.mark.parametrize("name", list(K_ONCE_CASES))
+def test_k_once_equals_fused(name):
+    # rope(K) written once into a workspace, then the attention rotating only
+    # Q: the same bits as the fused call; and the workspace holds rope_fwd_q's K
+    B, Hq, Hk, Sq, Sk, D, R, pairing, causal, pk = K_ONCE_CASES[name]
+    say(f"[gpu] attention K once vs fused {name}")
+    q, k, v = inputs(B, Hq, Hk, Sq, Sk, D, 8900 + Sq)
+    rows = max(Sq, Sk) + 8
+    gt, _ = tables(rows, R)
+    qp = positions(pk, B, Sq, rows, 8910)
+    kp = positions(pk, B, Sk, rows, 8920) if pk != "cls" else qp
+    kw = dict(pairing=pairing, rotary_dim=R, causal=causal, q_pos=qp, k_pos=kp)
+    fused = run(q, k, v, gt, **kw)
+    kd = k.to(DEV)
+    ws = torch.full_like(kd, float("nan"))
+    once = run(q, kd, v, gt, k_workspace=ws, **kw)
+    assert torch.equal(fused.view(torch.int16), once.view(torch.int16))
+    assert torch.equal(kd.cpu(), k)  # K itself is left as it was
+    kpos = torch.arange(Sk, dtype=torch.int32) if kp is None else kp
+    kr = kd.clone()
+    rp.rope_fwd_q(kr, gt[0], gt[1], pairing=pairing, rotary_dim=R, pos=kpos.to(DEV),
+                  pos_batch_stride=Sk if kpos.numel() >= B * Sk else 0)
+    assert torch.equal(ws.view(torch.int16), kr.view(torch.int16))
+
+
+def test_k_once_full_size_equals_fused():
+    w = W.ATTN_LLAMA_PREFILL
+    t = {key: x.to(DEV) for key, x in W.attn_tensors(w).items()}
+    say(f"[gpu] attention K once vs fused, {w.name} full size")
+    gt, _ = tables(w.table_rows, w.rotary_dim, w.theta)
+    kw = dict(pairing=w.pairing, rotary_dim=w.rotary_dim, causal=w.causal)
+    fused = rp.rope_attention(t["q"], t["k"], t["v"], gt[0], gt[1], **kw)
+    once = rp.rope_attention(t["q"], t["k"], t["v"], gt[0], gt[1],
+                             k_workspace=torch.empty_like(t["k"]), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), once.view(torch.int16))
+
+
 def test_no_keys_gives_zeros_and_empty_queries_do_nothing():
     q = W.normal((1, 2, 40, 128), "bf16", 8800).to(DEV)
     k = torch.empty((1, 1, 0, 128), dtype=torch.bfloat16, device=DEV)
