@@ -217,6 +217,19 @@ def test_k_once_equals_fused(name):
     assert torch.equal(ws.view(torch.int16), kr.view(torch.int16))
 
 
+def test_k_rotated_descriptor_with_rope_fwd_q():
+    # a caller that already holds rope(K) (here from rope_fwd_q) sets
+    # k_rotated: the same bits as the fused call
+    B, Hq, Hk, Sq, Sk, D, R = 1, 8, 2, 150, 150, 128, 128
+    q, k, v = inputs(B, Hq, Hk, Sq, Sk, D, 8960)
+    gt, _ = tables(Sk, R)
+    fused = run(q, k, v, gt, rotary_dim=R, causal=True)
+    kr = k.to(DEV)
+    rp.rope_fwd_q(kr, gt[0], gt[1], rotary_dim=R)
+    got = run(q, kr, v, gt, rotary_dim=R, causal=True, k_rotated=True)
+    assert torch.equal(fused.view(torch.int16), got.view(torch.int16))
+
+
 def test_k_once_full_size_equals_fused():
     w = W.ATTN_LLAMA_PREFILL
     t = {key: x.to(DEV) for key, x in W.attn_tensors(w).items()}
