@@ -73,6 +73,7 @@ struct AttnArgs {
   int32_t rotate;        // 0: no rotation (plain attention, for the unfused path)
   int32_t rotate_k;      // 0: K arrives rotated (or no rotation): stage it as it is
   int32_t causal;
+  int32_t split;         // 1: the two halves of the waves take alternate key tiles
   int32_t hw;            // query heads per workgroup (a power of 2 dividing Hq / Hk)
   int32_t rows;          // query rows of each head per workgroup: kRows / hw
   int32_t head_groups;   // Hq / hw
@@ -92,7 +93,7 @@ template <int D> ROPE_HD int64_t row_of(const AttnArgs& a, int b, int h, int hea
 }
 
 // K tile staging items, in three classes; item n of lane t in a class is
-// class item t + n * kBlock, and class item it covers key it / per_key,
+// class item t + n * NT (NT staging lanes), and class item it covers key it / per_key,
 // chunk it % per_key:
 //   - split-half pair items (R/16 = 2 H16 per key): chunk j rotates the
 //     pairs of dims 8j .. 8j + 7 with R/2 + 8j .. R/2 + 8j + 7;
@@ -101,11 +102,12 @@ template <int D> ROPE_HD int64_t row_of(const AttnArgs& a, int b, int h, int hea
 //   - interleaved items (D/8 per key): chunk j holds dims 8j .. 8j + 7,
 //     rotated (4 pairs) when 8j < R.
 // The counts are fixed by the instantiation (R = 32 H16 for split-half).
-template <int D, int PAIR, int H16> struct KPlan {
+template <int D, int PAIR, int H16, int NT = kBlock> struct KPlan {
   static constexpr int kPair = PAIR == kSplitHalf ? 2 * H16 : 0;
   static constexpr int kCopy = PAIR == kSplitHalf ? D / 8 - 4 * H16 : 0;
   static constexpr int kInter = PAIR == kSplitHalf ? 0 : D / 8;
-  static constexpr int lanes(int per_key) { return (kKeys * per_key + kBlock - 1) / kBlock; }
+  // NT: the lanes that stage a tile (the workgroup, or one wave group)
+  static constexpr int lanes(int per_key) { return (kKeys * per_key + NT - 1) / NT; }
   static constexpr int kPairN = lanes(kPair), kCopyN = lanes(kCopy), kInterN = lanes(kInter);
 };
 
@@ -116,6 +118,8 @@ template <int D> constexpr int k_lds_elems() { return kKeys * (D + kKPad); }
 template <int D> constexpr int v_lds_elems() { return D * (kKeys + kVPad); }
 template <int D> constexpr int buf_elems() { return k_lds_elems<D>() + v_lds_elems<D>(); }
 template <int D> constexpr int lds_bytes() { return 2 * 2 * buf_elems<D>(); }
+// split: a double buffer per half of the waves
+template <int D> constexpr int lds_bytes_split() { return 2 * 4 * buf_elems<D>(); }
 template <int D> ROPE_HD int k_lds(int buf, int key, int dim) {
   return buf * buf_elems<D>() + key * (D + kKPad) + dim;
 }
@@ -154,13 +158,17 @@ ROPE_HD Work work_of(const AttnArgs& a, int64_t blk) {
 }
 
 // Wave w of a workgroup: query head hg * hw + w / (kWaves / hw), rows
-// q_tile * rows + (w % (kWaves / hw)) * 32 .. + 31.
+// q_tile * rows + (w % (kWaves / hw)) * 32 .. + 31. Split: the two halves
+// of the waves (w / 4) hold the same rows and take alternate key tiles; the
+// role is that of wave w % 4 among 4.
 struct WaveRole {
   int h, row0;
 };
 ROPE_HD WaveRole wave_role(const AttnArgs& a, const Work& wk, int wave) {
-  const int per_head = kWaves / a.hw;
-  return WaveRole{wk.hg * a.hw + wave / per_head, wk.q_tile * a.rows + (wave % per_head) * 32};
+  const int waves = a.split ? kWaves / 2 : kWaves;
+  const int w = wave % waves;
+  const int per_head = waves / a.hw;
+  return WaveRole{wk.hg * a.hw + w / per_head, wk.q_tile * a.rows + (w % per_head) * 32};
 }
 
 // V tile staging: item it holds 4 consecutive keys (4 k4 .. 4 k4 + 3) of 8
@@ -260,13 +268,15 @@ __device__ __forceinline__ float wave_sum32(float x) {
 #endif
 
 // ------------------------------------------------------- tile staging
-template <int D> constexpr int v_items_max() { return (v_items<D>() + kBlock - 1) / kBlock; }
+template <int D, int NT = kBlock> constexpr int v_items_max() {
+  return (v_items<D>() + NT - 1) / NT;
+}
 constexpr int at_least_1(int n) { return n > 0 ? n : 1; }
 
 // Raw rows of one tile (and the cos/sin of its rotated items) held in
 // registers between fetch and staging.
-template <int D, int PAIR, int H16> struct KStage {
-  using P = KPlan<D, PAIR, H16>;
+template <int D, int PAIR, int H16, int NT = kBlock> struct KStage {
+  using P = KPlan<D, PAIR, H16, NT>;
   bf16x8 px1[at_least_1(P::kPairN)], px2[at_least_1(P::kPairN)];
   float pc[at_least_1(P::kPairN)][8], ps[at_least_1(P::kPairN)][8];
   bool prot[at_least_1(P::kPairN)];
@@ -275,22 +285,22 @@ template <int D, int PAIR, int H16> struct KStage {
   float ic[at_least_1(P::kInterN)][4], is[at_least_1(P::kInterN)][4];
   bool irot[at_least_1(P::kInterN)];
 };
-template <int D> struct VStage {
-  u32x4 x[v_items_max<D>()][4];  // 4 key rows x 8 dims, as bf16 pairs
+template <int D, int NT = kBlock> struct VStage {
+  u32x4 x[v_items_max<D, NT>()][4];  // 4 key rows x 8 dims, as bf16 pairs
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
-template <int D, int PAIR, int H16>
+template <int D, int PAIR, int H16, int NT = kBlock>
 __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* kbase, int k0,
-                                        int t, KStage<D, PAIR, H16>& ks) {
-  using P = KPlan<D, PAIR, H16>;
+                                        int t, KStage<D, PAIR, H16, NT>& ks) {
+  using P = KPlan<D, PAIR, H16, NT>;
   const int R = 2 * a.half;      // interleaved: the rotated dims
   constexpr int kR = 32 * H16;   // split-half: the rotated dims, fixed by the instantiation
   const bf16x8 z = {};
   if constexpr (P::kPair > 0) {
 #pragma unroll
     for (int n = 0; n < P::kPairN; ++n) {
-      const int it = t + n * kBlock;
+      const int it = t + n * NT;
       ks.px1[n] = z;
       ks.px2[n] = z;
       ks.prot[n] = false;
@@ -312,7 +322,7 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
   if constexpr (P::kCopy > 0) {
 #pragma unroll
     for (int n = 0; n < P::kCopyN; ++n) {
-      const int it = t + n * kBlock;
+      const int it = t + n * NT;
       ks.cx[n] = z;
       if (it < kKeys * P::kCopy) {
         const int key = k0 + it / P::kCopy, j = it % P::kCopy;
@@ -324,7 +334,7 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
   if constexpr (P::kInter > 0) {
 #pragma unroll
     for (int n = 0; n < P::kInterN; ++n) {
-      const int it = t + n * kBlock;
+      const int it = t + n * NT;
       ks.ix[n] = z;
       ks.irot[n] = false;
       if (it < kKeys * P::kInter) {
@@ -346,15 +356,15 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
 
 // Rotate the fetched K items with the cos/sin fetched beside them and write
 // them to the K tile of buffer `buf`.
-template <int D, int PAIR, int H16>
-__device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR, H16>& ks,
+template <int D, int PAIR, int H16, int NT = kBlock>
+__device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR, H16, NT>& ks,
                                         __bf16* lds, int buf) {
-  using P = KPlan<D, PAIR, H16>;
+  using P = KPlan<D, PAIR, H16, NT>;
   constexpr int kR = 32 * H16;   // split-half: the rotated dims, fixed by the instantiation
   if constexpr (P::kPair > 0) {
 #pragma unroll
     for (int n = 0; n < P::kPairN; ++n) {
-      const int it = t + n * kBlock;
+      const int it = t + n * NT;
       if (it < kKeys * P::kPair) {
         const int kk = it / P::kPair, j = it % P::kPair;
         if (ks.prot[n]) rotate_split8(ks.px1[n], ks.px2[n], ks.pc[n], ks.ps[n]);
@@ -366,7 +376,7 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
   if constexpr (P::kCopy > 0) {
 #pragma unroll
     for (int n = 0; n < P::kCopyN; ++n) {
-      const int it = t + n * kBlock;
+      const int it = t + n * NT;
       if (it < kKeys * P::kCopy) {
         const int kk = it / P::kCopy, j = it % P::kCopy;
         *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, kR + 8 * j)]) = ks.cx[n];
@@ -376,7 +386,7 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
   if constexpr (P::kInter > 0) {
 #pragma unroll
     for (int n = 0; n < P::kInterN; ++n) {
-      const int it = t + n * kBlock;
+      const int it = t + n * NT;
       if (it < kKeys * P::kInter) {
         const int kk = it / P::kInter, j = it % P::kInter;
         if (ks.irot[n]) rotate_inter8(ks.ix[n], ks.ic[n], ks.is[n]);
@@ -386,12 +396,12 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
   }
 }
 
-template <int D>
+template <int D, int NT = kBlock>
 __device__ __forceinline__ void fetch_v(const AttnArgs& a, const __bf16* vbase, int k0, int t,
-                                        VStage<D>& vs) {
+                                        VStage<D, NT>& vs) {
 #pragma unroll
-  for (int n = 0; n < v_items_max<D>(); ++n) {
-    const int it = t + n * kBlock;
+  for (int n = 0; n < v_items_max<D, NT>(); ++n) {
+    const int it = t + n * NT;
     if (it < v_items<D>()) {
       const VItem vi = v_item(it);
 #pragma unroll
@@ -409,12 +419,12 @@ __device__ __forceinline__ void fetch_v(const AttnArgs& a, const __bf16* vbase, 
 // V tile, transposed: 4 keys x 8 dims per item, 8-byte LDS writes. Word w
 // of a row holds dims 2w (low half) and 2w + 1 (high half); a byte permute
 // pairs the same half of two rows.
-template <int D>
-__device__ __forceinline__ void stage_v(int t, const VStage<D>& vs, __bf16* lds, int buf) {
+template <int D, int NT = kBlock>
+__device__ __forceinline__ void stage_v(int t, const VStage<D, NT>& vs, __bf16* lds, int buf) {
   constexpr uint32_t kLow = 0x05040100u, kHigh = 0x07060302u;
 #pragma unroll
-  for (int n = 0; n < v_items_max<D>(); ++n) {
-    const int it = t + n * kBlock;
+  for (int n = 0; n < v_items_max<D, NT>(); ++n) {
+    const int it = t + n * NT;
     if (it < v_items<D>()) {
       const VItem vi = v_item(it);
 #pragma unroll
@@ -436,13 +446,19 @@ __device__ __forceinline__ void stage_v(int t, const VStage<D>& vs, __bf16* lds,
 // H16: split-half pairs, (R/2)/16 (the register distance between the two
 // chunks of a pair; a compile-time constant so the registers stay registers);
 // 0 for interleaved pairs.
-template <int D, int PAIR, int H16, bool KR>
+template <int D, int PAIR, int H16, bool KR, bool SPLIT>
 __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   // K staging: rotated while staged (KR, the fused form), or copied as it
   // arrives (K already rotated; the copy-only plan keeps no cos/sin
   // registers for it)
   constexpr int KP = KR ? PAIR : kSplitHalf;
   constexpr int KH = KR ? H16 : 0;
+  // SPLIT (small grids): the two halves of the waves hold the same 128 rows
+  // and take alternate key tiles, each half staging its own tiles into its
+  // own double buffer (NT lanes stage a tile); their softmax states merge
+  // at the end. The chain of tiles a workgroup walks is halved.
+  constexpr int NT = SPLIT ? kBlock / 2 : kBlock;
+  constexpr int kStride = SPLIT ? 2 : 1;  // tiles between a group's steps
 #if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __bf16 lds[];
   const Work wk = work_of(a, blockIdx.x);
@@ -456,6 +472,10 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   const int qi = role.row0 + (lane & 31);  // this lane's query row
   constexpr int kSteps = D / 16;  // k-steps of S^T over the head dim
   const int R = 2 * a.half;
+  const int grp = SPLIT ? wave / (kWaves / 2) : 0;  // wave group (split)
+  const int ts = t - grp * NT;                       // lane among the group's stagers
+  // LDS buffer of a group's step: parity of the step, then the group
+  auto buf_of = [&](int step) { return SPLIT ? 2 * (step & 1) + grp : (step & 1); };
 
   const int n_tiles = key_tiles(a, q_tile);
   const __bf16* kbase = a.k + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
@@ -520,26 +540,29 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   // products: that buffer's last readers (tile kt - 1) all passed the
   // previous barrier, and its next readers wait for this iteration's
   // barrier. The fetched registers never cross an iteration.
-  if (n_tiles > 0) {
-    KStage<D, KP, KH> ks0;
-    VStage<D> vs0;
-    fetch_k<D, KP, KH>(a, b, kbase, 0, t, ks0);
-    fetch_v<D>(a, vbase, 0, t, vs0);
-    stage_k<D, KP, KH>(a, t, ks0, lds, 0);
-    stage_v<D>(t, vs0, lds, 0);
+  if (grp < n_tiles) {  // tile grp (tile 0 without split)
+    KStage<D, KP, KH, NT> ks0;
+    VStage<D, NT> vs0;
+    fetch_k<D, KP, KH, NT>(a, b, kbase, grp * kKeys, ts, ks0);
+    fetch_v<D, NT>(a, vbase, grp * kKeys, ts, vs0);
+    stage_k<D, KP, KH, NT>(a, ts, ks0, lds, buf_of(0));
+    stage_v<D, NT>(ts, vs0, lds, buf_of(0));
   }
   __syncthreads();
   // a wave whose rows all lie past Sq computes nothing (it still stages)
   const bool live = wq_first < a.seq_q;
   const float c = a.scale_log2e;
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  // every wave runs the same number of steps (the barriers are shared)
+  const int n_steps = SPLIT ? (n_tiles + 1) / 2 : n_tiles;
+  for (int step = 0; step < n_steps; ++step) {
+    const int kt = step * kStride + grp;  // this group's tile
     const int k0 = kt * kKeys;
-    const int buf = kt & 1;
-    const bool more = kt + 1 < n_tiles;
+    const int buf = buf_of(step);
+    const bool more = kt + kStride < n_tiles;
     // a tile wholly after this wave's causal diagonal adds nothing: its
     // scores are all masked, so the running max, sum and output stay as
     // they are (the wave still stages the next tile and meets the barriers)
-    const bool work = live && (!a.causal || k0 <= wq_last + causal_shift);
+    const bool work = live && kt < n_tiles && (!a.causal || k0 <= wq_last + causal_shift);
     // masks only where the tile reaches past Sk or this wave's diagonal
     const bool edge = k0 + kKeys > a.seq_k || (a.causal && k0 + kKeys - 1 > wq_first + causal_shift);
 
@@ -643,11 +666,11 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
       rescale(softmax(s0, p0));
       if (edge) mask(s1, 1);
     }
-    KStage<D, KP, KH> ks;
-    VStage<D> vs;
+    KStage<D, KP, KH, NT> ks;
+    VStage<D, NT> vs;
     if (more) {
-      fetch_k<D, KP, KH>(a, b, kbase, k0 + kKeys, t, ks);
-      fetch_v<D>(a, vbase, k0 + kKeys, t, vs);
+      fetch_k<D, KP, KH, NT>(a, b, kbase, k0 + kStride * kKeys, ts, ks);
+      fetch_v<D, NT>(a, vbase, k0 + kStride * kKeys, ts, vs);
     }
     if (work) {
       output(0, p0);
@@ -655,10 +678,39 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
       output(1, p1);
     }
     if (more) {
-      stage_k<D, KP, KH>(a, t, ks, lds, buf ^ 1);
-      stage_v<D>(t, vs, lds, buf ^ 1);
+      stage_k<D, KP, KH, NT>(a, ts, ks, lds, buf_of(step + 1));
+      stage_v<D, NT>(ts, vs, lds, buf_of(step + 1));
     }
     __syncthreads();
+  }
+
+  if constexpr (SPLIT) {
+    // Merge: group 1 leaves its running max, sum and output in LDS (every
+    // tile read ended at the last barrier), group 0 takes them for the same
+    // rows (the same lane of wave w - 4) and writes O. Per lane: m, l, then
+    // the D/32 x 16 accumulators.
+    constexpr int kState = 2 + 16 * (D / 32);
+    float* st = reinterpret_cast<float*>(lds) + ((wave & 3) * 64 + lane) * kState;
+    if (grp == 1) {
+      st[0] = m_run;
+      st[1] = l_run;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st[2 + 16 * i + j] = acc[i][j];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = st[0], l1 = st[1];
+    const float m = fmaxf(m_run, m1);
+    // a row with no visible key in either half keeps zeros
+    const float a0 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * c);
+    const float a1 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * c);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[i][j] = acc[i][j] * a0 + st[2 + 16 * i + j] * a1;
   }
 
   // ---- O = acc / l: lane holds dims dt*32 + 8*(j/4) + 4*hs + j%4 of its row

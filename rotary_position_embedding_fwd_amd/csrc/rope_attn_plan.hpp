@@ -116,8 +116,17 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   const int64_t group = Hq / Hk;
   int32_t hw = 1;
   while (hw < kWaves && group % (2 * hw) == 0) hw *= 2;
+  // Small grids (fewer workgroups than the 256 compute units) at head dim
+  // 64: split each workgroup's key tiles between its two halves of waves,
+  // 128 rows per workgroup, which halves the chain of tiles a workgroup
+  // walks and doubles the workgroups (measured on MI355X, RET's 1026-token
+  // example: see the attention design notes).
+  const int64_t grid_full = (Sq + kRows / hw - 1) / (kRows / hw) * (Hq / hw) * B;
+  a.split = (D == 64 && grid_full < 256) ? 1 : 0;
+  if (a.split && hw > kWaves / 2) hw = kWaves / 2;
+  const int32_t rows_wg = a.split ? kRows / 2 : kRows;
   a.hw = hw;
-  a.rows = kRows / hw;
+  a.rows = rows_wg / hw;
   a.head_groups = (int32_t)(Hq / hw);
   a.q_tiles = (int32_t)((Sq + a.rows - 1) / a.rows);
   a.scale_log2e = scale_log2e;
@@ -127,7 +136,8 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   pl->head_dim = (int)D;
   pl->pairing = d->pairing;
   pl->h16 = (rotate && d->pairing == ROPE_SPLIT_HALF) ? (int)(R / 32) : 0;
-  pl->lds = D == 64 ? lds_bytes<64>() : lds_bytes<128>();
+  pl->lds = D == 64 ? (a.split ? lds_bytes_split<64>() : lds_bytes<64>())
+                    : (a.split ? lds_bytes_split<128>() : lds_bytes<128>());
   return ROPE_OK;
 }
 

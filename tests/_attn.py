@@ -22,7 +22,12 @@ arithmetic, element by element, built from oracle results only:
      passes it by more than 8 in the base-2 exponent, so the weights stay
      below 2^8; a bf16 weight's relative rounding does not depend on its
      size), each off by its argument's rounding and exp2's error, which adds
-     ceil(Sk / 32) * ln2 * (2^-23 |x|max + 2^-22) to eps_i.
+     (ceil(Sk / 32) + 2) * ln2 * (2^-23 |x|max + 2^-22) to eps_i. The two
+     extra factors cover the split form (small grids at head dim 64), where
+     each half of the waves walks every other 64-key tile, at most
+     ceil(Sk / 64) + 1 steps of 32 keys, and the halves' states then merge
+     with one more rescale each; the merge's products and sum are two more
+     float32 roundings, inside the running-sum term's 128 spare keys.
   4. The final rounding of O to bf16: u * |O|.
 """
 from __future__ import annotations
@@ -146,7 +151,7 @@ def reference(q, k, v, cos: Optional[np.ndarray], sin: Optional[np.ndarray], *,
             e = np.where(visible, e, 0.0)
             if Sk:
                 xmax = np.where(visible, s, 0.0).max(axis=1)
-                rescale = -(-Sk // 32) * np.log(2.0) * (2.0 ** -23 * xmax + 2.0 ** -22)
+                rescale = (-(-Sk // 32) + 2) * np.log(2.0) * (2.0 ** -23 * xmax + 2.0 ** -22)
                 eps[b, h] = e.max(axis=1) + rescale
     grow = np.exp(2.0 * eps)[..., None]
     pre = a_abs * grow * (U16 + 2.0 * (Sk + 128) * 2.0 ** -24) + (grow - 1.0) * a_abs

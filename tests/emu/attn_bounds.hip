@@ -6,11 +6,14 @@
 // tile of the planned grid, forming each address with the kernel's own index
 // functions (work_of, wave_role, row_of, k_lds, v_lds, v_slot, query_pos,
 // key_pos, key_tiles, KPlan) and counting any that falls outside the exact extent of
-// its buffer. The tile pipeline is simulated phase by phase (stage tile 0;
-// then per tile, the reads of its buffer and the staging of the next tile
-// into the other one): each staging write must land in its tile's buffer,
-// no LDS cell may be written by two lanes in one phase, and every cell read
-// for tile kt must hold tile kt.
+// its buffer. The tile pipeline is simulated phase by phase, a phase being
+// the work between two barriers (stage the first tile; then per step, the
+// reads of the step's buffer and the staging of the next tile into the
+// other one; with split, each half of the waves does so on its own tiles and
+// buffers): each staging write must land in its tile's buffer, no LDS cell
+// may be written by two lanes or both read and written in one phase, and
+// every cell read for tile kt must hold tile kt. With split, the final merge
+// (the second half's softmax state through LDS) is checked the same way.
 //
 // usage: attn_bounds B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos [k_rotated]
 //   (qpos / kpos: 0 = no index, 1 = an index of Sq / Sk entries per batch;
@@ -46,19 +49,27 @@ struct Checker {
 // LDS cell ownership of one workgroup: the tile whose staging last wrote
 // each cell, and the lane that wrote it in the current staging phase.
 struct LdsModel {
-  std::vector<int> tile, writer;
-  explicit LdsModel(int n) : tile(n, -1), writer(n, -1) {}
+  std::vector<int> tile, writer, wrote_in, read_in;
+  explicit LdsModel(int n) : tile(n, -1), writer(n, -1), wrote_in(n, -1), read_in(n, -1) {}
 };
 
-template <int D, int PAIR, int H16, bool KR>
+template <int D, int PAIR, int H16, bool KR, bool SPLIT>
 void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_elems,
           int64_t qpos_elems, int64_t kpos_elems, Checker& ck) {
   const AttnArgs& a = pl.a;
-  const int lds_elems = lds_bytes<D>() / 2;
+  // the kernel's choice of staging lanes and tile stride, and its LDS
+  constexpr int NT = SPLIT ? kBlock / 2 : kBlock;
+  constexpr int kStride = SPLIT ? 2 : 1;
+  constexpr int kGroups = SPLIT ? 2 : 1;
+  ck.fail(SPLIT != (a.split != 0), "instantiation matches split");
+  ck.fail(SPLIT && D != 64, "split only at head dim 64");
+  ck.fail(pl.lds != (SPLIT ? lds_bytes_split<D>() : lds_bytes<D>()), "plan's LDS size");
+  ck.fail(pl.lds > 160 * 1024 / 2, "two workgroups per compute unit fit in LDS");
+  const int lds_elems = (int)(pl.lds / 2);
   const int R = 2 * a.half;
   // K staging: the kernel's plan for this instantiation (rotated while
   // staged, or the copy-only plan when K arrives rotated)
-  using P = KPlan<D, KR ? PAIR : kSplitHalf, KR ? H16 : 0>;
+  using P = KPlan<D, KR ? PAIR : kSplitHalf, KR ? H16 : 0, NT>;
   constexpr int kRK = KR ? 32 * H16 : 0;  // split-half: dims the pair items cover
   ck.fail(KR != (a.rotate_k != 0) && a.rotate, "instantiation matches rotate_k");
   // the instantiation's item classes cover each key's D dims exactly once
@@ -86,14 +97,21 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
   }
   // every (batch, head, row) is some wave's row exactly once
   ck.fail((int64_t)a.head_groups * a.hw != a.n_heads_q, "head groups cover the heads");
-  ck.fail(a.rows * a.hw != kRows || (int64_t)a.q_tiles * a.rows < a.seq_q, "rows cover Sq");
+  ck.fail(a.rows * a.hw != kRows / kGroups || (int64_t)a.q_tiles * a.rows < a.seq_q,
+          "rows cover Sq");
   ck.fail((a.n_heads_q / a.n_heads_k) % a.hw != 0, "a workgroup spans two K/V heads");
   // every (batch, query head, row < Sq) belongs to exactly one lane's query
+  // (with split: to one lane of the first half, whose twin in the second
+  // half holds the same row)
   std::vector<char> owned((size_t)a.batch * a.n_heads_q * a.seq_q, 0);
   for (int64_t blk = 0; blk < pl.grid; ++blk) {
     const Work wk = work_of(a, blk);
-    for (int wave = 0; wave < kWaves; ++wave) {
+    for (int wave = 0; wave < kWaves / kGroups; ++wave) {
       const WaveRole role = wave_role(a, wk, wave);
+      if (SPLIT) {
+        const WaveRole twin = wave_role(a, wk, wave + kWaves / 2);
+        ck.fail(twin.h != role.h || twin.row0 != role.row0, "split twins share rows");
+      }
       for (int r = 0; r < 32; ++r) {  // lanes r and r + 32 share row row0 + r
         const int qi = role.row0 + r;
         if (qi < a.seq_q && role.h >= 0 && role.h < a.n_heads_q)
@@ -133,28 +151,37 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
               ck.check(p * a.half + (s * 16 + hs * 8) / 2, 4, table_elems, "q cos/sin");
         }
       }
-      for (int dt = 0; dt < D / 32; ++dt)
-        for (int g = 0; g < 4; ++g) ck.check(qrow + dt * 32 + 8 * g + 4 * hs, 4, q_elems, "o store");
+      // only the first half of the waves writes O (split)
+      if (wave < kWaves / kGroups)
+        for (int dt = 0; dt < D / 32; ++dt)
+          for (int g = 0; g < 4; ++g)
+            ck.check(qrow + dt * 32 + 8 * g + 4 * hs, 4, q_elems, "o store");
     }
-    // the tile pipeline: stage tile 0 into buffer 0; then per tile kt,
-    // reads of buffer kt & 1, staging of tile kt + 1 into the other buffer
+    // the tile pipeline, phase by phase: group g stages tile g into buffer
+    // buf_of(g, 0); then in step s, group g reads tile s * kStride + g from
+    // buf_of(g, s) and stages tile s * kStride + g + kStride into
+    // buf_of(g, s + 1)
+    auto buf_of = [&](int g, int step) { return SPLIT ? 2 * (step & 1) + g : (step & 1); };
     LdsModel m(lds_elems);
-    auto stage = [&](int tile) {
-      const int buf = tile & 1, k0 = tile * kKeys;
-      std::fill(m.writer.begin(), m.writer.end(), -1);
+    int phase = 0;
+    auto stage = [&](int tile, int buf, int grp) {
+      const int k0 = tile * kKeys;
       auto wrote = [&](int off, int n, int t, const char* what) {
         ck.check(off, n, lds_elems, what);
         const int lo = buf * buf_elems<D>(), hi = lo + buf_elems<D>();
         ck.fail(off < lo || off + n > hi, "staging outside its buffer");
         for (int i = off; i < off + n && i >= 0 && i < lds_elems; ++i) {
-          ck.fail(m.writer[i] != -1 && m.writer[i] != t, "lds cell written by two lanes");
+          ck.fail(m.wrote_in[i] == phase && m.writer[i] != t, "lds cell written by two lanes");
+          ck.fail(m.read_in[i] == phase, "lds cell read and written in one phase");
           m.writer[i] = t;
+          m.wrote_in[i] = phase;
           m.tile[i] = tile;
         }
       };
-      for (int t = 0; t < kBlock; ++t) {
+      for (int ts = 0; ts < NT; ++ts) {
+        const int t = grp * NT + ts;
         // split-half pair items: rotate dims 8j.. with R/2 + 8j..
-        for (int it = t; it < kKeys * P::kPair; it += kBlock) {
+        for (int it = ts; it < kKeys * P::kPair; it += NT) {
           const int kk = it / P::kPair, j = it % P::kPair;
           const int key = k0 + kk;
           if (key < a.seq_k) {
@@ -168,14 +195,14 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
           wrote(k_lds<D>(buf, kk, kRK / 2 + 8 * j), 8, t, "k lds");
         }
         // split-half copy items: dims R + 8j..
-        for (int it = t; it < kKeys * P::kCopy; it += kBlock) {
+        for (int it = ts; it < kKeys * P::kCopy; it += NT) {
           const int kk = it / P::kCopy, j = it % P::kCopy;
           const int key = k0 + kk;
           if (key < a.seq_k) ck.check(kbase + (int64_t)key * D + kRK + 8 * j, 8, kv_elems, "k load");
           wrote(k_lds<D>(buf, kk, kRK + 8 * j), 8, t, "k lds");
         }
         // interleaved items: dims 8j.., rotated when 8j < R
-        for (int it = t; it < kKeys * P::kInter; it += kBlock) {
+        for (int it = ts; it < kKeys * P::kInter; it += NT) {
           const int kk = it / P::kInter, j = it % P::kInter;
           const int key = k0 + kk;
           if (key < a.seq_k) {
@@ -186,10 +213,11 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
           wrote(k_lds<D>(buf, kk, 8 * j), 8, t, "k lds");
         }
         // the lanes' item counts stay within the registers the kernel keeps
-        ck.fail((t + P::kPairN * kBlock) < kKeys * P::kPair, "pair items per lane");
-        ck.fail((t + P::kCopyN * kBlock) < kKeys * P::kCopy, "copy items per lane");
-        ck.fail((t + P::kInterN * kBlock) < kKeys * P::kInter, "interleaved items per lane");
-        for (int it = t; it < v_items<D>(); it += kBlock) {
+        ck.fail((ts + P::kPairN * NT) < kKeys * P::kPair, "pair items per lane");
+        ck.fail((ts + P::kCopyN * NT) < kKeys * P::kCopy, "copy items per lane");
+        ck.fail((ts + P::kInterN * NT) < kKeys * P::kInter, "interleaved items per lane");
+        ck.fail((ts + v_items_max<D, NT>() * NT) < v_items<D>(), "v items per lane");
+        for (int it = ts; it < v_items<D>(); it += NT) {
           const VItem vi = v_item(it);
           for (int r = 0; r < 4; ++r) {
             const int key = k0 + 4 * vi.k4 + r;
@@ -206,14 +234,21 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
     };
     auto read = [&](int off, int n, int tile, const char* what) {
       ck.check(off, n, lds_elems, what);
-      for (int i = off; i < off + n && i >= 0 && i < lds_elems; ++i)
+      for (int i = off; i < off + n && i >= 0 && i < lds_elems; ++i) {
         ck.fail(m.tile[i] != tile, "lds read of a cell not staged for this tile");
+        ck.fail(m.wrote_in[i] == phase, "lds cell read and written in one phase");
+        m.read_in[i] = phase;
+      }
     };
-    if (n_tiles > 0) stage(0);
-    for (int kt = 0; kt < n_tiles; ++kt) {
-      const int buf = kt & 1, k0 = kt * kKeys;
+    for (int g = 0; g < kGroups; ++g)
+      if (g < n_tiles) stage(g, buf_of(g, 0), g);
+    const int n_steps = (n_tiles + kStride - 1) / kStride;
+    for (int step = 0; step < n_steps; ++step) {
+      ++phase;  // the barrier before the step
       for (int t = 0; t < kBlock; ++t) {
-        const int lane = t & 63, wave = t >> 6, hs = lane >> 5;
+        const int lane = t & 63, wave = t >> 6, hs = lane >> 5, grp = wave / (kWaves / kGroups);
+        const int kt = step * kStride + grp, k0 = kt * kKeys, buf = buf_of(grp, step);
+        if (kt >= n_tiles) continue;
         const WaveRole role = wave_role(a, wk, wave);
         const int wq_last = imin(role.row0 + 31, a.seq_q - 1);
         if (role.row0 >= a.seq_q) continue;
@@ -236,7 +271,33 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
             }
           }
       }
-      if (kt + 1 < n_tiles) stage(kt + 1);
+      for (int g = 0; g < kGroups; ++g) {
+        const int kt = step * kStride + g;
+        if (kt + kStride < n_tiles) stage(kt + kStride, buf_of(g, step + 1), g);
+      }
+    }
+    if (SPLIT) {
+      // merge: after the last barrier, each lane of the second half writes
+      // its state (m, l, D/32 x 16 accumulators) to float slot
+      // ((wave & 3) * 64 + lane) * kState; after one more barrier its twin
+      // in the first half reads it
+      constexpr int kState = 2 + 16 * (D / 32);
+      const int cells = (int)(pl.lds / 4);
+      std::vector<int> who(cells, -1);
+      for (int t = kBlock / 2; t < kBlock; ++t) {
+        const int off = (((t >> 6) & 3) * 64 + (t & 63)) * kState;
+        ck.check(off, kState, cells, "merge state write");
+        for (int i = off; i < off + kState && i >= 0 && i < cells; ++i) {
+          ck.fail(who[i] != -1, "merge cell written by two lanes");
+          who[i] = t;
+        }
+      }
+      for (int t = 0; t < kBlock / 2; ++t) {
+        const int off = (((t >> 6) & 3) * 64 + (t & 63)) * kState;
+        ck.check(off, kState, cells, "merge state read");
+        for (int i = off; i < off + kState && i >= 0 && i < cells; ++i)
+          ck.fail(who[i] != t + kBlock / 2, "merge reads its twin's state");
+      }
     }
   }
 }
@@ -306,7 +367,7 @@ int main(int argc, char** argv) {
   }
   AttnPlan pl;
   const rope_status_t st = make_attn_plan(&d, &pl);
-  printf("plan %d\n", (int)st);
+  printf("plan %d\nsplit %d\n", (int)st, (int)pl.a.split);
   if (st != ROPE_OK || pl.empty) {
     printf("violations 0\naccesses 0\n");
     return 0;
@@ -319,10 +380,18 @@ int main(int argc, char** argv) {
                   HH = decltype(h_tag)::value;
     // the launcher's choice: K rotated in the kernel unless it arrives rotated
     // (a plan without rotation uses the rotating instantiation, H16 = 0)
-    if (pl.a.rotate_k || (PP == kSplitHalf && HH == 0))
-      walk<DD, PP, HH, true>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
-    else
-      walk<DD, PP, HH, false>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+    // (the split instantiations exist at head dim 64)
+    const bool kr = pl.a.rotate_k || (PP == kSplitHalf && HH == 0);
+    if constexpr (DD == 64) {
+      if (pl.a.split) {
+        if (kr) walk<DD, PP, HH, true, true>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+        else walk<DD, PP, HH, false, true>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+        return;
+      }
+    }
+    ck.fail(pl.a.split != 0, "split plan at head dim 128");
+    if (kr) walk<DD, PP, HH, true, false>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+    else walk<DD, PP, HH, false, false>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
