@@ -5,7 +5,9 @@ Two directions:
     softmax over 32-key steps in base 2 whose reference max moves only when
     a step's max passes it by more than 8, weights rounded to bf16 before
     they multiply V, float32 accumulation, bf16 output), written here in
-    numpy from that description, stays inside the bound;
+    numpy from that description, stays inside the bound, both as one walk
+    over the keys and as the split form's two walks over alternate 64-key
+    tiles merged at the end;
   - mistakes planted in the oracle (a key dropped, the causal diagonal moved
     by one, the wrong pairing, positions off by one, K left unrotated, the
     wrong K/V head for a query head) land outside it.
@@ -31,8 +33,13 @@ def _bf16(x):
 
 
 def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k_pos=None,
-                  scale=None):
-    """The kernel's arithmetic in numpy float32 (see the module docstring)."""
+                  scale=None, split=False):
+    """The kernel's arithmetic in numpy float32 (see the module docstring).
+
+    split: the form for small grids at head dim 64, where two halves of the
+    waves walk alternate 64-key tiles (half g: tiles g, g + 2, ...) with
+    their own running states, merged at the end by rescaling both to the
+    larger reference max."""
     qs, ks, vs = (oracle.torch_to_storage(t) for t in (q, k, v))
     B, Hq, Sq, D = qs.shape
     Hk, Sk = ks.shape[1], ks.shape[2]
@@ -51,27 +58,48 @@ def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k
             Q = qr[b, h].astype(np.float32)
             K = kr[b, h // g].astype(np.float32)
             V = vv[b, h // g]
-            m = np.full(Sq, -np.inf, np.float32)
-            l = np.zeros(Sq, np.float32)
-            acc = np.zeros((Sq, D), np.float32)
-            for k0 in range(0, Sk, 32):
-                kk = np.arange(k0, min(k0 + 32, Sk))
-                x = (Q @ K[kk].T) * c
-                if causal:
-                    x = np.where(kk[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq), x, -np.inf)
-                m_t = x.max(axis=1)
+            halves = []
+            for g0 in ((0, 1) if split else (0,)):
+                steps = [k0 for t0 in range(64 * g0, Sk, 128 if split else 64)
+                         for k0 in (t0, t0 + 32) if k0 < Sk]
+                halves.append(_walk(Q, K, V, c, steps, Sk, causal))
+            m, l, acc = halves[0]
+            if split:
+                m1, l1, acc1 = halves[1]
+                mm = np.maximum(m, m1)
                 with np.errstate(invalid="ignore"):
-                    move = m_t - m > 8
-                m_new = np.where(move, m_t, m).astype(np.float32)
-                alpha = np.where(move, np.exp2(m - m_new), np.float32(1)).astype(np.float32)
-                p = np.where(np.isneginf(x), np.float32(0), np.exp2(x - m_new[:, None]))
-                p = p.astype(np.float32)
-                l = l * alpha + p.sum(axis=1, dtype=np.float32)
-                acc = acc * alpha[:, None] + _bf16(p) @ V[kk]
-                m = m_new
+                    a0 = np.where(np.isneginf(mm), 0, np.exp2(m - mm)).astype(np.float32)
+                    a1 = np.where(np.isneginf(mm), 0, np.exp2(m1 - mm)).astype(np.float32)
+                l = (l * a0 + l1 * a1).astype(np.float32)
+                acc = (acc * a0[:, None] + acc1 * a1[:, None]).astype(np.float32)
             inv = np.where(l > 0, 1 / l, 0).astype(np.float32)
             out[b, h] = _bf16(acc * inv[:, None])
     return out
+
+
+def _walk(Q, K, V, c, steps, Sk, causal):
+    """One running softmax state over the 32-key steps starting at `steps`."""
+    Sq, D = Q.shape
+    m = np.full(Sq, -np.inf, np.float32)
+    l = np.zeros(Sq, np.float32)
+    acc = np.zeros((Sq, D), np.float32)
+    for k0 in steps:
+        kk = np.arange(k0, min(k0 + 32, Sk))
+        x = (Q @ K[kk].T) * c
+        if causal:
+            x = np.where(kk[None, :] <= np.arange(Sq)[:, None] + (Sk - Sq), x, -np.inf)
+        m_t = x.max(axis=1)
+        # (-inf - -inf gives NaN in the branches np.where discards)
+        with np.errstate(invalid="ignore"):
+            move = m_t - m > 8
+            m_new = np.where(move, m_t, m).astype(np.float32)
+            alpha = np.where(move, np.exp2(m - m_new), np.float32(1)).astype(np.float32)
+            p = np.where(np.isneginf(x), np.float32(0), np.exp2(x - m_new[:, None]))
+        p = p.astype(np.float32)
+        l = l * alpha + p.sum(axis=1, dtype=np.float32)
+        acc = acc * alpha[:, None] + _bf16(p) @ V[kk]
+        m = m_new
+    return m, l, acc
 
 
 CASES = [
@@ -83,13 +111,15 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["one_walk", "split_halves"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
-def test_kernel_model_inside_bound(orc, case):
+def test_kernel_model_inside_bound(orc, case, split):
     B, Hq, Hk, Sq, Sk, D, R, pairing, causal = case
     q, k, v = _inputs(B, Hq, Hk, Sq, Sk, D, 7100 + Sq)
     cos, sin = oracle.table(10000.0, R, max(Sq, Sk))
     ref, tol = A.reference(q, k, v, cos, sin, pairing=pairing, rotary_dim=R, causal=causal)
-    got = _kernel_model(q, k, v, cos, sin, pairing=pairing, R=R, theta=10000.0, causal=causal)
+    got = _kernel_model(q, k, v, cos, sin, pairing=pairing, R=R, theta=10000.0, causal=causal,
+                        split=split)
     err = np.abs(got - ref)
     assert (err <= tol).all(), float((err / tol).max())
     # the bound is not vacuous: well under the size of the outputs
@@ -97,8 +127,9 @@ def test_kernel_model_inside_bound(orc, case):
         oracle.torch_to_storage(v)))) + 0.01
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["one_walk", "split_halves"])
 @pytest.mark.parametrize("scale", [-0.3, 2.0, -2.0])
-def test_kernel_model_inside_bound_any_scale(orc, scale):
+def test_kernel_model_inside_bound_any_scale(orc, scale, split):
     # large |scale|: the row max jumps by more than 8 in the base-2 exponent
     # between many 32-key steps, so the model rescales often; negative: the
     # softmax of -|scale| S
@@ -107,7 +138,7 @@ def test_kernel_model_inside_bound_any_scale(orc, scale):
     cos, sin = oracle.table(10000.0, R, Sk)
     ref, tol = A.reference(q, k, v, cos, sin, rotary_dim=R, causal=True, scale=scale)
     got = _kernel_model(q, k, v, cos, sin, pairing="split_half", R=R, theta=10000.0,
-                        causal=True, scale=scale)
+                        causal=True, scale=scale, split=split)
     err = np.abs(got - ref)
     assert (err <= tol).all(), float((err / tol).max())
 
