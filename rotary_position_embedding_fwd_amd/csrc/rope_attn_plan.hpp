@@ -116,13 +116,14 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   const int64_t group = Hq / Hk;
   int32_t hw = 1;
   while (hw < kWaves && group % (2 * hw) == 0) hw *= 2;
-  // Small grids (fewer workgroups than the 256 compute units) at head dim
-  // 64: split each workgroup's key tiles between its two halves of waves,
-  // 128 rows per workgroup, which halves the chain of tiles a workgroup
-  // walks and doubles the workgroups (measured on MI355X, RET's 1026-token
-  // example: see the attention design notes).
+  // Small grids at head dim 64: split each workgroup's key tiles between
+  // its two halves of waves, 128 rows per workgroup, which halves the chain
+  // of dependent tiles a workgroup walks and doubles the workgroups. It pays
+  // while the doubled grid still fits the 256 compute units once (on
+  // MI355X, causal, 1024 tokens: 16 heads 24.1 us split vs 32.6, 32 heads
+  // 24.7 vs 33.2, but 48 heads 38.1 vs 33.4 and 64 heads 46.2 vs 33.6).
   const int64_t grid_full = (Sq + kRows / hw - 1) / (kRows / hw) * (Hq / hw) * B;
-  a.split = (D == 64 && grid_full < 256) ? 1 : 0;
+  a.split = (D == 64 && 2 * grid_full <= 256) ? 1 : 0;
   if (a.split && hw > kWaves / 2) hw = kWaves / 2;
   const int32_t rows_wg = a.split ? kRows / 2 : kRows;
   a.hw = hw;

@@ -69,6 +69,10 @@ SPLIT_CHOICE = [
     ((4, 32, 8, 520, 520, 64, 64, SPLIT, 1, 520, 0, 0), 0),
     ((1, 2, 1, 130, 130, 128, 128, SPLIT, 0, 200, 0, 0), 0),  # head dim 128: never
     ((1, 16, 2, 200, 200, 64, 64, SPLIT, 1, 200, 0, 0), 1),
+    # 128 workgroups unsplit: the split grid of 256 still fits the chip once
+    ((1, 32, 32, 1024, 1024, 64, 64, SPLIT, 1, 1024, 0, 0), 1),
+    # 192 workgroups unsplit: 384 split would put two on some compute units
+    ((1, 48, 48, 1024, 1024, 64, 64, SPLIT, 1, 1024, 0, 0), 0),
 ]
 
 
