@@ -22,29 +22,31 @@ namespace {
 // KR: the K tiles are rotated while staged (the fused form); otherwise K
 // arrives rotated and is staged by the copy-only plan, with no cos/sin
 // registers for it.
-template <int D, int PAIR, int H16, bool KR, bool SPLIT>
+template <int D, int PAIR, int H16, bool KR, int G>
 hipError_t launch_attention_one(const rope::attn::AttnPlan& pl, hipStream_t st) {
-  auto kernel = rope::attn::rope_attention_kernel<D, PAIR, H16, KR, SPLIT>;
+  auto kernel = rope::attn::rope_attention_kernel<D, PAIR, H16, KR, G>;
   // the double-buffered tiles take more than the default 64 KiB of dynamic
-  // LDS at head dim 128 (and with split buffers): raise the kernel's limit
-  // once (per process; the attribute belongs to the kernel, not to a device)
+  // LDS at head dim 128 (and with several wave groups): raise the kernel's
+  // limit once (per process; the attribute belongs to the kernel, not to a
+  // device)
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      SPLIT ? rope::attn::lds_bytes_split<D>() : rope::attn::lds_bytes<D>());
+      rope::attn::lds_bytes_groups<D>(G));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kernel, dim3((unsigned)pl.grid), dim3(rope::attn::kBlock), (unsigned)pl.lds,
                      st, pl.a);
   return hipGetLastError();
 }
 
-// the split form exists at head dim 64 only (the plan chooses it there)
+// several wave groups exist at head dim 64 only (the plan chooses them there)
 template <int D, int PAIR, int H16, bool KR>
 hipError_t launch_attention(const rope::attn::AttnPlan& pl, hipStream_t st) {
   if constexpr (D == 64) {
-    if (pl.a.split) return launch_attention_one<D, PAIR, H16, KR, true>(pl, st);
+    if (pl.a.groups == 2) return launch_attention_one<D, PAIR, H16, KR, 2>(pl, st);
+    if (pl.a.groups == 4) return launch_attention_one<D, PAIR, H16, KR, 4>(pl, st);
   }
-  if (pl.a.split) return hipErrorInvalidValue;  // unreachable: no plan splits at D = 128
-  return launch_attention_one<D, PAIR, H16, KR, false>(pl, st);
+  if (pl.a.groups != 1) return hipErrorInvalidValue;  // unreachable: see the plan
+  return launch_attention_one<D, PAIR, H16, KR, 1>(pl, st);
 }
 
 template <int D, int PAIR, int H16>

@@ -73,7 +73,7 @@ struct AttnArgs {
   int32_t rotate;        // 0: no rotation (plain attention, for the unfused path)
   int32_t rotate_k;      // 0: K arrives rotated (or no rotation): stage it as it is
   int32_t causal;
-  int32_t split;         // 1: the two halves of the waves take alternate key tiles
+  int32_t groups;        // wave groups taking turns on the key tiles: 1, 2 or 4
   int32_t hw;            // query heads per workgroup (a power of 2 dividing Hq / Hk)
   int32_t rows;          // query rows of each head per workgroup: kRows / hw
   int32_t head_groups;   // Hq / hw
@@ -118,8 +118,8 @@ template <int D> constexpr int k_lds_elems() { return kKeys * (D + kKPad); }
 template <int D> constexpr int v_lds_elems() { return D * (kKeys + kVPad); }
 template <int D> constexpr int buf_elems() { return k_lds_elems<D>() + v_lds_elems<D>(); }
 template <int D> constexpr int lds_bytes() { return 2 * 2 * buf_elems<D>(); }
-// split: a double buffer per half of the waves
-template <int D> constexpr int lds_bytes_split() { return 2 * 4 * buf_elems<D>(); }
+// G wave groups: a double buffer per group
+template <int D> constexpr int lds_bytes_groups(int g) { return 2 * 2 * g * buf_elems<D>(); }
 template <int D> ROPE_HD int k_lds(int buf, int key, int dim) {
   return buf * buf_elems<D>() + key * (D + kKPad) + dim;
 }
@@ -158,14 +158,15 @@ ROPE_HD Work work_of(const AttnArgs& a, int64_t blk) {
 }
 
 // Wave w of a workgroup: query head hg * hw + w / (kWaves / hw), rows
-// q_tile * rows + (w % (kWaves / hw)) * 32 .. + 31. Split: the two halves
-// of the waves (w / 4) hold the same rows and take alternate key tiles; the
-// role is that of wave w % 4 among 4.
+// q_tile * rows + (w % (kWaves / hw)) * 32 .. + 31. With G wave groups
+// (w / (kWaves / G)), the groups hold the same rows and take turns on the
+// key tiles; the role is that of wave w % (kWaves / G) among kWaves / G.
 struct WaveRole {
   int h, row0;
 };
-ROPE_HD WaveRole wave_role(const AttnArgs& a, const Work& wk, int wave) {
-  const int waves = a.split ? kWaves / 2 : kWaves;
+// (groups = a.groups, passed as the kernel's compile-time count)
+ROPE_HD WaveRole wave_role(const AttnArgs& a, const Work& wk, int wave, int groups) {
+  const int waves = kWaves / groups;
   const int w = wave % waves;
   const int per_head = waves / a.hw;
   return WaveRole{wk.hg * a.hw + w / per_head, wk.q_tile * a.rows + (w % per_head) * 32};
@@ -446,36 +447,38 @@ __device__ __forceinline__ void stage_v(int t, const VStage<D, NT>& vs, __bf16* 
 // H16: split-half pairs, (R/2)/16 (the register distance between the two
 // chunks of a pair; a compile-time constant so the registers stay registers);
 // 0 for interleaved pairs.
-template <int D, int PAIR, int H16, bool KR, bool SPLIT>
+template <int D, int PAIR, int H16, bool KR, int G>
 __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   // K staging: rotated while staged (KR, the fused form), or copied as it
   // arrives (K already rotated; the copy-only plan keeps no cos/sin
   // registers for it)
   constexpr int KP = KR ? PAIR : kSplitHalf;
   constexpr int KH = KR ? H16 : 0;
-  // SPLIT (small grids): the two halves of the waves hold the same 128 rows
-  // and take alternate key tiles, each half staging its own tiles into its
-  // own double buffer (NT lanes stage a tile); their softmax states merge
-  // at the end. The chain of tiles a workgroup walks is halved.
-  constexpr int NT = SPLIT ? kBlock / 2 : kBlock;
-  constexpr int kStride = SPLIT ? 2 : 1;  // tiles between a group's steps
+  // G wave groups (small grids; 1 otherwise): the groups hold the same
+  // 256 / G rows and take turns on the key tiles (group g: tiles g, g + G,
+  // ...), each staging its own tiles into its own double buffer (NT lanes
+  // stage a tile); their softmax states merge at the end. The chain of
+  // tiles a workgroup walks is divided by G.
+  static_assert(G == 1 || G == 2 || G == 4, "1, 2 or 4 wave groups");
+  constexpr int NT = kBlock / G;
+  constexpr int kStride = G;  // tiles between a group's steps
 #if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __bf16 lds[];
   const Work wk = work_of(a, blockIdx.x);
   const int q_tile = wk.q_tile, b = wk.b;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const WaveRole role = wave_role(a, wk, wave);
+  const WaveRole role = wave_role(a, wk, wave, G);
   const int h = role.h;
   const int hk = h / (a.n_heads_q / a.n_heads_k);  // the same for every wave
   const int hs = lane >> 5;  // which half of the wave: k slots 0-7 or 8-15
   const int qi = role.row0 + (lane & 31);  // this lane's query row
   constexpr int kSteps = D / 16;  // k-steps of S^T over the head dim
   const int R = 2 * a.half;
-  const int grp = SPLIT ? wave / (kWaves / 2) : 0;  // wave group (split)
-  const int ts = t - grp * NT;                       // lane among the group's stagers
+  const int grp = G == 1 ? 0 : wave / (kWaves / G);  // wave group
+  const int ts = t - grp * NT;          // lane among the group's stagers
   // LDS buffer of a group's step: parity of the step, then the group
-  auto buf_of = [&](int step) { return SPLIT ? 2 * (step & 1) + grp : (step & 1); };
+  auto buf_of = [&](int step) { return G * (step & 1) + grp; };
 
   const int n_tiles = key_tiles(a, q_tile);
   const __bf16* kbase = a.k + row_of<D>(a, b, hk, a.n_heads_k, a.seq_k, 0);
@@ -540,7 +543,7 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   // products: that buffer's last readers (tile kt - 1) all passed the
   // previous barrier, and its next readers wait for this iteration's
   // barrier. The fetched registers never cross an iteration.
-  if (grp < n_tiles) {  // tile grp (tile 0 without split)
+  if (grp < n_tiles) {  // tile grp (tile 0 with one group)
     KStage<D, KP, KH, NT> ks0;
     VStage<D, NT> vs0;
     fetch_k<D, KP, KH, NT>(a, b, kbase, grp * kKeys, ts, ks0);
@@ -553,7 +556,7 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   const bool live = wq_first < a.seq_q;
   const float c = a.scale_log2e;
   // every wave runs the same number of steps (the barriers are shared)
-  const int n_steps = SPLIT ? (n_tiles + 1) / 2 : n_tiles;
+  const int n_steps = (n_tiles + G - 1) / G;
   for (int step = 0; step < n_steps; ++step) {
     const int kt = step * kStride + grp;  // this group's tile
     const int k0 = kt * kKeys;
@@ -684,14 +687,18 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  if constexpr (SPLIT) {
-    // Merge: group 1 leaves its running max, sum and output in LDS (every
-    // tile read ended at the last barrier), group 0 takes them for the same
-    // rows (the same lane of wave w - 4) and writes O. Per lane: m, l, then
-    // the D/32 x 16 accumulators.
+  if constexpr (G > 1) {
+    // Merge: groups 1 .. G-1 leave their running max, sum and output in LDS
+    // (every tile read ended at the last barrier); group 0 takes them for
+    // the same rows (the same lane of waves w + kWaves/G, ...), rescales
+    // every state to the largest reference max and writes O. Per lane: m, l,
+    // then the D/32 x 16 accumulators.
     constexpr int kState = 2 + 16 * (D / 32);
-    float* st = reinterpret_cast<float*>(lds) + ((wave & 3) * 64 + lane) * kState;
-    if (grp == 1) {
+    constexpr int kWg = kWaves / G;  // waves per group
+    float* const base = reinterpret_cast<float*>(lds);
+    auto slot = [&](int g) { return base + (((g - 1) * kWg + wave % kWg) * 64 + lane) * kState; };
+    if (grp > 0) {
+      float* st = slot(grp);
       st[0] = m_run;
       st[1] = l_run;
 #pragma unroll
@@ -700,17 +707,28 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
         for (int j = 0; j < 16; ++j) st[2 + 16 * i + j] = acc[i][j];
     }
     __syncthreads();
-    if (grp == 1) return;
-    const float m1 = st[0], l1 = st[1];
-    const float m = fmaxf(m_run, m1);
-    // a row with no visible key in either half keeps zeros
-    const float a0 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * c);
-    const float a1 = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * c);
-    l_run = l_run * a0 + l1 * a1;
+    if (grp > 0) return;
+    float m = m_run;
+#pragma unroll
+    for (int g = 1; g < G; ++g) m = fmaxf(m, slot(g)[0]);
+    // a row with no visible key in any group keeps zeros
+    const bool none = m == -__builtin_inff();
+    const float a0 = none ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * c);
+    l_run = l_run * a0;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[i][j] = acc[i][j] * a0 + st[2 + 16 * i + j] * a1;
+      for (int j = 0; j < 16; ++j) acc[i][j] = acc[i][j] * a0;
+#pragma unroll
+    for (int g = 1; g < G; ++g) {
+      const float* st = slot(g);
+      const float ag = none ? 0.0f : __builtin_amdgcn_exp2f((st[0] - m) * c);
+      l_run = l_run + st[1] * ag;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = acc[i][j] + st[2 + 16 * i + j] * ag;
+    }
   }
 
   // ---- O = acc / l: lane holds dims dt*32 + 8*(j/4) + 4*hs + j%4 of its row

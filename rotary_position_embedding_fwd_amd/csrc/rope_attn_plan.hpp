@@ -116,16 +116,20 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   const int64_t group = Hq / Hk;
   int32_t hw = 1;
   while (hw < kWaves && group % (2 * hw) == 0) hw *= 2;
-  // Small grids at head dim 64: split each workgroup's key tiles between
-  // its two halves of waves, 128 rows per workgroup, which halves the chain
-  // of dependent tiles a workgroup walks and doubles the workgroups. It pays
-  // while the doubled grid still fits the 256 compute units once (on
-  // MI355X, causal, 1024 tokens: 16 heads 24.1 us split vs 32.6, 32 heads
-  // 24.7 vs 33.2, but 48 heads 38.1 vs 33.4 and 64 heads 46.2 vs 33.6).
+  // Small grids at head dim 64: G = 2 or 4 groups of waves share each
+  // workgroup's rows (256 / G of them) and take turns on its key tiles,
+  // which divides the chain of dependent tiles a workgroup walks by G and
+  // multiplies the workgroups by G. It pays while the grid still fits the
+  // 256 compute units once (on MI355X, causal, 1024 tokens, two groups:
+  // 16 heads 24.1 us vs 32.6, 32 heads 24.7 vs 33.2, but 48 heads 38.1 vs
+  // 33.4 and 64 heads 46.2 vs 33.6).
   const int64_t grid_full = (Sq + kRows / hw - 1) / (kRows / hw) * (Hq / hw) * B;
-  a.split = (D == 64 && 2 * grid_full <= 256) ? 1 : 0;
-  if (a.split && hw > kWaves / 2) hw = kWaves / 2;
-  const int32_t rows_wg = a.split ? kRows / 2 : kRows;
+  int32_t groups = 1;
+  if (D == 64)
+    while (groups < 4 && 2 * groups * grid_full <= 256) groups *= 2;
+  a.groups = groups;
+  while (hw > kWaves / groups) hw /= 2;  // a group's waves cover its heads
+  const int32_t rows_wg = kRows / groups;
   a.hw = hw;
   a.rows = rows_wg / hw;
   a.head_groups = (int32_t)(Hq / hw);
@@ -137,8 +141,7 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   pl->head_dim = (int)D;
   pl->pairing = d->pairing;
   pl->h16 = (rotate && d->pairing == ROPE_SPLIT_HALF) ? (int)(R / 32) : 0;
-  pl->lds = D == 64 ? (a.split ? lds_bytes_split<64>() : lds_bytes<64>())
-                    : (a.split ? lds_bytes_split<128>() : lds_bytes<128>());
+  pl->lds = D == 64 ? lds_bytes_groups<64>(groups) : lds_bytes_groups<128>(groups);
   return ROPE_OK;
 }
 

@@ -23,11 +23,12 @@ arithmetic, element by element, built from oracle results only:
      below 2^8; a bf16 weight's relative rounding does not depend on its
      size), each off by its argument's rounding and exp2's error, which adds
      (ceil(Sk / 32) + 2) * ln2 * (2^-23 |x|max + 2^-22) to eps_i. The two
-     extra factors cover the split form (small grids at head dim 64), where
-     each half of the waves walks every other 64-key tile, at most
-     ceil(Sk / 64) + 1 steps of 32 keys, and the halves' states then merge
-     with one more rescale each; the merge's products and sum are two more
-     float32 roundings, inside the running-sum term's 128 spare keys.
+     extra factors cover the form for small grids at head dim 64, where G =
+     2 or 4 groups of waves take turns on the 64-key tiles, each walking at
+     most 2 ceil(ceil(Sk / 64) / G) <= ceil(Sk / 64) + 1 steps of 32 keys,
+     and the groups' states then merge with one more rescale each; the
+     merge's products and sums are at most seven more float32 roundings,
+     inside the running-sum term's 128 spare keys.
   4. The final rounding of O to bf16: u * |O|.
 """
 from __future__ import annotations

@@ -9,11 +9,11 @@
 // its buffer. The tile pipeline is simulated phase by phase, a phase being
 // the work between two barriers (stage the first tile; then per step, the
 // reads of the step's buffer and the staging of the next tile into the
-// other one; with split, each half of the waves does so on its own tiles and
+// other one; with G wave groups, each group does so on its own tiles and
 // buffers): each staging write must land in its tile's buffer, no LDS cell
 // may be written by two lanes or both read and written in one phase, and
-// every cell read for tile kt must hold tile kt. With split, the final merge
-// (the second half's softmax state through LDS) is checked the same way.
+// every cell read for tile kt must hold tile kt. With G > 1, the final merge
+// (the other groups' softmax states through LDS) is checked the same way.
 //
 // usage: attn_bounds B Hq Hk Sq Sk D R pairing causal table_rows qpos kpos [k_rotated]
 //   (qpos / kpos: 0 = no index, 1 = an index of Sq / Sk entries per batch;
@@ -53,18 +53,20 @@ struct LdsModel {
   explicit LdsModel(int n) : tile(n, -1), writer(n, -1), wrote_in(n, -1), read_in(n, -1) {}
 };
 
-template <int D, int PAIR, int H16, bool KR, bool SPLIT>
+template <int D, int PAIR, int H16, bool KR, int G>
 void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_elems,
           int64_t qpos_elems, int64_t kpos_elems, Checker& ck) {
   const AttnArgs& a = pl.a;
   // the kernel's choice of staging lanes and tile stride, and its LDS
-  constexpr int NT = SPLIT ? kBlock / 2 : kBlock;
-  constexpr int kStride = SPLIT ? 2 : 1;
-  constexpr int kGroups = SPLIT ? 2 : 1;
-  ck.fail(SPLIT != (a.split != 0), "instantiation matches split");
-  ck.fail(SPLIT && D != 64, "split only at head dim 64");
-  ck.fail(pl.lds != (SPLIT ? lds_bytes_split<D>() : lds_bytes<D>()), "plan's LDS size");
-  ck.fail(pl.lds > 160 * 1024 / 2, "two workgroups per compute unit fit in LDS");
+  constexpr int NT = kBlock / G;
+  constexpr int kStride = G;
+  constexpr int kGroups = G;
+  constexpr bool SPLIT = G > 1;
+  ck.fail(G != a.groups, "instantiation matches the wave groups");
+  ck.fail(SPLIT && D != 64, "wave groups only at head dim 64");
+  ck.fail(pl.lds != lds_bytes_groups<D>(G), "plan's LDS size");
+  ck.fail(pl.lds > 160 * 1024, "the workgroup's LDS fits a compute unit");
+  ck.fail(G <= 2 && pl.lds > 160 * 1024 / 2, "two workgroups per compute unit fit in LDS");
   const int lds_elems = (int)(pl.lds / 2);
   const int R = 2 * a.half;
   // K staging: the kernel's plan for this instantiation (rotated while
@@ -101,16 +103,16 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
           "rows cover Sq");
   ck.fail((a.n_heads_q / a.n_heads_k) % a.hw != 0, "a workgroup spans two K/V heads");
   // every (batch, query head, row < Sq) belongs to exactly one lane's query
-  // (with split: to one lane of the first half, whose twin in the second
-  // half holds the same row)
+  // (with G groups: to one lane of group 0, whose twins in the other groups
+  // hold the same row)
   std::vector<char> owned((size_t)a.batch * a.n_heads_q * a.seq_q, 0);
   for (int64_t blk = 0; blk < pl.grid; ++blk) {
     const Work wk = work_of(a, blk);
     for (int wave = 0; wave < kWaves / kGroups; ++wave) {
-      const WaveRole role = wave_role(a, wk, wave);
-      if (SPLIT) {
-        const WaveRole twin = wave_role(a, wk, wave + kWaves / 2);
-        ck.fail(twin.h != role.h || twin.row0 != role.row0, "split twins share rows");
+      const WaveRole role = wave_role(a, wk, wave, G);
+      for (int g = 1; g < G; ++g) {
+        const WaveRole twin = wave_role(a, wk, wave + g * (kWaves / G), G);
+        ck.fail(twin.h != role.h || twin.row0 != role.row0, "group twins share rows");
       }
       for (int r = 0; r < 32; ++r) {  // lanes r and r + 32 share row row0 + r
         const int qi = role.row0 + r;
@@ -125,12 +127,12 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
     const Work wk = work_of(a, blk);
     const int b = wk.b;
     const int n_tiles = key_tiles(a, wk.q_tile);
-    const int hk0 = wave_role(a, wk, 0).h / (a.n_heads_q / a.n_heads_k);
+    const int hk0 = wave_role(a, wk, 0, G).h / (a.n_heads_q / a.n_heads_k);
     const int64_t kbase = row_of<D>(a, b, hk0, a.n_heads_k, a.seq_k, 0);
     // Q loads and rotation, O stores
     for (int t = 0; t < kBlock; ++t) {
       const int lane = t & 63, wave = t >> 6, hs = lane >> 5;
-      const WaveRole role = wave_role(a, wk, wave);
+      const WaveRole role = wave_role(a, wk, wave, G);
       ck.fail(role.h < 0 || role.h >= a.n_heads_q, "wave head");
       ck.fail(role.h / (a.n_heads_q / a.n_heads_k) != hk0, "waves of one workgroup share K/V");
       const int qi = role.row0 + (lane & 31);
@@ -151,7 +153,7 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
               ck.check(p * a.half + (s * 16 + hs * 8) / 2, 4, table_elems, "q cos/sin");
         }
       }
-      // only the first half of the waves writes O (split)
+      // only group 0 writes O
       if (wave < kWaves / kGroups)
         for (int dt = 0; dt < D / 32; ++dt)
           for (int g = 0; g < 4; ++g)
@@ -161,7 +163,7 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
     // buf_of(g, 0); then in step s, group g reads tile s * kStride + g from
     // buf_of(g, s) and stages tile s * kStride + g + kStride into
     // buf_of(g, s + 1)
-    auto buf_of = [&](int g, int step) { return SPLIT ? 2 * (step & 1) + g : (step & 1); };
+    auto buf_of = [&](int g, int step) { return G * (step & 1) + g; };
     LdsModel m(lds_elems);
     int phase = 0;
     auto stage = [&](int tile, int buf, int grp) {
@@ -249,7 +251,7 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
         const int lane = t & 63, wave = t >> 6, hs = lane >> 5, grp = wave / (kWaves / kGroups);
         const int kt = step * kStride + grp, k0 = kt * kKeys, buf = buf_of(grp, step);
         if (kt >= n_tiles) continue;
-        const WaveRole role = wave_role(a, wk, wave);
+        const WaveRole role = wave_role(a, wk, wave, G);
         const int wq_last = imin(role.row0 + 31, a.seq_q - 1);
         if (role.row0 >= a.seq_q) continue;
         if (a.causal && k0 > wq_last + (a.seq_k - a.seq_q)) continue;
@@ -277,27 +279,32 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
       }
     }
     if (SPLIT) {
-      // merge: after the last barrier, each lane of the second half writes
+      // merge: after the last barrier, each lane of groups 1 .. G-1 writes
       // its state (m, l, D/32 x 16 accumulators) to float slot
-      // ((wave & 3) * 64 + lane) * kState; after one more barrier its twin
-      // in the first half reads it
+      // ((g - 1) * kWg + wave % kWg) * 64 + lane, times kState; after one
+      // more barrier its twin in group 0 reads every group's slot
       constexpr int kState = 2 + 16 * (D / 32);
+      constexpr int kWg = kWaves / G;
       const int cells = (int)(pl.lds / 4);
       std::vector<int> who(cells, -1);
-      for (int t = kBlock / 2; t < kBlock; ++t) {
-        const int off = (((t >> 6) & 3) * 64 + (t & 63)) * kState;
+      auto slot = [&](int g, int wave, int lane) {
+        return (((g - 1) * kWg + wave % kWg) * 64 + lane) * kState;
+      };
+      for (int t = NT; t < kBlock; ++t) {
+        const int off = slot((t >> 6) / kWg, t >> 6, t & 63);
         ck.check(off, kState, cells, "merge state write");
         for (int i = off; i < off + kState && i >= 0 && i < cells; ++i) {
           ck.fail(who[i] != -1, "merge cell written by two lanes");
           who[i] = t;
         }
       }
-      for (int t = 0; t < kBlock / 2; ++t) {
-        const int off = (((t >> 6) & 3) * 64 + (t & 63)) * kState;
-        ck.check(off, kState, cells, "merge state read");
-        for (int i = off; i < off + kState && i >= 0 && i < cells; ++i)
-          ck.fail(who[i] != t + kBlock / 2, "merge reads its twin's state");
-      }
+      for (int t = 0; t < NT; ++t)
+        for (int g = 1; g < G; ++g) {
+          const int off = slot(g, t >> 6, t & 63);
+          ck.check(off, kState, cells, "merge state read");
+          for (int i = off; i < off + kState && i >= 0 && i < cells; ++i)
+            ck.fail(who[i] != t + g * NT, "merge reads its twin's state");
+        }
     }
   }
 }
@@ -367,7 +374,7 @@ int main(int argc, char** argv) {
   }
   AttnPlan pl;
   const rope_status_t st = make_attn_plan(&d, &pl);
-  printf("plan %d\nsplit %d\n", (int)st, (int)pl.a.split);
+  printf("plan %d\ngroups %d\n", (int)st, (int)pl.a.groups);
   if (st != ROPE_OK || pl.empty) {
     printf("violations 0\naccesses 0\n");
     return 0;
@@ -380,18 +387,19 @@ int main(int argc, char** argv) {
                   HH = decltype(h_tag)::value;
     // the launcher's choice: K rotated in the kernel unless it arrives rotated
     // (a plan without rotation uses the rotating instantiation, H16 = 0)
-    // (the split instantiations exist at head dim 64)
+    // (the instantiations with wave groups exist at head dim 64)
     const bool kr = pl.a.rotate_k || (PP == kSplitHalf && HH == 0);
+    auto go = [&](auto g_tag) {
+      constexpr int GG = decltype(g_tag)::value;
+      if (kr) walk<DD, PP, HH, true, GG>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+      else walk<DD, PP, HH, false, GG>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+    };
     if constexpr (DD == 64) {
-      if (pl.a.split) {
-        if (kr) walk<DD, PP, HH, true, true>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
-        else walk<DD, PP, HH, false, true>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
-        return;
-      }
+      if (pl.a.groups == 2) return go(std::integral_constant<int, 2>{});
+      if (pl.a.groups == 4) return go(std::integral_constant<int, 4>{});
     }
-    ck.fail(pl.a.split != 0, "split plan at head dim 128");
-    if (kr) walk<DD, PP, HH, true, false>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
-    else walk<DD, PP, HH, false, false>(pl, q_elems, kv_elems, table_elems, a1, a2, ck);
+    ck.fail(pl.a.groups != 1, "wave groups the launcher has no kernel for");
+    go(std::integral_constant<int, 1>{});
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;

@@ -7,9 +7,9 @@ fall inside its buffer. The double-buffered tile pipeline is simulated phase
 by phase: staging writes land in their tile's buffer, no LDS cell is written
 by two lanes in one phase, no cell is both read and written in one phase,
 and every cell read for tile kt holds tile kt. Small grids at head dim 64
-take the split form (the two halves of the waves walk alternate key tiles
-with their own buffers and merge their softmax states through LDS at the
-end): the walk follows each half and checks the merge's LDS slots.
+take 2 or 4 wave groups (the groups take turns on the key tiles with their
+own buffers and merge their softmax states through LDS at the end): the
+walk follows each group and checks the merge's LDS slots.
 The walk runs under AddressSanitizer, so the position reads are real reads
 of index arrays of exact size.
 """
@@ -55,24 +55,29 @@ CASES = [
     (1, 2, 2, 129, 129, 128, 64, INTER, 1, 130, 1, 1, 1),
     (2, 8, 2, 257, 300, 128, 96, SPLIT, 1, 300, 1, 0, 1),
     (1, 8, 8, 1026, 1026, 64, 32, SPLIT, 1, 1024, 1, 1, 1),
-    # head dim 64 with a grid of at least 256 workgroups: not split
+    # head dim 64 with a grid of at least 256 workgroups: one wave group
     (4, 32, 8, 520, 520, 64, 64, SPLIT, 1, 520, 0, 0),
     (4, 32, 8, 520, 520, 64, 64, INTER, 0, 520, 1, 1, 1),
-    # split with 8 query heads per K/V head (4 per workgroup), odd tile count
+    # four groups with 8 query heads per K/V head (2 per workgroup), a tile
+    # count that is not a multiple of 4
     (1, 16, 2, 200, 200, 64, 64, SPLIT, 1, 200, 0, 0),
     (1, 16, 2, 200, 200, 64, 32, SPLIT, 0, 200, 1, 1, 1),
+    # two groups (128 workgroups unsplit)
+    (1, 32, 32, 1024, 1024, 64, 64, SPLIT, 1, 1024, 0, 0),
+    (1, 32, 32, 300, 1024, 64, 64, INTER, 0, 1024, 1, 1, 1),
 ]
 
-# (case, expected split)
-SPLIT_CHOICE = [
-    ((1, 8, 8, 1026, 1026, 64, 32, SPLIT, 1, 1024, 1, 1), 1),
-    ((4, 32, 8, 520, 520, 64, 64, SPLIT, 1, 520, 0, 0), 0),
-    ((1, 2, 1, 130, 130, 128, 128, SPLIT, 0, 200, 0, 0), 0),  # head dim 128: never
-    ((1, 16, 2, 200, 200, 64, 64, SPLIT, 1, 200, 0, 0), 1),
-    # 128 workgroups unsplit: the split grid of 256 still fits the chip once
-    ((1, 32, 32, 1024, 1024, 64, 64, SPLIT, 1, 1024, 0, 0), 1),
-    # 192 workgroups unsplit: 384 split would put two on some compute units
-    ((1, 48, 48, 1024, 1024, 64, 64, SPLIT, 1, 1024, 0, 0), 0),
+# (case, expected wave groups)
+GROUP_CHOICE = [
+    ((1, 8, 8, 1026, 1026, 64, 32, SPLIT, 1, 1024, 1, 1), 4),   # 40 workgroups unsplit
+    ((4, 32, 8, 520, 520, 64, 64, SPLIT, 1, 520, 0, 0), 1),     # 288
+    ((1, 2, 1, 130, 130, 128, 128, SPLIT, 0, 200, 0, 0), 1),    # head dim 128: never
+    ((1, 16, 2, 200, 200, 64, 64, SPLIT, 1, 200, 0, 0), 4),     # 14, 8 heads -> 2 per group
+    ((1, 16, 16, 1024, 1024, 64, 64, SPLIT, 1, 1024, 0, 0), 4),  # 64: 256 with 4 groups
+    # 128 workgroups unsplit: 256 with two groups still fit the chip once
+    ((1, 32, 32, 1024, 1024, 64, 64, SPLIT, 1, 1024, 0, 0), 2),
+    # 192 workgroups unsplit: 384 with two groups would put two on some CUs
+    ((1, 48, 48, 1024, 1024, 64, 64, SPLIT, 1, 1024, 0, 0), 1),
 ]
 
 
@@ -120,9 +125,9 @@ def test_rejected_shapes_plan_nothing(harness):
         assert out["accesses"] == 0
 
 
-@pytest.mark.parametrize("case,split", SPLIT_CHOICE, ids=lambda c: "x".join(map(str, c))
+@pytest.mark.parametrize("case,groups", GROUP_CHOICE, ids=lambda c: "x".join(map(str, c))
                          if isinstance(c, tuple) else str(c))
-def test_split_choice(harness, case, split):
+def test_wave_group_choice(harness, case, groups):
     out, _ = walk(harness, case)
     assert out["plan"] == 0
-    assert out["split"] == split
+    assert out["groups"] == groups

@@ -6,8 +6,8 @@ Two directions:
     a step's max passes it by more than 8, weights rounded to bf16 before
     they multiply V, float32 accumulation, bf16 output), written here in
     numpy from that description, stays inside the bound, both as one walk
-    over the keys and as the split form's two walks over alternate 64-key
-    tiles merged at the end;
+    over the keys and as 2 or 4 walks that take turns on the 64-key tiles,
+    merged at the end (the form for small grids at head dim 64);
   - mistakes planted in the oracle (a key dropped, the causal diagonal moved
     by one, the wrong pairing, positions off by one, K left unrotated, the
     wrong K/V head for a query head) land outside it.
@@ -33,13 +33,13 @@ def _bf16(x):
 
 
 def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k_pos=None,
-                  scale=None, split=False):
+                  scale=None, groups=1):
     """The kernel's arithmetic in numpy float32 (see the module docstring).
 
-    split: the form for small grids at head dim 64, where two halves of the
-    waves walk alternate 64-key tiles (half g: tiles g, g + 2, ...) with
-    their own running states, merged at the end by rescaling both to the
-    larger reference max."""
+    groups: the form for small grids at head dim 64, where G = 2 or 4 groups
+    of waves take turns on the 64-key tiles (group g: tiles g, g + G, ...)
+    with their own running states, merged at the end by rescaling every
+    state to the largest reference max and adding them in group order."""
     qs, ks, vs = (oracle.torch_to_storage(t) for t in (q, k, v))
     B, Hq, Sq, D = qs.shape
     Hk, Sk = ks.shape[1], ks.shape[2]
@@ -58,20 +58,24 @@ def _kernel_model(q, k, v, cos, sin, *, pairing, R, theta, causal, q_pos=None, k
             Q = qr[b, h].astype(np.float32)
             K = kr[b, h // g].astype(np.float32)
             V = vv[b, h // g]
-            halves = []
-            for g0 in ((0, 1) if split else (0,)):
-                steps = [k0 for t0 in range(64 * g0, Sk, 128 if split else 64)
+            states = []
+            for g0 in range(groups):
+                steps = [k0 for t0 in range(64 * g0, Sk, 64 * groups)
                          for k0 in (t0, t0 + 32) if k0 < Sk]
-                halves.append(_walk(Q, K, V, c, steps, Sk, causal))
-            m, l, acc = halves[0]
-            if split:
-                m1, l1, acc1 = halves[1]
-                mm = np.maximum(m, m1)
+                states.append(_walk(Q, K, V, c, steps, Sk, causal))
+            m, l, acc = states[0]
+            if groups > 1:
+                mm = m.copy()
+                for mg, _, _ in states[1:]:
+                    mm = np.maximum(mm, mg)
                 with np.errstate(invalid="ignore"):
-                    a0 = np.where(np.isneginf(mm), 0, np.exp2(m - mm)).astype(np.float32)
-                    a1 = np.where(np.isneginf(mm), 0, np.exp2(m1 - mm)).astype(np.float32)
-                l = (l * a0 + l1 * a1).astype(np.float32)
-                acc = (acc * a0[:, None] + acc1 * a1[:, None]).astype(np.float32)
+                    f = [np.where(np.isneginf(mm), 0, np.exp2(mg - mm)).astype(np.float32)
+                         for mg, _, _ in states]
+                l = (l * f[0]).astype(np.float32)
+                acc = (acc * f[0][:, None]).astype(np.float32)
+                for (_, lg, accg), fg in zip(states[1:], f[1:]):
+                    l = (l + lg * fg).astype(np.float32)
+                    acc = (acc + accg * fg[:, None]).astype(np.float32)
             inv = np.where(l > 0, 1 / l, 0).astype(np.float32)
             out[b, h] = _bf16(acc * inv[:, None])
     return out
@@ -111,15 +115,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("split", [False, True], ids=["one_walk", "split_halves"])
+@pytest.mark.parametrize("groups", [1, 2, 4], ids=["one_group", "two_groups", "four_groups"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
-def test_kernel_model_inside_bound(orc, case, split):
+def test_kernel_model_inside_bound(orc, case, groups):
     B, Hq, Hk, Sq, Sk, D, R, pairing, causal = case
     q, k, v = _inputs(B, Hq, Hk, Sq, Sk, D, 7100 + Sq)
     cos, sin = oracle.table(10000.0, R, max(Sq, Sk))
     ref, tol = A.reference(q, k, v, cos, sin, pairing=pairing, rotary_dim=R, causal=causal)
     got = _kernel_model(q, k, v, cos, sin, pairing=pairing, R=R, theta=10000.0, causal=causal,
-                        split=split)
+                        groups=groups)
     err = np.abs(got - ref)
     assert (err <= tol).all(), float((err / tol).max())
     # the bound is not vacuous: well under the size of the outputs
@@ -127,9 +131,9 @@ def test_kernel_model_inside_bound(orc, case, split):
         oracle.torch_to_storage(v)))) + 0.01
 
 
-@pytest.mark.parametrize("split", [False, True], ids=["one_walk", "split_halves"])
+@pytest.mark.parametrize("groups", [1, 2, 4], ids=["one_group", "two_groups", "four_groups"])
 @pytest.mark.parametrize("scale", [-0.3, 2.0, -2.0])
-def test_kernel_model_inside_bound_any_scale(orc, scale, split):
+def test_kernel_model_inside_bound_any_scale(orc, scale, groups):
     # large |scale|: the row max jumps by more than 8 in the base-2 exponent
     # between many 32-key steps, so the model rescales often; negative: the
     # softmax of -|scale| S
@@ -138,7 +142,7 @@ def test_kernel_model_inside_bound_any_scale(orc, scale, split):
     cos, sin = oracle.table(10000.0, R, Sk)
     ref, tol = A.reference(q, k, v, cos, sin, rotary_dim=R, causal=True, scale=scale)
     got = _kernel_model(q, k, v, cos, sin, pairing="split_half", R=R, theta=10000.0,
-                        causal=True, scale=scale, split=split)
+                        causal=True, scale=scale, groups=groups)
     err = np.abs(got - ref)
     assert (err <= tol).all(), float((err / tol).max())
 

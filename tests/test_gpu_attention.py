@@ -86,9 +86,9 @@ CASES = {
     # GQA 3:1 (one head per workgroup), more queries than keys, not causal
     "gqa_3_to_1_sq_gt_sk": (1, 6, 2, 300, 100, 128, 64, "split_half", False, "none"),
     "batch_8_short": (8, 4, 2, 33, 65, 64, 32, "split_half", True, "random"),
-    # head dim 64 with grids of at least 256 workgroups: the form that does
-    # not split key tiles between the halves of the waves (the cases above at
-    # head dim 64 all take the split form)
+    # head dim 64 with grids of at least 256 workgroups: one wave group (the
+    # cases above at head dim 64 take four groups, the next one two)
+    "d64_two_wave_groups": (1, 24, 24, 1024, 1024, 64, 64, "split_half", True, "none"),
     "d64_wide_grid_split_half": (4, 32, 8, 520, 520, 64, 64, "split_half", True, "none"),
     "d64_wide_grid_interleaved": (2, 64, 8, 520, 520, 64, 64, "interleaved", False, "random"),
 }
