@@ -63,10 +63,13 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
   constexpr int kGroups = G;
   constexpr bool SPLIT = G > 1;
   ck.fail(G != a.groups, "instantiation matches the wave groups");
-  ck.fail(SPLIT && D != 64, "wave groups only at head dim 64");
+  // the launcher's instantiations: 2 or 4 groups at head dim 64; 2 at head
+  // dim 128 when K is staged by copy only
+  constexpr bool kCopyOnlyK = !KR || (PAIR == kSplitHalf && H16 == 0);
+  ck.fail(SPLIT && !(D == 64 || (D == 128 && G == 2 && kCopyOnlyK)),
+          "wave groups the launcher has no kernel for");
   ck.fail(pl.lds != lds_bytes_groups<D>(G), "plan's LDS size");
   ck.fail(pl.lds > 160 * 1024, "the workgroup's LDS fits a compute unit");
-  ck.fail(G <= 2 && pl.lds > 160 * 1024 / 2, "two workgroups per compute unit fit in LDS");
   const int lds_elems = (int)(pl.lds / 2);
   const int R = 2 * a.half;
   // K staging: the kernel's plan for this instantiation (rotated while
@@ -397,6 +400,8 @@ int main(int argc, char** argv) {
     if constexpr (DD == 64) {
       if (pl.a.groups == 2) return go(std::integral_constant<int, 2>{});
       if (pl.a.groups == 4) return go(std::integral_constant<int, 4>{});
+    } else {
+      if (pl.a.groups == 2) return go(std::integral_constant<int, 2>{});
     }
     ck.fail(pl.a.groups != 1, "wave groups the launcher has no kernel for");
     go(std::integral_constant<int, 1>{});
