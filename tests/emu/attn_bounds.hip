@@ -63,11 +63,7 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
   constexpr int kGroups = G;
   constexpr bool SPLIT = G > 1;
   ck.fail(G != a.groups, "instantiation matches the wave groups");
-  // the launcher's instantiations: 2 or 4 groups at head dim 64; 2 at head
-  // dim 128 when K is staged by copy only
-  constexpr bool kCopyOnlyK = !KR || (PAIR == kSplitHalf && H16 == 0);
-  ck.fail(SPLIT && !(D == 64 || (D == 128 && G == 2 && kCopyOnlyK)),
-          "wave groups the launcher has no kernel for");
+  ck.fail(SPLIT && D != 64, "wave groups only at head dim 64");
   ck.fail(pl.lds != lds_bytes_groups<D>(G), "plan's LDS size");
   ck.fail(pl.lds > 160 * 1024, "the workgroup's LDS fits a compute unit");
   const int lds_elems = (int)(pl.lds / 2);
@@ -400,8 +396,6 @@ int main(int argc, char** argv) {
     if constexpr (DD == 64) {
       if (pl.a.groups == 2) return go(std::integral_constant<int, 2>{});
       if (pl.a.groups == 4) return go(std::integral_constant<int, 4>{});
-    } else {
-      if (pl.a.groups == 2) return go(std::integral_constant<int, 2>{});
     }
     ck.fail(pl.a.groups != 1, "wave groups the launcher has no kernel for");
     go(std::integral_constant<int, 1>{});
