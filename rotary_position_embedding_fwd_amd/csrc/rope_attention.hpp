@@ -27,7 +27,10 @@
 // operand of O^T is one 16-byte LDS read per lane and step. Tiles are
 // double-buffered: the next tile is fetched while the current one is worked
 // on and staged into the other buffer after its products, with one barrier
-// per tile.
+// per tile. Small grids at head dim 64 use G = 2 or 4 wave groups instead:
+// 256 / G rows per workgroup, held by every group, each group taking every
+// G-th key tile into its own double buffer, the groups' softmax states
+// merged at the end (the rotated K is then staged per group's tiles).
 // The softmax runs in base 2 with the scale folded into log2(e), one online
 // step per 32-key half of a tile; the halves are software-pipelined so that
 // one half's softmax sits beside the other half's matrix instructions. Each
@@ -51,7 +54,7 @@ namespace attn {
 
 constexpr int kWaves = 8;
 constexpr int kBlock = 64 * kWaves;         // lanes per workgroup
-constexpr int kRows = 32 * kWaves;          // query rows per workgroup
+constexpr int kRows = 32 * kWaves;          // query rows per workgroup (one wave group)
 constexpr int kKeys = 64;                   // keys per tile
 constexpr int kKPad = 8;                    // K tile row padding (bf16)
 constexpr int kVPad = 8;                    // V^T tile row padding (bf16)
