@@ -13,10 +13,14 @@ Printed: one JSON line. `value` is achieved GB/s over the algorithmic bytes
 (read + write of the rotated part of every Q/K row once, each cos/sin row
 once, the indices once). It carries a `roofline` object for the dominant
 kernel (its launch duration measured with HIP events on the launch stream),
-a `cpu_baseline` (the CPU oracle timed on the host) and the decode-shape
-µs/call.
+`configs` with the same measurement on the other two large prefill
+workloads (BSHD interleaved fp16 and long context), the in-place stream
+ceiling at each workload's size, a `cpu_baseline` (the CPU oracle timed on
+the host, one thread and all host threads) and the decode-shape µs/call.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --summarize-trace TRACE_DIR BENCH_JSON   (rocprofv3 kernel trace
+        of a bench run -> per-kernel durations of the timed launches only)
 """
 from __future__ import annotations
 
@@ -36,7 +40,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "rotary_position_embedding_fwd_amd", "csrc", f)
                   for f in ("rope_kernels.hpp", "rope_plan.hpp", "librope.hip")]
-TRAFFIC_FILE = os.path.join(PROFILES, "traffic_rope_pair_lanes_kernel_bf16_llama_gqa_prefill.json")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_prefill_workloads.json")
 
 
 def kernel_source_hash() -> str:
@@ -75,17 +79,42 @@ def algorithmic_bytes(w, pos, tables: bool = True) -> int:
     return 2 * rotated + (4 * R * distinct if tables else 0) + idx_bytes
 
 
-def device_inputs(w, sets: int, which=("q", "k", "dq", "dk")):
-    import torch
+def device_inputs(w, sets: int, which=("q", "k", "dq", "dk"), grads_from_qk: bool = False):
+    """Seeded host tensors and `sets` device copies. grads_from_qk: draw only
+    q and k on the host and give each set dq, dk as device copies of them
+    (the values do not change the timing; drawing them costs seconds of host
+    time on the long-context shape)."""
     import workloads as W
-    t = W.tensors(w, which)
+    draw = ("q", "k") if grads_from_qk else which
+    t = W.tensors(w, draw)
     out = []
     for i in range(sets):
-        out.append({k: v.to("cuda") for k, v in t.items()})
+        d = {k: v.to("cuda") for k, v in t.items()}
+        if grads_from_qk:
+            d["dq"], d["dk"] = d["q"].clone(), d["k"].clone()
+        out.append(d)
     return t, out
 
 
-def time_prefill(w, steps: int, warmup: int, sets: int):
+SETTLE_MS = 100.0
+
+
+def settle(step, ms: float = SETTLE_MS):
+    """Run `step` untimed until `ms` of wall time have passed: the GPU's
+    clocks rise to their sustained level only after tens of milliseconds of
+    load (measured on MI355X: timed windows straight after idle vary by up to
+    20 % for a 23 µs kernel, and are steady after 50 ms of work)."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1000.0 < ms:
+        for _ in range(8):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
+def time_prefill(w, steps: int, warmup: int, sets: int, grads_from_qk: bool = False):
     """Time `steps` steps back to back between two HIP events on the launch
     stream. Forward and backward are the same kernel (the sign of sin is an
     argument), so the region divided by 2 * steps is that kernel's average
@@ -96,17 +125,20 @@ def time_prefill(w, steps: int, warmup: int, sets: int):
     pos = W.positions(w)
     cos, sin = rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta)
     cos, sin = cos.cuda(), sin.cuda()
-    host, bufs = device_inputs(w, sets)
+    host, bufs = device_inputs(w, sets, grads_from_qk=grads_from_qk)
     stream = torch.cuda.current_stream()
     kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim,
               pos=None if pos is None else pos.cuda(), stream=stream)
     fwd = [rp.prepare(b["q"], b["k"], cos, sin, **kw) for b in bufs]
     bwd = [rp.prepare(b["dq"], b["dk"], cos, sin, **kw) for b in bufs]
+    kw.pop("stream")
+    kernel = rp.rope_describe(bufs[0]["q"], bufs[0]["k"], cos, sin, **kw)
 
     def step(i):
         fwd[i % sets].rope_fwd_qk()
         bwd[i % sets].rope_bwd_qk()
 
+    settle(step)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -120,8 +152,51 @@ def time_prefill(w, steps: int, warmup: int, sets: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+    del fwd, bwd, bufs
+    torch.cuda.empty_cache()
+    return dict(total_ms=total_ms, wall_s=wall, pos=pos, host=host, kernel=kernel)
 
-    return dict(total_ms=total_ms, wall_s=wall, pos=pos, host=host)
+
+def _kernel_fields(desc: str) -> dict:
+    """rope_describe's line split into the kernel name and its key=value fields."""
+    parts = desc.split()
+    out = {"name": parts[0]}
+    for p in parts[1:]:
+        if "=" in p:
+            k, v = p.split("=", 1)
+            out[k] = int(v) if v.lstrip("-").isdigit() else v
+    return out
+
+
+# The other large prefill workloads, measured like the headline step:
+# (workload, steps, warmup, buffer sets). Sets are sized so one cycle of
+# them exceeds the 256 MB Infinity Cache.
+EXTRA_CONFIGS = (("BSHD_INTERLEAVED", 200, 40, 4), ("LONG_CONTEXT", 20, 10, 2))
+
+
+def time_config(w, steps: int, warmup: int, sets: int, ceiling: bool = True):
+    """One workload's fwd+bwd steps in place, as the headline step; beside it
+    the in-place stream ceiling over a buffer of the same Q+K size."""
+    r = time_prefill(w, steps, warmup, sets, grads_from_qk=True)
+    per_call = algorithmic_bytes(w, r["pos"])
+    avg_us = r["total_ms"] * 1000.0 / (2 * steps)
+    gbs = per_call / (avg_us * 1e-6) / 1e9
+    out = {"workload": w.name, "q_shape": list(w.q_shape), "k_shape": list(w.k_shape),
+           "storage_dtype": w.dtype, "layout": w.layout, "pairing": w.pairing,
+           "rotary_dim": w.rotary_dim, "table": [w.table_rows, w.rotary_dim // 2],
+           "theta": w.theta, "step": "rope_fwd_qk(Q,K) + rope_bwd_qk(dQ,dK), in place",
+           "steps": steps, "warmup": warmup, "buffer_sets": sets,
+           "algorithmic_bytes_per_call": per_call,
+           "us_per_launch": round(avg_us, 3), "GBps": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "kernel": r["kernel"], "traffic": stored_traffic(w.name)}
+    if ceiling:
+        e = 4 if w.dtype == "f32" else 2
+        qk = e * w.head_dim * w.batch * w.seq_len * (w.n_heads_q + w.n_heads_k)
+        c = stream_ceiling(qk, reps=max(10, steps), sets=max(2, -(-600_000_000 // qk)))
+        c["frac_achieved_of_ceiling"] = round(gbs / c["GBps"], 4)
+        out["measured_stream_ceiling"] = c
+    return out
 
 
 def time_decode(calls: int = 2000, warmup: int = 50, theta: bool = False):
@@ -147,6 +222,7 @@ def time_decode(calls: int = 2000, warmup: int = 50, theta: bool = False):
         return rp.prepare(q, k, cos, sin, layout=w.layout, pairing=w.pairing,
                           rotary_dim=w.rotary_dim, pos=pos, stream=st).rope_fwd_qk
     call = make(stream)
+    settle(lambda i: call())
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -186,43 +262,89 @@ def time_decode(calls: int = 2000, warmup: int = 50, theta: bool = False):
     torch.cuda.synchronize()
     graph_us = a.elapsed_time(b) * 1000.0 / (per_graph * replays)
     nbytes = algorithmic_bytes(w, pos.cpu(), tables=not theta)
+    desc = ("theta mode (rope_apply)" if theta else
+            rp.rope_describe(q, k, cos, sin, layout=w.layout, pairing=w.pairing,
+                             rotary_dim=w.rotary_dim, pos=pos))
     return {"workload": w.name, "angles": "theta" if theta else "tables",
             "us_per_call_graph_replay": round(graph_us, 3),
+            "empty_kernel_us_per_call_graph_replay": empty_kernel_floor(),
             "us_per_call_back_to_back": round(per_call_us, 3),
-            "us_kernel_event_median": round(kern[len(kern) // 2], 3),
-            "algorithmic_bytes": nbytes, "calls": calls,
-            "note": "graph replay: 100 captured calls per graph; back to back: Python "
-                    "ctypes launches, bound by the host call rate"}
+            "us_event_pair_median": round(kern[len(kern) // 2], 3),
+            "algorithmic_bytes": nbytes, "calls": calls, "warmup": warmup,
+            "graph_calls": per_graph * replays, "kernel": desc,
+            "note": "graph replay: 100 captured calls per graph replayed 20 times (no host "
+                    "launch cost); empty kernel: a one-workgroup kernel replayed the same "
+                    "way (the launch floor); back to back: Python ctypes launches, bound by "
+                    "the host call rate; event pair: one call between two HIP events, event "
+                    "overhead included (not a kernel duration: the kernel-only duration "
+                    "comes from the rocprofv3 trace)"}
 
 
-def stream_ceiling(nbytes: int = 3 << 29, reps: int = 20):
-    """GB/s of a plain in-place read+write stream (libstream_probe.so) over a
-    buffer larger than the 256 MB Infinity Cache: the attainable HBM rate of
-    an operation that reads and writes every byte once."""
+def _probe_lib():
     import ctypes
-    import torch
     path = os.path.join(ROOT, "rotary_position_embedding_fwd_amd", "libstream_probe.so")
     lib = ctypes.CDLL(path)
     lib.stream_rmw_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint,
                                      ctypes.c_void_p]
     lib.stream_rmw_probe.restype = ctypes.c_int
-    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    return lib
+
+
+def stream_ceiling(nbytes: int = 160 << 20, reps: int = 40, sets: int = 4):
+    """GB/s of a plain in-place read+write stream (libstream_probe.so) over
+    `nbytes` per launch, cycling through `sets` buffers whose total exceeds
+    the 256 MB Infinity Cache, launched back to back like the RoPE calls: the
+    attainable HBM rate of an operation that reads and writes every byte
+    once, at that size."""
+    import torch
+    lib = _probe_lib()
+    nbytes = (nbytes // 16) * 16
+    bufs = [torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(sets)]
     stream = torch.cuda.current_stream()
-    for _ in range(3):
-        assert lib.stream_rmw_probe(buf.data_ptr(), nbytes, 0, stream.cuda_stream) == 0
-    torch.cuda.synchronize()
+    for i in range(3):
+        assert lib.stream_rmw_probe(bufs[i % sets].data_ptr(), nbytes, 0,
+                                    stream.cuda_stream) == 0
+    settle(lambda i: lib.stream_rmw_probe(bufs[i % sets].data_ptr(), nbytes, 0,
+                                          stream.cuda_stream))
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record(stream)
-    for _ in range(reps):
-        lib.stream_rmw_probe(buf.data_ptr(), nbytes, 0, stream.cuda_stream)
+    for i in range(reps):
+        lib.stream_rmw_probe(bufs[i % sets].data_ptr(), nbytes, 0, stream.cuda_stream)
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1000.0 / reps
-    del buf
+    del bufs
+    torch.cuda.empty_cache()
     return {"kernel": "stream_rmw_kernel (16 B non-temporal load + store per lane)",
-            "bytes_per_launch": 2 * nbytes, "avg_launch_us": round(us, 2),
+            "bytes_per_launch": 2 * nbytes, "buffer_sets": sets, "avg_launch_us": round(us, 2),
             "GBps": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def empty_kernel_floor(calls: int = 100, replays: int = 20):
+    """µs per call of a one-workgroup kernel on 1 KiB, replayed from a captured
+    HIP graph: the launch floor under the decode measurement."""
+    import torch
+    lib = _probe_lib()
+    buf = torch.zeros(256, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(calls):
+            lib.stream_rmw_probe(buf.data_ptr(), 1024, 0, side.cuda_stream)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) * 1000.0 / (calls * replays), 3)
 
 
 def time_workload(w, launches=("auto", "rows", "token"), target_s: float = 0.15):
@@ -262,6 +384,7 @@ def _time_calls(out, fwd, bwd, sets, nbytes, target_s, stream, method=None):
     bm = method or "rope_bwd_qk"
     for name, calls in (("fwd", [getattr(c, fm) for c in fwd]),
                         ("bwd", [getattr(c, bm) for c in bwd])):
+        settle(lambda i: calls[i % sets]())
         for i in range(10):
             calls[i % sets]()
         torch.cuda.synchronize()
@@ -388,6 +511,7 @@ def attention_flops(w) -> int:
 def _time_event(fn, stream, target_s: float):
     """Average µs per call of fn() on `stream`, between HIP events."""
     import torch
+    settle(lambda i: fn())
     for _ in range(3):
         fn()
     torch.cuda.synchronize()
@@ -569,24 +693,62 @@ def time_layout_matrix(reps: int = 400):
             torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, host, pos, steps: int = 2):
-    """The CPU oracle, as it stands, on `steps` full steps (fwd + bwd) of w,
-    1 thread: about 10 s of CPU work on the Llama prefill workload."""
+def _oracle_call_slices(w, x, direction, pos):
+    """The oracle's calls for one tensor of workload w, one per (batch, head)
+    slice ([B,H,S,D]) or per batch ([B,S,H,D]); each slice keeps its own
+    positions, so the slices together compute exactly the whole call."""
+    import oracle
+    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, theta=w.theta,
+              table_rows=w.table_rows)
+    pv = None if pos is None else pos.numpy()
+    calls = []
+    if w.layout == "bhsd":
+        for b in range(x.shape[0]):
+            pb = None if pv is None else pv[b * w.pos_batch_stride:b * w.pos_batch_stride +
+                                              w.seq_len]
+            for h in range(x.shape[1]):
+                calls.append((x[b:b + 1, h:h + 1], dict(kw, pos=pb, direction=direction)))
+    else:
+        for b in range(x.shape[0]):
+            pb = None if pv is None else pv[b * w.pos_batch_stride:b * w.pos_batch_stride +
+                                              w.seq_len]
+            calls.append((x[b:b + 1], dict(kw, pos=pb, direction=direction)))
+    return [(lambda a=a, k=k: oracle.rope(a, w.dtype, **k)) for a, k in calls]
+
+
+def cpu_baseline(w, host, pos, steps: int = 2, all_steps: int = 4):
+    """The CPU oracle, as it stands: `steps` full steps (fwd of Q, K + bwd of
+    dQ, dK) of w on one thread (about 10 s on the Llama prefill workload),
+    then `all_steps` steps with the same calls cut into (batch, head) slices
+    run on every host thread; and the oracle's table build for w."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     orc = oracle
     orc.load()
-    nbytes = steps * 2 * algorithmic_bytes(w, pos)
+    arrs = {k: orc.torch_to_storage(v) for k, v in host.items()}
     kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim, theta=w.theta,
               pos=None if pos is None else pos.numpy(), pos_batch_stride=w.pos_batch_stride,
               table_rows=w.table_rows)
-    arrs = {k: orc.torch_to_storage(v) for k, v in host.items()}
     t0 = time.perf_counter()
     for _ in range(steps):
         orc.rope(arrs["q"], w.dtype, direction=1, **kw)
         orc.rope(arrs["k"], w.dtype, direction=1, **kw)
         orc.rope(arrs["dq"], w.dtype, direction=-1, **kw)
         orc.rope(arrs["dk"], w.dtype, direction=-1, **kw)
-    dt = time.perf_counter() - t0
+    dt1 = time.perf_counter() - t0
+    threads = max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                  else (os.cpu_count() or 1))
+    jobs = []
+    for name, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        jobs += _oracle_call_slices(w, arrs[name], direction, pos)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        for _ in range(all_steps):
+            list(ex.map(lambda f: f(), jobs))
+    dtn = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.table(w.theta, w.rotary_dim, w.table_rows)
+    dtab = time.perf_counter() - t0
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -596,23 +758,32 @@ def cpu_baseline(w, host, pos, steps: int = 2):
                     break
     except OSError:
         pass
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{steps} full steps (fwd of Q,K + bwd of dQ,dK) of {w.name}, "
-                      f"single-threaded scalar binary64 oracle",
+    step_bytes = 2 * algorithmic_bytes(w, pos)
+    return {"value": round(all_steps * step_bytes / dtn / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle", "seconds": round(dtn, 3),
+            "sample": f"{all_steps} full steps (fwd of Q,K + bwd of dQ,dK) of {w.name}, the "
+                      f"scalar binary64 oracle on (batch, head) slices over {threads} host "
+                      f"threads",
+            "single_thread": {"value": round(steps * step_bytes / dt1 / 1e9, 4), "unit": "GB/s",
+                              "cores": 1, "seconds": round(dt1, 3),
+                              "sample": f"{steps} full steps of {w.name}, one thread"},
+            "table_build_s": round(dtab, 4),
+            "table_build": f"the oracle's float32 cos/sin table [{w.table_rows}, "
+                           f"{w.rotary_dim // 2}] from theta {w.theta}",
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model}
 
 
-def stored_traffic():
-    """HBM traffic per launch from the committed rocprofv3 counter summary, or
-    None when the kernel sources changed since the counters were taken."""
+def stored_traffic(workload: str):
+    """HBM traffic per launch of `workload`'s kernel from the committed
+    rocprofv3 counter summary, or None when there is none or the kernel
+    sources changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t.get("workloads", {}).get(workload, {}).get("bytes_per_launch")
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
@@ -625,12 +796,22 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
     torch.cuda.synchronize()
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, out: str = TRAFFIC_FILE):
+def _bench_entries(b):
+    """(workload, kernel description, algorithmic bytes per call) of each timed
+    workload of a bench JSON line."""
+    out = [(b["config"]["workload"], b["roofline"]["launch"],
+            b["config"]["algorithmic_bytes_per_call"])]
+    for c in b.get("configs", []):
+        out.append((c["workload"], c["kernel"], c["algorithmic_bytes_per_call"]))
+    return out
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, bench_json: str, out: str = TRAFFIC_FILE):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
-    `bench.py --copy-calibration` into per-launch traffic of the forward
-    prefill kernel, scaled by the counters of the 1 GiB copy."""
+    `bench.py --copy-calibration` into per-launch HBM traffic of each timed
+    workload's kernel (matched by name and grid size), each counter scaled by
+    its reading for the 1 GiB device copy."""
     import csv
-    import workloads as W
 
     def read(d, counter):
         rows = []
@@ -638,34 +819,123 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str = TRAFFIC_FILE):
             with open(p) as f:
                 for r in csv.DictReader(f):
                     if r.get("Counter_Name") == counter:
-                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+                        rows.append((r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0),
+                                     int(r.get("Workgroup_Size", 0) or 0),
+                                     float(r["Counter_Value"])))
         return rows
 
-    def pick(rows, pred):
-        vals = [v for n, v in rows if pred(n)]
-        return sum(vals) / len(vals) if vals else None
+    def pick(rows, name, grid=None, block=None):
+        vals = [v for n, g, wg, v in rows
+                if name in n and (grid is None or g == grid) and (block is None or wg == block)]
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
-    # the kernel the bench's step runs (the one-chunk-per-lane rows kernel)
-    is_fwd = lambda n: "rope_pair_lanes_kernel" in n and "bf16" in n.replace("DF16b", "bf16")  # noqa
-    is_copy = lambda n: "copyBuffer" in n  # the runtime's device-to-device copy  # noqa
+    with open(bench_json) as f:
+        b = json.loads([ln for ln in f if ln.startswith("{")][-1])
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
-    f_k, w_k = pick(fetch, is_fwd), pick(write, is_fwd)
-    f_c, w_c = pick(fetch, is_copy), pick(write, is_copy)
     copy_bytes = 1 << 30
-    res = {"kernel": "rope_pair_lanes_kernel<__bf16, 8, 4> (forward and backward launches)",
-           "workload": W.LLAMA_GQA_PREFILL.name,
-           "fetch_kib_per_launch": f_k, "write_kib_per_launch": w_k,
-           "copy_fetch_kib": f_c, "copy_write_kib": w_c}
-    if None not in (f_k, w_k, f_c, w_c):
-        rf, rw = copy_bytes / (f_c * 1024), copy_bytes / (w_c * 1024)
-        res.update({"fetch_scale": rf, "write_scale": rw,
-                    "bytes_per_launch": round(f_k * 1024 * rf + w_k * 1024 * rw),
-                    "algorithmic_bytes_per_launch":
-                        algorithmic_bytes(W.LLAMA_GQA_PREFILL, None)})
+    f_c, _ = pick(fetch, "copyBuffer")  # the runtime's device-to-device copy
+    w_c, _ = pick(write, "copyBuffer")
+    res = {"copy_bytes": copy_bytes, "copy_fetch_kib": f_c, "copy_write_kib": w_c,
+           "workloads": {}}
+    if f_c and w_c:
+        res["fetch_scale"] = copy_bytes / (f_c * 1024)
+        res["write_scale"] = copy_bytes / (w_c * 1024)
+    for workload, launch, alg in _bench_entries(b):
+        k = _kernel_fields(launch)
+        items = k.get("grid", 0) * k.get("block", 0)
+        f_k, nf = pick(fetch, k["name"], items, k.get("block"))
+        w_k, nw = pick(write, k["name"], items, k.get("block"))
+        e = {"kernel": k["name"], "grid": k.get("grid"), "block": k.get("block"),
+             "fetch_kib_per_launch": f_k, "write_kib_per_launch": w_k,
+             "dispatches": [nf, nw], "algorithmic_bytes_per_launch": alg}
+        if None not in (f_k, w_k) and "fetch_scale" in res:
+            e["bytes_per_launch"] = round(f_k * 1024 * res["fetch_scale"] +
+                                          w_k * 1024 * res["write_scale"])
+            e["traffic_over_algorithmic"] = round(e["bytes_per_launch"] / alg, 4)
+        res["workloads"][workload] = e
     res["kernel_source_hash"] = kernel_source_hash()
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res))
+
+
+def _trace_rows(trace_dir: str):
+    """Kernel dispatches of a rocprofv3 --kernel-trace run, in dispatch order:
+    (name, workgroup size, grid size in work-items, duration ns)."""
+    import csv
+    rows = []
+    for p in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r.get("Dispatch_Id", 0) or 0), r["Kernel_Name"],
+                             int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 0)) or 0),
+                             int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0),
+                             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    return [r[1:] for r in rows]
+
+
+def _stats_us(ns):
+    import statistics
+    us = [x / 1000.0 for x in ns]
+    return {"launches": len(us), "mean_us": round(statistics.fmean(us), 3),
+            "median_us": round(statistics.median(us), 3), "min_us": round(min(us), 3),
+            "max_us": round(max(us), 3)}
+
+
+def summarize_trace(trace_dir: str, bench_json: str):
+    """Per-kernel durations of the launches bench.py timed, from a rocprofv3
+    kernel trace of that bench run: for each timed workload, the dispatches
+    of its kernel with its grid, in order, minus the warmup launches, then
+    exactly the timed ones. Prints one JSON object (mean, median, min, max
+    µs per launch, and GB/s over the algorithmic bytes)."""
+    with open(bench_json) as f:
+        line = [ln for ln in f if ln.startswith("{")][-1]
+    b = json.loads(line)
+    rows = _trace_rows(trace_dir)
+    entries = [dict(workload=b["config"]["workload"], launch=b["roofline"]["launch"],
+                    warmup=b["warmup"], steps=b["steps"],
+                    bytes=b["config"]["algorithmic_bytes_per_call"],
+                    bench_us=b["roofline"]["avg_launch_us"])]
+    for c in b.get("configs", []):
+        entries.append(dict(workload=c["workload"], launch=c["kernel"], warmup=c["warmup"],
+                            steps=c["steps"], bytes=c["algorithmic_bytes_per_call"],
+                            bench_us=c["us_per_launch"]))
+    out = {"trace_dir": trace_dir, "workloads": []}
+    used = set()
+    for e in entries:
+        k = _kernel_fields(e["launch"])
+        items = k.get("grid", 0) * k.get("block", 0)
+        idx = [i for i, (name, wg, grid, _) in enumerate(rows)
+               if i not in used and k["name"] in name and wg == k.get("block") and
+               grid == items]
+        skip, take = 2 * e["warmup"], 2 * e["steps"]
+        timed = idx[skip:skip + take]
+        used.update(idx[:skip + take])
+        res = {"workload": e["workload"], "kernel": k["name"], "grid": k.get("grid"),
+               "block": k.get("block"), "dispatches_found": len(idx),
+               "warmup_dropped": min(skip, len(idx)),
+               "bench_event_avg_launch_us": e["bench_us"]}
+        if timed:
+            st = _stats_us([rows[i][3] for i in timed])
+            st["GBps_at_mean"] = round(e["bytes"] / (st["mean_us"] * 1e-6) / 1e9, 1)
+            st["frac_at_mean"] = round(st["GBps_at_mean"] / HBM_PEAK_GBS, 4)
+            res.update(st)
+        out["workloads"].append(res)
+    if "decode" in b and b["decode"].get("kernel"):
+        k = _kernel_fields(b["decode"]["kernel"])
+        items = k.get("grid", 0) * k.get("block", 0)
+        idx = [i for i, (name, wg, grid, _) in enumerate(rows)
+               if i not in used and k["name"] in name and wg == k.get("block") and
+               grid == items]
+        if idx:
+            res = {"workload": b["decode"]["workload"], "kernel": k["name"],
+                   "grid": k.get("grid"), "block": k.get("block"),
+                   "note": "every decode dispatch (warmup, eager, event-pair and graph "
+                           "replays)"}
+            res.update(_stats_us([rows[i][3] for i in idx]))
+            out["decode"] = res
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -678,9 +948,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the BSHD interleaved and long-context configs")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"))
     ap.add_argument("--workloads", action="store_true",
                     help="time every workload (both grid shapes); one JSON line each")
     ap.add_argument("--general-form", action="store_true",
@@ -699,6 +972,9 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the RoPE path has no cross-GPU step, "
@@ -750,7 +1026,8 @@ def main():
     launches = 2 * args.steps
     avg_launch_us = r["total_ms"] * 1000.0 / launches
     achieved = per_call / (avg_launch_us * 1e-6) / 1e9
-    traffic = stored_traffic()
+    traffic = stored_traffic(w.name)
+    kernel = _kernel_fields(r["kernel"])
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -763,6 +1040,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "storage_dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "q_shape": list(w.q_shape), "k_shape": list(w.k_shape),
                    "storage_dtype": w.dtype, "layout": w.layout, "pairing": w.pairing,
@@ -774,16 +1052,23 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "rope_pair_lanes_kernel<__bf16, 8, 4> (fwd and bwd launches)",
+                     "kernel": kernel["name"] + " (fwd and bwd launches)",
+                     "launch": r["kernel"],
                      "algorithmic_bytes_per_launch": per_call,
                      "avg_launch_us": round(avg_launch_us, 3),
                      "launches_timed": launches},
         "wall_s_timed": round(r["wall_s"], 4),
     }
     if not args.no_ceiling:
-        ceil = stream_ceiling()
+        e = 2
+        qk = e * w.head_dim * w.batch * w.seq_len * (w.n_heads_q + w.n_heads_k)
+        ceil = stream_ceiling(qk, reps=2 * args.steps, sets=max(2, -(-600_000_000 // qk)))
         ceil["frac_achieved_of_ceiling"] = round(achieved / ceil["GBps"], 4)
         out["roofline"]["measured_stream_ceiling"] = ceil
+    if not args.no_configs:
+        out["configs"] = [time_config(getattr(W, name), st, wu, sets,
+                                      ceiling=not args.no_ceiling)
+                          for name, st, wu, sets in EXTRA_CONFIGS]
     if not args.no_decode:
         out["decode"] = time_decode()
     if not args.no_cpu_baseline:

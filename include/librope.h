@@ -88,8 +88,11 @@ typedef enum rope_pairing { ROPE_SPLIT_HALF = 0, ROPE_INTERLEAVED = 1 } rope_pai
 /* Which grid shape to launch. AUTO walks memory in order: the token shape
  * when a token's heads are adjacent ([B,S,H,D], packed QKV) and at decode
  * (seq_len 1), the rows shape for [B,H,S,D] unless there are too few tokens
- * to fill the device. The two shapes run the same per-pair arithmetic and
- * give bit-identical results. */
+ * to fill the device; within each, AUTO may also pick a form that only it
+ * launches (one (token, head) chunk per lane for [B,H,S,D] split-half calls,
+ * items over the whole call for dense [B,S,H,D] interleaved calls). Every
+ * shape runs the same per-pair arithmetic and gives bit-identical results;
+ * ROWS and TOKEN force the named shape's general kernels (for comparisons). */
 typedef enum rope_launch {
   ROPE_LAUNCH_AUTO = 0,
   ROPE_LAUNCH_ROWS = 1,  /* lanes over (token, chunk), loop over heads */
@@ -120,7 +123,11 @@ typedef struct rope_desc {
   int64_t pos_batch_stride; /* index of token (b, s) is pos[b * stride + s]; 0 shares one row */
 } rope_desc_t;
 
-/* Forward RoPE on Q and K in one launch, in place.
+/* Forward RoPE on Q and K in one launch, in place (How Unsloth Optimizes
+ * RoPE ..., Triton Kernel Architecture for RoPE: one kernel rotates the query
+ * and key heads of a token together, so each cos/sin row is read once for
+ * both; Manual Triton Kernel Invocation: Q, K, cos, sin, optional int32
+ * positions and the number of K heads are its arguments).
  * q: device, d->dtype elements in d->layout, shape with n_heads_q heads.
  * k: device, same with n_heads_k heads; must not overlap q.
  * ROPE_ERR_ALIAS when q and k overlap, or either overlaps cos, sin or the
@@ -353,6 +360,17 @@ rope_status_t rope_attention_fwd_k_once(const rope_attn_desc_t *d, void *k_works
  * interpolate_factor that is not finite and > 0. */
 rope_status_t rope_build_table(float *cos_out, float *sin_out, int64_t table_rows,
                                int64_t rotary_dim, double theta, double interpolate_factor);
+
+/* Which kernel and grid rope_fwd_qk (with_k != 0) or rope_fwd_q (with_k ==
+ * 0) would launch for these arguments on the current device, as one line of
+ * text ("rope_head_lanes_kernel dtype=bf16 vec=8 ... grid=10240 block=512
+ * ..."; the kernel name is the one traces show). For benchmarks and
+ * diagnostics: nothing is enqueued, q and k are not dereferenced, and the
+ * backward calls launch the same kernel. buf: host memory of len bytes,
+ * always NUL-terminated. Errors as rope_fwd_qk (validation), ROPE_ERR_NULL
+ * for a NULL or empty buf, ROPE_ERR_HIP when there is no current device. */
+rope_status_t rope_describe(const void *q, const void *k, const rope_desc_t *d, int with_k,
+                            char *buf, int64_t len);
 
 /* A static, human-readable name for a status code ("unknown status" for
  * codes this library never returns). */

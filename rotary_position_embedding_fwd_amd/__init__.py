@@ -145,6 +145,8 @@ def lib():
         L.rope_attention_fwd_k_once.argtypes = [ctypes.POINTER(RopeAttnDesc), P, P]
         L.rope_attention_fwd_k_once.restype = ctypes.c_int
         L.rope_attention_fwd.restype = ctypes.c_int
+        L.rope_describe.argtypes = [P, P, D, ctypes.c_int, ctypes.c_char_p, ctypes.c_int64]
+        L.rope_describe.restype = ctypes.c_int
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_status_string.restype = ctypes.c_char_p
         L.rope_version.argtypes = []
@@ -245,8 +247,25 @@ def _check(status: int, where: str):
         raise RopeError(status, where)
 
 
+def _on_one_device(where: str, *tensors):
+    """Every tensor a call hands to librope must be GPU memory of one device:
+    the library cannot tell a host pointer from a device pointer without
+    touching the GPU, and a kernel that dereferences a host pointer faults.
+    None entries (absent optional operands) are skipped."""
+    ts = [t for t in tensors if t is not None]
+    if not ts:
+        return
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError(f"{where}: every tensor must be on the GPU, got one on {t.device}")
+        if t.device != dev:
+            raise ValueError(f"{where}: tensors on {dev} and {t.device}; use one device")
+
+
 def rope_fwd_qk(q, k, cos, sin, *, stream=None, **kw):
     """Forward RoPE on q and k in place (one launch). See make_desc for options."""
+    _on_one_device("rope_fwd_qk", q, k, cos, sin, kw.get("pos"))
     d = make_desc(q, k, cos, sin, **kw)
     _check(lib().rope_fwd_qk(q.data_ptr(), k.data_ptr(), ctypes.byref(d), _stream(stream)),
            "rope_fwd_qk")
@@ -255,6 +274,7 @@ def rope_fwd_qk(q, k, cos, sin, *, stream=None, **kw):
 
 def rope_bwd_qk(dq, dk, cos, sin, *, stream=None, **kw):
     """Backward RoPE on gradients dq and dk in place."""
+    _on_one_device("rope_bwd_qk", dq, dk, cos, sin, kw.get("pos"))
     d = make_desc(dq, dk, cos, sin, **kw)
     _check(lib().rope_bwd_qk(dq.data_ptr(), dk.data_ptr(), ctypes.byref(d), _stream(stream)),
            "rope_bwd_qk")
@@ -263,6 +283,7 @@ def rope_bwd_qk(dq, dk, cos, sin, *, stream=None, **kw):
 
 def rope_fwd_q(q, cos, sin, *, stream=None, **kw):
     """Forward RoPE on q only, in place."""
+    _on_one_device("rope_fwd_q", q, cos, sin, kw.get("pos"))
     d = make_desc(q, None, cos, sin, **kw)
     _check(lib().rope_fwd_q(q.data_ptr(), ctypes.byref(d), _stream(stream)), "rope_fwd_q")
     return q
@@ -270,9 +291,22 @@ def rope_fwd_q(q, cos, sin, *, stream=None, **kw):
 
 def rope_bwd_q(dq, cos, sin, *, stream=None, **kw):
     """Backward RoPE on dq only, in place."""
+    _on_one_device("rope_bwd_q", dq, cos, sin, kw.get("pos"))
     d = make_desc(dq, None, cos, sin, **kw)
     _check(lib().rope_bwd_q(dq.data_ptr(), ctypes.byref(d), _stream(stream)), "rope_bwd_q")
     return dq
+
+
+def rope_describe(q, k, cos, sin, **kw) -> str:
+    """The kernel and grid rope_fwd_qk(q, k, ...) (or rope_fwd_q when k is
+    None) would launch on the current device; nothing is enqueued."""
+    _on_one_device("rope_describe", q, k, cos, sin, kw.get("pos"))
+    d = make_desc(q, k, cos, sin, **kw)
+    buf = ctypes.create_string_buffer(512)
+    _check(lib().rope_describe(q.data_ptr(), None if k is None else k.data_ptr(),
+                               ctypes.byref(d), int(k is not None), buf, len(buf)),
+           "rope_describe")
+    return buf.value.decode()
 
 
 TABLE_LAYOUTS = ("half", "duplicated", "interleaved")
@@ -386,6 +420,7 @@ def make_apply_desc(q, k, cos, sin, *, q_out=None, k_out=None, direction: int = 
 def rope_apply(q, k, cos, sin, *, stream=None, **kw):
     """General call: strided views, optional outputs (q_out, k_out), direction
     +1/-1, table layouts. Returns the tensors that hold the result."""
+    _on_one_device("rope_apply", q, k, cos, sin, kw.get("pos"), kw.get("q_out"), kw.get("k_out"))
     d = make_apply_desc(q, k, cos, sin, **kw)
     _check(lib().rope_apply(ctypes.byref(d), _stream(stream)), "rope_apply")
     qo = kw.get("q_out")
@@ -414,6 +449,8 @@ def rope_apply_xpos(q, k, cos, sin, xpos_q, xpos_k, *, stream=None, **kw):
     that hold the result."""
     if kw.get("theta") is not None:
         raise ValueError("XPOS factors come with cos/sin tables, not theta")
+    _on_one_device("rope_apply_xpos", q, k, cos, sin, xpos_q, xpos_k, kw.get("pos"),
+                   kw.get("q_out"), kw.get("k_out"))
     d = make_apply_desc(q, k, cos, sin, **kw)
     zq, zk = _xpos_ptrs(xpos_q, xpos_k, cos)
     _check(lib().rope_apply_xpos(ctypes.byref(d), zq, zk, _stream(stream)), "rope_apply_xpos")
@@ -429,6 +466,7 @@ class Prepared:
 
     def __init__(self, q, k, cos, sin, stream=None, **kw):
         self._keep = (q, k, cos, sin, kw.get("pos"))
+        _on_one_device("prepare", q, k, cos, sin, kw.get("pos"))
         self.desc = make_desc(q, k, cos, sin, **kw)
         self._q = q.data_ptr()
         self._k = k.data_ptr() if k is not None else None
@@ -457,6 +495,8 @@ class PreparedApplyXpos:
                       kw.get("k_out"))
         if kw.get("theta") is not None:
             raise ValueError("XPOS factors come with cos/sin tables, not theta")
+        _on_one_device("prepare_apply_xpos", q, k, cos, sin, xpos_q, xpos_k, kw.get("pos"),
+                       kw.get("q_out"), kw.get("k_out"))
         self.desc = make_apply_desc(q, k, cos, sin, **kw)
         self._zq, self._zk = _xpos_ptrs(xpos_q, xpos_k, cos)
         self._stream = _stream(stream)
@@ -479,6 +519,8 @@ class PreparedApply:
 
     def __init__(self, q, k, cos, sin, stream=None, **kw):
         self._keep = (q, k, cos, sin, kw.get("pos"), kw.get("q_out"), kw.get("k_out"))
+        _on_one_device("prepare_apply", q, k, cos, sin, kw.get("pos"), kw.get("q_out"),
+                       kw.get("k_out"))
         self.desc = make_apply_desc(q, k, cos, sin, **kw)
         self._stream = _stream(stream)
         self._pdesc = ctypes.byref(self.desc)
@@ -571,9 +613,18 @@ def make_attn_desc(q, k, v, cos, sin, o, *, pairing: str = "split_half",
     d.rotate = int(bool(rotate))
     d.q, d.k, d.v, d.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
     if cos is not None:
-        if cos.dim() != 2 or tuple(sin.shape) != tuple(cos.shape):
+        import torch
+        if sin is None or cos.dim() != 2 or tuple(sin.shape) != tuple(cos.shape):
             raise ValueError("cos and sin must be [table_rows, R/2]")
-        d.rotary_dim = 2 * cos.shape[1] if rotary_dim is None else rotary_dim
+        if cos.dtype != torch.float32 or sin.dtype != torch.float32:
+            raise ValueError("cos and sin must be float32")
+        if not cos.is_contiguous() or not sin.is_contiguous():
+            raise ValueError("cos and sin must be contiguous [table_rows, R/2] tables")
+        R = 2 * cos.shape[1] if rotary_dim is None else int(rotary_dim)
+        if cos.shape[1] != R // 2 or R % 2:
+            raise ValueError(f"tables have {cos.shape[1]} columns, rotary_dim {R} needs "
+                             f"{R // 2}")
+        d.rotary_dim = R
         d.cos, d.sin = cos.data_ptr(), sin.data_ptr()
         d.table_rows = cos.shape[0]
     else:
@@ -604,6 +655,8 @@ def rope_attention(q, k, v, cos, sin, *, o=None, stream=None, k_workspace=None, 
     import torch
     if o is None:
         o = torch.empty_like(q)
+    _on_one_device("rope_attention", q, k, v, cos, sin, o, kw.get("q_pos"), kw.get("k_pos"),
+                   k_workspace)
     d = make_attn_desc(q, k, v, cos, sin, o, **kw)
     ws = _k_workspace(k_workspace, k)
     if ws is None:
@@ -619,6 +672,8 @@ class PreparedAttention:
 
     def __init__(self, q, k, v, cos, sin, o, stream=None, k_workspace=None, **kw):
         self._keep = (q, k, v, cos, sin, o, kw.get("q_pos"), kw.get("k_pos"), k_workspace)
+        _on_one_device("prepare_attention", q, k, v, cos, sin, o, kw.get("q_pos"),
+                       kw.get("k_pos"), k_workspace)
         self.desc = make_attn_desc(q, k, v, cos, sin, o, **kw)
         self._ws = _k_workspace(k_workspace, k)
         self._stream = _stream(stream)

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 
 #include "librope.h"
 #include "rope_kernels.hpp"
@@ -15,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 10200;  // 1.2.0: angles computed from theta, interpolate_factor
+constexpr int kVersion = 10300;  // 1.3.0: head-lanes and flat kernels, rope_describe
 constexpr int kMaxDevices = 64;
 
 // Compute units per device, read once per device.
@@ -43,6 +44,7 @@ struct GpuLauncher {
     const int mode = pl.token ? pl.token_mode() : -1;
     const unsigned lds = (unsigned)pl.lds_bytes;
     constexpr int RT = rope::kSrcRuntime;
+    if (launch_only_auto<T, V, PAIR, AL, OOP>(grid, block)) return;
     if (mode == rope::kTokenOne && pl.a.angles)
       hipLaunchKernelGGL(
           (rope::rope_token_kernel<T, V, PAIR, AL, rope::kTokenOne, OOP, rope::kTrigTheta>), grid,
@@ -64,6 +66,37 @@ struct GpuLauncher {
     else if (!launch_pair<T, V, PAIR, AL, OOP>(grid, block))
       hipLaunchKernelGGL((rope::rope_rows_kernel<T, V, PAIR, AL, 4, OOP>), grid, block, 0, st,
                          pl.a);
+  }
+
+  // the forms only the automatic launch picks, instantiated for the calls the
+  // planner gives them (in place; head lanes: split-half 16-byte chunks;
+  // flat: interleaved pairs)
+  template <typename T, int V, int PAIR, bool AL, bool OOP>
+  bool launch_only_auto(dim3 grid, dim3 block) {
+    const bool idx = pl.a.pos != nullptr;
+    if constexpr (!OOP && AL && PAIR == rope::kSplitHalf && V * sizeof(T) == 16) {
+      if (pl.head_lanes) {
+        if (idx)
+          hipLaunchKernelGGL((rope::rope_head_lanes_kernel<T, V, PAIR, AL, OOP, true>), grid,
+                             block, 0, st, pl.a);
+        else
+          hipLaunchKernelGGL((rope::rope_head_lanes_kernel<T, V, PAIR, AL, OOP, false>), grid,
+                             block, 0, st, pl.a);
+        return true;
+      }
+    }
+    if constexpr (!OOP && AL && PAIR == rope::kInterleaved) {
+      if (pl.flat) {
+        if (idx)
+          hipLaunchKernelGGL((rope::rope_flat_kernel<T, V, PAIR, AL, OOP, true>), grid, block,
+                             0, st, pl.a);
+        else
+          hipLaunchKernelGGL((rope::rope_flat_kernel<T, V, PAIR, AL, OOP, false>), grid, block,
+                             0, st, pl.a);
+        return true;
+      }
+    }
+    return false;
   }
 
   // the one-chunk-per-lane rows kernel, for the plans that chose it
@@ -102,6 +135,31 @@ rope_status_t run_apply(const rope_apply_desc_t* d, void* stream) {
   return rope::dispatch(pl, launcher) == hipSuccess ? ROPE_OK : ROPE_ERR_HIP;
 }
 
+// The kernel a plan launches, as it is named in traces, and its grid.
+void describe_plan(const rope::Plan& pl, char* buf, int64_t len) {
+  const char* kernel = "none (empty call)";
+  if (!pl.empty) {
+    if (pl.flat)
+      kernel = "rope_flat_kernel";
+    else if (pl.head_lanes)
+      kernel = "rope_head_lanes_kernel";
+    else if (pl.token)
+      kernel = "rope_token_kernel";
+    else if (pl.pair)
+      kernel = "rope_pair_lanes_kernel";
+    else
+      kernel = "rope_rows_kernel";
+  }
+  static const char* kDtypes[] = {"f32", "f16", "bf16"};
+  const char* dt = pl.dtype >= 0 && pl.dtype <= 2 ? kDtypes[pl.dtype] : "?";
+  snprintf(buf, (size_t)len,
+           "%s dtype=%s vec=%d pairing=%s grid=%lld block=%d lanes_per_token=%d "
+           "tokens_per_workgroup=%d heads_per_group=%d%s",
+           kernel, dt, pl.vec, pl.pairing == ROPE_INTERLEAVED ? "interleaved" : "split_half",
+           (long long)pl.grid, pl.block, pl.a.lanes, pl.a.tokens_per_block,
+           pl.a.heads_per_group, pl.oop ? " out_of_place" : "");
+}
+
 rope_status_t run(void* q, void* k, const rope_desc_t* d, void* stream, bool with_k,
                   int direction) {
   rope_apply_desc_t a;
@@ -131,6 +189,24 @@ rope_status_t rope_bwd_q(void* dq, const rope_desc_t* d, void* stream) {
 }
 
 rope_status_t rope_apply(const rope_apply_desc_t* d, void* stream) { return run_apply(d, stream); }
+
+rope_status_t rope_describe(const void* q, const void* k, const rope_desc_t* d, int with_k,
+                            char* buf, int64_t len) {
+  if (!buf || len < 1) return ROPE_ERR_NULL;
+  buf[0] = 0;
+  rope_apply_desc_t a;
+  const rope_status_t st = rope::desc_to_apply(q, k, d, with_k != 0, 1, &a);
+  if (st != ROPE_OK) return st;
+  const rope_status_t vs = rope::validate_apply(&a);
+  if (vs != ROPE_OK) return vs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ROPE_ERR_HIP;
+  rope::Plan pl;
+  const rope_status_t ps = rope::make_plan_apply(&a, cu_count(dev), &pl);
+  if (ps != ROPE_OK) return ps;
+  describe_plan(pl, buf, len);
+  return ROPE_OK;
+}
 
 rope_status_t rope_build_table(float* cos_out, float* sin_out, int64_t table_rows,
                                int64_t rotary_dim, double theta, double interpolate_factor) {

@@ -90,6 +90,9 @@ struct Args {
   View q_out, k_out;         // equal to the inputs in place
   double l2_step;            // angles from theta: -2 log2(theta) / R
   double interp;             // angles from theta: positions are divided by it
+  int64_t n_items_q;         // flat shape: the items of Q (n_tokens * n_heads_q * lanes)
+  int32_t tokens_shift;      // head-lanes shape: log2(tokens_per_block)
+  int32_t pad0;
 };
 
 // ------------------------------------------------------------ storage I/O
@@ -644,6 +647,144 @@ __global__ void __launch_bounds__(kRowsBlock) rope_pair_lanes_kernel(Args a) {
   else
     pair_lanes_body<T, V, U, kTrigScalar>(a);
 #endif
+}
+
+// One lane's chunk c of the row of token (b, s) at `in`, rotated into `out`.
+// The row load and the cos/sin loads are issued back to back. IDX (whether
+// the call has an index tensor) is a compile-time choice, made by the host
+// per launch: where the two cases shared one body, the compiler joined them
+// after the loads and made the cos/sin loads wait for the row load.
+//   IDX false: positions are the sequence indices, all inside the table (the
+//     host rejects seq_len > table_rows without an index), so nothing is
+//     skipped and nothing branches.
+//   IDX true: a skipped token (position out of the table) asks for row 0 of
+//     the table like the others and only its store is dropped (out of place
+//     its row is copied); with no table rows at all every token is skipped
+//     and no table read is issued.
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, int SRC, bool IDX>
+ROPE_HD void rotate_one_chunk(const Args& a, const T* in, T* out, int64_t b, int64_t s, int c) {
+  RowChunk<T, V, PAIR, ALIGNED> r;
+  r.load(in, c, a.half);
+  Trig<V, PAIR> t;
+  if constexpr (!IDX) {
+    t.template load<SRC>(a, s, c * ChunkGeom<V, PAIR>::kPairs);
+  } else {
+    const int64_t p = token_pos(a, b, s);
+    if (SRC != kTrigTheta && a.table_rows == 0) {  // uniform: nothing to rotate
+      if constexpr (OOP) copy_span<T, V, ALIGNED>(in, out, 0, a.head_dim, c, a.lanes);
+      return;
+    }
+    t.template load<SRC>(a, p < 0 ? 0 : p, c * ChunkGeom<V, PAIR>::kPairs);
+    if (p < 0) {  // skipped token: in place nothing is written
+      if constexpr (OOP) copy_span<T, V, ALIGNED>(in, out, 0, a.head_dim, c, a.lanes);
+      return;
+    }
+  }
+  r.rotate(t);
+  r.store(out, c, a.half);
+  if constexpr (OOP) copy_span<T, V, ALIGNED>(in, out, 2 * a.half, a.head_dim, c, a.lanes);
+}
+
+// ------------------------------------------------------- head-lanes shape
+// One chunk of one (token, head) per lane and nothing looped: a workgroup
+// holds tokens_per_block consecutive tokens x `lanes` chunks x heads_per_group
+// heads of one head group, lanes numbered chunk fastest, then token, then
+// head. A wave therefore covers whole rotated spans of consecutive tokens of
+// one head (or of two), every lane issues its row loads and its cos/sin loads
+// at once, and the heads of the group ask for the same cos/sin rows, which
+// the first wave brings into the compute unit's cache for the others.
+// Workgroup ids run over all token tiles of head group 0, then group 1, ...
+// Chosen for [B,H,S,D] views whose rows are split-half pairs in 16-byte
+// chunks; the planner fixes the workgroup's token and head counts from the
+// distance between heads.
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, int SRC, bool IDX>
+ROPE_HD void head_lanes_body(const Args& a, int64_t block, int thread) {
+  const int c = thread & (a.lanes - 1);
+  const int rest = thread >> a.lanes_shift;
+  const int tl = rest & (a.tokens_per_block - 1);
+  const int hl = rest >> a.tokens_shift;
+  const int64_t group = block / a.n_tiles;
+  const int64_t tile = block - group * a.n_tiles;
+  const int64_t n = (tile << a.tokens_shift) + tl;
+  const int h = (int)group * a.heads_per_group + hl;
+  if (n >= a.n_tokens || hl >= a.heads_per_group || h >= a.n_heads_q + a.n_heads_k) return;
+  const int64_t b = n / a.seq_len;
+  const int64_t s = n - b * a.seq_len;
+  const bool is_q = h < a.n_heads_q;
+  const int hh = is_q ? h : h - a.n_heads_q;
+  const T* in = view_row<T>(is_q ? a.q_in : a.k_in, hh, b, s);
+  T* out = OOP ? view_row<T>(is_q ? a.q_out : a.k_out, hh, b, s) : const_cast<T*>(in);
+  rotate_one_chunk<T, V, PAIR, ALIGNED, OOP, SRC, IDX>(a, in, out, b, s, c);
+}
+
+// Every (source, index) form, chosen at run time: for the host emulation.
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP>
+ROPE_HD void head_lanes_entry(const Args& a, int64_t block, int thread) {
+  if (a.angles)
+    head_lanes_body<T, V, PAIR, ALIGNED, OOP, kTrigTheta, true>(a, block, thread);
+  else if (!a.t_vec)
+    head_lanes_body<T, V, PAIR, ALIGNED, OOP, kTrigScalar, true>(a, block, thread);
+  else if (a.pos)
+    head_lanes_body<T, V, PAIR, ALIGNED, OOP, kTrigVec, true>(a, block, thread);
+  else
+    head_lanes_body<T, V, PAIR, ALIGNED, OOP, kTrigVec, false>(a, block, thread);
+}
+
+// The planner gives this shape [rows, R/2]-style tables only (kTrigVec).
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, bool IDX>
+__global__ void __launch_bounds__(1024) rope_head_lanes_kernel(Args a) {
+  head_lanes_body<T, V, PAIR, ALIGNED, OOP, kTrigVec, IDX>(a, blockIdx.x, threadIdx.x);
+}
+
+// ------------------------------------------------------------- flat shape
+// One (token, head, chunk) item per lane, items numbered over the whole call:
+// all of Q's (token, head, chunk) items, then all of K's, chunk fastest. For
+// views whose rows are dense in token-major order ([B,S,H,D] contiguous)
+// consecutive lanes and consecutive workgroups then walk each tensor in memory
+// order, one tensor after the other, like a plain stream. Small workgroups
+// (kFlatBlock lanes) measured best on MI355X.
+constexpr int kFlatBlock = 64;
+
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, int SRC, bool IDX>
+ROPE_HD void flat_body(const Args& a, int64_t block, int thread) {
+  int64_t g = block * kFlatBlock + thread;
+  if (g >= a.n_items) return;
+  const bool is_q = g < a.n_items_q;
+  if (!is_q) g -= a.n_items_q;
+  const int heads = is_q ? a.n_heads_q : a.n_heads_k;
+  int64_t row;
+  int c;
+  if (a.lanes_shift >= 0) {
+    row = g >> a.lanes_shift;
+    c = (int)(g & (a.lanes - 1));
+  } else {
+    row = g / a.lanes;
+    c = (int)(g - row * a.lanes);
+  }
+  const int64_t n = row / heads;
+  const int h = (int)(row - n * heads);
+  const int64_t b = n / a.seq_len;
+  const int64_t s = n - b * a.seq_len;
+  const T* in = view_row<T>(is_q ? a.q_in : a.k_in, h, b, s);
+  T* out = OOP ? view_row<T>(is_q ? a.q_out : a.k_out, h, b, s) : const_cast<T*>(in);
+  rotate_one_chunk<T, V, PAIR, ALIGNED, OOP, SRC, IDX>(a, in, out, b, s, c);
+}
+
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP>
+ROPE_HD void flat_entry(const Args& a, int64_t block, int thread) {
+  if (a.angles)
+    flat_body<T, V, PAIR, ALIGNED, OOP, kTrigTheta, true>(a, block, thread);
+  else if (!a.t_vec)
+    flat_body<T, V, PAIR, ALIGNED, OOP, kTrigScalar, true>(a, block, thread);
+  else if (a.pos)
+    flat_body<T, V, PAIR, ALIGNED, OOP, kTrigVec, true>(a, block, thread);
+  else
+    flat_body<T, V, PAIR, ALIGNED, OOP, kTrigVec, false>(a, block, thread);
+}
+
+template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, bool IDX>
+__global__ void __launch_bounds__(kFlatBlock) rope_flat_kernel(Args a) {
+  flat_body<T, V, PAIR, ALIGNED, OOP, kTrigVec, IDX>(a, blockIdx.x, threadIdx.x);
 }
 
 // ------------------------------------------------------------- token shape

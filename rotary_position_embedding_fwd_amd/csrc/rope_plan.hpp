@@ -30,6 +30,8 @@ struct Plan {
   bool single;     // token shape: the grid covers every token, no loops
   bool oop;        // some output differs from its input
   bool pair;       // rows shape, one chunk per lane (rope_pair_lanes_kernel)
+  bool head_lanes; // rows shape, one (token, head) chunk per lane (rope_head_lanes_kernel)
+  bool flat;       // token shape, items over the whole call (rope_flat_kernel)
   int64_t lds_bytes;  // dynamic shared memory per workgroup
 
   // token shape: which rope_token_kernel instantiation runs the plan
@@ -330,6 +332,21 @@ inline View to_view(const rope_view_t& v) {
   return View{static_cast<char*>(v.data), v.stride_b, v.stride_h, v.stride_s};
 }
 
+// Q and K views ([B,S,H,D] order) whose rows are dense: heads adjacent,
+// tokens adjacent, batches adjacent.
+inline bool dense_token_major(const rope_apply_desc_t* d) {
+  const int64_t D = d->head_dim, S = d->seq_len;
+  const rope_view_t* views[2] = {&d->q_in, &d->k_in};
+  const int64_t heads[2] = {d->n_heads_q, d->n_heads_k};
+  for (int i = 0; i < 2; ++i) {
+    if (heads[i] == 0) continue;
+    const rope_view_t& v = *views[i];
+    if (v.stride_h != D || v.stride_s != heads[i] * D) return false;
+    if (d->batch > 1 && v.stride_b != S * v.stride_s) return false;
+  }
+  return true;
+}
+
 // Validate and plan one call. `cus` is the device's compute-unit count.
 inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* pl) {
   const rope_status_t vs = validate_apply(d);
@@ -439,6 +456,23 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
     pl->grid = blocks < max_grid ? blocks : max_grid;
     pl->single = pl->grid == blocks && pl->block >= lanes_needed;
     if (a.angles && pl->single) pl->lds_bytes = theta_shared_bytes(tpb, a.half);
+    // Flat shape for dense token-major calls of many tokens: items numbered
+    // over the whole call, so the grid streams Q and then K in memory order.
+    // Measured on MI355X with interleaved pairs, [8,2048,16+16,64] fp16 in
+    // place: 22.9 us against 23.8 us for the token kernel (one token per
+    // workgroup). Split-half calls keep the token kernel (not measured here).
+    const int64_t flat_items = a.n_tokens * per_token;
+    if (d->launch == ROPE_LAUNCH_AUTO && d->seq_len > 1 && !pl->oop && !a.angles && a.t_vec &&
+        d->pairing == ROPE_INTERLEAVED && pl->aligned && dense_token_major(d) &&
+        flat_items / kFlatBlock < ((int64_t)1 << 30)) {
+      pl->flat = true;
+      pl->single = false;
+      a.tokens_per_block = 1;
+      a.n_items_q = a.n_tokens * (int64_t)a.n_heads_q * a.lanes;
+      a.n_items = flat_items;
+      pl->block = kFlatBlock;
+      pl->grid = (flat_items + kFlatBlock - 1) / kFlatBlock;
+    }
   } else {
     // Head groups, walked in group-slow order (all tiles of group 0, then of
     // group 1, ...): on MI355X this streams HBM best when a lane walks 4 heads
@@ -470,6 +504,49 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
     // groups, 600 us against 472 us; angles from theta, where both lanes of
     // a pair would evaluate the same sin/cos, 73.3 us against 58.3 us.
     // Lanes then count both halves' chunks: twice the items.
+    // Head lanes (rope_head_lanes_kernel): split-half pairs in 16-byte
+    // chunks, in place, cos/sin from [rows, R/2]-style tables, at least 8
+    // heads. Each lane rotates one chunk of one (token, head) and nothing is
+    // looped; the workgroup's token and head counts come from the distance
+    // between consecutive heads' rows, measured on MI355X with bf16
+    // [B, 32+8, S, 128] calls of 2.7 GB (fwd/bwd in place, cold):
+    //   heads <= 2 MiB apart (S <= 4096): 64 lanes of consecutive tokens per
+    //     head, 8 heads per workgroup. Llama [4,32+8,4096,128]: 53.0-54.3 us
+    //     against 54.8-55.6 us for the one-chunk-per-lane rows kernel.
+    //   heads >= 16 MiB apart (S >= 65536): 32 lanes per head, 20 heads.
+    //     [1,32+8,131072,128]: 430 us against 470-479 us; [2,..,65536,..]:
+    //     449 us against 587-591 us.
+    //   in between (S = 16384, 32768) the rows kernels measured as fast or
+    //     faster (467-471 us against 475-505 us), so they stay.
+    const int64_t head_gap = d->q_in.stride_h * elem_bytes(d->dtype);
+    int hl_span = 0, hl_heads = 0;
+    if (head_gap <= ((int64_t)2 << 20)) {
+      hl_span = 64;
+      hl_heads = 8;
+    } else if (head_gap >= ((int64_t)16 << 20)) {
+      hl_span = 32;
+      hl_heads = 20;
+    }
+    pl->head_lanes = d->launch == ROPE_LAUNCH_AUTO && hl_span > 0 &&
+                     d->pairing == ROPE_SPLIT_HALF && !pl->oop && pl->aligned && !a.angles &&
+                     a.t_vec && (int64_t)v * elem_bytes(d->dtype) == 16 && a.lanes_shift >= 0 &&
+                     a.lanes <= hl_span && h_total >= 8;
+    if (pl->head_lanes) {
+      int tshift = 0;
+      while ((a.lanes << (tshift + 1)) <= hl_span) ++tshift;
+      const int hpg = hl_heads < h_total ? hl_heads : h_total;
+      a.tokens_per_block = 1 << tshift;
+      a.tokens_shift = tshift;
+      a.heads_per_group = hpg;
+      a.n_groups = (h_total + hpg - 1) / hpg;
+      a.n_tiles = (a.n_tokens + a.tokens_per_block - 1) / a.tokens_per_block;
+      a.group_slow = 1;
+      const int64_t n_wg = a.n_tiles * a.n_groups;
+      if (n_wg > 0x7fffffff) return ROPE_ERR_SHAPE;
+      pl->grid = n_wg;
+      pl->block = (a.lanes << tshift) * hpg;
+      return ROPE_OK;
+    }
     pl->pair = d->pairing == ROPE_SPLIT_HALF && !pl->oop && pl->aligned && !a.angles &&
                (int64_t)v * elem_bytes(d->dtype) == 16 && a.lanes_shift >= 0 &&
                a.lanes <= kPairLanesMax && g <= 4;

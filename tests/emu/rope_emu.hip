@@ -151,6 +151,16 @@ struct HostRunner {
         return;
       }
     }
+    if (pl.head_lanes || pl.flat) {
+      for (int64_t blk = 0; blk < pl.grid; ++blk)
+        for (int t = 0; t < pl.block; ++t) {
+          if (pl.head_lanes)
+            rope::head_lanes_entry<T, V, PAIR, AL, OOP>(pl.a, blk, t);
+          else
+            rope::flat_entry<T, V, PAIR, AL, OOP>(pl.a, blk, t);
+        }
+      return;
+    }
     if (pl.token && pl.a.angles && pl.token_mode() != rope::kTokenLoop) {
       for (int64_t blk = 0; blk < pl.grid; ++blk) {
         if (pl.token_mode() == rope::kTokenOne)
@@ -189,11 +199,11 @@ struct HostRunner {
 void print_plan(const rope::Plan& pl) {
   printf("empty %d\ntoken %d\nvec %d\naligned %d\ngrid %lld\nblock %d\nlanes %d\n"
          "heads_per_group %d\nn_groups %d\ngroup_slow %d\nsingle %d\noop %d\nt_vec %d\n"
-         "tokens_per_block %d\nangles %d\nlds_bytes %lld\npair %d\n",
+         "tokens_per_block %d\nangles %d\nlds_bytes %lld\npair %d\nhead_lanes %d\nflat %d\n",
          (int)pl.empty, (int)pl.token, pl.vec, (int)pl.aligned, (long long)pl.grid, pl.block,
          pl.a.lanes, pl.a.heads_per_group, pl.a.n_groups, pl.a.group_slow, (int)pl.single,
          (int)pl.oop, pl.a.t_vec, pl.a.tokens_per_block, pl.a.angles,
-         (long long)pl.lds_bytes, (int)pl.pair);
+         (long long)pl.lds_bytes, (int)pl.pair, (int)pl.head_lanes, (int)pl.flat);
 }
 
 // test-only overrides of the rows-kernel grid (one chunk or a chunk pair per
@@ -207,6 +217,20 @@ void apply_overrides(rope::Plan& pl, std::map<std::string, long long>& kv) {
     pl.a.n_items = pl.a.n_tokens * pl.a.lanes;
     pl.a.n_tiles = (pl.a.n_items + rope::kRowsBlock - 1) / rope::kRowsBlock;
     pl.grid = pl.a.n_tiles * pl.a.n_groups;
+  }
+  if (!pl.empty && pl.head_lanes && (kv["heads_per_group"] > 0 || kv.count("hl_tshift"))) {
+    // the head-lanes grid with other token and head counts per workgroup
+    const int h_total = pl.a.n_heads_q + pl.a.n_heads_k;
+    if (kv.count("hl_tshift")) {
+      pl.a.tokens_shift = (int32_t)kv["hl_tshift"];
+      pl.a.tokens_per_block = 1 << pl.a.tokens_shift;
+      pl.a.n_tiles = (pl.a.n_tokens + pl.a.tokens_per_block - 1) / pl.a.tokens_per_block;
+    }
+    if (kv["heads_per_group"] > 0) pl.a.heads_per_group = (int32_t)kv["heads_per_group"];
+    pl.a.n_groups = (h_total + pl.a.heads_per_group - 1) / pl.a.heads_per_group;
+    pl.block = (pl.a.lanes << pl.a.tokens_shift) * pl.a.heads_per_group;
+    pl.grid = pl.a.n_tiles * pl.a.n_groups;
+    return;
   }
   if (!pl.empty && !pl.token && kv["heads_per_group"] > 0) {
     const int h_total = pl.a.n_heads_q + pl.a.n_heads_k;

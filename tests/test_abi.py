@@ -455,3 +455,75 @@ def test_attention_sizes_whose_byte_counts_overflow():
 ])
 def test_apply_extents_that_overflow_are_rejected(change):
     assert call_apply(apply_desc(**change)) == SHAPE
+
+
+# ----------------------------------------- the binding guards host pointers
+def _cpu_operands():
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    c = torch.zeros(8, 32)
+    return q, k, c
+
+
+def test_binding_rejects_host_tensors_before_any_library_call(monkeypatch):
+    """librope cannot tell a host pointer from a device pointer without
+    touching the GPU; every binding call must refuse host tensors itself,
+    before it reaches the C library (replaced here by one that fails the
+    test if called)."""
+    def no_call():
+        raise AssertionError("the C library was reached with host tensors")
+    monkeypatch.setattr(rp, "lib", no_call)
+    q, k, c = _cpu_operands()
+    pos = torch.zeros(8, dtype=torch.int32)
+    calls = [
+        lambda: rp.rope_fwd_qk(q, k, c, c),
+        lambda: rp.rope_bwd_qk(q, k, c, c),
+        lambda: rp.rope_fwd_q(q, c, c),
+        lambda: rp.rope_bwd_q(q, c, c, pos=pos),
+        lambda: rp.rope_apply(q, k, c, c),
+        lambda: rp.rope_apply(q, k, None, None, theta=1e4),
+        lambda: rp.rope_apply_xpos(q, k, c, c, c, c),
+        lambda: rp.prepare(q, k, c, c),
+        lambda: rp.prepare_apply(q, k, c, c),
+        lambda: rp.prepare_apply_xpos(q, k, c, c, c, c),
+        lambda: rp.rope_attention(q, k, k, c, c),
+        lambda: rp.prepare_attention(q, k, k, c, c, torch.empty_like(q)),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="on the GPU"):
+            call()
+
+
+def test_attention_descriptor_checks_its_tables():
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    o = torch.empty_like(q)
+    c = torch.zeros(8, 32)
+    d = rp.make_attn_desc(q, k, k, c, c, o)
+    assert d.rotary_dim == 64 and d.table_rows == 8
+    d = rp.make_attn_desc(q, k, k, c[:, :16].contiguous(), c[:, :16].contiguous(), o,
+                          rotary_dim=32)
+    assert d.rotary_dim == 32
+    bad = [
+        dict(cos=c.to(torch.bfloat16), sin=c.to(torch.bfloat16)),        # not float32
+        dict(cos=torch.zeros(8, 64)[:, ::2], sin=torch.zeros(8, 64)[:, ::2]),  # column slice
+        dict(cos=c, sin=c, rotary_dim=32),                                 # R/2 != columns
+        dict(cos=c, sin=torch.zeros(8, 16)),                               # sin unlike cos
+        dict(cos=c, sin=None),
+    ]
+    for b in bad:
+        kw = dict(b)
+        cos, sin = kw.pop("cos"), kw.pop("sin")
+        with pytest.raises(ValueError):
+            rp.make_attn_desc(q, k, k, cos, sin, o, **kw)
+
+
+def test_describe_validates_without_a_device():
+    L = rp.lib()
+    buf = ctypes.create_string_buffer(256)
+    assert L.rope_describe(A16, A16 * 3, ctypes.byref(good_desc()), 1, None, 256) == NULL
+    assert L.rope_describe(A16, A16 * 3, ctypes.byref(good_desc()), 1, buf, 0) == NULL
+    bad = good_desc()
+    bad.rotary_dim = 3
+    assert L.rope_describe(A16, A16 * 3, ctypes.byref(bad), 1, buf, 256) == SHAPE
+    assert buf.value == b""

@@ -617,3 +617,43 @@ def test_theta_packed_qkv_in_place():
     _check_view(w, gc[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D), k, 1, None, what="k")
     assert torch.equal(gc[..., (Hq + Hk) * D:].view(torch.int16),
                        qkv[..., (Hq + Hk) * D:].view(torch.int16))
+
+
+# ------------------------------------------- head-lanes and flat launch shapes
+
+@pytest.mark.parametrize("direction", [1, -1])
+@pytest.mark.parametrize("spec", [
+    dict(batch=2, seq_len=512, table_rows=512),                          # 40 heads: 8 + .. + 8
+    dict(batch=1, seq_len=1500, table_rows=1500, n_heads_q=9, n_heads_k=3),  # groups 8 + 4
+    dict(batch=3, seq_len=333, table_rows=333, head_dim=256, rotary_dim=256, dtype="f16"),
+])
+def test_head_lanes_equal_rows_kernels_and_oracle(spec, direction):
+    """[B,H,S,D] split-half calls that the planner gives to the head-lanes
+    kernel (one chunk of one (token, head) per lane): every element against
+    the oracle, and bit for bit against the rows kernels of the same call."""
+    w = W.LLAMA_GQA_PREFILL.scaled(**spec)
+    say(f"[gpu] head lanes q{tuple(w.q_shape)} k{tuple(w.k_shape)} {w.dtype} dir={direction}")
+    check_full(w, direction)
+    t = W.tensors(w)
+    a = run_qk(w, t["q"], t["k"], direction)
+    b = run_qk(w, t["q"], t["k"], direction, launch="rows")
+    assert np.array_equal(_bits(a[0]), _bits(b[0])) and np.array_equal(_bits(a[1]), _bits(b[1]))
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+@pytest.mark.parametrize("spec", [
+    dict(batch=2, seq_len=333, table_rows=333),
+    dict(batch=1, seq_len=700, table_rows=700, n_heads_q=12, n_heads_k=4, dtype="bf16",
+         rotary_dim=48),
+])
+def test_flat_equals_token_kernel_and_oracle(spec, direction):
+    """Dense [B,S,H,D] interleaved calls run the flat kernel (one item per
+    lane over the whole call): every element against the oracle, and bit for
+    bit against the token kernel of the same call."""
+    w = W.BSHD_INTERLEAVED.scaled(**spec)
+    say(f"[gpu] flat q{tuple(w.q_shape)} {w.dtype} R={w.rotary_dim} dir={direction}")
+    check_full(w, direction)
+    t = W.tensors(w)
+    a = run_qk(w, t["q"], t["k"], direction)
+    b = run_qk(w, t["q"], t["k"], direction, launch="token")
+    assert np.array_equal(_bits(a[0]), _bits(b[0])) and np.array_equal(_bits(a[1]), _bits(b[1]))

@@ -153,6 +153,8 @@ def test_auto_shape_selection(emu):
     assert check(emu, SMALL["decode"], cus=1)["token"] == 1
     assert check(emu, SMALL["llama_ragged"])["token"] == 1  # 154 tokens on 256 CUs
     plan = check(emu, SMALL["llama_ragged"], cus=1)  # same tokens, a 1-CU device
+    assert plan["token"] == 0 and plan["group_slow"] == 1 and plan["head_lanes"] == 1
+    plan = check(emu, SMALL["llama_ragged"], launch="rows", cus=1)
     assert plan["token"] == 0 and plan["group_slow"] == 1 and plan["heads_per_group"] == 4
     # the same tokens as [B,S,H,D]: token shape on any device
     assert check(emu, SMALL["llama_ragged"].scaled(layout="bshd"), cus=1)["token"] == 1
@@ -816,15 +818,28 @@ def plan_of(emu, w, launch="auto", cus=256):
 
 
 def test_full_size_plans(emu):
-    # Llama prefill: rows shape, 4-head groups, one chunk per lane (16 lanes
-    # per token); long context: 8-head groups (its cos/sin table is re-read
-    # per group), a chunk pair per lane
+    # Llama prefill (heads 1 MiB apart): head lanes, 8 tokens x 8 heads per
+    # workgroup; long context (heads 32 MiB apart): 4 tokens x 20 heads
     p = plan_of(emu, W.LLAMA_GQA_PREFILL)
-    assert (p["token"], p["heads_per_group"], p["pair"], p["lanes"]) == (0, 4, 1, 16), p
+    assert (p["token"], p["head_lanes"], p["tokens_per_block"], p["heads_per_group"],
+            p["block"], p["grid"]) == (0, 1, 8, 8, 512, 2048 * 5), p
     p = plan_of(emu, W.LONG_CONTEXT)
+    assert (p["token"], p["head_lanes"], p["tokens_per_block"], p["heads_per_group"],
+            p["block"], p["grid"]) == (0, 1, 4, 20, 640, 32768 * 2), p
+    # an explicit rows launch keeps the rows kernels: one chunk per lane in
+    # 4-head groups at Llama prefill, chunk pairs in 8-head groups at long
+    # context (its cos/sin table is re-read per group)
+    p = plan_of(emu, W.LLAMA_GQA_PREFILL, launch="rows")
+    assert (p["token"], p["heads_per_group"], p["pair"], p["lanes"]) == (0, 4, 1, 16), p
+    p = plan_of(emu, W.LONG_CONTEXT, launch="rows")
     assert (p["token"], p["heads_per_group"], p["pair"], p["lanes"]) == (0, 8, 0, 8), p
+    # heads 4 and 8 MiB apart: the rows kernels
+    for S in (16384, 32768):
+        p = plan_of(emu, W.LONG_CONTEXT.scaled(batch=131072 // S, seq_len=S, table_rows=S))
+        assert (p["token"], p["head_lanes"]) == (0, 0), p
     assert plan_of(emu, W.DECODE)["token"] == 1
-    assert plan_of(emu, W.BSHD_INTERLEAVED)["token"] == 1
+    p = plan_of(emu, W.BSHD_INTERLEAVED)
+    assert (p["token"], p["flat"], p["block"], p["grid"]) == (1, 1, 64, 8 * 2048 * 32 * 8 // 64), p
 
 
 def test_theta_angles_keep_chunk_pairs(emu):
@@ -833,3 +848,103 @@ def test_theta_angles_keep_chunk_pairs(emu):
     w = W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=40, table_rows=40)
     plan = _theta_case(emu, w, launch="rows")
     assert plan["pair"] == 0 and plan["lanes"] == 8, plan
+
+
+# -------------------------------------------------------- head-lanes shape
+# [B,H,S,D] split-half calls in 16-byte chunks, in place, with tables: one
+# chunk of one (token, head) per lane, tokens_per_block x lanes x
+# heads_per_group lanes per workgroup. Each case must equal the oracle and,
+# bit for bit, the rows kernels of the same call (launch="rows").
+HEAD_LANES_CASES = {
+    # name: workload, expected (tokens_per_block, heads_per_group)
+    "llama_ragged": (W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=77, table_rows=80), (8, 8)),
+    "heads_not_a_multiple": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=21, table_rows=21,
+                                                        n_heads_q=9, n_heads_k=3), (8, 8)),
+    "partial_indexed_skips": (W.PARTIAL_INDEXED.scaled(seq_len=130, pos_start_max=9000),
+                              (32, 8)),
+    "f16_R256": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=19, head_dim=256, rotary_dim=256,
+                                            dtype="f16", table_rows=19, n_heads_q=6,
+                                            n_heads_k=2), (4, 8)),
+    "f32_R128": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=23, dtype="f32", table_rows=23,
+                                            n_heads_q=8, n_heads_k=1), (4, 8)),
+}
+
+
+@pytest.mark.parametrize("name", list(HEAD_LANES_CASES))
+@pytest.mark.parametrize("direction", [1, -1])
+def test_head_lanes_match_oracle_and_rows(emu, name, direction):
+    w, (tpb, hpg) = HEAD_LANES_CASES[name]
+    plan = check(emu, w, direction, cus=1,
+                 expect=dict(token=0, head_lanes=1, tokens_per_block=tpb, heads_per_group=hpg))
+    q, k, wpos, cos, sin = _inputs(w)
+    _, q1, k1 = run_emu(emu, w, q, k, cos, sin, wpos, direction, "auto", cus=1)
+    plan0, q0, k0 = run_emu(emu, w, q, k, cos, sin, wpos, direction, "rows", cus=1)
+    assert plan0["head_lanes"] == 0
+    assert np.array_equal(q1, q0) and np.array_equal(k1, k0)
+    assert plan["block"] == plan["lanes"] * tpb * hpg
+
+
+@pytest.mark.parametrize("tshift,heads", [(2, 20), (0, 1), (5, 3), (1, 40)])
+def test_head_lanes_any_token_and_head_counts(emu, tshift, heads):
+    """The long-sequence form (4 tokens x 20 heads) and other counts cover
+    every row once, with ragged token tiles and head groups."""
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=37, table_rows=40, n_heads_q=16,
+                                   n_heads_k=8)
+    check(emu, w, -1, cus=1, expect=dict(head_lanes=1, heads_per_group=heads,
+                                         tokens_per_block=1 << tshift),
+          overrides=dict(hl_tshift=tshift, heads_per_group=heads))
+
+
+def test_head_lanes_only_where_they_apply(emu):
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=40, table_rows=40)
+    assert check(emu, w, cus=1)["head_lanes"] == 1
+    # explicit rows or token launch, interleaved pairs, 8-byte chunks, fewer
+    # than 8 heads, angles from theta: not this shape
+    assert check(emu, w, launch="rows", cus=1)["head_lanes"] == 0
+    assert check(emu, w, launch="token", cus=1)["head_lanes"] == 0
+    assert check(emu, w.scaled(pairing=W.INTERLEAVED), cus=1)["head_lanes"] == 0
+    assert check(emu, w, q_offset=4, cus=1)["head_lanes"] == 0
+    assert check(emu, w.scaled(n_heads_q=5, n_heads_k=2), cus=1)["head_lanes"] == 0
+    assert _theta_case(emu, w, cus=1)["head_lanes"] == 0
+
+
+# -------------------------------------------------------------- flat shape
+FLAT_CASES = {
+    "bshd_interleaved_ragged": W.BSHD_INTERLEAVED.scaled(batch=3, seq_len=45, table_rows=45),
+    "q_heads_differ": W.BSHD_INTERLEAVED.scaled(batch=2, seq_len=13, table_rows=13,
+                                                n_heads_q=12, n_heads_k=4),
+    "partial_rotary_bf16": W.BSHD_INTERLEAVED.scaled(batch=2, seq_len=17, table_rows=17,
+                                                     dtype="bf16", rotary_dim=48),
+    "f32_odd_lanes": W.BSHD_INTERLEAVED.scaled(batch=1, seq_len=29, table_rows=29,
+                                               dtype="f32", head_dim=24, rotary_dim=24),
+    "skipped_tokens": W.PARTIAL_INDEXED.scaled(seq_len=70, pos_start_max=9000, layout="bshd",
+                                               pairing="interleaved"),
+}
+
+
+@pytest.mark.parametrize("name", list(FLAT_CASES))
+@pytest.mark.parametrize("direction", [1, -1])
+def test_flat_matches_oracle_and_token_kernel(emu, name, direction):
+    w = FLAT_CASES[name]
+    plan = check(emu, w, direction, expect=dict(token=1, flat=1, block=64))
+    q, k, wpos, cos, sin = _inputs(w)
+    _, q1, k1 = run_emu(emu, w, q, k, cos, sin, wpos, direction, "auto")
+    plan0, q0, k0 = run_emu(emu, w, q, k, cos, sin, wpos, direction, "token")
+    assert plan0["flat"] == 0
+    assert np.array_equal(q1, q0) and np.array_equal(k1, k0)
+    assert plan["grid"] * 64 >= (w.n_heads_q + w.n_heads_k) * w.batch * w.seq_len
+
+
+def test_flat_q_only_and_misaligned(emu):
+    w = FLAT_CASES["bshd_interleaved_ragged"]
+    assert check(emu, w, with_k=False)["flat"] == 1
+    # 4-byte aligned base: 2-element chunks, still flat
+    assert check(emu, w, q_offset=2, expect=dict(vec=2))["flat"] == 1
+
+
+def test_flat_only_where_it_applies(emu):
+    w = FLAT_CASES["bshd_interleaved_ragged"]
+    assert check(emu, w.scaled(pairing=W.SPLIT_HALF))["flat"] == 0
+    assert check(emu, w.scaled(seq_len=1, table_rows=1))["flat"] == 0
+    assert check(emu, w.scaled(layout="bhsd"))["flat"] == 0
+    assert check(emu, w, launch="token")["flat"] == 0
