@@ -347,6 +347,22 @@ rope_status_t rope_attention_fwd(const rope_attn_desc_t *d, void *stream);
 rope_status_t rope_attention_fwd_k_once(const rope_attn_desc_t *d, void *k_workspace,
                                         void *stream);
 
+/* rope_attention_fwd_k_once without a caller workspace, for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): rope(K) is staged in a device array the
+ * library holds, 64 MiB per device (K of up to 32 Mi bf16 values, e.g.
+ * [4, 8, 8192, 128]), set aside when the library's code is loaded on a device
+ * and kept until the process ends. This call allocates nothing.
+ * Same descriptor, result (bit for bit) and errors as
+ * rope_attention_fwd_k_once, plus ROPE_ERR_SHAPE when B * Hk * Sk * D bf16
+ * values exceed 64 MiB, and ROPE_ERR_HIP when the array's address cannot be
+ * obtained. Every call on one device uses the same array: calls that overlap
+ * on one device (different streams, or different host threads, with no
+ * ordering between them) race and give wrong results; calls ordered on one
+ * stream do not. The array keeps the last call's rope(K); each call writes
+ * all of the part it reads before reading it. */
+rope_status_t rope_attention_fwd_k_once_noalloc(const rope_attn_desc_t *d, void *stream);
+
 /* Fill host float32 tables cos_out/sin_out, each [table_rows, R/2] row-major,
  * with cos and sin of (p / interpolate_factor) * theta^(-2i/R) for row p and
  * column i: the exponent -2i/R, the scaled position and the angle are formed

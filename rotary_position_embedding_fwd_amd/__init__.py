@@ -144,6 +144,8 @@ def lib():
         L.rope_attention_fwd.argtypes = [ctypes.POINTER(RopeAttnDesc), P]
         L.rope_attention_fwd_k_once.argtypes = [ctypes.POINTER(RopeAttnDesc), P, P]
         L.rope_attention_fwd_k_once.restype = ctypes.c_int
+        L.rope_attention_fwd_k_once_noalloc.argtypes = [ctypes.POINTER(RopeAttnDesc), P]
+        L.rope_attention_fwd_k_once_noalloc.restype = ctypes.c_int
         L.rope_attention_fwd.restype = ctypes.c_int
         L.rope_describe.argtypes = [P, P, D, ctypes.c_int, ctypes.c_char_p, ctypes.c_int64]
         L.rope_describe.restype = ctypes.c_int
@@ -664,6 +666,19 @@ def rope_attention(q, k, v, cos, sin, *, o=None, stream=None, k_workspace=None, 
     else:
         _check(lib().rope_attention_fwd_k_once(ctypes.byref(d), ws, _stream(stream)),
                "rope_attention_fwd_k_once")
+    return o
+
+
+def rope_attention_noalloc(q, k, v, cos, sin, o, *, stream=None, **kw):
+    """rope_attention with K rotated once into the library's own device array
+    (rope_attention_fwd_k_once_noalloc): the same result as passing a
+    k_workspace, for callers that cannot allocate. o must be given (nothing
+    is allocated here either). Calls that overlap on one device race."""
+    _on_one_device("rope_attention_noalloc", q, k, v, cos, sin, o, kw.get("q_pos"),
+                   kw.get("k_pos"))
+    d = make_attn_desc(q, k, v, cos, sin, o, **kw)
+    _check(lib().rope_attention_fwd_k_once_noalloc(ctypes.byref(d), _stream(stream)),
+           "rope_attention_fwd_k_once_noalloc")
     return o
 
 

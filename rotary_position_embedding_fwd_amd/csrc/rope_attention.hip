@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "librope.h"
 #include "rope_attn_plan.hpp"
 
@@ -72,6 +74,31 @@ hipError_t launch_attention_d(const rope::attn::AttnPlan& pl, hipStream_t st) {
     }
   }
   return hipErrorInvalidValue;  // unreachable: the plan bounds h16 by D / 32
+}
+
+// ------------------------------------------- allocation-free K-once call
+// rope_attention_fwd_k_once_noalloc stages rope(K) in this file-scope device
+// array instead of a caller buffer. Each device that loads the library holds
+// its own copy (kNoAllocKBytes) until the process ends. Host code never uses
+// the array's name as an address: the address of each device's copy is looked
+// up once per device with hipGetSymbolAddress and kept below.
+constexpr int64_t kNoAllocKBytes = (int64_t)64 << 20;  // rope(K) of up to 32 Mi bf16 values
+static __device__ __align__(256) unsigned char scratch[kNoAllocKBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+
+// The address of `scratch` on device `dev`, which must be the current device;
+// nullptr if the runtime cannot give it. Two threads that race here both store
+// the same address.
+void* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_scratch[dev].store(q, std::memory_order_release);
+  return q;
 }
 
 }  // namespace
@@ -153,4 +180,23 @@ extern "C" rope_status_t rope_attention_fwd_k_once(const rope_attn_desc_t* d, vo
   da.k = k_workspace;
   da.k_rotated = 1;
   return rope_attention_fwd(&da, stream);
+}
+
+extern "C" rope_status_t rope_attention_fwd_k_once_noalloc(const rope_attn_desc_t* d,
+                                                           void* stream) {
+  if (!d) return ROPE_ERR_NULL;
+  if (d->k_rotated) return ROPE_ERR_SHAPE;  // this call rotates K itself
+  rope::attn::AttnPlan pl;
+  const rope_status_t st = rope::attn::make_attn_plan(d, &pl);
+  if (st != ROPE_OK || pl.empty) return st;
+  const bool rotate = d->rotate && d->rotary_dim > 0;
+  if (!rotate || d->seq_len_k == 0) return rope_attention_fwd(d, stream);  // no K to rotate
+  // the plan has checked that the extents fit in int64
+  const int64_t kbytes = d->batch * d->n_heads_k * d->seq_len_k * d->head_dim * 2;
+  if (kbytes > kNoAllocKBytes) return ROPE_ERR_SHAPE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ROPE_ERR_HIP;
+  void* ws = device_scratch(dev);
+  if (!ws) return ROPE_ERR_HIP;
+  return rope_attention_fwd_k_once(d, ws, stream);
 }

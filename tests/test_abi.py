@@ -488,6 +488,7 @@ def test_binding_rejects_host_tensors_before_any_library_call(monkeypatch):
         lambda: rp.prepare_apply_xpos(q, k, c, c, c, c),
         lambda: rp.rope_attention(q, k, k, c, c),
         lambda: rp.prepare_attention(q, k, k, c, c, torch.empty_like(q)),
+        lambda: rp.rope_attention_noalloc(q, k, k, c, c, torch.empty_like(q)),
     ]
     for call in calls:
         with pytest.raises(ValueError, match="on the GPU"):
@@ -527,3 +528,19 @@ def test_describe_validates_without_a_device():
     bad.rotary_dim = 3
     assert L.rope_describe(A16, A16 * 3, ctypes.byref(bad), 1, buf, 256) == SHAPE
     assert buf.value == b""
+
+
+def test_no_alloc_attention_rejects_k_beyond_its_array():
+    """rope_attention_fwd_k_once_noalloc stages rope(K) in a 64 MiB device
+    array: a larger K is ROPE_ERR_SHAPE, found on the host before any HIP
+    call; a K that fits passes validation (and then needs a device)."""
+    L = rp.lib()
+    far = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, cos=5 << 40, sin=6 << 40)
+    # K = 2 * 2 * 65537 * 128 bf16 values: 2 KiB more than 64 MiB
+    big = attn_desc(seq_len_q=65537, seq_len_k=65537, table_rows=65537, **far)
+    assert L.rope_attention_fwd_k_once_noalloc(ctypes.byref(big), None) == SHAPE
+    fits = attn_desc(seq_len_q=65536, seq_len_k=65536, table_rows=65536, **far)
+    assert L.rope_attention_fwd_k_once_noalloc(ctypes.byref(fits), None) == HIP
+    assert L.rope_attention_fwd_k_once_noalloc(None, None) == NULL
+    assert L.rope_attention_fwd_k_once_noalloc(ctypes.byref(attn_desc(k_rotated=1)),
+                                                None) == SHAPE
