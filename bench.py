@@ -819,10 +819,18 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_json: str, out: str = TR
             with open(p) as f:
                 for r in csv.DictReader(f):
                     if r.get("Counter_Name") == counter:
-                        rows.append((r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0),
+                        rows.append((int(r.get("Dispatch_Id", 0) or 0), r["Kernel_Name"],
+                                     int(r.get("Grid_Size", 0) or 0),
                                      int(r.get("Workgroup_Size", 0) or 0),
                                      float(r["Counter_Value"])))
-        return rows
+        rows.sort()
+        return [r[1:] for r in rows]
+
+    def calibration(rows, reps=3):
+        # the bench's own device-to-device clones run the same copy kernel;
+        # the calibration copies are the last `reps` of them
+        vals = [v for n, g, wg, v in rows if "copyBuffer" in n][-reps:]
+        return sum(vals) / len(vals) if len(vals) == reps else None
 
     def pick(rows, name, grid=None, block=None):
         vals = [v for n, g, wg, v in rows
@@ -833,8 +841,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, bench_json: str, out: str = TR
         b = json.loads([ln for ln in f if ln.startswith("{")][-1])
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
     copy_bytes = 1 << 30
-    f_c, _ = pick(fetch, "copyBuffer")  # the runtime's device-to-device copy
-    w_c, _ = pick(write, "copyBuffer")
+    f_c = calibration(fetch)  # the runtime's device-to-device copy
+    w_c = calibration(write)
     res = {"copy_bytes": copy_bytes, "copy_fetch_kib": f_c, "copy_write_kib": w_c,
            "workloads": {}}
     if f_c and w_c:
@@ -909,12 +917,14 @@ def summarize_trace(trace_dir: str, bench_json: str):
         idx = [i for i, (name, wg, grid, _) in enumerate(rows)
                if i not in used and k["name"] in name and wg == k.get("block") and
                grid == items]
-        skip, take = 2 * e["warmup"], 2 * e["steps"]
-        timed = idx[skip:skip + take]
-        used.update(idx[:skip + take])
+        # the settle phase and the warmup come first; the timed launches are
+        # the last 2 * steps dispatches of this kernel and grid
+        take = 2 * e["steps"]
+        timed = idx[-take:] if len(idx) >= take else []
+        used.update(idx)
         res = {"workload": e["workload"], "kernel": k["name"], "grid": k.get("grid"),
                "block": k.get("block"), "dispatches_found": len(idx),
-               "warmup_dropped": min(skip, len(idx)),
+               "settle_and_warmup_dropped": max(0, len(idx) - take),
                "bench_event_avg_launch_us": e["bench_us"]}
         if timed:
             st = _stats_us([rows[i][3] for i in timed])

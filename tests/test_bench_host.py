@@ -61,13 +61,16 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
 
     fd, wd = tmp_path / "f", tmp_path / "w"
     # two launches of the Llama grid (10 x 512), one of the long-context grid (20 x 640)
-    write(fd, "FETCH_SIZE", [(kern, 5120, 512, 100.0), (kern, 5120, 512, 102.0),
-                             (kern, 12800, 640, 700.0),
-                             ("__amd_rocclr_copyBuffer", 1, 1, 524288.0),
-                             ("void at::native::vectorized_elementwise_kernel", 1, 1, 1.0)])
-    write(wd, "WRITE_SIZE", [(kern, 5120, 512, 200.0), (kern, 5120, 512, 200.0),
-                             (kern, 12800, 640, 900.0),
-                             ("__amd_rocclr_copyBuffer", 1, 1, 1048576.0)])
+    cp = "__amd_rocclr_copyBuffer"
+    # a device clone (the bench's own) before the launches, then the three
+    # calibration copies of 1 GiB at the end
+    write(fd, "FETCH_SIZE", [(cp, 1, 1, 1000.0), (kern, 5120, 512, 100.0),
+                             (kern, 5120, 512, 102.0), (kern, 12800, 640, 700.0),
+                             ("void at::native::vectorized_elementwise_kernel", 1, 1, 1.0)] +
+          [(cp, 1, 1, 524288.0)] * 3)
+    write(wd, "WRITE_SIZE", [(cp, 1, 1, 2000.0), (kern, 5120, 512, 200.0),
+                             (kern, 5120, 512, 200.0), (kern, 12800, 640, 900.0)] +
+          [(cp, 1, 1, 1048576.0)] * 3)
     bj = tmp_path / "b.json"
     bj.write_text("noise\n" + json.dumps(BENCH_LINE) + "\n")
     out = tmp_path / "t.json"
@@ -89,8 +92,8 @@ def test_trace_summary_drops_warmup_and_matches_grids(tmp_path):
     os.makedirs(d)
     kern = "void rope::rope_head_lanes_kernel<__bf16, 8, 0, true, false>(rope::Args)"
     rows = []
-    # Llama: 2 warmup steps (4 launches, slow) then 3 timed steps (6 launches)
-    rows += [(kern, 512, 5120, 9000)] * 4 + [(kern, 512, 5120, 1000)] * 6
+    # Llama: a settle phase and 2 warmup steps (slow), then 3 timed steps (6 launches)
+    rows += [(kern, 512, 5120, 9000)] * 11 + [(kern, 512, 5120, 1000)] * 6
     rows += [("stream_rmw_kernel", 64, 100, 5)]
     # long context: 1 warmup step then 2 timed steps
     rows += [(kern, 640, 12800, 9000)] * 2 + [(kern, 640, 12800, 2000)] * 4
@@ -110,8 +113,9 @@ def test_trace_summary_drops_warmup_and_matches_grids(tmp_path):
         bench.summarize_trace(str(tmp_path / "trace"), str(bj))
     res = json.loads(buf.getvalue())
     a, b = res["workloads"]
-    assert (a["launches"], a["mean_us"], a["max_us"], a["warmup_dropped"]) == (6, 1.0, 1.0, 4)
-    assert (b["launches"], b["mean_us"], b["warmup_dropped"]) == (4, 2.0, 2)
+    assert (a["launches"], a["mean_us"], a["max_us"], a["settle_and_warmup_dropped"]) == (
+        6, 1.0, 1.0, 11)
+    assert (b["launches"], b["mean_us"], b["settle_and_warmup_dropped"]) == (4, 2.0, 2)
 
 
 def test_more_than_one_gpu_is_refused():
