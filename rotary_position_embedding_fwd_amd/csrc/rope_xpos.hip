@@ -12,6 +12,11 @@ __global__ void __launch_bounds__(rope::xpos::kBlock)
   rope::xpos::xpos_block<T, V, PAIR, U>(a, blockIdx.x, (int)threadIdx.x);
 }
 
+template <typename T, int V, int PAIR, bool IDX, bool TOKEN>
+__global__ void __launch_bounds__(1024) rope_xpos_lanes_kernel(rope::xpos::XArgs a) {
+  rope::xpos::xpos_lanes<T, V, PAIR, IDX, TOKEN>(a, blockIdx.x, (int)threadIdx.x);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(rope::xpos::kBlock)
     rope_xpos_element_kernel(rope::xpos::XArgs a) {
@@ -25,6 +30,11 @@ struct Launcher {
   void chunked() {
     hipLaunchKernelGGL((rope_xpos_kernel<T, V, PAIR, U>), dim3((unsigned)pl.grid),
                        dim3(rope::xpos::kBlock), 0, st, pl.a);
+  }
+  template <typename T, int V, int PAIR, bool IDX, bool TOKEN>
+  void lanes() {
+    hipLaunchKernelGGL((rope_xpos_lanes_kernel<T, V, PAIR, IDX, TOKEN>),
+                       dim3((unsigned)pl.grid), dim3(pl.block), 0, st, pl.a);
   }
   template <typename T>
   void element() {

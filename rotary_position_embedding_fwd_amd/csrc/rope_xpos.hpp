@@ -66,6 +66,12 @@ struct XArgs {
   int32_t token_major;            // 1: lanes run token-slow (views with adjacent heads)
   int32_t t_vec;                  // 1: a chunk's table entries load as float4s
   int64_t n_items;                // lanes: head groups x tokens x row_items
+  // lanes shape
+  int32_t chunks_shift;           // log2(chunks)
+  int32_t tokens_per_block;       // head-major: tokens of a workgroup
+  int32_t tokens_shift;           // log2(tokens_per_block)
+  int32_t pad0;
+  int64_t n_tiles;                // head-major: token tiles per head group
 };
 
 // All items of one token that lane t of its workgroup owns.
@@ -255,12 +261,104 @@ ROPE_HD void xpos_block(const XArgs& a, int64_t blk, int t) {
   }
 }
 
+// ------------------------------------------------------------ lanes shape
+// One chunk of one (token, head) per lane and nothing looped: in place,
+// 16-byte chunks, [rows, R/2]-style tables (every table read a float4).
+//   head-major views (TOKEN false): the workgroups of rope_head_lanes_kernel,
+//     tokens_per_block tokens x chunks x heads_per_group heads, lanes chunk
+//     fastest, then token, then head; workgroups over the token tiles of head
+//     group 0 first. The heads of a group ask for the same cos/sin rows.
+//   token-major views (TOKEN true): one token per workgroup, lanes over
+//     (head, chunk), so a workgroup walks the token's adjacent rows.
+// A lane issues its row loads and its cos, sin and factor loads back to back;
+// whether the call has an index tensor (IDX) is a compile-time choice, so no
+// branch joins the two cases after the loads. A skipped token (IDX) asks for
+// table row 0 like the others and is not written.
+template <typename T, int V, int PAIR, bool IDX, bool TOKEN>
+ROPE_HD void xpos_lanes(const XArgs& a, int64_t blk, int t) {
+  constexpr int NP = PAIR == kSplitHalf ? V : V / 2;  // pairs per chunk
+  static_assert(NP % 4 == 0, "table entries move as float4s");
+  const int c = t & (a.chunks - 1);
+  const int rest = t >> a.chunks_shift;
+  const int h_total = a.n_heads_q + a.n_heads_k;
+  int64_t n;
+  int head;
+  if constexpr (TOKEN) {
+    n = blk;
+    head = rest;
+    if (head >= h_total) return;
+  } else {
+    const int tl = rest & (a.tokens_per_block - 1);
+    const int hl = rest >> a.tokens_shift;
+    const int64_t group = blk / a.n_tiles;
+    const int64_t tile = blk - group * a.n_tiles;
+    n = (tile << a.tokens_shift) + tl;
+    head = (int)group * a.heads_per_group + hl;
+    if (n >= a.n_tokens || hl >= a.heads_per_group || head >= h_total) return;
+  }
+  const int64_t b = n / a.seq_len, s = n - b * a.seq_len;
+  const bool is_k = head >= a.n_heads_q;
+  const int h = is_k ? head - a.n_heads_q : head;
+  const View& v = is_k ? a.k_in : a.q_in;
+  T* row = reinterpret_cast<T*>(v.base) + b * v.sb + h * v.sh + s * v.ss;
+  Chunk<T, V, true> x1, x2;  // split-half: both halves; interleaved: x1 only
+  if constexpr (PAIR == kSplitHalf) {
+    x1.load(row + c * V);
+    x2.load(row + a.half + c * V);
+  } else {
+    x1.load(row + c * V);
+  }
+  int64_t p = s;  // without an index the host has checked seq_len <= table_rows
+  if constexpr (IDX) {
+    if (a.table_rows == 0) return;  // uniform: every token is skipped
+    p = a.pos[b * a.pos_bs + s];
+    if (p >= a.table_rows) p = -1;
+  }
+  const int64_t base = (p < 0 ? 0 : p) * a.t_row + (int64_t)c * NP;
+  const float* zt = is_k ? a.zk : a.zq;
+  float cs[NP], sn[NP], z[NP];
+#pragma unroll
+  for (int j = 0; j < NP; j += 4) {
+    const float4 cv = *reinterpret_cast<const float4*>(a.cos + base + j);
+    const float4 sv = *reinterpret_cast<const float4*>(a.sin + base + j);
+    const float4 zv = *reinterpret_cast<const float4*>(zt + base + j);
+    cs[j] = cv.x; cs[j + 1] = cv.y; cs[j + 2] = cv.z; cs[j + 3] = cv.w;
+    sn[j] = sv.x; sn[j + 1] = sv.y; sn[j + 2] = sv.z; sn[j + 3] = sv.w;
+    z[j] = zv.x; z[j + 1] = zv.y; z[j + 2] = zv.z; z[j + 3] = zv.w;
+  }
+  if constexpr (IDX) {
+    if (p < 0) return;  // a skipped token: untouched in place
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    float y1, y2;
+    if constexpr (PAIR == kSplitHalf) {
+      rotate_pair(to_f32(x1.v[j]), to_f32(x2.v[j]), cs[j], a.sin_sign * sn[j], y1, y2);
+      x1.v[j] = from_f32<T>(y1 * z[j]);
+      x2.v[j] = from_f32<T>(y2 * z[j]);
+    } else {
+      rotate_pair(to_f32(x1.v[2 * j]), to_f32(x1.v[2 * j + 1]), cs[j], a.sin_sign * sn[j], y1,
+                  y2);
+      x1.v[2 * j] = from_f32<T>(y1 * z[j]);
+      x1.v[2 * j + 1] = from_f32<T>(y2 * z[j]);
+    }
+  }
+  if constexpr (PAIR == kSplitHalf) {
+    x1.store(row + c * V);
+    x2.store(row + a.half + c * V);
+  } else {
+    x1.store(row + c * V);
+  }
+}
+
 struct XPlan {
   XArgs a;
   bool empty;
   int dtype;
   int vec;         // chunk width V; 0: element shape
   int64_t grid;    // workgroups
+  int lanes;       // 0: chunked or element shape; 1: lanes, head-major; 2: lanes, token-major
+  int block;       // lanes per workgroup (lanes shape; the others use kBlock)
 };
 
 // Validate a rope_apply_xpos call and plan it. Never touches device memory.
@@ -343,6 +441,45 @@ inline rope_status_t make_xpos_plan(const rope_apply_desc_t* d, const float* zq,
                reinterpret_cast<uintptr_t>(zk) % 16 == 0) ? 1 : 0;
     pl->grid = (a.n_items + kBlock - 1) / kBlock;
     if (pl->grid > 0x7fffffff) return ROPE_ERR_SHAPE;
+    // The lanes shape (xpos_lanes) where it applies: in place, 16-byte
+    // chunks, a power-of-two number of chunks per row, table entries as
+    // float4s. Head-major views take the rope_head_lanes_kernel rule on the
+    // distance between heads (measured there; in between the rule leaves
+    // them to the chunked shape); token-major views one token per workgroup.
+    int cshift = -1;
+    for (int sh = 0; sh < 11; ++sh)
+      if ((1 << sh) == a.chunks) cshift = sh;
+    const int64_t head_gap = d->q_in.stride_h * elem_bytes(d->dtype);
+    if (!oop && a.t_vec && (int64_t)v * elem_bytes(d->dtype) == 16 && cshift >= 0) {
+      a.chunks_shift = cshift;
+      if (a.token_major) {
+        const int64_t lanes = ((h_total << cshift) + 63) / 64 * 64;
+        if (lanes <= 1024) {
+          pl->lanes = 2;
+          pl->block = (int)lanes;
+          pl->grid = a.n_tokens;
+        }
+      } else if (h_total >= 8 && (head_gap <= ((int64_t)2 << 20) ||
+                                  head_gap >= ((int64_t)16 << 20))) {
+        const int span = head_gap <= ((int64_t)2 << 20) ? 64 : 32;
+        const int hpg = (int)(h_total < (span == 64 ? 8 : 20) ? h_total : (span == 64 ? 8 : 20));
+        if (a.chunks <= span) {
+          int tshift = 0;
+          while ((a.chunks << (tshift + 1)) <= span) ++tshift;
+          a.tokens_per_block = 1 << tshift;
+          a.tokens_shift = tshift;
+          a.heads_per_group = hpg;
+          a.n_groups = (int32_t)((h_total + hpg - 1) / hpg);
+          a.n_tiles = (a.n_tokens + a.tokens_per_block - 1) / a.tokens_per_block;
+          const int64_t n_wg = a.n_tiles * a.n_groups;
+          if (n_wg <= 0x7fffffff) {
+            pl->lanes = 1;
+            pl->block = (a.chunks << tshift) * hpg;
+            pl->grid = n_wg;
+          }
+        }
+      }
+    }
   } else {
     pl->vec = 0;
     pl->grid = a.n_tokens;
@@ -415,8 +552,39 @@ bool dispatch_vec(const XPlan& pl, F& f) {
   return false;
 }
 
+// The lanes shape: split-half V = 16 / sizeof(T), or interleaved with V / 2 a
+// multiple of 4 (8 16-bit elements).
+template <typename T, class F>
+bool dispatch_lanes(const XPlan& pl, F& f) {
+  constexpr int V = 16 / (int)sizeof(T);
+  const bool idx = pl.a.pos != nullptr, tok = pl.lanes == 2;
+  if (!pl.a.interleaved) {
+    if (idx) tok ? f.template lanes<T, V, kSplitHalf, true, true>()
+                 : f.template lanes<T, V, kSplitHalf, true, false>();
+    else tok ? f.template lanes<T, V, kSplitHalf, false, true>()
+             : f.template lanes<T, V, kSplitHalf, false, false>();
+    return true;
+  }
+  if constexpr (V == 8) {
+    if (idx) tok ? f.template lanes<T, V, kInterleaved, true, true>()
+                 : f.template lanes<T, V, kInterleaved, true, false>();
+    else tok ? f.template lanes<T, V, kInterleaved, false, true>()
+             : f.template lanes<T, V, kInterleaved, false, false>();
+    return true;
+  }
+  return false;
+}
+
 template <class F>
 bool dispatch(const XPlan& pl, F& f) {
+  if (pl.lanes) {
+    switch (pl.dtype) {
+      case ROPE_F32: return dispatch_lanes<float>(pl, f);
+      case ROPE_F16: return dispatch_lanes<_Float16>(pl, f);
+      case ROPE_BF16: return dispatch_lanes<__bf16>(pl, f);
+    }
+    return false;
+  }
   if (pl.vec == 0) {
     switch (pl.dtype) {
       case ROPE_F32: f.template element<float>(); return true;

@@ -69,6 +69,12 @@ struct HostRunner {
       for (int t = 0; t < rope::xpos::kBlock; ++t)
         rope::xpos::xpos_block<T, V, PAIR, U>(pl.a, blk, t);
   }
+  template <typename T, int V, int PAIR, bool IDX, bool TOKEN>
+  void lanes() {
+    for (int64_t blk = 0; blk < pl.grid; ++blk)
+      for (int t = 0; t < pl.block; ++t)
+        rope::xpos::xpos_lanes<T, V, PAIR, IDX, TOKEN>(pl.a, blk, t);
+  }
   template <typename T>
   void element() {
     for (int64_t blk = 0; blk < pl.grid; ++blk)
@@ -139,8 +145,8 @@ int main(int argc, char** argv) {
   const rope_status_t st = rope::xpos::make_xpos_plan(&d, zq, kn ? zk : nullptr, &pl);
   printf("status %d\n", (int)st);
   if (st != ROPE_OK) return 0;
-  printf("vec %d\ngrid %lld\nheads_per_group %d\n", pl.vec, (long long)pl.grid,
-         (int)pl.a.heads_per_group);
+  printf("vec %d\ngrid %lld\nheads_per_group %d\nlanes %d\nblock %d\n", pl.vec,
+         (long long)pl.grid, (int)pl.a.heads_per_group, pl.lanes, pl.block);
   if (!pl.empty) {
     HostRunner run{pl};
     if (!rope::xpos::dispatch(pl, run)) {

@@ -90,6 +90,25 @@ CASES = [
 ]
 
 
+# The lanes shape (one chunk of one (token, head) per lane, in place,
+# 16-byte chunks): the fields above, then the expected form (1 head-major,
+# 2 token-major) and heads per workgroup group (head-major).
+LANES_CASES = [
+    (2, 300, 6, 2, 128, 128, "bf16", "split_half", "bhsd", False, "skip", 1, 512.0, 100.0, 8,
+     1, 8),
+    (1, 100, 9, 3, 128, 128, "bf16", "split_half", "bhsd", False, "none", -1, 64.0, 50.0, 8,
+     1, 8),
+    (1, 60, 6, 2, 64, 64, "f32", "split_half", "bhsd", False, "none", 1, 32.0, 20.0, 4, 1, 8),
+    (2, 50, 8, 2, 128, 128, "bf16", "split_half", "bshd", False, "none", 1, 512.0, 25.0, 8,
+     2, 1),
+    (1, 40, 4, 4, 64, 64, "f16", "interleaved", "bshd", False, "skip", -1, 16.0, 10.0, 8, 2, 1),
+    (3, 1, 5, 3, 64, 64, "bf16", "interleaved", "bhsd", False, "decode", 1, 8.0, 3.0, 8, 1, 8),
+    # heads 16 MiB apart: the long-sequence workgroups (chunks x 2 tokens x 8 heads)
+    (1, 32768, 6, 2, 128, 128, "f32", "split_half", "bhsd", False, "none", 1, 512.0, 16384.0,
+     4, 1, 8),
+]
+
+
 def case_id(c):
     return "-".join(str(x) for x in c[:12])
 
@@ -184,10 +203,25 @@ def run_emu(emu, c, q, k, pos, pbs, rows, cos, sin, zq, zk):
             return status, None, None
         run_emu.last_vec = int(out["vec"])
         run_emu.last_group = int(out["heads_per_group"])
+        run_emu.last_lanes = int(out["lanes"])
         go = np.fromfile(os.path.join(job, "q_out.bin"), dtype=qs.dtype).reshape(qs.shape)
         gk = None if ks is None else np.fromfile(os.path.join(job, "k_out.bin"),
                                                  dtype=ks.dtype).reshape(ks.shape)
         return 0, go, gk
+
+
+@pytest.mark.parametrize("c", LANES_CASES, ids=case_id)
+def test_emulated_lanes_shape_matches_oracle(orc, emu, c):
+    q, k, pos, pbs, rows, cos, sin, zq, zk = _case_data(c)
+    status, gq, gk = run_emu(emu, c, q, k, pos, pbs, rows, cos, sin, zq, zk)
+    assert status == 0
+    assert (run_emu.last_vec, run_emu.last_lanes) == (c[14], c[15])
+    if c[15] == 1:
+        assert run_emu.last_group == c[16]
+    eq, ek = _expected(c, q, k, pos, pbs, rows)
+    check(gq, eq, c[6], "q")
+    if ek is not None:
+        check(gk, ek, c[6], "k")
 
 
 @pytest.mark.parametrize("c", CASES, ids=case_id)
@@ -292,7 +326,7 @@ def _gpu_call(c, q, k, pos, pbs, rows, cos, sin, zq, zk, stream=None):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("c", CASES, ids=case_id)
+@pytest.mark.parametrize("c", CASES + LANES_CASES, ids=case_id)
 def test_gpu_matches_oracle(orc, c):
     print(f"xpos case {case_id(c)}", flush=True)
     q, k, pos, pbs, rows, cos, sin, zq, zk = _case_data(c)
