@@ -287,7 +287,32 @@ def _probe_lib():
     lib.stream_rmw_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint,
                                      ctypes.c_void_p]
     lib.stream_rmw_probe.restype = ctypes.c_int
+    lib.mfma_rate_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.mfma_rate_probe.restype = ctypes.c_int
     return lib
+
+
+def mfma_ceiling(blocks: int = 1024, iters: int = 4000, reps: int = 5):
+    """TFLOP/s that chains of v_mfma_f32_32x32x16_bf16 on register operands
+    sustain over the whole GPU (libstream_probe.so): the attainable rate of
+    the bf16 matrix cores, beside their published peak."""
+    import torch
+    lib = _probe_lib()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    settle(lambda i: lib.mfma_rate_probe(out.data_ptr(), blocks, iters, stream.cuda_stream))
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        assert lib.mfma_rate_probe(out.data_ptr(), blocks, iters, stream.cuda_stream) == 0
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / reps
+    flops = blocks * 4 * iters * 16 * 32768
+    return {"kernel": "mfma_rate_kernel (4 chains of v_mfma_f32_32x32x16_bf16 per wave)",
+            "flops_per_launch": flops, "avg_launch_us": round(us, 2),
+            "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1)}
 
 
 def stream_ceiling(nbytes: int = 160 << 20, reps: int = 40, sets: int = 4):
@@ -542,6 +567,7 @@ def time_attention(target_s: float = 0.5):
     import rotary_position_embedding_fwd_amd as rp
     import workloads as W
     stream = torch.cuda.current_stream()
+    ceiling = mfma_ceiling()
     results = []
     for w in W.ATTN_ALL:
         t = {k: v.cuda() for k, v in W.attn_tensors(w).items()}
@@ -584,6 +610,11 @@ def time_attention(target_s: float = 0.5):
             "k_once_TFLOPs": round(flops / (k_once_us * 1e-6) / 1e12, 1),
             "k_once_frac_of_mfma_bf16_peak": round(
                 flops / (k_once_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "attention_without_rotation_TFLOPs": round(flops / (plain_us * 1e-6) / 1e12, 1),
+            "measured_mfma_bf16_ceiling": ceiling,
+            "fused_frac_of_measured_mfma_ceiling": round(tf / ceiling["TFLOPs"], 4),
+            "k_once_frac_of_measured_mfma_ceiling": round(
+                flops / (k_once_us * 1e-6) / 1e12 / ceiling["TFLOPs"], 4),
             "reps": reps,
             "kernel": "rope_attention_kernel (v_mfma_f32_32x32x16_bf16)",
         })
@@ -806,6 +837,39 @@ def _bench_entries(b):
     return out
 
 
+def summarize_counters(pmc_dir: str, out: str):
+    """Mean of every counter of a rocprofv3 --pmc run per kernel launch shape
+    (kernel name, grid, workgroup size), with the dispatch count, into a small
+    JSON file (the raw per-dispatch files run to tens of MB)."""
+    import csv
+    acc = {}
+    for p in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0),
+                       int(r.get("Workgroup_Size", 0) or 0))
+                e = acc.setdefault(key, {"vgpr": r.get("VGPR_Count"),
+                                         "agpr": r.get("Accum_VGPR_Count"),
+                                         "lds": r.get("LDS_Block_Size"), "counters": {}})
+                s = e["counters"].setdefault(r["Counter_Name"], [0.0, 0])
+                s[0] += float(r["Counter_Value"])
+                s[1] += 1
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    d = e.setdefault("ns", {})
+                    d[r.get("Dispatch_Id")] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    res = []
+    for (name, grid, block), e in sorted(acc.items(), key=lambda kv: kv[0]):
+        n = max(c[1] for c in e["counters"].values())
+        ns = list(e.get("ns", {}).values())
+        res.append({"kernel": name, "grid": grid, "block": block, "dispatches": n,
+                    "vgpr": e["vgpr"], "agpr": e["agpr"], "lds": e["lds"],
+                    "mean_ns": sum(ns) / len(ns) if ns else None,
+                    "mean": {k: c[0] / c[1] for k, c in sorted(e["counters"].items())}})
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(f"{len(res)} launch shapes -> {out}")
+
+
 def summarize_pmc(fetch_dir: str, write_dir: str, bench_json: str, out: str = TRAFFIC_FILE):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
     `bench.py --copy-calibration` into per-launch HBM traffic of each timed
@@ -891,6 +955,19 @@ def _stats_us(ns):
             "max_us": round(max(us), 3)}
 
 
+def summarize_kernels(trace_dir: str, out: str):
+    """Per-kernel durations of every dispatch in a rocprofv3 kernel trace,
+    grouped by kernel name and grid, into a small JSON file."""
+    groups = {}
+    for name, wg, grid, ns in _trace_rows(trace_dir):
+        groups.setdefault((name, grid, wg), []).append(ns)
+    res = [dict(kernel=k[0], grid=k[1], block=k[2], **_stats_us(v))
+           for k, v in sorted(groups.items())]
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(f"{len(res)} launch shapes -> {out}")
+
+
 def summarize_trace(trace_dir: str, bench_json: str):
     """Per-kernel durations of the launches bench.py timed, from a rocprofv3
     kernel trace of that bench run: for each timed workload, the dispatches
@@ -964,6 +1041,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"))
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "OUT_JSON"),
+                    help="mean of each counter of a --pmc run per kernel launch shape")
+    ap.add_argument("--summarize-kernels", nargs=2, metavar=("TRACE_DIR", "OUT_JSON"),
+                    help="durations of every kernel of a --kernel-trace run per launch shape")
     ap.add_argument("--workloads", action="store_true",
                     help="time every workload (both grid shapes); one JSON line each")
     ap.add_argument("--general-form", action="store_true",
@@ -982,6 +1063,12 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_kernels:
+        summarize_kernels(*args.summarize_kernels)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)

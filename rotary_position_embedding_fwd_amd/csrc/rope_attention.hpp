@@ -581,6 +581,9 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
       for (int st = 0; st < kSteps; ++st)
         kf[st] = *reinterpret_cast<const bf16x8*>(
             &lds[k_lds<D>(buf, half * 32 + (lane & 31), st * 16 + hs * 8)]);
+      // keep every read of the half ahead of its first product (left to
+      // itself the compiler interleaves them, one LDS round trip per product)
+      __builtin_amdgcn_sched_barrier(0);
       floatx16 sh = {};
 #pragma unroll
       for (int st = 0; st < kSteps; ++st)
