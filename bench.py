@@ -280,6 +280,79 @@ def time_decode(calls: int = 2000, warmup: int = 50, theta: bool = False):
                     "comes from the rocprofv3 trace)"}
 
 
+def _graph_us_per_call(make, per_graph: int = 100, replays: int = 20) -> float:
+    """µs per call of make(stream)() replayed from a captured HIP graph of
+    `per_graph` calls (no host launch cost), after a settle phase."""
+    import torch
+    stream = torch.cuda.current_stream()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.graph(g, stream=side):
+        call = make(side)
+        for _ in range(per_graph):
+            call()
+    torch.cuda.synchronize()
+    settle(lambda i: g.replay())
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1000.0 / (per_graph * replays)
+
+
+def time_decode_sweep(batches=(1, 4, 16, 64, 128, 256, 512, 1024, 2048)):
+    """The decode call (one token per sequence, Q [n, 32, 1, 128], K [n, 8,
+    1, 128], bf16, a position per sequence) at several sequence counts n,
+    each replayed from a captured graph, beside the empty-kernel floor. A
+    least-squares line through (bytes, µs) splits the per-call time into a
+    fixed part and a part that grows with the bytes moved."""
+    import numpy as np
+    import torch
+    import rotary_position_embedding_fwd_amd as rp
+    import workloads as W
+    base = W.DECODE
+    cos, sin = rp.rope_build_table(base.table_rows, base.rotary_dim, base.theta)
+    cos, sin = cos.cuda(), sin.cuda()
+    floor = empty_kernel_floor()
+    rows = []
+    for n in batches:
+        w = base.scaled(batch=n)
+        pos = W.positions(w).cuda()
+        t = W.tensors(w, ("q", "k"))
+        q, k = t["q"].cuda(), t["k"].cuda()
+
+        def make(st):
+            return rp.prepare(q, k, cos, sin, layout=w.layout, pairing=w.pairing,
+                              rotary_dim=w.rotary_dim, pos=pos, stream=st).rope_fwd_qk
+        us = _graph_us_per_call(make)
+        nbytes = algorithmic_bytes(w, pos.cpu())
+        desc = rp.rope_describe(q, k, cos, sin, layout=w.layout, pairing=w.pairing,
+                                rotary_dim=w.rotary_dim, pos=pos)
+        rows.append({"sequences": n, "algorithmic_bytes": nbytes,
+                     "us_per_call_graph_replay": round(us, 3),
+                     "us_above_empty_kernel": round(us - floor, 3),
+                     "kernel": _kernel_fields(desc)})
+        del q, k, t
+    # the line through the counts up to the decode shape's 256 sequences
+    # (beyond it the operands no longer stay in the L2 caches between calls)
+    fit_rows = [r for r in rows if r["sequences"] <= base.batch]
+    x = np.array([r["algorithmic_bytes"] for r in fit_rows], dtype=np.float64)
+    y = np.array([r["us_per_call_graph_replay"] for r in fit_rows], dtype=np.float64)
+    slope, icpt = np.polyfit(x, y, 1)
+    return {"workload": "decode_bf16 sweep over sequence count", "rows": rows,
+            "empty_kernel_us_per_call_graph_replay": floor,
+            "fit": {"fixed_us": round(float(icpt), 3),
+                    "fixed_us_above_empty_kernel": round(float(icpt) - floor, 3),
+                    "GBps_of_the_growing_part": round(1e-3 / float(slope), 1)},
+            "note": "every row: 100 captured calls replayed 20 times on the same buffers; "
+                    "fit: least squares of µs per call against algorithmic bytes over the "
+                    "rows up to %d sequences" % base.batch}
+
+
 def _probe_lib():
     import ctypes
     path = os.path.join(ROOT, "rotary_position_embedding_fwd_amd", "libstream_probe.so")
@@ -503,7 +576,7 @@ def time_xpos(target_s: float = 0.15):
                "views": "[B,H,S,D]" if layout == "bhsd" else "packed QKV [B,S,H,D]",
                "xpos": {"scale_base": 512.0, "gamma": 0.4, "center": w.seq_len / 2},
                "buffer_sets": 3, "algorithmic_bytes_per_call": nbytes,
-               "kernel": "rope_xpos_kernel (16-byte chunks, 8 heads per lane)"}
+               "kernel": "rope_xpos_lanes_kernel (one 16-byte chunk of one (token, head) per lane)"}
         _time_calls(out, fwd, bwd, 3, nbytes, target_s, stream, method="rope_apply_xpos")
         results.append(out)
         plain_bytes = algorithmic_bytes(w, None)
@@ -1056,6 +1129,8 @@ def main():
                     help="rows vs token launch on token-major views, by shape and pairing")
     ap.add_argument("--xpos", action="store_true",
                     help="RoPE with XPOS factors (rope_apply_xpos) against plain rope_apply")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="decode calls at several sequence counts against the launch floor")
     ap.add_argument("--attention", action="store_true",
                     help="time attention with RoPE fused on the loaded Q/K blocks, against "
                          "rotation followed by attention")
@@ -1093,6 +1168,9 @@ def main():
     if args.xpos:
         for res in time_xpos():
             print(json.dumps(res), flush=True)
+        return
+    if args.decode_sweep:
+        print(json.dumps(time_decode_sweep()), flush=True)
         return
     if args.attention:
         for res in time_attention():
