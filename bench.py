@@ -753,8 +753,10 @@ LAYOUT_MATRIX_SHAPES = {
 
 def time_layout_matrix(reps: int = 400):
     """rows vs token launch on token-major views ([B,S,H,D] tensors and Q/K
-    views into a packed QKV buffer), both pairings: forward rope_apply in
-    place, reps calls over 3 buffer sets between two HIP events."""
+    views into a packed QKV buffer), both pairings, and the automatic
+    choice beside them (which may be a shape only it launches): forward
+    rope_apply in place, reps calls over 3 buffer sets between two HIP
+    events."""
     import torch
     import rotary_position_embedding_fwd_amd as rp
     import workloads as W
@@ -775,7 +777,7 @@ def time_layout_matrix(reps: int = 400):
                                  g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D), g))
             for pairing in ("split_half", "interleaved"):
                 res = {"shape": name, "view": view, "pairing": pairing}
-                for launch in ("rows", "token"):
+                for launch in ("rows", "token", "auto"):
                     calls = [rp.prepare_apply(x[0], x[1], cos, sin, layout="bshd",
                                               pairing=pairing, launch=launch,
                                               stream=stream).rope_apply for x in sets]

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 10300;  // 1.3.0: head-lanes and flat kernels, rope_describe
+constexpr int kVersion = 10400;  // 1.4.0: flat pair-lanes kernel for split-half token-major calls
 constexpr int kMaxDevices = 64;
 
 // Compute units per device, read once per device.
@@ -69,8 +69,8 @@ struct GpuLauncher {
   }
 
   // the forms only the automatic launch picks, instantiated for the calls the
-  // planner gives them (in place; head lanes: split-half 16-byte chunks;
-  // flat: interleaved pairs)
+  // planner gives them (in place; head lanes and flat pair lanes: split-half
+  // 16-byte chunks; flat: interleaved pairs)
   template <typename T, int V, int PAIR, bool AL, bool OOP>
   bool launch_only_auto(dim3 grid, dim3 block) {
     const bool idx = pl.a.pos != nullptr;
@@ -82,6 +82,14 @@ struct GpuLauncher {
         else
           hipLaunchKernelGGL((rope::rope_head_lanes_kernel<T, V, PAIR, AL, OOP, false>), grid,
                              block, 0, st, pl.a);
+        return true;
+      }
+      if (pl.flat) {
+        if (idx)
+          hipLaunchKernelGGL((rope::rope_flat_pair_kernel<T, V, true>), grid, block, 0, st, pl.a);
+        else
+          hipLaunchKernelGGL((rope::rope_flat_pair_kernel<T, V, false>), grid, block, 0, st,
+                             pl.a);
         return true;
       }
     }
@@ -139,7 +147,9 @@ rope_status_t run_apply(const rope_apply_desc_t* d, void* stream) {
 void describe_plan(const rope::Plan& pl, char* buf, int64_t len) {
   const char* kernel = "none (empty call)";
   if (!pl.empty) {
-    if (pl.flat)
+    if (pl.flat && pl.pairing == ROPE_SPLIT_HALF)
+      kernel = "rope_flat_pair_kernel";
+    else if (pl.flat)
       kernel = "rope_flat_kernel";
     else if (pl.head_lanes)
       kernel = "rope_head_lanes_kernel";

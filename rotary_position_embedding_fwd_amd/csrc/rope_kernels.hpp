@@ -787,6 +787,76 @@ __global__ void __launch_bounds__(kFlatBlock) rope_flat_kernel(Args a) {
   flat_body<T, V, PAIR, ALIGNED, OOP, kTrigVec, IDX>(a, blockIdx.x, threadIdx.x);
 }
 
+// Flat shape with split-half pairs: one 16-byte chunk per lane. The 2L
+// chunks of a row's rotated span (L = R / (2 V), a power of two <= 16) sit on
+// 2L consecutive lanes, lane c2 holding chunk c2 % L of half c2 / L, so every
+// row access of a wave covers whole consecutive spans, as a plain stream's
+// would; with a chunk pair per lane instead, each access of a wave covers one
+// half of every span (64 bytes of each 128-byte line at R = 64, 16-bit). The
+// pair partner's chunk (lane c2 ^ L, the same chunk of the other half) comes
+// from that lane's registers, and each lane writes only its own chunk, in the
+// steps of the pair-lanes rows kernel (rotate_own), which give rotate_pair's
+// bits. Rows start at multiples of 2L in the item numbering and 2L divides
+// the 64-lane workgroup, so both lanes of a pair are in one wave and share
+// every skip decision. begin() loads; the caller exchanges; finish() rotates
+// and stores.
+template <typename T, int V, int SRC, bool IDX> struct FlatPairWork {
+  using C = Chunk<T, V, true>;
+  Trig<V, kSplitHalf> t;
+  T* row;
+  bool upper, store;
+  C own, other;
+
+  // false: no item (past the end of the call)
+  ROPE_HD bool begin(const Args& a, int64_t block, int thread) {
+    int64_t g = block * kFlatBlock + thread;
+    if (g >= a.n_items) return false;
+    const bool is_q = g < a.n_items_q;
+    if (!is_q) g -= a.n_items_q;
+    const int heads = is_q ? a.n_heads_q : a.n_heads_k;
+    const int64_t r = g >> a.lanes_shift;
+    const int c2 = (int)(g & (a.lanes - 1));
+    const int L = a.lanes >> 1;
+    upper = (c2 & L) != 0;
+    const int c = c2 & (L - 1);
+    const int64_t n = r / heads;
+    const int h = (int)(r - n * heads);
+    const int64_t b = n / a.seq_len;
+    const int64_t s = n - b * a.seq_len;
+    row = const_cast<T*>(view_row<T>(is_q ? a.q_in : a.k_in, h, b, s)) + (upper ? a.half : 0) +
+          c * V;
+    own.load(row);
+    if constexpr (!IDX) {
+      store = true;
+      t.template load<SRC>(a, s, c * V);
+    } else {
+      const int64_t p = token_pos(a, b, s);
+      store = p >= 0;
+      // with no table rows every token is skipped and no table read is issued
+      if (SRC == kTrigTheta || a.table_rows > 0) t.template load<SRC>(a, p < 0 ? 0 : p, c * V);
+    }
+    return true;
+  }
+  ROPE_HD void finish() {
+    if (!store) return;  // a skipped token: nothing is written
+    const float sg = upper ? t.sign : -t.sign;
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      own.v[j] = from_f32<T>(rotate_own(to_f32(own.v[j]), to_f32(other.v[j]), t.c[j], sg * t.s[j]));
+    own.store(row);
+  }
+};
+
+template <typename T, int V, bool IDX>
+__global__ void __launch_bounds__(kFlatBlock) rope_flat_pair_kernel(Args a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  FlatPairWork<T, V, kTrigVec, IDX> w;
+  if (!w.begin(a, blockIdx.x, threadIdx.x)) return;
+  partner_chunk<T, V>(w.own, w.other, a.lanes >> 1);
+  w.finish();
+#endif
+}
+
 // ------------------------------------------------------------- token shape
 // Lanes cover (head, chunk) items of a token. Each lane's head rows are
 // requested before the position, so the row loads overlap the dependent

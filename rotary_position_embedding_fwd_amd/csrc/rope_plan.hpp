@@ -347,6 +347,17 @@ inline bool dense_token_major(const rope_apply_desc_t* d) {
   return true;
 }
 
+// Q and K views whose heads of a token are adjacent (a token's rows form one
+// contiguous stretch), whatever the token and batch strides: [B,S,H,D]
+// tensors and Q/K views into a packed QKV buffer.
+inline bool heads_adjacent(const rope_apply_desc_t* d) {
+  const rope_view_t* views[2] = {&d->q_in, &d->k_in};
+  const int64_t heads[2] = {d->n_heads_q, d->n_heads_k};
+  for (int i = 0; i < 2; ++i)
+    if (heads[i] > 1 && views[i]->stride_h != d->head_dim) return false;
+  return true;
+}
+
 // Validate and plan one call. `cus` is the device's compute-unit count.
 inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* pl) {
   const rope_status_t vs = validate_apply(d);
@@ -458,15 +469,40 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
     if (a.angles && pl->single) pl->lds_bytes = theta_shared_bytes(tpb, a.half);
     // Flat shape for dense token-major calls of many tokens: items numbered
     // over the whole call, so the grid streams Q and then K in memory order.
-    // Measured on MI355X with interleaved pairs, [8,2048,16+16,64] fp16 in
-    // place: 22.9 us against 23.8 us for the token kernel (one token per
-    // workgroup). Split-half calls keep the token kernel (not measured here).
-    const int64_t flat_items = a.n_tokens * per_token;
+    // Measured on MI355X in place, forward, fwd µs (flat / token kernel):
+    //   interleaved pairs: [8,2048,16+16,64] fp16 22.9 / 23.8,
+    //     [4,4096,32+32,64] bf16 42.3 / 43.3, [4,4096,32+8,128] bf16
+    //     52.6 / 56.5, but [2,4096,16+4,256] bf16 37.3 / 30.6: so rotated
+    //     spans up to 256 bytes;
+    //   split-half pairs, one 16-byte chunk per lane with the partner
+    //     exchange (rope_flat_pair_kernel): [8,2048,16+16,64] fp16
+    //     24.7 / 28.2 and [4,4096,32+32,64] bf16 46.7 / 54.2, where a chunk
+    //     pair per lane covers half of every 128-byte line per access; with
+    //     128-byte halves the token kernel's full-line accesses win
+    //     ([4,4096,32+8,128] 57.4 / 52.2, [2,4096,16+4,256] 35.4 / 27.4):
+    //     so spans up to 128 bytes (L = R / (2V) <= 4). The items are then
+    //     both halves' chunks, twice as many.
+    // Dense views only for interleaved pairs; split-half pairs also on views
+    // whose heads of a token are adjacent but whose tokens are not (Q/K in a
+    // packed QKV buffer): [8,2048,16+16,64] fp16 26.0 / 27.3 us and
+    // [4,4096,32+32,64] bf16 49.2 / 50.6 us, while interleaved packed views
+    // measured slower than the token kernel (24.2 / 23.6, 45.0 / 44.4).
+    const int64_t span_bytes = (int64_t)d->rotary_dim * elem_bytes(d->dtype);
+    const bool flat_pair = d->pairing == ROPE_SPLIT_HALF &&
+                           (int64_t)v * elem_bytes(d->dtype) == 16 && a.lanes_shift >= 0 &&
+                           span_bytes <= 128;
+    const bool flat_inter = d->pairing == ROPE_INTERLEAVED && span_bytes <= 256;
+    const int64_t flat_items = a.n_tokens * per_token * (flat_pair ? 2 : 1);
     if (d->launch == ROPE_LAUNCH_AUTO && d->seq_len > 1 && !pl->oop && !a.angles && a.t_vec &&
-        d->pairing == ROPE_INTERLEAVED && pl->aligned && dense_token_major(d) &&
+        ((flat_inter && dense_token_major(d)) || (flat_pair && heads_adjacent(d))) &&
+        pl->aligned &&
         flat_items / kFlatBlock < ((int64_t)1 << 30)) {
       pl->flat = true;
       pl->single = false;
+      if (flat_pair) {
+        a.lanes *= 2;
+        a.lanes_shift += 1;
+      }
       a.tokens_per_block = 1;
       a.n_items_q = a.n_tokens * (int64_t)a.n_heads_q * a.lanes;
       a.n_items = flat_items;

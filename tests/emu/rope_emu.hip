@@ -136,8 +136,47 @@ struct HostRunner {
       }
   }
 
+  // Flat shape with split-half pairs: the kernel's phases (load, partner
+  // exchange, rotate and store) run for every lane of the workgroup (one
+  // wave) before the next, each lane taking its partner's loaded chunk from
+  // that lane's registers.
+  template <typename T, int V, bool IDX>
+  void flat_pair_block(int64_t blk) {
+    using Work = rope::FlatPairWork<T, V, rope::kTrigVec, IDX>;
+    std::vector<Work> ws(pl.block);
+    std::vector<char> live(pl.block);
+    for (int t = 0; t < pl.block; ++t) live[t] = ws[t].begin(pl.a, blk, t);
+    const int L = pl.a.lanes >> 1;
+    for (int t = 0; t < pl.block; ++t) {
+      if (!live[t]) continue;
+      // a live lane's partner is live, in the same wave, holds the other
+      // half and makes the same skip decision
+      const int q = t ^ L;
+      if (q >= pl.block || !live[q] || (q >> 6) != (t >> 6) || ws[q].upper == ws[t].upper ||
+          ws[q].store != ws[t].store) {
+        fprintf(stderr, "flat pair lanes: lane %d has no partner\n", t);
+        exit(5);
+      }
+    }
+    for (int t = 0; t < pl.block; ++t)
+      if (live[t]) ws[t].other = ws[t ^ L].own;
+    for (int t = 0; t < pl.block; ++t)
+      if (live[t]) ws[t].finish();
+  }
+
   template <typename T, int V, int PAIR, bool AL, bool OOP>
   void go() {
+    if constexpr (PAIR == rope::kSplitHalf && AL && !OOP && V * sizeof(T) == 16) {
+      if (pl.flat) {
+        for (int64_t blk = 0; blk < pl.grid; ++blk) {
+          if (pl.a.pos)
+            flat_pair_block<T, V, true>(blk);
+          else
+            flat_pair_block<T, V, false>(blk);
+        }
+        return;
+      }
+    }
     if constexpr (PAIR == rope::kSplitHalf && AL && !OOP && V * sizeof(T) == 16) {
       if (!pl.token && pl.pair) {
         for (int64_t blk = 0; blk < pl.grid; ++blk) {

@@ -399,6 +399,33 @@ def test_packed_qkv_in_place(direction):
                        qkv[..., (Hq + Hk) * D:].view(torch.int16))
 
 
+@pytest.mark.parametrize("direction", [1, -1])
+def test_packed_qkv_flat_pair(direction):
+    """Packed QKV views with a 128-byte rotated span (head dim 64, bf16): the
+    flat pair-lanes kernel, against the oracle, bit for bit against the token
+    kernel, and the V part bit-exact."""
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=700, table_rows=700, head_dim=64,
+                                   rotary_dim=64, n_heads_q=16, n_heads_k=4)
+    B, S, Hq, Hk, D = w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim
+    qkv, q, k = _packed_views(B, S, Hq, Hk, D, w.dtype, 37)
+    say(f"[gpu] packed qkv flat pair {tuple(qkv.shape)} dir={direction}")
+    cos, sin = gpu_tables(w)
+    outs = []
+    for launch in ("auto", "token"):
+        g = qkv.to(DEV)
+        gq = g[..., :Hq * D].view(B, S, Hq, D)
+        gk = g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D)
+        rp.rope_apply(gq, gk, cos, sin, layout="bshd", direction=direction, launch=launch)
+        torch.cuda.synchronize()
+        outs.append(g.cpu())
+    gc = outs[0]
+    assert torch.equal(gc.view(torch.int16), outs[1].view(torch.int16))
+    _check_view(w, gc[..., :Hq * D].view(B, S, Hq, D), q, direction, None, what="q")
+    _check_view(w, gc[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D), k, direction, None, what="k")
+    assert torch.equal(gc[..., (Hq + Hk) * D:].view(torch.int16),
+                       qkv[..., (Hq + Hk) * D:].view(torch.int16))
+
+
 @pytest.mark.parametrize("launch", ["rows", "token"])
 def test_out_of_place_partial_rotary_skipped_tokens(launch):
     w = W.PARTIAL_INDEXED.scaled(seq_len=300, table_rows=9216)
@@ -657,3 +684,45 @@ def test_flat_equals_token_kernel_and_oracle(spec, direction):
     a = run_qk(w, t["q"], t["k"], direction)
     b = run_qk(w, t["q"], t["k"], direction, launch="token")
     assert np.array_equal(_bits(a[0]), _bits(b[0])) and np.array_equal(_bits(a[1]), _bits(b[1]))
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+@pytest.mark.parametrize("spec", [
+    dict(batch=2, seq_len=333, table_rows=333, pairing="split_half"),            # L = 4
+    dict(batch=1, seq_len=700, table_rows=700, n_heads_q=12, n_heads_k=4, dtype="bf16",
+         pairing="split_half", rotary_dim=32),                                    # L = 2
+    dict(batch=2, seq_len=257, table_rows=257, n_heads_q=8, n_heads_k=2, dtype="bf16",
+         pairing="split_half", head_dim=128, rotary_dim=64),                      # L = 4
+    dict(batch=1, seq_len=65, table_rows=65, n_heads_q=3, n_heads_k=1, dtype="f32",
+         pairing="split_half", head_dim=64, rotary_dim=32),                       # L = 4
+])
+def test_flat_pair_equals_token_kernel_and_oracle(spec, direction):
+    """Dense [B,S,H,D] split-half calls run the flat kernel with one chunk per
+    lane and the partner lane's chunk (rope_flat_pair_kernel): every element
+    against the oracle, and bit for bit against the token kernel's chunk
+    pairs of the same call."""
+    w = W.BSHD_INTERLEAVED.scaled(**spec)
+    say(f"[gpu] flat pair q{tuple(w.q_shape)} {w.dtype} R={w.rotary_dim} dir={direction}")
+    check_full(w, direction)
+    t = W.tensors(w)
+    a = run_qk(w, t["q"], t["k"], direction)
+    b = run_qk(w, t["q"], t["k"], direction, launch="token")
+    assert np.array_equal(_bits(a[0]), _bits(b[0])) and np.array_equal(_bits(a[1]), _bits(b[1]))
+    cos, sin = gpu_tables(w)
+    desc = rp.rope_describe(t["q"].to(DEV), t["k"].to(DEV), cos, sin, **opts(w))
+    assert desc.startswith("rope_flat_pair_kernel"), desc
+
+
+def test_flat_pair_skipped_tokens_and_describe():
+    """The indexed form (CLS tokens skipped, an offset start) on a [B,S,H,D]
+    split-half call, both directions against the oracle; rope_describe names
+    the kernel."""
+    w = W.PARTIAL_INDEXED.scaled(layout="bshd")
+    t = W.tensors(w)
+    pos = W.positions(w)
+    cos, sin = gpu_tables(w)
+    desc = rp.rope_describe(t["q"].to(DEV), t["k"].to(DEV), cos, sin, **opts(w, pos.to(DEV)))
+    say(f"[gpu] flat pair indexed: {desc}")
+    assert desc.startswith("rope_flat_pair_kernel"), desc
+    for direction in (1, -1):
+        check_full(w, direction)

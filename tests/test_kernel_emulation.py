@@ -260,11 +260,13 @@ def test_interleaved_lanes_take_two_items(emu, direction):
 
 
 def test_token_packing_keeps_the_chip_filled(emu):
-    """Tokens per workgroup shrink so the grid keeps 16 workgroups per CU."""
+    """Tokens per workgroup shrink so the grid keeps 16 workgroups per CU
+    (the token shape, forced: AUTO gives this dense view the flat shape)."""
     w = SMALL["llama_ragged"].scaled(n_heads_q=2, n_heads_k=1, head_dim=64, rotary_dim=64,
                                      layout="bshd")
-    assert check(emu, w, cus=1)["tokens_per_block"] == 9  # 154 // 16
-    assert check(emu, w, cus=256)["tokens_per_block"] == 1
+    assert check(emu, w, launch="token", cus=1)["tokens_per_block"] == 9  # 154 // 16
+    assert check(emu, w, launch="token", cus=256)["tokens_per_block"] == 1
+    assert check(emu, w)["flat"] == 1
 
 
 def test_many_heads_loop_in_token_shape(emu):
@@ -944,7 +946,96 @@ def test_flat_q_only_and_misaligned(emu):
 
 def test_flat_only_where_it_applies(emu):
     w = FLAT_CASES["bshd_interleaved_ragged"]
-    assert check(emu, w.scaled(pairing=W.SPLIT_HALF))["flat"] == 0
     assert check(emu, w.scaled(seq_len=1, table_rows=1))["flat"] == 0
+    # rotated spans past 256 bytes: the token kernel
+    assert check(emu, w.scaled(dtype="bf16", head_dim=256, rotary_dim=256))["flat"] == 0
     assert check(emu, w.scaled(layout="bhsd"))["flat"] == 0
     assert check(emu, w, launch="token")["flat"] == 0
+
+
+# ------------------------------------------- flat shape, split-half pairs
+# One 16-byte chunk per lane, the partner half's chunk from the partner lane
+# (rope_flat_pair_kernel), emulated with the wave's load, exchange and store
+# phases in lockstep. L = R / (2V) from 1 to 4 (rotated spans up to 128 bytes).
+FLAT_PAIR_CASES = {
+    "bshd_split_d64_fp16": W.BSHD_INTERLEAVED.scaled(batch=3, seq_len=45, table_rows=45,
+                                                     pairing=W.SPLIT_HALF),       # L = 4
+    "partial_r64_of_128_bf16": W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=21, table_rows=21,
+                                                          layout="bshd", rotary_dim=64),  # L = 4
+    "partial_r16_of_64": W.BSHD_INTERLEAVED.scaled(batch=2, seq_len=19, table_rows=19,
+                                                   pairing=W.SPLIT_HALF, dtype="bf16",
+                                                   rotary_dim=16),                # L = 1
+    "partial_r32_f32": W.BSHD_INTERLEAVED.scaled(batch=1, seq_len=23, table_rows=23,
+                                                 pairing=W.SPLIT_HALF, dtype="f32",
+                                                 rotary_dim=32),                  # L = 4
+    "q_heads_differ": W.BSHD_INTERLEAVED.scaled(batch=2, seq_len=13, table_rows=13,
+                                                pairing=W.SPLIT_HALF, n_heads_q=12,
+                                                n_heads_k=4),
+    "skipped_tokens": W.PARTIAL_INDEXED.scaled(seq_len=70, pos_start_max=9000, layout="bshd"),
+}
+
+
+@pytest.mark.parametrize("name", list(FLAT_PAIR_CASES))
+@pytest.mark.parametrize("direction", [1, -1])
+def test_flat_pair_matches_oracle_and_token_kernel(emu, name, direction):
+    """Every element against the oracle, and bit for bit against the token
+    kernel's chunk-pair form of the same call."""
+    w = FLAT_PAIR_CASES[name]
+    plan = check(emu, w, direction, expect=dict(token=1, flat=1, block=64))
+    half = w.rotary_dim // 2
+    vec = 16 // {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    assert plan["lanes"] == 2 * (half // vec), plan
+    q, k, wpos, cos, sin = _inputs(w)
+    _, q1, k1 = run_emu(emu, w, q, k, cos, sin, wpos, direction, "auto")
+    plan0, q0, k0 = run_emu(emu, w, q, k, cos, sin, wpos, direction, "token")
+    assert plan0["flat"] == 0
+    assert np.array_equal(q1, q0) and np.array_equal(k1, k0)
+
+
+def test_flat_pair_q_only(emu):
+    w = FLAT_PAIR_CASES["bshd_split_d64_fp16"]
+    assert check(emu, w, with_k=False)["flat"] == 1
+
+
+def test_flat_pair_only_where_it_applies(emu):
+    w = FLAT_PAIR_CASES["bshd_split_d64_fp16"]
+    # 4-byte aligned base: 2-element chunks, no partner exchange of 16 bytes
+    assert check(emu, w, q_offset=2, expect=dict(vec=2))["flat"] == 0
+    # 128-byte halves and wider (R = 128 and 256 in 16-bit): the token kernel
+    wide = W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=9, table_rows=9, layout="bshd")
+    assert check(emu, wide)["flat"] == 0
+    assert check(emu, wide.scaled(n_heads_q=3, n_heads_k=1, head_dim=256,
+                                  rotary_dim=256))["flat"] == 0
+    assert check(emu, w.scaled(layout="bhsd"))["flat"] == 0
+    assert check(emu, w, launch="token")["flat"] == 0
+
+
+@pytest.mark.parametrize("spec", [dict(head_dim=64, rotary_dim=64),
+                                  dict(head_dim=64, rotary_dim=32, table_rows=100)])
+def test_packed_qkv_flat_pair(emu, spec):
+    """Q and K as views into packed QKV storage at a 128-byte (or shorter)
+    rotated span: AUTO runs the flat pair-lanes kernel; the result equals the
+    token kernel's bit for bit, the oracle's on every element, and V's part
+    of each token is untouched."""
+    w = PACKED.scaled(**spec)
+    buf, qs, ks, _ = _packed(w, seed=8)
+    cos, sin = _half_tables(w)
+    pos = (W.random_positions(w.seq_len, 130, 11, low=-20) if spec.get("table_rows")
+           else None)
+    kw = dict(pos=pos, pos_batch_stride=0) if pos is not None else {}
+    plan, after, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, launch="auto", **kw)
+    assert plan["status"] == 0 and plan["flat"] == 1 and plan["oop"] == 0, plan
+    plan0, after0, _ = run_emu_apply(emu, w, buf, qs, ks, cos, sin, launch="token", **kw)
+    assert plan0["flat"] == 0
+    assert np.array_equal(P.storage(after), P.storage(after0))
+    qshape = (w.batch, w.n_heads_q, w.seq_len, w.head_dim)
+    kshape = (w.batch, w.n_heads_k, w.seq_len, w.head_dim)
+    extra = dict(pos_batch_stride=0) if pos is not None else {}
+    _assert_view(w, _strided(after, qs, qshape), _strided(buf, qs, qshape), 1, pos,
+                 w.n_heads_q, **extra)
+    _assert_view(w, _strided(after, ks, kshape), _strided(buf, ks, kshape), 1, pos,
+                 w.n_heads_k, **extra)
+    B, S, D, Hq, Hk = w.batch, w.seq_len, w.head_dim, w.n_heads_q, w.n_heads_k
+    v0 = buf.view(B, S, -1)[..., (Hq + Hk) * D:]
+    v1 = after.view(B, S, -1)[..., (Hq + Hk) * D:]
+    assert np.array_equal(P.storage(v0.contiguous()), P.storage(v1.contiguous()))
