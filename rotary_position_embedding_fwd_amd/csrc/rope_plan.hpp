@@ -563,7 +563,14 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
       hl_span = 32;
       hl_heads = 20;
     }
-    pl->head_lanes = d->launch == ROPE_LAUNCH_AUTO && hl_span > 0 &&
+    // Rotated spans under 256 bytes (halves under one 128-byte line) keep
+    // the pair-lanes rows kernel: there a chunk pair per lane makes each
+    // access of a wave cover half lines. Measured (fwd, head lanes / pair
+    // lanes): [4,32+8,4096,64] bf16 35.5 / 31.8 us, [4,32+32,4096,64] bf16
+    // 55.5 / 49.4, [8,16+16,2048,64] fp16 32.2 / 28.9, R = 64 of 128 bf16
+    // 34.0 / 32.2, R = 32 of 64 bf16 18.7 / 17.0.
+    const bool hl_wide = (int64_t)d->rotary_dim * elem_bytes(d->dtype) >= 256;
+    pl->head_lanes = d->launch == ROPE_LAUNCH_AUTO && hl_span > 0 && hl_wide &&
                      d->pairing == ROPE_SPLIT_HALF && !pl->oop && pl->aligned && !a.angles &&
                      a.t_vec && (int64_t)v * elem_bytes(d->dtype) == 16 && a.lanes_shift >= 0 &&
                      a.lanes <= hl_span && h_total >= 8;

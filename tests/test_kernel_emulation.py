@@ -862,8 +862,8 @@ HEAD_LANES_CASES = {
     "llama_ragged": (W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=77, table_rows=80), (8, 8)),
     "heads_not_a_multiple": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=21, table_rows=21,
                                                         n_heads_q=9, n_heads_k=3), (8, 8)),
-    "partial_indexed_skips": (W.PARTIAL_INDEXED.scaled(seq_len=130, pos_start_max=9000),
-                              (32, 8)),
+    "indexed_skips": (W.PARTIAL_INDEXED.scaled(seq_len=130, pos_start_max=9000, head_dim=128,
+                                              rotary_dim=128), (8, 8)),
     "f16_R256": (W.LLAMA_GQA_PREFILL.scaled(batch=1, seq_len=19, head_dim=256, rotary_dim=256,
                                             dtype="f16", table_rows=19, n_heads_q=6,
                                             n_heads_k=2), (4, 8)),
@@ -908,6 +908,12 @@ def test_head_lanes_only_where_they_apply(emu):
     assert check(emu, w, q_offset=4, cus=1)["head_lanes"] == 0
     assert check(emu, w.scaled(n_heads_q=5, n_heads_k=2), cus=1)["head_lanes"] == 0
     assert _theta_case(emu, w, cus=1)["head_lanes"] == 0
+    # rotated spans under 256 bytes keep the pair-lanes rows kernel (four
+    # sequences, so the table's re-reads allow 4-head groups)
+    plan = check(emu, w.scaled(batch=4, rotary_dim=64), cus=1)
+    assert plan["head_lanes"] == 0 and plan["pair"] == 1
+    plan = check(emu, W.PARTIAL_INDEXED.scaled(batch=4, seq_len=130, pos_start_max=9000), cus=1)
+    assert plan["head_lanes"] == 0
 
 
 # -------------------------------------------------------------- flat shape
