@@ -97,3 +97,24 @@ def test_head_lanes_long_form_with_a_ragged_head_group():
     for g, x, tag in ((qd.cpu(), t["q"], "q"), (kd.cpu(), t["k"], "k")):
         mx, n1 = _compare_sliced(w, g, x, 1, f"long form {tag}")
         say(f"[gpu]   {tag}: max distance {mx}, one unit off: {n1}")
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_flat_pair_full_size_every_element(direction):
+    """The BSHD workload's shape with split-half pairs ([8, 2048, 16+16, 64]
+    fp16): the flat pair-lanes kernel at full size, every element, both
+    directions; rope_describe confirms the kernel."""
+    w = W.BSHD_INTERLEAVED.scaled(pairing=W.SPLIT_HALF)
+    names = ("q", "k") if direction == 1 else ("dq", "dk")
+    say(f"[gpu] flat pair full size every element: dir={direction} q{tuple(w.q_shape)}")
+    t = W.tensors(w, names)
+    cos, sin = (x.to(DEV) for x in rp.rope_build_table(w.table_rows, w.rotary_dim, w.theta))
+    qd, kd = t[names[0]].to(DEV), t[names[1]].to(DEV)
+    kw = dict(layout=w.layout, pairing=w.pairing, rotary_dim=w.rotary_dim)
+    assert rp.rope_describe(qd, kd, cos, sin, **kw).startswith("rope_flat_pair_kernel")
+    fn = rp.rope_fwd_qk if direction == 1 else rp.rope_bwd_qk
+    fn(qd, kd, cos, sin, **kw)
+    torch.cuda.synchronize()
+    for g, x, tag in ((qd.cpu(), t[names[0]], "q"), (kd.cpu(), t[names[1]], "k")):
+        mx, n1 = _compare_sliced(w, g, x, direction, f"flat pair {tag} dir={direction}")
+        say(f"[gpu]   {tag}: max distance {mx}, one unit off: {n1} of {x.numel()}")
