@@ -1152,7 +1152,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the RoPE path has no cross-GPU step, "
-              "and this build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+              "and librope runs on a single MI355X per process. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
