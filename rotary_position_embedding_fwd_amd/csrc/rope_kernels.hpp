@@ -90,7 +90,6 @@ struct Args {
   View q_out, k_out;         // equal to the inputs in place
   double l2_step;            // angles from theta: -2 log2(theta) / R
   double interp;             // angles from theta: positions are divided by it
-  int64_t n_items_q;         // flat shape: the items of Q (n_tokens * n_heads_q * lanes)
   int32_t tokens_shift;      // head-lanes shape: log2(tokens_per_block)
   int32_t pad0;
 };
@@ -737,21 +736,23 @@ __global__ void __launch_bounds__(1024) rope_head_lanes_kernel(Args a) {
 }
 
 // ------------------------------------------------------------- flat shape
-// One (token, head, chunk) item per lane, items numbered over the whole call:
-// all of Q's (token, head, chunk) items, then all of K's, chunk fastest. For
-// views whose rows are dense in token-major order ([B,S,H,D] contiguous)
-// consecutive lanes and consecutive workgroups then walk each tensor in memory
-// order, one tensor after the other, like a plain stream. Small workgroups
-// (kFlatBlock lanes) measured best on MI355X.
+// One (token, head, chunk) item per lane, items numbered over the whole call
+// token by token, each token's Q heads then its K heads, chunk fastest. For
+// views whose heads of a token are adjacent ([B,S,H,D] tensors, Q and K in a
+// packed QKV buffer) consecutive lanes and consecutive workgroups then walk
+// the rows in memory order, token after token, like a plain stream (in a
+// packed buffer skipping only each token's V). Small workgroups (kFlatBlock
+// lanes) measured best on MI355X. (Numbering all of Q before all of K was
+// measured too: the same on [B,S,H,D] tensors, but on packed QKV the K pass
+// then touches 2 of every 12 KiB: 57.3 us against 54.6 us at [4, 4096,
+// 32+8, 128] bf16 with interleaved pairs, where the token kernel takes 57.3.)
 constexpr int kFlatBlock = 64;
 
 template <typename T, int V, int PAIR, bool ALIGNED, bool OOP, int SRC, bool IDX>
 ROPE_HD void flat_body(const Args& a, int64_t block, int thread) {
-  int64_t g = block * kFlatBlock + thread;
+  const int64_t g = block * kFlatBlock + thread;
   if (g >= a.n_items) return;
-  const bool is_q = g < a.n_items_q;
-  if (!is_q) g -= a.n_items_q;
-  const int heads = is_q ? a.n_heads_q : a.n_heads_k;
+  const int heads_all = a.n_heads_q + a.n_heads_k;
   int64_t row;
   int c;
   if (a.lanes_shift >= 0) {
@@ -761,8 +762,10 @@ ROPE_HD void flat_body(const Args& a, int64_t block, int thread) {
     row = g / a.lanes;
     c = (int)(g - row * a.lanes);
   }
-  const int64_t n = row / heads;
-  const int h = (int)(row - n * heads);
+  const int64_t n = row / heads_all;
+  const int hh = (int)(row - n * heads_all);
+  const bool is_q = hh < a.n_heads_q;
+  const int h = is_q ? hh : hh - a.n_heads_q;
   const int64_t b = n / a.seq_len;
   const int64_t s = n - b * a.seq_len;
   const T* in = view_row<T>(is_q ? a.q_in : a.k_in, h, b, s);
@@ -809,18 +812,18 @@ template <typename T, int V, int SRC, bool IDX> struct FlatPairWork {
 
   // false: no item (past the end of the call)
   ROPE_HD bool begin(const Args& a, int64_t block, int thread) {
-    int64_t g = block * kFlatBlock + thread;
+    const int64_t g = block * kFlatBlock + thread;
     if (g >= a.n_items) return false;
-    const bool is_q = g < a.n_items_q;
-    if (!is_q) g -= a.n_items_q;
-    const int heads = is_q ? a.n_heads_q : a.n_heads_k;
+    const int heads_all = a.n_heads_q + a.n_heads_k;
     const int64_t r = g >> a.lanes_shift;
     const int c2 = (int)(g & (a.lanes - 1));
     const int L = a.lanes >> 1;
     upper = (c2 & L) != 0;
     const int c = c2 & (L - 1);
-    const int64_t n = r / heads;
-    const int h = (int)(r - n * heads);
+    const int64_t n = r / heads_all;
+    const int hh = (int)(r - n * heads_all);
+    const bool is_q = hh < a.n_heads_q;
+    const int h = is_q ? hh : hh - a.n_heads_q;
     const int64_t b = n / a.seq_len;
     const int64_t s = n - b * a.seq_len;
     row = const_cast<T*>(view_row<T>(is_q ? a.q_in : a.k_in, h, b, s)) + (upper ? a.half : 0) +

@@ -332,21 +332,6 @@ inline View to_view(const rope_view_t& v) {
   return View{static_cast<char*>(v.data), v.stride_b, v.stride_h, v.stride_s};
 }
 
-// Q and K views ([B,S,H,D] order) whose rows are dense: heads adjacent,
-// tokens adjacent, batches adjacent.
-inline bool dense_token_major(const rope_apply_desc_t* d) {
-  const int64_t D = d->head_dim, S = d->seq_len;
-  const rope_view_t* views[2] = {&d->q_in, &d->k_in};
-  const int64_t heads[2] = {d->n_heads_q, d->n_heads_k};
-  for (int i = 0; i < 2; ++i) {
-    if (heads[i] == 0) continue;
-    const rope_view_t& v = *views[i];
-    if (v.stride_h != D || v.stride_s != heads[i] * D) return false;
-    if (d->batch > 1 && v.stride_b != S * v.stride_s) return false;
-  }
-  return true;
-}
-
 // Q and K views whose heads of a token are adjacent (a token's rows form one
 // contiguous stretch), whatever the token and batch strides: [B,S,H,D]
 // tensors and Q/K views into a packed QKV buffer.
@@ -482,11 +467,11 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
     //     ([4,4096,32+8,128] 57.4 / 52.2, [2,4096,16+4,256] 35.4 / 27.4):
     //     so spans up to 128 bytes (L = R / (2V) <= 4). The items are then
     //     both halves' chunks, twice as many.
-    // Dense views only for interleaved pairs; split-half pairs also on views
-    // whose heads of a token are adjacent but whose tokens are not (Q/K in a
-    // packed QKV buffer): [8,2048,16+16,64] fp16 26.0 / 27.3 us and
-    // [4,4096,32+32,64] bf16 49.2 / 50.6 us, while interleaved packed views
-    // measured slower than the token kernel (24.2 / 23.6, 45.0 / 44.4).
+    // Views whose heads of a token are adjacent, tokens adjacent or not (Q/K
+    // in a packed QKV buffer): with the items numbered token by token, packed
+    // [4,4096,32+8,128] bf16 interleaved 54.6 / 57.3 us, [8,2048,16+16,64]
+    // fp16 split-half 25.2 / 27.3, [4,4096,32+32,64] bf16 split-half
+    // 47.2 / 50.6.
     const int64_t span_bytes = (int64_t)d->rotary_dim * elem_bytes(d->dtype);
     const bool flat_pair = d->pairing == ROPE_SPLIT_HALF &&
                            (int64_t)v * elem_bytes(d->dtype) == 16 && a.lanes_shift >= 0 &&
@@ -494,7 +479,7 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
     const bool flat_inter = d->pairing == ROPE_INTERLEAVED && span_bytes <= 256;
     const int64_t flat_items = a.n_tokens * per_token * (flat_pair ? 2 : 1);
     if (d->launch == ROPE_LAUNCH_AUTO && d->seq_len > 1 && !pl->oop && !a.angles && a.t_vec &&
-        ((flat_inter && dense_token_major(d)) || (flat_pair && heads_adjacent(d))) &&
+        (flat_inter || flat_pair) && heads_adjacent(d) &&
         pl->aligned &&
         flat_items / kFlatBlock < ((int64_t)1 << 30)) {
       pl->flat = true;
@@ -504,7 +489,6 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
         a.lanes_shift += 1;
       }
       a.tokens_per_block = 1;
-      a.n_items_q = a.n_tokens * (int64_t)a.n_heads_q * a.lanes;
       a.n_items = flat_items;
       pl->block = kFlatBlock;
       pl->grid = (flat_items + kFlatBlock - 1) / kFlatBlock;

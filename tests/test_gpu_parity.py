@@ -400,12 +400,16 @@ def test_packed_qkv_in_place(direction):
 
 
 @pytest.mark.parametrize("direction", [1, -1])
-def test_packed_qkv_flat_pair(direction):
-    """Packed QKV views with a 128-byte rotated span (head dim 64, bf16): the
-    flat pair-lanes kernel, against the oracle, bit for bit against the token
-    kernel, and the V part bit-exact."""
-    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=700, table_rows=700, head_dim=64,
-                                   rotary_dim=64, n_heads_q=16, n_heads_k=4)
+@pytest.mark.parametrize("spec", [
+    dict(head_dim=64, rotary_dim=64),                 # split-half: flat pair lanes
+    dict(pairing="interleaved"),                      # interleaved, 256-byte spans: flat
+])
+def test_packed_qkv_flat_pair(spec, direction):
+    """Packed QKV views that AUTO gives a flat kernel (items token by token
+    over Q's then K's heads): against the oracle, bit for bit against the
+    token kernel, and the V part bit-exact."""
+    w = W.LLAMA_GQA_PREFILL.scaled(batch=2, seq_len=700, table_rows=700, n_heads_q=16,
+                                   n_heads_k=4, **spec)
     B, S, Hq, Hk, D = w.batch, w.seq_len, w.n_heads_q, w.n_heads_k, w.head_dim
     qkv, q, k = _packed_views(B, S, Hq, Hk, D, w.dtype, 37)
     say(f"[gpu] packed qkv flat pair {tuple(qkv.shape)} dir={direction}")
@@ -415,7 +419,8 @@ def test_packed_qkv_flat_pair(direction):
         g = qkv.to(DEV)
         gq = g[..., :Hq * D].view(B, S, Hq, D)
         gk = g[..., Hq * D:(Hq + Hk) * D].view(B, S, Hk, D)
-        rp.rope_apply(gq, gk, cos, sin, layout="bshd", direction=direction, launch=launch)
+        rp.rope_apply(gq, gk, cos, sin, layout="bshd", pairing=w.pairing, direction=direction,
+                      launch=launch)
         torch.cuda.synchronize()
         outs.append(g.cpu())
     gc = outs[0]

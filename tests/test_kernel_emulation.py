@@ -1017,12 +1017,16 @@ def test_flat_pair_only_where_it_applies(emu):
 
 
 @pytest.mark.parametrize("spec", [dict(head_dim=64, rotary_dim=64),
-                                  dict(head_dim=64, rotary_dim=32, table_rows=100)])
+                                  dict(head_dim=64, rotary_dim=32, table_rows=100),
+                                  dict(pairing="interleaved"),
+                                  dict(pairing="interleaved", head_dim=64, rotary_dim=48,
+                                       table_rows=100)])
 def test_packed_qkv_flat_pair(emu, spec):
-    """Q and K as views into packed QKV storage at a 128-byte (or shorter)
-    rotated span: AUTO runs the flat pair-lanes kernel; the result equals the
-    token kernel's bit for bit, the oracle's on every element, and V's part
-    of each token is untouched."""
+    """Q and K as views into packed QKV storage: AUTO runs a flat kernel
+    (split-half spans up to 128 bytes: pair lanes; interleaved spans up to
+    256 bytes), the items numbered token by token over Q's then K's heads;
+    the result equals the token kernel's bit for bit, the oracle's on every
+    element, and V's part of each token is untouched."""
     w = PACKED.scaled(**spec)
     buf, qs, ks, _ = _packed(w, seed=8)
     cos, sin = _half_tables(w)
