@@ -21,6 +21,7 @@ import rotary_position_embedding_fwd_amd as rp
 import workloads as W
 from tests import _exact as X
 from tests import _parity as P
+from tests._random_configs import draw as draw_config, workload as config_workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 EMU_SRC = os.path.join(ROOT, "tests", "emu", "rope_emu.hip")
@@ -1049,3 +1050,53 @@ def test_packed_qkv_flat_pair(emu, spec):
     v0 = buf.view(B, S, -1)[..., (Hq + Hk) * D:]
     v1 = after.view(B, S, -1)[..., (Hq + Hk) * D:]
     assert np.array_equal(P.storage(v0.contiguous()), P.storage(v1.contiguous()))
+
+
+RANDOM_EMU_CASES = 80
+RANDOM_EMU_CUS = (1, 4, 256)
+
+
+@pytest.mark.parametrize("case", range(RANDOM_EMU_CASES))
+def test_random_configurations_emulated(emu, case):
+    """Seeded random configurations (tests/_random_configs.py, restricted to
+    contiguous tensors, cos/sin tables and in-place calls): AUTO's kernel
+    against the oracle on every element, and bit for bit against both forced
+    grid shapes. The device size cycles through 1, 4 and 256 compute units,
+    so that small calls also take the shapes that AUTO keeps for calls that
+    fill the device."""
+    c = draw_config(20000 + case, 150_000, views=False)
+    cus = RANDOM_EMU_CUS[case % len(RANDOM_EMU_CUS)]
+    w = config_workload(c)
+    q = W.normal(w.q_shape, w.dtype, c["seed"])
+    k = W.normal(w.k_shape, w.dtype, c["seed"] + 50)
+    cos, sin = rp.rope_build_table(c["table_rows"], w.rotary_dim, w.theta)
+    pos = None if c["pos"] is None else torch.from_numpy(c["pos"])
+    pbs = c["pos_batch_stride"] or 0
+    outs = []
+    for launch in ("auto", "rows", "token"):
+        plan, qo, ko = run_emu(emu, w, q, k, cos, sin, pos, c["direction"], launch,
+                               cus=cus, pos_batch_stride=pbs)
+        assert plan["status"] == 0, (launch, plan)
+        outs.append((qo, ko))
+    for qo, ko in outs[1:]:
+        assert np.array_equal(qo, outs[0][0]) and np.array_equal(ko, outs[0][1])
+    masked = P.masked_tokens(w, pos, pos_batch_stride=pbs)
+    for got, x, what in ((outs[0][0], q, "q"), (outs[0][1], k, "k")):
+        P.assert_parity(got, P.oracle_rope(w, x, c["direction"], pos, pos_batch_stride=pbs),
+                        P.storage(x), w.dtype, w.layout, w.rotary_dim, masked,
+                        f"random case {case} {what}")
+
+
+def test_random_configurations_reach_every_kernel(emu):
+    """AUTO's plans over the emulated draws (those without an index) include
+    every kernel: head lanes, flat, flat pair lanes, pair lanes, token, rows."""
+    seen = set()
+    for case in range(RANDOM_EMU_CASES):
+        c = draw_config(20000 + case, 150_000, views=False)
+        if c["pos"] is not None:
+            continue
+        p = plan_of(emu, config_workload(c), cus=RANDOM_EMU_CUS[case % len(RANDOM_EMU_CUS)])
+        seen.add("flat_pair" if p["flat"] and c["pairing"] == W.SPLIT_HALF else
+                 "flat" if p["flat"] else "head_lanes" if p["head_lanes"] else
+                 "token" if p["token"] else "pair_lanes" if p["pair"] else "rows")
+    assert seen == {"flat_pair", "flat", "head_lanes", "token", "pair_lanes", "rows"}, seen
