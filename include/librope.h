@@ -295,7 +295,9 @@ rope_status_t rope_build_xpos_table(float *xpos_q, float *xpos_k, int64_t table_
  * Matrix-core kernel: the products run as bf16 with float32 accumulation and
  * the softmax weights are rounded to bf16 before they multiply V.
  * Limits: head_dim 64 or 128; split-half pairs need R % 32 == 0 and
- * interleaved pairs R % 8 == 0 (R = 0: no rotation). */
+ * interleaved pairs R % 8 == 0 (R = 0: no rotation); one head's K (and V)
+ * rows, Sk * D * 2 bytes, and a cos/sin table, table_rows * R/2 * 4 bytes,
+ * each under 4 GiB (the kernel addresses inside them with 32-bit offsets). */
 typedef struct rope_attn_desc {
   int64_t batch;
   int64_t n_heads_q;    /* Hq >= 1 */

@@ -238,8 +238,9 @@ ROPE_HD void rotate_inter8(bf16x8& x, const float* c, const float* s) {
 // n (4 or 8) table entries from `first` (a multiple of 4) of row p: 16-byte
 // loads (tables are 16-byte aligned and R/2 is a multiple of 4).
 ROPE_HD void load_cs(const AttnArgs& a, int64_t p, int first, int n, float* c, float* s) {
-  const float4* cr = reinterpret_cast<const float4*>(a.cos + p * a.half + first);
-  const float4* sr = reinterpret_cast<const float4*>(a.sin + p * a.half + first);
+  const uint32_t off = ((uint32_t)p * (uint32_t)a.half + (uint32_t)first) * 4u;
+  const float4* cr = reinterpret_cast<const float4*>(reinterpret_cast<const char*>(a.cos) + off);
+  const float4* sr = reinterpret_cast<const float4*>(reinterpret_cast<const char*>(a.sin) + off);
   for (int j = 0; j < n / 4; ++j) {
     const float4 cv = cr[j], sv = sr[j];
     c[4 * j] = cv.x;
@@ -276,6 +277,10 @@ template <int D, int NT = kBlock> constexpr int v_items_max() {
   return (v_items<D>() + NT - 1) / NT;
 }
 constexpr int at_least_1(int n) { return n > 0 ? n : 1; }
+// Whether staging item it (lane t + n * NT, t < NT, n below the per-lane
+// count) exists: always when the NT lanes share the items evenly, which the
+// compiler then knows without a per-lane test.
+ROPE_HD bool fits(int it, int items, int nt) { return items % nt == 0 || it < items; }
 
 // Raw rows of one tile (and the cos/sin of its rotated items) held in
 // registers between fetch and staging.
@@ -294,7 +299,10 @@ template <int D, int NT = kBlock> struct VStage {
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
-template <int D, int PAIR, int H16, int NT = kBlock>
+// CHECK false: the tile lies wholly inside Sk, key j sits at position j and
+// every position has a table row (no index, Sk <= table_rows), so no key is
+// tested and every key is rotated: the fetch has no branches.
+template <int D, int PAIR, int H16, int NT = kBlock, bool CHECK = true>
 __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* kbase, int k0,
                                         int t, KStage<D, PAIR, H16, NT>& ks) {
   using P = KPlan<D, PAIR, H16, NT>;
@@ -308,16 +316,21 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
       ks.px1[n] = z;
       ks.px2[n] = z;
       ks.prot[n] = false;
-      if (it < kKeys * P::kPair) {
+      if (fits(it, kKeys * P::kPair, NT)) {
         const int key = k0 + it / P::kPair, j = it % P::kPair;
-        if (key < a.seq_k) {
-          const __bf16* krow = kbase + (int64_t)key * D;
-          ks.px1[n] = *reinterpret_cast<const bf16x8*>(krow + 8 * j);
-          ks.px2[n] = *reinterpret_cast<const bf16x8*>(krow + 16 * H16 + 8 * j);
-          const int64_t p = a.rotate_k ? key_pos(a, b, key) : -1;
-          if (p >= 0) {
-            load_cs(a, p, 8 * j, 8, ks.pc[n], ks.ps[n]);
-            ks.prot[n] = true;
+        if (!CHECK || key < a.seq_k) {
+          const char* kb = reinterpret_cast<const char*>(kbase);
+          const uint32_t o1 = ((uint32_t)key * D + 8u * j) * 2u;
+          ks.px1[n] = *reinterpret_cast<const bf16x8*>(kb + o1);
+          ks.px2[n] = *reinterpret_cast<const bf16x8*>(kb + o1 + 32u * H16);
+          if constexpr (CHECK) {
+            const int64_t p = a.rotate_k ? key_pos(a, b, key) : -1;
+            if (p >= 0) {
+              load_cs(a, p, 8 * j, 8, ks.pc[n], ks.ps[n]);
+              ks.prot[n] = true;
+            }
+          } else {
+            load_cs(a, key, 8 * j, 8, ks.pc[n], ks.ps[n]);
           }
         }
       }
@@ -328,10 +341,11 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
     for (int n = 0; n < P::kCopyN; ++n) {
       const int it = t + n * NT;
       ks.cx[n] = z;
-      if (it < kKeys * P::kCopy) {
+      if (fits(it, kKeys * P::kCopy, NT)) {
         const int key = k0 + it / P::kCopy, j = it % P::kCopy;
-        if (key < a.seq_k)
-          ks.cx[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + kR + 8 * j);
+        if (!CHECK || key < a.seq_k)
+          ks.cx[n] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kbase) +
+                                                      ((uint32_t)key * D + kR + 8u * j) * 2u);
       }
     }
   }
@@ -341,15 +355,20 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
       const int it = t + n * NT;
       ks.ix[n] = z;
       ks.irot[n] = false;
-      if (it < kKeys * P::kInter) {
+      if (fits(it, kKeys * P::kInter, NT)) {
         const int key = k0 + it / P::kInter, j = it % P::kInter;
-        if (key < a.seq_k) {
-          ks.ix[n] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)key * D + 8 * j);
+        if (!CHECK || key < a.seq_k) {
+          ks.ix[n] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kbase) +
+                                                      ((uint32_t)key * D + 8u * j) * 2u);
           if (8 * j < R) {
-            const int64_t p = a.rotate_k ? key_pos(a, b, key) : -1;
-            if (p >= 0) {
-              load_cs(a, p, 4 * j, 4, ks.ic[n], ks.is[n]);
-              ks.irot[n] = true;
+            if constexpr (CHECK) {
+              const int64_t p = a.rotate_k ? key_pos(a, b, key) : -1;
+              if (p >= 0) {
+                load_cs(a, p, 4 * j, 4, ks.ic[n], ks.is[n]);
+                ks.irot[n] = true;
+              }
+            } else {
+              load_cs(a, key, 4 * j, 4, ks.ic[n], ks.is[n]);
             }
           }
         }
@@ -359,8 +378,9 @@ __device__ __forceinline__ void fetch_k(const AttnArgs& a, int b, const __bf16* 
 }
 
 // Rotate the fetched K items with the cos/sin fetched beside them and write
-// them to the K tile of buffer `buf`.
-template <int D, int PAIR, int H16, int NT = kBlock>
+// them to the K tile of buffer `buf`. CHECK false (the fetch's form): every
+// item is rotated, with no branches.
+template <int D, int PAIR, int H16, int NT = kBlock, bool CHECK = true>
 __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR, H16, NT>& ks,
                                         __bf16* lds, int buf) {
   using P = KPlan<D, PAIR, H16, NT>;
@@ -369,9 +389,9 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
 #pragma unroll
     for (int n = 0; n < P::kPairN; ++n) {
       const int it = t + n * NT;
-      if (it < kKeys * P::kPair) {
+      if (fits(it, kKeys * P::kPair, NT)) {
         const int kk = it / P::kPair, j = it % P::kPair;
-        if (ks.prot[n]) rotate_split8(ks.px1[n], ks.px2[n], ks.pc[n], ks.ps[n]);
+        if (!CHECK || ks.prot[n]) rotate_split8(ks.px1[n], ks.px2[n], ks.pc[n], ks.ps[n]);
         *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.px1[n];
         *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 16 * H16 + 8 * j)]) = ks.px2[n];
       }
@@ -381,7 +401,7 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
 #pragma unroll
     for (int n = 0; n < P::kCopyN; ++n) {
       const int it = t + n * NT;
-      if (it < kKeys * P::kCopy) {
+      if (fits(it, kKeys * P::kCopy, NT)) {
         const int kk = it / P::kCopy, j = it % P::kCopy;
         *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, kR + 8 * j)]) = ks.cx[n];
       }
@@ -391,29 +411,31 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, int t, KStage<D, PAIR
 #pragma unroll
     for (int n = 0; n < P::kInterN; ++n) {
       const int it = t + n * NT;
-      if (it < kKeys * P::kInter) {
+      if (fits(it, kKeys * P::kInter, NT)) {
         const int kk = it / P::kInter, j = it % P::kInter;
-        if (ks.irot[n]) rotate_inter8(ks.ix[n], ks.ic[n], ks.is[n]);
+        // (unchecked: every key is rotated, and exactly the chunks inside R)
+        if (CHECK ? ks.irot[n] : 8 * j < 2 * a.half) rotate_inter8(ks.ix[n], ks.ic[n], ks.is[n]);
         *reinterpret_cast<bf16x8*>(&lds[k_lds<D>(buf, kk, 8 * j)]) = ks.ix[n];
       }
     }
   }
 }
 
-template <int D, int NT = kBlock>
+template <int D, int NT = kBlock, bool CHECK = true>
 __device__ __forceinline__ void fetch_v(const AttnArgs& a, const __bf16* vbase, int k0, int t,
                                         VStage<D, NT>& vs) {
 #pragma unroll
   for (int n = 0; n < v_items_max<D, NT>(); ++n) {
     const int it = t + n * NT;
-    if (it < v_items<D>()) {
+    if (fits(it, v_items<D>(), NT)) {
       const VItem vi = v_item(it);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = k0 + 4 * vi.k4 + r;
         u32x4 z = {};
-        vs.x[n][r] = key < a.seq_k
-                         ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * D + vi.c * 8)
+        vs.x[n][r] = !CHECK || key < a.seq_k
+                         ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(vbase) +
+                                                           ((uint32_t)key * D + vi.c * 8u) * 2u)
                          : z;
       }
     }
@@ -429,7 +451,7 @@ __device__ __forceinline__ void stage_v(int t, const VStage<D, NT>& vs, __bf16* 
 #pragma unroll
   for (int n = 0; n < v_items_max<D, NT>(); ++n) {
     const int it = t + n * NT;
-    if (it < v_items<D>()) {
+    if (fits(it, v_items<D>(), NT)) {
       const VItem vi = v_item(it);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -447,6 +469,10 @@ __device__ __forceinline__ void stage_v(int t, const VStage<D, NT>& vs, __bf16* 
 #endif
 
 // ---------------------------------------------------------------- kernel
+template <bool B> struct Bool {
+  static constexpr bool value = B;
+};
+
 // H16: split-half pairs, (R/2)/16 (the register distance between the two
 // chunks of a pair; a compile-time constant so the registers stay registers);
 // 0 for interleaved pairs.
@@ -473,7 +499,8 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   const int lane = t & 63, wave = t >> 6;
   const WaveRole role = wave_role(a, wk, wave, G);
   const int h = role.h;
-  const int hk = h / (a.n_heads_q / a.n_heads_k);  // the same for every wave
+  // the same for every wave (readfirstlane: the compiler keeps it scalar)
+  const int hk = __builtin_amdgcn_readfirstlane(h / (a.n_heads_q / a.n_heads_k));
   const int hs = lane >> 5;  // which half of the wave: k slots 0-7 or 8-15
   const int qi = role.row0 + (lane & 31);  // this lane's query row
   constexpr int kSteps = D / 16;  // k-steps of S^T over the head dim
@@ -536,6 +563,8 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   for (int i = 0; i < D / 32; ++i) acc[i] = (floatx16){};
 
   const int causal_shift = a.seq_k - a.seq_q;
+  // every key is rotated at its own index (checked once: uniform)
+  const bool plain_keys = !KR || (a.k_pos == nullptr && a.seq_k <= a.table_rows);
   // this wave's query rows, for the masking decisions (uniform per wave)
   const int wq_first = role.row0;
   const int wq_last = imin(wq_first + 31, a.seq_q - 1);
@@ -560,17 +589,39 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   const float c = a.scale_log2e;
   // every wave runs the same number of steps (the barriers are shared)
   const int n_steps = (n_tiles + G - 1) / G;
-  for (int step = 0; step < n_steps; ++step) {
-    const int kt = step * kStride + grp;  // this group's tile
-    const int k0 = kt * kKeys;
-    const int buf = buf_of(step);
-    const bool more = kt + kStride < n_tiles;
+  struct Step {
+    int kt, k0;
+    bool more, work, edge, fast;
+  };
+  auto step_of = [&](int step) {
+    Step r;
+    r.kt = step * kStride + grp;  // this group's tile
+    r.k0 = r.kt * kKeys;
+    r.more = r.kt + kStride < n_tiles;
     // a tile wholly after this wave's causal diagonal adds nothing: its
     // scores are all masked, so the running max, sum and output stay as
     // they are (the wave still stages the next tile and meets the barriers)
-    const bool work = live && kt < n_tiles && (!a.causal || k0 <= wq_last + causal_shift);
+    r.work = live && r.kt < n_tiles && (!a.causal || r.k0 <= wq_last + causal_shift);
     // masks only where the tile reaches past Sk or this wave's diagonal
-    const bool edge = k0 + kKeys > a.seq_k || (a.causal && k0 + kKeys - 1 > wq_first + causal_shift);
+    r.edge = r.k0 + kKeys > a.seq_k ||
+             (a.causal && r.k0 + kKeys - 1 > wq_first + causal_shift);
+    // The common step: this wave has keys to take, none masked, the next
+    // tile lies wholly inside Sk and (when K is rotated here) its keys sit
+    // at positions 0 .. Sk - 1 of the table. Each condition, once false,
+    // stays false for the later steps, so the common steps come first.
+    r.fast = r.work && !r.edge && r.more && r.k0 + (kStride + 1) * kKeys <= a.seq_k && plain_keys;
+    return r;
+  };
+  // One step over a tile. FAST: the common step, with no branches (but the
+  // rare output rescale), so the compiler can place the vector work of the
+  // softmax, the fetch and the rotation between the matrix instructions. It
+  // runs in a loop of its own, so neither loop holds the other's registers.
+  auto run_step = [&](int step, auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const Step sp = step_of(step);
+    const int k0 = sp.k0;
+    const bool more = sp.more, work = sp.work, edge = sp.edge;
+    const int buf = buf_of(step);
 
     // S^T = K Q^T for one 32-key half of the tile: the half's K fragments are
     // read from LDS, then its chain of products. Lane slot j holds key
@@ -665,33 +716,64 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
     // The two halves are software-pipelined: the second half's score
     // products run beside the first half's softmax, and the first half's
     // output products beside the second half's softmax. The next tile's
-    // fetch is issued between the two, after the score products.
+    // fetch is issued between the two, after the score products, and its
+    // rotation runs beside the second half's output products.
     floatx16 s0, s1;
     bf16x8 p0[2], p1[2];
-    if (work) {
-      s0 = scores(0);
-      if (edge) mask(s0, 0);
-      s1 = scores(1);
-      rescale(softmax(s0, p0));
-      if (edge) mask(s1, 1);
-    }
     KStage<D, KP, KH, NT> ks;
     VStage<D, NT> vs;
-    if (more) {
-      fetch_k<D, KP, KH, NT>(a, b, kbase, k0 + kStride * kKeys, ts, ks);
-      fetch_v<D, NT>(a, vbase, k0 + kStride * kKeys, ts, vs);
-    }
-    if (work) {
+    const int k_next = k0 + kStride * kKeys;
+    if constexpr (FAST) {
+      s0 = scores(0);
+      s1 = scores(1);
+      rescale(softmax(s0, p0));
+      fetch_k<D, KP, KH, NT, false>(a, b, kbase, k_next, ts, ks);
+      fetch_v<D, NT, false>(a, vbase, k_next, ts, vs);
       output(0, p0);
       rescale(softmax(s1, p1));
       output(1, p1);
-    }
-    if (more) {
-      stage_k<D, KP, KH, NT>(a, ts, ks, lds, buf_of(step + 1));
+      stage_k<D, KP, KH, NT, false>(a, ts, ks, lds, buf_of(step + 1));
+      // the next tile's rotation between the second half's output products:
+      // per 16-key step, its V^T reads, then each product followed by a
+      // share of the rotation's vector instructions
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);  // LDS reads
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);   // VALU
+        }
+      }
       stage_v<D, NT>(ts, vs, lds, buf_of(step + 1));
+    } else {
+      if (work) {
+        s0 = scores(0);
+        if (edge) mask(s0, 0);
+        s1 = scores(1);
+        rescale(softmax(s0, p0));
+        if (edge) mask(s1, 1);
+      }
+      if (more) {
+        fetch_k<D, KP, KH, NT>(a, b, kbase, k_next, ts, ks);
+        fetch_v<D, NT>(a, vbase, k_next, ts, vs);
+      }
+      if (work) {
+        output(0, p0);
+        rescale(softmax(s1, p1));
+        output(1, p1);
+      }
+      if (more) {
+        stage_k<D, KP, KH, NT>(a, ts, ks, lds, buf_of(step + 1));
+        stage_v<D, NT>(ts, vs, lds, buf_of(step + 1));
+      }
     }
     __syncthreads();
-  }
+  };
+  int n_fast = 0;
+  while (n_fast < n_steps && step_of(n_fast).fast) ++n_fast;
+  for (int step = 0; step < n_fast; ++step) run_step(step, Bool<true>{});
+  for (int step = n_fast; step < n_steps; ++step) run_step(step, Bool<false>{});
 
   if constexpr (G > 1) {
     // Merge: groups 1 .. G-1 leave their running max, sum and output in LDS

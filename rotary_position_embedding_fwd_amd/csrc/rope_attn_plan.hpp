@@ -53,6 +53,10 @@ inline rope_status_t make_attn_plan(const rope_attn_desc_t* d, AttnPlan* pl) {
   // 32-bit index arithmetic inside the kernel
   const int64_t lim = (int64_t)1 << 30;
   if (B > lim || Hq > lim || Sq > lim || Sk > lim) return ROPE_ERR_SHAPE;
+  // the kernel reads one head's K and V rows and the tables through 32-bit
+  // byte offsets from a per-workgroup base: each must stay under 4 GiB
+  const int64_t lim32 = ((int64_t)1 << 32) - 16;
+  if (Sk * D * 2 > lim32 || (R > 0 && d->table_rows > lim32 / (R * 2))) return ROPE_ERR_SHAPE;
   // byte counts of Q/O and K/V (and the table) must not overflow
   int64_t qbytes = 0, kvbytes = 0, tbytes = 0;
   if (__builtin_mul_overflow(B * Hq, Sq, &qbytes) || __builtin_mul_overflow(qbytes, D * 2, &qbytes) ||

@@ -335,6 +335,10 @@ def call_attn(d):
     (dict(cos=A16 * 4096 + 64), ALIAS),               # table inside O
     (dict(q_pos=A16 * 4096, k_pos=A16 * 10000), ALIAS),
     (dict(k_rotated=2), SHAPE),
+    # one head's K/V rows, and a table, must each stay under 4 GiB (32-bit
+    # offsets in the kernel)
+    (dict(seq_len_k=1 << 24, causal=0, rotate=0), SHAPE),
+    (dict(table_rows=1 << 24), SHAPE),
 ])
 def test_attention_validation_errors(change, expected):
     assert call_attn(attn_desc(**change)) == expected
