@@ -66,6 +66,11 @@ void walk(const AttnPlan& pl, int64_t q_elems, int64_t kv_elems, int64_t table_e
   ck.fail(SPLIT && D != 64, "wave groups only at head dim 64");
   ck.fail(pl.lds != lds_bytes_groups<D>(G), "plan's LDS size");
   ck.fail(pl.lds > 160 * 1024, "the workgroup's LDS fits a compute unit");
+  // the kernel forms K/V and cos/sin addresses as 32-bit byte offsets from
+  // a head's (or the table's) base: every offset it can form must fit
+  ck.fail((int64_t)a.seq_k * D * 2 > ((int64_t)1 << 32) - 16, "K/V head rows under 4 GiB");
+  ck.fail(a.rotate && a.table_rows * a.half * 4 > ((int64_t)1 << 32) - 16,
+          "cos/sin table under 4 GiB");
   const int lds_elems = (int)(pl.lds / 2);
   const int R = 2 * a.half;
   // K staging: the kernel's plan for this instantiation (rotated while
