@@ -684,6 +684,8 @@ def time_attention(target_s: float = 0.5):
             "k_once_frac_of_mfma_bf16_peak": round(
                 flops / (k_once_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "attention_without_rotation_TFLOPs": round(flops / (plain_us * 1e-6) / 1e12, 1),
+            "attention_without_rotation_frac_of_mfma_bf16_peak": round(
+                flops / (plain_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "measured_mfma_bf16_ceiling": ceiling,
             "fused_frac_of_measured_mfma_ceiling": round(tf / ceiling["TFLOPs"], 4),
             "k_once_frac_of_measured_mfma_ceiling": round(
