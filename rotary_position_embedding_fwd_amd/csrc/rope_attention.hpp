@@ -478,6 +478,8 @@ template <bool B> struct Bool {
 // 0 for interleaved pairs.
 template <int D, int PAIR, int H16, bool KR, int G>
 __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
+  static_assert(G == 1 || G == 2 || G == 4, "1, 2 or 4 wave groups");
+#if defined(__HIP_DEVICE_COMPILE__)
   // K staging: rotated while staged (KR, the fused form), or copied as it
   // arrives (K already rotated; the copy-only plan keeps no cos/sin
   // registers for it)
@@ -488,10 +490,8 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
   // ...), each staging its own tiles into its own double buffer (NT lanes
   // stage a tile); their softmax states merge at the end. The chain of
   // tiles a workgroup walks is divided by G.
-  static_assert(G == 1 || G == 2 || G == 4, "1, 2 or 4 wave groups");
   constexpr int NT = kBlock / G;
   constexpr int kStride = G;  // tiles between a group's steps
-#if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __bf16 lds[];
   const Work wk = work_of(a, blockIdx.x);
   const int q_tile = wk.q_tile, b = wk.b;
