@@ -354,3 +354,57 @@ def test_gpu_full_llama_size(orc, direction):
     eq, ek = _expected(c, t["q"], t["k"], None, 0, rows)
     check(gq, eq, w.dtype, "q")
     check(gk, ek, w.dtype, "k")
+
+
+# ------------------------------------------------ seeded random configurations
+
+def random_case(seed: int, budget: int) -> tuple:
+    """One case in the tuple form above (its first 14 fields), drawn from
+    `seed`: sizes, dtype, pairing, layout, in/out of place, positions,
+    direction and the XPOS parameters; Q + K hold at most about `budget`
+    elements."""
+    r = np.random.RandomState(seed)
+    dtype = str(r.choice(["f32", "f16", "bf16"]))
+    pairing = str(r.choice(["split_half", "interleaved"]))
+    layout = str(r.choice(["bhsd", "bshd"]))
+    D = int(r.choice([8, 16, 32, 40, 64, 66, 72, 96, 128, 256]))
+    R = D - D % 2 if r.rand() < 0.6 else 2 * int(r.randint(1, D // 2 + 1))
+    Hq = int(r.choice([1, 2, 3, 5, 8, 12, 16, 32]))
+    Hk = int(r.randint(0, Hq + 1))
+    B = int(r.choice([1, 2, 3]))
+    S = int(r.choice([1, 2, 9, 64, 100, 300, 700]))
+    S = max(1, min(S, budget // max(1, B * (Hq + Hk) * D)))
+    pkind = str(r.choice(["none", "none", "skip"])) if S > 1 else str(r.choice(["none",
+                                                                                 "decode"]))
+    oop = bool(r.rand() < 0.3)
+    direction = int(r.choice([1, -1]))
+    sb = float(r.choice([2.0, 16.0, 512.0]))
+    center = float(r.randint(0, S + 1))
+    return (B, S, Hq, Hk, D, R, dtype, pairing, layout, oop, pkind, direction, sb, center)
+
+
+def _check_random(c, gq, gk):
+    q, k, pos, pbs, rows, cos, sin, zq, zk = _case_data(c, seed=9600)
+    eq, ek = _expected(c, q, k, pos, pbs, rows)
+    check(gq, eq, c[6], "q")
+    if ek is not None:
+        check(gk, ek, c[6], "k")
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_emulated_random_cases(orc, emu, case):
+    c = random_case(31000 + case, 120_000)
+    q, k, pos, pbs, rows, cos, sin, zq, zk = _case_data(c, seed=9600)
+    status, gq, gk = run_emu(emu, c, q, k, pos, pbs, rows, cos, sin, zq, zk)
+    assert status == 0, c
+    _check_random(c, gq, gk)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(60))
+def test_gpu_random_cases(orc, case):
+    c = random_case(32000 + case, 2_000_000)
+    print(f"xpos random case {case}: {c}", flush=True)
+    q, k, pos, pbs, rows, cos, sin, zq, zk = _case_data(c, seed=9600)
+    gq, gk = _gpu_call(c, q, k, pos, pbs, rows, cos, sin, zq, zk)
+    _check_random(c, gq, gk)
