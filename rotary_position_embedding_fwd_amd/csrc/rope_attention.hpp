@@ -120,7 +120,6 @@ template <int D, int PAIR, int H16, int NT = kBlock> struct KPlan {
 template <int D> constexpr int k_lds_elems() { return kKeys * (D + kKPad); }
 template <int D> constexpr int v_lds_elems() { return D * (kKeys + kVPad); }
 template <int D> constexpr int buf_elems() { return k_lds_elems<D>() + v_lds_elems<D>(); }
-template <int D> constexpr int lds_bytes() { return 2 * 2 * buf_elems<D>(); }
 // G wave groups: a double buffer per group
 template <int D> constexpr int lds_bytes_groups(int g) { return 2 * 2 * g * buf_elems<D>(); }
 template <int D> ROPE_HD int k_lds(int buf, int key, int dim) {
