@@ -732,9 +732,10 @@ __global__ void __launch_bounds__(kBlock, 2) rope_attention_kernel(AttnArgs a) {
       rescale(softmax(s1, p1));
       output(1, p1);
       stage_k<D, KP, KH, NT, false>(a, ts, ks, lds, buf_of(step + 1));
-      // the next tile's rotation between the second half's output products:
-      // per 16-key step, its V^T reads, then each product followed by a
-      // share of the rotation's vector instructions
+      // ask the scheduler for the next tile's rotation between the second
+      // half's output products: per 16-key step, its V^T reads, then each
+      // product followed by a share of the rotation's vector instructions
+      // (a scheduling hint; the instructions and their results are the same)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);  // LDS reads
