@@ -11,6 +11,8 @@ The output is compared with the oracle on every element under the bound of
 tests/_attn.py. The grid sizes the draws produce also reach the forms for
 small grids at head dim 64 (two or four wave groups).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,7 +23,8 @@ import workloads as W
 from tests import _attn as A
 
 DEV = "cuda"
-N_CASES = 40
+# LIBROPE_RANDOM_SCALE=n runs n times as many cases (a longer sweep on demand)
+N_CASES = 40 * int(os.environ.get("LIBROPE_RANDOM_SCALE", "1"))
 WORK_BUDGET = 1.5e8  # B * Hq * Sq * Sk * D per case, so the oracle and bound stay quick
 
 

@@ -15,6 +15,8 @@ every kernel rotates each pair with the same float32 steps, so the bits must
 agree whichever shape runs. Views' neighbours (the V part of a packed buffer)
 stay bit-exact, and out-of-place calls leave their inputs untouched.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -26,7 +28,8 @@ from tests import _parity as P
 from tests._random_configs import draw as _draw, workload
 
 DEV = "cuda"
-N_CASES = 160
+# LIBROPE_RANDOM_SCALE=n runs n times as many cases (a longer sweep on demand)
+N_CASES = 160 * int(os.environ.get("LIBROPE_RANDOM_SCALE", "1"))
 ELEMENT_BUDGET = 3 << 20  # Q + K elements per case, so the oracle takes well under a second
 
 

@@ -400,8 +400,12 @@ def test_emulated_random_cases(orc, emu, case):
     _check_random(c, gq, gk)
 
 
+# LIBROPE_RANDOM_SCALE=n runs n times as many GPU cases (a longer sweep on demand)
+GPU_RANDOM_CASES = 60 * int(os.environ.get("LIBROPE_RANDOM_SCALE", "1"))
+
+
 @pytest.mark.gpu
-@pytest.mark.parametrize("case", range(60))
+@pytest.mark.parametrize("case", range(GPU_RANDOM_CASES))
 def test_gpu_random_cases(orc, case):
     c = random_case(32000 + case, 2_000_000)
     print(f"xpos random case {case}: {c}", flush=True)
