@@ -470,6 +470,16 @@ def time_workload(w, launches=("auto", "rows", "token"), target_s: float = 0.15)
         out = {"workload": w.name, "launch": launch, "buffer_sets": sets,
                "algorithmic_bytes_per_call": nbytes}
         _time_calls(out, fwd, bwd, sets, nbytes, target_s, stream)
+        if launch == "auto" and nbytes < (64 << 20):
+            # small calls are bound by the launch: their µs per call replayed
+            # from a captured graph (one buffer set), beside the empty kernel's
+            b0 = bufs[0]
+            gkw = dict(kw, stream=None)
+
+            def make(st, b0=b0, gkw=gkw):
+                return rp.prepare(b0["q"], b0["k"], cos, sin, **dict(gkw, stream=st)).rope_fwd_qk
+            out["fwd_us_per_call_graph_replay"] = round(_graph_us_per_call(make), 3)
+            out["empty_kernel_us_per_call_graph_replay"] = empty_kernel_floor()
         results.append(out)
     del bufs
     torch.cuda.empty_cache()
