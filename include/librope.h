@@ -90,8 +90,9 @@ typedef enum rope_pairing { ROPE_SPLIT_HALF = 0, ROPE_INTERLEAVED = 1 } rope_pai
  * (seq_len 1), the rows shape for [B,H,S,D] unless there are too few tokens
  * to fill the device; within each, AUTO may also pick a form that only it
  * launches (one (token, head) chunk per lane for [B,H,S,D] split-half calls,
- * items over the whole call for dense [B,S,H,D] interleaved calls and for
- * token-major split-half calls with rotated spans up to 128 bytes). Every
+ * items over the whole call, token by token, for token-major interleaved
+ * calls with rotated spans up to 256 bytes and split-half calls with spans
+ * up to 128 bytes, where a token's heads are adjacent). Every
  * shape runs the same per-pair arithmetic and gives bit-identical results;
  * ROWS and TOKEN force the named shape's general kernels (for comparisons). */
 typedef enum rope_launch {

@@ -452,9 +452,11 @@ inline rope_status_t make_plan_apply(const rope_apply_desc_t* d, int cus, Plan* 
     pl->grid = blocks < max_grid ? blocks : max_grid;
     pl->single = pl->grid == blocks && pl->block >= lanes_needed;
     if (a.angles && pl->single) pl->lds_bytes = theta_shared_bytes(tpb, a.half);
-    // Flat shape for dense token-major calls of many tokens: items numbered
-    // over the whole call, so the grid streams Q and then K in memory order.
-    // Measured on MI355X in place, forward, fwd µs (flat / token kernel):
+    // Flat shape for token-major calls of many tokens whose heads of a token
+    // are adjacent: items numbered over the whole call token by token (each
+    // token's Q heads, then its K heads), so the grid walks the rows in
+    // memory order. Measured on MI355X in place, forward, on dense [B,S,H,D]
+    // tensors, fwd µs (flat / token kernel):
     //   interleaved pairs: [8,2048,16+16,64] fp16 22.9 / 23.8,
     //     [4,4096,32+32,64] bf16 42.3 / 43.3, [4,4096,32+8,128] bf16
     //     52.6 / 56.5, but [2,4096,16+4,256] bf16 37.3 / 30.6: so rotated
